@@ -1,0 +1,174 @@
+/*
+ * fs_sinkhorn.h -- C ABI of the streaming log-domain Sinkhorn solver for
+ * entropic optimal transport with squared-Euclidean cost on AMD MI355X
+ * (gfx950).
+ *
+ * What it computes.  "FlashSinkhorn: IO-Aware Entropic Optimal Transport on
+ * GPU" (gist.science explainer), section "Method", part 1: for point clouds
+ * X (n x d) with weights a and Y (m x d) with weights b, the stabilised
+ * log-domain Sinkhorn update
+ *     f_i <- -eps * LSE_j [ (g_j - C_ij)/eps + log b_j ],  C_ij = |x_i - y_j|^2,
+ * equals a row-wise log-sum-exp of the biased dot-product score matrix
+ * (2 x_i.y_j + g_j - |y_j|^2 + eps log b_j)/eps, plus |x_i|^2; the g-update is
+ * the mirror image with (Y, b, g) and (X, a, f) exchanged.  Part 2 of the same
+ * section: the n x m matrix is never stored; tiles of the other cloud are
+ * streamed past a resident block of rows while a running maximum and
+ * exp-sum are kept on chip.  Part 3: the transport plan
+ *     P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps)
+ * is applied to a matrix V (U = P.V, or the barycentric projection P.V / a)
+ * by the same streaming traversal, again without storing P.
+ *
+ * Conventions (every entry point):
+ *  - Array arguments are DEVICE pointers to float32, row-major, unless stated.
+ *    Point rows are contiguous: X[i*d + t].
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    All work is enqueued on it and is asynchronous unless stated.  Inputs must
+ *    stay valid until the enqueued work has finished.
+ *  - Every call returns an fs_status.  Argument errors detected on the host are
+ *    returned before anything is enqueued; fs_last_error() then gives a
+ *    thread-local message.  The library never aborts and never throws.
+ *  - The library never allocates device memory.  The caller passes one
+ *    workspace of fs_workspace_bytes() bytes, 256-byte aligned, which must
+ *    outlive the problem handle and must not be shared by two live handles.
+ *  - Results are deterministic: the same inputs, launch and device give
+ *    bit-identical outputs (no atomics in any reduction; fixed merge order).
+ */
+#ifndef FS_SINKHORN_H
+#define FS_SINKHORN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FS_OK = 0,
+    FS_ERR_INVALID_ARG = 1,   /* null pointer, bad size/enum/eps, forbidden alias */
+    FS_ERR_WORKSPACE = 2,     /* workspace too small or misaligned */
+    FS_ERR_DEVICE = 3,        /* no usable gfx950 device, or a HIP runtime error */
+    FS_ERR_NONFINITE = 4,     /* NaN/Inf in X, Y, a, b, or a weight <= 0 */
+    FS_ERR_NOT_CONVERGED = 5  /* tol > 0 and the residual stayed above tol */
+} fs_status;
+
+/* Element type of the score contraction 2 x.y (everything after it is fp32).
+ * AUTO: d <= 8 -> fp32 vector FMA; d > 8 -> fp32 matrix cores.
+ * BF16 / FP16: points (after a common shift, below) are rounded to
+ * bfloat16 / float16 with round-to-nearest-even and multiplied on matrix cores
+ * with fp32 accumulation; |x|^2 and |y|^2 are taken from the rounded points,
+ * so the solver solves the problem of the rounded clouds exactly (up to fp32).
+ * FP32 with d <= 8 uses vector FMA; FP32 with d > 8 uses fp32 matrix cores. */
+typedef enum {
+    FS_PREC_AUTO = 0,
+    FS_PREC_FP32 = 1,
+    FS_PREC_BF16 = 2,
+    FS_PREC_FP16 = 3
+} fs_score_prec;
+
+/* Opaque host handle.  It owns no device memory; it points into the
+ * caller's workspace.  Not thread-safe; distinct handles are independent. */
+typedef struct fs_problem fs_problem;
+
+/* Solve schedule.  Stage s (0..n_stages-1) uses
+ *   eps_s = eps_start * (eps_end/eps_start)^(s/(n_stages-1))   (n_stages > 1),
+ *   eps_s = eps_end                                             (n_stages == 1),
+ * for iters_per_stage alternating iterations (f-update, then g-update using the
+ * new f), carrying f and g across stages.  With tol > 0 the L1 marginal
+ * residual  sum_i |sum_j P_ij - a_i| + sum_j |sum_i P_ij - b_j|  of the current
+ * (f, g) is evaluated after every check_every-th iteration and the solve stops
+ * at the first one <= tol, returning that (f, g).  warm_start != 0 starts from
+ * the f, g passed in (g is what the first f-update reads); otherwise g starts
+ * at 0. */
+typedef struct {
+    int32_t n_stages;        /* >= 1 */
+    float eps_start;         /* > 0, used when n_stages > 1 */
+    float eps_end;           /* > 0 */
+    int32_t iters_per_stage; /* >= 0 */
+    float tol;               /* <= 0: fixed iteration count, never synchronises */
+    int32_t check_every;     /* >= 1 when tol > 0 */
+    int32_t warm_start;
+} fs_solve_opts;
+
+/* Filled on the host by fs_sinkhorn_solve (synchronises at the end when tol > 0). */
+typedef struct {
+    int32_t iters_done;
+    float final_eps;
+    float residual;          /* last evaluated residual; -1 if none was evaluated */
+} fs_solve_info;
+
+/* Bytes of workspace needed for a problem of this shape.  dv_max bounds the
+ * width of V in later fs_apply_transport calls (0: no transport).  Returns 0
+ * for invalid arguments.  Pure host function. */
+size_t fs_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t dv_max,
+                          fs_score_prec prec);
+
+/* Creates a problem: copies X (n x d) and Y (m x d) into the workspace after
+ * subtracting one common shift (the midpoint of the joint bounding box, which
+ * leaves every C_ij and hence f, g unchanged), converts them to the score
+ * element type, and precomputes |x|^2, |y|^2 and log-weights.  Writes f = 0
+ * and g = 0 (f: n floats, g: m floats; either may be NULL to skip).
+ * a (n) and b (m) are the weights; they must be > 0 and finite (sums are used
+ * as given).  Synchronises once to read back a validity flag:
+ * FS_ERR_NONFINITE if X, Y, a or b holds NaN/Inf or a weight is <= 0.
+ * Limits: 1 <= n, m <= 2^31 - 1; 1 <= d <= 1024; dv_max 0..4096. */
+fs_status fs_potentials_init(const float* X, const float* Y, const float* a,
+                             const float* b, int64_t n, int64_t m, int32_t d,
+                             int32_t dv_max, fs_score_prec prec, void* workspace,
+                             size_t workspace_bytes, float* f, float* g, void* stream,
+                             fs_problem** out);
+
+/* One f-update: f_out_i = -eps LSE_j[(g_j - C_ij)/eps + log b_j], all i.
+ * g (m floats) is read, f_out (n floats) is written.  If f_cur (n floats) is
+ * given, the row term of the residual of (f_cur, g),
+ *   sum_i |sum_j P_ij - a_i| = sum_i a_i |exp((f_cur_i - f_out_i)/eps) - 1|,
+ * is written to *row_resid (device, 1 float); row_resid may be NULL.
+ * f_out may alias f_cur only when row_resid is NULL. */
+fs_status fs_lse_update_f(fs_problem* p, float eps, const float* g, float* f_out,
+                          const float* f_cur, float* row_resid, void* stream);
+
+/* One g-update: g_out_j = -eps LSE_i[(f_i - C_ij)/eps + log a_i], all j; with
+ * g_cur given, *col_resid = sum_j b_j |exp((g_cur_j - g_out_j)/eps) - 1|, the
+ * column term of the residual of (f, g_cur). */
+fs_status fs_lse_update_g(fs_problem* p, float eps, const float* f, float* g_out,
+                          const float* g_cur, float* col_resid, void* stream);
+
+/* Both terms of the L1 marginal residual of (f, g): out2[0] = row term,
+ * out2[1] = column term (device, 2 floats).  Costs two dry-run updates. */
+fs_status fs_marginal_residual(fs_problem* p, float eps, const float* f, const float* g,
+                               float* out2, void* stream);
+
+/* The alternating solve described at fs_solve_opts, in place on f (n) and g (m).
+ * With tol <= 0 it is fully asynchronous.  info may be NULL.  Returns
+ * FS_ERR_NOT_CONVERGED (with valid f, g and info) if tol > 0 was not reached. */
+fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* opts, float* f, float* g,
+                            fs_solve_info* info, void* stream);
+
+/* Transport application: U = P.V with V (m x dv) and U (n x dv), P from (f, g)
+ * at this eps, or the barycentric projection U_i = (P.V)_i / a_i when
+ * divide_by_a != 0.  1 <= dv <= dv_max of the problem; U must not overlap V. */
+fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const float* g,
+                             const float* V, int32_t dv, float* U, int32_t divide_by_a,
+                             void* stream);
+
+/* Frees the host handle only (the workspace is the caller's). */
+void fs_destroy(fs_problem* p);
+
+/* Static text for a status code. */
+const char* fs_status_string(fs_status s);
+
+/* Thread-local detail message of the last failing call on this thread. */
+const char* fs_last_error(void);
+
+/* Introspection for tests and benchmarks (host): the score path chosen for the
+ * problem (0 = fp32 vector, 1 = fp32 matrix, 2 = bf16 matrix, 3 = fp16
+ * matrix), its padded dimension, and the split count used for the f- and
+ * g-update launches. */
+fs_status fs_problem_info(const fs_problem* p, int32_t* path, int32_t* d_pad,
+                          int32_t* f_splits, int32_t* g_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FS_SINKHORN_H */

@@ -1,0 +1,257 @@
+"""Thin ctypes binding of ``libfs_sinkhorn.so`` (the C ABI in include/fs_sinkhorn.h).
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the solver runs in the library's kernels.  If the
+library has not been built the calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "FS_OK", "FS_ERR_INVALID_ARG", "FS_ERR_WORKSPACE", "FS_ERR_DEVICE", "FS_ERR_NONFINITE",
+    "FS_ERR_NOT_CONVERGED", "PREC_AUTO", "PREC_FP32", "PREC_BF16", "PREC_FP16", "FsError",
+    "Problem", "load", "lib_path", "fs_workspace_bytes", "fs_potentials_init",
+    "fs_lse_update_f", "fs_lse_update_g", "fs_marginal_residual", "fs_sinkhorn_solve",
+    "fs_apply_transport", "fs_problem_info", "fs_status_string", "fs_last_error", "solve",
+]
+
+FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
+    FS_ERR_NOT_CONVERGED = range(6)
+PREC_AUTO, PREC_FP32, PREC_BF16, PREC_FP16 = range(4)
+_PREC_NAMES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16, "fp16": PREC_FP16}
+PATH_NAMES = {0: "fp32-valu", 1: "fp32-mfma", 2: "bf16-mfma", 3: "fp16-mfma"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfs_sinkhorn.so")
+
+
+class SolveOpts(ctypes.Structure):
+    _fields_ = [("n_stages", ctypes.c_int32), ("eps_start", ctypes.c_float),
+                ("eps_end", ctypes.c_float), ("iters_per_stage", ctypes.c_int32),
+                ("tol", ctypes.c_float), ("check_every", ctypes.c_int32),
+                ("warm_start", ctypes.c_int32)]
+
+
+class SolveInfo(ctypes.Structure):
+    _fields_ = [("iters_done", ctypes.c_int32), ("final_eps", ctypes.c_float),
+                ("residual", ctypes.c_float)]
+
+
+class FsError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_name(status)}: {message}")
+
+
+def _status_name(s: int) -> str:
+    lib = _LIB
+    if lib is None:
+        return str(s)
+    return lib.fs_status_string(s).decode()
+
+
+_vp = ctypes.c_void_p
+_fp = ctypes.c_void_p  # device float* passed as an address
+
+
+def load():
+    """Load the HIP library (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    i64, i32, f32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.fs_workspace_bytes.restype = sz
+    lib.fs_workspace_bytes.argtypes = [i64, i64, i32, i32, ctypes.c_int]
+    lib.fs_potentials_init.restype = ctypes.c_int
+    lib.fs_potentials_init.argtypes = [_fp, _fp, _fp, _fp, i64, i64, i32, i32, ctypes.c_int,
+                                       _vp, sz, _fp, _fp, _vp, ctypes.POINTER(_vp)]
+    lib.fs_lse_update_f.restype = ctypes.c_int
+    lib.fs_lse_update_f.argtypes = [_vp, f32, _fp, _fp, _fp, _fp, _vp]
+    lib.fs_lse_update_g.restype = ctypes.c_int
+    lib.fs_lse_update_g.argtypes = [_vp, f32, _fp, _fp, _fp, _fp, _vp]
+    lib.fs_marginal_residual.restype = ctypes.c_int
+    lib.fs_marginal_residual.argtypes = [_vp, f32, _fp, _fp, _fp, _vp]
+    lib.fs_sinkhorn_solve.restype = ctypes.c_int
+    lib.fs_sinkhorn_solve.argtypes = [_vp, ctypes.POINTER(SolveOpts), _fp, _fp,
+                                      ctypes.POINTER(SolveInfo), _vp]
+    lib.fs_apply_transport.restype = ctypes.c_int
+    lib.fs_apply_transport.argtypes = [_vp, f32, _fp, _fp, _fp, i32, _fp, i32, _vp]
+    lib.fs_destroy.restype = None
+    lib.fs_destroy.argtypes = [_vp]
+    lib.fs_status_string.restype = ctypes.c_char_p
+    lib.fs_status_string.argtypes = [ctypes.c_int]
+    lib.fs_last_error.restype = ctypes.c_char_p
+    lib.fs_last_error.argtypes = []
+    lib.fs_problem_info.restype = ctypes.c_int
+    lib.fs_problem_info.argtypes = [_vp] + [ctypes.POINTER(i32)] * 4
+    _LIB = lib
+    return lib
+
+
+def fs_status_string(s: int) -> str:
+    return load().fs_status_string(int(s)).decode()
+
+
+def fs_last_error() -> str:
+    return load().fs_last_error().decode()
+
+
+def _check(status: int, where: str, allow=()):
+    if status != FS_OK and status not in allow:
+        raise FsError(status, where, fs_last_error())
+    return status
+
+
+def _prec(prec) -> int:
+    if isinstance(prec, str):
+        return _PREC_NAMES[prec.lower()]
+    return int(prec)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements (has {t.numel()})")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class Problem:
+    """A problem handle plus the workspace tensor it lives in."""
+
+    def __init__(self, handle, workspace: torch.Tensor, n: int, m: int, d: int, dv_max: int):
+        self.handle = handle
+        self.workspace = workspace
+        self.n, self.m, self.d, self.dv_max = n, m, d, dv_max
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.fs_destroy(self.handle)
+            self.handle = None
+
+    @property
+    def info(self) -> dict:
+        return fs_problem_info(self)
+
+
+def fs_workspace_bytes(n: int, m: int, d: int, dv_max: int = 0, prec="auto") -> int:
+    return int(load().fs_workspace_bytes(n, m, d, dv_max, _prec(prec)))
+
+
+def fs_potentials_init(X: torch.Tensor, Y: torch.Tensor, a: torch.Tensor, b: torch.Tensor, *,
+                       dv_max: int = 0, prec="auto", f: Optional[torch.Tensor] = None,
+                       g: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> Problem:
+    lib = load()
+    n, d = X.shape
+    m = Y.shape[0]
+    if Y.shape[1] != d:
+        raise ValueError("X and Y must have the same number of columns")
+    need = lib.fs_workspace_bytes(n, m, d, dv_max, _prec(prec))
+    if need == 0:
+        _check(FS_ERR_INVALID_ARG, "fs_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=X.device)
+    base = workspace.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    avail = workspace.numel() - (aligned - base)
+    h = _vp()
+    st = lib.fs_potentials_init(_dev(X, "X", n * d), _dev(Y, "Y", m * d), _dev(a, "a", n),
+                                _dev(b, "b", m), n, m, d, dv_max, _prec(prec), aligned, avail,
+                                _dev(f, "f", n), _dev(g, "g", m), _stream(stream),
+                                ctypes.byref(h))
+    _check(st, "fs_potentials_init")
+    return Problem(h, workspace, n, m, d, dv_max)
+
+
+def fs_lse_update_f(p: Problem, eps: float, g, f_out, f_cur=None, row_resid=None, stream=None):
+    return _check(load().fs_lse_update_f(p.handle, float(eps), _dev(g, "g", p.m),
+                                         _dev(f_out, "f_out", p.n), _dev(f_cur, "f_cur", p.n),
+                                         _dev(row_resid, "row_resid", 1), _stream(stream)),
+                  "fs_lse_update_f")
+
+
+def fs_lse_update_g(p: Problem, eps: float, f, g_out, g_cur=None, col_resid=None, stream=None):
+    return _check(load().fs_lse_update_g(p.handle, float(eps), _dev(f, "f", p.n),
+                                         _dev(g_out, "g_out", p.m), _dev(g_cur, "g_cur", p.m),
+                                         _dev(col_resid, "col_resid", 1), _stream(stream)),
+                  "fs_lse_update_g")
+
+
+def fs_marginal_residual(p: Problem, eps: float, f, g, out2, stream=None):
+    return _check(load().fs_marginal_residual(p.handle, float(eps), _dev(f, "f", p.n),
+                                              _dev(g, "g", p.m), _dev(out2, "out2", 2),
+                                              _stream(stream)), "fs_marginal_residual")
+
+
+def fs_sinkhorn_solve(p: Problem, f, g, *, eps_end: float, iters_per_stage: int,
+                      n_stages: int = 1, eps_start: Optional[float] = None, tol: float = 0.0,
+                      check_every: int = 10, warm_start: bool = False, stream=None,
+                      raise_not_converged: bool = True) -> dict:
+    opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
+                     float(eps_end), int(iters_per_stage), float(tol), int(check_every),
+                     int(bool(warm_start)))
+    info = SolveInfo()
+    st = load().fs_sinkhorn_solve(p.handle, ctypes.byref(opts), _dev(f, "f", p.n),
+                                  _dev(g, "g", p.m), ctypes.byref(info), _stream(stream))
+    allow = () if raise_not_converged else (FS_ERR_NOT_CONVERGED,)
+    _check(st, "fs_sinkhorn_solve", allow)
+    return {"status": st, "iters_done": info.iters_done, "final_eps": info.final_eps,
+            "residual": info.residual}
+
+
+def fs_apply_transport(p: Problem, eps: float, f, g, V, U, divide_by_a: bool = False,
+                       stream=None):
+    dv = V.shape[1]
+    return _check(load().fs_apply_transport(p.handle, float(eps), _dev(f, "f", p.n),
+                                            _dev(g, "g", p.m), _dev(V, "V", p.m * dv), dv,
+                                            _dev(U, "U", p.n * dv), int(bool(divide_by_a)),
+                                            _stream(stream)), "fs_apply_transport")
+
+
+def fs_problem_info(p: Problem) -> dict:
+    vals = [ctypes.c_int32() for _ in range(4)]
+    _check(load().fs_problem_info(p.handle, *[ctypes.byref(v) for v in vals]), "fs_problem_info")
+    path, dp, fs_, gs = (v.value for v in vals)
+    return {"path": PATH_NAMES.get(path, str(path)), "d_pad": dp, "f_splits": fs_,
+            "g_splits": gs}
+
+
+def solve(X, Y, a, b, *, eps: float, iters: int, prec="auto", n_stages: int = 1,
+          eps_start: Optional[float] = None, tol: float = 0.0, check_every: int = 10,
+          dv_max: int = 0):
+    """Convenience: init + solve; returns (problem, f, g, info)."""
+    dev = X.device
+    f = torch.empty(X.shape[0], dtype=torch.float32, device=dev)
+    g = torch.empty(Y.shape[0], dtype=torch.float32, device=dev)
+    p = fs_potentials_init(X, Y, a, b, dv_max=dv_max, prec=prec, f=f, g=g)
+    info = fs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=iters, n_stages=n_stages,
+                             eps_start=eps_start, tol=tol, check_every=check_every,
+                             raise_not_converged=False)
+    return p, f, g, info

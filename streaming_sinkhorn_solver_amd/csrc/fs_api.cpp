@@ -1,0 +1,548 @@
+// fs_api.cpp -- host side of the C ABI declared in include/fs_sinkhorn.h:
+// argument validation, workspace layout, path and launch-shape selection, and
+// the alternating solve loop (one stream, no host round trips unless a
+// residual stop was asked for).
+//
+// The iteration follows "FlashSinkhorn: IO-Aware Entropic Optimal Transport
+// on GPU" (gist.science explainer), section "Method", part 1 (the f-update and
+// its mirror g-update, alternated); the annealing and residual stop are the
+// schedule options of fs_solve_opts.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fs_internal.h"
+#include "fs_sinkhorn.h"
+
+using namespace fs;
+
+struct fs_problem {
+    int device;
+    int path;
+    int64_t n, m;
+    int d;       // true dimension
+    int dp;      // operand row stride in elements
+    int lse_dp;  // the dp value passed to the LSE/transport launchers
+    int dv_max;
+    int f_split, f_kps;  // split count / keys per split of the f-update (rows X, keys Y)
+    int g_split, g_kps;
+    Cloud X, Y;
+    float* shift;
+    float* bbox_min;
+    float* bbox_max;
+    int* flag;
+    float2* part;
+    float* resid_part;
+    float* scal;      // [0..1] residual outputs, [2..3] transport scale pair
+    float* pot_tmp;   // max(n, m) floats
+    void* vt;         // f16 [dv_max][m_pad] (matrix paths with dv_max > 0)
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+fs_status fail(fs_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+fs_status hip_fail(hipError_t e, const char* where) {
+    return fail(FS_ERR_DEVICE, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+constexpr int kBboxParts = 64;
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t pad_rows(int64_t n) { return (n + kRowPad - 1) / kRowPad * kRowPad; }
+int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+struct Shape {
+    int path = -1;
+    int dp = 0;      // stride
+    int lse_dp = 0;  // launcher dp
+    size_t es = 4;   // element size
+    int f_split = 1, f_kps = 0, g_split = 1, g_kps = 0;
+};
+
+// Returns FS_OK and fills sh, or an error.
+fs_status choose_path(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec,
+                      Shape& sh) {
+    if (n < 1 || m < 1 || n > 0x7fffffffLL || m > 0x7fffffffLL)
+        return fail(FS_ERR_INVALID_ARG, "n and m must be in [1, 2^31-1] (got n=%lld, m=%lld)",
+                    (long long)n, (long long)m);
+    if (d < 1 || d > 1024)
+        return fail(FS_ERR_INVALID_ARG, "d must be in [1, 1024] (got %d)", d);
+    if (dv_max < 0 || dv_max > 4096)
+        return fail(FS_ERR_INVALID_ARG, "dv_max must be in [0, 4096] (got %d)", dv_max);
+    switch (prec) {
+        case FS_PREC_AUTO:
+        case FS_PREC_FP32:
+            if (d <= 8) {
+                sh.path = PATH_VALU;
+                sh.dp = d <= 4 ? 4 : 8;
+                sh.lse_dp = d;
+                sh.es = 4;
+            } else if (d <= 512) {
+                sh.path = PATH_MFMA_F32;
+                sh.dp = 8 * next_pow2((d + 7) / 8);
+                sh.lse_dp = sh.dp;
+                sh.es = 4;
+            } else {
+                return fail(FS_ERR_INVALID_ARG,
+                            "fp32 scores support d <= 512 (got %d); use FS_PREC_BF16 or FS_PREC_FP16",
+                            d);
+            }
+            break;
+        case FS_PREC_BF16:
+        case FS_PREC_FP16:
+            sh.path = prec == FS_PREC_BF16 ? PATH_MFMA_BF16 : PATH_MFMA_F16;
+            sh.dp = 16 * next_pow2((d + 15) / 16);
+            sh.lse_dp = sh.dp;
+            sh.es = 2;
+            break;
+        default:
+            return fail(FS_ERR_INVALID_ARG, "unknown fs_score_prec %d", (int)prec);
+    }
+    return FS_OK;
+}
+
+// Key-range split so that (row blocks x splits) fills the GPU in a near-whole
+// number of rounds, preferring few splits.
+void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_out,
+                  int& kps_out) {
+    const int rpb = lse_rows_per_block(path, lse_dp, (int)n_rows);
+    const int64_t R = (n_rows + rpb - 1) / rpb;
+    const int slots = path == PATH_VALU ? 1024 : 256;
+    const int tile = path == PATH_VALU ? 16 : kKeyTile;
+    const int64_t min_keys = path == PATH_VALU ? 1024 : 256;
+    int bestS = 1;
+    int64_t bestK = (n_keys + tile - 1) / tile * tile;
+    double best = -1.0;
+    for (int S = 1; S <= 64; ++S) {
+        int64_t kps = ((n_keys + S - 1) / S + tile - 1) / tile * tile;
+        if (S > 1 && kps < min_keys) break;
+        const int64_t Se = (n_keys + kps - 1) / kps;
+        if (Se != S) continue;
+        const int64_t blocks = R * Se;
+        const int64_t rounds = (blocks + slots - 1) / slots;
+        const double eff = (double)blocks / (double)(rounds * slots);
+        const double score = eff - 0.003 * (double)(Se - 1);
+        if (score > best + 1e-12) {
+            best = score;
+            bestS = (int)Se;
+            bestK = kps;
+        }
+    }
+    S_out = bestS;
+    kps_out = (int)bestK;
+}
+
+struct Layout {
+    size_t shift, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
+        vt, total;
+};
+
+Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = up(o + bytes, kAlign);
+        return at;
+    };
+    const int64_t np = pad_rows(n), mp = pad_rows(m);
+    L.shift = take(sizeof(float) * d);
+    L.bmin = take(sizeof(float) * 2 * kBboxParts * d);
+    L.bmax = take(sizeof(float) * 2 * kBboxParts * d);
+    L.flag = take(sizeof(int) * 4);
+    L.xops = take(sh.es * (size_t)np * sh.dp);
+    L.yops = take(sh.es * (size_t)mp * sh.dp);
+    L.xn = take(sizeof(float) * n);
+    L.xl = take(sizeof(float) * n);
+    L.xw = take(sizeof(float) * n);
+    L.yn = take(sizeof(float) * m);
+    L.yl = take(sizeof(float) * m);
+    L.yw = take(sizeof(float) * m);
+    const size_t part_elems = std::max((size_t)(sh.f_split > 1 ? sh.f_split * n : 0),
+                                       (size_t)(sh.g_split > 1 ? sh.g_split * m : 0));
+    L.part = take(sizeof(float2) * (part_elems > 0 ? part_elems : 1));
+    L.rpart = take(sizeof(float) * ((std::max(n, m) + 127) / 128 + 64));
+    L.scal = take(sizeof(float) * 8);
+    L.ptmp = take(sizeof(float) * std::max(n, m));
+    const bool vt = dv_max > 0 && sh.path != PATH_VALU;
+    L.vt = take(vt ? (size_t)2 * dv_max * mp : 0);
+    L.total = o;
+    return L;
+}
+
+fs_status plan(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec, Shape& sh,
+               Layout& L) {
+    fs_status st = choose_path(n, m, d, dv_max, prec, sh);
+    if (st != FS_OK) return st;
+    choose_split(sh.path, sh.lse_dp, n, m, sh.f_split, sh.f_kps);
+    choose_split(sh.path, sh.lse_dp, m, n, sh.g_split, sh.g_kps);
+    L = make_layout(n, m, d, dv_max, sh);
+    return FS_OK;
+}
+
+fs_status check_device(int* dev_out) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) return fail(FS_ERR_DEVICE, "no HIP device available");
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipDeviceProp_t prop;
+    if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess)
+        return hip_fail(e, "hipGetDeviceProperties");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(FS_ERR_DEVICE, "device %d is %s; this library is built for gfx950 only", dev,
+                    prop.gcnArchName);
+    *dev_out = dev;
+    return FS_OK;
+}
+
+bool finite_pos(float v) { return std::isfinite(v) && v > 0.f; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = (const char*)a;
+    const char* y = (const char*)b;
+    return x < y + nb && y < x + na;
+}
+
+LseArgs base_args(const fs_problem* p, bool f_side, float eps) {
+    LseArgs a{};
+    const Cloud& R = f_side ? p->X : p->Y;
+    const Cloud& K = f_side ? p->Y : p->X;
+    a.rows = R.ops;
+    a.row_nrm = R.nrm;
+    a.row_w = R.w;
+    a.keys = K.ops;
+    a.key_nrm = K.nrm;
+    a.key_lw2 = K.lw2;
+    a.n_rows = (int)R.n;
+    a.n_keys = (int)K.n;
+    a.dp = p->lse_dp;
+    const double e = (double)eps;
+    a.c_bias = (float)(1.4426950408889634 / e);
+    a.c_score = (float)(2.8853900817779268 / e);
+    a.out_scale = (float)(-e * 0.6931471805599453);
+    a.n_split = f_side ? p->f_split : p->g_split;
+    a.keys_per_split = f_side ? p->f_kps : p->g_kps;
+    a.part = p->part;
+    a.resid_part = p->resid_part;
+    return a;
+}
+
+// One half-step: out = update(other potential); optional residual of (cur, other).
+fs_status half_step(fs_problem* p, bool f_side, float eps, const float* other, float* out,
+                    const float* cur, float* resid, int mode, hipStream_t s) {
+    LseArgs a = base_args(p, f_side, eps);
+    a.key_pot = other;
+    a.out = out;
+    a.mode = mode;
+    a.cur = cur;
+    a.resid_out = resid;
+    hipError_t e = launch_lse(p->path, a, s);
+    if (e != hipSuccess) return hip_fail(e, f_side ? "f-update launch" : "g-update launch");
+    return FS_OK;
+}
+
+bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fs_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec) {
+    Shape sh;
+    Layout L;
+    if (plan(n, m, d, dv_max, prec, sh, L) != FS_OK) return 0;
+    return L.total;
+}
+
+fs_status fs_potentials_init(const float* X, const float* Y, const float* a, const float* b,
+                             int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec,
+                             void* workspace, size_t workspace_bytes, float* f, float* g,
+                             void* stream, fs_problem** out) {
+    if (!out) return fail(FS_ERR_INVALID_ARG, "out handle pointer is NULL");
+    *out = nullptr;
+    if (!X || !Y || !a || !b) return fail(FS_ERR_INVALID_ARG, "X, Y, a and b must be non-NULL");
+    Shape sh;
+    Layout L;
+    fs_status st = plan(n, m, d, dv_max, prec, sh, L);
+    if (st != FS_OK) return st;
+    if (!workspace) return fail(FS_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace % kAlign)
+        return fail(FS_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    if (workspace_bytes < L.total)
+        return fail(FS_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    L.total);
+    int dev = 0;
+    if ((st = check_device(&dev)) != FS_OK) return st;
+
+    fs_problem* p = new (std::nothrow) fs_problem();
+    if (!p) return fail(FS_ERR_DEVICE, "host allocation failed");
+    char* w = (char*)workspace;
+    p->device = dev;
+    p->path = sh.path;
+    p->n = n;
+    p->m = m;
+    p->d = d;
+    p->dp = sh.dp;
+    p->lse_dp = sh.lse_dp;
+    p->dv_max = dv_max;
+    p->f_split = sh.f_split;
+    p->f_kps = sh.f_kps;
+    p->g_split = sh.g_split;
+    p->g_kps = sh.g_kps;
+    p->shift = (float*)(w + L.shift);
+    p->bbox_min = (float*)(w + L.bmin);
+    p->bbox_max = (float*)(w + L.bmax);
+    p->flag = (int*)(w + L.flag);
+    p->X = Cloud{w + L.xops, (float*)(w + L.xn), (float*)(w + L.xl), (float*)(w + L.xw), n,
+                 pad_rows(n)};
+    p->Y = Cloud{w + L.yops, (float*)(w + L.yn), (float*)(w + L.yl), (float*)(w + L.yw), m,
+                 pad_rows(m)};
+    p->part = (float2*)(w + L.part);
+    p->resid_part = (float*)(w + L.rpart);
+    p->scal = (float*)(w + L.scal);
+    p->pot_tmp = (float*)(w + L.ptmp);
+    p->vt = (dv_max > 0 && sh.path != PATH_VALU) ? (void*)(w + L.vt) : nullptr;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = launch_zero_flag(p->flag, s)) != hipSuccess) goto hip_error;
+    if ((e = launch_bbox(X, n, Y, m, d, p->bbox_min, p->bbox_max, kBboxParts, p->shift, s)) !=
+        hipSuccess)
+        goto hip_error;
+    if ((e = launch_convert(X, n, p->X.n_pad, d, p->dp, p->path, p->shift, p->X.ops, p->X.nrm,
+                            p->flag, s)) != hipSuccess)
+        goto hip_error;
+    if ((e = launch_convert(Y, m, p->Y.n_pad, d, p->dp, p->path, p->shift, p->Y.ops, p->Y.nrm,
+                            p->flag, s)) != hipSuccess)
+        goto hip_error;
+    if ((e = launch_weights(a, n, p->X.lw2, p->X.w, f, p->flag, s)) != hipSuccess) goto hip_error;
+    if ((e = launch_weights(b, m, p->Y.lw2, p->Y.w, g, p->flag, s)) != hipSuccess) goto hip_error;
+    {
+        int flag = 0;
+        if ((e = hipMemcpyAsync(&flag, p->flag, sizeof(int), hipMemcpyDeviceToHost, s)) !=
+            hipSuccess)
+            goto hip_error;
+        if ((e = hipStreamSynchronize(s)) != hipSuccess) goto hip_error;
+        if (flag) {
+            delete p;
+            if (flag & 1) return fail(FS_ERR_NONFINITE, "X or Y holds a NaN or Inf");
+            if (flag & 2) return fail(FS_ERR_NONFINITE, "a weight is <= 0, subnormal, NaN or Inf");
+            return fail(FS_ERR_INVALID_ARG,
+                        "a shifted coordinate overflows the fp16 range; scale the points "
+                        "(and eps by the square of the scale) or use FS_PREC_BF16");
+        }
+    }
+    *out = p;
+    return FS_OK;
+hip_error:
+    delete p;
+    return hip_fail(e, "fs_potentials_init");
+}
+
+fs_status fs_lse_update_f(fs_problem* p, float eps, const float* g, float* f_out,
+                          const float* f_cur, float* row_resid, void* stream) {
+    if (!p || !g || !f_out) return fail(FS_ERR_INVALID_ARG, "NULL handle, g or f_out");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (row_resid && !f_cur) return fail(FS_ERR_INVALID_ARG, "row_resid needs f_cur");
+    if (row_resid && overlaps(f_out, 4 * p->n, f_cur, 4 * p->n))
+        return fail(FS_ERR_INVALID_ARG, "f_out may not overlap f_cur when a residual is asked");
+    if (overlaps(f_out, 4 * p->n, g, 4 * p->m))
+        return fail(FS_ERR_INVALID_ARG, "f_out overlaps g");
+    return half_step(p, true, eps, g, f_out, row_resid ? f_cur : nullptr, row_resid, 0,
+                     (hipStream_t)stream);
+}
+
+fs_status fs_lse_update_g(fs_problem* p, float eps, const float* f, float* g_out,
+                          const float* g_cur, float* col_resid, void* stream) {
+    if (!p || !f || !g_out) return fail(FS_ERR_INVALID_ARG, "NULL handle, f or g_out");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (col_resid && !g_cur) return fail(FS_ERR_INVALID_ARG, "col_resid needs g_cur");
+    if (col_resid && overlaps(g_out, 4 * p->m, g_cur, 4 * p->m))
+        return fail(FS_ERR_INVALID_ARG, "g_out may not overlap g_cur when a residual is asked");
+    if (overlaps(g_out, 4 * p->m, f, 4 * p->n))
+        return fail(FS_ERR_INVALID_ARG, "g_out overlaps f");
+    return half_step(p, false, eps, f, g_out, col_resid ? g_cur : nullptr, col_resid, 0,
+                     (hipStream_t)stream);
+}
+
+fs_status fs_marginal_residual(fs_problem* p, float eps, const float* f, const float* g,
+                               float* out2, void* stream) {
+    if (!p || !f || !g || !out2) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    hipStream_t s = (hipStream_t)stream;
+    fs_status st = half_step(p, true, eps, g, p->pot_tmp, f, out2, 0, s);
+    if (st != FS_OK) return st;
+    return half_step(p, false, eps, f, p->pot_tmp, g, out2 + 1, 0, s);
+}
+
+fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, float* g,
+                            fs_solve_info* info, void* stream) {
+    if (!p || !o || !f || !g) return fail(FS_ERR_INVALID_ARG, "NULL handle, opts, f or g");
+    if (o->n_stages < 1) return fail(FS_ERR_INVALID_ARG, "n_stages must be >= 1");
+    if (o->iters_per_stage < 0) return fail(FS_ERR_INVALID_ARG, "iters_per_stage must be >= 0");
+    if (!eps_ok(o->eps_end) || (o->n_stages > 1 && !eps_ok(o->eps_start)))
+        return fail(FS_ERR_INVALID_ARG, "eps_start/eps_end must be finite and > 0");
+    if (!std::isfinite(o->tol)) return fail(FS_ERR_INVALID_ARG, "tol must be finite");
+    if (o->tol > 0.f && o->check_every < 1)
+        return fail(FS_ERR_INVALID_ARG, "check_every must be >= 1 when tol > 0");
+    if (overlaps(f, 4 * p->n, g, 4 * p->m)) return fail(FS_ERR_INVALID_ARG, "f overlaps g");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (!o->warm_start) {
+        if ((e = launch_fill(g, p->m, 0.f, s)) != hipSuccess) return hip_fail(e, "fill g");
+        if ((e = launch_fill(f, p->n, 0.f, s)) != hipSuccess) return hip_fail(e, "fill f");
+    }
+    const bool use_tol = o->tol > 0.f;
+    int done = 0;
+    float resid = -1.f;
+    float eps = o->eps_end;
+    bool converged = false;
+    bool have_next_f = false;  // pot_tmp already holds the next f-update (same eps)
+    fs_status st;
+    auto check = [&](float eps_c, bool& reusable_next) -> fs_status {
+        // Row term of the residual of (f, g) via a dry-run f-update into
+        // pot_tmp; the column term is identically zero after a g-update (the
+        // stored g is exactly the g-update of f, and the pass is deterministic).
+        fs_status s2 = half_step(p, true, eps_c, g, p->pot_tmp, f, p->scal, 0, s);
+        if (s2 != FS_OK) return s2;
+        float h = 0.f;
+        hipError_t e2 = hipMemcpyAsync(&h, p->scal, sizeof(float), hipMemcpyDeviceToHost, s);
+        if (e2 == hipSuccess) e2 = hipStreamSynchronize(s);
+        if (e2 != hipSuccess) return hip_fail(e2, "residual readback");
+        resid = h;
+        reusable_next = true;
+        return FS_OK;
+    };
+    for (int st_i = 0; st_i < o->n_stages && !converged; ++st_i) {
+        if (o->n_stages == 1)
+            eps = o->eps_end;
+        else
+            eps = (float)((double)o->eps_start *
+                          std::pow((double)o->eps_end / (double)o->eps_start,
+                                   (double)st_i / (double)(o->n_stages - 1)));
+        if (have_next_f) have_next_f = false;  // new stage: eps changed
+        for (int it = 0; it < o->iters_per_stage; ++it) {
+            if (have_next_f) {
+                if ((e = hipMemcpyAsync(f, p->pot_tmp, sizeof(float) * p->n,
+                                        hipMemcpyDeviceToDevice, s)) != hipSuccess)
+                    return hip_fail(e, "copy f");
+                have_next_f = false;
+            } else if ((st = half_step(p, true, eps, g, f, nullptr, nullptr, 0, s)) != FS_OK) {
+                return st;
+            }
+            if ((st = half_step(p, false, eps, f, g, nullptr, nullptr, 0, s)) != FS_OK) return st;
+            ++done;
+            if (use_tol && done % o->check_every == 0) {
+                bool reusable = false;
+                if ((st = check(eps, reusable)) != FS_OK) return st;
+                if (resid <= o->tol) {
+                    converged = true;
+                    break;
+                }
+                have_next_f = reusable;
+            }
+        }
+    }
+    if (use_tol && !converged && (done == 0 || done % o->check_every != 0)) {
+        bool dummy = false;
+        if ((st = check(eps, dummy)) != FS_OK) return st;
+        converged = resid <= o->tol;
+    }
+    if (info) {
+        info->iters_done = done;
+        info->final_eps = eps;
+        info->residual = use_tol ? resid : -1.f;
+    }
+    if (use_tol && !converged)
+        return fail(FS_ERR_NOT_CONVERGED, "residual %g above tol %g after %d iterations",
+                    (double)resid, (double)o->tol, done);
+    return FS_OK;
+}
+
+fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const float* g,
+                             const float* V, int32_t dv, float* U, int32_t divide_by_a,
+                             void* stream) {
+    if (!p || !f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (dv < 1 || dv > p->dv_max)
+        return fail(FS_ERR_INVALID_ARG, "dv must be in [1, dv_max=%d] (got %d)", p->dv_max, dv);
+    if (overlaps(U, (size_t)4 * p->n * dv, V, (size_t)4 * p->m * dv))
+        return fail(FS_ERR_INVALID_ARG, "U overlaps V");
+    hipStream_t s = (hipStream_t)stream;
+    // Exact row LSE (base 2) of the f-update scores under g.
+    fs_status st = half_step(p, true, eps, g, p->pot_tmp, nullptr, nullptr, 1, s);
+    if (st != FS_OK) return st;
+    TransportArgs t{};
+    t.rows = p->X.ops;
+    t.row_lse2 = p->pot_tmp;
+    t.row_pot = f;
+    t.row_nrm = p->X.nrm;
+    t.row_w = p->X.w;
+    t.keys = p->Y.ops;
+    t.key_pot = g;
+    t.key_nrm = p->Y.nrm;
+    t.key_lw2 = p->Y.lw2;
+    t.V = V;
+    t.Vt = p->vt;
+    t.v_unscale_dev = nullptr;
+    t.n_rows = (int)p->n;
+    t.n_keys = (int)p->m;
+    t.dp = p->lse_dp;
+    t.dv = dv;
+    t.c_bias = (float)(1.4426950408889634 / (double)eps);
+    t.c_score = (float)(2.8853900817779268 / (double)eps);
+    t.divide_by_a = divide_by_a ? 1 : 0;
+    t.U = U;
+    hipError_t e = launch_transport(p->path, t, p->scal + 2, p->vt, p->Y.n_pad, s);
+    if (e != hipSuccess) return hip_fail(e, "transport launch");
+    return FS_OK;
+}
+
+void fs_destroy(fs_problem* p) { delete p; }
+
+const char* fs_status_string(fs_status s) {
+    switch (s) {
+        case FS_OK: return "FS_OK";
+        case FS_ERR_INVALID_ARG: return "FS_ERR_INVALID_ARG";
+        case FS_ERR_WORKSPACE: return "FS_ERR_WORKSPACE";
+        case FS_ERR_DEVICE: return "FS_ERR_DEVICE";
+        case FS_ERR_NONFINITE: return "FS_ERR_NONFINITE";
+        case FS_ERR_NOT_CONVERGED: return "FS_ERR_NOT_CONVERGED";
+    }
+    return "FS_ERR_UNKNOWN";
+}
+
+const char* fs_last_error(void) { return g_err.c_str(); }
+
+fs_status fs_problem_info(const fs_problem* p, int32_t* path, int32_t* d_pad, int32_t* f_splits,
+                          int32_t* g_splits) {
+    if (!p) return fail(FS_ERR_INVALID_ARG, "NULL handle");
+    if (path) *path = p->path;
+    if (d_pad) *d_pad = p->dp;
+    if (f_splits) *f_splits = p->f_split;
+    if (g_splits) *g_splits = p->g_split;
+    return FS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// fs_internal.h -- declarations shared by the host library and the kernel
+// translation units (launchers and their argument blocks).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fs {
+
+// Score path of a problem.
+enum Path : int { PATH_VALU = 0, PATH_MFMA_F32 = 1, PATH_MFMA_BF16 = 2, PATH_MFMA_F16 = 3 };
+
+// Rows per workgroup of the matrix-core kernels is 4 waves x 32 x qb; clouds are
+// padded to a multiple of this so no kernel ever reads past an operand.
+constexpr int kRowPad = 512;
+// Keys per streamed tile (one 32-row MFMA operand block).
+constexpr int kKeyTile = 32;
+
+// One side of the problem, stored in the caller's workspace.
+struct Cloud {
+    void* ops;      // shifted, converted points [n_pad][dp] (fp32 / bf16 / fp16), zero padded
+    float* nrm;     // |p~|^2 from the converted points [n]
+    float* lw2;     // log2 of the weights [n]
+    float* w;       // copy of the weights [n]
+    int64_t n;
+    int64_t n_pad;
+};
+
+// Arguments of one streaming log-sum-exp pass ("half-step"): for every row
+// point p_i of one cloud, LSE2_i = log2 sum_j 2^(z2_ij) with
+//   z2_ij = c_score * (p~_i . q~_j) + beta_j,
+//   beta_j = (pot_j - |q~_j|^2) * c_bias + log2 w_j,
+// over the key points q_j of the other cloud.  Outputs (finalize stage):
+//   mode 0: out_i = out_scale * LSE2_i + |p~_i|^2      (the new potential)
+//   mode 1: out_i = LSE2_i
+// and, if cur != nullptr, the residual sum_i w_i |2^((cur_i - out_i) c_bias) - 1|.
+struct LseArgs {
+    const void* rows;
+    const float* row_nrm;
+    const float* row_w;
+    const void* keys;
+    const float* key_pot;
+    const float* key_nrm;
+    const float* key_lw2;
+    int n_rows;
+    int n_keys;
+    int dp;
+    float c_bias;     // log2(e) / eps
+    float c_score;    // 2 log2(e) / eps
+    float out_scale;  // -eps ln 2
+    int n_split;      // key-range splits (1: finalize in the streaming kernel)
+    int keys_per_split;
+    float2* part;     // [n_split][n_rows] partial (M, s) when n_split > 1
+    int mode;
+    float* out;
+    const float* cur;
+    float* resid_part;  // one partial per finalizing block
+    float* resid_out;   // 1 float
+};
+
+// Arguments of the transport application U = P.V (or P.V / a).
+struct TransportArgs {
+    const void* rows;        // X~ [n_pad][dp]
+    const float* row_lse2;   // exact LSE2 of each row under the current g
+    const float* row_pot;    // f
+    const float* row_nrm;    // |x~|^2
+    const float* row_w;      // a
+    const void* keys;        // Y~ [m_pad][dp]
+    const float* key_pot;    // g
+    const float* key_nrm;    // |y~|^2
+    const float* key_lw2;    // log2 b
+    const float* V;          // fp32 [m][dv] (vector path)
+    const void* Vt;          // f16 [dv][m_pad] scaled copy (matrix path)
+    const float* v_unscale_dev;  // device float 2^-s undoing the copy's scaling
+    int n_rows, n_keys, dp, dv;
+    float c_bias, c_score;
+    int divide_by_a;
+    float* U;                // [n][dv]
+};
+
+// ---- launchers (each returns the first HIP error, enqueues on `s`) ----
+hipError_t launch_zero_flag(int* flag, hipStream_t s);
+hipError_t launch_bbox(const float* X, int64_t n, const float* Y, int64_t m, int d,
+                       float* part_min, float* part_max, int parts_per_cloud, float* shift,
+                       hipStream_t s);
+hipError_t launch_convert(const float* P, int64_t n, int64_t n_pad, int d, int dp, int path,
+                          const float* shift, void* ops, float* nrm, int* flag, hipStream_t s);
+hipError_t launch_weights(const float* w, int64_t n, float* lw2, float* wcopy, float* pot,
+                          int* flag, hipStream_t s);
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+
+// Streaming LSE pass (+ merge when split).  `path` selects the kernel family,
+// `dp` the padded dimension.
+hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s);
+// Rows handled by one workgroup of the streaming kernel (path, dp as passed
+// in LseArgs, rows of the pass).
+int lse_rows_per_block(int path, int dp, int n_rows);
+
+// Transport: V -> f16 transposed scaled copy, then the streaming product.
+hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratch,
+                            void* Vt_buf, int64_t m_pad, hipStream_t s);
+
+}  // namespace fs

@@ -1,0 +1,229 @@
+"""GPU parity: the HIP solver against the float64 oracle, same seeded inputs,
+same fixed iteration count, element by element.
+
+Tolerances (on every potential entry, after the same number of iterations):
+  fp32 score paths       max|f - f_ref|, max|g - g_ref| <= 1e-3 eps
+  bf16/fp16 score paths  <= 2e-2 eps against the oracle on the original
+                         points, and <= 2e-3 eps against the oracle run on the
+                         rounded points the path actually uses (isolates
+                         kernel error from quantisation)
+  transport              ||U - U_ref||_F / ||U_ref||_F <= 1e-3
+Sizes span several tiles and splits with ragged tails; the oracle finishes
+each case in seconds.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import dev, gpu_solve, host, max_err, oracle_solve, rounded_operands
+from streaming_sinkhorn_solver_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_FP32 = 1e-3
+TOL_LOWP = 2e-2
+TOL_LOWP_ROUNDED = 2e-3
+
+
+def _problem(seed, n, m, d, weights="exp", scale=1.0):
+    w = workloads.random_cloud(seed, n, m, d, weights=weights, scale=scale)
+    return w.X, w.Y, w.a, w.b
+
+
+def test_c1_full_against_stored_oracle(fs):
+    import os
+
+    w = workloads.make("c1")
+    _, f, g, _, _ = gpu_solve(w.X, w.Y, w.a, w.b, eps=w.eps, iters=w.iters)
+    gold = os.path.join(os.path.dirname(__file__), "golden")
+    f_ref = np.loadtxt(os.path.join(gold, "c1_oracle_f_iter100.txt"))
+    g_ref = np.loadtxt(os.path.join(gold, "c1_oracle_g_iter100.txt"))
+    assert max_err(host(f), f_ref) <= TOL_FP32 * w.eps
+    assert max_err(host(g), g_ref) <= TOL_FP32 * w.eps
+
+
+@pytest.mark.parametrize("d", [1, 2, 3, 4, 5, 8])
+def test_valu_path_ragged(fs, d):
+    X, Y, a, b = _problem(100 + d, 1000 + 37 * d, 777, d)
+    eps = 0.2
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=15)
+    assert p.info["path"] == "fp32-valu"
+    ref = oracle_solve(X, Y, a, b, eps=eps, iters=15)
+    assert max_err(host(f), ref["f"]) <= TOL_FP32 * eps
+    assert max_err(host(g), ref["g"]) <= TOL_FP32 * eps
+
+
+@pytest.mark.parametrize("d,n,m", [(9, 700, 1100), (16, 1500, 900), (64, 2100, 1700),
+                                   (100, 600, 1300), (256, 640, 500)])
+def test_fp32_mfma_path(fs, d, n, m):
+    X, Y, a, b = _problem(200 + d, n, m, d, scale=1.0 / np.sqrt(d))
+    eps = 0.05
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=12)
+    assert p.info["path"] == "fp32-mfma"
+    ref = oracle_solve(X, Y, a, b, eps=eps, iters=12)
+    assert max_err(host(f), ref["f"]) <= TOL_FP32 * eps
+    assert max_err(host(g), ref["g"]) <= TOL_FP32 * eps
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp16"])
+@pytest.mark.parametrize("d,n,m", [(16, 900, 1300), (64, 1200, 1000), (200, 700, 650),
+                                   (512, 1000, 900), (1024, 500, 700)])
+def test_lowp_mfma_path(fs, prec, d, n, m):
+    # The 50k x 50k, 512-D recipe's distribution (two 10-component Gaussian
+    # mixtures, Dirichlet weights, eps 0.1) at small sizes and several d.
+    w = workloads.make("c3", n=n, m=m, d=d)
+    X, Y, a, b, eps = w.X, w.Y, w.a, w.b, w.eps
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=10, prec=prec)
+    assert p.info["path"] == f"{prec}-mfma"
+    Xr, Yr = rounded_operands(X, Y, prec)
+    rr = oracle_solve(Xr, Yr, a, b, eps=eps, iters=10)
+    assert max_err(host(f), rr["f"]) <= TOL_LOWP_ROUNDED * eps
+    assert max_err(host(g), rr["g"]) <= TOL_LOWP_ROUNDED * eps
+    if prec == "bf16" and d < 200:
+        # bf16 keeps 8 significant bits: at d < ~200 on this distribution the
+        # rounding of the points alone moves f by more than 2e-2 eps (the
+        # rounded-point check above is the kernel's parity check).
+        return
+    ref = oracle_solve(X, Y, a, b, eps=eps, iters=10)
+    assert max_err(host(f), ref["f"]) <= TOL_LOWP * eps
+    assert max_err(host(g), ref["g"]) <= TOL_LOWP * eps
+
+
+def test_split_path_is_exercised(fs):
+    # Sizes for which the launch heuristic splits the key range.
+    X, Y, a, b = _problem(400, 4000, 3000, 64, scale=0.125)
+    eps = 0.05
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=5)
+    info = p.info
+    assert info["f_splits"] > 1 and info["g_splits"] > 1, info
+    ref = oracle_solve(X, Y, a, b, eps=eps, iters=5)
+    assert max_err(host(f), ref["f"]) <= TOL_FP32 * eps
+    assert max_err(host(g), ref["g"]) <= TOL_FP32 * eps
+
+
+def test_residual_matches_oracle(fs):
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    X, Y, a, b = _problem(500, 900, 1100, 3)
+    eps = 0.3
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=7)
+    out2 = torch.zeros(2, dtype=torch.float32, device="cuda")
+    binding.fs_marginal_residual(p, eps, f, g, out2)
+    torch.cuda.synchronize()
+    tot, rt, ct = oracle.marginal_residual(X, Y, a, b, host(f), host(g), eps)
+    r = out2.cpu().numpy()
+    assert abs(r[0] - rt) <= 1e-3 * max(rt, 1e-6) + 1e-6
+    assert abs(r[1] - ct) <= 1e-5
+
+
+def test_power_of_two_scaling_bit_exact(fs):
+    for prec, d in (("auto", 3), ("auto", 32), ("bf16", 64)):
+        X, Y, a, b = _problem(600 + d, 800, 700, d)
+        eps = 0.25
+        _, f1, g1, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=6, prec=prec)
+        _, f2, g2, _, _ = gpu_solve(2 * X, 2 * Y, a, b, eps=4 * eps, iters=6, prec=prec)
+        np.testing.assert_array_equal(host(f2), 4 * host(f1))
+        np.testing.assert_array_equal(host(g2), 4 * host(g1))
+
+
+def test_row_permutation(fs):
+    X, Y, a, b = _problem(700, 1200, 900, 3)
+    perm = np.random.default_rng(701).permutation(1200)
+    eps = 0.2
+    _, f1, g1, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=5)
+    _, f2, g2, _, _ = gpu_solve(X[perm], Y, a[perm], b, eps=eps, iters=5)
+    assert max_err(host(f2), host(f1)[perm]) <= 1e-5 * eps
+    assert max_err(host(g2), host(g1)) <= 1e-5 * eps
+
+
+def test_deterministic_repeat(fs):
+    X, Y, a, b = _problem(800, 3000, 2500, 64, scale=0.125)
+    _, f1, g1, _, _ = gpu_solve(X, Y, a, b, eps=0.05, iters=4)
+    _, f2, g2, _, _ = gpu_solve(X, Y, a, b, eps=0.05, iters=4)
+    np.testing.assert_array_equal(host(f1), host(f2))
+    np.testing.assert_array_equal(host(g1), host(g2))
+
+
+@pytest.mark.parametrize("prec,d", [("auto", 3), ("auto", 64), ("bf16", 512), ("fp16", 256)])
+def test_transport(fs, prec, d):
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    X, Y, a, b = _problem(900 + d, 700, 850, d, scale=1.0 / np.sqrt(d))
+    rng = np.random.default_rng(901)
+    V = rng.standard_normal((850, 70)).astype(np.float32)
+    eps = 0.1
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=8, prec=prec, dv_max=128)
+    Vd = dev(V)
+    U = torch.empty((700, 70), dtype=torch.float32, device="cuda")
+    T = torch.empty((700, 70), dtype=torch.float32, device="cuda")
+    binding.fs_apply_transport(p, eps, f, g, Vd, U, divide_by_a=False)
+    binding.fs_apply_transport(p, eps, f, g, Vd, T, divide_by_a=True)
+    torch.cuda.synchronize()
+    if prec in ("bf16", "fp16"):
+        Xr, Yr = rounded_operands(X, Y, prec)
+    else:
+        Xr, Yr = X, Y
+    U_ref = oracle.transport(Xr, Yr, a, b, host(f), host(g), V, eps)
+    T_ref = oracle.transport(Xr, Yr, a, b, host(f), host(g), V, eps, divide_by_a=True)
+    for got, ref in ((host(U), U_ref), (host(T), T_ref)):
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert rel <= 1e-3, rel
+
+
+def test_tol_stop_and_annealing(fs):
+    # The annealed 1024-D recipe (eps 1 -> 0.01) at a small size, fp16 scores.
+    w = workloads.make("c4", n=600, m=500)
+    _, f, g, info, _ = gpu_solve(w.X, w.Y, w.a, w.b, eps=w.eps, eps_start=w.eps_start,
+                                 n_stages=4, iters=6, prec="fp16")
+    assert info["iters_done"] == 24
+    Xr, Yr = rounded_operands(w.X, w.Y, "fp16")
+    rr = oracle_solve(Xr, Yr, w.a, w.b, eps=w.eps, eps_start=w.eps_start, n_stages=4, iters=6)
+    assert max_err(host(f), rr["f"]) <= TOL_LOWP_ROUNDED * w.eps
+    assert max_err(host(g), rr["g"]) <= TOL_LOWP_ROUNDED * w.eps
+    ref = oracle_solve(w.X, w.Y, w.a, w.b, eps=w.eps, eps_start=w.eps_start, n_stages=4, iters=6)
+    assert max_err(host(f), ref["f"]) <= TOL_LOWP * w.eps
+    assert max_err(host(g), ref["g"]) <= TOL_LOWP * w.eps
+    # tolerance stop
+    X, Y, a, b = _problem(1000, 500, 400, 3)
+    _, f, g, info, _ = gpu_solve(X, Y, a, b, eps=0.5, iters=2000, tol=1e-4, check_every=5)
+    assert info["status"] == 0 and 0 < info["iters_done"] < 2000
+    assert info["iters_done"] % 5 == 0
+    tot, _, _ = oracle.marginal_residual(X, Y, a, b, host(f), host(g), 0.5)
+    assert tot <= 2e-4
+    # unreachable tolerance: NOT_CONVERGED with valid outputs
+    _, f, g, info, _ = gpu_solve(X, Y, a, b, eps=0.5, iters=3, tol=1e-12, check_every=2)
+    assert info["status"] == 5 and info["iters_done"] == 3
+    assert np.all(np.isfinite(host(f)))
+
+
+def test_error_paths(fs):
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    X, Y, a, b = _problem(1100, 64, 48, 3)
+    Xb = X.copy()
+    Xb[5, 1] = np.nan
+    with pytest.raises(binding.FsError) as e:
+        binding.fs_potentials_init(dev(Xb), dev(Y), dev(a), dev(b))
+    assert e.value.status == binding.FS_ERR_NONFINITE
+    a0 = a.copy()
+    a0[3] = 0.0
+    with pytest.raises(binding.FsError) as e:
+        binding.fs_potentials_init(dev(X), dev(Y), dev(a0), dev(b))
+    assert e.value.status == binding.FS_ERR_NONFINITE
+    small = torch.empty(128, dtype=torch.uint8, device="cuda")
+    with pytest.raises(binding.FsError) as e:
+        binding.fs_potentials_init(dev(X), dev(Y), dev(a), dev(b), workspace=small)
+    assert e.value.status == binding.FS_ERR_WORKSPACE
+    p = binding.fs_potentials_init(dev(X), dev(Y), dev(a), dev(b))
+    f = torch.zeros(64, device="cuda")
+    g = torch.zeros(48, device="cuda")
+    with pytest.raises(binding.FsError) as e:
+        binding.fs_lse_update_f(p, -1.0, g, f)
+    assert e.value.status == binding.FS_ERR_INVALID_ARG
+    r = torch.zeros(1, device="cuda")
+    with pytest.raises(binding.FsError) as e:
+        binding.fs_lse_update_f(p, 0.1, g, f, f_cur=f, row_resid=r)
+    assert e.value.status == binding.FS_ERR_INVALID_ARG
