@@ -88,6 +88,8 @@ typedef struct {
     float tol;               /* <= 0: fixed iteration count, never synchronises */
     int32_t check_every;     /* >= 1 when tol > 0 */
     int32_t warm_start;
+    int32_t time_kernels;    /* != 0: time every streaming LSE kernel launch with HIP
+                                events on `stream` (synchronises once at the end) */
 } fs_solve_opts;
 
 /* Filled on the host by fs_sinkhorn_solve (synchronises at the end when tol > 0). */
@@ -95,6 +97,9 @@ typedef struct {
     int32_t iters_done;
     float final_eps;
     float residual;          /* last evaluated residual; -1 if none was evaluated */
+    int32_t lse_launches;    /* time_kernels: number of streaming LSE kernels timed */
+    float lse_ms;            /* time_kernels: their summed duration in milliseconds
+                                (the split-merge pass, when any, is not included) */
 } fs_solve_info;
 
 /* Bytes of workspace needed for a problem of this shape.  dv_max bounds the

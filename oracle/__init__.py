@@ -28,10 +28,11 @@ _I64 = ctypes.POINTER(ctypes.c_int64)
 _I32 = ctypes.POINTER(ctypes.c_int32)
 
 
-def build(force: bool = False) -> str:
-    from . import build as _b  # noqa: WPS433 (local build helper)
+def compile_library(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (see oracle/build.py)."""
+    from .build import build as _build
 
-    return _b.build(force=force)
+    return _build(force=force)
 
 
 def _load():
@@ -39,7 +40,7 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        build()
+        compile_library()
     lib = ctypes.CDLL(LIB_PATH)
     lib.oracle_version.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int

@@ -31,19 +31,20 @@ _LIB = None
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libfs_sinkhorn.so")
+    return os.environ.get("FS_SINKHORN_LIB") or os.path.join(_HERE, "libfs_sinkhorn.so")
 
 
 class SolveOpts(ctypes.Structure):
     _fields_ = [("n_stages", ctypes.c_int32), ("eps_start", ctypes.c_float),
                 ("eps_end", ctypes.c_float), ("iters_per_stage", ctypes.c_int32),
                 ("tol", ctypes.c_float), ("check_every", ctypes.c_int32),
-                ("warm_start", ctypes.c_int32)]
+                ("warm_start", ctypes.c_int32), ("time_kernels", ctypes.c_int32)]
 
 
 class SolveInfo(ctypes.Structure):
     _fields_ = [("iters_done", ctypes.c_int32), ("final_eps", ctypes.c_float),
-                ("residual", ctypes.c_float)]
+                ("residual", ctypes.c_float), ("lse_launches", ctypes.c_int32),
+                ("lse_ms", ctypes.c_float)]
 
 
 class FsError(RuntimeError):
@@ -213,17 +214,18 @@ def fs_marginal_residual(p: Problem, eps: float, f, g, out2, stream=None):
 def fs_sinkhorn_solve(p: Problem, f, g, *, eps_end: float, iters_per_stage: int,
                       n_stages: int = 1, eps_start: Optional[float] = None, tol: float = 0.0,
                       check_every: int = 10, warm_start: bool = False, stream=None,
-                      raise_not_converged: bool = True) -> dict:
+                      raise_not_converged: bool = True, time_kernels: bool = False) -> dict:
     opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
                      float(eps_end), int(iters_per_stage), float(tol), int(check_every),
-                     int(bool(warm_start)))
+                     int(bool(warm_start)), int(bool(time_kernels)))
     info = SolveInfo()
     st = load().fs_sinkhorn_solve(p.handle, ctypes.byref(opts), _dev(f, "f", p.n),
                                   _dev(g, "g", p.m), ctypes.byref(info), _stream(stream))
     allow = () if raise_not_converged else (FS_ERR_NOT_CONVERGED,)
     _check(st, "fs_sinkhorn_solve", allow)
     return {"status": st, "iters_done": info.iters_done, "final_eps": info.final_eps,
-            "residual": info.residual}
+            "residual": info.residual, "lse_launches": info.lse_launches,
+            "lse_ms": info.lse_ms}
 
 
 def fs_apply_transport(p: Problem, eps: float, f, g, V, U, divide_by_a: bool = False,

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "fs_internal.h"
 #include "fs_sinkhorn.h"
@@ -248,16 +249,46 @@ LseArgs base_args(const fs_problem* p, bool f_side, float eps) {
     return a;
 }
 
+// Optional HIP-event timing of the streaming kernels of a solve.
+struct KernelTimer {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // begin/end pairs
+    size_t used = 0;
+    hipError_t reserve(size_t pairs) {
+        on = true;
+        ev.assign(2 * pairs, nullptr);
+        for (auto& e : ev) {
+            hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) return r;
+        }
+        return hipSuccess;
+    }
+    void next(hipEvent_t& b, hipEvent_t& e) {
+        b = e = nullptr;
+        if (!on || used + 2 > ev.size()) return;
+        b = ev[used];
+        e = ev[used + 1];
+        used += 2;
+    }
+    ~KernelTimer() {
+        for (auto& e : ev)
+            if (e) (void)hipEventDestroy(e);
+    }
+};
+
 // One half-step: out = update(other potential); optional residual of (cur, other).
 fs_status half_step(fs_problem* p, bool f_side, float eps, const float* other, float* out,
-                    const float* cur, float* resid, int mode, hipStream_t s) {
+                    const float* cur, float* resid, int mode, hipStream_t s,
+                    KernelTimer* timer = nullptr) {
     LseArgs a = base_args(p, f_side, eps);
     a.key_pot = other;
     a.out = out;
     a.mode = mode;
     a.cur = cur;
     a.resid_out = resid;
-    hipError_t e = launch_lse(p->path, a, s);
+    hipEvent_t eb = nullptr, ee = nullptr;
+    if (timer) timer->next(eb, ee);
+    hipError_t e = launch_lse(p->path, a, s, eb, ee);
     if (e != hipSuccess) return hip_fail(e, f_side ? "f-update launch" : "g-update launch");
     return FS_OK;
 }
@@ -409,6 +440,12 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
     if (overlaps(f, 4 * p->n, g, 4 * p->m)) return fail(FS_ERR_INVALID_ARG, "f overlaps g");
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    KernelTimer timer;
+    if (o->time_kernels) {
+        const size_t half_steps = 2 * (size_t)o->n_stages * (size_t)o->iters_per_stage + 8;
+        if ((e = timer.reserve(half_steps)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    KernelTimer* tp = o->time_kernels ? &timer : nullptr;
     if (!o->warm_start) {
         if ((e = launch_fill(g, p->m, 0.f, s)) != hipSuccess) return hip_fail(e, "fill g");
         if ((e = launch_fill(f, p->n, 0.f, s)) != hipSuccess) return hip_fail(e, "fill f");
@@ -448,10 +485,11 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
                                         hipMemcpyDeviceToDevice, s)) != hipSuccess)
                     return hip_fail(e, "copy f");
                 have_next_f = false;
-            } else if ((st = half_step(p, true, eps, g, f, nullptr, nullptr, 0, s)) != FS_OK) {
+            } else if ((st = half_step(p, true, eps, g, f, nullptr, nullptr, 0, s, tp)) != FS_OK) {
                 return st;
             }
-            if ((st = half_step(p, false, eps, f, g, nullptr, nullptr, 0, s)) != FS_OK) return st;
+            if ((st = half_step(p, false, eps, f, g, nullptr, nullptr, 0, s, tp)) != FS_OK)
+                return st;
             ++done;
             if (use_tol && done % o->check_every == 0) {
                 bool reusable = false;
@@ -469,10 +507,24 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
         if ((st = check(eps, dummy)) != FS_OK) return st;
         converged = resid <= o->tol;
     }
+    float lse_ms = 0.f;
+    int lse_n = 0;
+    if (tp) {
+        if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "timing sync");
+        for (size_t k = 0; k + 1 < timer.used; k += 2) {
+            float ms = 0.f;
+            if ((e = hipEventElapsedTime(&ms, timer.ev[k], timer.ev[k + 1])) != hipSuccess)
+                return hip_fail(e, "hipEventElapsedTime");
+            lse_ms += ms;
+            ++lse_n;
+        }
+    }
     if (info) {
         info->iters_done = done;
         info->final_eps = eps;
         info->residual = use_tol ? resid : -1.f;
+        info->lse_launches = lse_n;
+        info->lse_ms = lse_ms;
     }
     if (use_tol && !converged)
         return fail(FS_ERR_NOT_CONVERGED, "residual %g above tol %g after %d iterations",

@@ -91,7 +91,10 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
 // Streaming LSE pass (+ merge when split).  `path` selects the kernel family,
 // `dp` the padded dimension.
-hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s);
+// ev_begin/ev_end (may be null) are recorded on `s` right before and after
+// the streaming kernel (not around the merge).
+hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s, hipEvent_t ev_begin = nullptr,
+                      hipEvent_t ev_end = nullptr);
 // Rows handled by one workgroup of the streaming kernel (path, dp as passed
 // in LseArgs, rows of the pass).
 int lse_rows_per_block(int path, int dp, int n_rows);

@@ -127,6 +127,19 @@ __global__ __launch_bounds__(256) void lse_valu_kernel(LseArgs a) {
 }
 
 // ------------------------------------------------------ matrix-core path
+#ifndef FS_MFMA_WAVES
+#define FS_MFMA_WAVES 8
+#endif
+#ifndef FS_MFMA_QB_MAX
+#define FS_MFMA_QB_MAX 2
+#endif
+constexpr int kMfmaWaves = FS_MFMA_WAVES;  // waves per workgroup of the matrix-core kernel
+constexpr int kQbMax = FS_MFMA_QB_MAX;     // cap on 32-row blocks per wave
+#ifdef FS_NO_PINGPONG
+constexpr bool kPingPong = false;
+#else
+constexpr bool kPingPong = true;  // opposite MFMA/epilogue order in the two wave halves
+#endif
 template <int OP>
 __device__ __forceinline__ f32x16 mfma_step(const uint4& av, const uint4& bv, f32x16 acc) {
     if constexpr (OP == OP_BF16) {
@@ -149,26 +162,44 @@ __device__ __forceinline__ f32x16 mfma_step(const uint4& av, const uint4& bv, f3
 
 // OP: score element type.  NG: 16-byte chunk pairs per operand row (a row is
 // 2*NG chunks; dp = 16*NG for 2-byte types, 8*NG for fp32).  QB: 32-row
-// blocks per wave.
-template <int OP, int NG, int QB>
-__global__ __launch_bounds__(256, 1) void lse_mfma_kernel(LseArgs a) {
-    constexpr int CPR = 2 * NG;                    // 16-byte chunks per row
+// blocks per wave.  WAVES: waves per workgroup.
+//
+// Software pipeline over 32-key tiles, one barrier per tile; iteration t:
+//   (1) direct global->LDS loads (global_load_lds_dwordx4) of tile t+2 into
+//       the buffer tile t used, plus its 32 key biases into registers;
+//   (2) the MFMAs of tile t+1 (A operand read from LDS, B resident);
+//   (3) the online-LSE epilogue of tile t, independent of (2), so the
+//       scheduler can overlap it with the matrix instructions;
+//   (4) wait for this wave's loads, publish the biases, barrier.
+// Tiles are stored XOR-swizzled (chunk c of key m at m*CPR + (c ^ (m & 7)))
+// so that the 32 keys read by one MFMA operand fetch hit distinct banks.
+template <int OP, int NG, int QB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
+    constexpr int CPR = 2 * NG;                      // 16-byte chunks per row
     constexpr int ROW_BYTES = CPR * 16;
-    constexpr int TILE_CHUNKS = kKeyTile * CPR;    // chunks per key tile
-    constexpr int LOADS = (TILE_CHUNKS + 255) / 256;
-    constexpr int SWZ = CPR >= 8 ? 7 : CPR - 1;    // XOR swizzle of the chunk index
+    constexpr int TILE_CHUNKS = kKeyTile * CPR;      // chunks per key tile (>= 64)
+    constexpr int TILE_INSTR = TILE_CHUNKS / 64;     // wave-wide 1 KiB loads per tile
+    constexpr int INSTR_PER_WAVE = (TILE_INSTR + WAVES - 1) / WAVES;
+    // XOR swizzle over 16 chunk columns (256 bytes = one pass over 64 banks)
+#ifndef FS_SWZ_COLS
+#define FS_SWZ_COLS 16
+#endif
+    constexpr int SWZ = CPR >= FS_SWZ_COLS ? FS_SWZ_COLS - 1 : CPR - 1;
+    constexpr int JB = SWZ + 1 < 2 * NG ? (SWZ + 1) / 2 : NG;  // chunk-pair classes per batch
+    constexpr int KB = NG / JB;                                  // batches per row
 
-    __shared__ uint4 kbuf[2][TILE_CHUNKS];
-    __shared__ float bbuf[2][kKeyTile];
+    __shared__ __attribute__((aligned(16))) uint4 kbuf0[TILE_CHUNKS];
+    __shared__ __attribute__((aligned(16))) uint4 kbuf1[TILE_CHUNKS];
+    __shared__ __attribute__((aligned(16))) float bbuf[3][kKeyTile];
     __shared__ float red[16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int ln = lane & 31;  // row of the B block (a query row) / row of the A block (a key)
-    const int h = lane >> 5;   // lane half: which 8 of each 16 contraction slots
+    const int ln = lane & 31;  // query row of the B block / key row of the A block
+    const int h = lane >> 5;   // lane half: contraction slots 8h..8h+7 of each 16
 
-    const int row0 = blockIdx.x * (4 * 32 * QB) + wave * (32 * QB);
+    const int row0 = blockIdx.x * (WAVES * 32 * QB) + wave * (32 * QB);
     const int split = blockIdx.y;
 
     // Resident row block: lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln.
@@ -188,36 +219,30 @@ __global__ __launch_bounds__(256, 1) void lse_mfma_kernel(LseArgs a) {
     const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
     const char* __restrict__ keys = (const char*)a.keys;
 
-    uint4 stg[LOADS];
-    float bstg = 0.f;
-// Global -> registers: tile t of this split (32 consecutive key rows) and the
-// 32 key biases beta_j = (pot_j - |q~_j|^2) c_bias + log2 w_j (-inf past the end).
-#define FS_LOAD_TILE(t_)                                                                      \
-    do {                                                                                      \
-        const char* base_ = keys + (int64_t)(j0 + (t_) * kKeyTile) * ROW_BYTES;               \
-        _Pragma("unroll") for (int l = 0; l < LOADS; ++l) {                                   \
-            const int c = l * 256 + tid;                                                      \
-            if (TILE_CHUNKS % 256 == 0 || c < TILE_CHUNKS)                                    \
-                stg[l] = *(const uint4*)(base_ + c * 16);                                     \
-        }                                                                                     \
-        if (tid < kKeyTile) {                                                                 \
-            const int j = j0 + (t_) * kKeyTile + tid;                                         \
-            bstg = j < j1 ? fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j])         \
-                          : -INFINITY;                                                        \
-        }                                                                                     \
-    } while (0)
-// Registers -> LDS buffer buf_, chunk c of key m at m*CPR + (c ^ (m & SWZ)).
-#define FS_STORE_TILE(buf_)                                                                   \
-    do {                                                                                      \
-        _Pragma("unroll") for (int l = 0; l < LOADS; ++l) {                                   \
-            const int c = l * 256 + tid;                                                      \
-            if (TILE_CHUNKS % 256 == 0 || c < TILE_CHUNKS) {                                  \
-                const int m = c / CPR, cc = c % CPR;                                          \
-                kbuf[(buf_)][m * CPR + (cc ^ (m & SWZ))] = stg[l];                            \
-            }                                                                                 \
-        }                                                                                     \
-        if (tid < kKeyTile) bbuf[(buf_)][tid] = bstg;                                         \
-    } while (0)
+    // (1) tile k -> LDS buffer `dst` (64-chunk slice L of the tile per
+    // wave-instruction; lane `lane` fetches the chunk that lands at position
+    // L*64+lane of the swizzled layout).
+    auto issue_tile = [&](int k, uint4* dst) __attribute__((always_inline)) {
+        const char* tbase = keys + (int64_t)(j0 + k * kKeyTile) * ROW_BYTES;
+#pragma unroll
+        for (int l = 0; l < INSTR_PER_WAVE; ++l) {
+            const int L = l * WAVES + wave;
+            if (TILE_INSTR % WAVES == 0 || L < TILE_INSTR) {
+                const int P = L * 64 + lane;
+                const int m = P / CPR, cp = P % CPR;
+                const char* src = tbase + m * ROW_BYTES + (cp ^ (m & SWZ)) * 16;
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)src, (__attribute__((address_space(3))) void*)(dst + L * 64), 16, 0,
+                    0);
+            }
+        }
+    };
+    auto load_beta = [&](int k) __attribute__((always_inline)) -> float {
+        const int j = j0 + k * kKeyTile + tid;
+        float b = -INFINITY;
+        if (tid < kKeyTile && j < j1) b = fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]);
+        return b;
+    };
 
     float M[QB], S[QB];
 #pragma unroll
@@ -226,34 +251,49 @@ __global__ __launch_bounds__(256, 1) void lse_mfma_kernel(LseArgs a) {
         S[qb] = 0.f;
     }
 
-    FS_LOAD_TILE(0);
-    FS_STORE_TILE(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) FS_LOAD_TILE(t + 1);
-
-        f32x16 acc[QB];
+    // (2) scores of the tile in `src` for all QB row blocks.  Operand chunk
+    // 2g+h of key ln sits at ln*CPR + ((2g+h) ^ (ln & SWZ)); with g = JB*k + j
+    // that is a per-lane base for each j plus the immediate offset 2*JB*k
+    // chunks, so a batch of JB fragments is fetched before its MFMAs.
+    int abase[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) abase[j] = (ln * CPR + ((2 * j + h) ^ (ln & SWZ))) * 16;
+    auto mfma_tile = [&](const uint4* src, f32x16 (&acc)[QB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][r] = 0.f;
-
-        const uint4* kb = kbuf[buf] + ln * CPR;
+        const char* kb = (const char*)src;
+#if defined(FS_UNBATCHED)
+        const uint4* kbu = src + ln * CPR;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const uint4 av = kb[(2 * g + h) ^ (ln & SWZ)];
+            const uint4 av = kbu[(2 * g + h) ^ (ln & SWZ)];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma_step<OP>(av, q[qb][g], acc[qb]);
         }
-
-        // Epilogue.  Accumulator register r of lane (ln, h) is the score of row
-        // ln with key 8*(r/4) + 4*h + (r%4) of the tile.
+        (void)kb;
+#else
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            uint4 av[JB];
+#pragma unroll
+            for (int j = 0; j < JB; ++j) av[j] = *(const uint4*)(kb + abase[j] + k * (2 * JB * 16));
+#pragma unroll
+            for (int j = 0; j < JB; ++j)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    acc[qb] = mfma_step<OP>(av[j], q[qb][JB * k + j], acc[qb]);
+        }
+#endif
+    };
+    // (3) online LSE of one tile.  Accumulator register r of lane (ln, h) is
+    // the score of row ln with key 8*(r/4) + 4*h + (r%4) of the tile.
+    auto epilogue = [&](const f32x16 (&acc)[QB], const float* bb) __attribute__((always_inline)) {
         float bv[16];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-            const float4 v = *(const float4*)&bbuf[buf][8 * qq + 4 * h];
+            const float4 v = *(const float4*)&bb[8 * qq + 4 * h];
             bv[4 * qq + 0] = v.x;
             bv[4 * qq + 1] = v.y;
             bv[4 * qq + 2] = v.z;
@@ -264,9 +304,9 @@ __global__ __launch_bounds__(256, 1) void lse_mfma_kernel(LseArgs a) {
             float z[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) z[r] = fmaf(acc[qb][r], a.c_score, bv[r]);
-            float tmax = z[0];
+            float tmax = fmaxf(z[0], z[1]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
+            for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
             const float Mn = fmaxf(M[qb], tmax);
             float s = S[qb] * ex2(M[qb] - Mn);
 #pragma unroll
@@ -274,10 +314,63 @@ __global__ __launch_bounds__(256, 1) void lse_mfma_kernel(LseArgs a) {
             S[qb] = s;
             M[qb] = Mn;
         }
+    };
 
-        if (t + 1 < ntiles) FS_STORE_TILE(buf ^ 1);
-        __syncthreads();
+    // prologue: tiles 0 and 1 in flight, tile 0's scores computed
+    float bn0 = 0.f, bn1 = 0.f;
+    issue_tile(0, kbuf0);
+    bn0 = load_beta(0);
+    if (ntiles > 1) {
+        issue_tile(1, kbuf1);
+        bn1 = load_beta(1);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid < kKeyTile) {
+        bbuf[0][tid] = bn0;
+        bbuf[1][tid] = bn1;
+    }
+    __syncthreads();
+
+    f32x16 accA[QB], accB[QB];
+    mfma_tile(kbuf0, accA);
+    // Every wave must be done reading tile 0 before stage 0 reloads kbuf0.
+    __syncthreads();
+
+    // one pipeline stage; CUR holds tile t, the next tile is read from NEXTBUF
+    // and tile t+2 is loaded into CURBUF (tile t's buffer, already consumed).
+#define FS_STAGE(t_, CUR, NXT, CURBUF, NEXTBUF)                                   \
+    do {                                                                          \
+        const int ts = (t_);                                                       \
+        float bn = 0.f;                                                           \
+        if (ts + 2 < ntiles) {                                                     \
+            issue_tile(ts + 2, CURBUF);                                            \
+            bn = load_beta(ts + 2);                                                \
+        }                                                                         \
+        /* The MFMAs run unconditionally (stale buffer on the last tile, result \
+           unused).  With two waves per SIMD the halves of the workgroup do the  \
+           two parts in opposite order, so each SIMD's matrix pipe is fed by one \
+           wave while the other runs its exp/VALU epilogue. */                    \
+        if (kPingPong && WAVES == 8 && wave >= 4) {                                            \
+            epilogue(CUR, bbuf[ts % 3]);                                          \
+            __builtin_amdgcn_sched_barrier(0);                                    \
+            mfma_tile(NEXTBUF, NXT);                                              \
+        } else {                                                                  \
+            mfma_tile(NEXTBUF, NXT);                                              \
+            if (WAVES == 8) __builtin_amdgcn_sched_barrier(0);                    \
+            epilogue(CUR, bbuf[ts % 3]);                                          \
+        }                                                                         \
+        if (ts + 2 < ntiles) {                                                     \
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                      \
+            if (tid < kKeyTile) bbuf[(ts + 2) % 3][tid] = bn;                       \
+        }                                                                         \
+        __syncthreads();                                                          \
+    } while (0)
+
+    for (int t = 0; t < ntiles; t += 2) {
+        FS_STAGE(t, accA, accB, kbuf0, kbuf1);
+        if (t + 1 < ntiles) FS_STAGE(t + 1, accB, accA, kbuf1, kbuf0);
+    }
+#undef FS_STAGE
 
     // Merge the two lane halves (same row, disjoint keys) and finish.
     float resid = 0.f;
@@ -299,9 +392,6 @@ __global__ __launch_bounds__(256, 1) void lse_mfma_kernel(LseArgs a) {
         if (tid == 0) a.resid_part[blockIdx.x] = resid;
     }
 }
-
-#undef FS_LOAD_TILE
-#undef FS_STORE_TILE
 
 // ----------------------------------------------------------------- merge
 __global__ __launch_bounds__(256) void lse_merge_kernel(LseArgs a) {
@@ -358,44 +448,49 @@ hipError_t valu_dispatch(int d, const LseArgs& a, hipStream_t s, int R) {
     }
 }
 
+constexpr int qb_cap(int qb) { return qb < kQbMax ? qb : kQbMax; }
+// Eight waves (two per SIMD, 32 rows each) when a 32-row resident block fits
+// in half the register file (ng * 4 <= 128 VGPRs); otherwise four.
+constexpr int waves_for(int ng) { return kMfmaWaves == 8 && ng <= 32 ? 8 : 4; }
+constexpr int qb_for(int op, int ng) {
+    return waves_for(ng) == 8 ? 1
+           : op == OP_F32      ? (ng <= 8 ? 4 : (ng <= 32 ? qb_cap(2) : 1))
+                               : (ng <= 32 ? qb_cap(2) : 1);
+}
+
 template <int OP, int NG, int QB>
 hipError_t mfma_launch(const LseArgs& a, hipStream_t s) {
-    constexpr int rpb = 4 * 32 * QB;
+    constexpr int W = waves_for(NG);
+    constexpr int rpb = W * 32 * QB;
     const dim3 grid((a.n_rows + rpb - 1) / rpb, a.n_split);
-    lse_mfma_kernel<OP, NG, QB><<<grid, 256, 0, s>>>(a);
+    lse_mfma_kernel<OP, NG, QB, W><<<grid, W * 64, 0, s>>>(a);
     return hipGetLastError();
+}
+
+// 32-row blocks per wave: as many as the resident row block's registers allow
+// (64 rows x 512 bf16 values = 256 VGPRs per lane), fewer for 8-wave groups.
+template <int OP, int NG>
+hipError_t mfma_launch_ng(const LseArgs& a, hipStream_t s) {
+    return mfma_launch<OP, NG, qb_for(OP, NG)>(a, s);
 }
 
 template <int OP>
 hipError_t mfma_dispatch(int ng, const LseArgs& a, hipStream_t s) {
-    if constexpr (OP == OP_F32) {
-        switch (ng) {
-            case 1: return mfma_launch<OP, 1, 4>(a, s);
-            case 2: return mfma_launch<OP, 2, 4>(a, s);
-            case 4: return mfma_launch<OP, 4, 4>(a, s);
-            case 8: return mfma_launch<OP, 8, 4>(a, s);
-            case 16: return mfma_launch<OP, 16, 2>(a, s);
-            case 32: return mfma_launch<OP, 32, 2>(a, s);
-            case 64: return mfma_launch<OP, 64, 1>(a, s);
-            default: return hipErrorInvalidValue;
-        }
-    } else {
-        switch (ng) {
-            case 1: return mfma_launch<OP, 1, 2>(a, s);
-            case 2: return mfma_launch<OP, 2, 2>(a, s);
-            case 4: return mfma_launch<OP, 4, 2>(a, s);
-            case 8: return mfma_launch<OP, 8, 2>(a, s);
-            case 16: return mfma_launch<OP, 16, 2>(a, s);
-            case 32: return mfma_launch<OP, 32, 2>(a, s);
-            case 64: return mfma_launch<OP, 64, 1>(a, s);
-            default: return hipErrorInvalidValue;
-        }
+    switch (ng) {
+        case 1: return mfma_launch_ng<OP, 1>(a, s);
+        case 2: return mfma_launch_ng<OP, 2>(a, s);
+        case 4: return mfma_launch_ng<OP, 4>(a, s);
+        case 8: return mfma_launch_ng<OP, 8>(a, s);
+        case 16: return mfma_launch_ng<OP, 16>(a, s);
+        case 32: return mfma_launch_ng<OP, 32>(a, s);
+        case 64: return mfma_launch_ng<OP, 64>(a, s);
+        default: return hipErrorInvalidValue;
     }
 }
 
 int mfma_qb(int path, int ng) {
-    if (path == PATH_MFMA_F32) return ng <= 8 ? 4 : (ng <= 32 ? 2 : 1);
-    return ng <= 32 ? 2 : 1;
+    const int op = path == PATH_MFMA_F32 ? OP_F32 : OP_BF16;
+    return qb_for(op, ng);
 }
 
 int ng_of(int path, int dp) { return path == PATH_MFMA_F32 ? dp / 8 : dp / 16; }
@@ -408,14 +503,17 @@ int valu_rows_per_lane(int n_rows) { return n_rows >= 65536 ? 4 : 1; }
 
 int lse_rows_per_block(int path, int dp, int n_rows) {
     if (path == PATH_VALU) return 256 * valu_rows_per_lane(n_rows);
-    return 4 * 32 * mfma_qb(path, ng_of(path, dp));
+    const int ng = ng_of(path, dp);
+    return waves_for(ng) * 32 * mfma_qb(path, ng);
 }
 
 // For the vector path LseArgs::dp is the true dimension d (<= 8); operand rows
 // are stored 4 (d <= 4) or 8 floats apart.  For the matrix paths it is the
 // padded dimension.
-hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s) {
+hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s, hipEvent_t ev_begin,
+                      hipEvent_t ev_end) {
     hipError_t e;
+    if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
     if (path == PATH_VALU) {
         const int R = valu_rows_per_lane(a.n_rows);
         e = valu_dispatch(a.dp, a, s, R);
@@ -431,6 +529,7 @@ hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s) {
             return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
+    if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
     int fin_blocks;
     if (a.n_split > 1) {
         fin_blocks = (a.n_rows + 255) / 256;
@@ -440,8 +539,8 @@ hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s) {
         const int R = valu_rows_per_lane(a.n_rows);
         fin_blocks = (a.n_rows + 256 * R - 1) / (256 * R);
     } else {
-        const int rpb = 4 * 32 * mfma_qb(path, ng_of(path, a.dp));
-        fin_blocks = (a.n_rows + rpb - 1) / rpb;
+        fin_blocks = (a.n_rows + lse_rows_per_block(path, a.dp, a.n_rows) - 1) /
+                     lse_rows_per_block(path, a.dp, a.n_rows);
     }
     if (a.cur) {
         resid_reduce_kernel<<<1, 256, 0, s>>>(a.resid_part, fin_blocks, a.resid_out);
