@@ -43,6 +43,34 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
+def counter_mode(w, half_steps: int = 6) -> None:
+    """Workload for hardware-counter runs: a 1 GiB elementwise read+write of
+    known size (the counters' calibration), then problem preparation and
+    `half_steps` alternating LSE passes of the benchmark workload."""
+    import torch
+
+    from streaming_sinkhorn_solver_amd import binding
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    X, Y, a, b = (torch.from_numpy(v).to(dev) for v in (w.X, w.Y, w.a, w.b))
+    f = torch.empty(w.n, device=dev)
+    g = torch.empty(w.m, device=dev)
+    p = binding.fs_potentials_init(X, Y, a, b, prec="bf16", f=f, g=g)
+    for k in range(half_steps):
+        if k % 2 == 0:
+            binding.fs_lse_update_f(p, w.eps, g, f)
+        else:
+            binding.fs_lse_update_g(p, w.eps, f, g)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_mode": "done", "half_steps": half_steps,
+                      "copy_bytes": float(1 << 30)}), flush=True)
+
+
 def traffic_per_launch():
     """Calibrated HBM bytes per LSE launch from the committed counter summary,
     or None if it is missing or was taken on another kernel source."""
@@ -56,7 +84,7 @@ def traffic_per_launch():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_s: float = 10.0) -> dict:
+def cpu_baseline(w, target_s: float = 15.0) -> dict:
     """The oracle's f-update on a sample of rows, scaled to iterations/s."""
     import numpy as np
 
@@ -64,11 +92,12 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
 
     rng = np.random.default_rng(0)
     g = np.zeros(w.m)
-    rows = rng.choice(w.n, size=32, replace=False)
+    k0 = 4 * oracle.num_threads()
+    rows = rng.choice(w.n, size=k0, replace=False)
     t0 = time.perf_counter()
     oracle.f_update_rows(w.X, w.Y, w.b, g, w.eps, rows)
     t1 = time.perf_counter() - t0
-    k = int(min(w.n, max(32, round(32 * target_s / max(t1, 1e-3)))))
+    k = int(min(w.n, max(k0, round(k0 * target_s / max(t1, 1e-3)))))
     rows = rng.choice(w.n, size=k, replace=False)
     t0 = time.perf_counter()
     oracle.f_update_rows(w.X, w.Y, w.b, g, w.eps, rows)
@@ -91,6 +120,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--iters", type=int, default=None, help="override iterations per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="run the hardware-counter workload instead of the benchmark")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -105,6 +136,9 @@ def main():
 
     binding.load()
     w = workloads.make("c3")
+    if args.counters:
+        counter_mode(w)
+        return
     iters = args.iters or w.iters
     dev = torch.device("cuda:0")
     X = torch.from_numpy(w.X).to(dev)

@@ -38,7 +38,7 @@ struct fs_problem {
     int* flag;
     float2* part;
     float* resid_part;
-    float* scal;      // [0..1] residual outputs, [2..3] transport scale pair
+    float* scal;      // [0..1] residual outputs, [2..4] transport scale pair and max bits
     float* pot_tmp;   // max(n, m) floats
     void* vt;         // f16 [dv_max][m_pad] (matrix paths with dv_max > 0)
 };

@@ -20,6 +20,8 @@
 // f16 copy of V (keys on the contraction axis, in the same slot order), so
 // the weights never leave registers.  V is copied once, transposed and scaled
 // by a power of two into the f16 range; the scale is undone exactly at the end.
+#include <algorithm>
+
 #include "fs_device.hpp"
 #include "fs_internal.h"
 
@@ -28,30 +30,37 @@ namespace fs {
 namespace {
 
 // ---------------------------------------------------- V -> f16, transposed
-// scratch[0] = 2^s, scratch[1] = 2^-s, with s chosen so max|V| 2^s <= 2^14.
+// max|V| over all entries as the bit pattern of a non-negative float (for
+// which integer order is float order), so an atomic max is order independent.
 __global__ __launch_bounds__(256) void vmax_kernel(const float* __restrict__ V, int64_t count,
-                                                   float* __restrict__ scratch) {
+                                                   unsigned* __restrict__ maxbits) {
     __shared__ float red[256];
     float mx = 0.f;
-    for (int64_t k = threadIdx.x; k < count; k += 256) mx = fmaxf(mx, fabsf(V[k]));
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < count; k += stride)
+        mx = fmaxf(mx, fabsf(V[k]));
     red[threadIdx.x] = mx;
     __syncthreads();
     for (int o = 128; o >= 1; o >>= 1) {
         if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
-        const float m = red[0];
-        int s = 0;
-        if (m > 0.f && m <= 3.402823466e38f) {
-            int e;
-            frexpf(m, &e);  // m in [2^(e-1), 2^e)
-            s = 14 - e;     // m 2^s < 2^14
-            s = s > 100 ? 100 : (s < -100 ? -100 : s);
-        }
-        scratch[0] = ldexpf(1.f, s);
-        scratch[1] = ldexpf(1.f, -s);
+    if (threadIdx.x == 0) atomicMax(maxbits, __float_as_uint(red[0]));
+}
+
+// scratch[0] = 2^s, scratch[1] = 2^-s, with s chosen so max|V| 2^s < 2^14.
+__global__ void vscale_kernel(const unsigned* __restrict__ maxbits, float* __restrict__ scratch) {
+    if (threadIdx.x != 0) return;
+    const float m = __uint_as_float(maxbits[0]);
+    int s = 0;
+    if (m > 0.f && m <= 3.402823466e38f) {
+        int e;
+        frexpf(m, &e);  // m in [2^(e-1), 2^e)
+        s = 14 - e;
+        s = s > 100 ? 100 : (s < -100 ? -100 : s);
     }
+    scratch[0] = ldexpf(1.f, s);
+    scratch[1] = ldexpf(1.f, -s);
 }
 
 // Vt[k][j] = f16(V[j][k] * 2^s) for j < m, 0 for m <= j < m_pad.
@@ -129,31 +138,42 @@ __device__ __forceinline__ f32x16 score_step(const uint4& av, const uint4& bv, f
     }
 }
 
-constexpr int kVtStride = 36;  // f16 elements per LDS row of the V^T tile (32 keys + pad)
-
-// Each wave: 32 rows; workgroup: 128 rows x (32*NB) output columns starting
-// at column blockIdx.y * 32 * NB.
+// Transport kernel: 4 waves x 32 rows, output columns [c0, c0 + 32*NB).
+// Pipeline stage t: DMA key tile t+2 and V^T tile t+1; score MFMAs of tile
+// t+1; for tile t the weights p = 2^(z2 - L) are packed to f16 in registers
+// and multiplied with the V^T tile on v_mfma_f32_32x32x16_f16.  Register r
+// of the score accumulator holds key 8*(r/4) + 4*h + (r%4); registers 0..7
+// and 8..15 are the A operands of the two products over the tile's 32 keys,
+// and the V^T fragments are fetched for the same keys in the same slot order.
+// V^T tile rows are 64 bytes (32 f16 keys); 16-byte chunk c of row r sits at
+// r*4 + (c ^ ((r >> 2) & 3)) so that 16 consecutive rows hit distinct banks.
 template <int OP, int NG, int NB>
-__global__ __launch_bounds__(256, 1) void transport_mfma_kernel(TransportArgs a) {
+__global__ __launch_bounds__(256, 1) void transport_mfma_kernel(TransportArgs a, int64_t m_pad) {
+    constexpr int WAVES = 4;
     constexpr int CPR = 2 * NG;
     constexpr int ROW_BYTES = CPR * 16;
     constexpr int TILE_CHUNKS = kKeyTile * CPR;
-    constexpr int LOADS = (TILE_CHUNKS + 255) / 256;
-    constexpr int SWZ = CPR >= 8 ? 7 : CPR - 1;
-    constexpr int DVC = 32 * NB;                          // output columns per workgroup
-    constexpr int VT_ELEMS = DVC * kKeyTile;              // f16 values of one V^T tile
-    constexpr int VLOADS = (VT_ELEMS / 8 + 255) / 256;    // 16-byte loads per thread
+    constexpr int TILE_INSTR = TILE_CHUNKS / 64;
+    constexpr int INSTR_PER_WAVE = (TILE_INSTR + WAVES - 1) / WAVES;
+    constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
+    constexpr int JB = SWZ + 1 < 2 * NG ? (SWZ + 1) / 2 : NG;
+    constexpr int KB = NG / JB;
+    constexpr int DVC = 32 * NB;
+    constexpr int VT_CHUNKS = DVC * 4;
+    constexpr int VT_INSTR = VT_CHUNKS / 64;
+    constexpr int VT_PER_WAVE = (VT_INSTR + WAVES - 1) / WAVES;
 
-    __shared__ uint4 kbuf[2][TILE_CHUNKS];
-    __shared__ float bbuf[2][kKeyTile];
-    __shared__ __attribute__((aligned(16))) _Float16 vbuf[2][DVC * kVtStride];
-    __shared__ float rowscale[4][32];
+    __shared__ __attribute__((aligned(16))) uint4 kbuf0[TILE_CHUNKS];
+    __shared__ __attribute__((aligned(16))) uint4 kbuf1[TILE_CHUNKS];
+    __shared__ __attribute__((aligned(16))) uint4 vbuf0[VT_CHUNKS];
+    __shared__ __attribute__((aligned(16))) uint4 vbuf1[VT_CHUNKS];
+    __shared__ __attribute__((aligned(16))) float bbuf[3][kKeyTile];
+    __shared__ float rowscale[WAVES][32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
-    const int row0 = blockIdx.x * 128 + wave * 32;
+    const int row0 = blockIdx.x * (WAVES * 32) + wave * 32;
     const int c0 = blockIdx.y * DVC;
-    const int64_t m_pad = ((int64_t)a.n_keys + kRowPad - 1) / kRowPad * kRowPad;
 
     uint4 q[NG];
     {
@@ -166,55 +186,61 @@ __global__ __launch_bounds__(256, 1) void transport_mfma_kernel(TransportArgs a)
 
     const int ntiles = (a.n_keys + kKeyTile - 1) / kKeyTile;
     const char* __restrict__ keys = (const char*)a.keys;
-    const _Float16* __restrict__ Vt = (const _Float16*)a.Vt;
+    const char* __restrict__ Vt = (const char*)a.Vt;
 
-    uint4 stg[LOADS];
-    uint4 vstg[VLOADS];
-    float bstg = 0.f;
-    auto load_tile = [&](int t) __attribute__((always_inline)) {
-        const char* base = keys + (int64_t)(t * kKeyTile) * ROW_BYTES;
+    auto issue_k = [&](int k, uint4* dst) __attribute__((always_inline)) {
+        const char* tbase = keys + (int64_t)(k * kKeyTile) * ROW_BYTES;
 #pragma unroll
-        for (int l = 0; l < LOADS; ++l) {
-            const int c = l * 256 + tid;
-            if (TILE_CHUNKS % 256 == 0 || c < TILE_CHUNKS) stg[l] = *(const uint4*)(base + c * 16);
-        }
-        if (tid < kKeyTile) {
-            const int j = t * kKeyTile + tid;
-            bstg = j < a.n_keys ? fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]) : -INFINITY;
-        }
-        // V^T tile: DVC rows (columns of V) x 32 keys, 4 chunks of 8 keys per row.
-#pragma unroll
-        for (int l = 0; l < VLOADS; ++l) {
-            const int c = l * 256 + tid;
-            if (c < VT_ELEMS / 8) {
-                const int vr = c >> 2, part = c & 3;
-                const int col = c0 + vr;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (col < a.dv) v = *(const uint4*)(Vt + (int64_t)col * m_pad + t * kKeyTile + part * 8);
-                vstg[l] = v;
+        for (int l = 0; l < INSTR_PER_WAVE; ++l) {
+            const int Li = l * WAVES + wave;
+            if (TILE_INSTR % WAVES == 0 || Li < TILE_INSTR) {
+                const int P = Li * 64 + lane;
+                const int m = P / CPR, cp = P % CPR;
+                const char* src = tbase + m * ROW_BYTES + (cp ^ (m & SWZ)) * 16;
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)src, (__attribute__((address_space(3))) void*)(dst + Li * 64), 16, 0,
+                    0);
             }
         }
     };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    auto issue_v = [&](int k, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int l = 0; l < LOADS; ++l) {
-            const int c = l * 256 + tid;
-            if (TILE_CHUNKS % 256 == 0 || c < TILE_CHUNKS) {
-                const int m = c / CPR, cc = c % CPR;
-                kbuf[buf][m * CPR + (cc ^ (m & SWZ))] = stg[l];
+        for (int l = 0; l < VT_PER_WAVE; ++l) {
+            const int Li = l * WAVES + wave;
+            if (VT_INSTR % WAVES == 0 || Li < VT_INSTR) {
+                const int P = Li * 64 + lane;
+                const int r = P >> 2, cp = P & 3;
+                const int col = min(c0 + r, a.dv - 1);  // rows past dv: any valid row, unused
+                const char* src = Vt + ((int64_t)col * m_pad + k * kKeyTile) * 2 +
+                                  (cp ^ ((r >> 2) & 3)) * 16;
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)src, (__attribute__((address_space(3))) void*)(dst + Li * 64), 16, 0,
+                    0);
             }
         }
-        if (tid < kKeyTile) bbuf[buf][tid] = bstg;
+    };
+    auto load_beta = [&](int k) __attribute__((always_inline)) -> float {
+        const int j = k * kKeyTile + tid;
+        float b = -INFINITY;
+        if (tid < kKeyTile && j < a.n_keys)
+            b = fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]);
+        return b;
+    };
+
+    int abase[JB];
 #pragma unroll
-        for (int l = 0; l < VLOADS; ++l) {
-            const int c = l * 256 + tid;
-            if (c < VT_ELEMS / 8) {
-                const int vr = c >> 2, part = c & 3;
-                // two 8-byte halves (rows are 72 bytes apart, 8-byte aligned)
-                uint2* dst = (uint2*)(&vbuf[buf][vr * kVtStride + part * 8]);
-                dst[0] = make_uint2(vstg[l].x, vstg[l].y);
-                dst[1] = make_uint2(vstg[l].z, vstg[l].w);
-            }
+    for (int j = 0; j < JB; ++j) abase[j] = (ln * CPR + ((2 * j + h) ^ (ln & SWZ))) * 16;
+    auto scores = [&](const uint4* src, f32x16& acc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const char* kb = (const char*)src;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            uint4 av[JB];
+#pragma unroll
+            for (int j = 0; j < JB; ++j) av[j] = *(const uint4*)(kb + abase[j] + k * (2 * JB * 16));
+#pragma unroll
+            for (int j = 0; j < JB; ++j) acc = score_step<OP>(av[j], q[JB * k + j], acc);
         }
     };
 
@@ -224,54 +250,81 @@ __global__ __launch_bounds__(256, 1) void transport_mfma_kernel(TransportArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) u[nb][r] = 0.f;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
-
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        const uint4* kb = kbuf[buf] + ln * CPR;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) acc = score_step<OP>(kb[(2 * g + h) ^ (ln & SWZ)], q[g], acc);
-
-        // weights p = 2^(z2 - L), register r <-> key 8*(r/4) + 4*h + (r%4)
+    // V^T fragment offsets (bytes within a tile) of this lane for chunk c.
+    auto voff = [&](int nb, int c) __attribute__((always_inline)) -> int {
+        const int r = nb * 32 + ln;
+        return (r * 4 + (c ^ ((r >> 2) & 3))) * 16 + 8 * h;
+    };
+    auto weights_pv = [&](const f32x16& acc, const float* bb, const uint4* vsrc)
+                          __attribute__((always_inline)) {
         f16x8 p0, p1;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-            const float4 bv = *(const float4*)&bbuf[buf][8 * qq + 4 * h];
-            const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+            const float4 bv = *(const float4*)&bb[8 * qq + 4 * h];
+            const float bq[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p = ex2(fmaf(acc[4 * qq + e], a.c_score, bb[e]) - L);
+                const float p = ex2(fmaf(acc[4 * qq + e], a.c_score, bq[e]) - L);
                 if (qq < 2)
                     p0[4 * qq + e] = (_Float16)p;
                 else
                     p1[4 * (qq - 2) + e] = (_Float16)p;
             }
         }
-        // U += P.V: A = weights (row ln, contraction slots 8h..8h+7), B = V^T
-        // rows (column c0+nb*32+ln) at the same keys.
-        const _Float16* vb = vbuf[buf];
+        const char* vb = (const char*)vsrc;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const _Float16* vr = vb + (nb * 32 + ln) * kVtStride;
-            const uint2 k0 = *(const uint2*)(vr + 4 * h);
-            const uint2 k1 = *(const uint2*)(vr + 8 + 4 * h);
-            const uint2 k2 = *(const uint2*)(vr + 16 + 4 * h);
-            const uint2 k3 = *(const uint2*)(vr + 24 + 4 * h);
+            const uint2 k0 = *(const uint2*)(vb + voff(nb, 0));
+            const uint2 k1 = *(const uint2*)(vb + voff(nb, 1));
+            const uint2 k2 = *(const uint2*)(vb + voff(nb, 2));
+            const uint2 k3 = *(const uint2*)(vb + voff(nb, 3));
             const f16x8 b0 = __builtin_bit_cast(f16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
             const f16x8 b1 = __builtin_bit_cast(f16x8, make_uint4(k2.x, k2.y, k3.x, k3.y));
             u[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(p0, b0, u[nb], 0, 0, 0);
             u[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(p1, b1, u[nb], 0, 0, 0);
         }
+    };
 
-        if (t + 1 < ntiles) store_tile(buf ^ 1);
-        __syncthreads();
+    // prologue: key tiles 0, 1 and V^T tile 0 loaded; scores of tile 0
+    float bn0 = 0.f, bn1 = 0.f;
+    issue_k(0, kbuf0);
+    issue_v(0, vbuf0);
+    bn0 = load_beta(0);
+    if (ntiles > 1) {
+        issue_k(1, kbuf1);
+        bn1 = load_beta(1);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid < kKeyTile) {
+        bbuf[0][tid] = bn0;
+        bbuf[1][tid] = bn1;
+    }
+    __syncthreads();
+    f32x16 accA, accB;
+    scores(kbuf0, accA);
+    __syncthreads();  // all waves done with key tile 0 before kbuf0 is reloaded
+
+#define FS_TSTAGE(t_, CUR, NXT, KCUR, KNEXT, VCUR, VNEXT)                          \
+    do {                                                                          \
+        const int ts = (t_);                                                      \
+        float bn = 0.f;                                                           \
+        if (ts + 2 < ntiles) {                                                    \
+            issue_k(ts + 2, KCUR);                                                \
+            bn = load_beta(ts + 2);                                               \
+        }                                                                         \
+        if (ts + 1 < ntiles) issue_v(ts + 1, VNEXT);                              \
+        scores(KNEXT, NXT);                                                       \
+        weights_pv(CUR, bbuf[ts % 3], VCUR);                                      \
+        if (ts + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     \
+        if (ts + 2 < ntiles && tid < kKeyTile) bbuf[(ts + 2) % 3][tid] = bn;       \
+        __syncthreads();                                                          \
+    } while (0)
+
+    for (int t = 0; t < ntiles; t += 2) {
+        FS_TSTAGE(t, accA, accB, kbuf0, kbuf1, vbuf0, vbuf1);
+        if (t + 1 < ntiles) FS_TSTAGE(t + 1, accB, accA, kbuf1, kbuf0, vbuf1, vbuf0);
+    }
+#undef FS_TSTAGE
 
     // Row factor 2^(L_i + (f_i - |x~_i|^2) c_bias) [* a_i] * 2^-s.
     if (h == 0) {
@@ -279,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void transport_mfma_kernel(TransportArgs a)
         if (myrow < a.n_rows) {
             sc = ex2(L + (a.row_pot[myrow] - a.row_nrm[myrow]) * a.c_bias);
             if (!a.divide_by_a) sc *= a.row_w[myrow];
-            sc *= a.v_unscale_dev ? a.v_unscale_dev[0] : 1.f;
+            sc *= a.v_unscale_dev[0];
         }
         rowscale[wave][ln] = sc;
     }
@@ -306,23 +359,24 @@ hipError_t transport_valu_launch(const TransportArgs& a, hipStream_t s) {
 }
 
 template <int OP, int NG>
-hipError_t transport_mfma_launch(const TransportArgs& a, hipStream_t s) {
-    constexpr int NB = NG >= 64 ? 2 : 4;
+hipError_t transport_mfma_launch(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
+    // output columns per workgroup: 256 (128 when the resident block is 256 VGPRs)
+    constexpr int NB = NG >= 64 ? 4 : 8;
     const dim3 grid((a.n_rows + 127) / 128, (a.dv + 32 * NB - 1) / (32 * NB));
-    transport_mfma_kernel<OP, NG, NB><<<grid, 256, 0, s>>>(a);
+    transport_mfma_kernel<OP, NG, NB><<<grid, 256, 0, s>>>(a, m_pad);
     return hipGetLastError();
 }
 
 template <int OP>
-hipError_t transport_mfma_dispatch(int ng, const TransportArgs& a, hipStream_t s) {
+hipError_t transport_mfma_dispatch(int ng, const TransportArgs& a, int64_t m_pad, hipStream_t s) {
     switch (ng) {
-        case 1: return transport_mfma_launch<OP, 1>(a, s);
-        case 2: return transport_mfma_launch<OP, 2>(a, s);
-        case 4: return transport_mfma_launch<OP, 4>(a, s);
-        case 8: return transport_mfma_launch<OP, 8>(a, s);
-        case 16: return transport_mfma_launch<OP, 16>(a, s);
-        case 32: return transport_mfma_launch<OP, 32>(a, s);
-        case 64: return transport_mfma_launch<OP, 64>(a, s);
+        case 1: return transport_mfma_launch<OP, 1>(a, m_pad, s);
+        case 2: return transport_mfma_launch<OP, 2>(a, m_pad, s);
+        case 4: return transport_mfma_launch<OP, 4>(a, m_pad, s);
+        case 8: return transport_mfma_launch<OP, 8>(a, m_pad, s);
+        case 16: return transport_mfma_launch<OP, 16>(a, m_pad, s);
+        case 32: return transport_mfma_launch<OP, 32>(a, m_pad, s);
+        case 64: return transport_mfma_launch<OP, 64>(a, m_pad, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -345,9 +399,16 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
             default: return hipErrorInvalidValue;
         }
     }
-    vmax_kernel<<<1, 256, 0, s>>>(a.V, (int64_t)a.n_keys * a.dv, scratch);
-    hipError_t e = hipGetLastError();
+    // scratch: [0..1] scale pair, [2] max bits
+    unsigned* maxbits = (unsigned*)(scratch + 2);
+    hipError_t e = launch_fill(scratch + 2, 1, 0.f, s);
     if (e != hipSuccess) return e;
+    const int64_t count = (int64_t)a.n_keys * a.dv;
+    const int64_t blocks = std::min<int64_t>((count + 255) / 256, 2048);
+    vmax_kernel<<<(unsigned)blocks, 256, 0, s>>>(a.V, count, maxbits);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    vscale_kernel<<<1, 64, 0, s>>>(maxbits, scratch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         const dim3 grid((unsigned)((m_pad + 31) / 32), (a.dv + 31) / 32);
         transpose_v_kernel<<<grid, 256, 0, s>>>(a.V, a.n_keys, m_pad, a.dv, scratch,
@@ -357,9 +418,9 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
     a.Vt = Vt_buf;
     a.v_unscale_dev = scratch + 1;
     const int ng = path == PATH_MFMA_F32 ? a.dp / 8 : a.dp / 16;
-    if (path == PATH_MFMA_F32) return transport_mfma_dispatch<OP_F32>(ng, a, s);
-    if (path == PATH_MFMA_BF16) return transport_mfma_dispatch<OP_BF16>(ng, a, s);
-    if (path == PATH_MFMA_F16) return transport_mfma_dispatch<OP_F16>(ng, a, s);
+    if (path == PATH_MFMA_F32) return transport_mfma_dispatch<OP_F32>(ng, a, m_pad, s);
+    if (path == PATH_MFMA_BF16) return transport_mfma_dispatch<OP_BF16>(ng, a, m_pad, s);
+    if (path == PATH_MFMA_F16) return transport_mfma_dispatch<OP_F16>(ng, a, m_pad, s);
     return hipErrorInvalidValue;
 }
 
