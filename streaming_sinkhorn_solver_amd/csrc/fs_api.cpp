@@ -123,7 +123,8 @@ fs_status choose_path(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_
 }
 
 // Key-range split so that (row blocks x splits) fills the GPU in a near-whole
-// number of rounds, preferring few splits.
+// number of rounds, preferring few splits, with every split no larger than
+// the kernel's key-range limit.
 void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_out,
                   int& kps_out) {
     const int rpb = lse_rows_per_block(path, lse_dp, (int)n_rows);
@@ -131,12 +132,14 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
     const int slots = path == PATH_VALU ? 1024 : 256;
     const int tile = path == PATH_VALU ? 16 : kKeyTile;
     const int64_t min_keys = path == PATH_VALU ? 1024 : 256;
-    int bestS = 1;
-    int64_t bestK = (n_keys + tile - 1) / tile * tile;
+    const int64_t max_keys = lse_max_keys_per_split(path, lse_dp);
+    int bestS = -1;
+    int64_t bestK = 0;
     double best = -1.0;
-    for (int S = 1; S <= 64; ++S) {
-        int64_t kps = ((n_keys + S - 1) / S + tile - 1) / tile * tile;
-        if (S > 1 && kps < min_keys) break;
+    for (int S = 1; S <= 4096; ++S) {
+        const int64_t kps = ((n_keys + S - 1) / S + tile - 1) / tile * tile;
+        if (kps > max_keys) continue;
+        if (S > 1 && kps < min_keys && bestS > 0) break;
         const int64_t Se = (n_keys + kps - 1) / kps;
         if (Se != S) continue;
         const int64_t blocks = R * Se;
@@ -148,6 +151,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
             bestS = (int)Se;
             bestK = kps;
         }
+        if (S >= 64 && bestS > 0) break;
     }
     S_out = bestS;
     kps_out = (int)bestK;

@@ -24,6 +24,23 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
+// One wave-wide 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4):
+// lane i's 16 bytes at `src` land at LDS byte address `lds_base + 16*i`
+// (`lds_base` must be wave-uniform).  Issued as inline assembly so the
+// compiler does not model it as an LDS store: the caller owns completion and
+// waits for it explicitly (s_waitcnt vmcnt) before a barrier publishes it.
+__device__ __forceinline__ void dma_to_lds16(const void* src, const void* lds_base) {
+    const uint32_t lds =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds_base);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+        : "memory", "m0");
+}
+
 // Combine two partial base-2 log-sum-exp states (M1, s1) and (M2, s2), each
 // meaning M + log2(s).  Either may be empty (M = -inf, s = 0).
 __device__ __forceinline__ void lse_merge(float& M, float& s, float M2, float s2) {

@@ -98,6 +98,9 @@ hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s, hipEvent_t ev_b
 // Rows handled by one workgroup of the streaming kernel (path, dp as passed
 // in LseArgs, rows of the pass).
 int lse_rows_per_block(int path, int dp, int n_rows);
+// Largest key range one workgroup of the streaming kernel may cover (its key
+// biases are held in LDS).
+int lse_max_keys_per_split(int path, int dp);
 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
 hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratch,

@@ -140,6 +140,32 @@ constexpr bool kPingPong = false;
 #else
 constexpr bool kPingPong = true;  // opposite MFMA/epilogue order in the two wave halves
 #endif
+#ifdef FS_INTERLEAVE
+constexpr bool kInterleave = true;
+#else
+constexpr bool kInterleave = false;
+#endif
+
+// Scheduling hint: spread the epilogue's vector instructions and the operand
+// fetches between the N matrix instructions of a stage (1 MFMA, 1 LDS read,
+// 5 VALU, repeated).
+// Workgroup barrier without the memory fence of __syncthreads(): only this
+// wave's LDS operations are waited for.  (The fence would also wait for every
+// outstanding global->LDS tile load, serialising the load pipeline; the
+// pipeline waits for exactly the tiles it needs with explicit vmcnt waits.)
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+}
 template <int OP>
 __device__ __forceinline__ f32x16 mfma_step(const uint4& av, const uint4& bv, f32x16 acc) {
     if constexpr (OP == OP_BF16) {
@@ -160,27 +186,41 @@ __device__ __forceinline__ f32x16 mfma_step(const uint4& av, const uint4& bv, f3
     }
 }
 
+// Pipeline depth (key-tile buffers) and the largest key range per workgroup
+// whose biases fit next to them in LDS (163,840 bytes on gfx950).
+constexpr int kLdsBytes = 163840;
+constexpr int nbuf_for(int ng) { return ng >= 64 ? 2 : 4; }
+constexpr int tile_bytes_for(int ng) { return kKeyTile * 2 * ng * 16; }
+constexpr int kps_max_for(int ng) {
+    return ((kLdsBytes - nbuf_for(ng) * tile_bytes_for(ng) - 2048) / 4 / kKeyTile * kKeyTile) < 16384
+               ? (kLdsBytes - nbuf_for(ng) * tile_bytes_for(ng) - 2048) / 4 / kKeyTile * kKeyTile
+               : 16384;
+}
+
 // OP: score element type.  NG: 16-byte chunk pairs per operand row (a row is
 // 2*NG chunks; dp = 16*NG for 2-byte types, 8*NG for fp32).  QB: 32-row
-// blocks per wave.  WAVES: waves per workgroup.
+// blocks per wave.  WAVES: waves per workgroup.  NBUF: key-tile buffers.
 //
-// Software pipeline over 32-key tiles, one barrier per tile; iteration t:
-//   (1) direct global->LDS loads (global_load_lds_dwordx4) of tile t+2 into
-//       the buffer tile t used, plus its 32 key biases into registers;
+// Software pipeline over 32-key tiles, one barrier per tile; stage t:
+//   (1) direct global->LDS loads (global_load_lds_dwordx4) of tile t+NBUF into
+//       the buffer tile t used, so every tile has NBUF-1 stages to arrive;
 //   (2) the MFMAs of tile t+1 (A operand read from LDS, B resident);
-//   (3) the online-LSE epilogue of tile t, independent of (2), so the
-//       scheduler can overlap it with the matrix instructions;
-//   (4) wait for this wave's loads, publish the biases, barrier.
-// Tiles are stored XOR-swizzled (chunk c of key m at m*CPR + (c ^ (m & 7)))
-// so that the 32 keys read by one MFMA operand fetch hit distinct banks.
+//   (3) the online-LSE epilogue of tile t, independent of (2);
+//   (4) wait until tile t+2 has landed (later tiles stay in flight), barrier.
+// The key biases of the workgroup's whole key range are computed into LDS
+// once, up front.  Tiles are stored XOR-swizzled (chunk c of key m at
+// m*CPR + (c ^ (m & SWZ))) so that one operand fetch hits distinct banks.
 template <int OP, int NG, int QB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
+    constexpr int NT = WAVES * 64;
     constexpr int CPR = 2 * NG;                      // 16-byte chunks per row
     constexpr int ROW_BYTES = CPR * 16;
     constexpr int TILE_CHUNKS = kKeyTile * CPR;      // chunks per key tile (>= 64)
     constexpr int TILE_INSTR = TILE_CHUNKS / 64;     // wave-wide 1 KiB loads per tile
     constexpr int INSTR_PER_WAVE = (TILE_INSTR + WAVES - 1) / WAVES;
-    // XOR swizzle over 16 chunk columns (256 bytes = one pass over 64 banks)
+    constexpr int MIN_INSTR = TILE_INSTR / WAVES;    // loads per tile issued by every wave
+    constexpr int NBUF = nbuf_for(NG);
+    constexpr int KPS_MAX = kps_max_for(NG);
 #ifndef FS_SWZ_COLS
 #define FS_SWZ_COLS 16
 #endif
@@ -190,7 +230,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 
     __shared__ __attribute__((aligned(16))) uint4 kbuf0[TILE_CHUNKS];
     __shared__ __attribute__((aligned(16))) uint4 kbuf1[TILE_CHUNKS];
-    __shared__ __attribute__((aligned(16))) float bbuf[3][kKeyTile];
+    __shared__ __attribute__((aligned(16))) uint4 kbuf2[NBUF > 2 ? TILE_CHUNKS : 1];
+    __shared__ __attribute__((aligned(16))) uint4 kbuf3[NBUF > 3 ? TILE_CHUNKS : 1];
+    __shared__ __attribute__((aligned(16))) float bkeys[KPS_MAX];
     __shared__ float red[16];
 
     const int tid = threadIdx.x;
@@ -201,19 +243,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 
     const int row0 = blockIdx.x * (WAVES * 32 * QB) + wave * (32 * QB);
     const int split = blockIdx.y;
-
-    // Resident row block: lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln.
-    uint4 q[QB][NG];
-    {
-        const char* __restrict__ rows = (const char*)a.rows;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const char* rp = rows + (int64_t)(row0 + qb * 32 + ln) * ROW_BYTES + h * 16;
-#pragma unroll
-            for (int g = 0; g < NG; ++g) q[qb][g] = *(const uint4*)(rp + g * 32);
-        }
-    }
-
     const int j0 = split * a.keys_per_split;
     const int j1 = min(a.n_keys, j0 + a.keys_per_split);
     const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
@@ -231,18 +260,33 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
                 const int P = L * 64 + lane;
                 const int m = P / CPR, cp = P % CPR;
                 const char* src = tbase + m * ROW_BYTES + (cp ^ (m & SWZ)) * 16;
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)src, (__attribute__((address_space(3))) void*)(dst + L * 64), 16, 0,
-                    0);
+                dma_to_lds16(src, dst + L * 64);
             }
         }
     };
-    auto load_beta = [&](int k) __attribute__((always_inline)) -> float {
-        const int j = j0 + k * kKeyTile + tid;
-        float b = -INFINITY;
-        if (tid < kKeyTile && j < j1) b = fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]);
-        return b;
+    auto buf = [&](int i) __attribute__((always_inline)) -> uint4* {
+        return i == 0 ? kbuf0 : i == 1 ? kbuf1 : i == 2 ? kbuf2 : kbuf3;
     };
+
+    // prologue: the first NBUF tiles in flight; key biases of the whole range
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k)
+        if (k < ntiles) issue_tile(k, buf(k));
+    for (int k = tid; k < ntiles * kKeyTile; k += NT) {
+        const int j = j0 + k;
+        bkeys[k] = j < j1 ? fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]) : -INFINITY;
+    }
+    // Resident row block: lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln.
+    uint4 q[QB][NG];
+    {
+        const char* __restrict__ rows = (const char*)a.rows;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const char* rp = rows + (int64_t)(row0 + qb * 32 + ln) * ROW_BYTES + h * 16;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) q[qb][g] = *(const uint4*)(rp + g * 32);
+        }
+    }
 
     float M[QB], S[QB];
 #pragma unroll
@@ -264,16 +308,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][r] = 0.f;
         const char* kb = (const char*)src;
-#if defined(FS_UNBATCHED)
-        const uint4* kbu = src + ln * CPR;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const uint4 av = kbu[(2 * g + h) ^ (ln & SWZ)];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma_step<OP>(av, q[qb][g], acc[qb]);
-        }
-        (void)kb;
-#else
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             uint4 av[JB];
@@ -285,7 +319,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
                 for (int qb = 0; qb < QB; ++qb)
                     acc[qb] = mfma_step<OP>(av[j], q[qb][JB * k + j], acc[qb]);
         }
-#endif
     };
     // (3) online LSE of one tile.  Accumulator register r of lane (ln, h) is
     // the score of row ln with key 8*(r/4) + 4*h + (r%4) of the tile.
@@ -315,20 +348,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
             M[qb] = Mn;
         }
     };
+    // (4) wait until at most `newer` tiles' loads (issued after tile t+2's)
+    // are outstanding for this wave.
+    auto wait_tiles = [&](int newer) __attribute__((always_inline)) {
+        if (MIN_INSTR == 0 || newer <= 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else if (newer == 1) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(MIN_INSTR) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * MIN_INSTR) : "memory");
+        }
+    };
 
-    // prologue: tiles 0 and 1 in flight, tile 0's scores computed
-    float bn0 = 0.f, bn1 = 0.f;
-    issue_tile(0, kbuf0);
-    bn0 = load_beta(0);
-    if (ntiles > 1) {
-        issue_tile(1, kbuf1);
-        bn1 = load_beta(1);
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (tid < kKeyTile) {
-        bbuf[0][tid] = bn0;
-        bbuf[1][tid] = bn1;
-    }
     __syncthreads();
 
     f32x16 accA[QB], accB[QB];
@@ -336,39 +368,36 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     // Every wave must be done reading tile 0 before stage 0 reloads kbuf0.
     __syncthreads();
 
-    // one pipeline stage; CUR holds tile t, the next tile is read from NEXTBUF
-    // and tile t+2 is loaded into CURBUF (tile t's buffer, already consumed).
-#define FS_STAGE(t_, CUR, NXT, CURBUF, NEXTBUF)                                   \
+    // one pipeline stage (tile t = ts, buffer slot I = ts % NBUF)
+#define FS_STAGE(t_, I, CUR, NXT)                                                  \
     do {                                                                          \
-        const int ts = (t_);                                                       \
-        float bn = 0.f;                                                           \
-        if (ts + 2 < ntiles) {                                                     \
-            issue_tile(ts + 2, CURBUF);                                            \
-            bn = load_beta(ts + 2);                                                \
-        }                                                                         \
+        const int ts = (t_);                                                      \
+        if (ts + NBUF < ntiles) issue_tile(ts + NBUF, buf(I));                    \
         /* The MFMAs run unconditionally (stale buffer on the last tile, result \
            unused).  With two waves per SIMD the halves of the workgroup do the  \
            two parts in opposite order, so each SIMD's matrix pipe is fed by one \
            wave while the other runs its exp/VALU epilogue. */                    \
-        if (kPingPong && WAVES == 8 && wave >= 4) {                                            \
-            epilogue(CUR, bbuf[ts % 3]);                                          \
+        if (kPingPong && WAVES == 8 && wave >= 4) {                               \
+            epilogue(CUR, bkeys + ts * kKeyTile);                                 \
             __builtin_amdgcn_sched_barrier(0);                                    \
-            mfma_tile(NEXTBUF, NXT);                                              \
+            mfma_tile(buf(((I) + 1) % NBUF), NXT);                                \
         } else {                                                                  \
-            mfma_tile(NEXTBUF, NXT);                                              \
-            if (WAVES == 8) __builtin_amdgcn_sched_barrier(0);                    \
-            epilogue(CUR, bbuf[ts % 3]);                                          \
+            mfma_tile(buf(((I) + 1) % NBUF), NXT);                                \
+            if (kPingPong && WAVES == 8) __builtin_amdgcn_sched_barrier(0);       \
+            epilogue(CUR, bkeys + ts * kKeyTile);                                 \
         }                                                                         \
-        if (ts + 2 < ntiles) {                                                     \
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                      \
-            if (tid < kKeyTile) bbuf[(ts + 2) % 3][tid] = bn;                       \
-        }                                                                         \
-        __syncthreads();                                                          \
+        /* tiles issued after tile ts+2: ts+3 .. min(ts+NBUF, ntiles-1) */        \
+        wait_tiles(min(ts + NBUF, ntiles - 1) - (ts + 2));                        \
+        stage_barrier();                                                          \
     } while (0)
 
-    for (int t = 0; t < ntiles; t += 2) {
-        FS_STAGE(t, accA, accB, kbuf0, kbuf1);
-        if (t + 1 < ntiles) FS_STAGE(t + 1, accB, accA, kbuf1, kbuf0);
+    for (int t = 0; t < ntiles; t += NBUF) {
+        FS_STAGE(t, 0, accA, accB);
+        if (t + 1 < ntiles) FS_STAGE(t + 1, 1, accB, accA);
+        if (NBUF > 2) {
+            if (t + 2 < ntiles) FS_STAGE(t + 2, 2, accA, accB);
+            if (t + 3 < ntiles) FS_STAGE(t + 3, 3, accB, accA);
+        }
     }
 #undef FS_STAGE
 
@@ -500,6 +529,11 @@ int ng_of(int path, int dp) { return path == PATH_MFMA_F32 ? dp / 8 : dp / 16; }
 // The vector path uses 4 rows per lane when there are enough rows to fill the
 // GPU, else 1.
 int valu_rows_per_lane(int n_rows) { return n_rows >= 65536 ? 4 : 1; }
+
+int lse_max_keys_per_split(int path, int dp) {
+    if (path == PATH_VALU) return 1 << 30;
+    return kps_max_for(ng_of(path, dp));
+}
 
 int lse_rows_per_block(int path, int dp, int n_rows) {
     if (path == PATH_VALU) return 256 * valu_rows_per_lane(n_rows);
