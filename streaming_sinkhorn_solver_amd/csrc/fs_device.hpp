@@ -24,21 +24,26 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
-// One wave-wide 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4):
-// lane i's 16 bytes at `src` land at LDS byte address `lds_base + 16*i`
-// (`lds_base` must be wave-uniform).  Issued as inline assembly so the
-// compiler does not model it as an LDS store: the caller owns completion and
-// waits for it explicitly (s_waitcnt vmcnt) before a barrier publishes it.
-__device__ __forceinline__ void dma_to_lds16(const void* src, const void* lds_base) {
-    const uint32_t lds =
-        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)lds_base);
+// One wave-wide 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4
+// in its scalar-base form): lane i's 16 bytes at `gbase + voff_i` land at LDS
+// byte address `lds_dst + 16*i`.  `gbase` and `lds_dst` must be wave-uniform.
+// Issued as inline assembly so the compiler does not model it as an LDS
+// store: the caller owns completion and waits for it explicitly (s_waitcnt
+// vmcnt) before a barrier publishes it.  M0 (the LDS destination register of
+// the instruction) is saved and restored around it.  The LDS address of a
+// __shared__ object is the low half of its generic address.
+__device__ __forceinline__ void dma_to_lds16(const char* gbase, uint32_t voff, const void* lds_dst) {
+    const uint32_t lds = (uint32_t)(uintptr_t)lds_dst;
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
-        : "memory", "m0");
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(gbase)
+        : "memory");
 }
 
 // Combine two partial base-2 log-sum-exp states (M1, s1) and (M2, s2), each

@@ -26,6 +26,8 @@
 //    matrix-core rate (2 n m d flops per half-step).
 // Both can split the key range across workgroups (partial (max, sum) pairs
 // merged afterwards in a fixed order), so results are deterministic.
+#include <type_traits>
+
 #include "fs_device.hpp"
 #include "fs_internal.h"
 
@@ -140,15 +142,27 @@ constexpr bool kPingPong = false;
 #else
 constexpr bool kPingPong = true;  // opposite MFMA/epilogue order in the two wave halves
 #endif
-#ifdef FS_INTERLEAVE
-constexpr bool kInterleave = true;
+#ifndef FS_APIPE
+#define FS_APIPE 8
+#endif
+constexpr int kAPipe = FS_APIPE;  // operand fragments in flight, one wave per SIMD
+#ifndef FS_APIPE8
+#define FS_APIPE8 4
+#endif
+constexpr int kAPipe8 = FS_APIPE8;  // operand fragments in flight, two waves per SIMD
+#ifdef FS_NO_PIN_SCHED
+constexpr bool kPinSched = false;
 #else
-constexpr bool kInterleave = false;
+constexpr bool kPinSched = true;
+#endif
+#ifndef FS_VALU_PER_SLOT
+#define FS_VALU_PER_SLOT 6
+#endif
+constexpr int kValuPerSlot = FS_VALU_PER_SLOT;  // epilogue instructions per operand fragment
+#ifndef FS_VALU_MASK
+#define FS_VALU_MASK 0x002
 #endif
 
-// Scheduling hint: spread the epilogue's vector instructions and the operand
-// fetches between the N matrix instructions of a stage (1 MFMA, 1 LDS read,
-// 5 VALU, repeated).
 // Workgroup barrier without the memory fence of __syncthreads(): only this
 // wave's LDS operations are waited for.  (The fence would also wait for every
 // outstanding global->LDS tile load, serialising the load pipeline; the
@@ -157,15 +171,6 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int N>
-__device__ __forceinline__ void interleave_hint() {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-}
 template <int OP>
 __device__ __forceinline__ f32x16 mfma_step(const uint4& av, const uint4& bv, f32x16 acc) {
     if constexpr (OP == OP_BF16) {
@@ -201,12 +206,23 @@ constexpr int kps_max_for(int ng) {
 // 2*NG chunks; dp = 16*NG for 2-byte types, 8*NG for fp32).  QB: 32-row
 // blocks per wave.  WAVES: waves per workgroup.  NBUF: key-tile buffers.
 //
-// Software pipeline over 32-key tiles, one barrier per tile; stage t:
-//   (1) direct global->LDS loads (global_load_lds_dwordx4) of tile t+NBUF into
-//       the buffer tile t used, so every tile has NBUF-1 stages to arrive;
-//   (2) the MFMAs of tile t+1 (A operand read from LDS, B resident);
-//   (3) the online-LSE epilogue of tile t, independent of (2);
-//   (4) wait until tile t+2 has landed (later tiles stay in flight), barrier.
+// Software pipeline over 32-key tiles with one workgroup barrier per tile.
+// Stage s:
+//   (1) direct global->LDS loads (global_load_lds_dwordx4) of tile s+NBUF-1
+//       into the buffer tile s-1 used, so a tile has NBUF-1 stages to arrive;
+//   (2) the scores of tile s: matrix instructions with the resident row block
+//       as one operand and key fragments streamed from LDS through a ring of
+//       AP registers as the other;
+//   (3) an online-LSE epilogue: of tile s right after (2), or of tile s-1
+//       before or threaded through (2) (see below);
+//   (4) wait until tile s+1 has landed (later tiles stay in flight), barrier.
+// Eight waves (two per SIMD): the two halves of the workgroup run opposite
+// orders -- waves 0-3 do scores then epilogue of tile s, waves 4-7 the
+// epilogue of tile s-1 then the scores of tile s -- so that each SIMD's matrix
+// pipe is fed by one wave while the other runs vector/transcendental work,
+// and every wave has a single accumulator set live during its matrix phase.
+// Four waves (one per SIMD, larger row blocks): the epilogue of tile s-1 is
+// threaded between the matrix instructions of tile s in four fenced chunks.
 // The key biases of the workgroup's whole key range are computed into LDS
 // once, up front.  Tiles are stored XOR-swizzled (chunk c of key m at
 // m*CPR + (c ^ (m & SWZ))) so that one operand fetch hits distinct banks.
@@ -221,12 +237,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     constexpr int MIN_INSTR = TILE_INSTR / WAVES;    // loads per tile issued by every wave
     constexpr int NBUF = nbuf_for(NG);
     constexpr int KPS_MAX = kps_max_for(NG);
-#ifndef FS_SWZ_COLS
-#define FS_SWZ_COLS 16
-#endif
-    constexpr int SWZ = CPR >= FS_SWZ_COLS ? FS_SWZ_COLS - 1 : CPR - 1;
-    constexpr int JB = SWZ + 1 < 2 * NG ? (SWZ + 1) / 2 : NG;  // chunk-pair classes per batch
-    constexpr int KB = NG / JB;                                  // batches per row
+    constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
+    constexpr int JB = SWZ + 1 < 2 * NG ? (SWZ + 1) / 2 : NG;  // chunk-pair classes
+    constexpr int APW = WAVES == 8 ? kAPipe8 : kAPipe;
+    constexpr int AP = APW < NG ? APW : NG;          // operand fragments in flight
+    constexpr int MF_PER_FRAG = QB * (OP == OP_F32 ? 4 : 1);
+    static_assert(NBUF == 2 || NBUF == 4, "pipeline depth");
 
     __shared__ __attribute__((aligned(16))) uint4 kbuf0[TILE_CHUNKS];
     __shared__ __attribute__((aligned(16))) uint4 kbuf1[TILE_CHUNKS];
@@ -237,7 +253,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 31;  // query row of the B block / key row of the A block
     const int h = lane >> 5;   // lane half: contraction slots 8h..8h+7 of each 16
 
@@ -250,17 +266,29 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 
     // (1) tile k -> LDS buffer `dst` (64-chunk slice L of the tile per
     // wave-instruction; lane `lane` fetches the chunk that lands at position
-    // L*64+lane of the swizzled layout).
+    // L*64+lane of the swizzled layout).  For rows of >= 64 chunks a slice
+    // lies in one key row m, so the source is a uniform base plus the lane's
+    // swizzled chunk, (lane ^ (m & SWZ)) * 16, formed at issue time.
+    const uint32_t lane16 = (uint32_t)lane * 16u;
     auto issue_tile = [&](int k, uint4* dst) __attribute__((always_inline)) {
         const char* tbase = keys + (int64_t)(j0 + k * kKeyTile) * ROW_BYTES;
 #pragma unroll
         for (int l = 0; l < INSTR_PER_WAVE; ++l) {
             const int L = l * WAVES + wave;
             if (TILE_INSTR % WAVES == 0 || L < TILE_INSTR) {
-                const int P = L * 64 + lane;
-                const int m = P / CPR, cp = P % CPR;
-                const char* src = tbase + m * ROW_BYTES + (cp ^ (m & SWZ)) * 16;
-                dma_to_lds16(src, dst + L * 64);
+                if constexpr (CPR >= 64) {
+                    constexpr int IPR = CPR / 64;  // slices per key row
+                    const int m = L / IPR;
+                    uint32_t sw = (uint32_t)(m & SWZ) * 16u;
+                    asm volatile("" : "+s"(sw));  // no hoisted per-lane offsets
+                    dma_to_lds16(tbase + m * ROW_BYTES + (L % IPR) * 1024, lane16 ^ sw,
+                                 dst + L * 64);
+                } else {
+                    const int P = L * 64 + lane;
+                    const int m = P / CPR, cp = P % CPR;
+                    dma_to_lds16(tbase, (uint32_t)(m * ROW_BYTES + (cp ^ (m & SWZ)) * 16),
+                                 dst + L * 64);
+                }
             }
         }
     };
@@ -268,15 +296,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         return i == 0 ? kbuf0 : i == 1 ? kbuf1 : i == 2 ? kbuf2 : kbuf3;
     };
 
-    // prologue: the first NBUF tiles in flight; key biases of the whole range
+    // prologue: tiles 0..NBUF-2 in flight (every split holds at least one
+    // key; the guard keeps an empty range from reading before it), the key
+    // biases of the whole range, the resident row block
+    if (ntiles > 0) {
 #pragma unroll
-    for (int k = 0; k < NBUF; ++k)
-        if (k < ntiles) issue_tile(k, buf(k));
+        for (int k = 0; k < NBUF - 1; ++k) issue_tile(min(k, ntiles - 1), buf(k));
+    }
     for (int k = tid; k < ntiles * kKeyTile; k += NT) {
         const int j = j0 + k;
         bkeys[k] = j < j1 ? fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]) : -INFINITY;
     }
-    // Resident row block: lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln.
+    // lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln
     uint4 q[QB][NG];
     {
         const char* __restrict__ rows = (const char*)a.rows;
@@ -286,6 +317,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) q[qb][g] = *(const uint4*)(rp + g * 32);
         }
+        // Consume the block here, so that the compiler's own waits for these
+        // loads are placed in the prologue: left to their first use inside
+        // the tile loop they would be re-executed every tile, and there they
+        // would also wait for the tile loads in flight.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                asm volatile("" ::"v"(q[qb][g].x), "v"(q[qb][g].y), "v"(q[qb][g].z), "v"(q[qb][g].w));
     }
 
     float M[QB], S[QB];
@@ -295,35 +335,77 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         S[qb] = 0.f;
     }
 
-    // (2) scores of the tile in `src` for all QB row blocks.  Operand chunk
-    // 2g+h of key ln sits at ln*CPR + ((2g+h) ^ (ln & SWZ)); with g = JB*k + j
-    // that is a per-lane base for each j plus the immediate offset 2*JB*k
-    // chunks, so a batch of JB fragments is fetched before its MFMAs.
+    // (2) scores of one tile for all QB row blocks.  Operand chunk 2g+h of key
+    // ln sits at ln*CPR + ((2g+h) ^ (ln & SWZ)); with g = JB*k + j that is a
+    // per-lane base for each j plus the immediate offset 2*JB*k chunks.  The
+    // fragments are software-pipelined: a ring of AP operand registers keeps
+    // AP LDS reads in flight ahead of the matrix instruction that consumes
+    // them, and the schedule is pinned to that order (left alone, the
+    // scheduler sinks each read next to its use and every matrix instruction
+    // waits out a full LDS round trip).
     int abase[JB];
 #pragma unroll
     for (int j = 0; j < JB; ++j) abase[j] = (ln * CPR + ((2 * j + h) ^ (ln & SWZ))) * 16;
-    auto mfma_tile = [&](const uint4* src, f32x16 (&acc)[QB]) __attribute__((always_inline)) {
+    auto frag_off = [&](int g) __attribute__((always_inline)) {
+        return abase[g % JB] + (g / JB) * (2 * JB * 16);
+    };
+    // start a tile: clear the accumulators, put the first AP fragments in flight
+    auto ring_begin = [&](const char* kb, uint4 (&av)[AP], f32x16 (&acc)[QB])
+                          __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][r] = 0.f;
-        const char* kb = (const char*)src;
 #pragma unroll
-        for (int k = 0; k < KB; ++k) {
-            uint4 av[JB];
+        for (int g = 0; g < AP; ++g) av[g] = *(const uint4*)(kb + frag_off(g));
+    };
+    // fragments [G0, G1): their matrix instructions, each followed by the
+    // read that refills its ring slot with fragment g + AP
+    auto ring_steps = [&](const char* kb, uint4 (&av)[AP], f32x16 (&acc)[QB], auto g0_c,
+                          auto g1_c) __attribute__((always_inline)) {
+        constexpr int G0 = decltype(g0_c)::value;
+        constexpr int G1 = decltype(g1_c)::value;
 #pragma unroll
-            for (int j = 0; j < JB; ++j) av[j] = *(const uint4*)(kb + abase[j] + k * (2 * JB * 16));
+        for (int g = G0; g < G1; ++g) {
 #pragma unroll
-            for (int j = 0; j < JB; ++j)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    acc[qb] = mfma_step<OP>(av[j], q[qb][JB * k + j], acc[qb]);
+            for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma_step<OP>(av[g % AP], q[qb][g], acc[qb]);
+            if (g + AP < NG) av[g % AP] = *(const uint4*)(kb + frag_off(g + AP));
         }
     };
+    // Pins the order of the current scheduling region for fragments
+    // [G0, G1): (the ring's first AP reads if FIRST), then per fragment its
+    // matrix instructions, its refill read and up to VPS vector instructions.
+    auto pin_steps = [&](auto g0_c, auto g1_c, auto first_c, auto vps_c)
+                         __attribute__((always_inline)) {
+        constexpr int G0 = decltype(g0_c)::value;
+        constexpr int G1 = decltype(g1_c)::value;
+        constexpr bool FIRST = decltype(first_c)::value;
+        constexpr int VPS = decltype(vps_c)::value;
+        if constexpr (kPinSched) {
+            if constexpr (FIRST) __builtin_amdgcn_sched_group_barrier(0x100, AP, 0);
+#pragma unroll
+            for (int g = G0; g < G1; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, MF_PER_FRAG, 0);
+                if (g + AP < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (VPS > 0) __builtin_amdgcn_sched_group_barrier(FS_VALU_MASK, VPS, 0);
+            }
+        }
+    };
+    using Zero = std::integral_constant<int, 0>;
+    using NGc = std::integral_constant<int, NG>;
+    // the whole score tile in one pinned region
+    auto mfma_tile = [&](const uint4* src, f32x16 (&acc)[QB]) __attribute__((always_inline)) {
+        const char* kb = (const char*)src;
+        uint4 av[AP];
+        ring_begin(kb, av, acc);
+        ring_steps(kb, av, acc, Zero{}, NGc{});
+        pin_steps(Zero{}, NGc{}, std::true_type{}, Zero{});
+    };
+
     // (3) online LSE of one tile.  Accumulator register r of lane (ln, h) is
-    // the score of row ln with key 8*(r/4) + 4*h + (r%4) of the tile.
-    auto epilogue = [&](const f32x16 (&acc)[QB], const float* bb) __attribute__((always_inline)) {
-        float bv[16];
+    // the score of row ln with key 8*(r/4) + 4*h + (r%4) of the tile; the
+    // tile's key biases are read in that order.
+    auto load_bias = [&](const float* bb, float (&bv)[16]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             const float4 v = *(const float4*)&bb[8 * qq + 4 * h];
@@ -332,74 +414,156 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
             bv[4 * qq + 2] = v.z;
             bv[4 * qq + 3] = v.w;
         }
+    };
+    // In parts, so it can be spread over a tile's matrix work: the biased
+    // scores, the tile maximum and the rescaled running sum; then the
+    // exponentials of scores [R0, R1); then the commit of the new state.
+    struct EpiState {
+        float z[QB][16];
+        float Mn[QB];
+        float s[QB];
+    };
+    auto epi_scores = [&](const f32x16 (&acc)[QB], const float (&bv)[16], EpiState& e)
+                          __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float z[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = fmaf(acc[qb][r], a.c_score, bv[r]);
-            float tmax = fmaxf(z[0], z[1]);
+            for (int r = 0; r < 16; ++r) e.z[qb][r] = fmaf(acc[qb][r], a.c_score, bv[r]);
+            float tmax = fmaxf(e.z[qb][0], e.z[qb][1]);
 #pragma unroll
-            for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
-            const float Mn = fmaxf(M[qb], tmax);
-            float s = S[qb] * ex2(M[qb] - Mn);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s += ex2(z[r] - Mn);
-            S[qb] = s;
-            M[qb] = Mn;
+            for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, e.z[qb][r]);
+            e.Mn[qb] = fmaxf(M[qb], tmax);
+            e.s[qb] = S[qb] * ex2(M[qb] - e.Mn[qb]);
         }
     };
-    // (4) wait until at most `newer` tiles' loads (issued after tile t+2's)
-    // are outstanding for this wave.
-    auto wait_tiles = [&](int newer) __attribute__((always_inline)) {
-        if (MIN_INSTR == 0 || newer <= 0) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        } else if (newer == 1) {
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(MIN_INSTR) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * MIN_INSTR) : "memory");
+    auto epi_exps = [&](EpiState& e, auto r0_c, auto r1_c) __attribute__((always_inline)) {
+        constexpr int R0 = decltype(r0_c)::value;
+        constexpr int R1 = decltype(r1_c)::value;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = R0; r < R1; ++r) e.s[qb] += ex2(e.z[qb][r] - e.Mn[qb]);
+    };
+    auto epi_commit = [&](EpiState& e) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            S[qb] = e.s[qb];
+            M[qb] = e.Mn[qb];
+            // keep the epilogue ahead of the stage's load wait and barrier
+            asm volatile("" : "+v"(S[qb]), "+v"(M[qb]));
         }
+    };
+    auto epilogue = [&](const f32x16 (&acc)[QB], const float* bb) __attribute__((always_inline)) {
+        float bv[16];
+        load_bias(bb, bv);
+        EpiState e;
+        epi_scores(acc, bv, e);
+        epi_exps(e, Zero{}, std::integral_constant<int, 16>{});
+        epi_commit(e);
+    };
+    // One wave per SIMD: the scores of one tile into `acc` and the epilogue
+    // of the previous tile (`prev`, biases `bv`) in four fenced chunks, each
+    // pinned to alternate matrix instructions, operand reads and epilogue
+    // instructions.
+    auto fused_chunks = [&](const uint4* src, f32x16 (&acc)[QB], const f32x16 (&prev)[QB],
+                            const float (&bv)[16]) __attribute__((always_inline)) {
+        constexpr int C = NG >= 4 ? NG / 4 : 1;  // fragments per chunk
+        using C1 = std::integral_constant<int, (C < NG ? C : NG)>;
+        using C2 = std::integral_constant<int, (2 * C < NG ? 2 * C : NG)>;
+        using C3 = std::integral_constant<int, (3 * C < NG ? 3 * C : NG)>;
+        using V = std::integral_constant<int, kValuPerSlot>;
+        const char* kb = (const char*)src;
+        uint4 av[AP];
+        EpiState e;
+        ring_begin(kb, av, acc);
+        ring_steps(kb, av, acc, Zero{}, C1{});
+        epi_scores(prev, bv, e);
+        pin_steps(Zero{}, C1{}, std::true_type{}, V{});
+        __builtin_amdgcn_sched_barrier(0);
+        ring_steps(kb, av, acc, C1{}, C2{});
+        epi_exps(e, Zero{}, std::integral_constant<int, 6>{});
+        pin_steps(C1{}, C2{}, std::false_type{}, V{});
+        __builtin_amdgcn_sched_barrier(0);
+        ring_steps(kb, av, acc, C2{}, C3{});
+        epi_exps(e, std::integral_constant<int, 6>{}, std::integral_constant<int, 11>{});
+        pin_steps(C2{}, C3{}, std::false_type{}, V{});
+        __builtin_amdgcn_sched_barrier(0);
+        ring_steps(kb, av, acc, C3{}, NGc{});
+        epi_exps(e, std::integral_constant<int, 11>{}, std::integral_constant<int, 16>{});
+        pin_steps(C3{}, NGc{}, std::false_type{}, V{});
+        epi_commit(e);
+    };
+    // (4) wait until at most `newer` tiles' loads (issued after tile s+1's)
+    // are outstanding for this wave.
+    auto wait_tiles = [&](auto newer_c) __attribute__((always_inline)) {
+        constexpr int NEWER = decltype(newer_c)::value;
+        if constexpr (MIN_INSTR == 0 || NEWER <= 0)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NEWER * MIN_INSTR) : "memory");
     };
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // waves whose epilogue runs one tile behind their scores
+    const bool lagging = WAVES != 8 || (kPingPong && wave >= 4);
+    // One stage (tile s in buffer slot I = s % NBUF; the load of tile
+    // s+NBUF-1 goes to slot I-1, which every wave finished reading before the
+    // previous barrier).  Past the end the load is clamped to the last tile:
+    // a redundant in-bounds copy into a slot that is never read again, which
+    // keeps the wait count constant.
+    auto stage = [&](int s, auto i_c, f32x16 (&acc)[QB], f32x16 (&prev)[QB])
+                     __attribute__((always_inline)) {
+        constexpr int I = decltype(i_c)::value;
+        issue_tile(min(s + NBUF - 1, ntiles - 1), buf((I + NBUF - 1) % NBUF));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (WAVES == 8) {
+            if (!lagging) {
+                mfma_tile(buf(I), acc);
+                __builtin_amdgcn_sched_barrier(0);
+                epilogue(acc, bkeys + s * kKeyTile);
+            } else {
+                if (s > 0) epilogue(prev, bkeys + (s - 1) * kKeyTile);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_tile(buf(I), acc);
+            }
+        } else {
+            if (s > 0) {
+                float bv[16];
+                load_bias(bkeys + (s - 1) * kKeyTile, bv);
+                __builtin_amdgcn_sched_barrier(0);
+                fused_chunks(buf(I), acc, prev, bv);
+            } else {
+                mfma_tile(buf(I), acc);
+            }
+        }
+        wait_tiles(std::integral_constant<int, NBUF - 2>{});
+        stage_barrier();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
     f32x16 accA[QB], accB[QB];
-    mfma_tile(kbuf0, accA);
-    // Every wave must be done reading tile 0 before stage 0 reloads kbuf0.
-    __syncthreads();
-
-    // one pipeline stage (tile t = ts, buffer slot I = ts % NBUF)
-#define FS_STAGE(t_, I, CUR, NXT)                                                  \
-    do {                                                                          \
-        const int ts = (t_);                                                      \
-        if (ts + NBUF < ntiles) issue_tile(ts + NBUF, buf(I));                    \
-        /* The MFMAs run unconditionally (stale buffer on the last tile, result \
-           unused).  With two waves per SIMD the halves of the workgroup do the  \
-           two parts in opposite order, so each SIMD's matrix pipe is fed by one \
-           wave while the other runs its exp/VALU epilogue. */                    \
-        if (kPingPong && WAVES == 8 && wave >= 4) {                               \
-            epilogue(CUR, bkeys + ts * kKeyTile);                                 \
-            __builtin_amdgcn_sched_barrier(0);                                    \
-            mfma_tile(buf(((I) + 1) % NBUF), NXT);                                \
-        } else {                                                                  \
-            mfma_tile(buf(((I) + 1) % NBUF), NXT);                                \
-            if (kPingPong && WAVES == 8) __builtin_amdgcn_sched_barrier(0);       \
-            epilogue(CUR, bkeys + ts * kKeyTile);                                 \
-        }                                                                         \
-        /* tiles issued after tile ts+2: ts+3 .. min(ts+NBUF, ntiles-1) */        \
-        wait_tiles(min(ts + NBUF, ntiles - 1) - (ts + 2));                        \
-        stage_barrier();                                                          \
-    } while (0)
-
     for (int t = 0; t < ntiles; t += NBUF) {
-        FS_STAGE(t, 0, accA, accB);
-        if (t + 1 < ntiles) FS_STAGE(t + 1, 1, accB, accA);
-        if (NBUF > 2) {
-            if (t + 2 < ntiles) FS_STAGE(t + 2, 2, accA, accB);
-            if (t + 3 < ntiles) FS_STAGE(t + 3, 3, accB, accA);
+        stage(t, I0{}, accA, accB);
+        if (t + 1 < ntiles) stage(t + 1, I1{}, accB, accA);
+        if constexpr (NBUF > 2) {
+            if (t + 2 < ntiles) stage(t + 2, I2{}, accA, accB);
+            if (t + 3 < ntiles) stage(t + 3, I3{}, accB, accA);
         }
     }
-#undef FS_STAGE
+    // the lagging waves' epilogue of the last tile
+    if (lagging && ntiles > 0) {
+        const float* bb = bkeys + (ntiles - 1) * kKeyTile;
+        if ((ntiles - 1) % 2 == 0)
+            epilogue(accA, bb);
+        else
+            epilogue(accB, bb);
+    }
+    // No tile load may still be writing this workgroup's LDS when it exits.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Merge the two lane halves (same row, disjoint keys) and finish.
     float resid = 0.f;
