@@ -303,9 +303,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 #pragma unroll
         for (int k = 0; k < NBUF - 1; ++k) issue_tile(min(k, ntiles - 1), buf(k));
     }
+    // Key bias in dot-product units: the base-2 score of a pair is
+    // c_score * (x~.y~ + bk) with bk = (g - |y~|^2)/2 + log2(b)/(2 c_bias)
+    // (c_score = 2 c_bias exactly), so bk can seed the accumulator.
+    const float half_inv_cb = 0.5f / a.c_bias;
     for (int k = tid; k < ntiles * kKeyTile; k += NT) {
         const int j = j0 + k;
-        bkeys[k] = j < j1 ? fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]) : -INFINITY;
+        bkeys[k] = j < j1 ? fmaf(a.key_lw2[j], half_inv_cb, 0.5f * (a.key_pot[j] - a.key_nrm[j]))
+                          : -INFINITY;
     }
     // lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln
     uint4 q[QB][NG];
@@ -349,13 +354,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     auto frag_off = [&](int g) __attribute__((always_inline)) {
         return abase[g % JB] + (g / JB) * (2 * JB * 16);
     };
-    // start a tile: clear the accumulators, put the first AP fragments in flight
-    auto ring_begin = [&](const char* kb, uint4 (&av)[AP], f32x16 (&acc)[QB])
+    // Start a tile: seed the accumulators with the tile's key biases
+    // (accumulator register r of lane (ln, h) holds the pair of row ln with
+    // key 8*(r/4) + 4*h + (r%4) of the tile) and put the first AP fragments
+    // in flight.
+    auto ring_begin = [&](const char* kb, const float* bb, uint4 (&av)[AP], f32x16 (&acc)[QB])
                           __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][r] = 0.f;
+            for (int qq = 0; qq < 4; ++qq) {
+                const float4 v = *(const float4*)&bb[8 * qq + 4 * h];
+                acc[qb][4 * qq + 0] = v.x;
+                acc[qb][4 * qq + 1] = v.y;
+                acc[qb][4 * qq + 2] = v.z;
+                acc[qb][4 * qq + 3] = v.w;
+            }
 #pragma unroll
         for (int g = 0; g < AP; ++g) av[g] = *(const uint4*)(kb + frag_off(g));
     };
@@ -382,7 +396,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         constexpr bool FIRST = decltype(first_c)::value;
         constexpr int VPS = decltype(vps_c)::value;
         if constexpr (kPinSched) {
-            if constexpr (FIRST) __builtin_amdgcn_sched_group_barrier(0x100, AP, 0);
+            if constexpr (FIRST) __builtin_amdgcn_sched_group_barrier(0x100, AP + 4 * QB, 0);
 #pragma unroll
             for (int g = G0; g < G1; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, MF_PER_FRAG, 0);
@@ -393,56 +407,45 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     };
     using Zero = std::integral_constant<int, 0>;
     using NGc = std::integral_constant<int, NG>;
-    // the whole score tile in one pinned region
-    auto mfma_tile = [&](const uint4* src, f32x16 (&acc)[QB]) __attribute__((always_inline)) {
+    // the whole score tile (key biases `bb`) in one pinned region
+    auto mfma_tile = [&](const uint4* src, const float* bb, f32x16 (&acc)[QB])
+                         __attribute__((always_inline)) {
         const char* kb = (const char*)src;
         uint4 av[AP];
-        ring_begin(kb, av, acc);
+        ring_begin(kb, bb, av, acc);
         ring_steps(kb, av, acc, Zero{}, NGc{});
         pin_steps(Zero{}, NGc{}, std::true_type{}, Zero{});
     };
 
-    // (3) online LSE of one tile.  Accumulator register r of lane (ln, h) is
-    // the score of row ln with key 8*(r/4) + 4*h + (r%4) of the tile; the
-    // tile's key biases are read in that order.
-    auto load_bias = [&](const float* bb, float (&bv)[16]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const float4 v = *(const float4*)&bb[8 * qq + 4 * h];
-            bv[4 * qq + 0] = v.x;
-            bv[4 * qq + 1] = v.y;
-            bv[4 * qq + 2] = v.z;
-            bv[4 * qq + 3] = v.w;
-        }
-    };
-    // In parts, so it can be spread over a tile's matrix work: the biased
-    // scores, the tile maximum and the rescaled running sum; then the
-    // exponentials of scores [R0, R1); then the commit of the new state.
+    // (3) online LSE of one tile from its accumulators (scores c_score*acc,
+    // c_score > 0).  In parts, so it can be spread over a tile's matrix work:
+    // the tile maximum and the rescaled running sum; then the exponentials
+    // of scores [R0, R1); then the commit of the new state.  A lane that has
+    // seen no key yet (every score -inf) keeps the empty state.
     struct EpiState {
-        float z[QB][16];
         float Mn[QB];
+        float sh[QB];
         float s[QB];
     };
-    auto epi_scores = [&](const f32x16 (&acc)[QB], const float (&bv)[16], EpiState& e)
-                          __attribute__((always_inline)) {
+    auto epi_max = [&](const f32x16 (&acc)[QB], EpiState& e) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
+            float tmax = fmaxf(acc[qb][0], acc[qb][1]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) e.z[qb][r] = fmaf(acc[qb][r], a.c_score, bv[r]);
-            float tmax = fmaxf(e.z[qb][0], e.z[qb][1]);
-#pragma unroll
-            for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, e.z[qb][r]);
-            e.Mn[qb] = fmaxf(M[qb], tmax);
-            e.s[qb] = S[qb] * ex2(M[qb] - e.Mn[qb]);
+            for (int r = 2; r < 16; ++r) tmax = fmaxf(tmax, acc[qb][r]);
+            e.Mn[qb] = fmaxf(M[qb], a.c_score * tmax);
+            e.sh[qb] = e.Mn[qb] == -INFINITY ? 0.f : e.Mn[qb];
+            e.s[qb] = S[qb] * ex2(M[qb] - e.sh[qb]);
         }
     };
-    auto epi_exps = [&](EpiState& e, auto r0_c, auto r1_c) __attribute__((always_inline)) {
+    auto epi_exps = [&](const f32x16 (&acc)[QB], EpiState& e, auto r0_c, auto r1_c)
+                        __attribute__((always_inline)) {
         constexpr int R0 = decltype(r0_c)::value;
         constexpr int R1 = decltype(r1_c)::value;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int r = R0; r < R1; ++r) e.s[qb] += ex2(e.z[qb][r] - e.Mn[qb]);
+            for (int r = R0; r < R1; ++r) e.s[qb] += ex2(fmaf(acc[qb][r], a.c_score, -e.sh[qb]));
     };
     auto epi_commit = [&](EpiState& e) __attribute__((always_inline)) {
 #pragma unroll
@@ -453,20 +456,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
             asm volatile("" : "+v"(S[qb]), "+v"(M[qb]));
         }
     };
-    auto epilogue = [&](const f32x16 (&acc)[QB], const float* bb) __attribute__((always_inline)) {
-        float bv[16];
-        load_bias(bb, bv);
+    auto epilogue = [&](const f32x16 (&acc)[QB]) __attribute__((always_inline)) {
         EpiState e;
-        epi_scores(acc, bv, e);
-        epi_exps(e, Zero{}, std::integral_constant<int, 16>{});
+        epi_max(acc, e);
+        epi_exps(acc, e, Zero{}, std::integral_constant<int, 16>{});
         epi_commit(e);
     };
-    // One wave per SIMD: the scores of one tile into `acc` and the epilogue
-    // of the previous tile (`prev`, biases `bv`) in four fenced chunks, each
+    // One wave per SIMD: the scores of one tile (biases `bb`) into `acc` and
+    // the epilogue of the previous tile (`prev`) in four fenced chunks, each
     // pinned to alternate matrix instructions, operand reads and epilogue
     // instructions.
-    auto fused_chunks = [&](const uint4* src, f32x16 (&acc)[QB], const f32x16 (&prev)[QB],
-                            const float (&bv)[16]) __attribute__((always_inline)) {
+    auto fused_chunks = [&](const uint4* src, const float* bb, f32x16 (&acc)[QB],
+                            const f32x16 (&prev)[QB]) __attribute__((always_inline)) {
         constexpr int C = NG >= 4 ? NG / 4 : 1;  // fragments per chunk
         using C1 = std::integral_constant<int, (C < NG ? C : NG)>;
         using C2 = std::integral_constant<int, (2 * C < NG ? 2 * C : NG)>;
@@ -475,26 +476,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         const char* kb = (const char*)src;
         uint4 av[AP];
         EpiState e;
-        ring_begin(kb, av, acc);
+        ring_begin(kb, bb, av, acc);
         ring_steps(kb, av, acc, Zero{}, C1{});
-        epi_scores(prev, bv, e);
+        epi_max(prev, e);
         pin_steps(Zero{}, C1{}, std::true_type{}, V{});
         __builtin_amdgcn_sched_barrier(0);
         ring_steps(kb, av, acc, C1{}, C2{});
-        epi_exps(e, Zero{}, std::integral_constant<int, 6>{});
+        epi_exps(prev, e, Zero{}, std::integral_constant<int, 6>{});
         pin_steps(C1{}, C2{}, std::false_type{}, V{});
         __builtin_amdgcn_sched_barrier(0);
         ring_steps(kb, av, acc, C2{}, C3{});
-        epi_exps(e, std::integral_constant<int, 6>{}, std::integral_constant<int, 11>{});
+        epi_exps(prev, e, std::integral_constant<int, 6>{}, std::integral_constant<int, 11>{});
         pin_steps(C2{}, C3{}, std::false_type{}, V{});
         __builtin_amdgcn_sched_barrier(0);
         ring_steps(kb, av, acc, C3{}, NGc{});
-        epi_exps(e, std::integral_constant<int, 11>{}, std::integral_constant<int, 16>{});
+        epi_exps(prev, e, std::integral_constant<int, 11>{}, std::integral_constant<int, 16>{});
         pin_steps(C3{}, NGc{}, std::false_type{}, V{});
         epi_commit(e);
     };
-    // (4) wait until at most `newer` tiles' loads (issued after tile s+1's)
-    // are outstanding for this wave.
+    // (4) wait until at most `newer` tiles' loads are outstanding for this
+    // wave (loads complete in order, so the older tiles have landed).
     auto wait_tiles = [&](auto newer_c) __attribute__((always_inline)) {
         constexpr int NEWER = decltype(newer_c)::value;
         if constexpr (MIN_INSTR == 0 || NEWER <= 0)
@@ -518,25 +519,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         constexpr int I = decltype(i_c)::value;
         issue_tile(min(s + NBUF - 1, ntiles - 1), buf((I + NBUF - 1) % NBUF));
         __builtin_amdgcn_sched_barrier(0);
+        const float* bb = bkeys + s * kKeyTile;
         if constexpr (WAVES == 8) {
             if (!lagging) {
-                mfma_tile(buf(I), acc);
+                mfma_tile(buf(I), bb, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                epilogue(acc, bkeys + s * kKeyTile);
+                epilogue(acc);
             } else {
-                if (s > 0) epilogue(prev, bkeys + (s - 1) * kKeyTile);
+                if (s > 0) epilogue(prev);
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_tile(buf(I), acc);
+                mfma_tile(buf(I), bb, acc);
             }
         } else {
-            if (s > 0) {
-                float bv[16];
-                load_bias(bkeys + (s - 1) * kKeyTile, bv);
-                __builtin_amdgcn_sched_barrier(0);
-                fused_chunks(buf(I), acc, prev, bv);
-            } else {
-                mfma_tile(buf(I), acc);
-            }
+            if (s > 0)
+                fused_chunks(buf(I), bb, acc, prev);
+            else
+                mfma_tile(buf(I), bb, acc);
         }
         wait_tiles(std::integral_constant<int, NBUF - 2>{});
         stage_barrier();
@@ -556,11 +554,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     }
     // the lagging waves' epilogue of the last tile
     if (lagging && ntiles > 0) {
-        const float* bb = bkeys + (ntiles - 1) * kKeyTile;
         if ((ntiles - 1) % 2 == 0)
-            epilogue(accA, bb);
+            epilogue(accA);
         else
-            epilogue(accB, bb);
+            epilogue(accB);
     }
     // No tile load may still be writing this workgroup's LDS when it exits.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
