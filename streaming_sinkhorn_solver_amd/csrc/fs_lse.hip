@@ -171,8 +171,8 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int OP>
-__device__ __forceinline__ f32x16 mfma_step(const uint4& av, const uint4& bv, f32x16 acc) {
+template <int OP, class TA, class TB>
+__device__ __forceinline__ f32x16 mfma_step(const TA& av, const TB& bv, f32x16 acc) {
     if constexpr (OP == OP_BF16) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                        __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
@@ -312,25 +312,34 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         bkeys[k] = j < j1 ? fmaf(a.key_lw2[j], half_inv_cb, 0.5f * (a.key_pot[j] - a.key_nrm[j]))
                           : -INFINITY;
     }
-    // lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln
-    uint4 q[QB][NG];
+    // lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln.  With one wave
+    // per SIMD and a block of more than 128 registers it is placed in the
+    // accumulation registers (AGPRs), which the matrix instructions read
+    // directly, leaving the vector registers to the accumulators, operand
+    // ring and epilogue.
+    constexpr bool Q_AGPR = WAVES == 4 && QB * NG * 4 > 128;
+    u32x4 q[QB][NG];
     {
         const char* __restrict__ rows = (const char*)a.rows;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const char* rp = rows + (int64_t)(row0 + qb * 32 + ln) * ROW_BYTES + h * 16;
 #pragma unroll
-            for (int g = 0; g < NG; ++g) q[qb][g] = *(const uint4*)(rp + g * 32);
+            for (int g = 0; g < NG; ++g) {
+                const u32x4 v = *(const u32x4*)(rp + g * 32);
+                // Either way the block is consumed here, so that the
+                // compiler's own waits for these loads are placed in the
+                // prologue: left to their first use inside the tile loop they
+                // would be re-executed every tile, and there they would also
+                // wait for the tile loads in flight.
+                if constexpr (Q_AGPR) {
+                    asm volatile("" : "=a"(q[qb][g]) : "0"(v));
+                } else {
+                    q[qb][g] = v;
+                    asm volatile("" ::"v"(q[qb][g]));
+                }
+            }
         }
-        // Consume the block here, so that the compiler's own waits for these
-        // loads are placed in the prologue: left to their first use inside
-        // the tile loop they would be re-executed every tile, and there they
-        // would also wait for the tile loads in flight.
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-                asm volatile("" ::"v"(q[qb][g].x), "v"(q[qb][g].y), "v"(q[qb][g].z), "v"(q[qb][g].w));
     }
 
     float M[QB], S[QB];
