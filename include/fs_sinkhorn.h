@@ -53,17 +53,24 @@ typedef enum {
 } fs_status;
 
 /* Element type of the score contraction 2 x.y (everything after it is fp32).
- * AUTO: d <= 8 -> fp32 vector FMA; d > 8 -> fp32 matrix cores.
+ * AUTO, FP32: fp32 scores on the matrix cores.  For d <= 8 the whole biased
+ *   score is one small fp32 matrix product per 32x32 block of pairs, so that
+ *   the vector unit is left almost entirely to the one exponential per pair;
+ *   for 8 < d <= 512 the points are zero-padded fp32 matrix operands.
+ * FP32_VALU (d <= 8 only): fp32 scores by vector FMA, one lane per row (the
+ *   plain vector formulation; slower on gfx950, where exponentials and vector
+ *   instructions share issue slots).
  * BF16 / FP16: points (after a common shift, below) are rounded to
- * bfloat16 / float16 with round-to-nearest-even and multiplied on matrix cores
- * with fp32 accumulation; |x|^2 and |y|^2 are taken from the rounded points,
- * so the solver solves the problem of the rounded clouds exactly (up to fp32).
- * FP32 with d <= 8 uses vector FMA; FP32 with d > 8 uses fp32 matrix cores. */
+ *   bfloat16 / float16 with round-to-nearest-even and multiplied on matrix
+ *   cores with fp32 accumulation; |x|^2 and |y|^2 are taken from the rounded
+ *   points, so the solver solves the problem of the rounded clouds exactly
+ *   (up to fp32). */
 typedef enum {
     FS_PREC_AUTO = 0,
     FS_PREC_FP32 = 1,
     FS_PREC_BF16 = 2,
-    FS_PREC_FP16 = 3
+    FS_PREC_FP16 = 3,
+    FS_PREC_FP32_VALU = 4
 } fs_score_prec;
 
 /* Opaque host handle.  It owns no device memory; it points into the

@@ -14,7 +14,8 @@ import torch
 
 __all__ = [
     "FS_OK", "FS_ERR_INVALID_ARG", "FS_ERR_WORKSPACE", "FS_ERR_DEVICE", "FS_ERR_NONFINITE",
-    "FS_ERR_NOT_CONVERGED", "PREC_AUTO", "PREC_FP32", "PREC_BF16", "PREC_FP16", "FsError",
+    "FS_ERR_NOT_CONVERGED", "PREC_AUTO", "PREC_FP32", "PREC_BF16", "PREC_FP16", "PREC_FP32_VALU",
+    "FsError",
     "Problem", "load", "lib_path", "fs_workspace_bytes", "fs_potentials_init",
     "fs_lse_update_f", "fs_lse_update_g", "fs_marginal_residual", "fs_sinkhorn_solve",
     "fs_apply_transport", "fs_problem_info", "fs_status_string", "fs_last_error", "solve",
@@ -22,9 +23,10 @@ __all__ = [
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
     FS_ERR_NOT_CONVERGED = range(6)
-PREC_AUTO, PREC_FP32, PREC_BF16, PREC_FP16 = range(4)
-_PREC_NAMES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16, "fp16": PREC_FP16}
-PATH_NAMES = {0: "fp32-valu", 1: "fp32-mfma", 2: "bf16-mfma", 3: "fp16-mfma"}
+PREC_AUTO, PREC_FP32, PREC_BF16, PREC_FP16, PREC_FP32_VALU = range(5)
+_PREC_NAMES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16, "fp16": PREC_FP16,
+               "fp32-valu": PREC_FP32_VALU}
+PATH_NAMES = {0: "fp32-valu", 1: "fp32-mfma", 2: "bf16-mfma", 3: "fp16-mfma", 4: "fp32-small-mfma"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

@@ -41,6 +41,9 @@ struct fs_problem {
     float* scal;      // [0..1] residual outputs, [2..4] transport scale pair and max bits
     float* pot_tmp;   // max(n, m) floats
     void* vt;         // f16 [dv_max][m_pad] (matrix paths with dv_max > 0)
+    float* krec;      // small-d matrix path: key records of one pass (fp32)
+    void* krec16;     //   fp16-split records (d <= 4)
+    void* kguard;     //   guard words of the packing
 };
 
 namespace {
@@ -91,10 +94,18 @@ fs_status choose_path(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_
     if (dv_max < 0 || dv_max > 4096)
         return fail(FS_ERR_INVALID_ARG, "dv_max must be in [0, 4096] (got %d)", dv_max);
     switch (prec) {
+        case FS_PREC_FP32_VALU:
+            if (d > 8)
+                return fail(FS_ERR_INVALID_ARG, "FS_PREC_FP32_VALU supports d <= 8 (got %d)", d);
+            sh.path = PATH_VALU;
+            sh.dp = d <= 4 ? 4 : 8;
+            sh.lse_dp = d;
+            sh.es = 4;
+            break;
         case FS_PREC_AUTO:
         case FS_PREC_FP32:
             if (d <= 8) {
-                sh.path = PATH_VALU;
+                sh.path = PATH_SMALL;
                 sh.dp = d <= 4 ? 4 : 8;
                 sh.lse_dp = d;
                 sh.es = 4;
@@ -129,9 +140,9 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
                   int& kps_out) {
     const int rpb = lse_rows_per_block(path, lse_dp, (int)n_rows);
     const int64_t R = (n_rows + rpb - 1) / rpb;
-    const int slots = path == PATH_VALU ? 1024 : 256;
-    const int tile = path == PATH_VALU ? 16 : kKeyTile;
-    const int64_t min_keys = path == PATH_VALU ? 1024 : 256;
+    const int slots = path == PATH_VALU ? 1024 : path == PATH_SMALL ? 512 : 256;
+    const int tile = lse_split_granule(path, lse_dp);
+    const int64_t min_keys = small_d_path(path) ? 2048 : 256;
     const int64_t max_keys = lse_max_keys_per_split(path, lse_dp);
     int bestS = -1;
     int64_t bestK = 0;
@@ -159,7 +170,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 
 struct Layout {
     size_t shift, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
-        vt, total;
+        vt, krec, krec16, kguard, total;
 };
 
 Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
@@ -189,8 +200,13 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.rpart = take(sizeof(float) * ((std::max(n, m) + 127) / 128 + 64));
     L.scal = take(sizeof(float) * 8);
     L.ptmp = take(sizeof(float) * std::max(n, m));
-    const bool vt = dv_max > 0 && sh.path != PATH_VALU;
+    const bool vt = dv_max > 0 && !small_d_path(sh.path);
     L.vt = take(vt ? (size_t)2 * dv_max * mp : 0);
+    const bool small = sh.path == PATH_SMALL;
+    const size_t kmax = (size_t)std::max(np, mp);
+    L.krec = take(small ? small_f32_rec_bytes(d) * kmax : 0);
+    L.krec16 = take(small ? small_f16_rec_bytes(d) * kmax : 0);
+    L.kguard = take(small ? 32 : 0);  // packing guard [2], cloud L1 maxima [2]
     L.total = o;
     return L;
 }
@@ -250,6 +266,11 @@ LseArgs base_args(const fs_problem* p, bool f_side, float eps) {
     a.keys_per_split = f_side ? p->f_kps : p->g_kps;
     a.part = p->part;
     a.resid_part = p->resid_part;
+    a.krec = p->krec;
+    a.krec16 = p->krec16;
+    a.krec_guard = p->kguard;
+    a.krec_keys = (int)K.n_pad;
+    a.row_l1 = R.l1max;
     return a;
 }
 
@@ -357,7 +378,14 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
     p->resid_part = (float*)(w + L.rpart);
     p->scal = (float*)(w + L.scal);
     p->pot_tmp = (float*)(w + L.ptmp);
-    p->vt = (dv_max > 0 && sh.path != PATH_VALU) ? (void*)(w + L.vt) : nullptr;
+    p->vt = (dv_max > 0 && !small_d_path(sh.path)) ? (void*)(w + L.vt) : nullptr;
+    p->krec = sh.path == PATH_SMALL ? (float*)(w + L.krec) : nullptr;
+    p->krec16 = sh.path == PATH_SMALL ? (void*)(w + L.krec16) : nullptr;
+    p->kguard = sh.path == PATH_SMALL ? (void*)(w + L.kguard) : nullptr;
+    if (sh.path == PATH_SMALL) {
+        p->X.l1max = (float*)(w + L.kguard) + 2;
+        p->Y.l1max = (float*)(w + L.kguard) + 3;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -370,6 +398,10 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
         goto hip_error;
     if ((e = launch_convert(Y, m, p->Y.n_pad, d, p->dp, p->path, p->shift, p->Y.ops, p->Y.nrm,
                             p->flag, s)) != hipSuccess)
+        goto hip_error;
+    if (p->path == PATH_SMALL &&
+        ((e = launch_row_l1max((const float*)p->X.ops, n, d, p->X.l1max, s)) != hipSuccess ||
+         (e = launch_row_l1max((const float*)p->Y.ops, m, d, p->Y.l1max, s)) != hipSuccess))
         goto hip_error;
     if ((e = launch_weights(a, n, p->X.lw2, p->X.w, f, p->flag, s)) != hipSuccess) goto hip_error;
     if ((e = launch_weights(b, m, p->Y.lw2, p->Y.w, g, p->flag, s)) != hipSuccess) goto hip_error;

@@ -8,7 +8,18 @@
 namespace fs {
 
 // Score path of a problem.
-enum Path : int { PATH_VALU = 0, PATH_MFMA_F32 = 1, PATH_MFMA_BF16 = 2, PATH_MFMA_F16 = 3 };
+// PATH_VALU: d <= 8, scores by vector FMA.  PATH_SMALL: d <= 8, scores (bias
+// included) on the fp32 matrix cores.  PATH_MFMA_*: padded d on the matrix
+// cores in the named element type.
+enum Path : int {
+    PATH_VALU = 0,
+    PATH_MFMA_F32 = 1,
+    PATH_MFMA_BF16 = 2,
+    PATH_MFMA_F16 = 3,
+    PATH_SMALL = 4
+};
+// Paths that keep the points as fp32 rows of 4 (d <= 4) or 8 floats.
+inline bool small_d_path(int path) { return path == PATH_VALU || path == PATH_SMALL; }
 
 // Rows per workgroup of the matrix-core kernels is 4 waves x 32 x qb; clouds are
 // padded to a multiple of this so no kernel ever reads past an operand.
@@ -24,6 +35,7 @@ struct Cloud {
     float* w;       // copy of the weights [n]
     int64_t n;
     int64_t n_pad;
+    float* l1max = nullptr;  // small-d matrix path: largest L1 norm of a point (device scalar)
 };
 
 // Arguments of one streaming log-sum-exp pass ("half-step"): for every row
@@ -56,6 +68,13 @@ struct LseArgs {
     const float* cur;
     float* resid_part;  // one partial per finalizing block
     float* resid_out;   // 1 float
+    // PATH_SMALL (workspace): key records of this pass, fp32 [krec_keys][2*kp]
+    // and, for d <= 4, fp16-split [krec_keys][16]; two guard words.
+    float* krec;
+    void* krec16;
+    void* krec_guard;
+    int krec_keys;      // records packed (the key cloud's padded count)
+    const float* row_l1;  // largest L1 norm of a row point (device scalar)
 };
 
 // Arguments of the transport application U = P.V (or P.V / a).
@@ -101,6 +120,20 @@ int lse_rows_per_block(int path, int dp, int n_rows);
 // Largest key range one workgroup of the streaming kernel may cover (its key
 // biases are held in LDS).
 int lse_max_keys_per_split(int path, int dp);
+// Key-range granularity of a split (keys per streamed tile).
+int lse_split_granule(int path, int dp);
+
+// PATH_SMALL: key-record slot pairs for dimension d, keys per streamed tile,
+// rows per workgroup; the streaming kernel (after packing the key records);
+// ev_begin is recorded after the packing.
+int small_kp(int d);
+int small_tile(int d);
+int small_rows_per_block();
+size_t small_f32_rec_bytes(int d);  // per key
+size_t small_f16_rec_bytes(int d);  // per key (0 if d > 4)
+// Largest L1 norm over the (converted, fp32) points of a cloud into *out.
+hipError_t launch_row_l1max(const float* ops, int64_t n, int d, float* out, hipStream_t s);
+hipError_t launch_lse_small(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin);
 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
 hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratch,

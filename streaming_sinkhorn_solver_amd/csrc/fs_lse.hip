@@ -701,12 +701,19 @@ int ng_of(int path, int dp) { return path == PATH_MFMA_F32 ? dp / 8 : dp / 16; }
 int valu_rows_per_lane(int n_rows) { return n_rows >= 65536 ? 4 : 1; }
 
 int lse_max_keys_per_split(int path, int dp) {
-    if (path == PATH_VALU) return 1 << 30;
+    if (small_d_path(path)) return 1 << 30;
     return kps_max_for(ng_of(path, dp));
+}
+
+int lse_split_granule(int path, int dp) {
+    if (path == PATH_VALU) return kValuTile;
+    if (path == PATH_SMALL) return small_tile(dp);
+    return kKeyTile;
 }
 
 int lse_rows_per_block(int path, int dp, int n_rows) {
     if (path == PATH_VALU) return 256 * valu_rows_per_lane(n_rows);
+    if (path == PATH_SMALL) return small_rows_per_block();
     const int ng = ng_of(path, dp);
     return waves_for(ng) * 32 * mfma_qb(path, ng);
 }
@@ -717,8 +724,11 @@ int lse_rows_per_block(int path, int dp, int n_rows) {
 hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s, hipEvent_t ev_begin,
                       hipEvent_t ev_end) {
     hipError_t e;
-    if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-    if (path == PATH_VALU) {
+    if (path == PATH_SMALL) {
+        e = launch_lse_small(a, s, ev_begin);
+    } else if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) {
+        return e;
+    } else if (path == PATH_VALU) {
         const int R = valu_rows_per_lane(a.n_rows);
         e = valu_dispatch(a.dp, a, s, R);
     } else {

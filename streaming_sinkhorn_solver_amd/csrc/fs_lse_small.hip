@@ -1,0 +1,436 @@
+// fs_lse_small.hip -- the streaming log-sum-exp pass for small dimensions
+// (d <= 8) with the scores formed on the matrix cores.
+//
+// "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU" (gist.science
+// explainer), section "Method": the update is a row-wise LSE of biased
+// dot-product scores (part 1), streamed tile by tile with an exact online
+// maximum/sum (part 2).  At d = 3 the contraction is a handful of products per
+// pair and the pass is bound by the exponential, one per pair.  On gfx950 the
+// transcendental unit, the vector ALU and the fp32 matrix instructions issue
+// from the same SIMD without overlapping (their costs add), so everything
+// besides the exponential has to be made cheap.  The whole score, bias
+// included, is one matrix product per block of 32 keys x 32 rows, with the
+// running reference in the accumulator input:
+//
+//   acc_ij = sum_k A_jk B_ki + C_i   with  A_j = (y~_j, beta_j, 0..),
+//                                          B_i = (c_score x~_i, 1, 0..),
+//                                          C_i = -R_i (every accumulator)
+//          = z2_ij - R_i
+//
+// where z2 is the base-2 score of the vector path and R_i a per-row reference
+// that plays the role of the running maximum.  The vector side is left with
+// one exponential and one addition per pair.
+//
+// Two operand formats:
+//  * fp16, d <= 4: every value v is split into fp16 parts (v = vh + vl, the
+//    bias into three parts); the 16 contraction slots hold the products
+//    rh*yh, rh*yl, rl*yh per coordinate and bh, bm, bl, so one
+//    v_mfma_f32_32x32x16_f16 (fp16 products are exact in fp32) gives the
+//    score with a relative error of a few 2^-22 per product.  A pass uses it
+//    only if c_score * max_i sum_c |x_ic| * max_jc |y_jc| <= 2^9 (f then moves
+//    by less than about 2e-4 eps from this error) and every bias fits fp16
+//    with margin; otherwise
+//  * fp32: A and B in fp32, ceil((d+1)/2) v_mfma_f32_32x32x2f32 per block.
+//
+// R_i is only moved when a block's terms 2^(z2 - R) grow large (their sum
+// above 2^64, checked with one compare) or on the row's first block; the move
+// goes to the block maximum if that exceeds R by more than 2^8.  (R, s) is
+// the same base-2 (max, sum) pair as in the exact online LSE, with R a valid
+// shift instead of the exact maximum: R + log2 s is unchanged, and the merge
+// and finalize stages are shared with the other paths.
+//
+// The key records (A rows, with the bias of the current potential) are packed
+// once per half-step by pack_key_records_kernel, streamed through LDS in tiles
+// of TK keys, and read by every wave of the workgroup.
+#include "fs_device.hpp"
+#include "fs_internal.h"
+
+namespace fs {
+
+namespace {
+
+constexpr int kSmallWaves = 8;        // waves per workgroup, 32 rows each
+constexpr float kSlack = 8.f;         // R moves to a block maximum more than 2^8 above it
+constexpr float kBigSum = 0x1p64f;    // common path: a block's terms sum to at most this
+constexpr float kF16Bound = 512.f;    // fp16 format: sum_c |c x_c| * max|y| <= this
+constexpr float kF16Range = 16384.f;  // fp16 format: |c x|, |y| <= this, |beta| <= twice it
+constexpr int kNbuf = 4;
+
+// Keys per streamed tile (splits are whole tiles): fp32 records are 2*KP
+// floats (8 KiB tiles for KP <= 2); fp16 records are 32 bytes.
+constexpr int small_tile_keys(int kp) { return kp <= 2 ? 512 : 256; }
+constexpr int f32_rec_bytes(int kp) { return 8 * kp; }
+constexpr int kF16RecBytes = 32;
+
+// Guard words written by the packing: the bits of max |y_c| over all keys,
+// and nonzero if a bias or coordinate does not fit the fp16 format.
+struct Guard {
+    unsigned ymax_bits;
+    unsigned bad;
+};
+
+// fp32 record of one key: slot k (0 <= k < 2*KP) of the contraction holds
+// y~_k (k < d), beta (k == d) or 0; slot k is stored at (k & 1) * KP + (k >> 1)
+// so that lane half h reads its KP values (slots h, h+2, ..) contiguously.
+// fp16 record (d <= 4): slots 3c, 3c+1, 3c+2 hold yh_c, yl_c, yh_c; slots
+// 3d..3d+2 the parts bh, bm, bl of beta; the rest 0.  Padding keys (j >=
+// n_keys) get beta = -inf (bh = -inf, the other parts 0).
+template <int KP>
+__global__ __launch_bounds__(256) void pack_key_records_kernel(
+    const float* __restrict__ keys, int stride, int d, int n_keys, int n_pad,
+    const float* __restrict__ pot, const float* __restrict__ nrm, const float* __restrict__ lw2,
+    float c_bias, float* __restrict__ rec32, _Float16* __restrict__ rec16, Guard* guard) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const bool in = j < n_pad;
+    const bool real = j < n_keys;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = (real && k < d) ? keys[(int64_t)j * stride + k] : 0.f;
+    const float beta = real ? fmaf(pot[j] - nrm[j], c_bias, lw2[j]) : -INFINITY;
+    float ymax = 0.f;
+    bool bad = false;
+    if (in) {
+        float v[2 * KP];
+#pragma unroll
+        for (int k = 0; k < 2 * KP; ++k)
+            v[(k & 1) * KP + (k >> 1)] = k < d ? y[k] : (k == d ? beta : 0.f);
+        float* o = rec32 + (int64_t)j * 2 * KP;
+#pragma unroll
+        for (int k = 0; k < 2 * KP; ++k) o[k] = v[k];
+        if (rec16) {
+            _Float16 hv[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) hv[k] = (_Float16)0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (c < d) {
+                    const _Float16 yh = (_Float16)y[c];
+                    const _Float16 yl = (_Float16)(y[c] - (float)yh);
+                    hv[3 * c] = yh;
+                    hv[3 * c + 1] = yl;
+                    hv[3 * c + 2] = yh;
+                    ymax = fmaxf(ymax, fabsf(y[c]));
+                }
+            }
+            if (real) {
+                const _Float16 bh = (_Float16)beta;
+                const float r1 = beta - (float)bh;
+                const _Float16 bm = (_Float16)r1;
+                const _Float16 bl = (_Float16)(r1 - (float)bm);
+                hv[3 * d] = bh;
+                hv[3 * d + 1] = bm;
+                hv[3 * d + 2] = bl;
+                bad = !(fabsf(beta) <= 2.f * kF16Range) || !(ymax <= kF16Range);
+            } else {
+                hv[3 * d] = (_Float16)(-INFINITY);
+            }
+            uint4 w0, w1;
+            __builtin_memcpy(&w0, &hv[0], 16);
+            __builtin_memcpy(&w1, &hv[8], 16);
+            uint4* o16 = (uint4*)(rec16 + (int64_t)j * 16);
+            o16[0] = w0;
+            o16[1] = w1;
+        }
+    }
+    if (rec16) {
+        // one atomic per wave for each guard word
+        float wm = ymax;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+        const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if ((threadIdx.x & 63) == 0) {
+            if (wm > 0.f) atomicMax(&guard->ymax_bits, __float_as_uint(wm));
+            if (wbad) atomicOr(&guard->bad, 1u);
+        }
+    }
+}
+
+template <int KP>
+__global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs a) {
+    constexpr int W = kSmallWaves;
+    constexpr bool HAS_F16 = KP <= 2;  // the fp16 format covers d <= 4
+    constexpr int TK = small_tile_keys(KP);
+    constexpr int F32_TILE = TK * f32_rec_bytes(KP);
+    constexpr int F16_TILE = HAS_F16 ? TK * kF16RecBytes : 0;
+    constexpr int BUF_BYTES = F16_TILE > F32_TILE ? F16_TILE : F32_TILE;
+    __shared__ __attribute__((aligned(16))) uint4 tbuf[kNbuf][BUF_BYTES / 16];
+    __shared__ float red[16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 31;
+    const int h = lane >> 5;
+    const int row = blockIdx.x * (W * 32) + wave * 32 + ln;  // rows are padded: always readable
+    const int split = blockIdx.y;
+    const int j0 = split * a.keys_per_split;
+    const int j1 = min(a.n_keys, j0 + a.keys_per_split);
+    const int ntiles = (j1 - j0 + TK - 1) / TK;
+    const int d = a.dp;
+    const int stride = d <= 4 ? 4 : 8;
+    const float* __restrict__ xr = (const float*)a.rows + (int64_t)row * stride;
+    float r[8];  // c_score * x~ of this lane's row
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = k < d ? a.c_score * xr[k < stride ? k : 0] : 0.f;
+
+    // Format of this pass (the same for every workgroup, so no result depends
+    // on which rows share a workgroup): fp16 if the bound holds for the
+    // largest row (L1 norm, from the problem set-up) against the largest key
+    // coordinate, and the packing flagged nothing.
+    bool use16 = false;
+    if constexpr (HAS_F16) {
+        const Guard* g = (const Guard*)a.krec_guard;
+        const float ymax = __uint_as_float(g->ymax_bits);
+        const float rl1 = a.c_score * *a.row_l1;
+        use16 = rl1 * ymax <= kF16Bound && rl1 <= kF16Range && g->bad == 0;
+    }
+
+    float R = 0.f;      // reference: the running maximum, moved lazily
+    float s = 0.f;      // sum of 2^(z2 - R) over the keys seen
+    float delta = 0.f;  // R minus the reference baked into cm (moves within a tile)
+    f32x16 cm;          // MFMA C operand: minus the reference, refreshed per tile
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cm[q] = 0.f;
+
+    auto block_max = [&](const f32x16& acc) __attribute__((always_inline)) {
+        float t = fmaxf(acc[0], acc[1]);
+#pragma unroll
+        for (int q = 2; q < 16; ++q) t = fmaxf(t, acc[q]);
+        return t;
+    };
+    // acc = z2 - (R - delta).  Common case -- no lane moved its reference in
+    // this tile (delta = 0) and the block's terms 2^acc sum to at most
+    // kBigSum (so none is large, let alone infinite): add them.  Checking the
+    // sum costs one compare; the maximum is only formed on the other path,
+    // which moves R, where needed, to the block maximum.  Only per-lane
+    // scalars change, so the common path carries no register-tuple copies.
+    auto epilogue = [&](const f32x16& acc) __attribute__((always_inline)) {
+        float e[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) e[q] = ex2(acc[q]);
+        // pairwise sum (short dependency chains)
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+            for (int q = 0; q < 16; q += 2 * w) e[q] += e[q + w];
+        if (__builtin_amdgcn_ballot_w64(!(e[0] <= kBigSum) || delta != 0.f)) {
+            const float t = block_max(acc) - delta;  // block maximum relative to R
+            const float dl = t > kSlack ? t : 0.f;
+            const float sh = delta + dl;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) e[q] = ex2(acc[q] - sh);
+            // same summation tree as the common path: a lane that does not
+            // move (dl = 0, sh = 0) gets bit-identical results on either path
+#pragma unroll
+            for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+                for (int q = 0; q < 16; q += 2 * w) e[q] += e[q + w];
+            s = s * ex2(-dl) + e[0];
+            R += dl;
+            delta = sh;
+        } else {
+            s += e[0];
+        }
+    };
+
+    // The tile loop for one operand format.
+    auto run = [&](auto f16_c) __attribute__((always_inline)) {
+        constexpr bool F16 = decltype(f16_c)::value;
+        constexpr int REC_BYTES = F16 ? kF16RecBytes : f32_rec_bytes(KP);
+        constexpr int TILE_BYTES = TK * REC_BYTES;
+        constexpr int TILE_INSTR = TILE_BYTES / 1024;  // wave-wide 1 KiB loads per tile
+        constexpr int INSTR_PER_WAVE = (TILE_INSTR + W - 1) / W;
+        constexpr int MIN_INSTR = TILE_INSTR / W;
+        constexpr int SUB = TK / 32;                   // 32-key blocks per tile
+        static_assert(TILE_BYTES % 1024 == 0 && TILE_BYTES <= BUF_BYTES, "tile geometry");
+        const char* __restrict__ recs =
+            F16 ? (const char*)a.krec16 + (int64_t)j0 * REC_BYTES
+                : (const char*)a.krec + (int64_t)j0 * REC_BYTES;
+
+        // tile k -> slot (contiguous copy; records past j1 in the last tile
+        // are padding records of score -inf: splits are whole tiles)
+        const uint32_t lane16 = (uint32_t)lane * 16u;
+        auto issue_tile = [&](int k, int slot) __attribute__((always_inline)) {
+#pragma unroll
+            for (int l = 0; l < INSTR_PER_WAVE; ++l) {
+                const int L = l * W + wave;
+                if (TILE_INSTR % W == 0 || L < TILE_INSTR)
+                    dma_to_lds16(recs + (int64_t)k * TILE_BYTES + L * 1024, lane16,
+                                 &tbuf[slot][L * 64]);
+            }
+        };
+        if (ntiles > 0) {
+#pragma unroll
+            for (int k = 0; k < kNbuf - 1; ++k) issue_tile(min(k, ntiles - 1), k);
+        }
+
+        // B operand of this lane: row `row`, the lane half's contraction slots
+        f16x8 b16;
+        float b32[KP];
+        if constexpr (F16) {
+            _Float16 sl[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) sl[k] = (_Float16)0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (c < d) {
+                    const _Float16 rh = (_Float16)r[c];
+                    const _Float16 rl = (_Float16)(r[c] - (float)rh);
+                    sl[3 * c] = rh;
+                    sl[3 * c + 1] = rh;
+                    sl[3 * c + 2] = rl;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (k >= 3 * d && k < 3 * d + 3) sl[k] = (_Float16)1.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) b16[k] = h ? sl[8 + k] : sl[k];
+        } else {
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                const int k = 2 * p + h;
+                b32[p] = k < d ? r[k] : (k == d ? 1.f : 0.f);
+            }
+        }
+        auto scores = [&](const char* rb, f32x16& acc) __attribute__((always_inline)) {
+            if constexpr (F16) {
+                const f16x8 av = *(const f16x8*)(rb + (size_t)ln * REC_BYTES + h * 16);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b16, cm, 0, 0, 0);
+            } else {
+                const float* rf = (const float*)rb + (size_t)ln * 2 * KP + h * KP;
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(rf[0], b32[0], cm, 0, 0, 0);
+#pragma unroll
+                for (int p = 1; p < KP; ++p)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(rf[p], b32[p], acc, 0, 0, 0);
+            }
+        };
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+
+        // R starts at the maximum of the first 32-key block (finite wherever
+        // the lane sees a key at all; a lane that never does keeps s = 0, the
+        // empty state).
+        if (ntiles > 0) {
+            f32x16 acc;
+            scores((const char*)&tbuf[0][0], acc);
+            const float t = block_max(acc);
+            R = t > -INFINITY ? t : 0.f;
+        }
+
+        for (int t = 0; t < ntiles; ++t) {
+            const int slot = t % kNbuf;
+            issue_tile(min(t + kNbuf - 1, ntiles - 1), (t + kNbuf - 1) % kNbuf);
+            const char* tb = (const char*)&tbuf[slot][0];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) cm[q] = -R;
+            delta = 0.f;
+            f32x16 acc0, acc1;
+            scores(tb, acc0);
+#pragma unroll
+            for (int u = 0; u < SUB; u += 2) {
+                scores(tb + (u + 1) * 32 * REC_BYTES, acc1);
+                epilogue(acc0);
+                if (u + 2 < SUB) scores(tb + (u + 2) * 32 * REC_BYTES, acc0);
+                epilogue(acc1);
+            }
+            // tiles issued after tile t+1: t+2 .. t+kNbuf-1
+            if constexpr (MIN_INSTR == 0)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kNbuf - 2) * MIN_INSTR) : "memory");
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    if constexpr (HAS_F16) {
+        if (use16)
+            run(std::true_type{});
+        else
+            run(std::false_type{});
+    } else {
+        run(std::false_type{});
+    }
+
+    // the two lane halves hold the same row over disjoint keys
+    float M = s > 0.f ? R : -INFINITY;
+    {
+        const float M2 = __shfl_xor(M, 32, 64);
+        const float S2 = __shfl_xor(s, 32, 64);
+        lse_merge(M, s, M2, S2);
+    }
+    float resid = 0.f;
+    if (h == 0 && row < a.n_rows) {
+        if (a.n_split == 1) {
+            const float lse2 = M + lg2(s);
+            float o = a.mode == 0 ? fmaf(a.out_scale, lse2, a.row_nrm[row]) : lse2;
+            if (a.cur) resid = a.row_w[row] * fabsf(ex2((a.cur[row] - o) * a.c_bias) - 1.f);
+            a.out[row] = o;
+        } else {
+            a.part[(int64_t)split * a.n_rows + row] = make_float2(M, s);
+        }
+    }
+    if (a.n_split == 1 && a.cur) {
+        resid = block_sum(resid, red);
+        if (tid == 0) a.resid_part[blockIdx.x] = resid;
+    }
+}
+
+template <int KP>
+hipError_t small_launch(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
+    hipError_t e;
+    const int n_pad_keys = a.krec_keys;
+    constexpr bool f16 = KP <= 2;
+    if (f16 && (e = launch_fill((float*)a.krec_guard, 2, 0.f, s)) != hipSuccess) return e;
+    pack_key_records_kernel<KP><<<(n_pad_keys + 255) / 256, 256, 0, s>>>(
+        (const float*)a.keys, a.dp <= 4 ? 4 : 8, a.dp, a.n_keys, n_pad_keys, a.key_pot, a.key_nrm,
+        a.key_lw2, a.c_bias, a.krec, f16 ? (_Float16*)a.krec16 : nullptr, (Guard*)a.krec_guard);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
+    const dim3 grid((a.n_rows + kSmallWaves * 32 - 1) / (kSmallWaves * 32), a.n_split);
+    lse_small_kernel<KP><<<grid, kSmallWaves * 64, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+// Largest L1 norm over the points of a cloud (bits of a non-negative float,
+// combined with atomicMax; *out must start at 0).
+__global__ __launch_bounds__(256) void row_l1max_kernel(const float* __restrict__ ops, int64_t n,
+                                                        int stride, int d, unsigned* out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    float v = 0.f;
+    if (i < n)
+        for (int k = 0; k < d; ++k) v += fabsf(ops[i * stride + k]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if ((threadIdx.x & 63) == 0 && v > 0.f) atomicMax(out, __float_as_uint(v));
+}
+
+}  // namespace
+
+hipError_t launch_row_l1max(const float* ops, int64_t n, int d, float* out, hipStream_t s) {
+    hipError_t e = launch_fill(out, 1, 0.f, s);
+    if (e != hipSuccess) return e;
+    row_l1max_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(ops, n, d <= 4 ? 4 : 8, d,
+                                                                 (unsigned*)out);
+    return hipGetLastError();
+}
+
+int small_kp(int d) { return (d + 2) / 2; }
+int small_tile(int d) { return small_tile_keys(small_kp(d)); }
+int small_rows_per_block() { return kSmallWaves * 32; }
+size_t small_f32_rec_bytes(int d) { return (size_t)f32_rec_bytes(small_kp(d)); }
+size_t small_f16_rec_bytes(int d) { return small_kp(d) <= 2 ? (size_t)kF16RecBytes : 0; }
+
+hipError_t launch_lse_small(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
+    switch (small_kp(a.dp)) {
+        case 1: return small_launch<1>(a, s, ev_begin);
+        case 2: return small_launch<2>(a, s, ev_begin);
+        case 3: return small_launch<3>(a, s, ev_begin);
+        case 4: return small_launch<4>(a, s, ev_begin);
+        case 5: return small_launch<5>(a, s, ev_begin);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fs

@@ -149,6 +149,7 @@ hipError_t launch_convert(const float* P, int64_t n, int64_t n_pad, int d, int d
     const int64_t blocks = (n_pad + 3) / 4;
     switch (path) {
         case PATH_VALU:
+        case PATH_SMALL:
         case PATH_MFMA_F32:
             convert_kernel<float><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, shift,
                                                          (float*)ops, nrm, flag);

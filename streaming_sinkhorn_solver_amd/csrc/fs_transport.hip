@@ -386,7 +386,7 @@ hipError_t transport_mfma_dispatch(int ng, const TransportArgs& a, int64_t m_pad
 hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, void* Vt_buf,
                             int64_t m_pad, hipStream_t s) {
     TransportArgs a = a0;
-    if (path == PATH_VALU) {
+    if (small_d_path(path)) {
         switch (a.dp) {
             case 1: return transport_valu_launch<1>(a, s);
             case 2: return transport_valu_launch<2>(a, s);
