@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
-"""Benchmark of the streaming log-domain Sinkhorn solver on one MI355X.
+"""Benchmark of the streaming log-sum-exp Sinkhorn solver on one MI355X.
 
-Workload (the recipe the headline metric is quoted on): n = m = 50,000
-points in 512-D, two 10-component Gaussian mixtures, Dirichlet(1) weights,
-eps = 0.1, bf16 matrix-core scores with fp32 accumulation.  One step is the
-whole hot path on resident inputs: problem preparation (shift, bf16
-conversion, norms, log-weights), 100 alternating f/g iterations and the
-barycentric projection P.Y / a.
+Default workload (the recipe the headline metric is quoted on): n = m =
+50,000 points in 512-D, two 10-component Gaussian mixtures, Dirichlet(1)
+weights, eps = 0.1, bf16 matrix-core scores with fp32 accumulation.  One step
+is the whole hot path on resident inputs: problem preparation (shift,
+conversion, norms, log-weights), the alternating f/g iterations and the
+transport product (here the barycentric projection P.Y / a).
+
+``--workload c1|c2|c4|c5`` runs one of the other recipes the same way (its own
+sizes, precision, schedule and transport), for measurements beside the
+headline line.
 
 Prints one JSON line with
   value      Sinkhorn iterations per second over whole steps
-  roofline   the streaming LSE kernel: algorithmic flops per launch
-             (2 n m d) over its mean launch duration, timed with HIP events
-             on the launch stream inside the timed region, against the
-             MI355X dense bf16 peak; `traffic` is the per-launch HBM bytes
-             from the committed rocprofv3 counter summary when it was taken
-             on the current kernel source, else null
-  cpu_baseline  the float64 oracle's f-update timed on this host's cores
-             on a bounded sample of rows of the same workload, scaled to
+  roofline   the streaming LSE kernel (the dominant kernel of every recipe):
+             algorithmic work per launch over its mean launch duration, timed
+             with HIP events on the launch stream inside the timed region.
+             Matrix-core recipes: 2 n m d flops per half-step against the
+             MI355X dense peak of the score element type.  d = 3 recipes:
+             one exponential per pair against the exponential peak, 256 CUs x
+             32 lanes/clock x 2.4 GHz = 19.66e12/s.  `traffic` is the
+             per-launch HBM bytes from the committed rocprofv3 counter summary
+             when it was taken on the current kernel source, else null
+  cpu_baseline  the float64 oracle's f-update timed on this host's cores on a
+             bounded sample of rows of the same workload, scaled to
              iterations per second
 """
 from __future__ import annotations
@@ -33,20 +40,50 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "Sinkhorn iters/sec and pair-evals/sec at n=m=50k, d=512; % of roofline"
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "lse_bf16_c3_traffic.json")
-KERNEL_SOURCE = os.path.join(HERE, "streaming_sinkhorn_solver_amd", "csrc", "fs_lse.hip")
+CSRC = os.path.join(HERE, "streaming_sinkhorn_solver_amd", "csrc")
+EXP_PEAK = 256 * 32 * 2.4e9 / 1e12  # T exponentials/s
+
+# recipe -> (score precision, roofline peak, unit, dtype label, description)
+RECIPES = {
+    "c1": ("auto", EXP_PEAK, "Texp/s", "f32",
+           "n=m=512, d=3, X~N(0,I), Y~N(0.5,I), uniform weights, eps=0.1, 100 iterations (seed 1)"),
+    "c2": ("fp32", 157.3, "TFLOP/s", "f32",
+           "n=m=10000, d=64, X~N(0,I/d), Y~N(mu,0.5 I/d), uniform weights, eps=0.05, "
+           "200 iterations (seed 2)"),
+    "c3": ("bf16", 2500.0, "TFLOP/s", "bf16",
+           "n=m=50000, d=512, two 10-component Gaussian mixtures, Dirichlet(1) weights, "
+           "eps=0.1, 100 alternating iterations + barycentric projection P.Y/a (seed 3)"),
+    "c4": ("fp16", 2500.0, "TFLOP/s", "f16",
+           "n=50000, m=30000, d=1024, X on the unit sphere, Y~N(0,I/d) with a 0.25 shift on 16 "
+           "coordinates, Exp(1) weights, eps 1 -> 0.01 over 10 stages x 20 iterations, "
+           "then U=P.V with V~N(0,I), width 1024 (seed 4)"),
+    "c5": ("auto", EXP_PEAK, "Texp/s", "f32",
+           "n=m=250000, d=3, X uniform in the unit cube, Y an 8-component mixture (std 0.05), "
+           "uniform weights, eps=0.01, 10 iterations (seed 5)"),
+}
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def file_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def counter_mode(w, half_steps: int = 6) -> None:
+def kernel_source_sha(workload: str = "c3") -> str:
+    """Hash of the source of the recipe's streaming LSE kernel."""
+    return file_sha("fs_lse_small.hip" if workload in ("c1", "c5") else "fs_lse.hip")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(HERE, "profiles", f"lse_{workload}_traffic.json")
+
+
+def counter_mode(w, prec: str, half_steps: int = 6) -> None:
     """Workload for hardware-counter runs: a 1 GiB elementwise read+write of
     known size (the counters' calibration), then problem preparation and
-    `half_steps` alternating LSE passes of the benchmark workload."""
+    `half_steps` alternating LSE passes of the recipe at its final eps."""
     import torch
 
     from streaming_sinkhorn_solver_amd import binding
@@ -60,7 +97,7 @@ def counter_mode(w, half_steps: int = 6) -> None:
     X, Y, a, b = (torch.from_numpy(v).to(dev) for v in (w.X, w.Y, w.a, w.b))
     f = torch.empty(w.n, device=dev)
     g = torch.empty(w.m, device=dev)
-    p = binding.fs_potentials_init(X, Y, a, b, prec="bf16", f=f, g=g)
+    p = binding.fs_potentials_init(X, Y, a, b, prec=prec, f=f, g=g)
     for k in range(half_steps):
         if k % 2 == 0:
             binding.fs_lse_update_f(p, w.eps, g, f)
@@ -71,15 +108,15 @@ def counter_mode(w, half_steps: int = 6) -> None:
                       "copy_bytes": float(1 << 30)}), flush=True)
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload: str):
     """Calibrated HBM bytes per LSE launch from the committed counter summary,
     or None if it is missing or was taken on another kernel source."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(workload)) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha") != kernel_source_sha():
+    if rec.get("kernel_source_sha") != kernel_source_sha(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -92,7 +129,7 @@ def cpu_baseline(w, target_s: float = 15.0) -> dict:
 
     rng = np.random.default_rng(0)
     g = np.zeros(w.m)
-    k0 = 4 * oracle.num_threads()
+    k0 = min(w.n, 4 * oracle.num_threads())
     rows = rng.choice(w.n, size=k0, replace=False)
     t0 = time.perf_counter()
     oracle.f_update_rows(w.X, w.Y, w.b, g, w.eps, rows)
@@ -118,7 +155,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--iters", type=int, default=None, help="override iterations per step")
+    ap.add_argument("--workload", default="c3", choices=sorted(RECIPES))
+    ap.add_argument("--iters", type=int, default=None, help="override iterations per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="run the hardware-counter workload instead of the benchmark")
@@ -135,32 +173,37 @@ def main():
     from streaming_sinkhorn_solver_amd import binding, workloads
 
     binding.load()
-    w = workloads.make("c3")
+    wl = args.workload
+    prec, peak, unit, dtype, desc = RECIPES[wl]
+    w = workloads.make(wl)
     if args.counters:
-        counter_mode(w)
+        counter_mode(w, prec)
         return
     iters = args.iters or w.iters
+    total_iters = iters * w.n_stages
     dev = torch.device("cuda:0")
     X = torch.from_numpy(w.X).to(dev)
     Y = torch.from_numpy(w.Y).to(dev)
     a = torch.from_numpy(w.a).to(dev)
     b = torch.from_numpy(w.b).to(dev)
-    V = Y  # barycentric projection of the target cloud
+    V = torch.from_numpy(w.V).to(dev) if w.V is not None else None
+    dv = 0 if V is None else V.shape[1]
     f = torch.empty(w.n, device=dev)
     g = torch.empty(w.m, device=dev)
-    T = torch.empty((w.n, w.d), device=dev)
-    ws_bytes = binding.fs_workspace_bytes(w.n, w.m, w.d, w.d, "bf16")
+    U = torch.empty((w.n, dv), device=dev) if dv else None
+    ws_bytes = binding.fs_workspace_bytes(w.n, w.m, w.d, dv, prec)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     stats = {"lse_ms": 0.0, "lse_launches": 0}
 
     def step(timed: bool):
-        p = binding.fs_potentials_init(X, Y, a, b, dv_max=w.d, prec="bf16", f=f, g=g,
-                                       workspace=ws)
-        info = binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, iters_per_stage=iters,
+        p = binding.fs_potentials_init(X, Y, a, b, dv_max=dv, prec=prec, f=f, g=g, workspace=ws)
+        info = binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, eps_start=w.eps_start,
+                                         n_stages=w.n_stages, iters_per_stage=iters,
                                          time_kernels=timed)
-        binding.fs_apply_transport(p, w.eps, f, g, V, T, divide_by_a=True)
+        if dv:
+            binding.fs_apply_transport(p, w.eps, f, g, V, U, divide_by_a=w.divide_by_a)
         if timed:
             stats["lse_ms"] += info["lse_ms"]
             stats["lse_launches"] += info["lse_launches"]
@@ -176,27 +219,35 @@ def main():
     dt = time.perf_counter() - t0
     info = p.info
 
-    total_iters = iters * args.steps
     ms_per_step = dt / args.steps * 1e3
-    it_s = total_iters / dt
-    pair_evals = 2.0 * w.n * w.m * total_iters
-    flops_per_launch = 2.0 * w.n * w.m * w.d  # score contraction of one half-step
+    it_s = total_iters * args.steps / dt
+    pair_evals = 2.0 * w.n * w.m * total_iters * args.steps
     lse_mean_ms = stats["lse_ms"] / max(stats["lse_launches"], 1)
-    achieved = flops_per_launch / (lse_mean_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_per_launch(),
-                "kernel": "lse_mfma_kernel<bf16, d_pad 512> (one half-step)",
+    # the LSE launches alternate f (n rows) and g (m rows); per launch the
+    # same n*m pairs
+    if unit == "TFLOP/s":
+        work = 2.0 * w.n * w.m * w.d  # score contraction flops of one half-step
+    else:
+        work = float(w.n) * w.m  # exponentials of one half-step
+    achieved = work / (lse_mean_ms * 1e-3) / 1e12
+    kernel = {"c1": "lse_small_kernel<2> (fp16 split scores)",
+              "c5": "lse_small_kernel<2> (fp16 split scores)",
+              "c2": "lse_mfma_kernel<fp32, d_pad 64>",
+              "c3": "lse_mfma_kernel<bf16, d_pad 512>",
+              "c4": "lse_mfma_kernel<fp16, d_pad 1024>"}[wl]
+    roofline = {"bound": "mfma" if unit == "TFLOP/s" else "alu",
+                "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic_per_launch(wl),
+                "kernel": kernel + " (one half-step)",
                 "mean_launch_ms": round(lse_mean_ms, 4), "launches": stats["lse_launches"]}
     out = {
         "metric": METRIC, "value": round(it_s, 3), "unit": "iters/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "n=m=50000, d=512, two 10-component Gaussian mixtures, "
-                               "Dirichlet(1) weights, eps=0.1, 100 alternating iterations + "
-                               "barycentric projection P.Y/a (seed 3)",
-                   "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "iters_per_step": iters,
+        "config": {"workload": desc, "recipe": wl, "n": w.n, "m": w.m, "d": w.d,
+                   "eps": w.eps, "eps_start": w.eps_start, "n_stages": w.n_stages,
+                   "iters_per_stage": iters, "transport_width": dv,
                    "score_path": info["path"], "f_splits": info["f_splits"],
                    "g_splits": info["g_splits"]},
         "pair_evals_per_s": pair_evals / dt,

@@ -47,6 +47,24 @@ __device__ __forceinline__ void dma_to_lds16(const char* gbase, uint32_t voff, c
         : "memory");
 }
 
+// XCD-aware work mapping of a 2-D grid (gridDim.x row blocks x gridDim.y key
+// splits).  Workgroups are dispatched to the 8 XCDs round-robin by linear id,
+// and each XCD has its own L2.  The linear ids of XCD x (x, x+8, ...) are
+// given consecutive entries of the split-major list of (split, row block)
+// pairs, so the workgroups an XCD runs at one time mostly stream the same
+// key range through its L2.  A bijection: every pair is computed once,
+// whatever the dispatch order.
+__device__ __forceinline__ void xcd_work(int& row_block, int& split) {
+    const int R = gridDim.x;
+    const int total = R * gridDim.y;
+    const int id = blockIdx.x + blockIdx.y * R;
+    const int x = id & 7, k = id >> 3;
+    const int q = total >> 3, r = total & 7;
+    const int idx = x * q + min(x, r) + k;
+    split = idx / R;
+    row_block = idx - split * R;
+}
+
 // Combine two partial base-2 log-sum-exp states (M1, s1) and (M2, s2), each
 // meaning M + log2(s).  Either may be empty (M = -inf, s = 0).
 __device__ __forceinline__ void lse_merge(float& M, float& s, float M2, float s2) {

@@ -257,8 +257,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     const int ln = lane & 31;  // query row of the B block / key row of the A block
     const int h = lane >> 5;   // lane half: contraction slots 8h..8h+7 of each 16
 
-    const int row0 = blockIdx.x * (WAVES * 32 * QB) + wave * (32 * QB);
-    const int split = blockIdx.y;
+    int row_block, split;
+    xcd_work(row_block, split);
+    const int row0 = row_block * (WAVES * 32 * QB) + wave * (32 * QB);
     const int j0 = split * a.keys_per_split;
     const int j1 = min(a.n_keys, j0 + a.keys_per_split);
     const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
@@ -588,7 +589,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     }
     if (a.n_split == 1 && a.cur) {
         resid = block_sum(resid, red);
-        if (tid == 0) a.resid_part[blockIdx.x] = resid;
+        if (tid == 0) a.resid_part[row_block] = resid;
     }
 }
 

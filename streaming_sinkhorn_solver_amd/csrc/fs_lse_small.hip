@@ -161,8 +161,9 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 31;
     const int h = lane >> 5;
-    const int row = blockIdx.x * (W * 32) + wave * 32 + ln;  // rows are padded: always readable
-    const int split = blockIdx.y;
+    int row_block, split;
+    xcd_work(row_block, split);
+    const int row = row_block * (W * 32) + wave * 32 + ln;  // rows are padded: always readable
     const int j0 = split * a.keys_per_split;
     const int j1 = min(a.n_keys, j0 + a.keys_per_split);
     const int ntiles = (j1 - j0 + TK - 1) / TK;
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     }
     if (a.n_split == 1 && a.cur) {
         resid = block_sum(resid, red);
-        if (tid == 0) a.resid_part[blockIdx.x] = resid;
+        if (tid == 0) a.resid_part[row_block] = resid;
     }
 }
 

@@ -2,7 +2,8 @@
 
     python -m streaming_sinkhorn_solver_amd.profiling stats DB OUT.md --command "..."
     python -m streaming_sinkhorn_solver_amd.profiling traffic FETCH_DB WRITE_DB OUT.json \
-        --copy-bytes B --kernel lse_mfma_kernel --command-fetch "..." --command-write "..."
+        --copy-bytes B --kernel lse_mfma_kernel --source fs_lse.hip \
+        --command-fetch "..." --command-write "..."
 
 `stats` tabulates kernel-trace durations (calls, mean, min, max, share).
 `traffic` turns the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of one
@@ -23,8 +24,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def kernel_source_sha(path: str = os.path.join(HERE, "csrc", "fs_lse.hip")) -> str:
-    with open(path, "rb") as fh:
+def kernel_source_sha(name: str = "fs_lse.hip") -> str:
+    """First 16 hex digits of the SHA-256 of a kernel source under csrc/."""
+    with open(os.path.join(HERE, "csrc", name), "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
@@ -74,7 +76,8 @@ def counter_per_dispatch(db: str, counter: str, name_substr: str):
 
 
 def write_traffic(fetch_db: str, write_db: str, out_json: str, copy_bytes: float,
-                  kernel: str, copy_kernel: str, commands: dict) -> dict:
+                  kernel: str, copy_kernel: str, commands: dict,
+                  source: str = "fs_lse.hip") -> dict:
     kib = 1024.0
     f_k, nf = counter_per_dispatch(fetch_db, "FETCH_SIZE", kernel)
     w_k, nw = counter_per_dispatch(write_db, "WRITE_SIZE", kernel)
@@ -83,7 +86,7 @@ def write_traffic(fetch_db: str, write_db: str, out_json: str, copy_bytes: float
     ff = copy_bytes / (f_c * kib)
     fw = copy_bytes / (w_c * kib)
     rec = {
-        "kernel": kernel, "kernel_source_sha": kernel_source_sha(),
+        "kernel": kernel, "kernel_source": source, "kernel_source_sha": kernel_source_sha(source),
         "fetch_kib_per_launch_raw": f_k, "write_kib_per_launch_raw": w_k,
         "copy_bytes": copy_bytes, "copy_fetch_kib_raw": f_c, "copy_write_kib_raw": w_c,
         "fetch_scale": ff, "write_scale": fw,
@@ -111,6 +114,7 @@ def main(argv=None):
     s2.add_argument("--copy-bytes", type=float, required=True)
     s2.add_argument("--kernel", default="lse_mfma_kernel")
     s2.add_argument("--copy-kernel", default="elementwise")
+    s2.add_argument("--source", default="fs_lse.hip", help="kernel source file under csrc/")
     s2.add_argument("--command-fetch", required=True)
     s2.add_argument("--command-write", required=True)
     a = ap.parse_args(argv)
@@ -119,7 +123,7 @@ def main(argv=None):
         print(a.out)
     else:
         rec = write_traffic(a.fetch_db, a.write_db, a.out, a.copy_bytes, a.kernel, a.copy_kernel,
-                            {"fetch": a.command_fetch, "write": a.command_write})
+                            {"fetch": a.command_fetch, "write": a.command_write}, a.source)
         print(json.dumps(rec, indent=1))
     return 0
 
