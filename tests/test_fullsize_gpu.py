@@ -1,0 +1,91 @@
+"""Full-size spot checks: each recipe at its real shape, in the precision and
+launch configuration bench.py times (same sizes, same score path, hence the
+same key-range splits and workgroup counts).
+
+After a few GPU iterations at the recipe's final eps, one more GPU f-update
+and g-update are compared, on 512 seeded rows and columns, with the oracle's
+single update from the same GPU potentials.  This isolates the kernels'
+error from trajectory drift at a cost of 512 m d + 512 n d per check.  The
+oracle sees the points the path computes with: the joint bounding-box shift
+applied in float32, and for bf16/fp16 paths the rounded points.
+
+Tolerances (max over the sampled entries, in units of eps), from the
+arithmetic of each path:
+  fp32 matrix path (C2, d = 64)     1e-4  fp32 rounding of the expanded score
+                                          c_score x.y + beta (|z2| ~ 1e2 in
+                                          base-2 units): ~1e-5 eps
+  bf16 path vs rounded (C3)         1e-4  fp32 accumulation of 512 exact
+                                          products: ~sqrt(d) 2^-24 c_score |x.y|
+                                          ~ 3e-5 eps at eps = 0.1
+  fp16 path vs rounded (C4)         5e-4  the same at d = 1024, eps = 0.01:
+                                          ~ 1e-4 to 4e-4 eps (little averaging
+                                          over keys in a concentrated plan)
+  d = 3 matrix path (C1, C5)        2e-4  the fp16 split's ~2^-21 relative
+                                          error per product under the path's
+                                          guard (c_score * max L1 * max|y| <= 2^9)
+"""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import bbox_shift, dev, host, round_bf16, round_f16
+from streaming_sinkhorn_solver_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+# recipe -> (score precision, tolerance in eps, expected path)
+RECIPES = {
+    "c1": ("auto", 2e-4, "fp32-small-mfma"),
+    "c2": ("fp32", 1e-4, "fp32-mfma"),
+    "c3": ("bf16", 1e-4, "bf16-mfma"),
+    "c4": ("fp16", 5e-4, "fp16-mfma"),
+    "c5": ("auto", 2e-4, "fp32-small-mfma"),
+}
+SAMPLES = 512
+WARM_ITERS = 3
+
+
+def _operands(w, prec):
+    s = bbox_shift(w.X, w.Y)
+    Xs = (w.X - s).astype(np.float32)
+    Ys = (w.Y - s).astype(np.float32)
+    if prec == "bf16":
+        return round_bf16(Xs), round_bf16(Ys)
+    if prec == "fp16":
+        return round_f16(Xs), round_f16(Ys)
+    return Xs, Ys
+
+
+@pytest.mark.parametrize("name", sorted(RECIPES))
+def test_full_size_one_step(fs, name):
+    import torch
+
+    from streaming_sinkhorn_solver_amd import binding
+
+    prec, tol, path = RECIPES[name]
+    w = workloads.make(name)
+    Xd, Yd, ad, bd = dev(w.X), dev(w.Y), dev(w.a), dev(w.b)
+    f = torch.empty(w.n, device="cuda")
+    g = torch.empty(w.m, device="cuda")
+    p = binding.fs_potentials_init(Xd, Yd, ad, bd, prec=prec, f=f, g=g)
+    assert p.info["path"] == path
+    binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, iters_per_stage=WARM_ITERS)
+    f1 = torch.empty_like(f)
+    g1 = torch.empty_like(g)
+    binding.fs_lse_update_f(p, w.eps, g, f1)
+    binding.fs_lse_update_g(p, w.eps, f1, g1)
+    torch.cuda.synchronize()
+    gh, f1h, g1h = host(g), host(f1), host(g1)
+    assert np.all(np.isfinite(f1h)) and np.all(np.isfinite(g1h))
+
+    X, Y = _operands(w, prec)
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(w.n, size=min(SAMPLES, w.n), replace=False))
+    cols = np.sort(rng.choice(w.m, size=min(SAMPLES, w.m), replace=False))
+    f_ref = oracle.f_update_rows(X, Y, w.b, gh, w.eps, rows)
+    g_ref = oracle.g_update_cols(X, Y, w.a, f1h, w.eps, cols)
+    ef = float(np.max(np.abs(f1h[rows] - f_ref))) / w.eps
+    eg = float(np.max(np.abs(g1h[cols] - g_ref))) / w.eps
+    print(f"{name}: f {ef:.2e} eps, g {eg:.2e} eps (tolerance {tol:g} eps), splits "
+          f"{p.info['f_splits']}/{p.info['g_splits']}")
+    assert ef <= tol and eg <= tol
