@@ -4,8 +4,8 @@
 Default workload (the recipe the headline metric is quoted on): n = m =
 50,000 points in 512-D, two 10-component Gaussian mixtures, Dirichlet(1)
 weights, eps = 0.1, bf16 matrix-core scores with fp32 accumulation.  One step
-is the whole hot path on resident inputs: problem preparation (shift,
-conversion, norms, log-weights), the alternating f/g iterations and the
+is the whole hot path on resident inputs: problem preparation (centring,
+conversion, per-point cost terms, log-weights), the alternating f/g iterations and the
 transport product (here the barycentric projection P.Y / a).
 
 ``--workload c1|c2|c4|c5`` runs one of the other recipes the same way (its own

@@ -60,11 +60,12 @@ typedef enum {
  * FP32_VALU (d <= 8 only): fp32 scores by vector FMA, one lane per row (the
  *   plain vector formulation; slower on gfx950, where exponentials and vector
  *   instructions share issue slots).
- * BF16 / FP16: points (after a common shift, below) are rounded to
- *   bfloat16 / float16 with round-to-nearest-even and multiplied on matrix
- *   cores with fp32 accumulation; |x|^2 and |y|^2 are taken from the rounded
- *   points, so the solver solves the problem of the rounded clouds exactly
- *   (up to fp32). */
+ * BF16 / FP16: the centred points (below) are rounded to bfloat16 /
+ *   float16 with round-to-nearest-even and multiplied on matrix cores with
+ *   fp32 accumulation; the per-point cost terms A, B stay fp32 from the
+ *   unrounded points, so only the product x'.y' carries the rounding.
+ *   The effective cost is C~_ij = A_i + B_j - 2 x~'_i.y~'_j, where x~', y~'
+ *   are the rounded centred points. */
 typedef enum {
     FS_PREC_AUTO = 0,
     FS_PREC_FP32 = 1,
@@ -116,9 +117,14 @@ size_t fs_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t dv_max,
                           fs_score_prec prec);
 
 /* Creates a problem: copies X (n x d) and Y (m x d) into the workspace after
- * subtracting one common shift (the midpoint of the joint bounding box, which
- * leaves every C_ij and hence f, g unchanged), converts them to the score
- * element type, and precomputes |x|^2, |y|^2 and log-weights.  Writes f = 0
+ * centring each cloud on the midpoint of its own bounding box (nu for X, mu
+ * for Y, each computed as (min + max) * 0.5f per coordinate in fp32),
+ * converts the centred points x' = x - nu, y' = y - mu (fp32 subtraction) to
+ * the score element type, and precomputes the per-point cost terms
+ * A_i = |x_i - mu|^2 - |nu - mu|^2/2 and B_j = |y_j - nu|^2 - |nu - mu|^2/2
+ * (fp32, from the unrounded points) and the log-weights.  Exactly,
+ * C_ij = |x_i - y_j|^2 = A_i + B_j - 2 x'_i.y'_j, so f and g do not depend
+ * on the centres.  Writes f = 0
  * and g = 0 (f: n floats, g: m floats; either may be NULL to skip).
  * a (n) and b (m) are the weights; they must be > 0 and finite (sums are used
  * as given).  Synchronises once to read back a validity flag:

@@ -32,7 +32,7 @@ struct fs_problem {
     int f_split, f_kps;  // split count / keys per split of the f-update (rows X, keys Y)
     int g_split, g_kps;
     Cloud X, Y;
-    float* shift;
+    float* centre;  // [2][d]: centre of X, then of Y
     float* bbox_min;
     float* bbox_max;
     int* flag;
@@ -169,7 +169,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 }
 
 struct Layout {
-    size_t shift, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
+    size_t centre, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
         vt, krec, krec16, kguard, total;
 };
 
@@ -182,7 +182,7 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
         return at;
     };
     const int64_t np = pad_rows(n), mp = pad_rows(m);
-    L.shift = take(sizeof(float) * d);
+    L.centre = take(sizeof(float) * 2 * d);
     L.bmin = take(sizeof(float) * 2 * kBboxParts * d);
     L.bmax = take(sizeof(float) * 2 * kBboxParts * d);
     L.flag = take(sizeof(int) * 4);
@@ -366,7 +366,7 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
     p->f_kps = sh.f_kps;
     p->g_split = sh.g_split;
     p->g_kps = sh.g_kps;
-    p->shift = (float*)(w + L.shift);
+    p->centre = (float*)(w + L.centre);
     p->bbox_min = (float*)(w + L.bmin);
     p->bbox_max = (float*)(w + L.bmax);
     p->flag = (int*)(w + L.flag);
@@ -390,14 +390,14 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if ((e = launch_zero_flag(p->flag, s)) != hipSuccess) goto hip_error;
-    if ((e = launch_bbox(X, n, Y, m, d, p->bbox_min, p->bbox_max, kBboxParts, p->shift, s)) !=
+    if ((e = launch_bbox(X, n, Y, m, d, p->bbox_min, p->bbox_max, kBboxParts, p->centre, s)) !=
         hipSuccess)
         goto hip_error;
-    if ((e = launch_convert(X, n, p->X.n_pad, d, p->dp, p->path, p->shift, p->X.ops, p->X.nrm,
-                            p->flag, s)) != hipSuccess)
+    if ((e = launch_convert(X, n, p->X.n_pad, d, p->dp, p->path, p->centre, p->centre + d,
+                            p->X.ops, p->X.nrm, p->flag, s)) != hipSuccess)
         goto hip_error;
-    if ((e = launch_convert(Y, m, p->Y.n_pad, d, p->dp, p->path, p->shift, p->Y.ops, p->Y.nrm,
-                            p->flag, s)) != hipSuccess)
+    if ((e = launch_convert(Y, m, p->Y.n_pad, d, p->dp, p->path, p->centre + d, p->centre,
+                            p->Y.ops, p->Y.nrm, p->flag, s)) != hipSuccess)
         goto hip_error;
     if (p->path == PATH_SMALL &&
         ((e = launch_row_l1max((const float*)p->X.ops, n, d, p->X.l1max, s)) != hipSuccess ||
@@ -416,7 +416,7 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
             if (flag & 1) return fail(FS_ERR_NONFINITE, "X or Y holds a NaN or Inf");
             if (flag & 2) return fail(FS_ERR_NONFINITE, "a weight is <= 0, subnormal, NaN or Inf");
             return fail(FS_ERR_INVALID_ARG,
-                        "a shifted coordinate overflows the fp16 range; scale the points "
+                        "a centred coordinate overflows the fp16 range; scale the points "
                         "(and eps by the square of the scale) or use FS_PREC_BF16");
         }
     }

@@ -29,8 +29,8 @@ constexpr int kKeyTile = 32;
 
 // One side of the problem, stored in the caller's workspace.
 struct Cloud {
-    void* ops;      // shifted, converted points [n_pad][dp] (fp32 / bf16 / fp16), zero padded
-    float* nrm;     // |p~|^2 from the converted points [n]
+    void* ops;      // centred, converted points [n_pad][dp] (fp32 / bf16 / fp16), zero padded
+    float* nrm;     // cost term A(x) or B(y) of the centred split [n]
     float* lw2;     // log2 of the weights [n]
     float* w;       // copy of the weights [n]
     int64_t n;
@@ -82,11 +82,11 @@ struct TransportArgs {
     const void* rows;        // X~ [n_pad][dp]
     const float* row_lse2;   // exact LSE2 of each row under the current g
     const float* row_pot;    // f
-    const float* row_nrm;    // |x~|^2
+    const float* row_nrm;    // rows' cost term (A(x) for X, B(y) for Y)
     const float* row_w;      // a
     const void* keys;        // Y~ [m_pad][dp]
     const float* key_pot;    // g
-    const float* key_nrm;    // |y~|^2
+    const float* key_nrm;    // keys' cost term
     const float* key_lw2;    // log2 b
     const float* V;          // fp32 [m][dv] (vector path)
     const void* Vt;          // f16 [dv][m_pad] scaled copy (matrix path)
@@ -100,10 +100,11 @@ struct TransportArgs {
 // ---- launchers (each returns the first HIP error, enqueues on `s`) ----
 hipError_t launch_zero_flag(int* flag, hipStream_t s);
 hipError_t launch_bbox(const float* X, int64_t n, const float* Y, int64_t m, int d,
-                       float* part_min, float* part_max, int parts_per_cloud, float* shift,
+                       float* part_min, float* part_max, int parts_per_cloud, float* centres,
                        hipStream_t s);
 hipError_t launch_convert(const float* P, int64_t n, int64_t n_pad, int d, int dp, int path,
-                          const float* shift, void* ops, float* nrm, int* flag, hipStream_t s);
+                          const float* own_centre, const float* other_centre, void* ops,
+                          float* nrm, int* flag, hipStream_t s);
 hipError_t launch_weights(const float* w, int64_t n, float* lw2, float* wcopy, float* pot,
                           int* flag, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);

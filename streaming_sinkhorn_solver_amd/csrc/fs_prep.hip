@@ -1,17 +1,25 @@
-// fs_prep.hip -- one-time preparation of a problem: common shift of both
-// clouds, conversion to the score element type, squared norms, log-weights
-// and input validation.
+// fs_prep.hip -- one-time preparation of a problem: centring of each cloud,
+// conversion to the score element type, the per-point terms of the expanded
+// cost, log-weights and input validation.
 //
 // The pages ("FlashSinkhorn" explainer, "Method" part 1) call the bias terms
 // of the attention form "precomputed log-weight biases"; this pass computes
 // everything of that kind that does not depend on the potentials, once.
 //
-// Common shift.  C_ij = |x_i - y_j|^2 is unchanged when both clouds move by
-// the same vector, so f and g are unchanged too.  Moving both clouds to the
-// midpoint of their joint bounding box keeps |x|^2 and |y|^2 small, which
-// bounds the cancellation of the expanded form |x|^2 + |y|^2 - 2 x.y that the
-// streaming kernels evaluate in fp32.  Min and max are exact, so the shift
-// (min + max) * 0.5 is reproducible bit for bit by any IEEE implementation.
+// Centring.  With nu the centre of X, mu the centre of Y, x' = x - nu,
+// y' = y - mu and delta = nu - mu, the cost splits exactly as
+//   |x - y|^2 = A(x) + B(y) - 2 x'.y',
+//   A(x) = |x - mu|^2 - |delta|^2 / 2,   B(y) = |y - nu|^2 - |delta|^2 / 2
+// (expand |x' - y' + delta|^2).  The streaming kernels contract x'.y' on the
+// matrix cores and take A, B (fp32, from the unrounded points) as row and key
+// terms.  Centring each cloud on its own keeps the contracted operands as
+// small as the clouds' spreads allow, so the rounding of x', y' to bf16/fp16
+// and the fp32 accumulation move the score by as little as possible; a shift
+// common to both clouds would leave the offset between them (a cluster of Y
+// displaced from X, say) in the operands, where it multiplies the rounding
+// error.  Each centre is the midpoint of its cloud's bounding box: min and max
+// are exact, so (min + max) * 0.5 is reproducible bit for bit by any IEEE
+// implementation.
 #include "fs_device.hpp"
 #include "fs_internal.h"
 
@@ -46,22 +54,25 @@ __global__ __launch_bounds__(256) void bbox_partial_kernel(const float* __restri
     pmax[(int64_t)part * d + k] = mx;
 }
 
+// Centre of one cloud from its parts' boxes.  grid = (ceil(d/256), 2): y-block
+// 0 reduces X's parts into centre[0..d), 1 Y's parts into centre[d..2d).
 __global__ __launch_bounds__(256) void bbox_final_kernel(const float* __restrict__ pmin,
                                                          const float* __restrict__ pmax,
-                                                         int total_parts, int d,
-                                                         float* __restrict__ shift) {
+                                                         int parts, int d,
+                                                         float* __restrict__ centre) {
     const int k = blockIdx.x * 256 + threadIdx.x;
     if (k >= d) return;
+    const int64_t base = (int64_t)blockIdx.y * parts * d;
     float mn = INFINITY, mx = -INFINITY;
-    for (int p = 0; p < total_parts; ++p) {
-        mn = fminf(mn, pmin[(int64_t)p * d + k]);
-        mx = fmaxf(mx, pmax[(int64_t)p * d + k]);
+    for (int p = 0; p < parts; ++p) {
+        mn = fminf(mn, pmin[base + (int64_t)p * d + k]);
+        mx = fmaxf(mx, pmax[base + (int64_t)p * d + k]);
     }
-    // Midpoint of the joint bounding box; 0 if the coordinate is all-NaN
-    // (the convert pass reports the NaN).
-    float s = (mn + mx) * 0.5f;
-    if (!(s == s) || s == INFINITY || s == -INFINITY) s = 0.f;
-    shift[k] = s;
+    // Midpoint of the bounding box; 0 if the coordinate is all-NaN or
+    // unbounded (the convert pass reports the NaN / Inf).
+    float c = (mn + mx) * 0.5f;
+    if (!(fabsf(c) <= 3.402823466e38f)) c = 0.f;
+    centre[(int64_t)blockIdx.y * d + k] = c;
 }
 
 template <typename T>
@@ -73,34 +84,38 @@ __device__ __forceinline__ __bf16 to_elem<__bf16>(float v) { return (__bf16)v; }
 template <>
 __device__ __forceinline__ _Float16 to_elem<_Float16>(float v) { return (_Float16)v; }  // RNE
 
-// One wave per row: ops[i][k] = T(P[i][k] - shift[k]) (0 in the padding),
-// nrm[i] = sum_k float(ops[i][k])^2 in a fixed order.
+// One wave per row: ops[i][k] = T(P[i][k] - own[k]) (0 in the padding) and
+// the row's cost term |P[i] - oth|^2 - |own - oth|^2 / 2 in fp32, summed in a
+// fixed order (own: this cloud's centre, oth: the other cloud's).
 template <typename T>
 __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ P, int64_t n,
                                                       int64_t n_pad, int d, int dp,
-                                                      const float* __restrict__ shift,
+                                                      const float* __restrict__ own,
+                                                      const float* __restrict__ oth,
                                                       T* __restrict__ ops,
                                                       float* __restrict__ nrm,
                                                       int* __restrict__ flag) {
     const int lane = threadIdx.x & 63;
     const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (i >= n_pad) return;
-    float acc = 0.f;
+    float acc = 0.f, off = 0.f;
     int bad = 0;
     for (int k = lane; k < dp; k += 64) {
         T t = to_elem<T>(0.f);
         if (i < n && k < d) {
             const float v = P[i * d + k];
             if (!(fabsf(v) <= 3.402823466e38f)) bad |= FLAG_NONFINITE_POINT;
-            t = to_elem<T>(v - shift[k]);
-            const float tf = (float)t;
-            if (!(fabsf(tf) <= 3.402823466e38f)) bad |= FLAG_RANGE;
-            acc += tf * tf;
+            t = to_elem<T>(v - own[k]);
+            if (!(fabsf((float)t) <= 3.402823466e38f)) bad |= FLAG_RANGE;
+            const float u = v - oth[k], c = own[k] - oth[k];
+            acc = fmaf(u, u, acc);
+            off = fmaf(c, c, off);
         }
         ops[i * dp + k] = t;
     }
     acc = wave_sum(acc);
-    if (i < n && lane == 0) nrm[i] = acc;
+    off = wave_sum(off);
+    if (i < n && lane == 0) nrm[i] = fmaf(off, -0.5f, acc);
     if (bad) atomicOr(flag, bad);
 }
 
@@ -133,33 +148,34 @@ hipError_t launch_zero_flag(int* flag, hipStream_t s) {
 }
 
 hipError_t launch_bbox(const float* X, int64_t n, const float* Y, int64_t m, int d,
-                       float* part_min, float* part_max, int parts, float* shift,
+                       float* part_min, float* part_max, int parts, float* centres,
                        hipStream_t s) {
     const dim3 grid((d + 255) / 256, parts);
     bbox_partial_kernel<<<grid, 256, 0, s>>>(X, n, d, parts, part_min, part_max);
     bbox_partial_kernel<<<grid, 256, 0, s>>>(Y, m, d, parts, part_min + (int64_t)parts * d,
                                              part_max + (int64_t)parts * d);
-    bbox_final_kernel<<<(d + 255) / 256, 256, 0, s>>>(part_min, part_max, 2 * parts, d, shift);
+    bbox_final_kernel<<<dim3((d + 255) / 256, 2), 256, 0, s>>>(part_min, part_max, parts, d,
+                                                               centres);
     return hipGetLastError();
 }
 
 hipError_t launch_convert(const float* P, int64_t n, int64_t n_pad, int d, int dp, int path,
-                          const float* shift, void* ops, float* nrm, int* flag,
+                          const float* own, const float* oth, void* ops, float* nrm, int* flag,
                           hipStream_t s) {
     const int64_t blocks = (n_pad + 3) / 4;
     switch (path) {
         case PATH_VALU:
         case PATH_SMALL:
         case PATH_MFMA_F32:
-            convert_kernel<float><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, shift,
+            convert_kernel<float><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, own, oth,
                                                          (float*)ops, nrm, flag);
             break;
         case PATH_MFMA_BF16:
-            convert_kernel<__bf16><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, shift,
+            convert_kernel<__bf16><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, own, oth,
                                                           (__bf16*)ops, nrm, flag);
             break;
         case PATH_MFMA_F16:
-            convert_kernel<_Float16><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, shift,
+            convert_kernel<_Float16><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, own, oth,
                                                             (_Float16*)ops, nrm, flag);
             break;
         default:

@@ -5,8 +5,9 @@ Tolerances (on every potential entry, after the same number of iterations):
   fp32 score paths       max|f - f_ref|, max|g - g_ref| <= 1e-3 eps
   bf16/fp16 score paths  <= 2e-2 eps against the oracle on the original
                          points, and <= 2e-3 eps against the oracle run on the
-                         rounded points the path actually uses (isolates
-                         kernel error from quantisation)
+                         problem the path actually solves (the rounded
+                         centred points plus the fp32 per-point cost terms;
+                         isolates kernel error from quantisation)
   transport              ||U - U_ref||_F / ||U_ref||_F <= 1e-3
 Sizes span several tiles and splits with ragged tails; the oracle finishes
 each case in seconds.
@@ -15,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import dev, gpu_solve, host, max_err, oracle_solve, rounded_operands
+from helpers import RoundedProblem, dev, gpu_solve, host, max_err, oracle_solve
 from streaming_sinkhorn_solver_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -120,14 +121,14 @@ def test_lowp_mfma_path(fs, prec, d, n, m):
     X, Y, a, b, eps = w.X, w.Y, w.a, w.b, w.eps
     p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=10, prec=prec)
     assert p.info["path"] == f"{prec}-mfma"
-    Xr, Yr = rounded_operands(X, Y, prec)
-    rr = oracle_solve(Xr, Yr, a, b, eps=eps, iters=10)
+    rr = RoundedProblem(X, Y, prec).solve(a, b, eps=eps, iters=10)
     assert max_err(host(f), rr["f"]) <= TOL_LOWP_ROUNDED * eps
     assert max_err(host(g), rr["g"]) <= TOL_LOWP_ROUNDED * eps
-    if prec == "bf16" and d < 200:
-        # bf16 keeps 8 significant bits: at d < ~200 on this distribution the
-        # rounding of the points alone moves f by more than 2e-2 eps (the
-        # rounded-point check above is the kernel's parity check).
+    if prec == "bf16" and d < 64:
+        # bf16 keeps 8 significant bits: at d = 16 on this distribution the
+        # rounding of the centred points alone moves f by about 3e-2 eps
+        # (the oracle on the path's own problem, above, is the kernel's
+        # parity check there).
         return
     ref = oracle_solve(X, Y, a, b, eps=eps, iters=10)
     assert max_err(host(f), ref["f"]) <= TOL_LOWP * eps
@@ -228,11 +229,12 @@ def test_transport(fs, prec, d):
     binding.fs_apply_transport(p, eps, f, g, Vd, T, divide_by_a=True)
     torch.cuda.synchronize()
     if prec in ("bf16", "fp16"):
-        Xr, Yr = rounded_operands(X, Y, prec)
+        rp = RoundedProblem(X, Y, prec)
+        U_ref = rp.transport(a, b, host(f), host(g), V, eps)
+        T_ref = rp.transport(a, b, host(f), host(g), V, eps, divide_by_a=True)
     else:
-        Xr, Yr = X, Y
-    U_ref = oracle.transport(Xr, Yr, a, b, host(f), host(g), V, eps)
-    T_ref = oracle.transport(Xr, Yr, a, b, host(f), host(g), V, eps, divide_by_a=True)
+        U_ref = oracle.transport(X, Y, a, b, host(f), host(g), V, eps)
+        T_ref = oracle.transport(X, Y, a, b, host(f), host(g), V, eps, divide_by_a=True)
     for got, ref in ((host(U), U_ref), (host(T), T_ref)):
         rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
         assert rel <= 1e-3, rel
@@ -249,20 +251,29 @@ def _c4_annealed(prec):
 
 def test_annealing_matches_rounded_oracle(fs):
     # Kernel exactness on the annealed schedule: the fp16 path solves the
-    # problem of the fp16-rounded clouds (norms from the rounded points).
+    # problem of the rounded centred clouds exactly up to fp32.
     w, f, g = _c4_annealed("fp16")
-    Xr, Yr = rounded_operands(w.X, w.Y, "fp16")
-    rr = oracle_solve(Xr, Yr, w.a, w.b, eps=w.eps, eps_start=w.eps_start, n_stages=4, iters=6)
+    rr = RoundedProblem(w.X, w.Y, "fp16").solve(w.a, w.b, eps=w.eps, eps_start=w.eps_start,
+                                                n_stages=4, iters=6)
     assert max_err(host(f), rr["f"]) <= TOL_LOWP_ROUNDED * w.eps
     assert max_err(host(g), rr["g"]) <= TOL_LOWP_ROUNDED * w.eps
 
 
-@pytest.mark.xfail(strict=True, reason=(
-    "fp16 rounding of the 1024-D points alone moves f by about 2e-4 (max over "
-    "entries) at eps = 0.01, just above 2e-2 eps; a compensated score mode is "
-    "needed for the annealed recipe's final stages"))
-def test_annealing_fp16_against_unrounded_oracle(fs):
+def test_annealing_fp16_against_oracle(fs):
+    # The parity bar on the original points at the final eps = 0.01: fp16
+    # rounding of the centred 1024-D points moves f by about 5e-3 eps here.
     w, f, g = _c4_annealed("fp16")
+    ref = oracle_solve(w.X, w.Y, w.a, w.b, eps=w.eps, eps_start=w.eps_start, n_stages=4, iters=6)
+    assert max_err(host(f), ref["f"]) <= TOL_LOWP * w.eps
+    assert max_err(host(g), ref["g"]) <= TOL_LOWP * w.eps
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "bf16 keeps 8 significant bits: on the annealed 1024-D recipe at eps = 0.01 "
+    "the rounding of the centred points alone moves f by about 4.5e-2 eps, over "
+    "the 2e-2 eps bar; that recipe runs in fp16 (same matrix-core rate)"))
+def test_annealing_bf16_against_oracle(fs):
+    w, f, g = _c4_annealed("bf16")
     ref = oracle_solve(w.X, w.Y, w.a, w.b, eps=w.eps, eps_start=w.eps_start, n_stages=4, iters=6)
     assert max_err(host(f), ref["f"]) <= TOL_LOWP * w.eps
     assert max_err(host(g), ref["g"]) <= TOL_LOWP * w.eps
