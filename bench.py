@@ -22,7 +22,11 @@ Prints one JSON line with
              one exponential per pair against the exponential peak, 256 CUs x
              32 lanes/clock x 2.4 GHz = 19.66e12/s.  `traffic` is the
              per-launch HBM bytes from the committed rocprofv3 counter summary
-             when it was taken on the current kernel source, else null
+             when it was taken on the current kernel source, else null.
+             `peak_measured` / `frac_measured`: the same against the rate a
+             probe kernel of that unit alone (fs_probe_peak: independent chains
+             of the score path's matrix instruction, or of v_exp_f32) reaches
+             on this GPU right after the timed region
   cpu_baseline  the float64 oracle's f-update timed on this host's cores on a
              bounded sample of rows of the same workload, scaled to
              iterations per second
@@ -42,6 +46,9 @@ sys.path.insert(0, HERE)
 METRIC = "Sinkhorn iters/sec and pair-evals/sec at n=m=50k, d=512; % of roofline"
 CSRC = os.path.join(HERE, "streaming_sinkhorn_solver_amd", "csrc")
 EXP_PEAK = 256 * 32 * 2.4e9 / 1e12  # T exponentials/s
+
+# recipe -> the fs_probe_peak kind of its bounding unit
+PROBES = {"c1": "exp", "c2": "mfma-fp32", "c3": "mfma-bf16", "c4": "mfma-fp16", "c5": "exp"}
 
 # recipe -> (score precision, roofline peak, unit, dtype label, description)
 RECIPES = {
@@ -235,9 +242,14 @@ def main():
               "c2": "lse_mfma_kernel<fp32, d_pad 64>",
               "c3": "lse_mfma_kernel<bf16, d_pad 512>",
               "c4": "lse_mfma_kernel<fp16, d_pad 1024>"}[wl]
+    sink = torch.zeros(1, device=dev)
+    peak_measured = binding.fs_probe_peak(PROBES[wl], sink) / 1e12
     roofline = {"bound": "mfma" if unit == "TFLOP/s" else "alu",
                 "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic_per_launch(wl),
+                "peak_measured": round(peak_measured, 2),
+                "frac_measured": round(achieved / peak_measured, 4),
+                "peak_probe": PROBES[wl],
                 "kernel": kernel + " (one half-step)",
                 "mean_launch_ms": round(lse_mean_ms, 4), "launches": stats["lse_launches"]}
     out = {

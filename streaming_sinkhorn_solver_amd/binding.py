@@ -1,4 +1,5 @@
-"""Thin ctypes binding of ``libfs_sinkhorn.so`` (the C ABI in include/fs_sinkhorn.h).
+"""Thin ctypes binding of ``libfs_sinkhorn.so`` (the C ABI in include/fs_sinkhorn.h
+and include/fs_probe.h).
 
 Argument marshalling only: torch tensors provide device memory and the current
 HIP stream; every step of the solver runs in the library's kernels.  If the
@@ -19,6 +20,7 @@ __all__ = [
     "Problem", "load", "lib_path", "fs_workspace_bytes", "fs_potentials_init",
     "fs_lse_update_f", "fs_lse_update_g", "fs_marginal_residual", "fs_sinkhorn_solve",
     "fs_apply_transport", "fs_problem_info", "fs_status_string", "fs_last_error", "solve",
+    "PROBE_KINDS", "fs_probe_peak",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -26,6 +28,7 @@ FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
 PREC_AUTO, PREC_FP32, PREC_BF16, PREC_FP16, PREC_FP32_VALU = range(5)
 _PREC_NAMES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16, "fp16": PREC_FP16,
                "fp32-valu": PREC_FP32_VALU}
+PROBE_KINDS = {"mfma-bf16": 1, "mfma-fp16": 2, "mfma-fp32": 3, "exp": 4}
 PATH_NAMES = {0: "fp32-valu", 1: "fp32-mfma", 2: "bf16-mfma", 3: "fp16-mfma", 4: "fp32-small-mfma"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +104,8 @@ def load():
     lib.fs_last_error.argtypes = []
     lib.fs_problem_info.restype = ctypes.c_int
     lib.fs_problem_info.argtypes = [_vp] + [ctypes.POINTER(i32)] * 4
+    lib.fs_probe_peak.restype = ctypes.c_int
+    lib.fs_probe_peak.argtypes = [ctypes.c_int, _fp, i32, _vp, ctypes.POINTER(ctypes.c_double)]
     _LIB = lib
     return lib
 
@@ -245,6 +250,18 @@ def fs_problem_info(p: Problem) -> dict:
     path, dp, fs_, gs = (v.value for v in vals)
     return {"path": PATH_NAMES.get(path, str(path)), "d_pad": dp, "f_splits": fs_,
             "g_splits": gs}
+
+
+def fs_probe_peak(kind: str, sink, reps: int = 9, stream=None) -> float:
+    """Median rate of the unit probe `kind` (a key of PROBE_KINDS): flop/s for
+    the matrix-core probes, exponentials/s for "exp".  `sink` is a device
+    float tensor of >= 1 element."""
+    rate = ctypes.c_double()
+    if sink.numel() < 1:
+        raise ValueError("sink must have at least one element")
+    _check(load().fs_probe_peak(PROBE_KINDS[kind], _dev(sink, "sink"), int(reps),
+                                _stream(stream), ctypes.byref(rate)), "fs_probe_peak")
+    return rate.value
 
 
 def solve(X, Y, a, b, *, eps: float, iters: int, prec="auto", n_stages: int = 1,

@@ -12,11 +12,13 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
 
 #include "fs_internal.h"
+#include "fs_probe.h"
 #include "fs_sinkhorn.h"
 
 using namespace fs;
@@ -622,6 +624,40 @@ const char* fs_status_string(fs_status s) {
 }
 
 const char* fs_last_error(void) { return g_err.c_str(); }
+
+fs_status fs_probe_peak(fs_probe_kind kind, float* sink, int32_t reps, void* stream,
+                        double* rate) {
+    if (kind < FS_PROBE_MFMA_BF16 || kind > FS_PROBE_EXP)
+        return fail(FS_ERR_INVALID_ARG, "unknown fs_probe_kind %d", (int)kind);
+    if (reps < 1 || reps > 64) return fail(FS_ERR_INVALID_ARG, "reps must be in [1, 64]");
+    if (!sink || !rate) return fail(FS_ERR_INVALID_ARG, "NULL sink or rate");
+    const int blocks = probe_blocks();
+    if (blocks <= 0) return fail(FS_ERR_DEVICE, "no usable device for the probe");
+    hipStream_t s = (hipStream_t)stream;
+    std::vector<hipEvent_t> ev(2 * reps, nullptr);
+    std::vector<double> r;
+    hipError_t e = hipSuccess;
+    for (auto& x : ev)
+        if ((e = hipEventCreate(&x)) != hipSuccess) break;
+    if (e == hipSuccess) e = launch_probe((int)kind, blocks, sink, s);  // untimed
+    for (int i = 0; e == hipSuccess && i < reps; ++i) {
+        if ((e = hipEventRecord(ev[2 * i], s)) != hipSuccess) break;
+        if ((e = launch_probe((int)kind, blocks, sink, s)) != hipSuccess) break;
+        e = hipEventRecord(ev[2 * i + 1], s);
+    }
+    if (e == hipSuccess) e = hipEventSynchronize(ev[2 * reps - 1]);
+    for (int i = 0; e == hipSuccess && i < reps; ++i) {
+        float ms = 0.f;
+        if ((e = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1])) != hipSuccess) break;
+        r.push_back(probe_work_per_launch((int)kind, blocks) / (ms * 1e-3));
+    }
+    for (auto x : ev)
+        if (x) (void)hipEventDestroy(x);
+    if (e != hipSuccess) return hip_fail(e, "fs_probe_peak");
+    std::sort(r.begin(), r.end());
+    *rate = r.size() % 2 ? r[r.size() / 2] : 0.5 * (r[r.size() / 2 - 1] + r[r.size() / 2]);
+    return FS_OK;
+}
 
 fs_status fs_problem_info(const fs_problem* p, int32_t* path, int32_t* d_pad, int32_t* f_splits,
                           int32_t* g_splits) {

@@ -109,6 +109,11 @@ hipError_t launch_weights(const float* w, int64_t n, float* lw2, float* wcopy, f
                           int* flag, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
+// ---- throughput probes (fs_probe.hip) ----
+int probe_blocks();  // workgroups per probe launch on the current device; 0 on error
+double probe_work_per_launch(int kind, int blocks);  // flops or exponentials
+hipError_t launch_probe(int kind, int blocks, float* sink, hipStream_t s);
+
 // Streaming LSE pass (+ merge when split).  `path` selects the kernel family,
 // `dp` the padded dimension.
 // ev_begin/ev_end (may be null) are recorded on `s` right before and after

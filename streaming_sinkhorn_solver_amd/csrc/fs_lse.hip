@@ -162,6 +162,16 @@ constexpr int kValuPerSlot = FS_VALU_PER_SLOT;  // epilogue instructions per ope
 #ifndef FS_VALU_MASK
 #define FS_VALU_MASK 0x002
 #endif
+#ifdef FS_EXACT_MAX
+constexpr bool kLazyRef = false;
+#else
+constexpr bool kLazyRef = true;  // two waves per SIMD: lazy LSE reference (below)
+#endif
+// Lazy reference: a tile's terms 2^(z2 - R) are summed against the running
+// reference R as they come; only when some lane's tile sum is not at most
+// this bound (a score more than ~64 above R, or R still -inf) does the wave
+// move R to the exact running maximum and rescale.
+constexpr float kLazyBound = 0x1p64f;
 
 // Workgroup barrier without the memory fence of __syncthreads(): only this
 // wave's LDS operations are waited for.  (The fence would also wait for every
@@ -244,10 +254,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     constexpr int MF_PER_FRAG = QB * (OP == OP_F32 ? 4 : 1);
     static_assert(NBUF == 2 || NBUF == 4, "pipeline depth");
 
-    __shared__ __attribute__((aligned(16))) uint4 kbuf0[TILE_CHUNKS];
-    __shared__ __attribute__((aligned(16))) uint4 kbuf1[TILE_CHUNKS];
-    __shared__ __attribute__((aligned(16))) uint4 kbuf2[NBUF > 2 ? TILE_CHUNKS : 1];
-    __shared__ __attribute__((aligned(16))) uint4 kbuf3[NBUF > 3 ? TILE_CHUNKS : 1];
+    constexpr int TILE_BYTES = TILE_CHUNKS * 16;
+    __shared__ __attribute__((aligned(16))) uint4 kbuf[NBUF * TILE_CHUNKS];
     __shared__ __attribute__((aligned(16))) float bkeys[KPS_MAX];
     __shared__ float red[16];
 
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         }
     };
     auto buf = [&](int i) __attribute__((always_inline)) -> uint4* {
-        return i == 0 ? kbuf0 : i == 1 ? kbuf1 : i == 2 ? kbuf2 : kbuf3;
+        return kbuf + i * TILE_CHUNKS;
     };
 
     // prologue: tiles 0..NBUF-2 in flight (every split holds at least one
@@ -358,17 +366,35 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     // them, and the schedule is pinned to that order (left alone, the
     // scheduler sinks each read next to its use and every matrix instruction
     // waits out a full LDS round trip).
-    int abase[JB];
+    // An LDS read takes a 16-bit immediate offset, so slots that start at or
+    // beyond 64 KiB address from a second set of bases, abase + 64 KiB.  With
+    // two waves per SIMD there are registers to spare and the set is kept in
+    // registers (opaque to the compiler, which would otherwise form every
+    // such fragment address with a vector add in every stage); with one wave
+    // per SIMD the resident block leaves none, and the adds stay.
+    constexpr bool HI_BASES = WAVES == 8 && NBUF * TILE_BYTES > 0x10000;
+    int abase[JB], abase_hi[JB];
 #pragma unroll
-    for (int j = 0; j < JB; ++j) abase[j] = (ln * CPR + ((2 * j + h) ^ (ln & SWZ))) * 16;
-    auto frag_off = [&](int g) __attribute__((always_inline)) {
-        return abase[g % JB] + (g / JB) * (2 * JB * 16);
+    for (int j = 0; j < JB; ++j) {
+        abase[j] = (ln * CPR + ((2 * j + h) ^ (ln & SWZ))) * 16;
+        abase_hi[j] = abase[j] + 0x10000;
+        if constexpr (HI_BASES) asm volatile("" : "+v"(abase_hi[j]));
+    }
+    // fragment g of the tile in slot I
+    auto frag = [&](auto i_c, int g) __attribute__((always_inline)) -> uint4 {
+        constexpr int OFF = decltype(i_c)::value * TILE_BYTES;
+        const char* base = (const char*)kbuf;
+        if constexpr (OFF >= 0x10000)
+            return *(const uint4*)(base + abase_hi[g % JB] + (OFF - 0x10000) +
+                                   (g / JB) * (2 * JB * 16));
+        else
+            return *(const uint4*)(base + abase[g % JB] + OFF + (g / JB) * (2 * JB * 16));
     };
     // Start a tile: seed the accumulators with the tile's key biases
     // (accumulator register r of lane (ln, h) holds the pair of row ln with
     // key 8*(r/4) + 4*h + (r%4) of the tile) and put the first AP fragments
     // in flight.
-    auto ring_begin = [&](const char* kb, const float* bb, uint4 (&av)[AP], f32x16 (&acc)[QB])
+    auto ring_begin = [&](auto i_c, const float* bb, uint4 (&av)[AP], f32x16 (&acc)[QB])
                           __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -381,11 +407,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
                 acc[qb][4 * qq + 3] = v.w;
             }
 #pragma unroll
-        for (int g = 0; g < AP; ++g) av[g] = *(const uint4*)(kb + frag_off(g));
+        for (int g = 0; g < AP; ++g) av[g] = frag(i_c, g);
     };
     // fragments [G0, G1): their matrix instructions, each followed by the
     // read that refills its ring slot with fragment g + AP
-    auto ring_steps = [&](const char* kb, uint4 (&av)[AP], f32x16 (&acc)[QB], auto g0_c,
+    auto ring_steps = [&](auto i_c, uint4 (&av)[AP], f32x16 (&acc)[QB], auto g0_c,
                           auto g1_c) __attribute__((always_inline)) {
         constexpr int G0 = decltype(g0_c)::value;
         constexpr int G1 = decltype(g1_c)::value;
@@ -393,7 +419,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         for (int g = G0; g < G1; ++g) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma_step<OP>(av[g % AP], q[qb][g], acc[qb]);
-            if (g + AP < NG) av[g % AP] = *(const uint4*)(kb + frag_off(g + AP));
+            if (g + AP < NG) av[g % AP] = frag(i_c, g + AP);
         }
     };
     // Pins the order of the current scheduling region for fragments
@@ -418,12 +444,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     using Zero = std::integral_constant<int, 0>;
     using NGc = std::integral_constant<int, NG>;
     // the whole score tile (key biases `bb`) in one pinned region
-    auto mfma_tile = [&](const uint4* src, const float* bb, f32x16 (&acc)[QB])
+    auto mfma_tile = [&](auto i_c, const float* bb, f32x16 (&acc)[QB])
                          __attribute__((always_inline)) {
-        const char* kb = (const char*)src;
         uint4 av[AP];
-        ring_begin(kb, bb, av, acc);
-        ring_steps(kb, av, acc, Zero{}, NGc{});
+        ring_begin(i_c, bb, av, acc);
+        ring_steps(i_c, av, acc, Zero{}, NGc{});
         pin_steps(Zero{}, NGc{}, std::true_type{}, Zero{});
     };
 
@@ -472,34 +497,66 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         epi_exps(acc, e, Zero{}, std::integral_constant<int, 16>{});
         epi_commit(e);
     };
+    // The same state update with a lazy reference: (M, S) keeps meaning
+    // M + log2(S) = LSE2 of the keys seen, but M is only a valid shift, moved
+    // to the running maximum when a tile's terms against it would not stay
+    // below kLazyBound (always on the first tile, when M is -inf).  Saves the
+    // tile maximum and the rescale on the common path.
+    auto epilogue_lazy = [&](const f32x16 (&acc)[QB]) __attribute__((always_inline)) {
+        float t[QB];
+        bool slow = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float e[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) e[r] = ex2(fmaf(acc[qb][r], a.c_score, -M[qb]));
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int r = 0; r < w; ++r) e[r] += e[r + w];
+            t[qb] = e[0];
+            slow = slow || !(t[qb] <= kLazyBound);
+        }
+        if (__builtin_amdgcn_ballot_w64(slow)) {
+            EpiState x;
+            epi_max(acc, x);
+            epi_exps(acc, x, Zero{}, std::integral_constant<int, 16>{});
+            epi_commit(x);
+        } else {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                S[qb] += t[qb];
+                asm volatile("" : "+v"(S[qb]), "+v"(M[qb]));
+            }
+        }
+    };
     // One wave per SIMD: the scores of one tile (biases `bb`) into `acc` and
     // the epilogue of the previous tile (`prev`) in four fenced chunks, each
     // pinned to alternate matrix instructions, operand reads and epilogue
     // instructions.
-    auto fused_chunks = [&](const uint4* src, const float* bb, f32x16 (&acc)[QB],
+    auto fused_chunks = [&](auto i_c, const float* bb, f32x16 (&acc)[QB],
                             const f32x16 (&prev)[QB]) __attribute__((always_inline)) {
         constexpr int C = NG >= 4 ? NG / 4 : 1;  // fragments per chunk
         using C1 = std::integral_constant<int, (C < NG ? C : NG)>;
         using C2 = std::integral_constant<int, (2 * C < NG ? 2 * C : NG)>;
         using C3 = std::integral_constant<int, (3 * C < NG ? 3 * C : NG)>;
         using V = std::integral_constant<int, kValuPerSlot>;
-        const char* kb = (const char*)src;
         uint4 av[AP];
         EpiState e;
-        ring_begin(kb, bb, av, acc);
-        ring_steps(kb, av, acc, Zero{}, C1{});
+        ring_begin(i_c, bb, av, acc);
+        ring_steps(i_c, av, acc, Zero{}, C1{});
         epi_max(prev, e);
         pin_steps(Zero{}, C1{}, std::true_type{}, V{});
         __builtin_amdgcn_sched_barrier(0);
-        ring_steps(kb, av, acc, C1{}, C2{});
+        ring_steps(i_c, av, acc, C1{}, C2{});
         epi_exps(prev, e, Zero{}, std::integral_constant<int, 6>{});
         pin_steps(C1{}, C2{}, std::false_type{}, V{});
         __builtin_amdgcn_sched_barrier(0);
-        ring_steps(kb, av, acc, C2{}, C3{});
+        ring_steps(i_c, av, acc, C2{}, C3{});
         epi_exps(prev, e, std::integral_constant<int, 6>{}, std::integral_constant<int, 11>{});
         pin_steps(C2{}, C3{}, std::false_type{}, V{});
         __builtin_amdgcn_sched_barrier(0);
-        ring_steps(kb, av, acc, C3{}, NGc{});
+        ring_steps(i_c, av, acc, C3{}, NGc{});
         epi_exps(prev, e, std::integral_constant<int, 11>{}, std::integral_constant<int, 16>{});
         pin_steps(C3{}, NGc{}, std::false_type{}, V{});
         epi_commit(e);
@@ -532,19 +589,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         const float* bb = bkeys + s * kKeyTile;
         if constexpr (WAVES == 8) {
             if (!lagging) {
-                mfma_tile(buf(I), bb, acc);
+                mfma_tile(i_c, bb, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                epilogue(acc);
+                if constexpr (kLazyRef)
+                    epilogue_lazy(acc);
+                else
+                    epilogue(acc);
             } else {
-                if (s > 0) epilogue(prev);
+                if (s > 0) {
+                    if constexpr (kLazyRef)
+                        epilogue_lazy(prev);
+                    else
+                        epilogue(prev);
+                }
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_tile(buf(I), bb, acc);
+                mfma_tile(i_c, bb, acc);
             }
         } else {
             if (s > 0)
-                fused_chunks(buf(I), bb, acc, prev);
+                fused_chunks(i_c, bb, acc, prev);
             else
-                mfma_tile(buf(I), bb, acc);
+                mfma_tile(i_c, bb, acc);
         }
         wait_tiles(std::integral_constant<int, NBUF - 2>{});
         stage_barrier();

@@ -1,6 +1,6 @@
 """The C-ABI library loads on a host without a GPU, exports every function
-declared in include/fs_sinkhorn.h, and rejects bad arguments on the host
-before touching a device (no compute calls here)."""
+declared in include/*.h, and rejects bad arguments on the host before
+touching a device (no compute calls here)."""
 import ctypes
 import os
 import re
@@ -10,14 +10,17 @@ import pytest
 from streaming_sinkhorn_solver_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fs_sinkhorn.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(fs_[a-z_]+)\s*\(", text)
-    return sorted(set(names))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(fs_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +33,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"fs_potentials_init", "fs_lse_update_f", "fs_lse_update_g", "fs_sinkhorn_solve",
-            "fs_apply_transport", "fs_workspace_bytes", "fs_destroy"} <= set(names)
+            "fs_apply_transport", "fs_workspace_bytes", "fs_destroy",
+            "fs_probe_peak"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -79,3 +83,14 @@ def test_no_device_is_reported_not_crashed(lib):
     st = lib.fs_potentials_init(256, 256, 256, 256, 10, 10, 3, 0, 0, 4096, need, None, None,
                                 None, ctypes.byref(h))
     assert st == binding.FS_ERR_DEVICE
+
+
+def test_probe_argument_validation(lib):
+    rate = ctypes.c_double()
+    # bad kind, bad repetition count, NULL sink: rejected before any device call
+    assert lib.fs_probe_peak(0, 16, 3, None, ctypes.byref(rate)) == binding.FS_ERR_INVALID_ARG
+    assert lib.fs_probe_peak(5, 16, 3, None, ctypes.byref(rate)) == binding.FS_ERR_INVALID_ARG
+    assert lib.fs_probe_peak(1, 16, 0, None, ctypes.byref(rate)) == binding.FS_ERR_INVALID_ARG
+    assert lib.fs_probe_peak(1, 16, 65, None, ctypes.byref(rate)) == binding.FS_ERR_INVALID_ARG
+    assert lib.fs_probe_peak(1, None, 3, None, ctypes.byref(rate)) == binding.FS_ERR_INVALID_ARG
+    assert lib.fs_probe_peak(1, 16, 3, None, None) == binding.FS_ERR_INVALID_ARG
