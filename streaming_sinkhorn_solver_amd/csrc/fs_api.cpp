@@ -43,6 +43,8 @@ struct fs_problem {
     float* scal;      // [0..1] residual outputs, [2..4] transport scale pair and max bits
     float* pot_tmp;   // max(n, m) floats
     void* vt;         // f16 [dv_max][m_pad] (matrix paths with dv_max > 0)
+    float* kbias;     // [m_pad] key biases of the streaming transport kernel
+    float* upart;     // [kTransportMaxSplit][n][dv_max] its partial products
     float* krec;      // small-d matrix path: key records of one pass (fp32)
     void* krec16;     //   fp16-split records (d <= 4)
     void* kguard;     //   guard words of the packing
@@ -172,7 +174,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 
 struct Layout {
     size_t centre, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
-        vt, krec, krec16, kguard, total;
+        vt, kbias, upart, krec, krec16, kguard, total;
 };
 
 Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
@@ -204,6 +206,9 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.ptmp = take(sizeof(float) * std::max(n, m));
     const bool vt = dv_max > 0 && !small_d_path(sh.path);
     L.vt = take(vt ? (size_t)2 * dv_max * mp : 0);
+    const bool streams = vt && transport_streams(sh.path, sh.lse_dp);
+    L.kbias = take(streams ? sizeof(float) * mp : 0);
+    L.upart = take(streams ? sizeof(float) * kTransportMaxSplit * (size_t)n * dv_max : 0);
     const bool small = sh.path == PATH_SMALL;
     const size_t kmax = (size_t)std::max(np, mp);
     L.krec = take(small ? small_f32_rec_bytes(d) * kmax : 0);
@@ -381,6 +386,11 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
     p->scal = (float*)(w + L.scal);
     p->pot_tmp = (float*)(w + L.ptmp);
     p->vt = (dv_max > 0 && !small_d_path(sh.path)) ? (void*)(w + L.vt) : nullptr;
+    {
+        const bool streams = p->vt && transport_streams(sh.path, sh.lse_dp);
+        p->kbias = streams ? (float*)(w + L.kbias) : nullptr;
+        p->upart = streams ? (float*)(w + L.upart) : nullptr;
+    }
     p->krec = sh.path == PATH_SMALL ? (float*)(w + L.krec) : nullptr;
     p->krec16 = sh.path == PATH_SMALL ? (void*)(w + L.krec16) : nullptr;
     p->kguard = sh.path == PATH_SMALL ? (void*)(w + L.kguard) : nullptr;
@@ -604,7 +614,8 @@ fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const flo
     t.c_score = (float)(2.8853900817779268 / (double)eps);
     t.divide_by_a = divide_by_a ? 1 : 0;
     t.U = U;
-    hipError_t e = launch_transport(p->path, t, p->scal + 2, p->vt, p->Y.n_pad, s);
+    hipError_t e =
+        launch_transport(p->path, t, p->scal + 2, p->vt, p->Y.n_pad, p->kbias, p->upart, s);
     if (e != hipSuccess) return hip_fail(e, "transport launch");
     return FS_OK;
 }

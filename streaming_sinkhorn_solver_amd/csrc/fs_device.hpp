@@ -74,6 +74,14 @@ __device__ __forceinline__ void lse_merge(float& M, float& s, float M2, float s2
     M = Mn;
 }
 
+// Workgroup barrier without the memory fence of __syncthreads(): only this
+// wave's LDS operations are waited for.  (The fence would also wait for every
+// outstanding global->LDS tile load, serialising the load pipeline; the
+// pipeline waits for exactly the tiles it needs with explicit vmcnt waits.)
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Score element types of the matrix-core paths.
 enum ScoreOp : int { OP_F32 = 1, OP_BF16 = 2, OP_F16 = 3 };
 

@@ -95,6 +95,12 @@ struct TransportArgs {
     float c_bias, c_score;
     int divide_by_a;
     float* U;                // [n][dv]
+    // streaming matrix kernel (d_pad <= 512 for 2-byte types)
+    const float* key_bias;   // [m_pad] key biases in dot-product units (-inf padding)
+    float* U_part;           // [n_split][n][dv] partial products of the key ranges
+    int64_t part_stride;     // n * dv
+    int n_split;             // key ranges (1: U written directly)
+    int keys_per_split;      // multiple of 32
 };
 
 // ---- launchers (each returns the first HIP error, enqueues on `s`) ----
@@ -142,7 +148,13 @@ hipError_t launch_row_l1max(const float* ops, int64_t n, int d, float* out, hipS
 hipError_t launch_lse_small(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin);
 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
+// Matrix paths: the streaming transport kernel serves operand rows of up to
+// 512 two-byte (or 256 fp32) values and may split the key range into up to
+// kTransportMaxSplit parts, whose partial products need n * dv floats each.
+constexpr int kTransportMaxSplit = 4;
+bool transport_streams(int path, int dp);
 hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratch,
-                            void* Vt_buf, int64_t m_pad, hipStream_t s);
+                            void* Vt_buf, int64_t m_pad, float* key_bias_buf, float* part_buf,
+                            hipStream_t s);
 
 }  // namespace fs

@@ -173,13 +173,6 @@ constexpr bool kLazyRef = true;  // two waves per SIMD: lazy LSE reference (belo
 // move R to the exact running maximum and rescale.
 constexpr float kLazyBound = 0x1p64f;
 
-// Workgroup barrier without the memory fence of __syncthreads(): only this
-// wave's LDS operations are waited for.  (The fence would also wait for every
-// outstanding global->LDS tile load, serialising the load pipeline; the
-// pipeline waits for exactly the tiles it needs with explicit vmcnt waits.)
-__device__ __forceinline__ void stage_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int OP, class TA, class TB>
 __device__ __forceinline__ f32x16 mfma_step(const TA& av, const TB& bv, f32x16 acc) {

@@ -63,11 +63,13 @@ __global__ void vscale_kernel(const unsigned* __restrict__ maxbits, float* __res
     scratch[1] = ldexpf(1.f, -s);
 }
 
-// Vt[k][j] = f16(V[j][k] * 2^s) for j < m, 0 for m <= j < m_pad.
+// Vt[k][pos(j)] = f16(V[j][k] * 2^s) for j < m, 0 for m <= j < m_pad, where
+// pos(j) = j, or with `swap` j with bits 2 and 3 exchanged (the key order the
+// streaming kernel reads: each 16-key group as [0-3, 8-11, 4-7, 12-15]).
 __global__ __launch_bounds__(256) void transpose_v_kernel(const float* __restrict__ V, int m,
                                                           int64_t m_pad, int dv,
                                                           const float* __restrict__ scratch,
-                                                          _Float16* __restrict__ Vt) {
+                                                          _Float16* __restrict__ Vt, int swap) {
     __shared__ float tile[32][33];
     const float sc = scratch[0];
     const int j0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
@@ -79,7 +81,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const float* __restric
     __syncthreads();
     for (int yy = ty; yy < 32; yy += 8) {
         const int k = k0 + yy, j = j0 + tx;
-        if (k < dv && j < m_pad) Vt[(int64_t)k * m_pad + j] = (_Float16)tile[tx][yy];
+        const int pj = swap ? (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1) : j;
+        if (k < dv && j < m_pad) Vt[(int64_t)k * m_pad + pj] = (_Float16)tile[tx][yy];
     }
 }
 
@@ -351,6 +354,377 @@ __global__ __launch_bounds__(256, 1) void transport_mfma_kernel(TransportArgs a,
     }
 }
 
+// ------------------------------------------- streaming kernel (d <= 512)
+// Key biases in dot-product units, the seeds of the score accumulators:
+// kb[j] = (g_j - B_j)/2 + log2(b_j)/(2 c_bias) (c_score = 2 c_bias), -inf for
+// the padding keys m <= j < m_pad.  Written with the same expression as the
+// LSE kernel's seeds, so both passes form bit-identical scores.
+__global__ __launch_bounds__(256) void key_bias_kernel(TransportArgs a, int64_t m_pad,
+                                                       float* __restrict__ kb) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= m_pad) return;
+    kb[j] = j < a.n_keys
+                ? fmaf(a.key_lw2[j], 0.5f / a.c_bias, 0.5f * (a.key_pot[j] - a.key_nrm[j]))
+                : -INFINITY;
+}
+
+// U = P.V for one (row block, column block, key range): 4 waves x 32 rows,
+// 32*NBV output columns, keys [j0, j1).  Everything the pass needs per row
+// stays in registers: the resident row block (B operand of the scores), the
+// 16 score accumulators of two tiles and the NBV output blocks (32 x 32 each;
+// with NBV = 16 they take the 256 accumulation registers).
+//
+// Stage t (32-key tiles; K slot t%2 holds tile t, V slot t%2 holds V^T of
+// tile t):
+//   (1) DMA key tile t+2 (and its 32 biases) into the K slot tile t used and
+//       the V^T tile t+1 into the other V slot (loads past the end are
+//       clamped to the last tile: in-bounds copies into slots no one reads);
+//   (2) the score instructions of tile t+1 (accumulators seeded with the key
+//       biases, as in the LSE kernel);
+//   (3) the weights of tile t, p = 2^(c_score acc - L) in (0, 1], packed to
+//       f16 in accumulator order: register r of lane (row, h) holds key
+//       8(r/4) + 4h + (r%4), so registers 0..7 and 8..15 are the A operands
+//       of the two 16-key products of the tile;
+//   (4) the P.V instructions of tile t against V^T fragments read from LDS;
+//   (5) wait for this stage's loads, barrier.
+// V^T rows hold the keys of each 16-key group in the order [0-3, 8-11, 4-7,
+// 12-15] (bits 2 and 3 of the key index swapped), so that the eight keys lane
+// half h needs for one product -- 4h..4h+3 and 8+4h..8+4h+3 -- are one
+// 16-byte chunk, 2q + h for group q; chunk c of V^T row r is stored at
+// r*4 + (c ^ ((r >> 2) & 3)), conflict-free for 16 consecutive rows.
+template <int OP, int NG, int NBV>
+__global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs a,
+                                                                  int64_t m_pad) {
+    constexpr int WAVES = 4;
+    constexpr int CPR = 2 * NG;
+    constexpr int ROW_BYTES = CPR * 16;
+    constexpr int KT_CHUNKS = kKeyTile * CPR;
+    constexpr int KT_INSTR = KT_CHUNKS / 64;
+    constexpr int KT_PER_WAVE = (KT_INSTR + WAVES - 1) / WAVES;
+    constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
+    constexpr int JB = SWZ + 1 < 2 * NG ? (SWZ + 1) / 2 : NG;
+    constexpr int AP = NG < 4 ? NG : 4;  // key fragments in flight
+    constexpr int DVC = 32 * NBV;
+    constexpr int VT_CHUNKS = DVC * 4;
+    constexpr int VT_INSTR = VT_CHUNKS / 64;
+    constexpr int VT_PER_WAVE = (VT_INSTR + WAVES - 1) / WAVES;
+
+    // tile slots: three when they fit in LDS (loads then have two stages to
+    // land), else two (one stage)
+    constexpr int NB = 3 * (KT_CHUNKS + VT_CHUNKS) * 16 + 1024 <= 163840 ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) uint4 kbuf[NB * KT_CHUNKS];
+    __shared__ __attribute__((aligned(16))) uint4 vbuf[NB * VT_CHUNKS];
+    __shared__ __attribute__((aligned(16))) float bbuf[NB * kKeyTile];
+    __shared__ float rowscale[WAVES][32];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 31, h = lane >> 5;
+    int row_block, yb;
+    xcd_work(row_block, yb);
+    const int n_cb = (a.dv + DVC - 1) / DVC;
+    const int cb = yb % n_cb, split = yb / n_cb;
+    const int row0 = row_block * (WAVES * 32) + wave * 32;
+    const int c0 = cb * DVC;
+    const int j0 = split * a.keys_per_split;
+    const int j1 = min(a.n_keys, j0 + a.keys_per_split);
+    const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
+    const char* __restrict__ keys = (const char*)a.keys;
+    const char* __restrict__ Vt = (const char*)a.Vt;
+    const char* __restrict__ kbias = (const char*)a.key_bias;
+
+    // (1) loads.  K: as the LSE kernel (64-chunk slices, swizzled).  V^T:
+    // LDS position P = L*64 + lane is row r = P/4 of the tile, stored chunk
+    // P%4, fetched from source chunk (P%4) ^ ((r >> 2) & 3); the per-lane
+    // offsets do not depend on the tile.  Columns past dv read row dv-1.
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    uint32_t voffs[VT_PER_WAVE];
+#pragma unroll
+    for (int l = 0; l < VT_PER_WAVE; ++l) {
+        const int P = (l * WAVES + wave) * 64 + lane;
+        const int r = P >> 2, cp = P & 3;
+        const int col = min(c0 + r, a.dv - 1);
+        voffs[l] = (uint32_t)((int64_t)col * m_pad * 2) + (uint32_t)((cp ^ ((r >> 2) & 3)) * 16);
+    }
+    auto issue_k = [&](int k, int slot) __attribute__((always_inline)) {
+        const char* tbase = keys + (int64_t)(j0 + k * kKeyTile) * ROW_BYTES;
+        uint4* dst = kbuf + slot * KT_CHUNKS;
+#pragma unroll
+        for (int l = 0; l < KT_PER_WAVE; ++l) {
+            const int L = l * WAVES + wave;
+            if (KT_INSTR % WAVES == 0 || L < KT_INSTR) {
+                if constexpr (CPR >= 64) {
+                    constexpr int IPR = CPR / 64;
+                    const int m = L / IPR;
+                    uint32_t sw = (uint32_t)(m & SWZ) * 16u;
+                    asm volatile("" : "+s"(sw));
+                    dma_to_lds16(tbase + m * ROW_BYTES + (L % IPR) * 1024, lane16 ^ sw,
+                                 dst + L * 64);
+                } else {
+                    const int P = L * 64 + lane;
+                    const int m = P / CPR, cp = P % CPR;
+                    dma_to_lds16(tbase, (uint32_t)(m * ROW_BYTES + (cp ^ (m & SWZ)) * 16),
+                                 dst + L * 64);
+                }
+            }
+        }
+        // every wave copies the 32 biases (the same bytes to the same place),
+        // so that every wave issues the same number of loads per stage
+        if (lane < 8)
+            dma_to_lds16(kbias + (int64_t)(j0 + k * kKeyTile) * 4, lane16,
+                         bbuf + slot * kKeyTile);
+    };
+    auto issue_v = [&](int k, int slot) __attribute__((always_inline)) {
+        const char* tbase = Vt + (int64_t)(j0 + k * kKeyTile) * 2;
+        uint4* dst = vbuf + slot * VT_CHUNKS;
+#pragma unroll
+        for (int l = 0; l < VT_PER_WAVE; ++l) {
+            const int L = l * WAVES + wave;
+            if (VT_INSTR % WAVES == 0 || L < VT_INSTR) dma_to_lds16(tbase, voffs[l], dst + L * 64);
+        }
+    };
+
+    // prologue: K tiles 0, 1 (clamped), V^T tile 0, the resident rows
+#pragma unroll
+    for (int k = 0; k < NB; ++k) issue_k(min(k, ntiles - 1), k);
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k) issue_v(min(k, ntiles - 1), k);
+    u32x4 q[NG];
+    {
+        const char* rp = (const char*)a.rows + (int64_t)(row0 + ln) * ROW_BYTES + h * 16;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            q[g] = *(const u32x4*)(rp + g * 32);
+            asm volatile("" ::"v"(q[g]));  // waits for these loads stay in the prologue
+        }
+    }
+    const int myrow = row0 + ln;
+    // rows past n: L = +inf makes every weight 0
+    float L = myrow < a.n_rows ? a.row_lse2[myrow] : INFINITY;
+    asm volatile("" : "+v"(L));  // its load's wait stays in the prologue
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // (2) scores of the tile in K slot SL (biases in bias slot SL): the key
+    // fragments stream from LDS through a ring of AP registers kept ahead of
+    // the matrix instruction that consumes them.
+    int abase[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) abase[j] = (ln * CPR + ((2 * j + h) ^ (ln & SWZ))) * 16;
+    auto kfrag = [&](const char* kb, int g) __attribute__((always_inline)) -> uint4 {
+        return *(const uint4*)(kb + abase[g % JB] + (g / JB) * (2 * JB * 16));
+    };
+    auto score_begin = [&](int slot, f32x16& acc, uint4 (&av)[AP]) __attribute__((always_inline)) {
+        const char* kb = (const char*)(kbuf + slot * KT_CHUNKS);
+        const float* bb = bbuf + slot * kKeyTile;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const float4 v = *(const float4*)&bb[8 * qq + 4 * h];
+            acc[4 * qq + 0] = v.x;
+            acc[4 * qq + 1] = v.y;
+            acc[4 * qq + 2] = v.z;
+            acc[4 * qq + 3] = v.w;
+        }
+#pragma unroll
+        for (int g = 0; g < AP; ++g) av[g] = kfrag(kb, g);
+    };
+    // fragments [G0, G1) of the tile in K slot `slot`
+    auto score_steps = [&](int slot, f32x16& acc, uint4 (&av)[AP], auto g0_c, auto g1_c)
+                           __attribute__((always_inline)) {
+        constexpr int G0 = decltype(g0_c)::value;
+        constexpr int G1 = decltype(g1_c)::value;
+        const char* kb = (const char*)(kbuf + slot * KT_CHUNKS);
+#pragma unroll
+        for (int g = G0; g < G1; ++g) {
+            acc = score_step<OP>(av[g % AP], __builtin_bit_cast(uint4, q[g]), acc);
+            if (g + AP < NG) av[g % AP] = kfrag(kb, g + AP);
+        }
+    };
+    auto scores = [&](int slot, f32x16& acc) __attribute__((always_inline)) {
+        uint4 av[AP];
+        score_begin(slot, acc, av);
+        score_steps(slot, acc, av, std::integral_constant<int, 0>{},
+                    std::integral_constant<int, NG>{});
+    };
+    // (3) weights of scores [R0, R1) of a tile
+    auto weights = [&](const f32x16& acc, f16x8& p0, f16x8& p1, auto r0_c, auto r1_c)
+                       __attribute__((always_inline)) {
+        constexpr int R0 = decltype(r0_c)::value;
+        constexpr int R1 = decltype(r1_c)::value;
+#pragma unroll
+        for (int r = R0; r < R1; ++r) {
+            const float w = ex2(fmaf(acc[r], a.c_score, -L));
+            if (r < 8)
+                p0[r] = (_Float16)w;
+            else
+                p1[r - 8] = (_Float16)w;
+        }
+    };
+    // (4) P.V of a tile against the V^T tile in V slot SL.  Fragment k is the
+    // 16-key half k%2 of output block k/2: chunk 2(k%2) + h of V^T row
+    // 32(k/2) + ln; a ring of APV fragments runs ahead of the instructions.
+    constexpr int NVF = 2 * NBV;
+    constexpr int APV = NVF < 4 ? NVF : 4;
+    f32x16 u[NBV];
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) u[nb][r] = 0.f;
+    auto vfrag = [&](const char* vb, int k) __attribute__((always_inline)) -> uint4 {
+        const int r = (k >> 1) * 32 + ln;
+        return *(const uint4*)(vb + (r * 4 + ((2 * (k & 1) + h) ^ ((r >> 2) & 3))) * 16);
+    };
+    auto pv = [&](int slot, const f16x8& p0, const f16x8& p1) __attribute__((always_inline)) {
+        const char* vb = (const char*)(vbuf + slot * VT_CHUNKS);
+        uint4 bv[APV];
+#pragma unroll
+        for (int k = 0; k < APV; ++k) bv[k] = vfrag(vb, k);
+#pragma unroll
+        for (int k = 0; k < NVF; ++k) {
+            u[k >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                (k & 1) ? p1 : p0, __builtin_bit_cast(f16x8, bv[k % APV]), u[k >> 1], 0, 0, 0);
+            if (k + APV < NVF) bv[k % APV] = vfrag(vb, k + APV);
+        }
+    };
+    // Pins the order of a stage's two scheduling regions (left alone, the
+    // scheduler hoists every LDS read of the region to its top, which needs
+    // more registers than the row block and the output blocks leave):
+    //   scores + weights: bias and first key reads, then per key fragment its
+    //     matrix instruction(s), its refill read, up to 2 vector instructions
+    //     and one exponential of the weights;
+    //   P.V: the first V^T reads, then per fragment its matrix instruction
+    //     and refill read.
+    constexpr int MF_PER_FRAG = OP == OP_F32 ? 4 : 1;
+    auto pin_scores = [&](auto g0_c, auto g1_c, auto first_c) __attribute__((always_inline)) {
+        constexpr int G0 = decltype(g0_c)::value;
+        constexpr int G1 = decltype(g1_c)::value;
+        if constexpr (decltype(first_c)::value)
+            __builtin_amdgcn_sched_group_barrier(0x100, AP + 4, 0);
+#pragma unroll
+        for (int g = G0; g < G1; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, MF_PER_FRAG, 0);
+            if (g + AP < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+        }
+    };
+    auto pin_pv = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_group_barrier(0x100, APV, 0);
+#pragma unroll
+        for (int k = 0; k < NVF; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (k + APV < NVF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // One accumulator set: at the start of stage t it holds the scores of
+    // tile t, which move to vector registers (the only copy) before the
+    // scores of tile t+1 are seeded into it.  The stage body is the same
+    // every time (slots by parity), so the output blocks stay in place
+    // across the loop.  The weights of tile t are spread over the score
+    // instructions of tile t+1 in four fenced chunks.
+    constexpr int CH = NG >= 4 ? NG / 4 : 1;  // fragments per chunk
+    using F0 = std::integral_constant<int, 0>;
+    using F1 = std::integral_constant<int, (CH < NG ? CH : NG)>;
+    using F2 = std::integral_constant<int, (2 * CH < NG ? 2 * CH : NG)>;
+    using F3 = std::integral_constant<int, (3 * CH < NG ? 3 * CH : NG)>;
+    using F4 = std::integral_constant<int, NG>;
+    using W0 = std::integral_constant<int, 0>;
+    using W1 = std::integral_constant<int, 4>;
+    using W2 = std::integral_constant<int, 8>;
+    using W3 = std::integral_constant<int, 12>;
+    using W4 = std::integral_constant<int, 16>;
+    f32x16 acc;
+    scores(0, acc);
+    __syncthreads();  // every wave is done with K slot 0 before tile 2 lands there
+    // loads one wave issues per stage (bias copy included); waiting until
+    // only the current stage's are outstanding lands every older tile
+    constexpr int PER_STAGE = (KT_INSTR % WAVES == 0 ? KT_INSTR / WAVES : -1000) + 1 +
+                              (VT_INSTR % WAVES == 0 ? VT_INSTR / WAVES : -1000);
+    int cs = 0, ns = 1, ls = NB - 1;  // slots of tiles t, t+1 and t+NB-1
+    for (int t = 0; t < ntiles; ++t) {
+        issue_k(min(t + NB, ntiles - 1), cs);
+        issue_v(min(t + NB - 1, ntiles - 1), ls);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 cur = acc;
+        asm volatile("" : "+v"(cur));
+        f16x8 p0, p1;
+        uint4 av[AP];
+        score_begin(ns, acc, av);
+        score_steps(ns, acc, av, F0{}, F1{});
+        weights(cur, p0, p1, W0{}, W1{});
+        pin_scores(F0{}, F1{}, std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        score_steps(ns, acc, av, F1{}, F2{});
+        weights(cur, p0, p1, W1{}, W2{});
+        pin_scores(F1{}, F2{}, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        score_steps(ns, acc, av, F2{}, F3{});
+        weights(cur, p0, p1, W2{}, W3{});
+        pin_scores(F2{}, F3{}, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        score_steps(ns, acc, av, F3{}, F4{});
+        weights(cur, p0, p1, W3{}, W4{});
+        pin_scores(F3{}, F4{}, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        pv(cs, p0, p1);
+        pin_pv();
+        if constexpr (NB == 3 && PER_STAGE > 0)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_STAGE) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        stage_barrier();
+        ls = cs;
+        cs = ns;
+        ns = ns + 1 == NB ? 0 : ns + 1;
+    }
+
+    // Row factor 2^(L_i + (f_i - A_i) c_bias) [* a_i] * 2^-s, or 1 when the
+    // key range is one of several (the merge applies it to the sum).
+    if (h == 0) {
+        float sc = 0.f;
+        if (myrow < a.n_rows) {
+            if (a.n_split == 1) {
+                sc = ex2(L + (a.row_pot[myrow] - a.row_nrm[myrow]) * a.c_bias);
+                if (!a.divide_by_a) sc *= a.row_w[myrow];
+                sc *= a.v_unscale_dev[0];
+            } else {
+                sc = 1.f;
+            }
+        }
+        rowscale[wave][ln] = sc;
+    }
+    __syncthreads();
+    float* out = a.n_split == 1 ? a.U : a.U_part + (int64_t)split * a.part_stride;
+    // output register r of lane (ln, h): row 8(r/4) + 4h + (r%4), column ln
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+        const int col = c0 + nb * 32 + ln;
+        if (col >= a.dv) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
+            const int row = row0 + rr;
+            if (row < a.n_rows) out[(int64_t)row * a.dv + col] = u[nb][r] * rowscale[wave][rr];
+        }
+    }
+}
+
+// U = (sum over key ranges of the partial products, in range order) times
+// the row factor.
+__global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)a.n_rows * a.dv;
+    if (idx >= total) return;
+    const int row = (int)(idx / a.dv);
+    float acc = 0.f;
+    for (int s = 0; s < a.n_split; ++s) acc += a.U_part[(int64_t)s * a.part_stride + idx];
+    float sc = ex2(a.row_lse2[row] + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
+    if (!a.divide_by_a) sc *= a.row_w[row];
+    sc *= a.v_unscale_dev[0];
+    a.U[idx] = acc * sc;
+}
+
 template <int D>
 hipError_t transport_valu_launch(const TransportArgs& a, hipStream_t s) {
     const dim3 grid((a.n_rows + 255) / 256, (a.dv + 31) / 32);
@@ -381,10 +755,75 @@ hipError_t transport_mfma_dispatch(int ng, const TransportArgs& a, int64_t m_pad
     }
 }
 
+template <int OP, int NG, int NBV>
+hipError_t transport_stream_launch(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
+    const int n_cb = (a.dv + 32 * NBV - 1) / (32 * NBV);
+    const dim3 grid((a.n_rows + 127) / 128, n_cb * a.n_split);
+    transport_stream_kernel<OP, NG, NBV><<<grid, 256, 0, s>>>(a, m_pad);
+    return hipGetLastError();
+}
+
+template <int OP, int NG>
+hipError_t transport_stream_nbv(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
+    return a.dv <= 128 ? transport_stream_launch<OP, NG, 4>(a, m_pad, s)
+                       : transport_stream_launch<OP, NG, 8>(a, m_pad, s);
+}
+
+template <int OP>
+hipError_t transport_stream_dispatch(int ng, const TransportArgs& a, int64_t m_pad,
+                                     hipStream_t s) {
+    switch (ng) {
+        case 1: return transport_stream_nbv<OP, 1>(a, m_pad, s);
+        case 2: return transport_stream_nbv<OP, 2>(a, m_pad, s);
+        case 4: return transport_stream_nbv<OP, 4>(a, m_pad, s);
+        case 8: return transport_stream_nbv<OP, 8>(a, m_pad, s);
+        case 16: return transport_stream_nbv<OP, 16>(a, m_pad, s);
+        case 32: return transport_stream_nbv<OP, 32>(a, m_pad, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Key-range splits of the streaming kernel: the count whose workgroups
+// (row blocks x column blocks x splits) fill the compute units in whole
+// rounds best, charging each workgroup a fixed start-up of 8 tiles and each
+// extra range the traffic of its partial product (written once, read once).
+void transport_split(const TransportArgs& a, int max_split, int& S, int& kps) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    const int nbv = a.dv <= 128 ? 4 : 8;
+    const int64_t wg = (int64_t)((a.n_rows + 127) / 128) * ((a.dv + 32 * nbv - 1) / (32 * nbv));
+    const int64_t m_tiles = (a.n_keys + kKeyTile - 1) / kKeyTile;
+    // one tile-stage of a workgroup ~ 1 us; partial traffic at ~4 bytes/ps
+    double best = 1e300;
+    S = 1;
+    kps = (int)(m_tiles * kKeyTile);
+    for (int s = 1; s <= max_split && s <= m_tiles; ++s) {
+        const int64_t tiles = (m_tiles + s - 1) / s;
+        if ((s - 1) * tiles >= m_tiles) continue;  // every range holds a key
+        const int64_t rounds = (wg * s + cus - 1) / cus;
+        double t = (double)rounds * (double)(tiles + 8);
+        if (s > 1) t += (double)(s + 1) * a.n_rows * (double)a.dv * 4.0 / 4e6;
+        if (t < best - 1e-9) {
+            best = t;
+            S = s;
+            kps = (int)(tiles * kKeyTile);
+        }
+    }
+}
+
 }  // namespace
 
+bool transport_streams(int path, int dp) {
+    if (small_d_path(path)) return false;
+    const int ng = path == PATH_MFMA_F32 ? dp / 8 : dp / 16;
+    return ng <= 32;
+}
+
 hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, void* Vt_buf,
-                            int64_t m_pad, hipStream_t s) {
+                            int64_t m_pad, float* key_bias_buf, float* part_buf, hipStream_t s) {
     TransportArgs a = a0;
     if (small_d_path(path)) {
         switch (a.dp) {
@@ -409,15 +848,35 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
     if ((e = hipGetLastError()) != hipSuccess) return e;
     vscale_kernel<<<1, 64, 0, s>>>(maxbits, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const bool streams = transport_streams(path, a.dp);
     {
         const dim3 grid((unsigned)((m_pad + 31) / 32), (a.dv + 31) / 32);
         transpose_v_kernel<<<grid, 256, 0, s>>>(a.V, a.n_keys, m_pad, a.dv, scratch,
-                                                (_Float16*)Vt_buf);
+                                                (_Float16*)Vt_buf, streams ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     a.Vt = Vt_buf;
     a.v_unscale_dev = scratch + 1;
     const int ng = path == PATH_MFMA_F32 ? a.dp / 8 : a.dp / 16;
+    if (streams) {
+        if (!key_bias_buf || !part_buf) return hipErrorInvalidValue;
+        key_bias_kernel<<<(unsigned)((m_pad + 255) / 256), 256, 0, s>>>(a, m_pad, key_bias_buf);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        a.key_bias = key_bias_buf;
+        a.U_part = part_buf;
+        a.part_stride = (int64_t)a.n_rows * a.dv;
+        transport_split(a, kTransportMaxSplit, a.n_split, a.keys_per_split);
+        if (path == PATH_MFMA_F32)
+            e = transport_stream_dispatch<OP_F32>(ng, a, m_pad, s);
+        else if (path == PATH_MFMA_BF16)
+            e = transport_stream_dispatch<OP_BF16>(ng, a, m_pad, s);
+        else
+            e = transport_stream_dispatch<OP_F16>(ng, a, m_pad, s);
+        if (e != hipSuccess || a.n_split == 1) return e;
+        const int64_t total = (int64_t)a.n_rows * a.dv;
+        transport_merge_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
+        return hipGetLastError();
+    }
     if (path == PATH_MFMA_F32) return transport_mfma_dispatch<OP_F32>(ng, a, m_pad, s);
     if (path == PATH_MFMA_BF16) return transport_mfma_dispatch<OP_BF16>(ng, a, m_pad, s);
     if (path == PATH_MFMA_F16) return transport_mfma_dispatch<OP_F16>(ng, a, m_pad, s);

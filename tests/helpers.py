@@ -82,9 +82,10 @@ class RoundedProblem:
         return oracle.g_update_cols(self.Xr, self.Yr, a, np.asarray(f) - self.alpha, eps,
                                     cols) + self.beta[cols]
 
-    def transport(self, a, b, f, g, V, eps, divide_by_a=False):
+    def transport(self, a, b, f, g, V, eps, divide_by_a=False, rows=None):
         return oracle.transport(self.Xr, self.Yr, a, b, np.asarray(f) - self.alpha,
-                                np.asarray(g) - self.beta, V, eps, divide_by_a=divide_by_a)
+                                np.asarray(g) - self.beta, V, eps, divide_by_a=divide_by_a,
+                                rows=rows)
 
 
 def gpu_solve(X, Y, a, b, *, eps, iters, prec="auto", n_stages=1, eps_start=None, tol=0.0,

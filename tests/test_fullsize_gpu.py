@@ -87,3 +87,42 @@ def test_full_size_one_step(fs, name):
           f"{p.info['f_splits']}/{p.info['g_splits']}")
     assert ef <= tol and eg <= tol
     assert uf <= bar * w.eps and ug <= bar * w.eps
+
+
+# recipe -> rows sampled for the transport check
+TRANSPORT = {"c3": 64, "c4": 32}
+
+
+@pytest.mark.parametrize("name", sorted(TRANSPORT))
+def test_full_size_transport(fs, name):
+    """The transport at full size, in the launch configuration bench.py times
+    (same shapes, so the same column blocks and key-range splits), on sampled
+    rows against the oracle on the path's own problem; parity bar 1e-3
+    relative (Frobenius over the sampled rows)."""
+    import torch
+
+    from streaming_sinkhorn_solver_amd import binding
+
+    prec, _, path = RECIPES[name]
+    w = workloads.make(name)
+    Xd, Yd, ad, bd, Vd = dev(w.X), dev(w.Y), dev(w.a), dev(w.b), dev(w.V)
+    dv = w.V.shape[1]
+    f = torch.empty(w.n, device="cuda")
+    g = torch.empty(w.m, device="cuda")
+    p = binding.fs_potentials_init(Xd, Yd, ad, bd, prec=prec, f=f, g=g, dv_max=dv)
+    assert p.info["path"] == path
+    binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, iters_per_stage=WARM_ITERS)
+    U = torch.empty((w.n, dv), device="cuda")
+    binding.fs_apply_transport(p, w.eps, f, g, Vd, U, divide_by_a=w.divide_by_a)
+    torch.cuda.synchronize()
+    Uh = host(U)
+    assert np.all(np.isfinite(Uh))
+    rows = np.sort(np.random.default_rng(77).choice(w.n, size=TRANSPORT[name], replace=False))
+    rp = RoundedProblem(w.X, w.Y, prec)
+    ref = rp.transport(w.a, w.b, host(f), host(g), w.V, w.eps, divide_by_a=w.divide_by_a,
+                       rows=rows)
+    rel = np.linalg.norm(Uh[rows] - ref) / np.linalg.norm(ref)
+    worst = np.max(np.linalg.norm(Uh[rows] - ref, axis=1) / np.linalg.norm(ref, axis=1))
+    print(f"{name} transport: relative error {rel:.2e} (worst row {worst:.2e}) on "
+          f"{len(rows)} rows")
+    assert rel <= 1e-3

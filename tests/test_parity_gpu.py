@@ -211,20 +211,26 @@ def test_deterministic_repeat(fs):
     np.testing.assert_array_equal(host(g1), host(g2))
 
 
-@pytest.mark.parametrize("prec,d", [("auto", 3), ("fp32-valu", 3), ("auto", 64), ("bf16", 512),
-                                    ("fp16", 256)])
-def test_transport(fs, prec, d):
+# (precision, d, width of V): the vector paths (d = 3), the streaming matrix
+# kernel with 128-column blocks (dv <= 128) and 256-column blocks (two
+# blocks for dv = 300, one ragged), key-range splits with their merge (the
+# launch heuristic splits these small row counts), and the 1024-D kernel.
+@pytest.mark.parametrize("prec,d,dv", [("auto", 3, 70), ("fp32-valu", 3, 70), ("auto", 64, 70),
+                                       ("auto", 64, 300), ("bf16", 512, 70),
+                                       ("bf16", 512, 300), ("fp16", 256, 70),
+                                       ("fp16", 128, 513), ("fp16", 1024, 100)])
+def test_transport(fs, prec, d, dv):
     import torch
     from streaming_sinkhorn_solver_amd import binding
 
     X, Y, a, b = _problem(900 + d, 700, 850, d, scale=1.0 / np.sqrt(d))
-    rng = np.random.default_rng(901)
-    V = rng.standard_normal((850, 70)).astype(np.float32)
+    rng = np.random.default_rng(901 + dv)
+    V = rng.standard_normal((850, dv)).astype(np.float32)
     eps = 0.1
-    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=8, prec=prec, dv_max=128)
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=8, prec=prec, dv_max=max(dv, 128))
     Vd = dev(V)
-    U = torch.empty((700, 70), dtype=torch.float32, device="cuda")
-    T = torch.empty((700, 70), dtype=torch.float32, device="cuda")
+    U = torch.empty((700, dv), dtype=torch.float32, device="cuda")
+    T = torch.empty((700, dv), dtype=torch.float32, device="cuda")
     binding.fs_apply_transport(p, eps, f, g, Vd, U, divide_by_a=False)
     binding.fs_apply_transport(p, eps, f, g, Vd, T, divide_by_a=True)
     torch.cuda.synchronize()
