@@ -169,6 +169,39 @@ fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const flo
                              const float* V, int32_t dv, float* U, int32_t divide_by_a,
                              void* stream);
 
+/* Column-side application (the transposed plan): U_j = sum_i P_ij W_i with W
+ * (n x dv) and U (m x dv), or U_j / b_j when divide_by_b != 0.  Same limits
+ * and error behaviour as fs_apply_transport.  ("FlashSinkhorn" explainer,
+ * "Method" part 3: transport-matrix applications as streamed weighted
+ * averages.) */
+fs_status fs_apply_transport_t(fs_problem* p, float eps, const float* f, const float* g,
+                               const float* W, int32_t dv, float* U, int32_t divide_by_b,
+                               void* stream);
+
+/* Gradient of the dual objective
+ *   D(f, g; X, Y) = <a,f> + <b,g> - eps sum_ij a_i b_j (exp((f_i+g_j-C_ij)/eps) - 1)
+ * with respect to the points at fixed (f, g), for C = |x - y|^2:
+ *   grad_x_i = 2 sum_j P_ij (x_i - y_j),  grad_y_j = 2 sum_i P_ij (y_j - x_i).
+ * At converged potentials this is the gradient of the entropic OT value
+ * (envelope theorem); it is the backward pass of the end-to-end workload
+ * ("FlashSinkhorn" explainer, "Method" part 3 and "Results").  X (n x d) and
+ * Y (m x d) are the fp32 points passed to fs_potentials_init; grad_x (n x d)
+ * and grad_y (m x d) are written, either may be NULL, neither may overlap X
+ * or Y.  Each output costs one exact LSE pass and one transport application
+ * of width d (so the problem needs dv_max >= d, else FS_ERR_INVALID_ARG).
+ * The matrix paths carry the transport's relative error (about 1e-3 of the
+ * terms); the transported values are the other cloud's points minus its
+ * centre, which keeps that error relative to the cloud's spread. */
+fs_status fs_gradient(fs_problem* p, float eps, const float* f, const float* g, const float* X,
+                      const float* Y, float* grad_x, float* grad_y, void* stream);
+
+/* out[0] (device, one double) = <a,f> + <b,g>, summed in fp64 in a fixed
+ * order.  After an f- or g-update the plan's total mass is sum(a) or sum(b),
+ * so with equal totals the exponential term of D vanishes and this is the
+ * dual value (the entropic OT loss at convergence). */
+fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* out,
+                        void* stream);
+
 /* Frees the host handle only (the workspace is the caller's). */
 void fs_destroy(fs_problem* p);
 

@@ -8,7 +8,10 @@ exactly, calls the C functions and returns numpy arrays.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, a dense scaling-form Sinkhorn, brute-force assignment,
-1-D sorted matching and exact metamorphic relations.
+1-D sorted matching and exact metamorphic relations; the gradient and the
+dual objective by central finite differences of the converged dual value,
+by translation invariance and by the single-target closed form
+(``tests/test_oracle_gradient.py``).
 """
 from __future__ import annotations
 
@@ -39,8 +42,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        compile_library()
+    compile_library(force=False)  # no-op unless missing or older than oracle.c
     lib = ctypes.CDLL(LIB_PATH)
     lib.oracle_version.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -65,8 +67,14 @@ def _load():
                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_double, ctypes.c_int32, _I64,
                                      ctypes.c_int64, _D]
+    lib.oracle_gradient.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int32, ctypes.c_double, _D, _D]
+    lib.oracle_dual_objective.restype = ctypes.c_double
+    lib.oracle_dual_objective.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
     for name in ("oracle_f_update", "oracle_g_update", "oracle_f_update_rows",
-                 "oracle_g_update_cols", "oracle_sinkhorn", "oracle_transport"):
+                 "oracle_g_update_cols", "oracle_sinkhorn", "oracle_transport",
+                 "oracle_gradient"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -180,6 +188,38 @@ def marginal_residual(X, Y, a, b, f, g, eps: float):
     tot = lib.oracle_marginal_residual(_p(X), _p(Y), _p(a), _p(b), _p(f), _p(g), n, m, d,
                                        float(eps), ctypes.byref(r1), ctypes.byref(r2))
     return float(tot), float(r1.value), float(r2.value)
+
+
+def transport_t(X, Y, a, b, f, g, W, eps: float, divide_by_b: bool = False,
+                cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """U_j = sum_i P_ij W_i (or / b_j): the plan of the swapped problem
+    (Y, X, b, a, g, f) is P transposed, so this is `transport` of that
+    problem."""
+    return transport(Y, X, b, a, g, f, W, eps, divide_by_a=divide_by_b, rows=cols)
+
+
+def gradient(X, Y, a, b, f, g, eps: float):
+    """(grad_x, grad_y) of the dual objective at fixed (f, g):
+    grad_x_i = 2 sum_j P_ij (x_i - y_j), grad_y_j = 2 sum_i P_ij (y_j - x_i)."""
+    lib = _load()
+    X, Y, a, b, f, g = (_f64(v) for v in (X, Y, a, b, f, g))
+    n, d = X.shape
+    m = Y.shape[0]
+    gX = np.empty((n, d))
+    gY = np.empty((m, d))
+    _check(lib.oracle_gradient(_p(X), _p(Y), _p(a), _p(b), _p(f), _p(g), n, m, d, float(eps),
+                               _p(gX), _p(gY)))
+    return gX, gY
+
+
+def dual_objective(X, Y, a, b, f, g, eps: float) -> float:
+    """D = <a,f> + <b,g> - eps sum_ij a_i b_j (exp((f_i + g_j - C_ij)/eps) - 1)."""
+    lib = _load()
+    X, Y, a, b, f, g = (_f64(v) for v in (X, Y, a, b, f, g))
+    n, d = X.shape
+    m = Y.shape[0]
+    return float(lib.oracle_dual_objective(_p(X), _p(Y), _p(a), _p(b), _p(f), _p(g), n, m, d,
+                                           float(eps)))
 
 
 def transport(X, Y, a, b, f, g, V, eps: float, divide_by_a: bool = False,

@@ -24,6 +24,13 @@
  *   - annealed runs use eps_s = eps0 (eps_end/eps0)^(s/(S-1)), s = 0..S-1,
  *     with f and g carried from stage to stage;
  *   - the marginal residual is the L1 error of both marginals of P.
+ * Section "Method", part 3 (differentiation): the barycentric projection and
+ * the gradient are weighted averages under the plan.  The gradient here is
+ * that of the dual objective
+ *     D = <a,f> + <b,g> - eps sum_ij a_i b_j (exp((f_i + g_j - C_ij)/eps) - 1)
+ * with respect to the points at fixed (f, g): d/dx_i = sum_j P_ij dC_ij/dx_i
+ * = 2 sum_j P_ij (x_i - y_j), and symmetrically for y_j; each summed as its
+ * definition reads, pair by pair.
  * Natural log/exp from libm, two-pass log-sum-exp (max, then sum), costs by
  * direct coordinate differences, OpenMP over the output index only.
  */
@@ -35,7 +42,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_VERSION 1
+#define ORACLE_VERSION 2
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -247,4 +254,56 @@ int oracle_transport(const double* X, const double* Y, const double* a, const do
         }
     }
     return 0;
+}
+
+/* grad_x_i = 2 sum_j P_ij (x_i - y_j) (n x d) and grad_y_j = 2 sum_i P_ij
+ * (y_j - x_i) (m x d), P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps); either
+ * output may be NULL. */
+int oracle_gradient(const double* X, const double* Y, const double* a, const double* b,
+                    const double* f, const double* g, int64_t n, int64_t m, int32_t d,
+                    double eps, double* gX, double* gY) {
+    if (gX) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            double* gi = gX + i * (int64_t)d;
+            const double* xi = X + i * (int64_t)d;
+            for (int32_t t = 0; t < d; ++t) gi[t] = 0.0;
+            for (int64_t j = 0; j < m; ++j) {
+                const double* yj = Y + j * (int64_t)d;
+                const double p = a[i] * b[j] * exp((f[i] + g[j] - sq_dist(xi, yj, d)) / eps);
+                for (int32_t t = 0; t < d; ++t) gi[t] += 2.0 * p * (xi[t] - yj[t]);
+            }
+        }
+    }
+    if (gY) {
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < m; ++j) {
+            double* gj = gY + j * (int64_t)d;
+            const double* yj = Y + j * (int64_t)d;
+            for (int32_t t = 0; t < d; ++t) gj[t] = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                const double* xi = X + i * (int64_t)d;
+                const double p = a[i] * b[j] * exp((f[i] + g[j] - sq_dist(xi, yj, d)) / eps);
+                for (int32_t t = 0; t < d; ++t) gj[t] += 2.0 * p * (yj[t] - xi[t]);
+            }
+        }
+    }
+    return 0;
+}
+
+/* The dual objective D above, with its exponential term summed pair by pair. */
+double oracle_dual_objective(const double* X, const double* Y, const double* a,
+                             const double* b, const double* f, const double* g, int64_t n,
+                             int64_t m, int32_t d, double eps) {
+    double lin = 0.0, ex = 0.0;
+    for (int64_t i = 0; i < n; ++i) lin += a[i] * f[i];
+    for (int64_t j = 0; j < m; ++j) lin += b[j] * g[j];
+#pragma omp parallel for schedule(static) reduction(+ : ex)
+    for (int64_t i = 0; i < n; ++i) {
+        for (int64_t j = 0; j < m; ++j) {
+            const double c = sq_dist(X + i * (int64_t)d, Y + j * (int64_t)d, d);
+            ex += a[i] * b[j] * (exp((f[i] + g[j] - c) / eps) - 1.0);
+        }
+    }
+    return lin - eps * ex;
 }

@@ -20,7 +20,7 @@ __all__ = [
     "Problem", "load", "lib_path", "fs_workspace_bytes", "fs_potentials_init",
     "fs_lse_update_f", "fs_lse_update_g", "fs_marginal_residual", "fs_sinkhorn_solve",
     "fs_apply_transport", "fs_problem_info", "fs_status_string", "fs_last_error", "solve",
-    "PROBE_KINDS", "fs_probe_peak",
+    "PROBE_KINDS", "fs_probe_peak", "fs_apply_transport_t", "fs_gradient", "fs_dual_value",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -104,6 +104,12 @@ def load():
     lib.fs_last_error.argtypes = []
     lib.fs_problem_info.restype = ctypes.c_int
     lib.fs_problem_info.argtypes = [_vp] + [ctypes.POINTER(i32)] * 4
+    lib.fs_apply_transport_t.restype = ctypes.c_int
+    lib.fs_apply_transport_t.argtypes = [_vp, f32, _fp, _fp, _fp, i32, _fp, i32, _vp]
+    lib.fs_gradient.restype = ctypes.c_int
+    lib.fs_gradient.argtypes = [_vp, f32, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
+    lib.fs_dual_value.restype = ctypes.c_int
+    lib.fs_dual_value.argtypes = [_vp, _fp, _fp, ctypes.c_void_p, _vp]
     lib.fs_probe_peak.restype = ctypes.c_int
     lib.fs_probe_peak.argtypes = [ctypes.c_int, _fp, i32, _vp, ctypes.POINTER(ctypes.c_double)]
     _LIB = lib
@@ -242,6 +248,34 @@ def fs_apply_transport(p: Problem, eps: float, f, g, V, U, divide_by_a: bool = F
                                             _dev(g, "g", p.m), _dev(V, "V", p.m * dv), dv,
                                             _dev(U, "U", p.n * dv), int(bool(divide_by_a)),
                                             _stream(stream)), "fs_apply_transport")
+
+
+def fs_apply_transport_t(p: Problem, eps: float, f, g, W, U, divide_by_b: bool = False,
+                         stream=None):
+    dv = W.shape[1]
+    return _check(load().fs_apply_transport_t(p.handle, float(eps), _dev(f, "f", p.n),
+                                              _dev(g, "g", p.m), _dev(W, "W", p.n * dv), dv,
+                                              _dev(U, "U", p.m * dv), int(bool(divide_by_b)),
+                                              _stream(stream)), "fs_apply_transport_t")
+
+
+def fs_gradient(p: Problem, eps: float, f, g, X, Y, grad_x=None, grad_y=None, stream=None):
+    return _check(load().fs_gradient(p.handle, float(eps), _dev(f, "f", p.n), _dev(g, "g", p.m),
+                                     _dev(X, "X", p.n * p.d), _dev(Y, "Y", p.m * p.d),
+                                     _dev(grad_x, "grad_x", p.n * p.d),
+                                     _dev(grad_y, "grad_y", p.m * p.d), _stream(stream)),
+                  "fs_gradient")
+
+
+def fs_dual_value(p: Problem, f, g, out=None, stream=None) -> torch.Tensor:
+    """<a,f> + <b,g> into a one-element float64 device tensor (returned)."""
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=f.device)
+    if out.dtype != torch.float64 or not out.is_cuda or out.numel() < 1:
+        raise TypeError("out must be a float64 device tensor")
+    _check(load().fs_dual_value(p.handle, _dev(f, "f", p.n), _dev(g, "g", p.m), out.data_ptr(),
+                                _stream(stream)), "fs_dual_value")
+    return out
 
 
 def fs_problem_info(p: Problem) -> dict:

@@ -205,10 +205,13 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.scal = take(sizeof(float) * 8);
     L.ptmp = take(sizeof(float) * std::max(n, m));
     const bool vt = dv_max > 0 && !small_d_path(sh.path);
-    L.vt = take(vt ? (size_t)2 * dv_max * mp : 0);
+    // transport buffers serve both sides (keys Y for P.V, keys X for P^T.W)
+    const size_t kp = (size_t)std::max(np, mp);
+    L.vt = take(vt ? (size_t)2 * dv_max * kp : 0);
     const bool streams = vt && transport_streams(sh.path, sh.lse_dp);
-    L.kbias = take(streams ? sizeof(float) * mp : 0);
-    L.upart = take(streams ? sizeof(float) * kTransportMaxSplit * (size_t)n * dv_max : 0);
+    L.kbias = take(streams ? sizeof(float) * kp : 0);
+    L.upart = take(streams ? sizeof(float) * kTransportMaxSplit * (size_t)std::max(n, m) * dv_max
+                           : 0);
     const bool small = sh.path == PATH_SMALL;
     const size_t kmax = (size_t)std::max(np, mp);
     L.krec = take(small ? small_f32_rec_bytes(d) * kmax : 0);
@@ -326,6 +329,53 @@ fs_status half_step(fs_problem* p, bool f_side, float eps, const float* other, f
 }
 
 bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.f; }
+
+// One transport application.  f_side: U_i = sum_j P_ij (V_j - voff) over the
+// keys Y (U: n x dv, V: m x dv); otherwise U_j = sum_i P_ij (V_i - voff) over
+// the keys X (U: m x dv, V: n x dv).  divide_by_w divides by a_i (b_j).
+// Leaves the rows' exact LSE2 in pot_tmp.
+fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, const float* g,
+                         const float* V, int32_t dv, float* U, int32_t divide_by_w,
+                         const float* voff, hipStream_t s) {
+    if (!p || !f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (dv < 1 || dv > p->dv_max)
+        return fail(FS_ERR_INVALID_ARG, "dv must be in [1, dv_max=%d] (got %d)", p->dv_max, dv);
+    const Cloud& R = f_side ? p->X : p->Y;
+    const Cloud& K = f_side ? p->Y : p->X;
+    if (overlaps(U, (size_t)4 * R.n * dv, V, (size_t)4 * K.n * dv))
+        return fail(FS_ERR_INVALID_ARG, "U overlaps V");
+    const float* row_pot = f_side ? f : g;
+    const float* key_pot = f_side ? g : f;
+    // exact row LSE (base 2) of this side's update scores
+    fs_status st = half_step(p, f_side, eps, key_pot, p->pot_tmp, nullptr, nullptr, 1, s);
+    if (st != FS_OK) return st;
+    TransportArgs t{};
+    t.rows = R.ops;
+    t.row_lse2 = p->pot_tmp;
+    t.row_pot = row_pot;
+    t.row_nrm = R.nrm;
+    t.row_w = R.w;
+    t.keys = K.ops;
+    t.key_pot = key_pot;
+    t.key_nrm = K.nrm;
+    t.key_lw2 = K.lw2;
+    t.V = V;
+    t.v_off = voff;
+    t.Vt = p->vt;
+    t.v_unscale_dev = nullptr;
+    t.n_rows = (int)R.n;
+    t.n_keys = (int)K.n;
+    t.dp = p->lse_dp;
+    t.dv = dv;
+    t.c_bias = (float)(1.4426950408889634 / (double)eps);
+    t.c_score = (float)(2.8853900817779268 / (double)eps);
+    t.divide_by_a = divide_by_w ? 1 : 0;
+    t.U = U;
+    hipError_t e = launch_transport(p->path, t, p->scal + 2, p->vt, K.n_pad, p->kbias, p->upart, s);
+    if (e != hipSuccess) return hip_fail(e, "transport launch");
+    return FS_OK;
+}
 
 }  // namespace
 
@@ -583,40 +633,56 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
 fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const float* g,
                              const float* V, int32_t dv, float* U, int32_t divide_by_a,
                              void* stream) {
-    if (!p || !f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL argument");
-    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
-    if (dv < 1 || dv > p->dv_max)
-        return fail(FS_ERR_INVALID_ARG, "dv must be in [1, dv_max=%d] (got %d)", p->dv_max, dv);
-    if (overlaps(U, (size_t)4 * p->n * dv, V, (size_t)4 * p->m * dv))
-        return fail(FS_ERR_INVALID_ARG, "U overlaps V");
+    return transport_side(p, true, eps, f, g, V, dv, U, divide_by_a, nullptr,
+                          (hipStream_t)stream);
+}
+
+fs_status fs_apply_transport_t(fs_problem* p, float eps, const float* f, const float* g,
+                               const float* W, int32_t dv, float* U, int32_t divide_by_b,
+                               void* stream) {
+    return transport_side(p, false, eps, f, g, W, dv, U, divide_by_b, nullptr,
+                          (hipStream_t)stream);
+}
+
+fs_status fs_gradient(fs_problem* p, float eps, const float* f, const float* g, const float* X,
+                      const float* Y, float* grad_x, float* grad_y, void* stream) {
+    if (!p || !f || !g || !X || !Y) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (p->dv_max < p->d)
+        return fail(FS_ERR_INVALID_ARG,
+                    "the gradient needs dv_max >= d at init (dv_max=%d, d=%d)", p->dv_max, p->d);
+    if (grad_x && (overlaps(grad_x, (size_t)4 * p->n * p->d, X, (size_t)4 * p->n * p->d) ||
+                   overlaps(grad_x, (size_t)4 * p->n * p->d, Y, (size_t)4 * p->m * p->d)))
+        return fail(FS_ERR_INVALID_ARG, "grad_x overlaps X or Y");
+    if (grad_y && (overlaps(grad_y, (size_t)4 * p->m * p->d, X, (size_t)4 * p->n * p->d) ||
+                   overlaps(grad_y, (size_t)4 * p->m * p->d, Y, (size_t)4 * p->m * p->d)))
+        return fail(FS_ERR_INVALID_ARG, "grad_y overlaps X or Y");
     hipStream_t s = (hipStream_t)stream;
-    // Exact row LSE (base 2) of the f-update scores under g.
-    fs_status st = half_step(p, true, eps, g, p->pot_tmp, nullptr, nullptr, 1, s);
-    if (st != FS_OK) return st;
-    TransportArgs t{};
-    t.rows = p->X.ops;
-    t.row_lse2 = p->pot_tmp;
-    t.row_pot = f;
-    t.row_nrm = p->X.nrm;
-    t.row_w = p->X.w;
-    t.keys = p->Y.ops;
-    t.key_pot = g;
-    t.key_nrm = p->Y.nrm;
-    t.key_lw2 = p->Y.lw2;
-    t.V = V;
-    t.Vt = p->vt;
-    t.v_unscale_dev = nullptr;
-    t.n_rows = (int)p->n;
-    t.n_keys = (int)p->m;
-    t.dp = p->lse_dp;
-    t.dv = dv;
-    t.c_bias = (float)(1.4426950408889634 / (double)eps);
-    t.c_score = (float)(2.8853900817779268 / (double)eps);
-    t.divide_by_a = divide_by_a ? 1 : 0;
-    t.U = U;
-    hipError_t e =
-        launch_transport(p->path, t, p->scal + 2, p->vt, p->Y.n_pad, p->kbias, p->upart, s);
-    if (e != hipSuccess) return hip_fail(e, "transport launch");
+    const float c_bias = (float)(1.4426950408889634 / (double)eps);
+    const float* nu = p->centre;          // centre of X
+    const float* mu = p->centre + p->d;   // centre of Y
+    if (grad_x) {
+        // grad_x <- sum_j P_ij (y_j - mu), then 2 (r_i (x_i - mu) - that)
+        fs_status st = transport_side(p, true, eps, f, g, Y, p->d, grad_x, 0, mu, s);
+        if (st != FS_OK) return st;
+        hipError_t e = launch_grad_finish(X, mu, p->pot_tmp, f, p->X.nrm, p->X.w, c_bias, p->n,
+                                          p->d, grad_x, s);
+        if (e != hipSuccess) return hip_fail(e, "gradient launch");
+    }
+    if (grad_y) {
+        fs_status st = transport_side(p, false, eps, f, g, X, p->d, grad_y, 0, nu, s);
+        if (st != FS_OK) return st;
+        hipError_t e = launch_grad_finish(Y, nu, p->pot_tmp, g, p->Y.nrm, p->Y.w, c_bias, p->m,
+                                          p->d, grad_y, s);
+        if (e != hipSuccess) return hip_fail(e, "gradient launch");
+    }
+    return FS_OK;
+}
+
+fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* out,
+                        void* stream) {
+    if (!p || !f || !g || !out) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    hipError_t e = launch_dual_value(p->X.w, f, p->n, p->Y.w, g, p->m, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dual value launch");
     return FS_OK;
 }
 

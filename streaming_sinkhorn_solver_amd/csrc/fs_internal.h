@@ -89,6 +89,7 @@ struct TransportArgs {
     const float* key_nrm;    // keys' cost term
     const float* key_lw2;    // log2 b
     const float* V;          // fp32 [m][dv] (vector path)
+    const float* v_off;      // nullable [dv]: the product uses V - v_off (row-broadcast)
     const void* Vt;          // f16 [dv][m_pad] scaled copy (matrix path)
     const float* v_unscale_dev;  // device float 2^-s undoing the copy's scaling
     int n_rows, n_keys, dp, dv;
@@ -114,6 +115,13 @@ hipError_t launch_convert(const float* P, int64_t n, int64_t n_pad, int d, int d
 hipError_t launch_weights(const float* w, int64_t n, float* lw2, float* wcopy, float* pot,
                           int* flag, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+
+// ---- gradient pieces and dual value (fs_grad.hip) ----
+hipError_t launch_grad_finish(const float* P, const float* c, const float* lse2, const float* pot,
+                              const float* nrm, const float* w, float c_bias, int64_t n, int d,
+                              float* G, hipStream_t s);
+hipError_t launch_dual_value(const float* a, const float* f, int64_t n, const float* b,
+                             const float* g, int64_t m, double* out, hipStream_t s);
 
 // ---- throughput probes (fs_probe.hip) ----
 int probe_blocks();  // workgroups per probe launch on the current device; 0 on error
