@@ -162,6 +162,11 @@ constexpr int kValuPerSlot = FS_VALU_PER_SLOT;  // epilogue instructions per ope
 #ifndef FS_VALU_MASK
 #define FS_VALU_MASK 0x002
 #endif
+#ifdef FS_NO_LAG_DMA
+constexpr bool kLagDma = false;
+#else
+constexpr bool kLagDma = true;  // two waves per SIMD: the lagging waves issue all tile loads
+#endif
 #ifdef FS_EXACT_MAX
 constexpr bool kLazyRef = false;
 #else
@@ -236,8 +241,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     constexpr int ROW_BYTES = CPR * 16;
     constexpr int TILE_CHUNKS = kKeyTile * CPR;      // chunks per key tile (>= 64)
     constexpr int TILE_INSTR = TILE_CHUNKS / 64;     // wave-wide 1 KiB loads per tile
-    constexpr int INSTR_PER_WAVE = (TILE_INSTR + WAVES - 1) / WAVES;
-    constexpr int MIN_INSTR = TILE_INSTR / WAVES;    // loads per tile issued by every wave
+    // With two waves per SIMD the tile loads are issued by the four lagging
+    // waves only (whose epilogue phase has issue slots to spare), so the
+    // leading waves go from the barrier straight into their matrix work.
+    constexpr bool LAG_DMA = WAVES == 8 && kLagDma && kPingPong;
+    constexpr int DMA_WAVES = LAG_DMA ? WAVES / 2 : WAVES;
+    constexpr int INSTR_PER_WAVE = (TILE_INSTR + DMA_WAVES - 1) / DMA_WAVES;
+    constexpr int MIN_INSTR = TILE_INSTR / DMA_WAVES;  // loads per tile of every loading wave
     constexpr int NBUF = nbuf_for(NG);
     constexpr int KPS_MAX = kps_max_for(NG);
     constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;
@@ -272,12 +282,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     // lies in one key row m, so the source is a uniform base plus the lane's
     // swizzled chunk, (lane ^ (m & SWZ)) * 16, formed at issue time.
     const uint32_t lane16 = (uint32_t)lane * 16u;
+    const int dwave = LAG_DMA ? wave - WAVES / 2 : wave;  // index among the loading waves
     auto issue_tile = [&](int k, uint4* dst) __attribute__((always_inline)) {
         const char* tbase = keys + (int64_t)(j0 + k * kKeyTile) * ROW_BYTES;
 #pragma unroll
         for (int l = 0; l < INSTR_PER_WAVE; ++l) {
-            const int L = l * WAVES + wave;
-            if (TILE_INSTR % WAVES == 0 || L < TILE_INSTR) {
+            const int L = l * DMA_WAVES + dwave;
+            if (TILE_INSTR % DMA_WAVES == 0 || L < TILE_INSTR) {
                 if constexpr (CPR >= 64) {
                     constexpr int IPR = CPR / 64;  // slices per key row
                     const int m = L / IPR;
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     // prologue: tiles 0..NBUF-2 in flight (every split holds at least one
     // key; the guard keeps an empty range from reading before it), the key
     // biases of the whole range, the resident row block
-    if (ntiles > 0) {
+    if (ntiles > 0 && (!LAG_DMA || dwave >= 0)) {
 #pragma unroll
         for (int k = 0; k < NBUF - 1; ++k) issue_tile(min(k, ntiles - 1), buf(k));
     }
@@ -577,8 +588,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     auto stage = [&](int s, auto i_c, f32x16 (&acc)[QB], f32x16 (&prev)[QB])
                      __attribute__((always_inline)) {
         constexpr int I = decltype(i_c)::value;
-        issue_tile(min(s + NBUF - 1, ntiles - 1), buf((I + NBUF - 1) % NBUF));
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!LAG_DMA) {
+            issue_tile(min(s + NBUF - 1, ntiles - 1), buf((I + NBUF - 1) % NBUF));
+            __builtin_amdgcn_sched_barrier(0);
+        }
         const float* bb = bkeys + s * kKeyTile;
         if constexpr (WAVES == 8) {
             if (!lagging) {
@@ -589,6 +602,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
                 else
                     epilogue(acc);
             } else {
+                if constexpr (LAG_DMA) {
+                    issue_tile(min(s + NBUF - 1, ntiles - 1), buf((I + NBUF - 1) % NBUF));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (s > 0) {
                     if constexpr (kLazyRef)
                         epilogue_lazy(prev);
