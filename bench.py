@@ -27,6 +27,10 @@ Prints one JSON line with
              probe kernel of that unit alone (fs_probe_peak: independent chains
              of the score path's matrix instruction, or of v_exp_f32) reaches
              on this GPU right after the timed region
+  phases_ms  mean time per step of problem preparation, the solve and the
+             transport (HIP events on the solver's stream)
+  backward   (recipes with a transport of width >= d) one fs_gradient call
+             for both clouds at the final potentials, timed after the steps
   cpu_baseline  the float64 oracle's f-update timed on this host's cores on a
              bounded sample of rows of the same workload, scaled to
              iterations per second
@@ -202,19 +206,27 @@ def main():
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    stats = {"lse_ms": 0.0, "lse_launches": 0}
+    stats = {"lse_ms": 0.0, "lse_launches": 0, "init": 0.0, "solve": 0.0, "transport": 0.0}
 
     def step(timed: bool):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
         p = binding.fs_potentials_init(X, Y, a, b, dv_max=dv, prec=prec, f=f, g=g, workspace=ws)
+        ev[1].record()
         info = binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, eps_start=w.eps_start,
                                          n_stages=w.n_stages, iters_per_stage=iters,
                                          time_kernels=timed)
+        ev[2].record()
         if dv:
             binding.fs_apply_transport(p, w.eps, f, g, V, U, divide_by_a=w.divide_by_a)
+        ev[3].record()
         if timed:
             stats["lse_ms"] += info["lse_ms"]
             stats["lse_launches"] += info["lse_launches"]
+            stats["events"].append(ev)
         return p
+
+    stats["events"] = []
 
     for _ in range(args.warmup):
         p = step(False)
@@ -225,6 +237,29 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     info = p.info
+
+    for ev in stats["events"]:
+        stats["init"] += ev[0].elapsed_time(ev[1])
+        stats["solve"] += ev[1].elapsed_time(ev[2])
+        stats["transport"] += ev[2].elapsed_time(ev[3])
+    phases = {k: round(stats[k] / args.steps, 3) for k in ("init", "solve", "transport")}
+    backward = None
+    if dv >= w.d:
+        # the backward pass of the end-to-end workload at the final
+        # potentials: gradients with respect to both clouds (outside the
+        # timed steps; one untimed call first)
+        gX = torch.empty((w.n, w.d), device=dev)
+        gY = torch.empty((w.m, w.d), device=dev)
+        binding.fs_gradient(p, w.eps, f, g, X, Y, gX, gY)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        binding.fs_gradient(p, w.eps, f, g, X, Y, gX, gY)
+        e1.record()
+        torch.cuda.synchronize()
+        backward = {"gradient_ms": round(e0.elapsed_time(e1), 3),
+                    "what": "fs_gradient for both clouds at the final potentials (two exact "
+                            "LSE passes and two transport applications of width d)"}
+        del gX, gY
 
     ms_per_step = dt / args.steps * 1e3
     it_s = total_iters * args.steps / dt
@@ -263,8 +298,11 @@ def main():
                    "score_path": info["path"], "f_splits": info["f_splits"],
                    "g_splits": info["g_splits"]},
         "pair_evals_per_s": pair_evals / dt,
+        "phases_ms": phases,
         "roofline": roofline,
     }
+    if backward:
+        out["backward"] = backward
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
