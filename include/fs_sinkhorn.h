@@ -74,6 +74,14 @@ typedef enum {
     FS_PREC_FP32_VALU = 4
 } fs_score_prec;
 
+/* Ground cost.  SQEUCLIDEAN: C_ij = |x_i - y_j|^2.  COSINE: C_ij =
+ * 2 - 2 cos(x_i, y_j) = |x_i/|x_i| - y_j/|y_j||^2, the squared-Euclidean
+ * cost of the normalised points (the "FlashSinkhorn" explainer, section
+ * "Significance and claims", names cosine distance, via normalisation, among
+ * the costs the attention form covers); every point must have non-zero
+ * length. */
+typedef enum { FS_COST_SQEUCLIDEAN = 0, FS_COST_COSINE = 1 } fs_cost;
+
 /* Opaque host handle.  It owns no device memory; it points into the
  * caller's workspace.  Not thread-safe; distinct handles are independent. */
 typedef struct fs_problem fs_problem;
@@ -135,6 +143,20 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a,
                              int32_t dv_max, fs_score_prec prec, void* workspace,
                              size_t workspace_bytes, float* f, float* g, void* stream,
                              fs_problem** out);
+
+/* fs_potentials_init with a choice of ground cost.  COSINE normalises the
+ * points inside the preparation pass (X and Y are read as given, never
+ * written) and otherwise runs the squared-Euclidean path on the unit
+ * vectors; the workspace size is the same.  Every later call (updates,
+ * solve, transport, gradient) uses that cost; fs_gradient returns the
+ * gradient with respect to the points as given, taken back through the
+ * normalisation.  FS_ERR_INVALID_ARG for an unknown cost or, for COSINE, a
+ * point of zero length. */
+fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a,
+                                  const float* b, int64_t n, int64_t m, int32_t d,
+                                  int32_t dv_max, fs_score_prec prec, fs_cost cost,
+                                  void* workspace, size_t workspace_bytes, float* f, float* g,
+                                  void* stream, fs_problem** out);
 
 /* One f-update: f_out_i = -eps LSE_j[(g_j - C_ij)/eps + log b_j], all i.
  * g (m floats) is read, f_out (n floats) is written.  If f_cur (n floats) is

@@ -21,6 +21,7 @@ __all__ = [
     "fs_lse_update_f", "fs_lse_update_g", "fs_marginal_residual", "fs_sinkhorn_solve",
     "fs_apply_transport", "fs_problem_info", "fs_status_string", "fs_last_error", "solve",
     "PROBE_KINDS", "fs_probe_peak", "fs_apply_transport_t", "fs_gradient", "fs_dual_value",
+    "COST_SQEUCLIDEAN", "COST_COSINE",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -28,6 +29,8 @@ FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
 PREC_AUTO, PREC_FP32, PREC_BF16, PREC_FP16, PREC_FP32_VALU = range(5)
 _PREC_NAMES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16, "fp16": PREC_FP16,
                "fp32-valu": PREC_FP32_VALU}
+COST_SQEUCLIDEAN, COST_COSINE = 0, 1
+_COST_NAMES = {"sqeuclidean": COST_SQEUCLIDEAN, "cosine": COST_COSINE}
 PROBE_KINDS = {"mfma-bf16": 1, "mfma-fp16": 2, "mfma-fp32": 3, "exp": 4}
 PATH_NAMES = {0: "fp32-valu", 1: "fp32-mfma", 2: "bf16-mfma", 3: "fp16-mfma", 4: "fp32-small-mfma"}
 
@@ -104,6 +107,10 @@ def load():
     lib.fs_last_error.argtypes = []
     lib.fs_problem_info.restype = ctypes.c_int
     lib.fs_problem_info.argtypes = [_vp] + [ctypes.POINTER(i32)] * 4
+    lib.fs_potentials_init_cost.restype = ctypes.c_int
+    lib.fs_potentials_init_cost.argtypes = [_fp, _fp, _fp, _fp, i64, i64, i32, i32,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, sz,
+                                            _fp, _fp, _vp, ctypes.POINTER(_vp)]
     lib.fs_apply_transport_t.restype = ctypes.c_int
     lib.fs_apply_transport_t.argtypes = [_vp, f32, _fp, _fp, _fp, i32, _fp, i32, _vp]
     lib.fs_gradient.restype = ctypes.c_int
@@ -181,7 +188,8 @@ def fs_workspace_bytes(n: int, m: int, d: int, dv_max: int = 0, prec="auto") -> 
 def fs_potentials_init(X: torch.Tensor, Y: torch.Tensor, a: torch.Tensor, b: torch.Tensor, *,
                        dv_max: int = 0, prec="auto", f: Optional[torch.Tensor] = None,
                        g: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       stream=None) -> Problem:
+                       stream=None, cost: str = "sqeuclidean") -> Problem:
+    """fs_potentials_init, or fs_potentials_init_cost for cost="cosine"."""
     lib = load()
     n, d = X.shape
     m = Y.shape[0]
@@ -196,10 +204,19 @@ def fs_potentials_init(X: torch.Tensor, Y: torch.Tensor, a: torch.Tensor, b: tor
     aligned = (base + 255) // 256 * 256
     avail = workspace.numel() - (aligned - base)
     h = _vp()
-    st = lib.fs_potentials_init(_dev(X, "X", n * d), _dev(Y, "Y", m * d), _dev(a, "a", n),
-                                _dev(b, "b", m), n, m, d, dv_max, _prec(prec), aligned, avail,
-                                _dev(f, "f", n), _dev(g, "g", m), _stream(stream),
-                                ctypes.byref(h))
+    if cost not in _COST_NAMES:
+        raise ValueError(f"cost must be one of {sorted(_COST_NAMES)}")
+    if _COST_NAMES[cost] == COST_SQEUCLIDEAN:
+        st = lib.fs_potentials_init(_dev(X, "X", n * d), _dev(Y, "Y", m * d), _dev(a, "a", n),
+                                    _dev(b, "b", m), n, m, d, dv_max, _prec(prec), aligned,
+                                    avail, _dev(f, "f", n), _dev(g, "g", m), _stream(stream),
+                                    ctypes.byref(h))
+    else:
+        st = lib.fs_potentials_init_cost(_dev(X, "X", n * d), _dev(Y, "Y", m * d),
+                                         _dev(a, "a", n), _dev(b, "b", m), n, m, d, dv_max,
+                                         _prec(prec), _COST_NAMES[cost], aligned, avail,
+                                         _dev(f, "f", n), _dev(g, "g", m), _stream(stream),
+                                         ctypes.byref(h))
     _check(st, "fs_potentials_init")
     return Problem(h, workspace, n, m, d, dv_max)
 
@@ -300,12 +317,12 @@ def fs_probe_peak(kind: str, sink, reps: int = 9, stream=None) -> float:
 
 def solve(X, Y, a, b, *, eps: float, iters: int, prec="auto", n_stages: int = 1,
           eps_start: Optional[float] = None, tol: float = 0.0, check_every: int = 10,
-          dv_max: int = 0):
+          dv_max: int = 0, cost: str = "sqeuclidean"):
     """Convenience: init + solve; returns (problem, f, g, info)."""
     dev = X.device
     f = torch.empty(X.shape[0], dtype=torch.float32, device=dev)
     g = torch.empty(Y.shape[0], dtype=torch.float32, device=dev)
-    p = fs_potentials_init(X, Y, a, b, dv_max=dv_max, prec=prec, f=f, g=g)
+    p = fs_potentials_init(X, Y, a, b, dv_max=dv_max, prec=prec, f=f, g=g, cost=cost)
     info = fs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=iters, n_stages=n_stages,
                              eps_start=eps_start, tol=tol, check_every=check_every,
                              raise_not_converged=False)

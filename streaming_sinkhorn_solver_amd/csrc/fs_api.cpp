@@ -25,6 +25,7 @@ using namespace fs;
 
 struct fs_problem {
     int device;
+    int cost;  // fs_cost
     int path;
     int64_t n, m;
     int d;       // true dimension
@@ -174,7 +175,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 
 struct Layout {
     size_t centre, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
-        vt, kbias, upart, krec, krec16, kguard, total;
+        vt, kbias, upart, krec, krec16, kguard, rsx, rsy, total;
 };
 
 Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
@@ -217,6 +218,8 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.krec = take(small ? small_f32_rec_bytes(d) * kmax : 0);
     L.krec16 = take(small ? small_f16_rec_bytes(d) * kmax : 0);
     L.kguard = take(small ? 32 : 0);  // packing guard [2], cloud L1 maxima [2]
+    L.rsx = take(sizeof(float) * n);  // cosine cost: 1/|x_i|
+    L.rsy = take(sizeof(float) * m);
     L.total = o;
     return L;
 }
@@ -336,7 +339,7 @@ bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.f; }
 // Leaves the rows' exact LSE2 in pot_tmp.
 fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, const float* g,
                          const float* V, int32_t dv, float* U, int32_t divide_by_w,
-                         const float* voff, hipStream_t s) {
+                         const float* voff, const float* vrs, hipStream_t s) {
     if (!p || !f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL argument");
     if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (dv < 1 || dv > p->dv_max)
@@ -362,6 +365,7 @@ fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, 
     t.key_lw2 = K.lw2;
     t.V = V;
     t.v_off = voff;
+    t.v_rscale = vrs;
     t.Vt = p->vt;
     t.v_unscale_dev = nullptr;
     t.n_rows = (int)R.n;
@@ -392,7 +396,18 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
                              int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec,
                              void* workspace, size_t workspace_bytes, float* f, float* g,
                              void* stream, fs_problem** out) {
+    return fs_potentials_init_cost(X, Y, a, b, n, m, d, dv_max, prec, FS_COST_SQEUCLIDEAN,
+                                   workspace, workspace_bytes, f, g, stream, out);
+}
+
+fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a,
+                                  const float* b, int64_t n, int64_t m, int32_t d,
+                                  int32_t dv_max, fs_score_prec prec, fs_cost cost,
+                                  void* workspace, size_t workspace_bytes, float* f, float* g,
+                                  void* stream, fs_problem** out) {
     if (!out) return fail(FS_ERR_INVALID_ARG, "out handle pointer is NULL");
+    if (cost != FS_COST_SQEUCLIDEAN && cost != FS_COST_COSINE)
+        return fail(FS_ERR_INVALID_ARG, "unknown fs_cost %d", (int)cost);
     *out = nullptr;
     if (!X || !Y || !a || !b) return fail(FS_ERR_INVALID_ARG, "X, Y, a and b must be non-NULL");
     Shape sh;
@@ -412,6 +427,7 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
     if (!p) return fail(FS_ERR_DEVICE, "host allocation failed");
     char* w = (char*)workspace;
     p->device = dev;
+    p->cost = (int)cost;
     p->path = sh.path;
     p->n = n;
     p->m = m;
@@ -448,18 +464,26 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
         p->X.l1max = (float*)(w + L.kguard) + 2;
         p->Y.l1max = (float*)(w + L.kguard) + 3;
     }
+    if (cost == FS_COST_COSINE) {
+        p->X.rscale = (float*)(w + L.rsx);
+        p->Y.rscale = (float*)(w + L.rsy);
+    }
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if ((e = launch_zero_flag(p->flag, s)) != hipSuccess) goto hip_error;
-    if ((e = launch_bbox(X, n, Y, m, d, p->bbox_min, p->bbox_max, kBboxParts, p->centre, s)) !=
-        hipSuccess)
+    if (cost == FS_COST_COSINE &&
+        ((e = launch_inv_norm(X, n, d, p->X.rscale, p->flag, s)) != hipSuccess ||
+         (e = launch_inv_norm(Y, m, d, p->Y.rscale, p->flag, s)) != hipSuccess))
         goto hip_error;
-    if ((e = launch_convert(X, n, p->X.n_pad, d, p->dp, p->path, p->centre, p->centre + d,
-                            p->X.ops, p->X.nrm, p->flag, s)) != hipSuccess)
+    if ((e = launch_bbox(X, p->X.rscale, n, Y, p->Y.rscale, m, d, p->bbox_min, p->bbox_max,
+                         kBboxParts, p->centre, s)) != hipSuccess)
         goto hip_error;
-    if ((e = launch_convert(Y, m, p->Y.n_pad, d, p->dp, p->path, p->centre + d, p->centre,
-                            p->Y.ops, p->Y.nrm, p->flag, s)) != hipSuccess)
+    if ((e = launch_convert(X, p->X.rscale, n, p->X.n_pad, d, p->dp, p->path, p->centre,
+                            p->centre + d, p->X.ops, p->X.nrm, p->flag, s)) != hipSuccess)
+        goto hip_error;
+    if ((e = launch_convert(Y, p->Y.rscale, m, p->Y.n_pad, d, p->dp, p->path, p->centre + d,
+                            p->centre, p->Y.ops, p->Y.nrm, p->flag, s)) != hipSuccess)
         goto hip_error;
     if (p->path == PATH_SMALL &&
         ((e = launch_row_l1max((const float*)p->X.ops, n, d, p->X.l1max, s)) != hipSuccess ||
@@ -477,6 +501,9 @@ fs_status fs_potentials_init(const float* X, const float* Y, const float* a, con
             delete p;
             if (flag & 1) return fail(FS_ERR_NONFINITE, "X or Y holds a NaN or Inf");
             if (flag & 2) return fail(FS_ERR_NONFINITE, "a weight is <= 0, subnormal, NaN or Inf");
+            if (flag & 8)
+                return fail(FS_ERR_INVALID_ARG,
+                            "cosine cost: a point has zero (or non-finite) length");
             return fail(FS_ERR_INVALID_ARG,
                         "a centred coordinate overflows the fp16 range; scale the points "
                         "(and eps by the square of the scale) or use FS_PREC_BF16");
@@ -633,14 +660,14 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
 fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const float* g,
                              const float* V, int32_t dv, float* U, int32_t divide_by_a,
                              void* stream) {
-    return transport_side(p, true, eps, f, g, V, dv, U, divide_by_a, nullptr,
+    return transport_side(p, true, eps, f, g, V, dv, U, divide_by_a, nullptr, nullptr,
                           (hipStream_t)stream);
 }
 
 fs_status fs_apply_transport_t(fs_problem* p, float eps, const float* f, const float* g,
                                const float* W, int32_t dv, float* U, int32_t divide_by_b,
                                void* stream) {
-    return transport_side(p, false, eps, f, g, W, dv, U, divide_by_b, nullptr,
+    return transport_side(p, false, eps, f, g, W, dv, U, divide_by_b, nullptr, nullptr,
                           (hipStream_t)stream);
 }
 
@@ -662,17 +689,17 @@ fs_status fs_gradient(fs_problem* p, float eps, const float* f, const float* g, 
     const float* mu = p->centre + p->d;   // centre of Y
     if (grad_x) {
         // grad_x <- sum_j P_ij (y_j - mu), then 2 (r_i (x_i - mu) - that)
-        fs_status st = transport_side(p, true, eps, f, g, Y, p->d, grad_x, 0, mu, s);
+        fs_status st = transport_side(p, true, eps, f, g, Y, p->d, grad_x, 0, mu, p->Y.rscale, s);
         if (st != FS_OK) return st;
-        hipError_t e = launch_grad_finish(X, mu, p->pot_tmp, f, p->X.nrm, p->X.w, c_bias, p->n,
-                                          p->d, grad_x, s);
+        hipError_t e = launch_grad_finish(X, p->X.rscale, mu, p->pot_tmp, f, p->X.nrm, p->X.w,
+                                          c_bias, p->n, p->d, grad_x, s);
         if (e != hipSuccess) return hip_fail(e, "gradient launch");
     }
     if (grad_y) {
-        fs_status st = transport_side(p, false, eps, f, g, X, p->d, grad_y, 0, nu, s);
+        fs_status st = transport_side(p, false, eps, f, g, X, p->d, grad_y, 0, nu, p->X.rscale, s);
         if (st != FS_OK) return st;
-        hipError_t e = launch_grad_finish(Y, nu, p->pot_tmp, g, p->Y.nrm, p->Y.w, c_bias, p->m,
-                                          p->d, grad_y, s);
+        hipError_t e = launch_grad_finish(Y, p->Y.rscale, nu, p->pot_tmp, g, p->Y.nrm, p->Y.w,
+                                          c_bias, p->m, p->d, grad_y, s);
         if (e != hipSuccess) return hip_fail(e, "gradient launch");
     }
     return FS_OK;

@@ -16,9 +16,15 @@ namespace fs {
 
 namespace {
 
-// G[i][k] = 2 (r_i (P[i][k] - c[k]) - G[i][k]), r_i = 2^(L_i + (pot_i - nrm_i) c_bias) w_i
-// (the row sums of the plan: the same factor the transport applies to row i).
+// One wave per row.  With p_i = P[i] (or P[i] rscale_i, unit length, for the
+// cosine cost) and r_i = 2^(L_i + (pot_i - nrm_i) c_bias) w_i (the row sums of
+// the plan: the same factor the transport applies to row i):
+//   G_i <- 2 (r_i (p_i - c) - G_i),
+// the gradient with respect to p_i; for the cosine cost it is then taken back
+// through p_i = x_i / |x_i|, whose Jacobian is (I - p_i p_i^T) / |x_i|:
+//   G_i <- rscale_i (G_i - p_i (p_i . G_i)).
 __global__ __launch_bounds__(256) void grad_finish_kernel(const float* __restrict__ P,
+                                                          const float* __restrict__ rscale,
                                                           const float* __restrict__ c,
                                                           const float* __restrict__ lse2,
                                                           const float* __restrict__ pot,
@@ -26,12 +32,25 @@ __global__ __launch_bounds__(256) void grad_finish_kernel(const float* __restric
                                                           const float* __restrict__ w,
                                                           float c_bias, int64_t n, int d,
                                                           float* __restrict__ G) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= n * d) return;
-    const int64_t i = idx / d;
-    const int k = (int)(idx - i * d);
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= n) return;
     const float r = ex2(lse2[i] + (pot[i] - nrm[i]) * c_bias) * w[i];
-    G[idx] = 2.f * fmaf(r, P[idx] - c[k], -G[idx]);
+    const float s = rscale ? rscale[i] : 1.f;
+    float dot = 0.f;
+    for (int k = lane; k < d; k += 64) {
+        const int64_t idx = i * d + k;
+        const float p = P[idx] * s;
+        const float gk = 2.f * fmaf(r, p - c[k], -G[idx]);
+        G[idx] = gk;
+        dot = fmaf(p, gk, dot);
+    }
+    if (!rscale) return;
+    dot = wave_sum(dot);
+    for (int k = lane; k < d; k += 64) {
+        const int64_t idx = i * d + k;
+        G[idx] = s * fmaf(-P[idx] * s, dot, G[idx]);
+    }
 }
 
 // out[0] = sum_i a_i f_i + sum_j b_j g_j, accumulated in fp64 in a fixed
@@ -57,13 +76,13 @@ __global__ __launch_bounds__(1024) void dual_value_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_grad_finish(const float* P, const float* c, const float* lse2, const float* pot,
-                              const float* nrm, const float* w, float c_bias, int64_t n, int d,
-                              float* G, hipStream_t s) {
-    const int64_t total = n * d;
-    if (total <= 0) return hipSuccess;
-    grad_finish_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(P, c, lse2, pot, nrm, w,
-                                                                       c_bias, n, d, G);
+hipError_t launch_grad_finish(const float* P, const float* rscale, const float* c,
+                              const float* lse2, const float* pot, const float* nrm,
+                              const float* w, float c_bias, int64_t n, int d, float* G,
+                              hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    grad_finish_kernel<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(P, rscale, c, lse2, pot, nrm, w,
+                                                               c_bias, n, d, G);
     return hipGetLastError();
 }
 

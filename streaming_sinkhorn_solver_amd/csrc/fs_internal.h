@@ -36,6 +36,7 @@ struct Cloud {
     int64_t n;
     int64_t n_pad;
     float* l1max = nullptr;  // small-d matrix path: largest L1 norm of a point (device scalar)
+    float* rscale = nullptr; // cosine cost: 1/|p_i| [n] (the solver's points are p_i/|p_i|)
 };
 
 // Arguments of one streaming log-sum-exp pass ("half-step"): for every row
@@ -90,6 +91,7 @@ struct TransportArgs {
     const float* key_lw2;    // log2 b
     const float* V;          // fp32 [m][dv] (vector path)
     const float* v_off;      // nullable [dv]: the product uses V - v_off (row-broadcast)
+    const float* v_rscale;   // nullable [keys]: ... and V_j * v_rscale[j] before the offset
     const void* Vt;          // f16 [dv][m_pad] scaled copy (matrix path)
     const float* v_unscale_dev;  // device float 2^-s undoing the copy's scaling
     int n_rows, n_keys, dp, dv;
@@ -106,20 +108,27 @@ struct TransportArgs {
 
 // ---- launchers (each returns the first HIP error, enqueues on `s`) ----
 hipError_t launch_zero_flag(int* flag, hipStream_t s);
-hipError_t launch_bbox(const float* X, int64_t n, const float* Y, int64_t m, int d,
-                       float* part_min, float* part_max, int parts_per_cloud, float* centres,
-                       hipStream_t s);
-hipError_t launch_convert(const float* P, int64_t n, int64_t n_pad, int d, int dp, int path,
-                          const float* own_centre, const float* other_centre, void* ops,
-                          float* nrm, int* flag, hipStream_t s);
+// xscale / yscale / rscale (nullable): per-point factors applied on reading
+// (1/|p| for the cosine cost)
+hipError_t launch_inv_norm(const float* P, int64_t n, int d, float* inv, int* flag,
+                           hipStream_t s);
+hipError_t launch_bbox(const float* X, const float* xscale, int64_t n, const float* Y,
+                       const float* yscale, int64_t m, int d, float* part_min, float* part_max,
+                       int parts_per_cloud, float* centres, hipStream_t s);
+hipError_t launch_convert(const float* P, const float* rscale, int64_t n, int64_t n_pad, int d,
+                          int dp, int path, const float* own_centre, const float* other_centre,
+                          void* ops, float* nrm, int* flag, hipStream_t s);
 hipError_t launch_weights(const float* w, int64_t n, float* lw2, float* wcopy, float* pot,
                           int* flag, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
 // ---- gradient pieces and dual value (fs_grad.hip) ----
-hipError_t launch_grad_finish(const float* P, const float* c, const float* lse2, const float* pot,
-                              const float* nrm, const float* w, float c_bias, int64_t n, int d,
-                              float* G, hipStream_t s);
+// rscale (nullable): cosine cost -- the points are P_i rscale_i, and the
+// gradient is taken back through that normalisation
+hipError_t launch_grad_finish(const float* P, const float* rscale, const float* c,
+                              const float* lse2, const float* pot, const float* nrm,
+                              const float* w, float c_bias, int64_t n, int d, float* G,
+                              hipStream_t s);
 hipError_t launch_dual_value(const float* a, const float* f, int64_t n, const float* b,
                              const float* g, int64_t m, double* out, hipStream_t s);
 

@@ -27,14 +27,17 @@ namespace fs {
 
 namespace {
 
-enum : int { FLAG_NONFINITE_POINT = 1, FLAG_BAD_WEIGHT = 2, FLAG_RANGE = 4 };
+enum : int { FLAG_NONFINITE_POINT = 1, FLAG_BAD_WEIGHT = 2, FLAG_RANGE = 4, FLAG_ZERO_NORM = 8 };
 
 __global__ void zero_flag_kernel(int* flag) {
     if (threadIdx.x == 0) flag[0] = 0;
 }
 
 // Per-coordinate min/max of one row chunk.  grid = (ceil(d/256), parts).
+// rscale (nullable): the points are P[r] * rscale[r] (unit rows for the
+// cosine cost).
 __global__ __launch_bounds__(256) void bbox_partial_kernel(const float* __restrict__ P,
+                                                           const float* __restrict__ rscale,
                                                            int64_t n, int d, int parts,
                                                            float* __restrict__ pmin,
                                                            float* __restrict__ pmax) {
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(256) void bbox_partial_kernel(const float* __restri
     const int64_t r1 = r0 + chunk < n ? r0 + chunk : n;
     float mn = INFINITY, mx = -INFINITY;
     for (int64_t r = r0; r < r1; ++r) {
-        const float v = P[r * d + k];
+        const float v = rscale ? P[r * d + k] * rscale[r] : P[r * d + k];
         mn = fminf(mn, v);
         mx = fmaxf(mx, v);
     }
@@ -88,7 +91,8 @@ __device__ __forceinline__ _Float16 to_elem<_Float16>(float v) { return (_Float1
 // the row's cost term |P[i] - oth|^2 - |own - oth|^2 / 2 in fp32, summed in a
 // fixed order (own: this cloud's centre, oth: the other cloud's).
 template <typename T>
-__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ P, int64_t n,
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ P,
+                                                      const float* __restrict__ rscale, int64_t n,
                                                       int64_t n_pad, int d, int dp,
                                                       const float* __restrict__ own,
                                                       const float* __restrict__ oth,
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
     for (int k = lane; k < dp; k += 64) {
         T t = to_elem<T>(0.f);
         if (i < n && k < d) {
-            const float v = P[i * d + k];
+            const float v = rscale ? P[i * d + k] * rscale[i] : P[i * d + k];
             if (!(fabsf(v) <= 3.402823466e38f)) bad |= FLAG_NONFINITE_POINT;
             t = to_elem<T>(v - own[k]);
             if (!(fabsf((float)t) <= 3.402823466e38f)) bad |= FLAG_RANGE;
@@ -117,6 +121,28 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
     off = wave_sum(off);
     if (i < n && lane == 0) nrm[i] = fmaf(off, -0.5f, acc);
     if (bad) atomicOr(flag, bad);
+}
+
+// One wave per row: inv[i] = 1 / |P[i]| (cosine cost: the points are
+// normalised to unit length, where |x^ - y^|^2 = 2 - 2 cos(x, y)).  A zero or
+// non-finite row is flagged.
+__global__ __launch_bounds__(256) void inv_norm_kernel(const float* __restrict__ P, int64_t n,
+                                                       int d, float* __restrict__ inv,
+                                                       int* __restrict__ flag) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= n) return;
+    float s = 0.f;
+    for (int k = lane; k < d; k += 64) {
+        const float v = P[i * d + k];
+        s = fmaf(v, v, s);
+    }
+    s = wave_sum(s);
+    if (lane == 0) {
+        const bool ok = s > 0.f && s <= 3.402823466e38f;
+        inv[i] = ok ? 1.0f / sqrtf(s) : 0.f;
+        if (!ok) atomicOr(flag, FLAG_ZERO_NORM);
+    }
 }
 
 __global__ __launch_bounds__(256) void weights_kernel(const float* __restrict__ w, int64_t n,
@@ -147,35 +173,42 @@ hipError_t launch_zero_flag(int* flag, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_bbox(const float* X, int64_t n, const float* Y, int64_t m, int d,
-                       float* part_min, float* part_max, int parts, float* centres,
-                       hipStream_t s) {
+hipError_t launch_inv_norm(const float* P, int64_t n, int d, float* inv, int* flag,
+                           hipStream_t s) {
+    inv_norm_kernel<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(P, n, d, inv, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_bbox(const float* X, const float* xscale, int64_t n, const float* Y,
+                       const float* yscale, int64_t m, int d, float* part_min, float* part_max,
+                       int parts, float* centres, hipStream_t s) {
     const dim3 grid((d + 255) / 256, parts);
-    bbox_partial_kernel<<<grid, 256, 0, s>>>(X, n, d, parts, part_min, part_max);
-    bbox_partial_kernel<<<grid, 256, 0, s>>>(Y, m, d, parts, part_min + (int64_t)parts * d,
+    bbox_partial_kernel<<<grid, 256, 0, s>>>(X, xscale, n, d, parts, part_min, part_max);
+    bbox_partial_kernel<<<grid, 256, 0, s>>>(Y, yscale, m, d, parts,
+                                             part_min + (int64_t)parts * d,
                                              part_max + (int64_t)parts * d);
     bbox_final_kernel<<<dim3((d + 255) / 256, 2), 256, 0, s>>>(part_min, part_max, parts, d,
                                                                centres);
     return hipGetLastError();
 }
 
-hipError_t launch_convert(const float* P, int64_t n, int64_t n_pad, int d, int dp, int path,
-                          const float* own, const float* oth, void* ops, float* nrm, int* flag,
-                          hipStream_t s) {
+hipError_t launch_convert(const float* P, const float* rscale, int64_t n, int64_t n_pad, int d,
+                          int dp, int path, const float* own, const float* oth, void* ops,
+                          float* nrm, int* flag, hipStream_t s) {
     const int64_t blocks = (n_pad + 3) / 4;
     switch (path) {
         case PATH_VALU:
         case PATH_SMALL:
         case PATH_MFMA_F32:
-            convert_kernel<float><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, own, oth,
+            convert_kernel<float><<<blocks, 256, 0, s>>>(P, rscale, n, n_pad, d, dp, own, oth,
                                                          (float*)ops, nrm, flag);
             break;
         case PATH_MFMA_BF16:
-            convert_kernel<__bf16><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, own, oth,
+            convert_kernel<__bf16><<<blocks, 256, 0, s>>>(P, rscale, n, n_pad, d, dp, own, oth,
                                                           (__bf16*)ops, nrm, flag);
             break;
         case PATH_MFMA_F16:
-            convert_kernel<_Float16><<<blocks, 256, 0, s>>>(P, n, n_pad, d, dp, own, oth,
+            convert_kernel<_Float16><<<blocks, 256, 0, s>>>(P, rscale, n, n_pad, d, dp, own, oth,
                                                             (_Float16*)ops, nrm, flag);
             break;
         default:

@@ -32,14 +32,24 @@ namespace {
 // ---------------------------------------------------- V -> f16, transposed
 // max|V| over all entries as the bit pattern of a non-negative float (for
 // which integer order is float order), so an atomic max is order independent.
+__device__ __forceinline__ float v_value(const float* __restrict__ V, int64_t j, int dv, int k,
+                                         const float* __restrict__ rs,
+                                         const float* __restrict__ off) {
+    float v = V[j * dv + k];
+    if (rs) v *= rs[j];
+    if (off) v -= off[k];
+    return v;
+}
+
 __global__ __launch_bounds__(256) void vmax_kernel(const float* __restrict__ V, int64_t count,
-                                                   int dv, const float* __restrict__ off,
+                                                   int dv, const float* __restrict__ rs,
+                                                   const float* __restrict__ off,
                                                    unsigned* __restrict__ maxbits) {
     __shared__ float red[256];
     float mx = 0.f;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < count; k += stride)
-        mx = fmaxf(mx, fabsf(off ? V[k] - off[k % dv] : V[k]));
+        mx = fmaxf(mx, fabsf(v_value(V, k / dv, dv, (int)(k % dv), rs, off)));
     red[threadIdx.x] = mx;
     __syncthreads();
     for (int o = 128; o >= 1; o >>= 1) {
@@ -64,14 +74,15 @@ __global__ void vscale_kernel(const unsigned* __restrict__ maxbits, float* __res
     scratch[1] = ldexpf(1.f, -s);
 }
 
-// Vt[k][pos(j)] = f16((V[j][k] - off[k]) * 2^s) (off: 0 when NULL) for j < m,
-// 0 for m <= j < m_pad, where
+// Vt[k][pos(j)] = f16((V[j][k] rs[j] - off[k]) * 2^s) (rs: 1 and off: 0 when
+// NULL) for j < m, 0 for m <= j < m_pad, where
 // pos(j) = j, or with `swap` j with bits 2 and 3 exchanged (the key order the
 // streaming kernel reads: each 16-key group as [0-3, 8-11, 4-7, 12-15]).
 __global__ __launch_bounds__(256) void transpose_v_kernel(const float* __restrict__ V, int m,
                                                           int64_t m_pad, int dv,
                                                           const float* __restrict__ scratch,
                                                           _Float16* __restrict__ Vt, int swap,
+                                                          const float* __restrict__ rs,
                                                           const float* __restrict__ off) {
     __shared__ float tile[32][33];
     const float sc = scratch[0];
@@ -79,8 +90,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const float* __restric
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
     for (int yy = ty; yy < 32; yy += 8) {
         const int j = j0 + yy, k = k0 + tx;
-        tile[yy][tx] =
-            (j < m && k < dv) ? (V[(int64_t)j * dv + k] - (off ? off[k] : 0.f)) * sc : 0.f;
+        tile[yy][tx] = (j < m && k < dv) ? v_value(V, j, dv, k, rs, off) * sc : 0.f;
     }
     __syncthreads();
     for (int yy = ty; yy < 32; yy += 8) {
@@ -113,10 +123,9 @@ __global__ __launch_bounds__(256) void transport_valu_kernel(TransportArgs a) {
 #pragma unroll
         for (int k = 0; k < D; ++k) z = fmaf(x[k], keys[(int64_t)j * DP + k], z);
         const float p = ex2(z - L);
-        const float* vr = a.V + (int64_t)j * a.dv + c0;
 #pragma unroll
         for (int c = 0; c < DVC; ++c)
-            if (c0 + c < a.dv) u[c] = fmaf(p, a.v_off ? vr[c] - a.v_off[c0 + c] : vr[c], u[c]);
+            if (c0 + c < a.dv) u[c] = fmaf(p, v_value(a.V, j, a.dv, c0 + c, a.v_rscale, a.v_off), u[c]);
     }
     if (!live) return;
     float sc = ex2(L + (a.row_pot[i] - a.row_nrm[i]) * a.c_bias);
@@ -848,7 +857,7 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
     if (e != hipSuccess) return e;
     const int64_t count = (int64_t)a.n_keys * a.dv;
     const int64_t blocks = std::min<int64_t>((count + 255) / 256, 2048);
-    vmax_kernel<<<(unsigned)blocks, 256, 0, s>>>(a.V, count, a.dv, a.v_off, maxbits);
+    vmax_kernel<<<(unsigned)blocks, 256, 0, s>>>(a.V, count, a.dv, a.v_rscale, a.v_off, maxbits);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     vscale_kernel<<<1, 64, 0, s>>>(maxbits, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -856,7 +865,8 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
     {
         const dim3 grid((unsigned)((m_pad + 31) / 32), (a.dv + 31) / 32);
         transpose_v_kernel<<<grid, 256, 0, s>>>(a.V, a.n_keys, m_pad, a.dv, scratch,
-                                                (_Float16*)Vt_buf, streams ? 1 : 0, a.v_off);
+                                                (_Float16*)Vt_buf, streams ? 1 : 0, a.v_rscale,
+                                                a.v_off);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     a.Vt = Vt_buf;

@@ -28,6 +28,15 @@ def centres(X: np.ndarray, Y: np.ndarray):
     return mid(X), mid(Y)
 
 
+def normalise_rows(P) -> np.ndarray:
+    """The cosine cost's points as the library forms them: each row times
+    float32(1 / sqrt(float32 sum of squares)), in float32."""
+    P = np.asarray(P, dtype=np.float32)
+    s = np.sum(P.astype(np.float64) ** 2, axis=1)
+    inv = (1.0 / np.sqrt(s.astype(np.float32))).astype(np.float32)
+    return (P * inv[:, None]).astype(np.float32)
+
+
 def round_bf16(x32: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
@@ -89,13 +98,13 @@ class RoundedProblem:
 
 
 def gpu_solve(X, Y, a, b, *, eps, iters, prec="auto", n_stages=1, eps_start=None, tol=0.0,
-              check_every=10, dv_max=0):
+              check_every=10, dv_max=0, cost="sqeuclidean"):
     from streaming_sinkhorn_solver_amd import binding
 
     Xd, Yd, ad, bd = dev(X), dev(Y), dev(a), dev(b)
     p, f, g, info = binding.solve(Xd, Yd, ad, bd, eps=eps, iters=iters, prec=prec,
                                   n_stages=n_stages, eps_start=eps_start, tol=tol,
-                                  check_every=check_every, dv_max=dv_max)
+                                  check_every=check_every, dv_max=dv_max, cost=cost)
     import torch
 
     torch.cuda.synchronize()

@@ -1,7 +1,7 @@
 """GPU parity of the backward-pass operations: the column-side transport
 P^T.W, the gradient of the dual with respect to the points, and the dual
 value, against the float64 oracle on the same seeded inputs and the same GPU
-potentials.
+potentials; and of the cosine cost (solve and gradient).
 
 Bars:
   P^T.W          relative Frobenius error <= 1e-3 (the transport bar: f16
@@ -129,3 +129,79 @@ def test_dual_value(fs, prec, d):
     v = float(binding.fs_dual_value(p, f, g).cpu()[0])
     want = float(np.asarray(a, np.float64) @ host(f) + np.asarray(b, np.float64) @ host(g))
     assert abs(v - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def _back(P, Pn, G):
+    """A gradient with respect to normalised points Pn = P/|P|, taken back to
+    the raw points P: (G - Pn (Pn . G)) / |P| per row."""
+    return (G - Pn * np.sum(Pn * G, axis=1, keepdims=True)) / np.linalg.norm(
+        P, axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("prec,d,n,m", [("auto", 3, 700, 900), ("auto", 64, 900, 600),
+                                        ("bf16", 256, 600, 700)])
+def test_cosine_cost(fs, prec, d, n, m):
+    """C = 2 - 2 cos(x, y): potentials against the oracle on the normalised
+    clouds (formed in float32 as the library does, see helpers), gradients
+    against the chain rule through the normalisation (pinned by finite
+    differences in test_oracle_gradient.py)."""
+    import torch
+
+    from helpers import max_err, normalise_rows, oracle_solve
+    from streaming_sinkhorn_solver_amd import binding
+
+    rng = np.random.default_rng(500 + d)
+    X = (rng.standard_normal((n, d)) + 0.3).astype(np.float32)
+    Y = (rng.standard_normal((m, d)) * 1.5 - 0.2).astype(np.float32)
+    a = rng.standard_exponential(n)
+    b = rng.standard_exponential(m)
+    a, b = (a / a.sum()).astype(np.float32), (b / b.sum()).astype(np.float32)
+    eps = 0.05
+    p, f, g, _, (Xd, Yd, _, _) = gpu_solve(X, Y, a, b, eps=eps, iters=10, prec=prec,
+                                           dv_max=d, cost="cosine")
+    Xn, Yn = normalise_rows(X), normalise_rows(Y)
+    fh, gh = host(f), host(g)
+    if prec in ("bf16", "fp16"):
+        ref = RoundedProblem(Xn, Yn, prec).solve(a, b, eps=eps, iters=10)
+        tol = 2e-3
+    else:
+        ref = oracle_solve(Xn, Yn, a, b, eps=eps, iters=10)
+        tol = 1e-3
+    assert max_err(fh, ref["f"]) <= tol * eps and max_err(gh, ref["g"]) <= tol * eps
+    gX = torch.empty((n, d), device="cuda")
+    gY = torch.empty((m, d), device="cuda")
+    binding.fs_gradient(p, eps, f, g, Xd, Yd, gX, gY)
+    torch.cuda.synchronize()
+    nu, mu = (c.astype(np.float64) for c in centres(Xn, Yn))
+    Xn64, Yn64 = Xn.astype(np.float64), Yn.astype(np.float64)
+    for side, got, P_, Pn, Qn, c in (("row", host(gX), X, Xn64, Yn64, mu),
+                                     ("col", host(gY), Y, Yn64, Xn64, nu)):
+        moved = _plan_products(Xn, Yn, a, b, fh, gh, eps, prec, Qn - c, side)
+        mass = _plan_products(Xn, Yn, a, b, fh, gh, eps, prec, np.ones((Qn.shape[0], 1)), side)
+        want = _back(np.asarray(P_, np.float64), Pn, 2.0 * (mass * (Pn - c) - moved))
+        bar = 1e-3 * 2.0 * np.linalg.norm(moved) / np.min(np.linalg.norm(P_, axis=1))
+        err = np.linalg.norm(got - want)
+        print(f"cosine {prec} d={d} {side}: error {err / bar * 1e-3:.2e} of the bar's scale, "
+              f"{err / np.linalg.norm(want):.2e} of the gradient")
+        assert err <= bar
+        # the cosine cost ignores the points' lengths: grad . p = 0 per row
+        assert np.max(np.abs(np.sum(got * P_, axis=1))) <= 1e-4 * np.max(np.abs(got)) * \
+            np.max(np.linalg.norm(P_, axis=1))
+
+
+def test_cosine_rejects_zero_length_points(fs):
+    import torch
+
+    from streaming_sinkhorn_solver_amd import binding
+
+    X = np.random.default_rng(0).standard_normal((100, 8)).astype(np.float32)
+    X[17] = 0.0
+    Y = np.random.default_rng(1).standard_normal((90, 8)).astype(np.float32)
+    a = np.full(100, 0.01, np.float32)
+    b = np.full(90, 1 / 90, np.float32)
+    with pytest.raises(binding.FsError) as e:
+        binding.fs_potentials_init(dev(X), dev(Y), dev(a), dev(b), cost="cosine")
+    assert e.value.status == binding.FS_ERR_INVALID_ARG
+    # the same points under the squared-Euclidean cost are fine
+    binding.fs_potentials_init(dev(X), dev(Y), dev(a), dev(b))
+    torch.cuda.synchronize()

@@ -161,3 +161,53 @@ def test_pins_catch_planted_gradient_mistakes(mutant):
     bad = gX / 2 if mutant == "no_factor_2" else -gX
     with pytest.raises(AssertionError):
         np.testing.assert_allclose(bad, 2 * a[:, None] * (X - Y[0]), rtol=1e-11, atol=1e-13)
+
+
+def _normalise(P):
+    return P / np.linalg.norm(P, axis=1, keepdims=True)
+
+
+def _cosine_gradient(X, Y, a, b, f, g, eps):
+    """The gradient for C = 2 - 2 cos, from the oracle's gradient with respect
+    to the normalised points taken back through x -> x/|x| (Jacobian
+    (I - x^ x^T)/|x|)."""
+    Xn, Yn = _normalise(X), _normalise(Y)
+    gXn, gYn = oracle.gradient(Xn, Yn, a, b, f, g, eps)
+
+    def back(P, Pn, G):
+        return (G - Pn * np.sum(Pn * G, axis=1, keepdims=True)) / np.linalg.norm(
+            P, axis=1, keepdims=True)
+
+    return back(X, Xn, gXn), back(Y, Yn, gYn)
+
+
+def test_g7_cosine_cost_chain_rule_by_finite_differences():
+    # OT with C = 2 - 2 cos(x, y) is the squared-Euclidean OT of the
+    # normalised clouds; its gradient with respect to the raw points, by
+    # central differences of the converged value, matches the chain rule.
+    X, Y, a, b = _problem(18, 5, 6, 3)
+    eps = 0.3
+    f, g = _converged(_normalise(X), _normalise(Y), a, b, eps)
+    C = 2.0 - 2.0 * (_normalise(X) @ _normalise(Y).T)
+    np.testing.assert_allclose(C, ((_normalise(X)[:, None] - _normalise(Y)[None]) ** 2).sum(-1),
+                               atol=1e-14)
+    gX, gY = _cosine_gradient(X, Y, a, b, f, g, eps)
+    h = 1e-5
+
+    def val(Xq, Yq):
+        return _ot_value(_normalise(Xq), _normalise(Yq), a, b, eps)
+
+    for i, k in [(0, 0), (2, 1), (4, 2)]:
+        Xp, Xm = X.copy(), X.copy()
+        Xp[i, k] += h
+        Xm[i, k] -= h
+        fd = (val(Xp, Y) - val(Xm, Y)) / (2 * h)
+        assert abs(fd - gX[i, k]) <= 1e-6 * (1 + abs(gX[i, k]))
+    for j, k in [(1, 0), (5, 2)]:
+        Yp, Ym = Y.copy(), Y.copy()
+        Yp[j, k] += h
+        Ym[j, k] -= h
+        fd = (val(X, Yp) - val(X, Ym)) / (2 * h)
+        assert abs(fd - gY[j, k]) <= 1e-6 * (1 + abs(gY[j, k]))
+    # scale invariance of the cosine cost: the gradient is orthogonal to x_i
+    assert np.max(np.abs(np.sum(gX * X, axis=1))) <= 1e-12
