@@ -27,6 +27,10 @@ Prints one JSON line with
              probe kernel of that unit alone (fs_probe_peak: independent chains
              of the score path's matrix instruction, or of v_exp_f32) reaches
              on this GPU right after the timed region
+  clocks     mean socket power and graphics clock sampled with amd-smi during
+             the timed steps (null when the tool is unavailable).  Context
+             only: the tool reports averages over its own window, which for
+             runs of a few seconds includes the idle time before them
   phases_ms  mean time per step of problem preparation, the solve and the
              transport (HIP events on the solver's stream)
   backward   (recipes with a transport of width >= d) one fs_gradient call
@@ -41,7 +45,9 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -130,6 +136,43 @@ def traffic_per_launch(workload: str):
     if rec.get("kernel_source_sha") != kernel_source_sha(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+class PowerSampler(threading.Thread):
+    """Samples socket power and the graphics clocks with `amd-smi metric`
+    while the timed steps run (best effort: no samples if the tool is absent
+    or fails)."""
+
+    def __init__(self, gpu: int = 0, period_s: float = 0.5):
+        super().__init__(daemon=True)
+        self.gpu, self.period = gpu, period_s
+        self.halt = threading.Event()
+        self.power, self.clk = [], []
+
+    def run(self):
+        cmd = ["amd-smi", "metric", "-g", str(self.gpu), "--power", "--clock", "--json"]
+        while not self.halt.is_set():
+            try:
+                res = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+                data = json.loads(res.stdout)
+                gd = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+                self.power.append(float(gd["power"]["socket_power"]["value"]))
+                clks = [float(v["clk"]["value"]) for k, v in gd["clock"].items()
+                        if k.startswith("gfx_") and isinstance(v, dict)
+                        and isinstance(v.get("clk"), dict)]
+                if clks:
+                    self.clk.append(sum(clks) / len(clks))
+            except Exception:
+                return
+            self.halt.wait(self.period)
+
+    def summary(self):
+        if not self.power:
+            return None
+        return {"source": "amd-smi metric during the timed steps", "samples": len(self.power),
+                "socket_power_w_mean": round(sum(self.power) / len(self.power), 1),
+                "gfx_clock_mhz_mean": round(sum(self.clk) / len(self.clk), 1) if self.clk
+                else None}
 
 
 def cpu_baseline(w, target_s: float = 15.0) -> dict:
@@ -231,11 +274,15 @@ def main():
     for _ in range(args.warmup):
         p = step(False)
     torch.cuda.synchronize()
+    sampler = PowerSampler()
+    sampler.start()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         p = step(True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    sampler.halt.set()
+    sampler.join(timeout=30)
     info = p.info
 
     for ev in stats["events"]:
@@ -287,6 +334,7 @@ def main():
                 "peak_probe": PROBES[wl],
                 "kernel": kernel + " (one half-step)",
                 "mean_launch_ms": round(lse_mean_ms, 4), "launches": stats["lse_launches"]}
+    clocks = sampler.summary()
     out = {
         "metric": METRIC, "value": round(it_s, 3), "unit": "iters/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
@@ -299,6 +347,7 @@ def main():
                    "g_splits": info["g_splits"]},
         "pair_evals_per_s": pair_evals / dt,
         "phases_ms": phases,
+        "clocks": clocks,
         "roofline": roofline,
     }
     if backward:
