@@ -45,6 +45,7 @@ struct fs_problem {
     float* pot_tmp;   // max(n, m) floats
     void* vt;         // f16 [dv_max][m_pad] (matrix paths with dv_max > 0)
     float* kbias;     // [m_pad] key biases of the streaming transport kernel
+    float* lbias;     // [max(n_pad, m_pad)] key seeds of the 1024-wide LSE kernel
     float* upart;     // [kTransportMaxSplit][n][dv_max] its partial products
     float* krec;      // small-d matrix path: key records of one pass (fp32)
     void* krec16;     //   fp16-split records (d <= 4)
@@ -175,7 +176,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 
 struct Layout {
     size_t centre, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
-        vt, kbias, upart, krec, krec16, kguard, rsx, rsy, total;
+        vt, kbias, upart, krec, krec16, kguard, rsx, rsy, lbias, total;
 };
 
 Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
@@ -220,6 +221,7 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.kguard = take(small ? 32 : 0);  // packing guard [2], cloud L1 maxima [2]
     L.rsx = take(sizeof(float) * n);  // cosine cost: 1/|x_i|
     L.rsy = take(sizeof(float) * m);
+    L.lbias = take(lse_wide(sh.path, sh.lse_dp) ? sizeof(float) * kmax : 0);
     L.total = o;
     return L;
 }
@@ -284,6 +286,8 @@ LseArgs base_args(const fs_problem* p, bool f_side, float eps) {
     a.krec_guard = p->kguard;
     a.krec_keys = (int)K.n_pad;
     a.row_l1 = R.l1max;
+    a.kbias = p->lbias;
+    a.kbias_keys = (int)K.n_pad;
     return a;
 }
 
@@ -457,6 +461,7 @@ fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a
         p->kbias = streams ? (float*)(w + L.kbias) : nullptr;
         p->upart = streams ? (float*)(w + L.upart) : nullptr;
     }
+    p->lbias = lse_wide(sh.path, sh.lse_dp) ? (float*)(w + L.lbias) : nullptr;
     p->krec = sh.path == PATH_SMALL ? (float*)(w + L.krec) : nullptr;
     p->krec16 = sh.path == PATH_SMALL ? (void*)(w + L.krec16) : nullptr;
     p->kguard = sh.path == PATH_SMALL ? (void*)(w + L.kguard) : nullptr;

@@ -76,6 +76,10 @@ struct LseArgs {
     void* krec_guard;
     int krec_keys;      // records packed (the key cloud's padded count)
     const float* row_l1;  // largest L1 norm of a row point (device scalar)
+    // 1024-wide split-contraction kernel (workspace): key biases in
+    // dot-product units of this pass [keys' padded count]
+    float* kbias;
+    int kbias_keys;
 };
 
 // Arguments of the transport application U = P.V (or P.V / a).
@@ -149,6 +153,9 @@ int lse_rows_per_block(int path, int dp, int n_rows);
 // Largest key range one workgroup of the streaming kernel may cover (its key
 // biases are held in LDS).
 int lse_max_keys_per_split(int path, int dp);
+// true when the pass runs the split-contraction kernel for 1024-wide two-byte
+// rows, which needs LseArgs::kbias (one float per padded key)
+bool lse_wide(int path, int dp);
 // Key-range granularity of a split (keys per streamed tile).
 int lse_split_granule(int path, int dp);
 

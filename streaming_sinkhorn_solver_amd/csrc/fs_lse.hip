@@ -668,6 +668,263 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     }
 }
 
+// ------------------------------------- 1024-wide rows: split contraction
+// Key biases of one pass in dot-product units (the seeds of the score
+// accumulators, as in lse_mfma_kernel): kb[j] = (pot_j - nrm_j)/2 +
+// log2(w_j)/(2 c_bias), -inf for the padding keys.
+__global__ __launch_bounds__(256) void key_seed_kernel(LseArgs a) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= a.kbias_keys) return;
+    a.kbias[j] = j < a.n_keys ? fmaf(a.key_lw2[j], 0.5f / a.c_bias,
+                                     0.5f * (a.key_pot[j] - a.key_nrm[j]))
+                              : -INFINITY;
+}
+
+// Rows of 1024 two-byte values are too wide for two waves per SIMD to each
+// hold a 32-row block (256 registers), and one wave per SIMD that reads a
+// key fragment from LDS for every matrix instruction cannot keep the matrix
+// pipe busy.  So the contraction is split: the two waves of a SIMD (w and
+// w+4) hold the SAME 32 rows, wave w the first 512 values of each row and
+// wave w+4 the last 512, and each forms the partial scores of its half for
+// all 32 keys of a tile.  Each finalises 16 of the tile's keys -- wave w keys
+// 0-15 (accumulator registers 0-7), wave w+4 keys 16-31 (registers 8-15) --
+// after adding the partner's partial for those keys, passed through LDS.
+// The key biases seed wave w's partials only, so every score gets them once.
+//
+// Stage s (tile s in slot s%2; the next tile's load into the other slot):
+//   wave w   : scores of tile s (its half) -> write registers 8-15 for the
+//              partner -> epilogue of tile s-1 (its registers 0-7 of that
+//              tile plus the partner's, written in stage s-1);
+//   wave w+4 : issue the loads of tile s+1 -> epilogue of tile s-1 (registers
+//              8-15 plus the partner's) -> scores of tile s -> write
+//              registers 0-7 for the partner;
+//   wait for the loads, barrier.
+// The two waves of a SIMD thus run opposite phases (matrix / vector), and the
+// exchange buffers alternate by tile parity, so a buffer is rewritten only
+// two stages after it was written, one barrier after it was read.  The LSE
+// state uses the lazy reference of the two-wave kernel.  At the end the two
+// halves of each row's key set are merged through LDS, then the lane halves.
+template <int OP>
+__global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
+    constexpr int CPR = 128;                  // 16-byte chunks per row
+    constexpr int ROW_BYTES = CPR * 16;       // 2 KiB
+    constexpr int TILE_CHUNKS = kKeyTile * CPR;
+    constexpr int TILE_BYTES = TILE_CHUNKS * 16;  // 64 KiB
+    constexpr int LOADS = TILE_CHUNKS / 64 / 4;   // 1 KiB loads per tile per loading wave
+    constexpr int HG = 32;                    // fragments per half row
+    constexpr int JB = 8;
+    constexpr int AP = 4;
+    __shared__ __attribute__((aligned(16))) uint4 kbuf[2 * TILE_CHUNKS];  // 128 KiB
+    // [tile parity][row group][direction][quad][lane]: direction 0 carries
+    // registers 8-15 (to the second wave), 1 registers 0-7 (to the first)
+    __shared__ __attribute__((aligned(16))) float4 xbuf[2][4][2][2][64];    // 32 KiB
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave & 3, dh = wave >> 2;  // row group, contraction half
+    const bool first = dh == 0;
+    const int ln = lane & 31, h = lane >> 5;
+    int row_block, split;
+    xcd_work(row_block, split);
+    const int row0 = row_block * 128 + rg * 32;
+    const int j0 = split * a.keys_per_split;
+    const int j1 = min(a.n_keys, j0 + a.keys_per_split);
+    const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
+    const char* __restrict__ keys = (const char*)a.keys;
+
+    // tile loads: by the second waves only, 16 slices of 1 KiB each
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    auto issue_tile = [&](int k, int slot) __attribute__((always_inline)) {
+        const char* tbase = keys + (int64_t)(j0 + k * kKeyTile) * ROW_BYTES;
+        uint4* dst = kbuf + slot * TILE_CHUNKS;
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) {
+            const int L = l * 4 + rg;
+            const int m = L >> 1;
+            uint32_t sw = (uint32_t)(m & 15) * 16u;
+            asm volatile("" : "+s"(sw));
+            dma_to_lds16(tbase + m * ROW_BYTES + (L & 1) * 1024, lane16 ^ sw, dst + L * 64);
+        }
+    };
+    if (!first && ntiles > 0) issue_tile(0, 0);
+
+    // this wave's half of the resident rows: fragment g is chunk
+    // 64 dh + 2g + h of row row0 + ln
+    u32x4 q[HG];
+    {
+        const char* rp = (const char*)a.rows + (int64_t)(row0 + ln) * ROW_BYTES + (dh * 64 + h) * 16;
+#pragma unroll
+        for (int g = 0; g < HG; ++g) q[g] = *(const u32x4*)(rp + g * 32);
+        // consumed here, so the compiler's waits for these loads stay in the
+        // prologue (all loads in flight first, then in-order waits)
+#pragma unroll
+        for (int g = 0; g < HG; ++g) asm volatile("" ::"v"(q[g]));
+    }
+    // key fragment g of this half: chunk 64 dh + 2g + h of key ln, stored at
+    // ln*CPR + (chunk ^ (ln & 15)); the XOR stays inside the half's 64 chunks.
+    // Slot 1 starts at 64 KiB, beyond an LDS read's immediate offset: it
+    // addresses from a second, register-held set of bases.
+    int abase[JB], abase_hi[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+        abase[j] = (ln * CPR + dh * 64 + ((2 * j + h) ^ (ln & 15))) * 16;
+        abase_hi[j] = abase[j] + TILE_BYTES;
+        asm volatile("" : "+v"(abase_hi[j]));
+    }
+    auto frag = [&](auto slot_c, int g) __attribute__((always_inline)) -> uint4 {
+        const char* base = (const char*)kbuf;
+        if constexpr (decltype(slot_c)::value == 1)
+            return *(const uint4*)(base + abase_hi[g % JB] + (g / JB) * 256);
+        else
+            return *(const uint4*)(base + abase[g % JB] + (g / JB) * 256);
+    };
+    // key biases of tile k for this lane's accumulator order (first waves)
+    const float* __restrict__ kb = a.kbias + j0;
+    auto load_bias = [&](int k, float4 (&bv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) bv[qq] = *(const float4*)(kb + k * kKeyTile + 8 * qq + 4 * h);
+    };
+    float4 bnext[4];
+    if (first && ntiles > 0) load_bias(0, bnext);
+
+    // partial scores of tile (slot SL) into acc
+    auto scores = [&](auto slot_c, f32x16& acc) __attribute__((always_inline)) {
+        if (first) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                acc[4 * qq + 0] = bnext[qq].x;
+                acc[4 * qq + 1] = bnext[qq].y;
+                acc[4 * qq + 2] = bnext[qq].z;
+                acc[4 * qq + 3] = bnext[qq].w;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        }
+        uint4 av[AP];
+#pragma unroll
+        for (int g = 0; g < AP; ++g) av[g] = frag(slot_c, g);
+#pragma unroll
+        for (int g = 0; g < HG; ++g) {
+            acc = mfma_step<OP>(av[g % AP], q[g], acc);
+            if (g + AP < HG) av[g % AP] = frag(slot_c, g + AP);
+        }
+        if constexpr (kPinSched) {
+            __builtin_amdgcn_sched_group_barrier(0x100, AP, 0);
+#pragma unroll
+            for (int g = 0; g < HG; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (g + AP < HG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+    };
+    // the partner's registers for this wave's keys
+    auto put = [&](const f32x16& acc, int par) __attribute__((always_inline)) {
+        const int base = first ? 8 : 0;  // registers the partner finalises
+        float4* dst = &xbuf[par][rg][first ? 0 : 1][0][0];
+        dst[lane] = make_float4(acc[base + 0], acc[base + 1], acc[base + 2], acc[base + 3]);
+        dst[64 + lane] = make_float4(acc[base + 4], acc[base + 5], acc[base + 6], acc[base + 7]);
+    };
+    // online LSE over this wave's 16 keys of a tile: own registers plus the
+    // partner's (lazy reference as in lse_mfma_kernel)
+    float M = -INFINITY, S = 0.f;
+    auto epilogue = [&](const f32x16& acc, int par) __attribute__((always_inline)) {
+        const int base = first ? 0 : 8;
+        const float4* src = &xbuf[par][rg][first ? 1 : 0][0][0];
+        const float4 p0 = src[lane], p1 = src[64 + lane];
+        float v[8] = {acc[base + 0] + p0.x, acc[base + 1] + p0.y, acc[base + 2] + p0.z,
+                      acc[base + 3] + p0.w, acc[base + 4] + p1.x, acc[base + 5] + p1.y,
+                      acc[base + 6] + p1.z, acc[base + 7] + p1.w};
+        float e[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) e[r] = ex2(fmaf(v[r], a.c_score, -M));
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+            for (int r = 0; r < w; ++r) e[r] += e[r + w];
+        if (__builtin_amdgcn_ballot_w64(!(e[0] <= kLazyBound))) {
+            float tmax = v[0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, v[r]);
+            const float Mn = fmaxf(M, a.c_score * tmax);
+            const float sh = Mn == -INFINITY ? 0.f : Mn;
+            float t = S * ex2(M - sh);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t += ex2(fmaf(v[r], a.c_score, -sh));
+            S = t;
+            M = Mn;
+        } else {
+            S += e[0];
+        }
+        asm volatile("" : "+v"(S), "+v"(M));
+    };
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    f32x16 accA, accB;
+    auto stage = [&](int s, auto slot_c, f32x16& acc, f32x16& prev) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot_c)::value;
+        if (first) {
+            scores(slot_c, acc);
+            load_bias(min(s + 1, ntiles - 1), bnext);
+            __builtin_amdgcn_sched_barrier(0);
+            put(acc, s & 1);
+            if (s > 0) epilogue(prev, (s - 1) & 1);
+        } else {
+            issue_tile(min(s + 1, ntiles - 1), 1 - SL);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s > 0) epilogue(prev, (s - 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            scores(slot_c, acc);
+            put(acc, s & 1);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        stage_barrier();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        stage(t, S0{}, accA, accB);
+        if (t + 1 < ntiles) stage(t + 1, S1{}, accB, accA);
+    }
+    // the epilogue of the last tile (its exchange landed before the last barrier)
+    if (ntiles > 0) {
+        if ((ntiles - 1) % 2 == 0)
+            epilogue(accA, (ntiles - 1) & 1);
+        else
+            epilogue(accB, (ntiles - 1) & 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave is done with the tile and exchange buffers
+
+    // Merge the two key halves of each row (second wave -> first through
+    // LDS), then the lane halves, and finish.
+    float2* mrg = (float2*)kbuf;
+    if (!first) mrg[rg * 64 + lane] = make_float2(M, S);
+    __syncthreads();
+    float resid = 0.f;
+    if (first) {
+        const float2 o = mrg[rg * 64 + lane];
+        lse_merge(M, S, o.x, o.y);
+        const float M2 = __shfl_xor(M, 32, 64);
+        const float S2 = __shfl_xor(S, 32, 64);
+        lse_merge(M, S, M2, S2);
+        const int row = row0 + ln;
+        if (h == 0 && row < a.n_rows) {
+            if (a.n_split == 1)
+                resid = finalize_row(a, row, M + lg2(S));
+            else
+                a.part[(int64_t)split * a.n_rows + row] = make_float2(M, S);
+        }
+    }
+    if (a.n_split == 1 && a.cur) {
+        // block_sum's first barrier orders the merge reads before its writes
+        resid = block_sum(resid, (float*)kbuf);
+        if (tid == 0) a.resid_part[row_block] = resid;
+    }
+}
+
 // ----------------------------------------------------------------- merge
 __global__ __launch_bounds__(256) void lse_merge_kernel(LseArgs a) {
     __shared__ float red[16];
@@ -770,14 +1027,31 @@ int mfma_qb(int path, int ng) {
 
 int ng_of(int path, int dp) { return path == PATH_MFMA_F32 ? dp / 8 : dp / 16; }
 
+#ifdef FS_NO_WIDE_LSE
+constexpr bool kWideLse = false;
+#else
+constexpr bool kWideLse = true;
+#endif
+
+template <int OP>
+hipError_t wide_launch(const LseArgs& a, hipStream_t s) {
+    const dim3 grid((a.n_rows + 127) / 128, a.n_split);
+    lse_wide_kernel<OP><<<grid, 512, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool lse_wide(int path, int dp) {
+    return kWideLse && (path == PATH_MFMA_BF16 || path == PATH_MFMA_F16) && dp == 1024;
+}
 
 // The vector path uses 4 rows per lane when there are enough rows to fill the
 // GPU, else 1.
 int valu_rows_per_lane(int n_rows) { return n_rows >= 65536 ? 4 : 1; }
 
 int lse_max_keys_per_split(int path, int dp) {
-    if (small_d_path(path)) return 1 << 30;
+    if (small_d_path(path) || lse_wide(path, dp)) return 1 << 30;
     return kps_max_for(ng_of(path, dp));
 }
 
@@ -790,6 +1064,7 @@ int lse_split_granule(int path, int dp) {
 int lse_rows_per_block(int path, int dp, int n_rows) {
     if (path == PATH_VALU) return 256 * valu_rows_per_lane(n_rows);
     if (path == PATH_SMALL) return small_rows_per_block();
+    if (lse_wide(path, dp)) return 128;
     const int ng = ng_of(path, dp);
     return waves_for(ng) * 32 * mfma_qb(path, ng);
 }
@@ -800,10 +1075,20 @@ int lse_rows_per_block(int path, int dp, int n_rows) {
 hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s, hipEvent_t ev_begin,
                       hipEvent_t ev_end) {
     hipError_t e;
+    const bool wide = lse_wide(path, a.dp);
+    if (wide) {
+        // the key seeds go first, outside the kernel's timed bracket
+        if (!a.kbias || a.kbias_keys < (a.n_keys + kKeyTile - 1) / kKeyTile * kKeyTile)
+            return hipErrorInvalidValue;
+        key_seed_kernel<<<(a.kbias_keys + 255) / 256, 256, 0, s>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (path == PATH_SMALL) {
         e = launch_lse_small(a, s, ev_begin);
     } else if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) {
         return e;
+    } else if (wide) {
+        e = path == PATH_MFMA_BF16 ? wide_launch<OP_BF16>(a, s) : wide_launch<OP_F16>(a, s);
     } else if (path == PATH_VALU) {
         const int R = valu_rows_per_lane(a.n_rows);
         e = valu_dispatch(a.dp, a, s, R);

@@ -147,6 +147,45 @@ def test_split_path_is_exercised(fs):
     assert max_err(host(g), ref["g"]) <= TOL_FP32 * eps
 
 
+@pytest.mark.parametrize("prec", ["fp16", "bf16"])
+def test_wide_rows_unsplit_with_residual(fs, prec):
+    # 1024-D two-byte rows: 32,700 rows fill 256 row blocks of 128, so the
+    # f-update runs unsplit (finalize and per-block residual in the kernel);
+    # the g-update over those 32,700 keys runs split.  1,100 keys leave a
+    # ragged last tile.  Sampled rows and columns against the oracle on the
+    # path's own problem; the residual against its definition evaluated on
+    # the GPU's own outputs.
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    n, m = 32700, 1100
+    w = workloads.make("c4", n=n, m=m)
+    eps = 0.05
+    Xd, Yd, ad, bd = dev(w.X), dev(w.Y), dev(w.a), dev(w.b)
+    f = torch.empty(n, device="cuda")
+    g = torch.empty(m, device="cuda")
+    p = binding.fs_potentials_init(Xd, Yd, ad, bd, prec=prec, f=f, g=g)
+    assert p.info["f_splits"] == 1 and p.info["g_splits"] > 1, p.info
+    binding.fs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=3)
+    f1 = torch.empty_like(f)
+    g1 = torch.empty_like(g)
+    r = torch.zeros(1, device="cuda")
+    binding.fs_lse_update_f(p, eps, g, f1, f_cur=f, row_resid=r)
+    binding.fs_lse_update_g(p, eps, f1, g1)
+    torch.cuda.synchronize()
+    fh, gh, f1h, g1h = host(f), host(g), host(f1), host(g1)
+    rng = np.random.default_rng(77)
+    rows = np.sort(np.concatenate([rng.choice(n, 200, replace=False), [0, 127, 128, n - 1]]))
+    cols = np.sort(np.concatenate([rng.choice(m, 100, replace=False), [0, m - 1]]))
+    rp = RoundedProblem(w.X, w.Y, prec)
+    assert max_err(f1h[rows], rp.f_update_rows(w.b, gh, eps, rows)) <= TOL_LOWP_ROUNDED * eps
+    assert max_err(g1h[cols], rp.g_update_cols(w.a, f1h, eps, cols)) <= TOL_LOWP_ROUNDED * eps
+    want = float(np.sum(np.asarray(w.a, np.float64) *
+                        np.abs(np.exp((fh.astype(np.float64) - f1h) / eps) - 1.0)))
+    got = float(r.cpu()[0])
+    assert abs(got - want) <= 1e-4 * want + 1e-7, (got, want)
+
+
 def test_residual_matches_oracle(fs):
     import torch
     from streaming_sinkhorn_solver_amd import binding
