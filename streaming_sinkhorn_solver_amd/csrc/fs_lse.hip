@@ -177,6 +177,10 @@ constexpr bool kLazyRef = true;  // two waves per SIMD: lazy LSE reference (belo
 // this bound (a score more than ~64 above R, or R still -inf) does the wave
 // move R to the exact running maximum and rescale.
 constexpr float kLazyBound = 0x1p64f;
+#ifndef FS_WIDE_DMA
+#define FS_WIDE_DMA 1
+#endif
+constexpr int kWideDma = FS_WIDE_DMA;  // tile-load placement of the 1024-wide kernel
 
 
 template <int OP, class TA, class TB>
@@ -334,22 +338,31 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     u32x4 q[QB][NG];
     {
         const char* __restrict__ rows = (const char*)a.rows;
+        // Either way the block is consumed here, so that the compiler's own
+        // waits for these loads are placed in the prologue: left to their
+        // first use inside the tile loop they would be re-executed every
+        // tile, and there they would also wait for the tile loads in flight.
+        // Loads go out in batches of QLB before the first of them is
+        // consumed (staged in vector registers on the way to the AGPRs).
+        constexpr int QLB = Q_AGPR ? 8 : NG;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const char* rp = rows + (int64_t)(row0 + qb * 32 + ln) * ROW_BYTES + h * 16;
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const u32x4 v = *(const u32x4*)(rp + g * 32);
-                // Either way the block is consumed here, so that the
-                // compiler's own waits for these loads are placed in the
-                // prologue: left to their first use inside the tile loop they
-                // would be re-executed every tile, and there they would also
-                // wait for the tile loads in flight.
-                if constexpr (Q_AGPR) {
-                    asm volatile("" : "=a"(q[qb][g]) : "0"(v));
-                } else {
-                    q[qb][g] = v;
-                    asm volatile("" ::"v"(q[qb][g]));
+            for (int g0 = 0; g0 < NG; g0 += QLB) {
+                u32x4 v[QLB];
+#pragma unroll
+                for (int u = 0; u < QLB; ++u)
+                    if (g0 + u < NG) v[u] = *(const u32x4*)(rp + (g0 + u) * 32);
+#pragma unroll
+                for (int u = 0; u < QLB; ++u) {
+                    if (g0 + u >= NG) continue;
+                    if constexpr (Q_AGPR) {
+                        asm volatile("" : "=a"(q[qb][g0 + u]) : "0"(v[u]));
+                    } else {
+                        q[qb][g0 + u] = v[u];
+                        asm volatile("" ::"v"(q[qb][g0 + u]));
+                    }
                 }
             }
         }
@@ -710,7 +723,6 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
     constexpr int ROW_BYTES = CPR * 16;       // 2 KiB
     constexpr int TILE_CHUNKS = kKeyTile * CPR;
     constexpr int TILE_BYTES = TILE_CHUNKS * 16;  // 64 KiB
-    constexpr int LOADS = TILE_CHUNKS / 64 / 4;   // 1 KiB loads per tile per loading wave
     constexpr int HG = 32;                    // fragments per half row
     constexpr int JB = 8;
     constexpr int AP = 4;
@@ -732,21 +744,28 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
     const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
     const char* __restrict__ keys = (const char*)a.keys;
 
-    // tile loads: by the second waves only, 16 slices of 1 KiB each
+    // Tile loads: 64 slices of 1 KiB (half a key row each).  kWideDma 0: the
+    // second waves issue 16 slices each at the start of a stage; 1: the first
+    // waves issue 16 each, one after every other matrix instruction; 2: both,
+    // 8 each (second waves at the start, first waves every fourth matrix
+    // instruction).
+    constexpr int SHARE = kWideDma == 2 ? 8 : 16;
+    const bool loader = kWideDma == 2 || (kWideDma == 1) == first;
     const uint32_t lane16 = (uint32_t)lane * 16u;
-    auto issue_tile = [&](int k, int slot) __attribute__((always_inline)) {
+    auto issue_slice = [&](int k, int slot, int l) __attribute__((always_inline)) {
+        const int L = kWideDma == 2 ? l * 8 + rg + 4 * dh : l * 4 + rg;
         const char* tbase = keys + (int64_t)(j0 + k * kKeyTile) * ROW_BYTES;
-        uint4* dst = kbuf + slot * TILE_CHUNKS;
-#pragma unroll
-        for (int l = 0; l < LOADS; ++l) {
-            const int L = l * 4 + rg;
-            const int m = L >> 1;
-            uint32_t sw = (uint32_t)(m & 15) * 16u;
-            asm volatile("" : "+s"(sw));
-            dma_to_lds16(tbase + m * ROW_BYTES + (L & 1) * 1024, lane16 ^ sw, dst + L * 64);
-        }
+        const int m = L >> 1;
+        uint32_t sw = (uint32_t)(m & 15) * 16u;
+        asm volatile("" : "+s"(sw));
+        dma_to_lds16(tbase + m * ROW_BYTES + (L & 1) * 1024, lane16 ^ sw,
+                     kbuf + slot * TILE_CHUNKS + L * 64);
     };
-    if (!first && ntiles > 0) issue_tile(0, 0);
+    auto issue_tile = [&](int k, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int l = 0; l < SHARE; ++l) issue_slice(k, slot, l);
+    };
+    if (loader && ntiles > 0) issue_tile(0, 0);
 
     // this wave's half of the resident rows: fragment g is chunk
     // 64 dh + 2g + h of row row0 + ln
@@ -787,8 +806,10 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
     float4 bnext[4];
     if (first && ntiles > 0) load_bias(0, bnext);
 
-    // partial scores of tile (slot SL) into acc
-    auto scores = [&](auto slot_c, f32x16& acc) __attribute__((always_inline)) {
+    // partial scores of tile (slot SL) into acc; with DE > 0, slice l of tile
+    // kd goes to the other slot after matrix instruction DE*l + DE-1
+    auto scores = [&](auto slot_c, f32x16& acc, auto de_c, int kd) __attribute__((always_inline)) {
+        constexpr int DE = decltype(de_c)::value;
         if (first) {
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
@@ -808,6 +829,8 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
         for (int g = 0; g < HG; ++g) {
             acc = mfma_step<OP>(av[g % AP], q[g], acc);
             if (g + AP < HG) av[g % AP] = frag(slot_c, g + AP);
+            if constexpr (DE > 0)
+                if (g % DE == DE - 1) issue_slice(kd, 1 - decltype(slot_c)::value, g / DE);
         }
         if constexpr (kPinSched) {
             __builtin_amdgcn_sched_group_barrier(0x100, AP, 0);
@@ -867,18 +890,21 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
     f32x16 accA, accB;
     auto stage = [&](int s, auto slot_c, f32x16& acc, f32x16& prev) __attribute__((always_inline)) {
         constexpr int SL = decltype(slot_c)::value;
+        using DF = std::integral_constant<int, kWideDma == 0 ? 0 : (kWideDma == 1 ? 2 : 4)>;
+        using D0 = std::integral_constant<int, 0>;
+        const int kn = min(s + 1, ntiles - 1);
         if (first) {
-            scores(slot_c, acc);
+            scores(slot_c, acc, DF{}, kn);
             load_bias(min(s + 1, ntiles - 1), bnext);
             __builtin_amdgcn_sched_barrier(0);
             put(acc, s & 1);
             if (s > 0) epilogue(prev, (s - 1) & 1);
         } else {
-            issue_tile(min(s + 1, ntiles - 1), 1 - SL);
+            if constexpr (kWideDma != 1) issue_tile(kn, 1 - SL);
             __builtin_amdgcn_sched_barrier(0);
             if (s > 0) epilogue(prev, (s - 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
-            scores(slot_c, acc);
+            scores(slot_c, acc, D0{}, kn);
             put(acc, s & 1);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
