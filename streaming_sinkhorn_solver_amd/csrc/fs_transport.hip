@@ -154,6 +154,22 @@ __device__ __forceinline__ f32x16 score_step(const uint4& av, const uint4& bv, f
     }
 }
 
+// 16x16x32 score step of the 1024-wide kernel (two-byte types only)
+template <int OP>
+__device__ __forceinline__ f32x4 mfma16_step(const uint4& av, const u32x4& bv, f32x4 acc) {
+    if constexpr (OP == OP_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                       __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                      __builtin_bit_cast(f16x8, bv), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const _Float16 l = (_Float16)lo, h = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
 // Transport kernel: 4 waves x 32 rows, output columns [c0, c0 + 32*NB).
 // Pipeline stage t: DMA key tile t+2 and V^T tile t+1; score MFMAs of tile
 // t+1; for tile t the weights p = 2^(z2 - L) are packed to f16 in registers
@@ -723,6 +739,288 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
     }
 }
 
+// ------------------------------------- streaming kernel, 1024-wide rows
+// U = P.V for 1024-wide two-byte rows.  Rows this wide leave no room for a
+// 32-row resident block next to a wide output block in one wave, so the work
+// of a 32-row group is split over a pair of waves (on different SIMDs), as in
+// the 1024-wide LSE kernel: wave dh of the pair holds half dh of the
+// contraction (512 values of each row, 128 registers) and output columns
+// [dh*32*NBV, (dh+1)*32*NBV) of the workgroup's column block (NBV blocks of
+// 32 columns in the accumulation registers; 256 at NBV = 16).  Two pairs make
+// a 64-row workgroup.
+//
+// Keys stream in 16-key tiles (so that double-buffered key and V^T tiles fit
+// in LDS next to each other).  Per tile each wave forms the partial scores of
+// its half with v_mfma_f32_16x16x32 (keys x rows, two 16-row blocks per key
+// fragment; the first wave's accumulators are seeded with the key biases),
+// the pair exchanges the partials through LDS, and each wave forms the
+// weights p = 2^(c_score (own + partner) - L) of all 16 keys x 32 rows.  In
+// the score layout lane l holds rows l%16 of both row blocks for keys
+// 4(l/16)..+3; one v_permlane16_swap per packed register pair turns that into
+// the A layout of v_mfma_f32_32x32x16_f16 (lane l: row l%32, keys
+// 8(l/32)..+7), which multiplies the V^T tile of the same 16 keys.
+//
+// Stage t (K, bias slot t%2 hold tile t; V slot (t-1)%2 holds V^T of tile t-1):
+//   the partner's partial of tile t-1 is read; the score instructions of tile
+//   t run with the loads of K(t+1), its biases and V^T(t) interleaved (one
+//   slice per key fragment); then the weights of tile t-1 and its P.V
+//   instructions; the wave's partial of tile t goes to the exchange buffer
+//   (and stays in registers); loads waited for, barrier.  A last stage does
+//   only the weights and P.V of the last tile.
+// LDS: V^T row c (a column of V) holds the tile's 16 keys as two 16-byte
+// chunks, stored at c*2 + (half ^ ((c >> 3) & 1)) so that 16 consecutive rows
+// hit distinct banks.
+template <int OP, int NBV>
+__global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a, int64_t m_pad) {
+    constexpr int CPR = 128;                    // 16-byte chunks per key row (1024 values)
+    constexpr int ROW_BYTES = CPR * 16;
+    constexpr int KT = 16;                      // keys per tile
+    constexpr int KT_CHUNKS = KT * CPR;         // 32 KiB
+    constexpr int KT_SLICES = KT_CHUNKS / 64;   // 32 slices of 1 KiB
+    constexpr int DVC = 64 * NBV;               // columns per workgroup (both waves of a pair)
+    constexpr int VT_CHUNKS = DVC * 2;          // 16 keys x 2 bytes per column
+    constexpr int VT_SLICES = VT_CHUNKS / 64;
+    constexpr int VT_PER_WAVE = (VT_SLICES + 3) / 4;
+    constexpr int KS = 16;                      // 32-value contraction steps per half row
+    constexpr int AP = 4;                       // key fragments in flight
+    constexpr int APV = NBV < 4 ? NBV : 4;      // V^T fragments in flight
+    static_assert(KT_SLICES == 32 && VT_PER_WAVE <= 8, "tile shapes");
+
+    __shared__ __attribute__((aligned(16))) uint4 kbuf[2 * KT_CHUNKS];
+    __shared__ __attribute__((aligned(16))) uint4 vbuf[2 * VT_CHUNKS];
+    __shared__ __attribute__((aligned(16))) float bbuf[2][KT];
+    // [tile parity][row group][wave of the pair][row block][lane]
+    __shared__ __attribute__((aligned(16))) float4 xbuf[2][2][2][2][64];
+    __shared__ float rowscale[64];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave >> 1, dh = wave & 1;
+    const int l16 = lane & 15, kg = lane >> 4;  // score layout: row, key group
+    const int l32 = lane & 31, hh = lane >> 5;  // P.V layout: row / column, key half
+    int row_block, yb;
+    xcd_work(row_block, yb);
+    const int n_cb = (a.dv + DVC - 1) / DVC;
+    const int cb0 = yb % n_cb, split = yb / n_cb;
+    const int row0 = row_block * 64 + rg * 32;
+    const int c0 = cb0 * DVC;
+    const int j0 = split * a.keys_per_split;
+    const int j1 = min(a.n_keys, j0 + a.keys_per_split);
+    const int ntiles = (j1 - j0 + KT - 1) / KT;
+    const char* __restrict__ keys = (const char*)a.keys;
+    const char* __restrict__ Vt = (const char*)a.Vt;
+    const char* __restrict__ kbias = (const char*)a.key_bias;
+
+    // ---- loads: K slices L = 4l + wave (l < 8), V^T slices 4l + wave (< VT_SLICES)
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    // V^T slice L, lane: tile row c = (64 L + lane) / 2, stored chunk lane & 1,
+    // which holds key half (lane & 1) ^ ((c >> 3) & 1)
+    auto voff = [&](int L) __attribute__((always_inline)) -> uint32_t {
+        const int c = 32 * L + (lane >> 1);
+        const int kh = (lane & 1) ^ ((c >> 3) & 1);
+        const int col = min(c0 + c, a.dv - 1);  // columns past dv: any valid one, unused
+        return (uint32_t)col * (uint32_t)(m_pad * 2) + (uint32_t)(kh * 16);
+    };
+    auto issue_k_slice = [&](int k, int slot, int l) __attribute__((always_inline)) {
+        const int L = 4 * l + wave;
+        const int m = L >> 1;
+        const char* src = keys + (int64_t)(j0 + k * KT + m) * ROW_BYTES + (L & 1) * 1024;
+        uint32_t sw = (uint32_t)(m & 15) * 16u;
+        asm volatile("" : "+s"(sw));
+        dma_to_lds16(src, lane16 ^ sw, kbuf + slot * KT_CHUNKS + L * 64);
+    };
+    auto issue_v_slice = [&](int k, int slot, int l) __attribute__((always_inline)) {
+        const int L = 4 * l + wave;
+        if (VT_SLICES % 4 == 0 || L < VT_SLICES)
+            dma_to_lds16(Vt + (int64_t)(j0 + k * KT) * 2, voff(L), vbuf + slot * VT_CHUNKS + L * 64);
+    };
+    auto issue_bias = [&](int k, int slot) __attribute__((always_inline)) {
+        if (wave == 0 && lane < 4)
+            dma_to_lds16(kbias + (int64_t)(j0 + k * KT) * 4, lane16, &bbuf[slot][0]);
+    };
+    if (ntiles > 0) {
+#pragma unroll
+        for (int l = 0; l < 8; ++l) issue_k_slice(0, 0, l);
+        issue_bias(0, 0);
+    }
+
+    // ---- resident rows: q[rb][ks] = chunk 64 dh + 4 ks + kg of row row0 + 16 rb + l16
+    u32x4 q[2][KS];
+    {
+        const char* rp = (const char*)a.rows + (int64_t)(row0 + l16) * ROW_BYTES + (64 * dh + kg) * 16;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) q[rb][ks] = *(const u32x4*)(rp + rb * 16 * ROW_BYTES + ks * 64);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(q[rb][ks]));
+    }
+    // rows past n: L = +inf makes every weight 0
+    float Lr[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = row0 + 16 * rb + l16;
+        Lr[rb] = row < a.n_rows ? a.row_lse2[row] : INFINITY;
+        asm volatile("" : "+v"(Lr[rb]));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // key fragment ks of the tile in slot `slot`: chunk 64 dh + 4 ks + kg of
+    // key l16, stored at l16*CPR + (chunk ^ l16)
+    int kbase[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kbase[j] = (l16 * CPR + 64 * dh + ((4 * j + kg) ^ l16)) * 16;
+    auto kfrag = [&](int slot, int ks) __attribute__((always_inline)) -> uint4 {
+        return *(const uint4*)((const char*)kbuf + kbase[ks & 3] + slot * (KT_CHUNKS * 16) +
+                               (ks >> 2) * 256);
+    };
+    // V^T fragment of output block cb (this wave's half): row
+    // dh*32*NBV + 32 cb + l32, key half hh
+    const int vrow = dh * 32 * NBV + l32;
+    const int vbase = (vrow * 2 + (hh ^ ((vrow >> 3) & 1))) * 16;
+    auto vfrag = [&](int slot, int cb) __attribute__((always_inline)) -> uint4 {
+        return *(const uint4*)((const char*)vbuf + vbase + slot * (VT_CHUNKS * 16) + cb * 1024);
+    };
+
+    f32x16 u[NBV];
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) u[nb][r] = 0.f;
+
+    for (int t = 0; t <= ntiles; ++t) {
+        const int cs = t & 1, ps = cs ^ 1;
+        if (t < ntiles) {
+            // scores of tile t, the loads of the next tiles interleaved
+            const int kn = min(t + 1, ntiles - 1);
+            f32x4 acc[2];
+            {
+                float4 seed = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (dh == 0) seed = *(const float4*)&bbuf[cs][4 * kg];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    acc[rb][0] = seed.x;
+                    acc[rb][1] = seed.y;
+                    acc[rb][2] = seed.z;
+                    acc[rb][3] = seed.w;
+                }
+            }
+            uint4 av[AP];
+#pragma unroll
+            for (int g = 0; g < AP; ++g) av[g] = kfrag(cs, g);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    acc[rb] = mfma16_step<OP>(av[ks % AP], q[rb][ks], acc[rb]);
+                if (ks + AP < KS) av[ks % AP] = kfrag(cs, ks + AP);
+                if (ks < 8)
+                    issue_k_slice(kn, ps, ks);
+                else if (ks - 8 < VT_PER_WAVE)
+                    issue_v_slice(t, cs, ks - 8);
+                if (ks == 0) issue_bias(kn, ps);
+            }
+            // pinned ring order: the seed and first AP reads, then per key
+            // fragment its two matrix instructions and its refill read
+            __builtin_amdgcn_sched_group_barrier(0x100, AP + 1, 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (ks + AP < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // this wave's partial of tile t, for both waves of the pair
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                xbuf[cs][rg][dh][rb][lane] = make_float4(acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]);
+        }
+        if (t > 0) {
+            // weights and P.V of tile t-1 (both partials from the exchange buffer)
+            float z[2][4];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const float4 o = xbuf[ps][rg][dh][rb][lane];
+                const float4 p = xbuf[ps][rg][dh ^ 1][rb][lane];
+                z[rb][0] = o.x + p.x;
+                z[rb][1] = o.y + p.y;
+                z[rb][2] = o.z + p.z;
+                z[rb][3] = o.w + p.w;
+            }
+            uint32_t x[2], y[2];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                x[hp] = pack_f16x2(ex2(fmaf(z[0][2 * hp], a.c_score, -Lr[0])),
+                                   ex2(fmaf(z[0][2 * hp + 1], a.c_score, -Lr[0])));
+                y[hp] = pack_f16x2(ex2(fmaf(z[1][2 * hp], a.c_score, -Lr[1])),
+                                   ex2(fmaf(z[1][2 * hp + 1], a.c_score, -Lr[1])));
+            }
+            // lane rows 2i keep row block 0 and take the odd neighbour's
+            // row-block-0 keys; rows 2i+1 keep block 1 and take the even
+            // neighbour's: afterwards lane l holds row l%32, keys 8(l/32)..+7
+            const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+            uint4 au;
+            au.x = s0[0];
+            au.y = s1[0];
+            au.z = s0[1];
+            au.w = s1[1];
+            const f16x8 A = __builtin_bit_cast(f16x8, au);
+            __builtin_amdgcn_sched_barrier(0);
+            uint4 bv[APV];
+#pragma unroll
+            for (int k = 0; k < APV; ++k) bv[k] = vfrag(ps, k);
+#pragma unroll
+            for (int k = 0; k < NBV; ++k) {
+                u[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(f16x8, bv[k % APV]),
+                                                            u[k], 0, 0, 0);
+                if (k + APV < NBV) bv[k % APV] = vfrag(ps, k + APV);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, APV, 0);
+#pragma unroll
+            for (int k = 0; k < NBV; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (k + APV < NBV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        stage_barrier();
+    }
+
+    // Row factor 2^(L_i + (f_i - A_i) c_bias) [* a_i] * 2^-s, or 1 when the
+    // key range is one of several (the merge applies it to the sum).
+    if (dh == 0 && hh == 0) {
+        const int row = row0 + l32;
+        float sc = 0.f;
+        if (row < a.n_rows) {
+            if (a.n_split == 1) {
+                sc = ex2(a.row_lse2[row] + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
+                if (!a.divide_by_a) sc *= a.row_w[row];
+                sc *= a.v_unscale_dev[0];
+            } else {
+                sc = 1.f;
+            }
+        }
+        rowscale[rg * 32 + l32] = sc;
+    }
+    __syncthreads();
+    float* out = a.n_split == 1 ? a.U : a.U_part + (int64_t)split * a.part_stride;
+    // output register r of lane (l32, hh): row 8(r/4) + 4hh + (r%4), column l32
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+        const int col = c0 + dh * 32 * NBV + nb * 32 + l32;
+        if (col >= a.dv) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int row = row0 + rr;
+            if (row < a.n_rows) out[(int64_t)row * a.dv + col] = u[nb][r] * rowscale[rg * 32 + rr];
+        }
+    }
+}
+
 // U = (sum over key ranges of the partial products, in range order) times
 // the row factor.
 __global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a) {
@@ -782,6 +1080,29 @@ hipError_t transport_stream_nbv(const TransportArgs& a, int64_t m_pad, hipStream
                        : transport_stream_launch<OP, NG, 8>(a, m_pad, s);
 }
 
+// output blocks per wave of the 1024-wide kernel: the fewest that cover dv
+// in one column block (16: 1024 columns per workgroup)
+int wide_nbv(int dv) { return dv <= 64 ? 1 : dv <= 128 ? 2 : dv <= 256 ? 4 : dv <= 512 ? 8 : 16; }
+
+template <int OP, int NBV>
+hipError_t transport_wide_launch(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
+    const int n_cb = (a.dv + 64 * NBV - 1) / (64 * NBV);
+    const dim3 grid((a.n_rows + 63) / 64, n_cb * a.n_split);
+    transport_wide_kernel<OP, NBV><<<grid, 256, 0, s>>>(a, m_pad);
+    return hipGetLastError();
+}
+
+template <int OP>
+hipError_t transport_wide_dispatch(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
+    switch (wide_nbv(a.dv)) {
+        case 1: return transport_wide_launch<OP, 1>(a, m_pad, s);
+        case 2: return transport_wide_launch<OP, 2>(a, m_pad, s);
+        case 4: return transport_wide_launch<OP, 4>(a, m_pad, s);
+        case 8: return transport_wide_launch<OP, 8>(a, m_pad, s);
+        default: return transport_wide_launch<OP, 16>(a, m_pad, s);
+    }
+}
+
 template <int OP>
 hipError_t transport_stream_dispatch(int ng, const TransportArgs& a, int64_t m_pad,
                                      hipStream_t s) {
@@ -800,14 +1121,15 @@ hipError_t transport_stream_dispatch(int ng, const TransportArgs& a, int64_t m_p
 // (row blocks x column blocks x splits) fill the compute units in whole
 // rounds best, charging each workgroup a fixed start-up of 8 tiles and each
 // extra range the traffic of its partial product (written once, read once).
-void transport_split(const TransportArgs& a, int max_split, int& S, int& kps) {
+void transport_split(const TransportArgs& a, bool wide, int max_split, int& S, int& kps) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    const int nbv = a.dv <= 128 ? 4 : 8;
-    const int64_t wg = (int64_t)((a.n_rows + 127) / 128) * ((a.dv + 32 * nbv - 1) / (32 * nbv));
+    const int rpb = wide ? 64 : 128;
+    const int cpb = wide ? 64 * wide_nbv(a.dv) : 32 * (a.dv <= 128 ? 4 : 8);
+    const int64_t wg = (int64_t)((a.n_rows + rpb - 1) / rpb) * ((a.dv + cpb - 1) / cpb);
     const int64_t m_tiles = (a.n_keys + kKeyTile - 1) / kKeyTile;
     // one tile-stage of a workgroup ~ 1 us; partial traffic at ~4 bytes/ps
     double best = 1e300;
@@ -829,10 +1151,19 @@ void transport_split(const TransportArgs& a, int max_split, int& S, int& kps) {
 
 }  // namespace
 
+namespace {
+// the 1024-wide kernel: two-byte scores, 1024-value rows, and V^T offsets
+// (column x padded key count) within a load's 32-bit offset
+bool transport_wide(int path, int dp, int dv, int64_t m_pad) {
+    return (path == PATH_MFMA_BF16 || path == PATH_MFMA_F16) && dp == 1024 &&
+           (int64_t)dv * m_pad * 2 < ((int64_t)1 << 32);
+}
+}  // namespace
+
 bool transport_streams(int path, int dp) {
     if (small_d_path(path)) return false;
     const int ng = path == PATH_MFMA_F32 ? dp / 8 : dp / 16;
-    return ng <= 32;
+    return ng <= 32 || ((path == PATH_MFMA_BF16 || path == PATH_MFMA_F16) && ng == 64);
 }
 
 hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, void* Vt_buf,
@@ -861,11 +1192,12 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
     if ((e = hipGetLastError()) != hipSuccess) return e;
     vscale_kernel<<<1, 64, 0, s>>>(maxbits, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const bool streams = transport_streams(path, a.dp);
+    const bool wide = transport_wide(path, a.dp, a.dv, m_pad);
+    const bool streams = transport_streams(path, a.dp) && (a.dp < 1024 || wide);
     {
         const dim3 grid((unsigned)((m_pad + 31) / 32), (a.dv + 31) / 32);
         transpose_v_kernel<<<grid, 256, 0, s>>>(a.V, a.n_keys, m_pad, a.dv, scratch,
-                                                (_Float16*)Vt_buf, streams ? 1 : 0, a.v_rscale,
+                                                (_Float16*)Vt_buf, streams && !wide ? 1 : 0, a.v_rscale,
                                                 a.v_off);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -879,8 +1211,11 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
         a.key_bias = key_bias_buf;
         a.U_part = part_buf;
         a.part_stride = (int64_t)a.n_rows * a.dv;
-        transport_split(a, kTransportMaxSplit, a.n_split, a.keys_per_split);
-        if (path == PATH_MFMA_F32)
+        transport_split(a, wide, kTransportMaxSplit, a.n_split, a.keys_per_split);
+        if (wide)
+            e = path == PATH_MFMA_BF16 ? transport_wide_dispatch<OP_BF16>(a, m_pad, s)
+                                       : transport_wide_dispatch<OP_F16>(a, m_pad, s);
+        else if (path == PATH_MFMA_F32)
             e = transport_stream_dispatch<OP_F32>(ng, a, m_pad, s);
         else if (path == PATH_MFMA_BF16)
             e = transport_stream_dispatch<OP_BF16>(ng, a, m_pad, s);

@@ -285,6 +285,41 @@ def test_transport(fs, prec, d, dv):
         assert rel <= 1e-3, rel
 
 
+# The 1024-D streaming transport: every output-block width (dv = 40, 100,
+# 200, 300 and 1024 use 1, 2, 4, 8 and 16 blocks of 32 columns per wave),
+# two column blocks (dv = 1100), key counts that leave a ragged 16-key tile,
+# and the key-range splits the launch heuristic picks for these few rows
+# (and none at 6,000 rows).
+@pytest.mark.parametrize("prec,dv,n,m", [("fp16", 40, 700, 850), ("bf16", 100, 500, 1000),
+                                         ("fp16", 200, 300, 777), ("fp16", 300, 700, 850),
+                                         ("bf16", 1024, 400, 601), ("fp16", 1100, 260, 500),
+                                         ("fp16", 1024, 6000, 333)])
+def test_transport_wide_rows(fs, prec, dv, n, m):
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    w = workloads.make("c4", n=n, m=m)
+    rng = np.random.default_rng(dv + n)
+    V = rng.standard_normal((m, dv)).astype(np.float32)
+    eps = 0.05
+    p, f, g, _, _ = gpu_solve(w.X, w.Y, w.a, w.b, eps=eps, iters=5, prec=prec, dv_max=dv)
+    U = torch.empty((n, dv), dtype=torch.float32, device="cuda")
+    T = torch.empty((n, dv), dtype=torch.float32, device="cuda")
+    Vd = dev(V)
+    binding.fs_apply_transport(p, eps, f, g, Vd, U)
+    binding.fs_apply_transport(p, eps, f, g, Vd, T, divide_by_a=True)
+    torch.cuda.synchronize()
+    rows = None if n <= 1000 else np.sort(np.concatenate(
+        [rng.choice(n, 120, replace=False), [0, 63, 64, n - 1]]))
+    rp = RoundedProblem(w.X, w.Y, prec)
+    U_ref = rp.transport(w.a, w.b, host(f), host(g), V, eps, rows=rows)
+    T_ref = rp.transport(w.a, w.b, host(f), host(g), V, eps, divide_by_a=True, rows=rows)
+    for got, ref in ((host(U), U_ref), (host(T), T_ref)):
+        got = got if rows is None else got[rows]
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert rel <= 1e-3, rel
+
+
 def _c4_annealed(prec):
     # The annealed 1024-D recipe (eps 1 -> 0.01) at a small size.
     w = workloads.make("c4", n=600, m=500)
