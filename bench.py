@@ -323,7 +323,7 @@ def main():
               "c5": "lse_small_kernel<2> (fp16 split scores)",
               "c2": "lse_mfma_kernel<fp32, d_pad 64>",
               "c3": "lse_mfma_kernel<bf16, d_pad 512>",
-              "c4": "lse_mfma_kernel<fp16, d_pad 1024>"}[wl]
+              "c4": "lse_wide_kernel<fp16> (1024-wide rows, contraction split over wave pairs)"}[wl]
     sink = torch.zeros(1, device=dev)
     peak_measured = binding.fs_probe_peak(PROBES[wl], sink) / 1e12
     roofline = {"bound": "mfma" if unit == "TFLOP/s" else "alu",
