@@ -11,7 +11,10 @@ against closed forms, a dense scaling-form Sinkhorn, brute-force assignment,
 1-D sorted matching and exact metamorphic relations; the gradient and the
 dual objective by central finite differences of the converged dual value,
 by translation invariance and by the single-target closed form
-(``tests/test_oracle_gradient.py``).
+(``tests/test_oracle_gradient.py``).  ``oracle/hvp.py`` (numpy, dense) holds
+the Hessian-vector product, pinned by finite differences of the gradient at
+re-converged potentials, symmetry and a closed form
+(``tests/test_oracle_hvp.py``).
 """
 from __future__ import annotations
 
