@@ -224,6 +224,39 @@ fs_status fs_gradient(fs_problem* p, float eps, const float* f, const float* g, 
 fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* out,
                         void* stream);
 
+/* Streaming Hessian-vector product of the entropic OT loss with respect to
+ * the row cloud X ("FlashSinkhorn" explainer, "Method" part 3: HVPs as
+ * sequences of transport-vector and transport-matrix products; the pages
+ * give no formula, the one used is implicit differentiation through the
+ * Sinkhorn fixed point).  With P the plan of (f, g), r = P 1, c = P^T 1,
+ * dC_ij = 2 (x_i - y_j).v_i and dP_ij = P_ij (df_i + dg_j - dC_ij)/eps where
+ * (df, dg) keep both marginals of P fixed:
+ *   HV_i = 2 r_i v_i + 2 sum_j dP_ij (x_i - y_j).
+ * dg solves K dg = w - P^T (u/r), K = diag(c) - P^T diag(1/r) P, by conjugate
+ * gradients on the complement of the constant vector (K's null space) until
+ * the residual falls to cg_tol of its start or cg_max_iter iterations; each
+ * iteration is one row and one column transport of width 1.  Besides that:
+ * two exact LSE passes, transports of widths d, d+2, d+1, and the d*d
+ * second-moment columns in passes of at most dv_max (so the problem needs
+ * dv_max >= d + 2, else FS_ERR_INVALID_ARG).  At converged potentials r = a,
+ * c = b and this is the Hessian of the loss; at other potentials it is that
+ * of the plan (f, g) define.
+ * X (n x d), Y (m x d): the fp32 points given to fs_potentials_init; V, HV:
+ * n x d device arrays (HV may not overlap any input or the workspace).
+ * workspace: device memory of at least fs_hvp_workspace_bytes(p) bytes,
+ * owned by the caller, overwritten.  info (host, nullable): CG iterations and
+ * final relative residual.  Squared-Euclidean cost only.  The host waits for
+ * the stream twice per CG iteration (the CG scalars).  The transports' f16
+ * weights (about 1e-3 relative) bound the accuracy. */
+typedef struct {
+    int32_t cg_iters;
+    float cg_residual;
+} fs_hvp_info;
+size_t fs_hvp_workspace_bytes(const fs_problem* p);
+fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const float* X,
+                 const float* Y, const float* V, float* HV, float cg_tol, int32_t cg_max_iter,
+                 void* workspace, size_t workspace_bytes, fs_hvp_info* info, void* stream);
+
 /* Frees the host handle only (the workspace is the caller's). */
 void fs_destroy(fs_problem* p);
 

@@ -47,11 +47,13 @@ def plan(X, Y, a, b, f, g, eps):
     return np.exp(np.log(a)[:, None] + np.log(b)[None, :] + (f[:, None] + g[None, :] - C) / eps)
 
 
-def hvp(X, Y, a, b, f, g, V, eps, return_parts=False):
-    """(H V) of the entropic OT loss with respect to X, at the plan of (f, g)."""
+def hvp(X, Y, a, b, f, g, V, eps, return_parts=False, P=None):
+    """(H V) of the entropic OT loss with respect to X, at the plan of (f, g)
+    (or at a given dense plan P, with the cost derivative still taken from X
+    and Y: the form a solver whose scores round the points differentiates)."""
     X, Y, V = (np.asarray(t, np.float64) for t in (X, Y, V))
     n = X.shape[0]
-    P = plan(X, Y, a, b, f, g, eps)
+    P = plan(X, Y, a, b, f, g, eps) if P is None else np.asarray(P, np.float64)
     r, c = P.sum(1), P.sum(0)
     D = X[:, None, :] - Y[None, :, :]            # x_i - y_j, n x m x d
     dC = 2.0 * np.einsum("ijk,ik->ij", D, V)      # n x m

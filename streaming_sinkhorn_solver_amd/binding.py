@@ -21,6 +21,7 @@ __all__ = [
     "fs_lse_update_f", "fs_lse_update_g", "fs_marginal_residual", "fs_sinkhorn_solve",
     "fs_apply_transport", "fs_problem_info", "fs_status_string", "fs_last_error", "solve",
     "PROBE_KINDS", "fs_probe_peak", "fs_apply_transport_t", "fs_gradient", "fs_dual_value",
+    "fs_hvp", "fs_hvp_workspace_bytes",
     "COST_SQEUCLIDEAN", "COST_COSINE",
 ]
 
@@ -53,6 +54,10 @@ class SolveInfo(ctypes.Structure):
     _fields_ = [("iters_done", ctypes.c_int32), ("final_eps", ctypes.c_float),
                 ("residual", ctypes.c_float), ("lse_launches", ctypes.c_int32),
                 ("lse_ms", ctypes.c_float)]
+
+
+class HvpInfo(ctypes.Structure):
+    _fields_ = [("cg_iters", ctypes.c_int32), ("cg_residual", ctypes.c_float)]
 
 
 class FsError(RuntimeError):
@@ -117,6 +122,11 @@ def load():
     lib.fs_gradient.argtypes = [_vp, f32, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
     lib.fs_dual_value.restype = ctypes.c_int
     lib.fs_dual_value.argtypes = [_vp, _fp, _fp, ctypes.c_void_p, _vp]
+    lib.fs_hvp_workspace_bytes.restype = ctypes.c_size_t
+    lib.fs_hvp_workspace_bytes.argtypes = [_vp]
+    lib.fs_hvp.restype = ctypes.c_int
+    lib.fs_hvp.argtypes = [_vp, f32, _fp, _fp, _fp, _fp, _fp, _fp, f32, i32, ctypes.c_void_p,
+                           ctypes.c_size_t, ctypes.POINTER(HvpInfo), _vp]
     lib.fs_probe_peak.restype = ctypes.c_int
     lib.fs_probe_peak.argtypes = [ctypes.c_int, _fp, i32, _vp, ctypes.POINTER(ctypes.c_double)]
     _LIB = lib
@@ -282,6 +292,31 @@ def fs_gradient(p: Problem, eps: float, f, g, X, Y, grad_x=None, grad_y=None, st
                                      _dev(grad_x, "grad_x", p.n * p.d),
                                      _dev(grad_y, "grad_y", p.m * p.d), _stream(stream)),
                   "fs_gradient")
+
+
+def fs_hvp_workspace_bytes(p: Problem) -> int:
+    return int(load().fs_hvp_workspace_bytes(p.handle))
+
+
+def fs_hvp(p: Problem, eps: float, f, g, X, Y, V, HV, cg_tol: float = 1e-4,
+           cg_max_iter: int = 200, workspace=None, stream=None) -> dict:
+    """Hessian-vector product of the OT loss with respect to X into HV;
+    returns the CG iterations and final relative residual.  `workspace`: a
+    device tensor of at least fs_hvp_workspace_bytes(p) bytes (allocated
+    here if None)."""
+    need = fs_hvp_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=V.device)
+    if not workspace.is_cuda:
+        raise TypeError("workspace must be a device tensor")
+    info = HvpInfo()
+    _check(load().fs_hvp(p.handle, float(eps), _dev(f, "f", p.n), _dev(g, "g", p.m),
+                         _dev(X, "X", p.n * p.d), _dev(Y, "Y", p.m * p.d),
+                         _dev(V, "V", p.n * p.d), _dev(HV, "HV", p.n * p.d), float(cg_tol),
+                         int(cg_max_iter), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), ctypes.byref(info),
+                         _stream(stream)), "fs_hvp")
+    return {"cg_iters": info.cg_iters, "cg_residual": info.cg_residual}
 
 
 def fs_dual_value(p: Problem, f, g, out=None, stream=None) -> torch.Tensor:

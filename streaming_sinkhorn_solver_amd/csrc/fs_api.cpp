@@ -343,7 +343,8 @@ bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.f; }
 // Leaves the rows' exact LSE2 in pot_tmp.
 fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, const float* g,
                          const float* V, int32_t dv, float* U, int32_t divide_by_w,
-                         const float* voff, const float* vrs, hipStream_t s) {
+                         const float* voff, const float* vrs, hipStream_t s,
+                         const float* lse2 = nullptr) {
     if (!p || !f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL argument");
     if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (dv < 1 || dv > p->dv_max)
@@ -354,12 +355,15 @@ fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, 
         return fail(FS_ERR_INVALID_ARG, "U overlaps V");
     const float* row_pot = f_side ? f : g;
     const float* key_pot = f_side ? g : f;
-    // exact row LSE (base 2) of this side's update scores
-    fs_status st = half_step(p, f_side, eps, key_pot, p->pot_tmp, nullptr, nullptr, 1, s);
-    if (st != FS_OK) return st;
+    // exact row LSE (base 2) of this side's update scores, unless the caller
+    // holds it for these potentials
+    if (!lse2) {
+        fs_status st = half_step(p, f_side, eps, key_pot, p->pot_tmp, nullptr, nullptr, 1, s);
+        if (st != FS_OK) return st;
+    }
     TransportArgs t{};
     t.rows = R.ops;
-    t.row_lse2 = p->pot_tmp;
+    t.row_lse2 = lse2 ? lse2 : p->pot_tmp;
     t.row_pot = row_pot;
     t.row_nrm = R.nrm;
     t.row_w = R.w;
@@ -715,6 +719,188 @@ fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* o
     if (!p || !f || !g || !out) return fail(FS_ERR_INVALID_ARG, "NULL argument");
     hipError_t e = launch_dual_value(p->X.w, f, p->n, p->Y.w, g, p->m, out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "dual value launch");
+    return FS_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device scratch of fs_hvp, carved from the caller's workspace (floats, each
+// array 256-byte aligned; CH = second-moment columns per transport pass).
+struct HvpLayout {
+    size_t lse_r, lse_c, r, c, PY, W, PtW, u, rhs, dg, res, pd, Ap, Pp, Ptq, V2, T, M, V3, T3, dots,
+        total;
+    int ch;
+};
+
+HvpLayout hvp_layout(const fs_problem* p) {
+    HvpLayout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = up(o + bytes, kAlign);
+        return at;
+    };
+    const size_t n = (size_t)p->n, m = (size_t)p->m, d = (size_t)p->d;
+    L.ch = (int)std::min<int64_t>((int64_t)p->dv_max, (int64_t)d * d);
+    L.lse_r = take(4 * n);
+    L.lse_c = take(4 * m);
+    L.r = take(4 * n);
+    L.c = take(4 * m);
+    L.PY = take(4 * n * d);
+    L.W = take(4 * n * (d + 2));
+    L.PtW = take(4 * m * (d + 2));
+    L.u = take(4 * n);
+    L.rhs = take(4 * m);
+    L.dg = take(4 * m);
+    L.res = take(4 * m);
+    L.pd = take(4 * m);
+    L.Ap = take(4 * m);
+    L.Pp = take(4 * n);
+    L.Ptq = take(4 * m);
+    L.V2 = take(4 * m * (d + 1));
+    L.T = take(4 * n * (d + 1));
+    L.M = take(4 * n * d);
+    L.V3 = take(4 * m * (size_t)L.ch);
+    L.T3 = take(4 * n * (size_t)L.ch);
+    L.dots = take(sizeof(double) * 4);
+    L.total = o;
+    return L;
+}
+
+// (x.y, sum x) on the host (one workgroup reduction, then a synchronous copy)
+fs_status host_dots(const float* x, const float* y, int64_t len, double* dev, double out[2],
+                    hipStream_t s) {
+    hipError_t e = launch_dot(x, y, len, dev, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(out, dev, 2 * sizeof(double), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? FS_OK : hip_fail(e, "HVP reduction");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fs_hvp_workspace_bytes(const fs_problem* p) { return p ? hvp_layout(p).total : 0; }
+
+fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const float* X,
+                 const float* Y, const float* V, float* HV, float cg_tol, int32_t cg_max_iter,
+                 void* workspace, size_t workspace_bytes, fs_hvp_info* info, void* stream) {
+    if (!p || !f || !g || !X || !Y || !V || !HV || !workspace)
+        return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (p->cost != FS_COST_SQEUCLIDEAN)
+        return fail(FS_ERR_INVALID_ARG, "the HVP supports the squared-Euclidean cost only");
+    if (p->dv_max < p->d + 2)
+        return fail(FS_ERR_INVALID_ARG, "the HVP needs dv_max >= d + 2 at init (dv_max=%d, d=%d)",
+                    p->dv_max, p->d);
+    if (!(cg_tol >= 0.f) || cg_max_iter < 0)
+        return fail(FS_ERR_INVALID_ARG, "cg_tol must be >= 0 and cg_max_iter >= 0");
+    const HvpLayout L = hvp_layout(p);
+    if (workspace_bytes < L.total)
+        return fail(FS_ERR_WORKSPACE, "HVP workspace too small: %zu < %zu bytes", workspace_bytes,
+                    L.total);
+    const size_t nd = (size_t)4 * p->n * p->d;
+    if (overlaps(HV, nd, V, nd) || overlaps(HV, nd, X, nd) ||
+        overlaps(HV, nd, workspace, workspace_bytes) ||
+        overlaps(HV, nd, Y, (size_t)4 * p->m * p->d))
+        return fail(FS_ERR_INVALID_ARG, "HV overlaps an input or the workspace");
+    hipStream_t s = (hipStream_t)stream;
+    char* w = (char*)workspace;
+    auto F = [&](size_t off) { return (float*)(w + off); };
+    double* dots = (double*)(w + L.dots);
+    const int64_t n = p->n, m = p->m;
+    const int d = p->d;
+    const float c_bias = (float)(1.4426950408889634 / (double)eps);
+    const float* mu = p->centre + d;  // centre of Y: every point is taken relative to it
+    fs_status st;
+    hipError_t e;
+#define FS_HIP(call, what)                     \
+    do {                                       \
+        if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
+    } while (0)
+    // exact row and column LSEs (reused by every transport below), marginals
+    if ((st = half_step(p, true, eps, g, F(L.lse_r), nullptr, nullptr, 1, s)) != FS_OK) return st;
+    if ((st = half_step(p, false, eps, f, F(L.lse_c), nullptr, nullptr, 1, s)) != FS_OK) return st;
+    FS_HIP(launch_marginal(F(L.lse_r), f, p->X.nrm, p->X.w, c_bias, n, F(L.r), s), "HVP marginal");
+    FS_HIP(launch_marginal(F(L.lse_c), g, p->Y.nrm, p->Y.w, c_bias, m, F(L.c), s), "HVP marginal");
+    // PY = P (Y - mu); u, W = [V | s | u/r]; PtW = P^T W; rhs = w - P^T (u/r)
+    if ((st = transport_side(p, true, eps, f, g, Y, d, F(L.PY), 0, mu, nullptr, s, F(L.lse_r))) !=
+        FS_OK)
+        return st;
+    FS_HIP(launch_hvp_rows(X, V, mu, F(L.PY), F(L.r), n, d, F(L.u), F(L.W), s), "HVP rows");
+    if ((st = transport_side(p, false, eps, f, g, F(L.W), d + 2, F(L.PtW), 0, nullptr, nullptr, s,
+                             F(L.lse_c))) != FS_OK)
+        return st;
+    FS_HIP(launch_hvp_cols(Y, mu, F(L.PtW), m, d, F(L.rhs), s), "HVP columns");
+    // CG for K dg = rhs on the complement of the constant vector,
+    // K = diag(c) - P^T diag(1/r) P.  Vectors are kept mean-free.
+    double h[2];
+    auto project = [&](float* v) -> fs_status {  // v -= mean(v)
+        hipError_t e2 = launch_dot(v, v, m, dots, s);
+        if (e2 == hipSuccess) e2 = launch_axpby(0.f, v, 1.f, v, m, dots + 1, 1.0 / (double)m, s);
+        return e2 == hipSuccess ? FS_OK : hip_fail(e2, "HVP projection");
+    };
+    if ((st = project(F(L.rhs))) != FS_OK) return st;
+    FS_HIP(launch_fill(F(L.dg), m, 0.f, s), "HVP fill");
+    FS_HIP(launch_axpby(1.f, F(L.rhs), 0.f, F(L.res), m, nullptr, 0.0, s), "HVP copy");
+    FS_HIP(launch_axpby(1.f, F(L.rhs), 0.f, F(L.pd), m, nullptr, 0.0, s), "HVP copy");
+    if ((st = host_dots(F(L.res), F(L.res), m, dots, h, s)) != FS_OK) return st;
+    const double rr0 = h[0];
+    double rr = rr0, rel = rr0 > 0.0 ? 1.0 : 0.0;
+    int it = 0;
+    while (rr0 > 0.0 && it < cg_max_iter && rel > (double)cg_tol) {
+        // Ap = c pd - P^T ((P pd) / r)
+        if ((st = transport_side(p, true, eps, f, g, F(L.pd), 1, F(L.Pp), 0, nullptr, nullptr, s,
+                                 F(L.lse_r))) != FS_OK)
+            return st;
+        FS_HIP(launch_scale_sub(F(L.r), F(L.Pp), nullptr, n, 1, F(L.Pp), s), "HVP scale");
+        if ((st = transport_side(p, false, eps, f, g, F(L.Pp), 1, F(L.Ptq), 0, nullptr, nullptr, s,
+                                 F(L.lse_c))) != FS_OK)
+            return st;
+        FS_HIP(launch_scale_sub(F(L.c), F(L.pd), F(L.Ptq), m, 0, F(L.Ap), s), "HVP scale");
+        if ((st = host_dots(F(L.pd), F(L.Ap), m, dots, h, s)) != FS_OK) return st;
+        if (!(h[0] > 0.0)) break;  // no descent left (rounding): stop at the current dg
+        const double alpha = rr / h[0];
+        FS_HIP(launch_axpby((float)alpha, F(L.pd), 1.f, F(L.dg), m, nullptr, 0.0, s), "HVP update");
+        FS_HIP(launch_axpby((float)-alpha, F(L.Ap), 1.f, F(L.res), m, nullptr, 0.0, s),
+               "HVP update");
+        if ((st = host_dots(F(L.res), F(L.res), m, dots, h, s)) != FS_OK) return st;
+        FS_HIP(launch_axpby(0.f, F(L.res), 1.f, F(L.res), m, dots + 1, 1.0 / (double)m, s),
+               "HVP projection");
+        const double rr_new = std::max(h[0] - h[1] * h[1] / (double)m, 0.0);
+        ++it;
+        rel = std::sqrt(rr_new / rr0);
+        if (rel <= (double)cg_tol) break;
+        FS_HIP(launch_axpby(1.f, F(L.res), (float)(rr_new / rr), F(L.pd), m, nullptr, 0.0, s),
+               "HVP update");
+        rr = rr_new;
+    }
+    // T = P [dg (Y - mu) | dg]
+    FS_HIP(launch_hvp_dgy(Y, mu, F(L.dg), m, d, F(L.V2), s), "HVP dg columns");
+    if ((st = transport_side(p, true, eps, f, g, F(L.V2), d + 1, F(L.T), 0, nullptr, nullptr, s,
+                             F(L.lse_r))) != FS_OK)
+        return st;
+    // M_i = sum_j P_ij ((y_j - mu).v_i) (y_j - mu), from the d*d outer-product
+    // columns in passes of L.ch
+    FS_HIP(launch_fill(F(L.M), n * d, 0.f, s), "HVP fill");
+    for (int64_t q0 = 0; q0 < (int64_t)d * d; q0 += L.ch) {
+        const int wq = (int)std::min<int64_t>(L.ch, (int64_t)d * d - q0);
+        FS_HIP(launch_hvp_outer(Y, mu, m, d, q0, wq, F(L.V3), s), "HVP outer products");
+        if ((st = transport_side(p, true, eps, f, g, F(L.V3), wq, F(L.T3), 0, nullptr, nullptr, s,
+                                 F(L.lse_r))) != FS_OK)
+            return st;
+        FS_HIP(launch_hvp_moment(F(L.T3), V, n, d, q0, wq, F(L.M), s), "HVP moment");
+    }
+    FS_HIP(launch_hvp_final(V, F(L.r), F(L.u), F(L.W), F(L.PY), F(L.T), F(L.M), n, d,
+                            (float)(1.0 / (double)eps), HV, s),
+           "HVP assembly");
+#undef FS_HIP
+    if (info) {
+        info->cg_iters = it;
+        info->cg_residual = (float)rel;
+    }
     return FS_OK;
 }
 

@@ -133,6 +133,27 @@ hipError_t launch_grad_finish(const float* P, const float* rscale, const float* 
                               const float* lse2, const float* pot, const float* nrm,
                               const float* w, float c_bias, int64_t n, int d, float* G,
                               hipStream_t s);
+// streaming Hessian-vector product (fs_hvp.hip)
+hipError_t launch_marginal(const float* lse2, const float* pot, const float* nrm, const float* w,
+                           float c_bias, int64_t n, float* out, hipStream_t s);
+hipError_t launch_hvp_rows(const float* X, const float* V, const float* mu, const float* PY,
+                           const float* r, int64_t n, int d, float* u, float* W, hipStream_t s);
+hipError_t launch_hvp_cols(const float* Y, const float* mu, const float* PtW, int64_t m, int d,
+                           float* rhs, hipStream_t s);
+hipError_t launch_dot(const float* x, const float* y, int64_t len, double* out, hipStream_t s);
+hipError_t launch_axpby(float alpha, const float* x, float beta, float* y, int64_t len,
+                        const double* shift, double shift_scale, hipStream_t s);
+hipError_t launch_scale_sub(const float* a, const float* x, const float* y, int64_t len,
+                            int divide, float* out, hipStream_t s);
+hipError_t launch_hvp_dgy(const float* Y, const float* mu, const float* dg, int64_t m, int d,
+                          float* V2, hipStream_t s);
+hipError_t launch_hvp_outer(const float* Y, const float* mu, int64_t m, int d, int64_t q0, int w,
+                            float* V3, hipStream_t s);
+hipError_t launch_hvp_moment(const float* T3, const float* V, int64_t n, int d, int64_t q0, int w,
+                             float* M, hipStream_t s);
+hipError_t launch_hvp_final(const float* V, const float* r, const float* u, const float* W,
+                            const float* PY, const float* T, const float* M, int64_t n, int d,
+                            float inv_eps, float* HV, hipStream_t s);
 hipError_t launch_dual_value(const float* a, const float* f, int64_t n, const float* b,
                              const float* g, int64_t m, double* out, hipStream_t s);
 
