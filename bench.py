@@ -212,6 +212,8 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(RECIPES))
     ap.add_argument("--iters", type=int, default=None, help="override iterations per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hvp", action="store_true",
+                    help="skip the Hessian-vector product measurement (d <= 64 recipes)")
     ap.add_argument("--counters", action="store_true",
                     help="run the hardware-counter workload instead of the benchmark")
     args = ap.parse_args()
@@ -222,6 +224,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from streaming_sinkhorn_solver_amd import binding, workloads
@@ -308,6 +311,35 @@ def main():
                             "LSE passes and two transport applications of width d)"}
         del gX, gY
 
+    hvp = None
+    if w.d <= 64 and not args.no_hvp:
+        # the streaming Hessian-vector product at the final potentials (its
+        # own problem handle: it needs dv_max >= d + 2 and runs the d*d
+        # second-moment columns in one pass when dv_max >= d*d); outside the
+        # timed steps, one untimed call first
+        hdv = max(w.d + 2, min(w.d * w.d, 4096))
+        hws = torch.empty(binding.fs_workspace_bytes(w.n, w.m, w.d, hdv, prec) + 256,
+                          dtype=torch.uint8, device=dev)
+        fh, gh = torch.empty_like(f), torch.empty_like(g)
+        ph = binding.fs_potentials_init(X, Y, a, b, dv_max=hdv, prec=prec, f=fh, g=gh,
+                                        workspace=hws)
+        fh.copy_(f)
+        gh.copy_(g)
+        Vd = torch.from_numpy(np.random.default_rng(7).standard_normal((w.n, w.d))
+                              .astype(np.float32)).to(dev)
+        HV = torch.empty_like(Vd)
+        scratch = torch.empty(binding.fs_hvp_workspace_bytes(ph), dtype=torch.uint8, device=dev)
+        binding.fs_hvp(ph, w.eps, fh, gh, X, Y, Vd, HV, workspace=scratch)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        hinfo = binding.fs_hvp(ph, w.eps, fh, gh, X, Y, Vd, HV, workspace=scratch)
+        torch.cuda.synchronize()
+        hvp = {"hvp_ms": round((time.perf_counter() - t1) * 1e3, 3), **hinfo,
+               "what": "fs_hvp at the final potentials, random direction, CG to 1e-4 "
+                       "(two LSE passes; transports of widths d, d+2, d+1, d*d and two of "
+                       "width 1 per CG iteration; host synchronised per CG step)"}
+        del hws, scratch, HV, Vd, ph
+
     ms_per_step = dt / args.steps * 1e3
     it_s = total_iters * args.steps / dt
     pair_evals = 2.0 * w.n * w.m * total_iters * args.steps
@@ -352,6 +384,8 @@ def main():
     }
     if backward:
         out["backward"] = backward
+    if hvp:
+        out["hvp"] = hvp
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
