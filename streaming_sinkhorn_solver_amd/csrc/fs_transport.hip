@@ -101,39 +101,86 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------ vector path
-// One row per thread, 32 output columns per thread (grid.y over dv chunks).
-template <int D>
+// d <= 8: R rows per thread and DVC output columns per thread (grid.y over
+// column blocks; DVC the smallest of 1, 2, 4, 8, 16, 32 that covers dv, or 32
+// with several blocks).  Tiles of KT keys -- their coordinates, the biased
+// score term and the block's V values -- are staged in LDS by the whole
+// workgroup and read back as broadcasts, so each key costs one LDS pass per
+// wave instead of a chain of scalar loads per thread.  Per pair: D FMAs,
+// one exponential, DVC FMAs.
+template <int D, int R, int DVC>
 __global__ __launch_bounds__(256) void transport_valu_kernel(TransportArgs a) {
     constexpr int DP = D <= 4 ? 4 : 8;
-    constexpr int DVC = 32;
+    constexpr int KT = 64;
+    constexpr int KW = D + 1;  // coordinates, then the bias
+    __shared__ float kx[KT * KW];
+    __shared__ float kv[KT * DVC];
     const float* __restrict__ rows = (const float*)a.rows;
     const float* __restrict__ keys = (const float*)a.keys;
-    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int t = threadIdx.x;
+    const int64_t row_base = (int64_t)blockIdx.x * 256 * R;
     const int c0 = blockIdx.y * DVC;
-    const bool live = i < a.n_rows;
-    float x[D];
+    float x[R][D], L[R], u[R][DVC];
 #pragma unroll
-    for (int k = 0; k < D; ++k) x[k] = live ? rows[(int64_t)i * DP + k] * a.c_score : 0.f;
-    const float L = live ? a.row_lse2[i] : 0.f;
-    float u[DVC];
+    for (int r = 0; r < R; ++r) {
+        const int64_t i = row_base + r * 256 + t;
+        const bool live = i < a.n_rows;
 #pragma unroll
-    for (int c = 0; c < DVC; ++c) u[c] = 0.f;
-    for (int j = 0; j < a.n_keys; ++j) {
-        float z = fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]);
+        for (int k = 0; k < D; ++k) x[r][k] = live ? rows[i * DP + k] * a.c_score : 0.f;
+        L[r] = live ? a.row_lse2[i] : INFINITY;  // rows past n: every weight 0
 #pragma unroll
-        for (int k = 0; k < D; ++k) z = fmaf(x[k], keys[(int64_t)j * DP + k], z);
-        const float p = ex2(z - L);
+        for (int c = 0; c < DVC; ++c) u[r][c] = 0.f;
+    }
+    for (int j0 = 0; j0 < a.n_keys; j0 += KT) {
+        __syncthreads();  // the previous tile is consumed
+        for (int e = t; e < KT * KW; e += 256) {
+            const int jj = e / KW, k = e - jj * KW;
+            const int j = j0 + jj;
+            float v;
+            if (k < D)
+                v = j < a.n_keys ? keys[(int64_t)j * DP + k] : 0.f;
+            else
+                v = j < a.n_keys ? fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j])
+                                 : -INFINITY;
+            kx[e] = v;
+        }
+        for (int e = t; e < KT * DVC; e += 256) {
+            const int jj = e / DVC, c = e - jj * DVC;
+            const int j = j0 + jj;
+            kv[e] = (j < a.n_keys && c0 + c < a.dv)
+                        ? v_value(a.V, j, a.dv, c0 + c, a.v_rscale, a.v_off)
+                        : 0.f;
+        }
+        __syncthreads();
+        const int kn = min(KT, a.n_keys - j0);
+        for (int jj = 0; jj < kn; ++jj) {
+            float ky[KW], vv[DVC];
+#pragma unroll
+            for (int k = 0; k < KW; ++k) ky[k] = kx[jj * KW + k];
+#pragma unroll
+            for (int c = 0; c < DVC; ++c) vv[c] = kv[jj * DVC + c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float z = ky[D];
+#pragma unroll
+                for (int k = 0; k < D; ++k) z = fmaf(x[r][k], ky[k], z);
+                const float p = ex2(z - L[r]);
+#pragma unroll
+                for (int c = 0; c < DVC; ++c) u[r][c] = fmaf(p, vv[c], u[r][c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t i = row_base + r * 256 + t;
+        if (i >= a.n_rows) continue;
+        float sc = ex2(L[r] + (a.row_pot[i] - a.row_nrm[i]) * a.c_bias);
+        if (!a.divide_by_a) sc *= a.row_w[i];
+        float* ur = a.U + i * a.dv + c0;
 #pragma unroll
         for (int c = 0; c < DVC; ++c)
-            if (c0 + c < a.dv) u[c] = fmaf(p, v_value(a.V, j, a.dv, c0 + c, a.v_rscale, a.v_off), u[c]);
+            if (c0 + c < a.dv) ur[c] = u[r][c] * sc;
     }
-    if (!live) return;
-    float sc = ex2(L + (a.row_pot[i] - a.row_nrm[i]) * a.c_bias);
-    if (!a.divide_by_a) sc *= a.row_w[i];
-    float* ur = a.U + (int64_t)i * a.dv + c0;
-#pragma unroll
-    for (int c = 0; c < DVC; ++c)
-        if (c0 + c < a.dv) ur[c] = u[c] * sc;
 }
 
 // ------------------------------------------------------ matrix-core path
@@ -1036,11 +1083,30 @@ __global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a) {
     a.U[idx] = acc * sc;
 }
 
+template <int D, int DVC>
+hipError_t transport_valu_launch_c(const TransportArgs& a, hipStream_t s) {
+    // rows per thread: as many as the output registers allow, fewer when
+    // that would leave the GPU short of workgroups
+    constexpr int RMAX = DVC <= 8 ? 4 : (DVC == 16 ? 2 : 1);
+    const int n_cb = (a.dv + DVC - 1) / DVC;
+    if (RMAX > 1 && (int64_t)((a.n_rows + 256 * RMAX - 1) / (256 * RMAX)) * n_cb >= 1024) {
+        const dim3 grid((a.n_rows + 256 * RMAX - 1) / (256 * RMAX), n_cb);
+        transport_valu_kernel<D, RMAX, DVC><<<grid, 256, 0, s>>>(a);
+    } else {
+        const dim3 grid((a.n_rows + 255) / 256, n_cb);
+        transport_valu_kernel<D, 1, DVC><<<grid, 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t transport_valu_launch(const TransportArgs& a, hipStream_t s) {
-    const dim3 grid((a.n_rows + 255) / 256, (a.dv + 31) / 32);
-    transport_valu_kernel<D><<<grid, 256, 0, s>>>(a);
-    return hipGetLastError();
+    if (a.dv <= 1) return transport_valu_launch_c<D, 1>(a, s);
+    if (a.dv <= 2) return transport_valu_launch_c<D, 2>(a, s);
+    if (a.dv <= 4) return transport_valu_launch_c<D, 4>(a, s);
+    if (a.dv <= 8) return transport_valu_launch_c<D, 8>(a, s);
+    if (a.dv <= 16) return transport_valu_launch_c<D, 16>(a, s);
+    return transport_valu_launch_c<D, 32>(a, s);
 }
 
 template <int OP, int NG>

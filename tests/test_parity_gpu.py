@@ -285,6 +285,33 @@ def test_transport(fs, prec, d, dv):
         assert rel <= 1e-3, rel
 
 
+# The d <= 8 transport: every column-block width (dv = 1, 2, 4, 5, 16 and
+# 33, i.e. 1 to 32 columns per thread and two blocks), one and several rows
+# per thread (the larger row count fills enough workgroups for the latter),
+# and a key count that leaves a ragged tile of the LDS-staged key loop.
+@pytest.mark.parametrize("prec,d,dv,n", [("auto", 3, 1, 700), ("fp32-valu", 8, 2, 700),
+                                         ("auto", 5, 4, 1100), ("auto", 3, 5, 1_050_000),
+                                         ("fp32-valu", 3, 16, 700), ("auto", 7, 33, 700)])
+def test_transport_small_d(fs, prec, d, dv, n):
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    m = 850
+    X, Y, a, b = _problem(950 + d + dv, n, m, d, scale=1.0 / np.sqrt(d))
+    V = np.random.default_rng(dv).standard_normal((m, dv)).astype(np.float32)
+    eps = 0.1
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=4, prec=prec, dv_max=dv)
+    U = torch.empty((n, dv), dtype=torch.float32, device="cuda")
+    binding.fs_apply_transport(p, eps, f, g, dev(V), U)
+    torch.cuda.synchronize()
+    rows = None if n <= 2000 else np.sort(np.concatenate(
+        [np.random.default_rng(1).choice(n, 200, replace=False), [0, 1023, 1024, n - 1]]))
+    ref = oracle.transport(X, Y, a, b, host(f), host(g), V, eps, rows=rows)
+    got = host(U) if rows is None else host(U)[rows]
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-3, rel
+
+
 # The 1024-D streaming transport: every output-block width (dv = 40, 100,
 # 200, 300 and 1024 use 1, 2, 4, 8 and 16 blocks of 32 columns per wave),
 # two column blocks (dv = 1100), key counts that leave a ragged 16-key tile,
