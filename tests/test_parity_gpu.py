@@ -135,6 +135,37 @@ def test_lowp_mfma_path(fs, prec, d, n, m):
     assert max_err(host(g), ref["g"]) <= TOL_LOWP * eps
 
 
+@pytest.mark.parametrize("prec,d", [("fp16", 1024), ("bf16", 512), ("auto", 64)])
+@pytest.mark.parametrize("n,m", [(1, 1), (1, 70), (70, 1), (33, 17)])
+def test_matrix_paths_tiny_sides(fs, prec, d, n, m):
+    # Single points and sides shorter than one tile on the matrix-core
+    # kernels (the 1024-wide ones included): the solve and the transport.
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    w = workloads.make("c4", n=n, m=m, d=d)
+    eps = 0.05
+    dv = 40
+    p, f, g, _, _ = gpu_solve(w.X, w.Y, w.a, w.b, eps=eps, iters=4, prec=prec, dv_max=dv)
+    V = np.random.default_rng(n + m).standard_normal((m, dv)).astype(np.float32)
+    U = torch.empty((n, dv), device="cuda")
+    binding.fs_apply_transport(p, eps, f, g, dev(V), U)
+    torch.cuda.synchronize()
+    fh, gh = host(f), host(g)
+    assert np.all(np.isfinite(fh)) and np.all(np.isfinite(gh))
+    if prec in ("bf16", "fp16"):
+        rp = RoundedProblem(w.X, w.Y, prec)
+        ref = rp.solve(w.a, w.b, eps=eps, iters=4)
+        U_ref = rp.transport(w.a, w.b, fh, gh, V, eps)
+        tol = TOL_LOWP_ROUNDED
+    else:
+        ref = oracle_solve(w.X, w.Y, w.a, w.b, eps=eps, iters=4)
+        U_ref = oracle.transport(w.X, w.Y, w.a, w.b, fh, gh, V, eps)
+        tol = TOL_FP32
+    assert max_err(fh, ref["f"]) <= tol * eps and max_err(gh, ref["g"]) <= tol * eps
+    assert np.linalg.norm(host(U) - U_ref) <= 1e-3 * np.linalg.norm(U_ref)
+
+
 def test_split_path_is_exercised(fs):
     # Sizes for which the launch heuristic splits the key range.
     X, Y, a, b = _problem(400, 4000, 3000, 64, scale=0.125)
