@@ -13,18 +13,22 @@
 //    (row-stationary traversal).
 // The g-update is the same pass with the clouds' roles exchanged.
 //
-// Two kernel families:
-//  * lse_valu_kernel<D, R>: d <= 8.  Each lane owns R rows; keys are
-//    wave-uniform (scalar loads), scores are D fp32 FMAs per pair.  The bound
-//    is the vector ALU / transcendental issue rate (one exp2 per pair).
-//  * lse_mfma_kernel<OP, NG, QB>: d > 8.  The transposed score tile
+// Kernel families (the default d <= 8 path, lse_small_kernel, is in
+// fs_lse_small.hip):
+//  * lse_valu_kernel<D, R>: d <= 8, fp32 vector path.  Each lane owns R rows;
+//    keys are wave-uniform (scalar loads), scores are D fp32 FMAs per pair.
+//    The bound is the vector ALU / transcendental issue rate (one exp2 per
+//    pair).
+//  * lse_mfma_kernel<OP, NG, QB, WAVES>: d > 8.  The transposed score tile
 //    S^T = K~ Q~^T is formed on the gfx950 matrix cores
 //    (v_mfma_f32_32x32x{16_bf16,16_f16,2f32}), so every lane holds 16 scores of
 //    ONE row and the row reduction stays inside the lane.  The row block
-//    (4 waves x 32*QB rows x dp) lives in registers; 32-key tiles are
-//    double-buffered through LDS in an XOR-swizzled layout.  The bound is the
+//    (WAVES x 32*QB rows x dp) lives in registers; 32-key tiles stream
+//    through LDS slots in an XOR-swizzled layout.  The bound is the
 //    matrix-core rate (2 n m d flops per half-step).
-// Both can split the key range across workgroups (partial (max, sum) pairs
+//  * lse_wide_kernel<OP>: two-byte scores at dp = 1024, the contraction split
+//    over the two waves of each SIMD (see its comment).
+// All can split the key range across workgroups (partial (max, sum) pairs
 // merged afterwards in a fixed order), so results are deterministic.
 #include <type_traits>
 

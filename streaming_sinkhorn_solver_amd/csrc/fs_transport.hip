@@ -20,6 +20,11 @@
 // f16 copy of V (keys on the contraction axis, in the same slot order), so
 // the weights never leave registers.  V is copied once, transposed and scaled
 // by a power of two into the f16 range; the scale is undone exactly at the end.
+// Kernels: transport_stream_kernel (d_pad <= 512; 256 output columns per
+// workgroup), transport_wide_kernel (two-byte scores at d_pad = 1024; the
+// contraction and the output columns split over wave pairs),
+// transport_mfma_kernel (the remaining matrix case, fp32 at d_pad = 512) and
+// transport_valu_kernel (d <= 8, fp32 vector arithmetic).
 #include <algorithm>
 
 #include "fs_device.hpp"
