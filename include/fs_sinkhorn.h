@@ -233,7 +233,8 @@ fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* o
  * (df, dg) keep both marginals of P fixed:
  *   HV_i = 2 r_i v_i + 2 sum_j dP_ij (x_i - y_j).
  * dg solves K dg = w - P^T (u/r), K = diag(c) - P^T diag(1/r) P, by conjugate
- * gradients on the complement of the constant vector (K's null space) until
+ * gradients preconditioned by diag(c), on the complement of the constant
+ * vector (K's null space), until
  * the residual falls to cg_tol of its start or cg_max_iter iterations; each
  * iteration is one row and one column transport of width 1.  Besides that:
  * two exact LSE passes, transports of widths d, d+2, d+1, and the d*d

@@ -769,11 +769,12 @@ HvpLayout hvp_layout(const fs_problem* p) {
     return L;
 }
 
-// (x.y, sum x) on the host (one workgroup reduction, then a synchronous copy)
-fs_status host_dots(const float* x, const float* y, int64_t len, double* dev, double out[2],
+// (x.y, sum x, x.x) on the host (one workgroup reduction, then a synchronous
+// copy)
+fs_status host_dots(const float* x, const float* y, int64_t len, double* dev, double out[3],
                     hipStream_t s) {
     hipError_t e = launch_dot(x, y, len, dev, s);
-    if (e == hipSuccess) e = hipMemcpyAsync(out, dev, 2 * sizeof(double), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(out, dev, 3 * sizeof(double), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return e == hipSuccess ? FS_OK : hip_fail(e, "HVP reduction");
 }
@@ -834,21 +835,21 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
                              F(L.lse_c))) != FS_OK)
         return st;
     FS_HIP(launch_hvp_cols(Y, mu, F(L.PtW), m, d, F(L.rhs), s), "HVP columns");
-    // CG for K dg = rhs on the complement of the constant vector,
-    // K = diag(c) - P^T diag(1/r) P.  Vectors are kept mean-free.
-    double h[2];
-    auto project = [&](float* v) -> fs_status {  // v -= mean(v)
-        hipError_t e2 = launch_dot(v, v, m, dots, s);
-        if (e2 == hipSuccess) e2 = launch_axpby(0.f, v, 1.f, v, m, dots + 1, 1.0 / (double)m, s);
-        return e2 == hipSuccess ? FS_OK : hip_fail(e2, "HVP projection");
-    };
-    if ((st = project(F(L.rhs))) != FS_OK) return st;
+    // Preconditioned CG (M = diag(c), the diagonal of K's first term) for
+    // K dg = rhs on the complement of the constant vector,
+    // K = diag(c) - P^T diag(1/r) P.  The residual is kept mean-free (K's
+    // range); dg's own constant does not change dP.  Stops when the plain
+    // residual norm falls to cg_tol of its start.
+    double h[3];
+    if ((st = host_dots(F(L.rhs), F(L.rhs), m, dots, h, s)) != FS_OK) return st;
+    FS_HIP(launch_axpby(0.f, F(L.rhs), 1.f, F(L.rhs), m, dots + 1, 1.0 / (double)m, s),
+           "HVP projection");
+    const double rr0 = std::max(h[2] - h[1] * h[1] / (double)m, 0.0);
     FS_HIP(launch_fill(F(L.dg), m, 0.f, s), "HVP fill");
     FS_HIP(launch_axpby(1.f, F(L.rhs), 0.f, F(L.res), m, nullptr, 0.0, s), "HVP copy");
-    FS_HIP(launch_axpby(1.f, F(L.rhs), 0.f, F(L.pd), m, nullptr, 0.0, s), "HVP copy");
-    if ((st = host_dots(F(L.res), F(L.res), m, dots, h, s)) != FS_OK) return st;
-    const double rr0 = h[0];
-    double rr = rr0, rel = rr0 > 0.0 ? 1.0 : 0.0;
+    FS_HIP(launch_scale_sub(F(L.c), F(L.res), nullptr, m, 1, F(L.pd), s), "HVP precondition");
+    if ((st = host_dots(F(L.res), F(L.pd), m, dots, h, s)) != FS_OK) return st;
+    double rz = h[0], rel = rr0 > 0.0 ? 1.0 : 0.0;
     int it = 0;
     while (rr0 > 0.0 && it < cg_max_iter && rel > (double)cg_tol) {
         // Ap = c pd - P^T ((P pd) / r)
@@ -862,20 +863,24 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
         FS_HIP(launch_scale_sub(F(L.c), F(L.pd), F(L.Ptq), m, 0, F(L.Ap), s), "HVP scale");
         if ((st = host_dots(F(L.pd), F(L.Ap), m, dots, h, s)) != FS_OK) return st;
         if (!(h[0] > 0.0)) break;  // no descent left (rounding): stop at the current dg
-        const double alpha = rr / h[0];
+        const double alpha = rz / h[0];
         FS_HIP(launch_axpby((float)alpha, F(L.pd), 1.f, F(L.dg), m, nullptr, 0.0, s), "HVP update");
         FS_HIP(launch_axpby((float)-alpha, F(L.Ap), 1.f, F(L.res), m, nullptr, 0.0, s),
                "HVP update");
+        // res <- res - mean(res); z = res / c (into Ap, free now); r.z and |res|^2
         if ((st = host_dots(F(L.res), F(L.res), m, dots, h, s)) != FS_OK) return st;
         FS_HIP(launch_axpby(0.f, F(L.res), 1.f, F(L.res), m, dots + 1, 1.0 / (double)m, s),
                "HVP projection");
-        const double rr_new = std::max(h[0] - h[1] * h[1] / (double)m, 0.0);
+        const double rr_new = std::max(h[2] - h[1] * h[1] / (double)m, 0.0);
         ++it;
         rel = std::sqrt(rr_new / rr0);
         if (rel <= (double)cg_tol) break;
-        FS_HIP(launch_axpby(1.f, F(L.res), (float)(rr_new / rr), F(L.pd), m, nullptr, 0.0, s),
+        FS_HIP(launch_scale_sub(F(L.c), F(L.res), nullptr, m, 1, F(L.Ap), s), "HVP precondition");
+        if ((st = host_dots(F(L.res), F(L.Ap), m, dots, h, s)) != FS_OK) return st;
+        const double rz_new = h[0];
+        FS_HIP(launch_axpby(1.f, F(L.Ap), (float)(rz_new / rz), F(L.pd), m, nullptr, 0.0, s),
                "HVP update");
-        rr = rr_new;
+        rz = rz_new;
     }
     // T = P [dg (Y - mu) | dg]
     FS_HIP(launch_hvp_dgy(Y, mu, F(L.dg), m, d, F(L.V2), s), "HVP dg columns");

@@ -9,8 +9,9 @@
 //   dC_ij = 2 (x_i - y_j).v_i,   dP_ij = P_ij (df_i + dg_j - dC_ij) / eps,
 //   r_i df_i + (P dg)_i = u_i := sum_j P_ij dC_ij,
 //   (P^T df)_j + c_j dg_j = w_j := sum_i P_ij dC_ij,
-// solved for dg on the Schur complement K = diag(c) - P^T diag(1/r) P (CG on
-// the complement of the constant vector, K's null space), df = (u - P dg)/r.
+// solved for dg on the Schur complement K = diag(c) - P^T diag(1/r) P (CG
+// preconditioned by diag(c), on the complement of the constant vector, K's
+// null space), df = (u - P dg)/r.
 // With all points centred on the same vector mu (x~, y~) and s_i = x~_i.v_i,
 // PY_i = sum_j P_ij y~_j, M_i = sum_j P_ij (y~_j.v_i) y~_j:
 //   u_i = 2 (r_i s_i - PY_i.v_i),   w_j = 2 ((P^T s)_j - y~_j.(P^T V)_j),
@@ -81,29 +82,35 @@ __global__ __launch_bounds__(256) void hvp_cols_kernel(const float* __restrict__
         rhs[j] = 2.f * (PtW[j * (d + 2) + d] - t) - PtW[j * (d + 2) + d + 1];
 }
 
-// out[0] = sum_k x_k y_k, out[1] = sum_k x_k (one workgroup, fixed order, fp64)
+// out[0] = sum_k x_k y_k, out[1] = sum_k x_k, out[2] = sum_k x_k^2 (one
+// workgroup, fixed order, fp64)
 __global__ __launch_bounds__(1024) void dot_kernel(const float* __restrict__ x,
                                                    const float* __restrict__ y, int64_t len,
                                                    double* __restrict__ out) {
-    __shared__ double red[2][1024];
-    double s = 0.0, t = 0.0;
+    __shared__ double red[3][1024];
+    double s = 0.0, t = 0.0, q = 0.0;
     for (int64_t k = threadIdx.x; k < len; k += 1024) {
-        s += (double)x[k] * (double)y[k];
-        t += (double)x[k];
+        const double xv = (double)x[k];
+        s += xv * (double)y[k];
+        t += xv;
+        q += xv * xv;
     }
     red[0][threadIdx.x] = s;
     red[1][threadIdx.x] = t;
+    red[2][threadIdx.x] = q;
     __syncthreads();
     for (int o = 512; o >= 1; o >>= 1) {
         if ((int)threadIdx.x < o) {
             red[0][threadIdx.x] += red[0][threadIdx.x + o];
             red[1][threadIdx.x] += red[1][threadIdx.x + o];
+            red[2][threadIdx.x] += red[2][threadIdx.x + o];
         }
         __syncthreads();
     }
     if (threadIdx.x == 0) {
         out[0] = red[0][0];
         out[1] = red[1][0];
+        out[2] = red[2][0];
     }
 }
 
