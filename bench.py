@@ -312,12 +312,14 @@ def main():
         del gX, gY
 
     hvp = None
-    if w.d <= 64 and not args.no_hvp:
+    fused_moment = prec in ("bf16", "fp16") and 64 <= w.d <= 512
+    if (w.d <= 64 or fused_moment) and not args.no_hvp:
         # the streaming Hessian-vector product at the final potentials (its
-        # own problem handle: it needs dv_max >= d + 2 and runs the d*d
-        # second-moment columns in one pass when dv_max >= d*d); outside the
-        # timed steps, one untimed call first
-        hdv = max(w.d + 2, min(w.d * w.d, 4096))
+        # own problem handle: it needs dv_max >= d + 2; without the one-pass
+        # second-moment kernel it runs the d*d moment columns in passes of
+        # dv_max, one pass when dv_max >= d*d); outside the timed steps, one
+        # untimed call first
+        hdv = w.d + 2 if fused_moment else max(w.d + 2, min(w.d * w.d, 4096))
         hws = torch.empty(binding.fs_workspace_bytes(w.n, w.m, w.d, hdv, prec) + 256,
                           dtype=torch.uint8, device=dev)
         fh, gh = torch.empty_like(f), torch.empty_like(g)
@@ -336,8 +338,10 @@ def main():
         torch.cuda.synchronize()
         hvp = {"hvp_ms": round((time.perf_counter() - t1) * 1e3, 3), **hinfo,
                "what": "fs_hvp at the final potentials, random direction, CG to 1e-4 "
-                       "(two LSE passes; transports of widths d, d+2, d+1, d*d and two of "
-                       "width 1 per CG iteration; host synchronised per CG step)"}
+                       "(two LSE passes; transports of widths d, d+2, d+1, two of width 1 "
+                       "per CG step, and the second moment: one pass with the direction "
+                       "rows as a second resident block"
+                       + (")" if fused_moment else " replaced by d*d columns in passes)")}
         del hws, scratch, HV, Vd, ph
 
     ms_per_step = dt / args.steps * 1e3

@@ -237,9 +237,12 @@ fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* o
  * vector (K's null space), until
  * the residual falls to cg_tol of its start or cg_max_iter iterations; each
  * iteration is one row and one column transport of width 1.  Besides that:
- * two exact LSE passes, transports of widths d, d+2, d+1, and the d*d
- * second-moment columns in passes of at most dv_max (so the problem needs
- * dv_max >= d + 2, else FS_ERR_INVALID_ARG).  At converged potentials r = a,
+ * two exact LSE passes, transports of widths d, d+2, d+1, and the second
+ * moment sum_j P_ij ((y_j - c).v_i) (y_j - c): one pass of width d on the
+ * bf16/fp16 paths with d_pad 64..512 (the direction rows ride along as a
+ * second resident block, rounded to the score type after a per-row power-of-
+ * two scaling), else the d*d product columns in passes of at most dv_max
+ * (so the problem needs dv_max >= d + 2, else FS_ERR_INVALID_ARG).  At converged potentials r = a,
  * c = b and this is the Hessian of the loss; at other potentials it is that
  * of the plan (f, g) define.
  * X (n x d), Y (m x d): the fp32 points given to fs_potentials_init; V, HV:

@@ -344,7 +344,7 @@ bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.f; }
 fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, const float* g,
                          const float* V, int32_t dv, float* U, int32_t divide_by_w,
                          const float* voff, const float* vrs, hipStream_t s,
-                         const float* lse2 = nullptr) {
+                         const float* lse2 = nullptr, const void* rows2 = nullptr) {
     if (!p || !f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL argument");
     if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (dv < 1 || dv > p->dv_max)
@@ -384,6 +384,7 @@ fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, 
     t.c_score = (float)(2.8853900817779268 / (double)eps);
     t.divide_by_a = divide_by_w ? 1 : 0;
     t.U = U;
+    t.rows2 = rows2;
     hipError_t e = launch_transport(p->path, t, p->scal + 2, p->vt, K.n_pad, p->kbias, p->upart, s);
     if (e != hipSuccess) return hip_fail(e, "transport launch");
     return FS_OK;
@@ -730,9 +731,17 @@ namespace {
 // array 256-byte aligned; CH = second-moment columns per transport pass).
 struct HvpLayout {
     size_t lse_r, lse_c, r, c, PY, W, PtW, u, rhs, dg, res, pd, Ap, Pp, Ptq, V2, T, M, V3, T3, dots,
-        total;
+        vops, vsig, total;
     int ch;
+    bool fused;  // second moment by the one-pass kernel (else d*d columns in passes)
 };
+
+// The one-pass second-moment kernel serves two-byte scores at d_pad 64..512.
+bool hvp_fused(const fs_problem* p) {
+    return (p->path == PATH_MFMA_BF16 || p->path == PATH_MFMA_F16) && p->lse_dp >= 64 &&
+           p->lse_dp <= 512 && p->d <= 512 &&
+           (int64_t)p->d * p->Y.n_pad * 2 < ((int64_t)1 << 32);
+}
 
 HvpLayout hvp_layout(const fs_problem* p) {
     HvpLayout L{};
@@ -743,7 +752,8 @@ HvpLayout hvp_layout(const fs_problem* p) {
         return at;
     };
     const size_t n = (size_t)p->n, m = (size_t)p->m, d = (size_t)p->d;
-    L.ch = (int)std::min<int64_t>((int64_t)p->dv_max, (int64_t)d * d);
+    L.fused = hvp_fused(p);
+    L.ch = L.fused ? 0 : (int)std::min<int64_t>((int64_t)p->dv_max, (int64_t)d * d);
     L.lse_r = take(4 * n);
     L.lse_c = take(4 * m);
     L.r = take(4 * n);
@@ -765,6 +775,8 @@ HvpLayout hvp_layout(const fs_problem* p) {
     L.V3 = take(4 * m * (size_t)L.ch);
     L.T3 = take(4 * n * (size_t)L.ch);
     L.dots = take(sizeof(double) * 4);
+    L.vops = take(L.fused ? (size_t)2 * (size_t)p->X.n_pad * (size_t)p->lse_dp : 0);
+    L.vsig = take(L.fused ? 4 * n : 0);
     L.total = o;
     return L;
 }
@@ -887,19 +899,29 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
     if ((st = transport_side(p, true, eps, f, g, F(L.V2), d + 1, F(L.T), 0, nullptr, nullptr, s,
                              F(L.lse_r))) != FS_OK)
         return st;
-    // M_i = sum_j P_ij ((y_j - mu).v_i) (y_j - mu), from the d*d outer-product
-    // columns in passes of L.ch
-    FS_HIP(launch_fill(F(L.M), n * d, 0.f, s), "HVP fill");
-    for (int64_t q0 = 0; q0 < (int64_t)d * d; q0 += L.ch) {
-        const int wq = (int)std::min<int64_t>(L.ch, (int64_t)d * d - q0);
-        FS_HIP(launch_hvp_outer(Y, mu, m, d, q0, wq, F(L.V3), s), "HVP outer products");
-        if ((st = transport_side(p, true, eps, f, g, F(L.V3), wq, F(L.T3), 0, nullptr, nullptr, s,
-                                 F(L.lse_r))) != FS_OK)
+    // M_i = sum_j P_ij ((y_j - mu).v_i) (y_j - mu)
+    if (L.fused) {
+        // one pass: the direction rows (scaled per row into the score type)
+        // as a second resident block, weights P_ij (v_i sigma_i).y~_j
+        FS_HIP(launch_hvp_vconv(p->path, V, n, p->X.n_pad, d, p->lse_dp, w + L.vops, F(L.vsig), s),
+               "HVP direction rows");
+        if ((st = transport_side(p, true, eps, f, g, Y, d, F(L.M), 0, mu, nullptr, s, F(L.lse_r),
+                                 w + L.vops)) != FS_OK)
             return st;
-        FS_HIP(launch_hvp_moment(F(L.T3), V, n, d, q0, wq, F(L.M), s), "HVP moment");
+    } else {
+        // from the d*d outer-product columns in passes of L.ch
+        FS_HIP(launch_fill(F(L.M), n * d, 0.f, s), "HVP fill");
+        for (int64_t q0 = 0; q0 < (int64_t)d * d; q0 += L.ch) {
+            const int wq = (int)std::min<int64_t>(L.ch, (int64_t)d * d - q0);
+            FS_HIP(launch_hvp_outer(Y, mu, m, d, q0, wq, F(L.V3), s), "HVP outer products");
+            if ((st = transport_side(p, true, eps, f, g, F(L.V3), wq, F(L.T3), 0, nullptr, nullptr,
+                                     s, F(L.lse_r))) != FS_OK)
+                return st;
+            FS_HIP(launch_hvp_moment(F(L.T3), V, n, d, q0, wq, F(L.M), s), "HVP moment");
+        }
     }
-    FS_HIP(launch_hvp_final(V, F(L.r), F(L.u), F(L.W), F(L.PY), F(L.T), F(L.M), n, d,
-                            (float)(1.0 / (double)eps), HV, s),
+    FS_HIP(launch_hvp_final(V, F(L.r), F(L.u), F(L.W), F(L.PY), F(L.T), F(L.M),
+                            L.fused ? F(L.vsig) : nullptr, n, d, (float)(1.0 / (double)eps), HV, s),
            "HVP assembly");
 #undef FS_HIP
     if (info) {

@@ -185,6 +185,31 @@ __global__ __launch_bounds__(256) void hvp_moment_kernel(const float* __restrict
     M[k] = acc;
 }
 
+// Direction rows in the score type for the second-moment kernel: row i of
+// [n_pad][dp] is v_i sigma_i (zero-padded to dp; zero rows past n), sigma_i
+// the power of two that brings max_k |v_ik| into [0.5, 1); inv_sigma_i = 1 /
+// sigma_i undoes it exactly.  One wave per row.
+template <class T>
+__global__ __launch_bounds__(256) void hvp_vconv_kernel(const float* __restrict__ V, int64_t n,
+                                                        int64_t n_pad, int d, int dp,
+                                                        T* __restrict__ out,
+                                                        float* __restrict__ inv_sigma) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= n_pad) return;
+    float amax = 0.f;
+    if (i < n)
+        for (int k = lane; k < d; k += 64) amax = fmaxf(amax, fabsf(V[i * d + k]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    int e = 0;
+    if (amax > 0.f) frexpf(amax, &e);  // amax in [2^(e-1), 2^e)
+    const float sigma = ldexpf(1.f, -e);
+    for (int k = lane; k < dp; k += 64)
+        out[i * dp + k] = (T)(i < n && k < d ? V[i * d + k] * sigma : 0.f);
+    if (lane == 0 && i < n) inv_sigma[i] = ldexpf(1.f, e);
+}
+
 // df_i = (u_i - T_i[d]) / r_i;
 // HV_i = 2 r_i v_i - (2/eps) (df_i PY_i + T_i[0:d] - 2 s_i PY_i + 2 M_i),
 // s_i = W_i[d].
@@ -194,8 +219,9 @@ __global__ __launch_bounds__(256) void hvp_final_kernel(const float* __restrict_
                                                         const float* __restrict__ W,
                                                         const float* __restrict__ PY,
                                                         const float* __restrict__ T,
-                                                        const float* __restrict__ M, int64_t n,
-                                                        int d, float inv_eps,
+                                                        const float* __restrict__ M,
+                                                        const float* __restrict__ m_scale,
+                                                        int64_t n, int d, float inv_eps,
                                                         float* __restrict__ HV) {
     const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (k >= n * d) return;
@@ -205,7 +231,8 @@ __global__ __launch_bounds__(256) void hvp_final_kernel(const float* __restrict_
     const float df = ri > 0.f ? (u[i] - T[i * (d + 1) + d]) / ri : 0.f;
     const float s = W[i * (d + 2) + d];
     const float py = PY[k];
-    const float br = fmaf(df, py, T[i * (d + 1) + c]) + 2.f * fmaf(-s, py, M[k]);
+    const float mk = m_scale ? M[k] * m_scale[i] : M[k];
+    const float br = fmaf(df, py, T[i * (d + 1) + c]) + 2.f * fmaf(-s, py, mk);
     HV[k] = 2.f * fmaf(ri, V[k], -inv_eps * br);
 }
 
@@ -275,11 +302,26 @@ hipError_t launch_hvp_moment(const float* T3, const float* V, int64_t n, int d, 
 }
 
 hipError_t launch_hvp_final(const float* V, const float* r, const float* u, const float* W,
-                            const float* PY, const float* T, const float* M, int64_t n, int d,
-                            float inv_eps, float* HV, hipStream_t s) {
+                            const float* PY, const float* T, const float* M,
+                            const float* m_scale, int64_t n, int d, float inv_eps, float* HV,
+                            hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    hvp_final_kernel<<<blocks_for(n * d, 256), 256, 0, s>>>(V, r, u, W, PY, T, M, n, d, inv_eps,
-                                                           HV);
+    hvp_final_kernel<<<blocks_for(n * d, 256), 256, 0, s>>>(V, r, u, W, PY, T, M, m_scale, n, d,
+                                                           inv_eps, HV);
+    return hipGetLastError();
+}
+
+hipError_t launch_hvp_vconv(int path, const float* V, int64_t n, int64_t n_pad, int d, int dp,
+                            void* out, float* inv_sigma, hipStream_t s) {
+    if (n_pad <= 0) return hipSuccess;
+    if (path == PATH_MFMA_BF16)
+        hvp_vconv_kernel<__bf16><<<blocks_for(n_pad, 4), 256, 0, s>>>(V, n, n_pad, d, dp,
+                                                                      (__bf16*)out, inv_sigma);
+    else if (path == PATH_MFMA_F16)
+        hvp_vconv_kernel<_Float16><<<blocks_for(n_pad, 4), 256, 0, s>>>(V, n, n_pad, d, dp,
+                                                                        (_Float16*)out, inv_sigma);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

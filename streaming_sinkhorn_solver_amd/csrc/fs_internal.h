@@ -108,6 +108,9 @@ struct TransportArgs {
     int64_t part_stride;     // n * dv
     int n_split;             // key ranges (1: U written directly)
     int keys_per_split;      // multiple of 32
+    // second-moment form (Hessian-vector product): direction rows in the
+    // score type [n_pad][dp], or NULL for a plain transport
+    const void* rows2;
 };
 
 // ---- launchers (each returns the first HIP error, enqueues on `s`) ----
@@ -152,8 +155,11 @@ hipError_t launch_hvp_outer(const float* Y, const float* mu, int64_t m, int d, i
 hipError_t launch_hvp_moment(const float* T3, const float* V, int64_t n, int d, int64_t q0, int w,
                              float* M, hipStream_t s);
 hipError_t launch_hvp_final(const float* V, const float* r, const float* u, const float* W,
-                            const float* PY, const float* T, const float* M, int64_t n, int d,
-                            float inv_eps, float* HV, hipStream_t s);
+                            const float* PY, const float* T, const float* M,
+                            const float* m_scale, int64_t n, int d, float inv_eps, float* HV,
+                            hipStream_t s);
+hipError_t launch_hvp_vconv(int path, const float* V, int64_t n, int64_t n_pad, int d, int dp,
+                            void* out, float* inv_sigma, hipStream_t s);
 hipError_t launch_dual_value(const float* a, const float* f, int64_t n, const float* b,
                              const float* g, int64_t m, double* out, hipStream_t s);
 

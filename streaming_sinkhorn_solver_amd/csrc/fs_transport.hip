@@ -822,27 +822,41 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
 // LDS: V^T row c (a column of V) holds the tile's 16 keys as two 16-byte
 // chunks, stored at c*2 + (half ^ ((c >> 3) & 1)) so that 16 consecutive rows
 // hit distinct banks.
-template <int OP, int NBV>
+//
+// NG: 16-byte chunk pairs per operand row (d_pad = 16 NG); the transport uses
+// NG = 64, the second-moment form NG <= 32.  MOMENT: the second-moment form
+// of the Hessian-vector product, M_i = sum_j P_ij s_ij V_j with
+// s_ij = v~_i.y~_j: a second resident row block (a.rows2, the direction rows
+// scaled per row into the score type) is multiplied with the same key
+// fragments, its partials are exchanged with the scores', and the weights
+// become p_ij s_ij.
+template <int OP, int NG, int NBV, bool MOMENT>
 __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a, int64_t m_pad) {
-    constexpr int CPR = 128;                    // 16-byte chunks per key row (1024 values)
+    constexpr int CPR = 2 * NG;                 // 16-byte chunks per key row
     constexpr int ROW_BYTES = CPR * 16;
     constexpr int KT = 16;                      // keys per tile
-    constexpr int KT_CHUNKS = KT * CPR;         // 32 KiB
-    constexpr int KT_SLICES = KT_CHUNKS / 64;   // 32 slices of 1 KiB
+    constexpr int KT_CHUNKS = KT * CPR;         // 32 KiB at d_pad 1024
+    constexpr int KT_SLICES = KT_CHUNKS / 64;   // slices of 1 KiB
+    constexpr int KPW = (KT_SLICES + 3) / 4;    // key slices per wave
+    constexpr int SWZ = NG >= 16 ? 15 : NG - 1; // XOR swizzle, within a half row
     constexpr int DVC = 64 * NBV;               // columns per workgroup (both waves of a pair)
     constexpr int VT_CHUNKS = DVC * 2;          // 16 keys x 2 bytes per column
     constexpr int VT_SLICES = VT_CHUNKS / 64;
     constexpr int VT_PER_WAVE = (VT_SLICES + 3) / 4;
-    constexpr int KS = 16;                      // 32-value contraction steps per half row
-    constexpr int AP = 4;                       // key fragments in flight
+    constexpr int KS = NG / 4;                  // 32-value contraction steps per half row
+    constexpr int AP = KS < 4 ? KS : 4;         // key fragments in flight
     constexpr int APV = NBV < 4 ? NBV : 4;      // V^T fragments in flight
-    static_assert(KT_SLICES == 32 && VT_PER_WAVE <= 8, "tile shapes");
+    constexpr int NP = MOMENT ? 4 : 2;          // exchanged partial blocks per wave
+    constexpr int JOBS = KPW + VT_PER_WAVE;     // loads per wave per tile
+    static_assert(KS >= 1 && KPW <= 8 && VT_PER_WAVE <= 8, "tile shapes");
+    static_assert(!MOMENT || NG <= 32, "two resident blocks fit up to d_pad 512");
 
     __shared__ __attribute__((aligned(16))) uint4 kbuf[2 * KT_CHUNKS];
     __shared__ __attribute__((aligned(16))) uint4 vbuf[2 * VT_CHUNKS];
     __shared__ __attribute__((aligned(16))) float bbuf[2][KT];
-    // [tile parity][row group][wave of the pair][row block][lane]
-    __shared__ __attribute__((aligned(16))) float4 xbuf[2][2][2][2][64];
+    // [tile parity][row group][wave of the pair][partial block][lane]; blocks
+    // 0-1 the scores' row blocks, 2-3 (MOMENT) the direction scores'
+    __shared__ __attribute__((aligned(16))) float4 xbuf[2][2][2][NP][64];
     __shared__ float rowscale[64];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -875,11 +889,24 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
     };
     auto issue_k_slice = [&](int k, int slot, int l) __attribute__((always_inline)) {
         const int L = 4 * l + wave;
-        const int m = L >> 1;
-        const char* src = keys + (int64_t)(j0 + k * KT + m) * ROW_BYTES + (L & 1) * 1024;
-        uint32_t sw = (uint32_t)(m & 15) * 16u;
-        asm volatile("" : "+s"(sw));
-        dma_to_lds16(src, lane16 ^ sw, kbuf + slot * KT_CHUNKS + L * 64);
+        if (KT_SLICES % 4 != 0 && L >= KT_SLICES) return;
+        if constexpr (CPR >= 64) {
+            // a slice lies in one key row: uniform base, lane chunk ^ (m & SWZ)
+            constexpr int IPR = CPR / 64;
+            const int m = L / IPR;
+            const char* src = keys + (int64_t)(j0 + k * KT + m) * ROW_BYTES + (L % IPR) * 1024;
+            uint32_t sw = (uint32_t)(m & SWZ) * 16u;
+            asm volatile("" : "+s"(sw));
+            dma_to_lds16(src, lane16 ^ sw, kbuf + slot * KT_CHUNKS + L * 64);
+        } else {
+            // a slice spans 64 / CPR key rows: position P holds chunk
+            // (P % CPR) ^ (m & SWZ) of key m = P / CPR
+            const int P = L * 64 + lane;
+            const int m = P / CPR, cp = P % CPR;
+            dma_to_lds16(keys + (int64_t)(j0 + k * KT) * ROW_BYTES,
+                         (uint32_t)(m * ROW_BYTES + (cp ^ (m & SWZ)) * 16),
+                         kbuf + slot * KT_CHUNKS + L * 64);
+        }
     };
     auto issue_v_slice = [&](int k, int slot, int l) __attribute__((always_inline)) {
         const int L = 4 * l + wave;
@@ -892,22 +919,35 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
     };
     if (ntiles > 0) {
 #pragma unroll
-        for (int l = 0; l < 8; ++l) issue_k_slice(0, 0, l);
+        for (int l = 0; l < KPW; ++l) issue_k_slice(0, 0, l);
         issue_bias(0, 0);
     }
 
-    // ---- resident rows: q[rb][ks] = chunk 64 dh + 4 ks + kg of row row0 + 16 rb + l16
-    u32x4 q[2][KS];
+    // ---- resident rows: q[rb][ks] = chunk NG dh + 4 ks + kg of row row0 + 16 rb + l16
+    // (and the direction rows vq likewise, MOMENT)
+    u32x4 q[2][KS], vq[MOMENT ? 2 : 1][MOMENT ? KS : 1];
     {
-        const char* rp = (const char*)a.rows + (int64_t)(row0 + l16) * ROW_BYTES + (64 * dh + kg) * 16;
+        const int64_t off = (int64_t)(row0 + l16) * ROW_BYTES + (NG * dh + kg) * 16;
+        const char* rp = (const char*)a.rows + off;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) q[rb][ks] = *(const u32x4*)(rp + rb * 16 * ROW_BYTES + ks * 64);
+        if constexpr (MOMENT) {
+            const char* vp = (const char*)a.rows2 + off;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    vq[rb][ks] = *(const u32x4*)(vp + rb * 16 * ROW_BYTES + ks * 64);
+        }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(q[rb][ks]));
+            for (int ks = 0; ks < KS; ++ks) {
+                asm volatile("" ::"v"(q[rb][ks]));
+                if constexpr (MOMENT) asm volatile("" ::"v"(vq[rb][ks]));
+            }
     }
     // rows past n: L = +inf makes every weight 0
     float Lr[2];
@@ -920,11 +960,13 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // key fragment ks of the tile in slot `slot`: chunk 64 dh + 4 ks + kg of
-    // key l16, stored at l16*CPR + (chunk ^ l16)
+    // key fragment ks of the tile in slot `slot`: chunk NG dh + 4 ks + kg of
+    // key l16, stored at l16*CPR + (chunk ^ (l16 & SWZ)) (the XOR stays in
+    // the half)
     int kbase[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kbase[j] = (l16 * CPR + 64 * dh + ((4 * j + kg) ^ l16)) * 16;
+    for (int j = 0; j < 4; ++j)
+        kbase[j] = (l16 * CPR + NG * dh + (((4 * j + kg) & (NG - 1)) ^ (l16 & SWZ))) * 16;
     auto kfrag = [&](int slot, int ks) __attribute__((always_inline)) -> uint4 {
         return *(const uint4*)((const char*)kbuf + kbase[ks & 3] + slot * (KT_CHUNKS * 16) +
                                (ks >> 2) * 256);
@@ -948,16 +990,17 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
         if (t < ntiles) {
             // scores of tile t, the loads of the next tiles interleaved
             const int kn = min(t + 1, ntiles - 1);
-            f32x4 acc[2];
+            f32x4 acc[NP];
             {
                 float4 seed = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (dh == 0) seed = *(const float4*)&bbuf[cs][4 * kg];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    acc[rb][0] = seed.x;
-                    acc[rb][1] = seed.y;
-                    acc[rb][2] = seed.z;
-                    acc[rb][3] = seed.w;
+                for (int rb = 0; rb < NP; ++rb) {
+                    const bool sc = rb < 2;  // score blocks take the key biases
+                    acc[rb][0] = sc ? seed.x : 0.f;
+                    acc[rb][1] = sc ? seed.y : 0.f;
+                    acc[rb][2] = sc ? seed.z : 0.f;
+                    acc[rb][3] = sc ? seed.w : 0.f;
                 }
             }
             uint4 av[AP];
@@ -968,25 +1011,34 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
                     acc[rb] = mfma16_step<OP>(av[ks % AP], q[rb][ks], acc[rb]);
+                if constexpr (MOMENT) {
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+                        acc[2 + rb] = mfma16_step<OP>(av[ks % AP], vq[rb][ks], acc[2 + rb]);
+                }
                 if (ks + AP < KS) av[ks % AP] = kfrag(cs, ks + AP);
-                if (ks < 8)
-                    issue_k_slice(kn, ps, ks);
-                else if (ks - 8 < VT_PER_WAVE)
-                    issue_v_slice(t, cs, ks - 8);
+                // this step's share of the next tiles' loads
+#pragma unroll
+                for (int jb = ks * JOBS / KS; jb < (ks + 1) * JOBS / KS; ++jb) {
+                    if (jb < KPW)
+                        issue_k_slice(kn, ps, jb);
+                    else
+                        issue_v_slice(t, cs, jb - KPW);
+                }
                 if (ks == 0) issue_bias(kn, ps);
             }
             // pinned ring order: the seed and first AP reads, then per key
-            // fragment its two matrix instructions and its refill read
+            // fragment its matrix instructions and its refill read
             __builtin_amdgcn_sched_group_barrier(0x100, AP + 1, 0);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NP, 0);
                 if (ks + AP < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            // this wave's partial of tile t, for both waves of the pair
+            // this wave's partials of tile t, for both waves of the pair
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < NP; ++rb)
                 xbuf[cs][rg][dh][rb][lane] = make_float4(acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]);
         }
         if (t > 0) {
@@ -1001,13 +1053,28 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
                 z[rb][2] = o.z + p.z;
                 z[rb][3] = o.w + p.w;
             }
+            float wt[2][4];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wt[rb][e] = ex2(fmaf(z[rb][e], a.c_score, -Lr[rb]));
+            if constexpr (MOMENT) {
+                // weights p_ij s_ij
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    const float4 o = xbuf[ps][rg][dh][2 + rb][lane];
+                    const float4 p = xbuf[ps][rg][dh ^ 1][2 + rb][lane];
+                    wt[rb][0] *= o.x + p.x;
+                    wt[rb][1] *= o.y + p.y;
+                    wt[rb][2] *= o.z + p.z;
+                    wt[rb][3] *= o.w + p.w;
+                }
+            }
             uint32_t x[2], y[2];
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
-                x[hp] = pack_f16x2(ex2(fmaf(z[0][2 * hp], a.c_score, -Lr[0])),
-                                   ex2(fmaf(z[0][2 * hp + 1], a.c_score, -Lr[0])));
-                y[hp] = pack_f16x2(ex2(fmaf(z[1][2 * hp], a.c_score, -Lr[1])),
-                                   ex2(fmaf(z[1][2 * hp + 1], a.c_score, -Lr[1])));
+                x[hp] = pack_f16x2(wt[0][2 * hp], wt[0][2 * hp + 1]);
+                y[hp] = pack_f16x2(wt[1][2 * hp], wt[1][2 * hp + 1]);
             }
             // lane rows 2i keep row block 0 and take the odd neighbour's
             // row-block-0 keys; rows 2i+1 keep block 1 and take the even
@@ -1155,22 +1222,42 @@ hipError_t transport_stream_nbv(const TransportArgs& a, int64_t m_pad, hipStream
 // in one column block (16: 1024 columns per workgroup)
 int wide_nbv(int dv) { return dv <= 64 ? 1 : dv <= 128 ? 2 : dv <= 256 ? 4 : dv <= 512 ? 8 : 16; }
 
-template <int OP, int NBV>
+template <int OP, int NG, int NBV, bool MOMENT>
 hipError_t transport_wide_launch(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
     const int n_cb = (a.dv + 64 * NBV - 1) / (64 * NBV);
     const dim3 grid((a.n_rows + 63) / 64, n_cb * a.n_split);
-    transport_wide_kernel<OP, NBV><<<grid, 256, 0, s>>>(a, m_pad);
+    transport_wide_kernel<OP, NG, NBV, MOMENT><<<grid, 256, 0, s>>>(a, m_pad);
     return hipGetLastError();
+}
+
+template <int OP, int NG, bool MOMENT>
+hipError_t transport_wide_nbv(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
+    switch (wide_nbv(a.dv)) {
+        case 1: return transport_wide_launch<OP, NG, 1, MOMENT>(a, m_pad, s);
+        case 2: return transport_wide_launch<OP, NG, 2, MOMENT>(a, m_pad, s);
+        case 4: return transport_wide_launch<OP, NG, 4, MOMENT>(a, m_pad, s);
+        case 8: return transport_wide_launch<OP, NG, 8, MOMENT>(a, m_pad, s);
+        default: return transport_wide_launch<OP, NG, 16, MOMENT>(a, m_pad, s);
+    }
 }
 
 template <int OP>
 hipError_t transport_wide_dispatch(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
-    switch (wide_nbv(a.dv)) {
-        case 1: return transport_wide_launch<OP, 1>(a, m_pad, s);
-        case 2: return transport_wide_launch<OP, 2>(a, m_pad, s);
-        case 4: return transport_wide_launch<OP, 4>(a, m_pad, s);
-        case 8: return transport_wide_launch<OP, 8>(a, m_pad, s);
-        default: return transport_wide_launch<OP, 16>(a, m_pad, s);
+    return transport_wide_nbv<OP, 64, false>(a, m_pad, s);
+}
+
+// second-moment form: d_pad = 16 NG in {64, 128, 256, 512}, dv <= 512 (the
+// accumulation registers hold the direction block next to the scores')
+template <int OP>
+hipError_t transport_moment_dispatch(int ng, const TransportArgs& a, int64_t m_pad,
+                                     hipStream_t s) {
+    if (a.dv > 512) return hipErrorInvalidValue;
+    switch (ng) {
+        case 4: return transport_wide_nbv<OP, 4, true>(a, m_pad, s);
+        case 8: return transport_wide_nbv<OP, 8, true>(a, m_pad, s);
+        case 16: return transport_wide_nbv<OP, 16, true>(a, m_pad, s);
+        case 32: return transport_wide_nbv<OP, 32, true>(a, m_pad, s);
+        default: return hipErrorInvalidValue;
     }
 }
 
@@ -1263,8 +1350,12 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
     if ((e = hipGetLastError()) != hipSuccess) return e;
     vscale_kernel<<<1, 64, 0, s>>>(maxbits, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const bool wide = transport_wide(path, a.dp, a.dv, m_pad);
-    const bool streams = transport_streams(path, a.dp) && (a.dp < 1024 || wide);
+    const bool moment = a.rows2 != nullptr;
+    if (moment && !((path == PATH_MFMA_BF16 || path == PATH_MFMA_F16) && a.dp >= 64 &&
+                    a.dp <= 512 && a.dv <= 512 && (int64_t)a.dv * m_pad * 2 < ((int64_t)1 << 32)))
+        return hipErrorInvalidValue;
+    const bool wide = moment || transport_wide(path, a.dp, a.dv, m_pad);
+    const bool streams = moment || (transport_streams(path, a.dp) && (a.dp < 1024 || wide));
     {
         const dim3 grid((unsigned)((m_pad + 31) / 32), (a.dv + 31) / 32);
         transpose_v_kernel<<<grid, 256, 0, s>>>(a.V, a.n_keys, m_pad, a.dv, scratch,
@@ -1283,7 +1374,10 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
         a.U_part = part_buf;
         a.part_stride = (int64_t)a.n_rows * a.dv;
         transport_split(a, wide, kTransportMaxSplit, a.n_split, a.keys_per_split);
-        if (wide)
+        if (moment)
+            e = path == PATH_MFMA_BF16 ? transport_moment_dispatch<OP_BF16>(ng, a, m_pad, s)
+                                       : transport_moment_dispatch<OP_F16>(ng, a, m_pad, s);
+        else if (wide)
             e = path == PATH_MFMA_BF16 ? transport_wide_dispatch<OP_BF16>(a, m_pad, s)
                                        : transport_wide_dispatch<OP_F16>(a, m_pad, s);
         else if (path == PATH_MFMA_F32)

@@ -5,12 +5,18 @@ seeded inputs and the same GPU potentials.
 The reference plan is the one the path solves: the original points for the
 fp32 paths; for bf16/fp16 the rounded centred clouds with fp32 cost terms
 (tests/helpers.py), with the cost derivative 2 (x_i - y_j).v_i taken from the
-original points as the library does.  Bar: relative Frobenius error 2e-3.
-Every term of the product comes from transports whose f16 weights (in
-(0, 1], 2^-11 relative) and f16 copies of their inputs (scaled by a power of
-two, 2^-11 relative) carry about 1e-3 relative error per product, averaged
-down over the keys; the CG solve for dg stops at a residual of 1e-4 of its
-start.  Observed: 2e-6 (fp32 vector paths) to 1.3e-4 (bf16).
+original points as the library does.  Bar: relative Frobenius error 2e-3
+(5e-3 on the bf16 path).  Every term of the product comes from transports
+whose f16 weights (in (0, 1], 2^-11 relative) and f16 copies of their inputs
+(scaled by a power of two, 2^-11 relative) carry about 1e-3 relative error
+per product, averaged down over the keys; the CG solve for dg stops at a
+residual of 1e-4 of its start.  On the two-byte paths at d_pad 64..512 the
+second-moment term comes from one pass whose direction scores v_i.y~_j
+multiply copies of v and of the centred keys in the score type: bf16 keeps 8
+significant bits (2^-9 relative per element, against fp16's 2^-11), which
+moves that term by up to a few 1e-3 where few coordinates average it.
+Observed: 2e-6 (fp32 vector paths), 1-2e-4 (fp16), 5.7e-4 (bf16, d = 512),
+1.9e-3 (bf16, d = 64).
 """
 import numpy as np
 import pytest
@@ -22,8 +28,11 @@ from streaming_sinkhorn_solver_amd import workloads
 
 pytestmark = pytest.mark.gpu
 
+# two-byte paths at d_pad 64..512 take the one-pass second-moment kernel
+# (every row width it is built for); the others the d*d-column passes
 CASES = [("auto", 3, 300, 250, 0.3), ("fp32-valu", 3, 200, 260, 0.5), ("auto", 16, 400, 350, 0.2),
-         ("bf16", 64, 300, 280, None), ("fp16", 128, 260, 300, None)]
+         ("bf16", 64, 300, 280, None), ("fp16", 128, 260, 300, None),
+         ("fp16", 256, 330, 270, None), ("bf16", 512, 250, 300, None), ("fp16", 1024, 70, 90, None)]
 
 
 def _problem(prec, d, n, m):
@@ -65,7 +74,7 @@ def test_hvp_matches_oracle(fs, prec, d, n, m, eps):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     print(f"{prec} d={d}: HVP relative error {rel:.2e}, CG {info}")
     assert info["cg_residual"] <= 1e-4
-    assert rel <= 2e-3
+    assert rel <= (5e-3 if prec == "bf16" else 2e-3)
 
 
 def test_hvp_is_symmetric(fs):
