@@ -126,3 +126,35 @@ def test_full_size_transport(fs, name):
     print(f"{name} transport: relative error {rel:.2e} (worst row {worst:.2e}) on "
           f"{len(rows)} rows")
     assert rel <= 1e-3
+
+
+def test_full_size_hvp_symmetry(fs):
+    """The Hessian-vector product at the 50k x 50k x 512 recipe's full size
+    (bf16, the one-pass second moment, the launch heuristic's key-range
+    splits), where the dense oracle cannot go: <U, H V> = <V, H U> for two
+    seeded directions, and H V finite.  Bar 5e-3 relative, the bf16 HVP bar
+    (tests/test_hvp_gpu.py)."""
+    import torch
+
+    from streaming_sinkhorn_solver_amd import binding
+
+    prec = RECIPES["c3"][0]
+    w = workloads.make("c3")
+    Xd, Yd, ad, bd = dev(w.X), dev(w.Y), dev(w.a), dev(w.b)
+    f = torch.empty(w.n, device="cuda")
+    g = torch.empty(w.m, device="cuda")
+    p = binding.fs_potentials_init(Xd, Yd, ad, bd, prec=prec, f=f, g=g, dv_max=w.d + 2)
+    binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, iters_per_stage=20)
+    rng = np.random.default_rng(5)
+    U, V = (rng.standard_normal((w.n, w.d)).astype(np.float32) for _ in range(2))
+    HU, HV = torch.empty((w.n, w.d), device="cuda"), torch.empty((w.n, w.d), device="cuda")
+    scratch = torch.empty(binding.fs_hvp_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    iu = binding.fs_hvp(p, w.eps, f, g, Xd, Yd, dev(U), HU, workspace=scratch)
+    iv = binding.fs_hvp(p, w.eps, f, g, Xd, Yd, dev(V), HV, workspace=scratch)
+    torch.cuda.synchronize()
+    hu, hv = host(HU), host(HV)
+    assert np.all(np.isfinite(hu)) and np.all(np.isfinite(hv))
+    lhs = float(np.sum(U.astype(np.float64) * hv))
+    rhs = float(np.sum(V.astype(np.float64) * hu))
+    print(f"c3 HVP symmetry: {lhs:.6e} vs {rhs:.6e}; CG {iu} {iv}")
+    assert abs(lhs - rhs) <= 5e-3 * max(abs(lhs), abs(rhs))
