@@ -225,7 +225,7 @@ fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* o
                         void* stream);
 
 /* Streaming Hessian-vector product of the entropic OT loss with respect to
- * the row cloud X ("FlashSinkhorn" explainer, "Method" part 3: HVPs as
+ * one cloud, X below ("FlashSinkhorn" explainer, "Method" part 3: HVPs as
  * sequences of transport-vector and transport-matrix products; the pages
  * give no formula, the one used is implicit differentiation through the
  * Sinkhorn fixed point).  With P the plan of (f, g), r = P 1, c = P^T 1,
@@ -245,8 +245,11 @@ fs_status fs_dual_value(fs_problem* p, const float* f, const float* g, double* o
  * (so the problem needs dv_max >= d + 2, else FS_ERR_INVALID_ARG).  At converged potentials r = a,
  * c = b and this is the Hessian of the loss; at other potentials it is that
  * of the plan (f, g) define.
+ * wrt = 1 gives the Hessian with respect to Y instead (the same with the
+ * clouds, weights and potentials exchanged); other values FS_ERR_INVALID_ARG.
  * X (n x d), Y (m x d): the fp32 points given to fs_potentials_init; V, HV:
- * n x d device arrays (HV may not overlap any input or the workspace).
+ * device arrays the shape of the differentiated cloud (HV may not overlap
+ * any input or the workspace).
  * workspace: device memory of at least fs_hvp_workspace_bytes(p) bytes,
  * owned by the caller, overwritten.  info (host, nullable): CG iterations and
  * final relative residual.  Squared-Euclidean cost only.  The host waits for
@@ -258,8 +261,9 @@ typedef struct {
 } fs_hvp_info;
 size_t fs_hvp_workspace_bytes(const fs_problem* p);
 fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const float* X,
-                 const float* Y, const float* V, float* HV, float cg_tol, int32_t cg_max_iter,
-                 void* workspace, size_t workspace_bytes, fs_hvp_info* info, void* stream);
+                 const float* Y, int32_t wrt, const float* V, float* HV, float cg_tol,
+                 int32_t cg_max_iter, void* workspace, size_t workspace_bytes, fs_hvp_info* info,
+                 void* stream);
 
 /* Frees the host handle only (the workspace is the caller's). */
 void fs_destroy(fs_problem* p);

@@ -125,8 +125,8 @@ def load():
     lib.fs_hvp_workspace_bytes.restype = ctypes.c_size_t
     lib.fs_hvp_workspace_bytes.argtypes = [_vp]
     lib.fs_hvp.restype = ctypes.c_int
-    lib.fs_hvp.argtypes = [_vp, f32, _fp, _fp, _fp, _fp, _fp, _fp, f32, i32, ctypes.c_void_p,
-                           ctypes.c_size_t, ctypes.POINTER(HvpInfo), _vp]
+    lib.fs_hvp.argtypes = [_vp, f32, _fp, _fp, _fp, _fp, i32, _fp, _fp, f32, i32,
+                           ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(HvpInfo), _vp]
     lib.fs_probe_peak.restype = ctypes.c_int
     lib.fs_probe_peak.argtypes = [ctypes.c_int, _fp, i32, _vp, ctypes.POINTER(ctypes.c_double)]
     _LIB = lib
@@ -299,11 +299,14 @@ def fs_hvp_workspace_bytes(p: Problem) -> int:
 
 
 def fs_hvp(p: Problem, eps: float, f, g, X, Y, V, HV, cg_tol: float = 1e-4,
-           cg_max_iter: int = 200, workspace=None, stream=None) -> dict:
-    """Hessian-vector product of the OT loss with respect to X into HV;
-    returns the CG iterations and final relative residual.  `workspace`: a
-    device tensor of at least fs_hvp_workspace_bytes(p) bytes (allocated
-    here if None)."""
+           cg_max_iter: int = 200, workspace=None, stream=None, wrt: str = "x") -> dict:
+    """Hessian-vector product of the OT loss with respect to X (wrt="x") or
+    Y (wrt="y") into HV; returns the CG iterations and final relative
+    residual.  `workspace`: a device tensor of at least
+    fs_hvp_workspace_bytes(p) bytes (allocated here if None)."""
+    if wrt not in ("x", "y"):
+        raise ValueError("wrt must be 'x' or 'y'")
+    rows = p.n if wrt == "x" else p.m
     need = fs_hvp_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=V.device)
@@ -312,7 +315,8 @@ def fs_hvp(p: Problem, eps: float, f, g, X, Y, V, HV, cg_tol: float = 1e-4,
     info = HvpInfo()
     _check(load().fs_hvp(p.handle, float(eps), _dev(f, "f", p.n), _dev(g, "g", p.m),
                          _dev(X, "X", p.n * p.d), _dev(Y, "Y", p.m * p.d),
-                         _dev(V, "V", p.n * p.d), _dev(HV, "HV", p.n * p.d), float(cg_tol),
+                         0 if wrt == "x" else 1, _dev(V, "V", rows * p.d),
+                         _dev(HV, "HV", rows * p.d), float(cg_tol),
                          int(cg_max_iter), workspace.data_ptr(),
                          workspace.numel() * workspace.element_size(), ctypes.byref(info),
                          _stream(stream)), "fs_hvp")

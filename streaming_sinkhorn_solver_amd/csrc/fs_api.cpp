@@ -740,7 +740,7 @@ struct HvpLayout {
 bool hvp_fused(const fs_problem* p) {
     return (p->path == PATH_MFMA_BF16 || p->path == PATH_MFMA_F16) && p->lse_dp >= 64 &&
            p->lse_dp <= 512 && p->d <= 512 &&
-           (int64_t)p->d * p->Y.n_pad * 2 < ((int64_t)1 << 32);
+           (int64_t)p->d * std::max(p->X.n_pad, p->Y.n_pad) * 2 < ((int64_t)1 << 32);
 }
 
 HvpLayout hvp_layout(const fs_problem* p) {
@@ -751,7 +751,9 @@ HvpLayout hvp_layout(const fs_problem* p) {
         o = up(o + bytes, kAlign);
         return at;
     };
-    const size_t n = (size_t)p->n, m = (size_t)p->m, d = (size_t)p->d;
+    // either cloud can be the differentiated one: size both roles for the
+    // larger
+    const size_t n = (size_t)std::max(p->n, p->m), m = n, d = (size_t)p->d;
     L.fused = hvp_fused(p);
     L.ch = L.fused ? 0 : (int)std::min<int64_t>((int64_t)p->dv_max, (int64_t)d * d);
     L.lse_r = take(4 * n);
@@ -775,7 +777,9 @@ HvpLayout hvp_layout(const fs_problem* p) {
     L.V3 = take(4 * m * (size_t)L.ch);
     L.T3 = take(4 * n * (size_t)L.ch);
     L.dots = take(sizeof(double) * 4);
-    L.vops = take(L.fused ? (size_t)2 * (size_t)p->X.n_pad * (size_t)p->lse_dp : 0);
+    L.vops = take(L.fused ? (size_t)2 * (size_t)std::max(p->X.n_pad, p->Y.n_pad) *
+                                (size_t)p->lse_dp
+                          : 0);
     L.vsig = take(L.fused ? 4 * n : 0);
     L.total = o;
     return L;
@@ -798,10 +802,12 @@ extern "C" {
 size_t fs_hvp_workspace_bytes(const fs_problem* p) { return p ? hvp_layout(p).total : 0; }
 
 fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const float* X,
-                 const float* Y, const float* V, float* HV, float cg_tol, int32_t cg_max_iter,
-                 void* workspace, size_t workspace_bytes, fs_hvp_info* info, void* stream) {
+                 const float* Y, int32_t wrt, const float* V, float* HV, float cg_tol,
+                 int32_t cg_max_iter, void* workspace, size_t workspace_bytes, fs_hvp_info* info,
+                 void* stream) {
     if (!p || !f || !g || !X || !Y || !V || !HV || !workspace)
         return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (wrt != 0 && wrt != 1) return fail(FS_ERR_INVALID_ARG, "wrt must be 0 (X) or 1 (Y)");
     if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (p->cost != FS_COST_SQEUCLIDEAN)
         return fail(FS_ERR_INVALID_ARG, "the HVP supports the squared-Euclidean cost only");
@@ -814,8 +820,18 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
     if (workspace_bytes < L.total)
         return fail(FS_ERR_WORKSPACE, "HVP workspace too small: %zu < %zu bytes", workspace_bytes,
                     L.total);
-    const size_t nd = (size_t)4 * p->n * p->d;
-    if (overlaps(HV, nd, V, nd) || overlaps(HV, nd, X, nd) ||
+    // The differentiated cloud R ("rows") and the other one K ("keys"): X
+    // and Y, or exchanged.  Every formula below is written for R = X.
+    const bool xs = wrt == 0;
+    const int64_t n = xs ? p->n : p->m, m = xs ? p->m : p->n;
+    const float* Rp = xs ? X : Y;
+    const float* Kp = xs ? Y : X;
+    const float* fr = xs ? f : g;
+    const float* fk = xs ? g : f;
+    const Cloud& RC = xs ? p->X : p->Y;
+    const Cloud& KC = xs ? p->Y : p->X;
+    const size_t nd = (size_t)4 * n * p->d;
+    if (overlaps(HV, nd, V, nd) || overlaps(HV, nd, X, (size_t)4 * p->n * p->d) ||
         overlaps(HV, nd, workspace, workspace_bytes) ||
         overlaps(HV, nd, Y, (size_t)4 * p->m * p->d))
         return fail(FS_ERR_INVALID_ARG, "HV overlaps an input or the workspace");
@@ -823,10 +839,10 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
     char* w = (char*)workspace;
     auto F = [&](size_t off) { return (float*)(w + off); };
     double* dots = (double*)(w + L.dots);
-    const int64_t n = p->n, m = p->m;
     const int d = p->d;
     const float c_bias = (float)(1.4426950408889634 / (double)eps);
-    const float* mu = p->centre + d;  // centre of Y: every point is taken relative to it
+    // centre of K: every point is taken relative to it
+    const float* mu = xs ? p->centre + d : p->centre;
     fs_status st;
     hipError_t e;
 #define FS_HIP(call, what)                     \
@@ -834,19 +850,19 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
         if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
     } while (0)
     // exact row and column LSEs (reused by every transport below), marginals
-    if ((st = half_step(p, true, eps, g, F(L.lse_r), nullptr, nullptr, 1, s)) != FS_OK) return st;
-    if ((st = half_step(p, false, eps, f, F(L.lse_c), nullptr, nullptr, 1, s)) != FS_OK) return st;
-    FS_HIP(launch_marginal(F(L.lse_r), f, p->X.nrm, p->X.w, c_bias, n, F(L.r), s), "HVP marginal");
-    FS_HIP(launch_marginal(F(L.lse_c), g, p->Y.nrm, p->Y.w, c_bias, m, F(L.c), s), "HVP marginal");
-    // PY = P (Y - mu); u, W = [V | s | u/r]; PtW = P^T W; rhs = w - P^T (u/r)
-    if ((st = transport_side(p, true, eps, f, g, Y, d, F(L.PY), 0, mu, nullptr, s, F(L.lse_r))) !=
+    if ((st = half_step(p, xs, eps, fk, F(L.lse_r), nullptr, nullptr, 1, s)) != FS_OK) return st;
+    if ((st = half_step(p, !xs, eps, fr, F(L.lse_c), nullptr, nullptr, 1, s)) != FS_OK) return st;
+    FS_HIP(launch_marginal(F(L.lse_r), fr, RC.nrm, RC.w, c_bias, n, F(L.r), s), "HVP marginal");
+    FS_HIP(launch_marginal(F(L.lse_c), fk, KC.nrm, KC.w, c_bias, m, F(L.c), s), "HVP marginal");
+    // PY = P (K - mu); u, W = [V | s | u/r]; PtW = P^T W; rhs = w - P^T (u/r)
+    if ((st = transport_side(p, xs, eps, f, g, Kp, d, F(L.PY), 0, mu, nullptr, s, F(L.lse_r))) !=
         FS_OK)
         return st;
-    FS_HIP(launch_hvp_rows(X, V, mu, F(L.PY), F(L.r), n, d, F(L.u), F(L.W), s), "HVP rows");
-    if ((st = transport_side(p, false, eps, f, g, F(L.W), d + 2, F(L.PtW), 0, nullptr, nullptr, s,
+    FS_HIP(launch_hvp_rows(Rp, V, mu, F(L.PY), F(L.r), n, d, F(L.u), F(L.W), s), "HVP rows");
+    if ((st = transport_side(p, !xs, eps, f, g, F(L.W), d + 2, F(L.PtW), 0, nullptr, nullptr, s,
                              F(L.lse_c))) != FS_OK)
         return st;
-    FS_HIP(launch_hvp_cols(Y, mu, F(L.PtW), m, d, F(L.rhs), s), "HVP columns");
+    FS_HIP(launch_hvp_cols(Kp, mu, F(L.PtW), m, d, F(L.rhs), s), "HVP columns");
     // Preconditioned CG (M = diag(c), the diagonal of K's first term) for
     // K dg = rhs on the complement of the constant vector,
     // K = diag(c) - P^T diag(1/r) P.  The residual is kept mean-free (K's
@@ -865,11 +881,11 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
     int it = 0;
     while (rr0 > 0.0 && it < cg_max_iter && rel > (double)cg_tol) {
         // Ap = c pd - P^T ((P pd) / r)
-        if ((st = transport_side(p, true, eps, f, g, F(L.pd), 1, F(L.Pp), 0, nullptr, nullptr, s,
+        if ((st = transport_side(p, xs, eps, f, g, F(L.pd), 1, F(L.Pp), 0, nullptr, nullptr, s,
                                  F(L.lse_r))) != FS_OK)
             return st;
         FS_HIP(launch_scale_sub(F(L.r), F(L.Pp), nullptr, n, 1, F(L.Pp), s), "HVP scale");
-        if ((st = transport_side(p, false, eps, f, g, F(L.Pp), 1, F(L.Ptq), 0, nullptr, nullptr, s,
+        if ((st = transport_side(p, !xs, eps, f, g, F(L.Pp), 1, F(L.Ptq), 0, nullptr, nullptr, s,
                                  F(L.lse_c))) != FS_OK)
             return st;
         FS_HIP(launch_scale_sub(F(L.c), F(L.pd), F(L.Ptq), m, 0, F(L.Ap), s), "HVP scale");
@@ -895,17 +911,17 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
         rz = rz_new;
     }
     // T = P [dg (Y - mu) | dg]
-    FS_HIP(launch_hvp_dgy(Y, mu, F(L.dg), m, d, F(L.V2), s), "HVP dg columns");
-    if ((st = transport_side(p, true, eps, f, g, F(L.V2), d + 1, F(L.T), 0, nullptr, nullptr, s,
+    FS_HIP(launch_hvp_dgy(Kp, mu, F(L.dg), m, d, F(L.V2), s), "HVP dg columns");
+    if ((st = transport_side(p, xs, eps, f, g, F(L.V2), d + 1, F(L.T), 0, nullptr, nullptr, s,
                              F(L.lse_r))) != FS_OK)
         return st;
     // M_i = sum_j P_ij ((y_j - mu).v_i) (y_j - mu)
     if (L.fused) {
         // one pass: the direction rows (scaled per row into the score type)
         // as a second resident block, weights P_ij (v_i sigma_i).y~_j
-        FS_HIP(launch_hvp_vconv(p->path, V, n, p->X.n_pad, d, p->lse_dp, w + L.vops, F(L.vsig), s),
+        FS_HIP(launch_hvp_vconv(p->path, V, n, RC.n_pad, d, p->lse_dp, w + L.vops, F(L.vsig), s),
                "HVP direction rows");
-        if ((st = transport_side(p, true, eps, f, g, Y, d, F(L.M), 0, mu, nullptr, s, F(L.lse_r),
+        if ((st = transport_side(p, xs, eps, f, g, Kp, d, F(L.M), 0, mu, nullptr, s, F(L.lse_r),
                                  w + L.vops)) != FS_OK)
             return st;
     } else {
@@ -913,8 +929,8 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
         FS_HIP(launch_fill(F(L.M), n * d, 0.f, s), "HVP fill");
         for (int64_t q0 = 0; q0 < (int64_t)d * d; q0 += L.ch) {
             const int wq = (int)std::min<int64_t>(L.ch, (int64_t)d * d - q0);
-            FS_HIP(launch_hvp_outer(Y, mu, m, d, q0, wq, F(L.V3), s), "HVP outer products");
-            if ((st = transport_side(p, true, eps, f, g, F(L.V3), wq, F(L.T3), 0, nullptr, nullptr,
+            FS_HIP(launch_hvp_outer(Kp, mu, m, d, q0, wq, F(L.V3), s), "HVP outer products");
+            if ((st = transport_side(p, xs, eps, f, g, F(L.V3), wq, F(L.T3), 0, nullptr, nullptr,
                                      s, F(L.lse_r))) != FS_OK)
                 return st;
             FS_HIP(launch_hvp_moment(F(L.T3), V, n, d, q0, wq, F(L.M), s), "HVP moment");

@@ -47,11 +47,15 @@ def _problem(prec, d, n, m):
     return X, Y, (a / a.sum()).astype(np.float32), (b / b.sum()).astype(np.float32), None
 
 
-def _reference(X, Y, a, b, f, g, V, eps, prec):
+def _reference(X, Y, a, b, f, g, V, eps, prec, wrt="x"):
     if prec in ("bf16", "fp16"):
         rp = RoundedProblem(X, Y, prec)
         P = oracle_plan(rp.Xr, rp.Yr, a, b, f - rp.alpha, g - rp.beta, eps)
+        if wrt == "y":  # the same loss with the clouds exchanged: the plan transposed
+            return oracle_hvp(Y, X, b, a, g, f, V, eps, P=P.T)
         return oracle_hvp(X, Y, a, b, f, g, V, eps, P=P)
+    if wrt == "y":
+        return oracle_hvp(Y, X, b, a, g, f, V, eps)
     return oracle_hvp(X, Y, a, b, f, g, V, eps)
 
 
@@ -74,6 +78,26 @@ def test_hvp_matches_oracle(fs, prec, d, n, m, eps):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     print(f"{prec} d={d}: HVP relative error {rel:.2e}, CG {info}")
     assert info["cg_residual"] <= 1e-4
+    assert rel <= (5e-3 if prec == "bf16" else 2e-3)
+
+
+@pytest.mark.parametrize("prec,d,n,m,eps", [CASES[0], CASES[2], CASES[3], CASES[4]])
+def test_hvp_with_respect_to_y(fs, prec, d, n, m, eps):
+    import torch
+
+    from streaming_sinkhorn_solver_amd import binding
+
+    X, Y, a, b, weps = _problem(prec, d, n, m)
+    eps = eps or weps
+    p, f, g, _, (Xd, Yd, _, _) = gpu_solve(X, Y, a, b, eps=eps, iters=40, prec=prec,
+                                           dv_max=max(d + 2, min(d * d, 4096)))
+    V = np.random.default_rng(d + m).standard_normal((m, d)).astype(np.float32)
+    HV = torch.empty((m, d), device="cuda")
+    info = binding.fs_hvp(p, eps, f, g, Xd, Yd, dev(V), HV, wrt="y")
+    torch.cuda.synchronize()
+    ref = _reference(X, Y, a, b, host(f), host(g), V, eps, prec, wrt="y")
+    rel = np.linalg.norm(host(HV) - ref) / np.linalg.norm(ref)
+    print(f"{prec} d={d} wrt y: HVP relative error {rel:.2e}, CG {info}")
     assert rel <= (5e-3 if prec == "bf16" else 2e-3)
 
 
