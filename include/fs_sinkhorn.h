@@ -265,6 +265,104 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
                  int32_t cg_max_iter, void* workspace, size_t workspace_bytes, fs_hvp_info* info,
                  void* stream);
 
+/* ---- Block-sparse form for low-dimensional clouds ----------------------
+ * "FlashSinkhorn 2: block-sparse entropic optimal transport" (patty.io
+ * explainer).  Section on cutting space: points sorted along a Z-order
+ * (Morton) curve, so that a run of consecutive points is a compact group and
+ * a block of the cost matrix pairs two groups.  Section on guaranteeing the
+ * skip: a block is skipped when a bound on its mass is below a threshold
+ * that caps, at every iteration, the error the skipped blocks leave in every
+ * row and every column.  The page gives no formula; the reading used:
+ *
+ *  - Morton order: each coordinate is quantised over the cloud's bounding
+ *    box to B = floor(30/d) bits (q = min(2^B - 1, floor((x - lo) * scale)),
+ *    scale = 2^B / (hi - lo) or 0 for a flat axis, each step one correctly
+ *    rounded float32 operation) and bit k of coordinate c becomes bit
+ *    k*d + c of the code; points are ordered by code, ties by index.
+ *  - Blocks: 256 consecutive rows (one workgroup of the streaming kernel) and
+ *    32 consecutive keys (one matrix-core block).  For the f-update with the
+ *    current (f, g), every block carries a least-squares linear fit of its
+ *    potential; with c_I = max_{i in I} (f_i - u_I.x_i),
+ *    G_J = log sum_{j in J} b_j exp((g_j - v_J.y_j)/eps) and
+ *    H = max over the two boxes of u_I.x + v_J.y - |x - y|^2,
+ *    beta(I, J) = (c_I + H)/eps + G_J bounds log sum_{j in J} P_ij / a_i for
+ *    every row i of I.  J is kept for I when beta >= log(delta / N_J) (N_J key
+ *    blocks; the kernel keeps a hair more, a rounding margin), else skipped,
+ *    so the skipped mass of every row is below delta * a_i.  The g-update is
+ *    screened the same way with the clouds exchanged.
+ *  - Consequence (the certificate): with f_cur the potential being replaced,
+ *    0 <= f_sparse_i - f_dense_i <= eps log(1 + delta exp((f_sparse_i - f_cur_i)/eps)),
+ *    about eps * delta near the fixed point.  delta = 0 keeps every block
+ *    (the dense update, evaluated block by block).
+ *
+ * The clouds are expected in Morton order (fs_morton_sort), which only
+ * affects how many blocks are skipped, never the bound.
+ */
+
+/* Bytes of workspace for fs_morton_sort of n points in d dimensions
+ * (1 <= d <= 8); 0 for invalid arguments.  Pure host function. */
+size_t fs_morton_workspace_bytes(int64_t n, int32_t d);
+
+/* Sorts the n points X (n x d, device, fp32) into Morton order:
+ * X_sorted[i] = X[perm[i]], w_sorted[i] = w[perm[i]] (w, w_sorted: both NULL
+ * or both device arrays of n floats), perm (device, n int32).  Outputs may
+ * not overlap inputs.  workspace: fs_morton_workspace_bytes(n, d) bytes,
+ * 256-byte aligned, overwritten.  Deterministic (a stable radix sort, no
+ * atomics outside workgroup-local counters).  Limits: 1 <= n <= 2^31 - 1. */
+fs_status fs_morton_sort(const float* X, const float* w, int64_t n, int32_t d, float* X_sorted,
+                         float* w_sorted, int32_t* perm, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* dst[perm[i] * width + c] = src[i * width + c]: brings per-point results of
+ * a sorted problem back to the caller's order (device arrays; dst may not
+ * overlap src). */
+fs_status fs_unpermute(const float* src, const int32_t* perm, int64_t n, int32_t width,
+                       float* dst, void* stream);
+
+/* Workspace of the block-sparse form of a problem (boxes, fits, kept-block
+ * lists; the lists take 4 * ceil(n/256) * ceil(m/32) bytes at most, rounded
+ * up); 0 if the problem does not qualify.  Pure host function. */
+size_t fs_bs_workspace_bytes(const fs_problem* p);
+
+/* Enables the block-sparse form on a problem built by fs_potentials_init on
+ * Morton-ordered clouds with d <= 3, FS_PREC_AUTO or FS_PREC_FP32 and the
+ * squared-Euclidean cost (else FS_ERR_INVALID_ARG).  workspace:
+ * fs_bs_workspace_bytes(p) bytes, 256-byte aligned, owned by the caller,
+ * which must outlive the handle's block-sparse calls.  Computes the blocks'
+ * boxes and synchronises once (their magnitude).  Up to 2^27 - 544 points
+ * per cloud. */
+fs_status fs_bs_attach(fs_problem* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One block-sparse half-step: screening with (f_cur, g), then
+ * f_out_i = -eps log sum over the kept blocks' keys of b_j exp((g_j - C_ij)/eps).
+ * f_out may be f_cur (in place) unless row_resid is given; row_resid
+ * (device float, nullable) receives sum_i a_i |exp((f_cur_i - f_out_i)/eps) - 1|
+ * as fs_lse_update_f does.  delta in [0, 1).  The _g form is the mirror
+ * image (keys X, weights a). */
+fs_status fs_bs_lse_update_f(fs_problem* p, float eps, float delta, const float* g,
+                             const float* f_cur, float* f_out, float* row_resid, void* stream);
+fs_status fs_bs_lse_update_g(fs_problem* p, float eps, float delta, const float* f,
+                             const float* g_cur, float* g_out, float* col_resid, void* stream);
+
+/* fs_sinkhorn_solve with every half-step block-sparse (screened anew each
+ * time).  With tol > 0 the residual is that of the retained blocks' plan
+ * (within about delta of the dense one).  time_kernels times the streaming
+ * kernels only (not the fits and the screening). */
+fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* opts, float delta, float* f,
+                               float* g, fs_solve_info* info, void* stream);
+
+/* Introspection (host): side 0 = the f-update (rows X, keys Y), side 1 = the
+ * g-update.  fs_bs_shape: block counts and the row stride of the lists.
+ * fs_bs_read_screen (synchronises): the kept-block count of every row block
+ * from the last screening of that side, and, if lists is non-NULL, the kept
+ * key-block indices (increasing, padded to a multiple of 16 with the index
+ * of the sentinel block, ceil(keys_padded / 32)) of the last screening, which
+ * must be of that side. */
+fs_status fs_bs_shape(const fs_problem* p, int32_t side, int32_t* n_row_blocks,
+                      int32_t* n_key_blocks, int32_t* list_stride);
+fs_status fs_bs_read_screen(fs_problem* p, int32_t side, int32_t* counts, int32_t* lists,
+                            void* stream);
+
 /* Frees the host handle only (the workspace is the caller's). */
 void fs_destroy(fs_problem* p);
 

@@ -23,6 +23,9 @@ __all__ = [
     "PROBE_KINDS", "fs_probe_peak", "fs_apply_transport_t", "fs_gradient", "fs_dual_value",
     "fs_hvp", "fs_hvp_workspace_bytes",
     "COST_SQEUCLIDEAN", "COST_COSINE",
+    "fs_morton_workspace_bytes", "fs_morton_sort", "fs_unpermute", "fs_bs_workspace_bytes",
+    "fs_bs_attach", "fs_bs_lse_update_f", "fs_bs_lse_update_g", "fs_bs_sinkhorn_solve",
+    "fs_bs_shape", "fs_bs_read_screen",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -129,6 +132,26 @@ def load():
                            ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(HvpInfo), _vp]
     lib.fs_probe_peak.restype = ctypes.c_int
     lib.fs_probe_peak.argtypes = [ctypes.c_int, _fp, i32, _vp, ctypes.POINTER(ctypes.c_double)]
+    lib.fs_morton_workspace_bytes.restype = sz
+    lib.fs_morton_workspace_bytes.argtypes = [i64, i32]
+    lib.fs_morton_sort.restype = ctypes.c_int
+    lib.fs_morton_sort.argtypes = [_fp, _fp, i64, i32, _fp, _fp, _fp, _vp, sz, _vp]
+    lib.fs_unpermute.restype = ctypes.c_int
+    lib.fs_unpermute.argtypes = [_fp, _fp, i64, i32, _fp, _vp]
+    lib.fs_bs_workspace_bytes.restype = sz
+    lib.fs_bs_workspace_bytes.argtypes = [_vp]
+    lib.fs_bs_attach.restype = ctypes.c_int
+    lib.fs_bs_attach.argtypes = [_vp, _vp, sz, _vp]
+    for name in ("fs_bs_lse_update_f", "fs_bs_lse_update_g"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [_vp, f32, f32, _fp, _fp, _fp, _fp, _vp]
+    lib.fs_bs_sinkhorn_solve.restype = ctypes.c_int
+    lib.fs_bs_sinkhorn_solve.argtypes = [_vp, ctypes.POINTER(SolveOpts), f32, _fp, _fp,
+                                         ctypes.POINTER(SolveInfo), _vp]
+    lib.fs_bs_shape.restype = ctypes.c_int
+    lib.fs_bs_shape.argtypes = [_vp, i32] + [ctypes.POINTER(i32)] * 3
+    lib.fs_bs_read_screen.restype = ctypes.c_int
+    lib.fs_bs_read_screen.argtypes = [_vp, i32, _vp, _vp, _vp]
     _LIB = lib
     return lib
 
@@ -352,6 +375,130 @@ def fs_probe_peak(kind: str, sink, reps: int = 9, stream=None) -> float:
     _check(load().fs_probe_peak(PROBE_KINDS[kind], _dev(sink, "sink"), int(reps),
                                 _stream(stream), ctypes.byref(rate)), "fs_probe_peak")
     return rate.value
+
+
+def _idev(t, name: str, numel: int):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != numel:
+        raise TypeError(f"{name} must be a contiguous int32 tensor of {numel} elements")
+    return t.data_ptr()
+
+
+def fs_morton_workspace_bytes(n: int, d: int) -> int:
+    return int(load().fs_morton_workspace_bytes(n, d))
+
+
+def fs_morton_sort(X, w=None, X_sorted=None, w_sorted=None, perm=None, workspace=None,
+                   stream=None):
+    """Morton order of the points X (n x d); returns (X_sorted, w_sorted, perm)
+    with X_sorted[i] = X[perm[i]] (w_sorted None when w is None)."""
+    n, d = X.shape
+    dev = X.device
+    if X_sorted is None:
+        X_sorted = torch.empty_like(X)
+    if w is not None and w_sorted is None:
+        w_sorted = torch.empty_like(w)
+    if perm is None:
+        perm = torch.empty(n, dtype=torch.int32, device=dev)
+    need = fs_morton_workspace_bytes(n, d)
+    if need == 0:
+        _check(FS_ERR_INVALID_ARG, "fs_morton_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(load().fs_morton_sort(_dev(X, "X", n * d), _dev(w, "w", n), n, d,
+                                 _dev(X_sorted, "X_sorted", n * d), _dev(w_sorted, "w_sorted", n),
+                                 _idev(perm, "perm", n), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "fs_morton_sort")
+    return X_sorted, w_sorted, perm
+
+
+def fs_unpermute(src, perm, dst=None, stream=None):
+    """dst[perm[i]] = src[i] (rows of src.numel() // n floats)."""
+    n = perm.numel()
+    width = src.numel() // n
+    if dst is None:
+        dst = torch.empty_like(src)
+    _check(load().fs_unpermute(_dev(src, "src", n * width), _idev(perm, "perm", n), n, width,
+                               _dev(dst, "dst", n * width), _stream(stream)), "fs_unpermute")
+    return dst
+
+
+def fs_bs_workspace_bytes(p: Problem) -> int:
+    return int(load().fs_bs_workspace_bytes(p.handle))
+
+
+def fs_bs_attach(p: Problem, workspace=None, stream=None):
+    """Enables the block-sparse form; keeps the workspace on the handle."""
+    need = fs_bs_workspace_bytes(p)
+    if need == 0:
+        _check(FS_ERR_INVALID_ARG, "fs_bs_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=p.workspace.device)
+    _check(load().fs_bs_attach(p.handle, workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "fs_bs_attach")
+    p.bs_workspace = workspace
+    return p
+
+
+def fs_bs_lse_update_f(p: Problem, eps: float, delta: float, g, f_cur, f_out, row_resid=None,
+                       stream=None):
+    return _check(load().fs_bs_lse_update_f(p.handle, float(eps), float(delta),
+                                            _dev(g, "g", p.m), _dev(f_cur, "f_cur", p.n),
+                                            _dev(f_out, "f_out", p.n),
+                                            _dev(row_resid, "row_resid", 1), _stream(stream)),
+                  "fs_bs_lse_update_f")
+
+
+def fs_bs_lse_update_g(p: Problem, eps: float, delta: float, f, g_cur, g_out, col_resid=None,
+                       stream=None):
+    return _check(load().fs_bs_lse_update_g(p.handle, float(eps), float(delta),
+                                            _dev(f, "f", p.n), _dev(g_cur, "g_cur", p.m),
+                                            _dev(g_out, "g_out", p.m),
+                                            _dev(col_resid, "col_resid", 1), _stream(stream)),
+                  "fs_bs_lse_update_g")
+
+
+def fs_bs_sinkhorn_solve(p: Problem, f, g, *, eps_end: float, iters_per_stage: int,
+                         delta: float, n_stages: int = 1, eps_start: Optional[float] = None,
+                         tol: float = 0.0, check_every: int = 10, warm_start: bool = False,
+                         stream=None, raise_not_converged: bool = True,
+                         time_kernels: bool = False) -> dict:
+    opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
+                     float(eps_end), int(iters_per_stage), float(tol), int(check_every),
+                     int(bool(warm_start)), int(bool(time_kernels)))
+    info = SolveInfo()
+    st = load().fs_bs_sinkhorn_solve(p.handle, ctypes.byref(opts), float(delta),
+                                     _dev(f, "f", p.n), _dev(g, "g", p.m), ctypes.byref(info),
+                                     _stream(stream))
+    allow = () if raise_not_converged else (FS_ERR_NOT_CONVERGED,)
+    _check(st, "fs_bs_sinkhorn_solve", allow)
+    return {"status": st, "iters_done": info.iters_done, "final_eps": info.final_eps,
+            "residual": info.residual, "lse_launches": info.lse_launches,
+            "lse_ms": info.lse_ms}
+
+
+def fs_bs_shape(p: Problem, side: int) -> dict:
+    vals = [ctypes.c_int32() for _ in range(3)]
+    _check(load().fs_bs_shape(p.handle, int(side), *[ctypes.byref(v) for v in vals]),
+           "fs_bs_shape")
+    return {"row_blocks": vals[0].value, "key_blocks": vals[1].value, "stride": vals[2].value}
+
+
+def fs_bs_read_screen(p: Problem, side: int, lists: bool = False, stream=None):
+    """Kept-block counts per row block of the last screening of `side` (numpy
+    int32), and with lists=True the padded lists (row_blocks x stride)."""
+    import numpy as np
+
+    sh = fs_bs_shape(p, side)
+    counts = np.zeros(sh["row_blocks"], np.int32)
+    L = np.zeros((sh["row_blocks"], sh["stride"]), np.int32) if lists else None
+    _check(load().fs_bs_read_screen(p.handle, int(side), counts.ctypes.data,
+                                    L.ctypes.data if lists else None, _stream(stream)),
+           "fs_bs_read_screen")
+    return (counts, L) if lists else counts
 
 
 def solve(X, Y, a, b, *, eps: float, iters: int, prec="auto", n_stages: int = 1,

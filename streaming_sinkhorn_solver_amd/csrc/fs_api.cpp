@@ -50,6 +50,18 @@ struct fs_problem {
     float* krec;      // small-d matrix path: key records of one pass (fp32)
     void* krec16;     //   fp16-split records (d <= 4)
     void* kguard;     //   guard words of the packing
+    // block-sparse form (fs_bs_attach): side 0 = rows X / keys Y (f-update),
+    // side 1 = rows Y / keys X (g-update)
+    bool bs_on = false;
+    int bs_nbR[2] = {0, 0}, bs_nbK[2] = {0, 0}, bs_cap[2] = {0, 0};
+    float4* bs_rbox[2] = {nullptr, nullptr};  // [nbR][2] (lo, hi) of 256-row blocks
+    float4* bs_kbox[2] = {nullptr, nullptr};  // [nbK][2] of 32-key blocks
+    float4* bs_rfit = nullptr;                // per pass: (u, c) of the row blocks
+    float4* bs_kfit = nullptr;                // per pass: (v, G) of the key blocks
+    int* bs_cnt[2] = {nullptr, nullptr};      // kept blocks per row block, last pass of a side
+    int* bs_list = nullptr;                   // kept blocks of the last pass
+    int bs_last_side = -1;
+    float bs_mag = 1.f;                       // coordinate magnitude of the rounding margin
 };
 
 namespace {
@@ -216,8 +228,9 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
                            : 0);
     const bool small = sh.path == PATH_SMALL;
     const size_t kmax = (size_t)std::max(np, mp);
-    L.krec = take(small ? small_f32_rec_bytes(d) * kmax : 0);
-    L.krec16 = take(small ? small_f16_rec_bytes(d) * kmax : 0);
+    // (+32 records: the -inf sentinel block of the block-sparse form)
+    L.krec = take(small ? small_f32_rec_bytes(d) * (kmax + 32) : 0);
+    L.krec16 = take(small ? small_f16_rec_bytes(d) * (kmax + 32) : 0);
     L.kguard = take(small ? 32 : 0);  // packing guard [2], cloud L1 maxima [2]
     L.rsx = take(sizeof(float) * n);  // cosine cost: 1/|x_i|
     L.rsy = take(sizeof(float) * m);
@@ -1005,6 +1018,356 @@ fs_status fs_problem_info(const fs_problem* p, int32_t* path, int32_t* d_pad, in
     if (f_splits) *f_splits = p->f_split;
     if (g_splits) *g_splits = p->g_split;
     return FS_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Block-sparse low-dimensional form ("FlashSinkhorn 2" explainer, sections on
+// cutting space and on guaranteeing the skip; see fs_bsparse.hip).
+
+fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, const float* cur,
+                          const float* other, float* out, float* resid, hipStream_t s,
+                          hipEvent_t eb, hipEvent_t ee) {
+    const int side = f_side ? 0 : 1;
+    const Cloud& R = f_side ? p->X : p->Y;
+    const Cloud& K = f_side ? p->Y : p->X;
+    const float* cR = p->centre + (f_side ? 0 : p->d);
+    const float* cK = p->centre + (f_side ? p->d : 0);
+    const int nbR = p->bs_nbR[side], nbK = p->bs_nbK[side];
+    const float c_bias = (float)(1.4426950408889634 / (double)eps);
+    hipError_t e;
+    if ((e = launch_block_fit((const float*)R.ops, cR, p->d, R.n, 256, false, cur, nullptr, c_bias,
+                              p->bs_rfit, s)) != hipSuccess ||
+        (e = launch_block_fit((const float*)K.ops, cK, p->d, K.n, 32, true, other, K.lw2, c_bias,
+                              p->bs_kfit, s)) != hipSuccess)
+        return hip_fail(e, "block fit launch");
+    const float thr2 = delta > 0.f ? (float)std::log2((double)delta / (double)nbK) : -INFINITY;
+    const int sentinel = (int)(K.n_pad / 32);
+    if ((e = launch_screen(p->bs_rbox[side], p->bs_rfit, nbR, p->bs_kbox[side], p->bs_kfit, nbK,
+                           c_bias, thr2, p->bs_mag, p->bs_list, p->bs_cnt[side], p->bs_cap[side],
+                           sentinel, s)) != hipSuccess)
+        return hip_fail(e, "screening launch");
+    p->bs_last_side = side;
+    LseArgs a = base_args(p, f_side, eps);
+    a.key_pot = other;
+    a.out = out;
+    a.mode = 0;
+    a.cur = resid ? cur : nullptr;
+    a.resid_out = resid;
+    a.n_split = 1;
+    a.keys_per_split = (int)K.n_pad;
+    a.krec_keys = (int)K.n_pad + 32;
+    a.bs_list = p->bs_list;
+    a.bs_count = p->bs_cnt[side];
+    a.bs_cap = p->bs_cap[side];
+    a.bs_sentinel = sentinel;
+    if ((e = launch_lse(p->path, a, s, eb, ee)) != hipSuccess)
+        return hip_fail(e, f_side ? "block-sparse f-update launch" : "block-sparse g-update launch");
+    return FS_OK;
+}
+
+struct BsLayout {
+    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], list, total;
+};
+
+BsLayout bs_layout(const fs_problem* p) {
+    BsLayout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = up(o + bytes, kAlign);
+        return at;
+    };
+    const int64_t n = p->n, m = p->m;
+    const int64_t nbR[2] = {(n + 255) / 256, (m + 255) / 256};
+    const int64_t nbK[2] = {(m + 31) / 32, (n + 31) / 32};
+    for (int q = 0; q < 2; ++q) {
+        L.rbox[q] = take(sizeof(float4) * 2 * nbR[q]);
+        L.kbox[q] = take(sizeof(float4) * 2 * nbK[q]);
+        L.cnt[q] = take(sizeof(int) * nbR[q]);
+    }
+    L.rfit = take(sizeof(float4) * std::max(nbR[0], nbR[1]));
+    L.kfit = take(sizeof(float4) * std::max(nbK[0], nbK[1]));
+    const int64_t cap0 = (nbK[0] + 15) / 16 * 16, cap1 = (nbK[1] + 15) / 16 * 16;
+    L.list = take(sizeof(int) * (size_t)std::max(nbR[0] * cap0, nbR[1] * cap1));
+    L.total = o;
+    return L;
+}
+
+fs_status bs_check(const fs_problem* p) {
+    if (!p) return fail(FS_ERR_INVALID_ARG, "NULL handle");
+    if (p->path != PATH_SMALL || p->d > 3 || p->cost != FS_COST_SQEUCLIDEAN)
+        return fail(FS_ERR_INVALID_ARG,
+                    "the block-sparse form needs d <= 3, fp32 matrix-core scores (FS_PREC_AUTO or "
+                    "FS_PREC_FP32) and the squared-Euclidean cost");
+    // the kernel addresses records with 32-bit offsets: (padded keys + 32) x 32 bytes
+    if ((std::max(p->X.n_pad, p->Y.n_pad) + 32) * 32 > ((int64_t)1 << 32))
+        return fail(FS_ERR_INVALID_ARG, "the block-sparse form supports up to 2^27 - 544 points");
+    if (small_rows_per_block() != 256) return fail(FS_ERR_DEVICE, "row block mismatch");
+    return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fs_morton_workspace_bytes(int64_t n, int32_t d) {
+    if (n < 1 || n > 0x7fffffffLL || d < 1 || d > 8) return 0;
+    return morton_workspace_bytes(n);
+}
+
+fs_status fs_morton_sort(const float* X, const float* w, int64_t n, int32_t d, float* X_sorted,
+                         float* w_sorted, int32_t* perm, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (!X || !X_sorted || !perm) return fail(FS_ERR_INVALID_ARG, "X, X_sorted and perm must be non-NULL");
+    if ((w == nullptr) != (w_sorted == nullptr))
+        return fail(FS_ERR_INVALID_ARG, "w and w_sorted must both be given or both be NULL");
+    if (n < 1 || n > 0x7fffffffLL) return fail(FS_ERR_INVALID_ARG, "n must be in [1, 2^31-1]");
+    if (d < 1 || d > 8) return fail(FS_ERR_INVALID_ARG, "Morton order supports 1 <= d <= 8");
+    if (overlaps(X, 4 * (size_t)n * d, X_sorted, 4 * (size_t)n * d) ||
+        (w && overlaps(w, 4 * (size_t)n, w_sorted, 4 * (size_t)n)))
+        return fail(FS_ERR_INVALID_ARG, "outputs may not overlap inputs");
+    if (!workspace || (uintptr_t)workspace % kAlign)
+        return fail(FS_ERR_WORKSPACE, "workspace must be non-NULL and %zu-byte aligned", kAlign);
+    if (workspace_bytes < morton_workspace_bytes(n))
+        return fail(FS_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    morton_workspace_bytes(n));
+    int dev = 0;
+    fs_status st = check_device(&dev);
+    if (st != FS_OK) return st;
+    hipError_t e = launch_morton_sort(X, w, n, d, X_sorted, w_sorted, perm, workspace,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? FS_OK : hip_fail(e, "fs_morton_sort");
+}
+
+fs_status fs_unpermute(const float* src, const int32_t* perm, int64_t n, int32_t width, float* dst,
+                       void* stream) {
+    if (!src || !perm || !dst) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (n < 1 || n > 0x7fffffffLL || width < 1 || width > 65536)
+        return fail(FS_ERR_INVALID_ARG, "n must be in [1, 2^31-1] and width in [1, 65536]");
+    if (overlaps(src, 4 * (size_t)n * width, dst, 4 * (size_t)n * width))
+        return fail(FS_ERR_INVALID_ARG, "dst overlaps src");
+    hipError_t e = launch_unpermute(src, perm, n, width, dst, (hipStream_t)stream);
+    return e == hipSuccess ? FS_OK : hip_fail(e, "fs_unpermute");
+}
+
+size_t fs_bs_workspace_bytes(const fs_problem* p) {
+    if (!p || p->path != PATH_SMALL || p->d > 3) return 0;
+    return bs_layout(p).total;
+}
+
+fs_status fs_bs_attach(fs_problem* p, void* workspace, size_t workspace_bytes, void* stream) {
+    fs_status st = bs_check(p);
+    if (st != FS_OK) return st;
+    const BsLayout L = bs_layout(p);
+    if (!workspace || (uintptr_t)workspace % kAlign)
+        return fail(FS_ERR_WORKSPACE, "workspace must be non-NULL and %zu-byte aligned", kAlign);
+    if (workspace_bytes < L.total)
+        return fail(FS_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    L.total);
+    char* w = (char*)workspace;
+    const Cloud* rows[2] = {&p->X, &p->Y};
+    const Cloud* keys[2] = {&p->Y, &p->X};
+    for (int q = 0; q < 2; ++q) {
+        p->bs_nbR[q] = (int)((rows[q]->n + 255) / 256);
+        p->bs_nbK[q] = (int)((keys[q]->n + 31) / 32);
+        p->bs_cap[q] = (p->bs_nbK[q] + 15) / 16 * 16;
+        p->bs_rbox[q] = (float4*)(w + L.rbox[q]);
+        p->bs_kbox[q] = (float4*)(w + L.kbox[q]);
+        p->bs_cnt[q] = (int*)(w + L.cnt[q]);
+    }
+    p->bs_rfit = (float4*)(w + L.rfit);
+    p->bs_kfit = (float4*)(w + L.kfit);
+    p->bs_list = (int*)(w + L.list);
+    p->bs_last_side = -1;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    const float* cx = p->centre;
+    const float* cy = p->centre + p->d;
+    if ((e = launch_block_boxes((const float*)p->X.ops, cx, p->d, p->n, 256, p->bs_rbox[0], s)) !=
+            hipSuccess ||
+        (e = launch_block_boxes((const float*)p->Y.ops, cy, p->d, p->m, 32, p->bs_kbox[0], s)) !=
+            hipSuccess ||
+        (e = launch_block_boxes((const float*)p->Y.ops, cy, p->d, p->m, 256, p->bs_rbox[1], s)) !=
+            hipSuccess ||
+        (e = launch_block_boxes((const float*)p->X.ops, cx, p->d, p->n, 32, p->bs_kbox[1], s)) !=
+            hipSuccess)
+        return hip_fail(e, "block boxes");
+    // coordinate magnitude for the screening's rounding margin (read back once)
+    std::vector<float4> hb(2 * (size_t)std::max(p->bs_nbR[0], p->bs_nbR[1]));
+    double M[3] = {0, 0, 0};
+    for (int q = 0; q < 2; ++q) {
+        const size_t cnt = 2 * (size_t)p->bs_nbR[q];
+        if ((e = hipMemcpyAsync(hb.data(), p->bs_rbox[q], sizeof(float4) * cnt,
+                                hipMemcpyDeviceToHost, s)) != hipSuccess ||
+            (e = hipStreamSynchronize(s)) != hipSuccess)
+            return hip_fail(e, "box readback");
+        for (size_t k = 0; k < cnt; ++k) {
+            M[0] = std::max(M[0], (double)std::fabs(hb[k].x));
+            M[1] = std::max(M[1], (double)std::fabs(hb[k].y));
+            M[2] = std::max(M[2], (double)std::fabs(hb[k].z));
+        }
+    }
+    p->bs_mag = (float)(1.0 + 4.0 * (M[0] * M[0] + M[1] * M[1] + M[2] * M[2]));
+    p->bs_on = true;
+    return FS_OK;
+}
+
+fs_status fs_bs_lse_update_f(fs_problem* p, float eps, float delta, const float* g,
+                             const float* f_cur, float* f_out, float* row_resid, void* stream) {
+    fs_status st = bs_check(p);
+    if (st != FS_OK) return st;
+    if (!p->bs_on) return fail(FS_ERR_INVALID_ARG, "call fs_bs_attach first");
+    if (!g || !f_cur || !f_out) return fail(FS_ERR_INVALID_ARG, "NULL g, f_cur or f_out");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!(delta >= 0.f && delta < 1.f)) return fail(FS_ERR_INVALID_ARG, "delta must be in [0, 1)");
+    if (row_resid && overlaps(f_out, 4 * p->n, f_cur, 4 * p->n))
+        return fail(FS_ERR_INVALID_ARG, "f_out may not overlap f_cur when a residual is asked");
+    if (overlaps(f_out, 4 * p->n, g, 4 * p->m)) return fail(FS_ERR_INVALID_ARG, "f_out overlaps g");
+    return fs_bs_half_step(p, true, eps, delta, f_cur, g, f_out, row_resid, (hipStream_t)stream,
+                           nullptr, nullptr);
+}
+
+fs_status fs_bs_lse_update_g(fs_problem* p, float eps, float delta, const float* f,
+                             const float* g_cur, float* g_out, float* col_resid, void* stream) {
+    fs_status st = bs_check(p);
+    if (st != FS_OK) return st;
+    if (!p->bs_on) return fail(FS_ERR_INVALID_ARG, "call fs_bs_attach first");
+    if (!f || !g_cur || !g_out) return fail(FS_ERR_INVALID_ARG, "NULL f, g_cur or g_out");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!(delta >= 0.f && delta < 1.f)) return fail(FS_ERR_INVALID_ARG, "delta must be in [0, 1)");
+    if (col_resid && overlaps(g_out, 4 * p->m, g_cur, 4 * p->m))
+        return fail(FS_ERR_INVALID_ARG, "g_out may not overlap g_cur when a residual is asked");
+    if (overlaps(g_out, 4 * p->m, f, 4 * p->n)) return fail(FS_ERR_INVALID_ARG, "g_out overlaps f");
+    return fs_bs_half_step(p, false, eps, delta, g_cur, f, g_out, col_resid, (hipStream_t)stream,
+                           nullptr, nullptr);
+}
+
+fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delta, float* f,
+                               float* g, fs_solve_info* info, void* stream) {
+    fs_status st = bs_check(p);
+    if (st != FS_OK) return st;
+    if (!p->bs_on) return fail(FS_ERR_INVALID_ARG, "call fs_bs_attach first");
+    if (!o || !f || !g) return fail(FS_ERR_INVALID_ARG, "NULL opts, f or g");
+    if (o->n_stages < 1) return fail(FS_ERR_INVALID_ARG, "n_stages must be >= 1");
+    if (o->iters_per_stage < 0) return fail(FS_ERR_INVALID_ARG, "iters_per_stage must be >= 0");
+    if (!eps_ok(o->eps_end) || (o->n_stages > 1 && !eps_ok(o->eps_start)))
+        return fail(FS_ERR_INVALID_ARG, "eps_start/eps_end must be finite and > 0");
+    if (!std::isfinite(o->tol)) return fail(FS_ERR_INVALID_ARG, "tol must be finite");
+    if (o->tol > 0.f && o->check_every < 1)
+        return fail(FS_ERR_INVALID_ARG, "check_every must be >= 1 when tol > 0");
+    if (!(delta >= 0.f && delta < 1.f)) return fail(FS_ERR_INVALID_ARG, "delta must be in [0, 1)");
+    if (overlaps(f, 4 * p->n, g, 4 * p->m)) return fail(FS_ERR_INVALID_ARG, "f overlaps g");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    KernelTimer timer;
+    if (o->time_kernels) {
+        const size_t half_steps = 2 * (size_t)o->n_stages * (size_t)o->iters_per_stage + 8;
+        if ((e = timer.reserve(half_steps)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    if (!o->warm_start) {
+        if ((e = launch_fill(g, p->m, 0.f, s)) != hipSuccess) return hip_fail(e, "fill g");
+        if ((e = launch_fill(f, p->n, 0.f, s)) != hipSuccess) return hip_fail(e, "fill f");
+    }
+    const bool use_tol = o->tol > 0.f;
+    int done = 0;
+    float resid = -1.f, eps = o->eps_end;
+    bool converged = false;
+    auto check = [&](float eps_c) -> fs_status {
+        // row term of the residual of (f, g) from a dry-run update into pot_tmp;
+        // the column term is zero right after a g-update
+        fs_status s2 = fs_bs_half_step(p, true, eps_c, delta, f, g, p->pot_tmp, p->scal, s,
+                                       nullptr, nullptr);
+        if (s2 != FS_OK) return s2;
+        float h = 0.f;
+        hipError_t e2 = hipMemcpyAsync(&h, p->scal, sizeof(float), hipMemcpyDeviceToHost, s);
+        if (e2 == hipSuccess) e2 = hipStreamSynchronize(s);
+        if (e2 != hipSuccess) return hip_fail(e2, "residual readback");
+        resid = h;
+        return FS_OK;
+    };
+    for (int si = 0; si < o->n_stages && !converged; ++si) {
+        eps = o->n_stages == 1
+                  ? o->eps_end
+                  : (float)((double)o->eps_start *
+                            std::pow((double)o->eps_end / (double)o->eps_start,
+                                     (double)si / (double)(o->n_stages - 1)));
+        for (int it = 0; it < o->iters_per_stage; ++it) {
+            hipEvent_t eb = nullptr, ee = nullptr;
+            if (o->time_kernels) timer.next(eb, ee);
+            if ((st = fs_bs_half_step(p, true, eps, delta, f, g, f, nullptr, s, eb, ee)) != FS_OK)
+                return st;
+            if (o->time_kernels) timer.next(eb, ee);
+            if ((st = fs_bs_half_step(p, false, eps, delta, g, f, g, nullptr, s, eb, ee)) != FS_OK)
+                return st;
+            ++done;
+            if (use_tol && done % o->check_every == 0) {
+                if ((st = check(eps)) != FS_OK) return st;
+                if (resid <= o->tol) {
+                    converged = true;
+                    break;
+                }
+            }
+        }
+    }
+    if (use_tol && !converged && (done == 0 || done % o->check_every != 0)) {
+        if ((st = check(eps)) != FS_OK) return st;
+        converged = resid <= o->tol;
+    }
+    float lse_ms = 0.f;
+    int lse_n = 0;
+    if (o->time_kernels) {
+        if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "timing sync");
+        for (size_t k = 0; k + 1 < timer.used; k += 2) {
+            float ms = 0.f;
+            if ((e = hipEventElapsedTime(&ms, timer.ev[k], timer.ev[k + 1])) != hipSuccess)
+                return hip_fail(e, "hipEventElapsedTime");
+            lse_ms += ms;
+            ++lse_n;
+        }
+    }
+    if (info) {
+        info->iters_done = done;
+        info->final_eps = eps;
+        info->residual = use_tol ? resid : -1.f;
+        info->lse_launches = lse_n;
+        info->lse_ms = lse_ms;
+    }
+    if (use_tol && !converged)
+        return fail(FS_ERR_NOT_CONVERGED, "residual %g above tol %g after %d iterations",
+                    (double)resid, (double)o->tol, done);
+    return FS_OK;
+}
+
+fs_status fs_bs_shape(const fs_problem* p, int32_t side, int32_t* n_row_blocks,
+                      int32_t* n_key_blocks, int32_t* list_stride) {
+    if (!p || !p->bs_on) return fail(FS_ERR_INVALID_ARG, "NULL handle or fs_bs_attach not called");
+    if (side != 0 && side != 1) return fail(FS_ERR_INVALID_ARG, "side must be 0 or 1");
+    if (n_row_blocks) *n_row_blocks = p->bs_nbR[side];
+    if (n_key_blocks) *n_key_blocks = p->bs_nbK[side];
+    if (list_stride) *list_stride = p->bs_cap[side];
+    return FS_OK;
+}
+
+fs_status fs_bs_read_screen(fs_problem* p, int32_t side, int32_t* counts, int32_t* lists,
+                            void* stream) {
+    if (!p || !p->bs_on) return fail(FS_ERR_INVALID_ARG, "NULL handle or fs_bs_attach not called");
+    if (side != 0 && side != 1) return fail(FS_ERR_INVALID_ARG, "side must be 0 or 1");
+    if (!counts) return fail(FS_ERR_INVALID_ARG, "counts is NULL");
+    if (lists && p->bs_last_side != side)
+        return fail(FS_ERR_INVALID_ARG, "the lists held are those of side %d", p->bs_last_side);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(counts, p->bs_cnt[side], sizeof(int) * p->bs_nbR[side],
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && lists)
+        e = hipMemcpyAsync(lists, p->bs_list,
+                           sizeof(int) * (size_t)p->bs_nbR[side] * p->bs_cap[side],
+                           hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? FS_OK : hip_fail(e, "fs_bs_read_screen");
 }
 
 }  // extern "C"

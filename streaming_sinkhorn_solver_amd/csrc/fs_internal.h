@@ -80,6 +80,14 @@ struct LseArgs {
     // dot-product units of this pass [keys' padded count]
     float* kbias;
     int kbias_keys;
+    // block-sparse form (PATH_SMALL, d <= 3; see fs_bsparse.hip): per row
+    // block of 256 rows, the kept 32-key blocks [row blocks][bs_cap] padded to
+    // whole tiles of 16 with bs_sentinel (the block of -inf records right
+    // after the padded keys), and their count.  NULL: the dense pass.
+    const int* bs_list;
+    const int* bs_count;
+    int bs_cap;
+    int bs_sentinel;
 };
 
 // Arguments of the transport application U = P.V (or P.V / a).
@@ -197,6 +205,35 @@ size_t small_f16_rec_bytes(int d);  // per key (0 if d > 4)
 // Largest L1 norm over the (converted, fp32) points of a cloud into *out.
 hipError_t launch_row_l1max(const float* ops, int64_t n, int d, float* out, hipStream_t s);
 hipError_t launch_lse_small(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin);
+// the block-sparse form (a.bs_list set, a.n_split == 1, d <= 3; the key
+// records must hold the sentinel block: a.krec_keys = padded keys + 32)
+hipError_t launch_lse_small_sparse(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin);
+
+// ---- block-sparse low-dimensional path (fs_bsparse.hip) ----
+// Bits per coordinate of the Morton code (30 / d).
+int morton_bits(int d);
+size_t morton_workspace_bytes(int64_t n);
+// Sorts the n points of X (n x d, d <= 8) by Morton code (ties by index) into
+// Xo, gathers w (nullable) into wo, and writes the permutation (Xo[i] =
+// X[perm[i]]).  ws: morton_workspace_bytes(n) bytes, 256-aligned.
+hipError_t launch_morton_sort(const float* X, const float* w, int64_t n, int d, float* Xo,
+                              float* wo, int32_t* perm, void* ws, hipStream_t s);
+// dst[perm[i]] = src[i] for rows of `width` floats.
+hipError_t launch_unpermute(const float* src, const int32_t* perm, int64_t n, int width,
+                            float* dst, hipStream_t s);
+// Boxes (lo, hi) of the blocks of gs (32 or 256) consecutive points of a cloud
+// stored as centred fp32 rows of 4 (plus its centre).
+hipError_t launch_block_boxes(const float* ops, const float* centre, int d, int64_t n, int gs,
+                              float4* box, hipStream_t s);
+// Per-block linear fit of a potential: rows (gs 256, key false) -> (u, c),
+// keys (gs 32, key true) -> (v, G) with G in base 2 (uses lw2 and c_bias).
+hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_t n, int gs,
+                            bool key, const float* pot, const float* lw2, float c_bias,
+                            float4* fit, hipStream_t s);
+// Kept key blocks of every row block (threshold thr2 = log2(delta / nbK)).
+hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const float4* kbox,
+                         const float4* kfit, int nbK, float c_bias, float thr2, float mag,
+                         int* list, int* count, int cap, int sentinel, hipStream_t s);
 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
 // Matrix paths: the streaming transport kernel serves operand rows of up to

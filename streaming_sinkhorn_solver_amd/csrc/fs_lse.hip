@@ -1114,7 +1114,7 @@ hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s, hipEvent_t ev_b
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (path == PATH_SMALL) {
-        e = launch_lse_small(a, s, ev_begin);
+        e = a.bs_list ? launch_lse_small_sparse(a, s, ev_begin) : launch_lse_small(a, s, ev_begin);
     } else if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) {
         return e;
     } else if (wide) {

@@ -145,7 +145,34 @@ __global__ __launch_bounds__(256) void pack_key_records_kernel(
     }
 }
 
-template <int KP>
+// Scalar load of N consecutive words at a wave-uniform address, waited for
+// at once (the loads of the key tiles are counted by vmcnt alone).
+template <int N>
+__device__ __forceinline__ void sload_words(const int* p, int (&o)[N]) {
+    if constexpr (N == 1) {
+        int r;
+        asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+        o[0] = r;
+    } else if constexpr (N == 2) {
+        long long r;
+        asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+        o[0] = (int)r;
+        o[1] = (int)(r >> 32);
+    } else {
+        static_assert(N == 4, "1, 2 or 4 words");
+        u32x4 r;
+        asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = (int)r[q];
+    }
+}
+
+// SPARSE: the block-sparse form.  The workgroup's keys are not a contiguous
+// range but the 32-key blocks listed for its row block by the screening
+// (LseArgs::bs_list, padded to whole tiles with a block of -inf records);
+// a tile gathers 16 listed blocks, each wave-wide copy instruction fetching
+// whole blocks at per-lane offsets.  No key-range split.
+template <int KP, bool SPARSE = false>
 __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs a) {
     constexpr int W = kSmallWaves;
     constexpr bool HAS_F16 = KP <= 2;  // the fp16 format covers d <= 4
@@ -164,9 +191,12 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     int row_block, split;
     xcd_work(row_block, split);
     const int row = row_block * (W * 32) + wave * 32 + ln;  // rows are padded: always readable
-    const int j0 = split * a.keys_per_split;
+    constexpr int SUB_BLOCKS = TK / 32;  // 32-key blocks per tile
+    const int j0 = SPARSE ? 0 : split * a.keys_per_split;
     const int j1 = min(a.n_keys, j0 + a.keys_per_split);
-    const int ntiles = (j1 - j0 + TK - 1) / TK;
+    const int* __restrict__ lst = SPARSE ? a.bs_list + (int64_t)row_block * a.bs_cap : nullptr;
+    const int ntiles = SPARSE ? (a.bs_count[row_block] + SUB_BLOCKS - 1) / SUB_BLOCKS
+                              : (j1 - j0 + TK - 1) / TK;
     const int d = a.dp;
     const int stride = d <= 4 ? 4 : 8;
     const float* __restrict__ xr = (const float*)a.rows + (int64_t)row * stride;
@@ -255,9 +285,28 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
 #pragma unroll
             for (int l = 0; l < INSTR_PER_WAVE; ++l) {
                 const int L = l * W + wave;
-                if (TILE_INSTR % W == 0 || L < TILE_INSTR)
-                    dma_to_lds16(recs + (int64_t)k * TILE_BYTES + L * 1024, lane16,
-                                 &tbuf[slot][L * 64]);
+                if (TILE_INSTR % W == 0 || L < TILE_INSTR) {
+                    if constexpr (SPARSE) {
+                        // instruction L covers blocks L*BPI .. L*BPI+BPI-1 of the tile;
+                        // lane `lane` fetches 16 bytes of block L*BPI + lane/LPB
+                        constexpr int BLK = 32 * REC_BYTES;
+                        constexpr int BPI = 1024 / BLK;
+                        constexpr int LPB = 64 / BPI;
+                        static_assert(1024 % BLK == 0, "whole blocks per instruction");
+                        int ent[BPI];
+                        sload_words<BPI>(lst + k * SUB_BLOCKS + L * BPI, ent);
+                        int J = ent[0];
+#pragma unroll
+                        for (int q = 1; q < BPI; ++q)
+                            if (lane / LPB == q) J = ent[q];
+                        const uint32_t Jc = min((uint32_t)J, (uint32_t)a.bs_sentinel);
+                        dma_to_lds16(recs, Jc * (uint32_t)BLK + (uint32_t)(lane % LPB) * 16u,
+                                     &tbuf[slot][L * 64]);
+                    } else {
+                        dma_to_lds16(recs + (int64_t)k * TILE_BYTES + L * 1024, lane16,
+                                     &tbuf[slot][L * 64]);
+                    }
+                }
             }
         };
         if (ntiles > 0) {
@@ -378,7 +427,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     }
 }
 
-template <int KP>
+template <int KP, bool SPARSE = false>
 hipError_t small_launch(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
     hipError_t e;
     const int n_pad_keys = a.krec_keys;
@@ -389,8 +438,8 @@ hipError_t small_launch(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
         a.key_lw2, a.c_bias, a.krec, f16 ? (_Float16*)a.krec16 : nullptr, (Guard*)a.krec_guard);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-    const dim3 grid((a.n_rows + kSmallWaves * 32 - 1) / (kSmallWaves * 32), a.n_split);
-    lse_small_kernel<KP><<<grid, kSmallWaves * 64, 0, s>>>(a);
+    const dim3 grid((a.n_rows + kSmallWaves * 32 - 1) / (kSmallWaves * 32), SPARSE ? 1 : a.n_split);
+    lse_small_kernel<KP, SPARSE><<<grid, kSmallWaves * 64, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -422,6 +471,15 @@ int small_tile(int d) { return small_tile_keys(small_kp(d)); }
 int small_rows_per_block() { return kSmallWaves * 32; }
 size_t small_f32_rec_bytes(int d) { return (size_t)f32_rec_bytes(small_kp(d)); }
 size_t small_f16_rec_bytes(int d) { return small_kp(d) <= 2 ? (size_t)kF16RecBytes : 0; }
+
+hipError_t launch_lse_small_sparse(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
+    if (a.n_split != 1 || !a.bs_list || !a.bs_count) return hipErrorInvalidValue;
+    switch (small_kp(a.dp)) {
+        case 1: return small_launch<1, true>(a, s, ev_begin);
+        case 2: return small_launch<2, true>(a, s, ev_begin);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_lse_small(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
     switch (small_kp(a.dp)) {

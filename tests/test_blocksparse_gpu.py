@@ -1,0 +1,255 @@
+"""GPU parity of the block-sparse low-dimensional form (Morton order, block
+screening, retained-block updates) against the oracle (oracle/blocksparse.py
+and the dense oracle update).
+
+* Morton order: bit-exact permutation (the codes are integer decisions taken
+  in float32 on both sides, every step correctly rounded).
+* Updates: the kept blocks are a choice the two sides make in different
+  precisions (fp32 fits and bounds here, float64 in the oracle), so the
+  lists are compared by what is unique: every block the GPU skips carries a
+  true mass below delta / N_J of its rows' targets (brute force), and every
+  block the oracle keeps with a margin is kept.  The potentials are then
+  compared with the dense oracle update through the certificate,
+      -tol <= f_gpu - f_dense <= eps log(1 + delta exp((f_gpu - f_cur)/eps)) + tol,
+  with tol = 1e-3 eps, the fp32 parity bar of the dense path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import blocksparse as obs
+from helpers import dev, host
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3  # x eps
+
+
+def _bind():
+    from streaming_sinkhorn_solver_amd import binding as B
+    return B
+
+
+def _cloud(rng, n, d, kind):
+    if kind == "uniform":
+        return rng.uniform(0, 1, (n, d))
+    if kind == "mixture":
+        means = rng.uniform(0.2, 0.8, (8, d))
+        return means[rng.integers(0, 8, n)] + rng.normal(0, 0.05, (n, d))
+    if kind == "dups":
+        base = rng.uniform(0, 1, (max(1, n // 7), d))
+        return base[rng.integers(0, len(base), n)]
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("n,d,kind", [(1, 3, "uniform"), (5, 1, "uniform"), (4095, 3, "uniform"),
+                                      (4097, 2, "mixture"), (30001, 3, "dups"),
+                                      (300_003, 3, "mixture"), (70_000, 1, "uniform"),
+                                      (20_000, 8, "uniform")])
+def test_morton_sort_bit_exact(n, d, kind):
+    import torch
+
+    B = _bind()
+    rng = np.random.default_rng(n + d)
+    X = _cloud(rng, n, d, kind).astype(np.float32)
+    w = rng.standard_exponential(n).astype(np.float32)
+    Xs, ws, perm = B.fs_morton_sort(dev(X), dev(w))
+    torch.cuda.synchronize()
+    ref = obs.morton_order(X)
+    got = perm.cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(Xs.cpu().numpy(), X[ref])
+    assert np.array_equal(ws.cpu().numpy(), w[ref])
+    back = B.fs_unpermute(Xs, perm)
+    assert np.array_equal(back.cpu().numpy(), X)
+
+
+def _sorted_problem(seed, n, m, d, xkind="uniform", ykind="mixture"):
+    rng = np.random.default_rng(seed)
+    X = _cloud(rng, n, d, xkind)
+    Y = _cloud(rng, m, d, ykind)
+    X = X[obs.morton_order(X.astype(np.float32))].astype(np.float32)
+    Y = Y[obs.morton_order(Y.astype(np.float32))].astype(np.float32)
+    a = rng.standard_exponential(n)
+    b = rng.standard_exponential(m)
+    return X, Y, (a / a.sum()).astype(np.float32), (b / b.sum()).astype(np.float32)
+
+
+def _gpu_problem(X, Y, a, b):
+    B = _bind()
+    p = B.fs_potentials_init(dev(X), dev(Y), dev(a), dev(b))
+    B.fs_bs_attach(p)
+    return p
+
+
+def _check_lists(p, side, R, K, w_keys, pot_rows, pot_keys, eps, delta):
+    """Every skipped block's true mass is below delta/N_J of its rows' targets;
+    every block the oracle keeps with a margin is kept."""
+    B = _bind()
+    counts, L = B.fs_bs_read_screen(p, side, lists=True)
+    nbR, nbK = len(counts), (len(K) + 31) // 32
+    ref_lists, beta, thr = obs.screen(R, K, w_keys, pot_rows, pot_keys, eps, delta, 256, 32,
+                                      return_bounds=True)
+    R64, K64 = R.astype(np.float64), K.astype(np.float64)
+    skipped = 0
+    for I in range(nbR):
+        kept = L[I, :counts[I]]
+        assert np.all(np.diff(kept) > 0) and kept.min() >= 0 and kept.max() < nbK
+        pad = L[I, counts[I]:(counts[I] + 15) // 16 * 16]
+        assert np.all(pad == (len(K) + 511) // 512 * 512 // 32)
+        sure = np.nonzero(beta[I] >= thr + 1e-3)[0]
+        assert set(sure.tolist()) <= set(kept.tolist())
+        skip = np.setdiff1d(np.arange(nbK), kept)
+        skipped += len(skip)
+        if len(skip) == 0:
+            continue
+        rows = np.arange(I * 256, min((I + 1) * 256, len(R)))
+        keys = np.concatenate([np.arange(J * 32, min(J * 32 + 32, len(K))) for J in skip])
+        blk = np.concatenate([np.full(min(J * 32 + 32, len(K)) - J * 32, k)
+                              for k, J in enumerate(skip)])
+        C = ((R64[rows, None, :] - K64[None, keys, :]) ** 2).sum(-1)
+        z = np.exp((pot_rows[rows, None] + pot_keys[None, keys] - C) / eps) * w_keys[None, keys]
+        mass = np.zeros((len(rows), len(skip)))
+        np.add.at(mass.T, blk, z.T)
+        assert mass.max() < delta / nbK * 1.001
+    return skipped / (nbR * nbK)
+
+
+def _dense_converged(X, Y, a, b, eps, iters=400):
+    r = oracle.sinkhorn(X, Y, a, b, eps=eps, iters=iters)
+    return r["f"], r["g"]
+
+
+# min_skip: the share of block pairs that must have been skipped (at these
+# sizes a 256-row block spans a large part of the cloud, so it is small)
+@pytest.mark.parametrize("n,m,d,eps,delta,min_skip", [(3000, 2500, 3, 2e-3, 1e-3, 0.02),
+                                                      (1000, 4100, 2, 1e-3, 1e-4, 0.05),
+                                                      (700, 900, 1, 1e-3, 1e-3, 0.05),
+                                                      (200, 20, 3, 5e-3, 1e-3, 0.0)])
+def test_bs_update_certificate(n, m, d, eps, delta, min_skip):
+    import torch
+
+    B = _bind()
+    X, Y, a, b = _sorted_problem(n + m, n, m, d)
+    f, g = _dense_converged(X, Y, a, b, eps, iters=150)
+    p = _gpu_problem(X, Y, a, b)
+    fd, gd = dev(f), dev(g)
+    f_out = torch.empty_like(fd)
+    B.fs_bs_lse_update_f(p, eps, delta, gd, fd, f_out)
+    torch.cuda.synchronize()
+    fs = host(f_out)
+    frac_f = _check_lists(p, 0, X, Y, b.astype(np.float64), f, g, eps, delta)
+    ref = oracle.f_update(X, Y, b, g, eps)
+    cert = obs.certificate(fs, f, eps, delta)
+    diff = fs - ref
+    assert diff.min() >= -TOL * eps
+    assert np.all(diff <= cert + TOL * eps)
+    # the g side, from the new f
+    g_out = torch.empty_like(gd)
+    B.fs_bs_lse_update_g(p, eps, delta, f_out, gd, g_out)
+    torch.cuda.synchronize()
+    gs = host(g_out)
+    frac_g = _check_lists(p, 1, Y, X, a.astype(np.float64), g, fs, eps, delta)
+    ref = oracle.g_update(X, Y, a, fs, eps)
+    cert = obs.certificate(gs, g, eps, delta)
+    assert (gs - ref).min() >= -TOL * eps
+    assert np.all(gs - ref <= cert + TOL * eps)
+    print(f"skipped block pairs: f {frac_f:.3f}  g {frac_g:.3f}")
+    assert frac_f >= min_skip and frac_g >= min_skip
+
+
+def test_bs_delta_zero_is_the_dense_update():
+    import torch
+
+    B = _bind()
+    X, Y, a, b = _sorted_problem(21, 1500, 1300, 3)
+    rng = np.random.default_rng(22)
+    eps = 0.01
+    g = rng.normal(0, 0.01, 1300)
+    f = rng.normal(0, 0.01, 1500)
+    p = _gpu_problem(X, Y, a, b)
+    out = torch.empty(1500, device="cuda")
+    B.fs_bs_lse_update_f(p, eps, 0.0, dev(g), dev(f), out)
+    counts = B.fs_bs_read_screen(p, 0)
+    assert np.all(counts == (1300 + 31) // 32)
+    ref = oracle.f_update(X, Y, b, g, eps)
+    assert np.max(np.abs(host(out) - ref)) <= TOL * eps
+    dense = torch.empty_like(out)
+    B.fs_lse_update_f(p, eps, dev(g), dense)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(host(out) - host(dense))) <= 1e-4 * eps
+
+
+def test_bs_solve_fixed_iterations():
+    """Ten block-sparse iterations from zero against the oracle's sparse
+    iteration, and delta = 0 against the dense oracle iteration."""
+    import torch
+
+    B = _bind()
+    X, Y, a, b = _sorted_problem(31, 1200, 1000, 3)
+    eps, iters = 5e-3, 10
+    p = _gpu_problem(X, Y, a, b)
+    f = torch.zeros(1200, device="cuda")
+    g = torch.zeros(1000, device="cuda")
+    B.fs_bs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=iters, delta=0.0)
+    torch.cuda.synchronize()
+    r = oracle.sinkhorn(X, Y, a, b, eps=eps, iters=iters)
+    assert np.max(np.abs(host(f) - r["f"])) <= TOL * eps * 5
+    assert np.max(np.abs(host(g) - r["g"])) <= TOL * eps * 5
+    # with skipping: the iterates follow the oracle's sparse iteration; the two
+    # keep slightly different block sets, each within the certificate of the
+    # other's dense update, so per iteration they can drift by about
+    # eps * delta * exp(spread); compare after iterations from a warm start
+    fw, gw = _dense_converged(X, Y, a, b, eps, iters=200)
+    f = dev(fw)
+    g = dev(gw)
+    B.fs_bs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=3, delta=1e-4, warm_start=True)
+    torch.cuda.synchronize()
+    fo, go = obs.sinkhorn_sparse(X, Y, a, b, eps, 3, 1e-4, f0=fw, g0=gw)
+    assert np.max(np.abs(host(f) - fo)) <= TOL * eps * 3
+    assert np.max(np.abs(host(g) - go)) <= TOL * eps * 3
+
+
+def test_bs_solve_residual_stop():
+    import torch
+
+    B = _bind()
+    X, Y, a, b = _sorted_problem(41, 2000, 1800, 2)
+    eps = 0.02
+    p = _gpu_problem(X, Y, a, b)
+    f = torch.zeros(2000, device="cuda")
+    g = torch.zeros(1800, device="cuda")
+    info = B.fs_bs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=2000, delta=1e-5,
+                                  tol=1e-3, check_every=5)
+    assert info["residual"] <= 1e-3
+    res = oracle.marginal_residual(X, Y, a, b, host(f), host(g), eps)
+    assert res[0] + res[1] <= 2e-3
+
+
+def test_bs_argument_errors():
+    import torch
+
+    B = _bind()
+    rng = np.random.default_rng(51)
+    X = rng.normal(size=(300, 4)).astype(np.float32)
+    a = np.full(300, 1 / 300, np.float32)
+    p4 = B.fs_potentials_init(dev(X), dev(X), dev(a), dev(a))
+    assert B.fs_bs_workspace_bytes(p4) == 0
+    with pytest.raises(B.FsError):
+        B.fs_bs_attach(p4)
+    X3 = X[:, :3].copy()
+    pb = B.fs_potentials_init(dev(X3), dev(X3), dev(a), dev(a), prec="bf16")
+    with pytest.raises(B.FsError):
+        B.fs_bs_attach(pb)
+    p3 = B.fs_potentials_init(dev(X3), dev(X3), dev(a), dev(a))
+    f = torch.zeros(300, device="cuda")
+    with pytest.raises(B.FsError):  # not attached
+        B.fs_bs_lse_update_f(p3, 0.1, 1e-3, f, f, torch.empty_like(f))
+    B.fs_bs_attach(p3)
+    for delta in (-0.1, 1.0, float("nan")):
+        with pytest.raises(B.FsError):
+            B.fs_bs_lse_update_f(p3, 0.1, delta, f, f, torch.empty_like(f))
+    with pytest.raises(B.FsError):  # residual with in-place output
+        B.fs_bs_lse_update_f(p3, 0.1, 1e-3, f, f, f, row_resid=torch.empty(1, device="cuda"))
+    with pytest.raises(B.FsError):
+        B.fs_morton_sort(dev(np.zeros((10, 9), np.float32)))
