@@ -43,6 +43,15 @@ here is:
   every block of I would be skipped, the one with the largest bound is kept.
   With zero slopes H is minus the squared box gap
       gap2(I, J) = sum_c max(0, lo_Jc - hi_Ic, lo_Ic - hi_Jc)^2.
+  A second bound of the same form comes from the dot-product split of the
+  exponent, f_i + g_j - C_ij = phi_i + psi_j + 2 x_i.y_j with phi_i =
+  f_i - |x_i|^2, psi_j = g_j - |y_j|^2: the same fits and offsets taken of
+  phi and psi, and
+      H2(I, J) = max over the two boxes of (u2_I.x + v2_J.y + 2 x.y),
+  a bilinear function per coordinate, whose maximum over a rectangle is at a
+  corner.  The first form is tight where f is nearly linear over a block
+  (little displacement), the second where phi is (a map that concentrates
+  mass); beta is the smaller of the two bounds.
   The same rule with the roles of the clouds swapped screens the g-update
   (per column).
 * Retained-block update: f_i = -eps log sum over the kept blocks' keys of
@@ -52,7 +61,7 @@ here is:
 
 Pins (tests/test_oracle_blocksparse.py): bit interleaving against a
 recursive Z-order enumeration; quantisation endpoints, monotonicity and the
-degenerate axis; the box gap and H against brute-force maxima over the
+degenerate axis; the box gap, H and H2 against brute-force maxima over the
 blocks' points and a fine grid of the boxes; delta = 0 against the dense
 oracle update; the per-block mass bound against brute force on every
 skipped block; the certificate against the dense update.
@@ -161,6 +170,15 @@ def pair_bound(u, v, lo1, hi1, lo2, hi2) -> float:
     return float(sum(hmax1(u[c], v[c], lo1[c], hi1[c], lo2[c], hi2[c]) for c in range(len(u))))
 
 
+def bilinear_bound(u, v, lo1, hi1, lo2, hi2) -> float:
+    """H2 = max over the box pair of u.x + v.y + 2 x.y (corners, per coordinate)."""
+    tot = 0.0
+    for c in range(len(u)):
+        tot += max(u[c] * x + v[c] * y + 2.0 * x * y for x in (lo1[c], hi1[c])
+                   for y in (lo2[c], hi2[c]))
+    return float(tot)
+
+
 def screen(R, K, w_keys, pot_rows, pot_keys, eps: float, delta: float, BR: int = 256,
            BK: int = 32, return_bounds: bool = False):
     """Kept key blocks (ascending indices) of every row block, for the update
@@ -174,23 +192,30 @@ def screen(R, K, w_keys, pot_rows, pot_keys, eps: float, delta: float, BR: int =
     rlo, rhi = block_boxes(R, BR)
     klo, khi = block_boxes(K, BK)
     nbR, nbK = rlo.shape[0], klo.shape[0]
-    U, c = [], []
+    U, c, U2, c2 = [], [], [], []
     for I in range(nbR):
         P, f = R[I * BR:(I + 1) * BR], pot_rows[I * BR:(I + 1) * BR]
+        phi = f - (P * P).sum(axis=1)
         U.append(slope(P, f))
         c.append((f - P @ U[-1]).max())
-    V, G = [], []
+        U2.append(slope(P, phi))
+        c2.append((phi - P @ U2[-1]).max())
+    V, G, V2, G2 = [], [], [], []
     for J in range(nbK):
         Q, g, w = K[J * BK:(J + 1) * BK], pot_keys[J * BK:(J + 1) * BK], w_keys[J * BK:(J + 1) * BK]
+        psi = g - (Q * Q).sum(axis=1)
         V.append(slope(Q, g))
         G.append(_lse(np.log(w) + (g - Q @ V[-1]) / eps))
+        V2.append(slope(Q, psi))
+        G2.append(_lse(np.log(w) + (psi - Q @ V2[-1]) / eps))
     thr = np.log(delta / nbK) if delta > 0 else -np.inf
     beta = np.empty((nbR, nbK))
     lists = []
     for I in range(nbR):
         for J in range(nbK):
             H = pair_bound(U[I], V[J], rlo[I], rhi[I], klo[J], khi[J])
-            beta[I, J] = c[I] / eps + G[J] + H / eps
+            H2 = bilinear_bound(U2[I], V2[J], rlo[I], rhi[I], klo[J], khi[J])
+            beta[I, J] = min(c[I] / eps + G[J] + H / eps, c2[I] / eps + G2[J] + H2 / eps)
         keep = np.nonzero(beta[I] >= thr)[0]
         if keep.size == 0:
             keep = np.array([int(np.argmax(beta[I]))])

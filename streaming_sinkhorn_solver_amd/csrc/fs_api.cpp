@@ -56,10 +56,12 @@ struct fs_problem {
     int bs_nbR[2] = {0, 0}, bs_nbK[2] = {0, 0}, bs_cap[2] = {0, 0};
     float4* bs_rbox[2] = {nullptr, nullptr};  // [nbR][2] (lo, hi) of 256-row blocks
     float4* bs_kbox[2] = {nullptr, nullptr};  // [nbK][2] of 32-key blocks
-    float4* bs_rfit = nullptr;                // per pass: (u, c) of the row blocks
-    float4* bs_kfit = nullptr;                // per pass: (v, G) of the key blocks
+    float4* bs_rfit = nullptr;                // per pass: [2] fits (u, c) of the row blocks
+    float4* bs_kfit = nullptr;                // per pass: [2] fits (v, G) of the key blocks
     int* bs_cnt[2] = {nullptr, nullptr};      // kept blocks per row block, last pass of a side
+    int* bs_best = nullptr;                   // per row block: the block of largest bound
     int* bs_list = nullptr;                   // kept blocks of the last pass
+    float2* bs_part = nullptr;                // [kBsMaxSplit][max(n, m)] partials
     int bs_last_side = -1;
     float bs_mag = 1.f;                       // coordinate magnitude of the rounding margin
 };
@@ -1028,6 +1030,12 @@ namespace {
 // Block-sparse low-dimensional form ("FlashSinkhorn 2" explainer, sections on
 // cutting space and on guaranteeing the skip; see fs_bsparse.hip).
 
+// Workgroups per row block of the block-sparse pass: the lists' tiles are
+// dealt to S workgroups so that about 2048 are launched (uneven list lengths
+// then even out over several rounds of the 256 compute units).
+constexpr int kBsMaxSplit = 8;
+int bs_splits(int nbR) { return std::max(1, std::min(kBsMaxSplit, (2048 + nbR - 1) / nbR)); }
+
 fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, const float* cur,
                           const float* other, float* out, float* resid, hipStream_t s,
                           hipEvent_t eb, hipEvent_t ee) {
@@ -1047,8 +1055,8 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
     const float thr2 = delta > 0.f ? (float)std::log2((double)delta / (double)nbK) : -INFINITY;
     const int sentinel = (int)(K.n_pad / 32);
     if ((e = launch_screen(p->bs_rbox[side], p->bs_rfit, nbR, p->bs_kbox[side], p->bs_kfit, nbK,
-                           c_bias, thr2, p->bs_mag, p->bs_list, p->bs_cnt[side], p->bs_cap[side],
-                           sentinel, s)) != hipSuccess)
+                           c_bias, thr2, p->bs_mag, p->bs_list, p->bs_cnt[side], p->bs_best,
+                           p->bs_cap[side], sentinel, s)) != hipSuccess)
         return hip_fail(e, "screening launch");
     p->bs_last_side = side;
     LseArgs a = base_args(p, f_side, eps);
@@ -1057,11 +1065,13 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
     a.mode = 0;
     a.cur = resid ? cur : nullptr;
     a.resid_out = resid;
-    a.n_split = 1;
+    a.n_split = bs_splits(nbR);
+    a.part = p->bs_part;
     a.keys_per_split = (int)K.n_pad;
     a.krec_keys = (int)K.n_pad + 32;
     a.bs_list = p->bs_list;
     a.bs_count = p->bs_cnt[side];
+    a.bs_best = p->bs_best;
     a.bs_cap = p->bs_cap[side];
     a.bs_sentinel = sentinel;
     if ((e = launch_lse(p->path, a, s, eb, ee)) != hipSuccess)
@@ -1070,7 +1080,7 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
 }
 
 struct BsLayout {
-    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], list, total;
+    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], best, list, part, total;
 };
 
 BsLayout bs_layout(const fs_problem* p) {
@@ -1089,10 +1099,12 @@ BsLayout bs_layout(const fs_problem* p) {
         L.kbox[q] = take(sizeof(float4) * 2 * nbK[q]);
         L.cnt[q] = take(sizeof(int) * nbR[q]);
     }
-    L.rfit = take(sizeof(float4) * std::max(nbR[0], nbR[1]));
-    L.kfit = take(sizeof(float4) * std::max(nbK[0], nbK[1]));
+    L.rfit = take(sizeof(float4) * 2 * std::max(nbR[0], nbR[1]));
+    L.best = take(sizeof(int) * std::max(nbR[0], nbR[1]));
+    L.kfit = take(sizeof(float4) * 2 * std::max(nbK[0], nbK[1]));
     const int64_t cap0 = (nbK[0] + 15) / 16 * 16, cap1 = (nbK[1] + 15) / 16 * 16;
     L.list = take(sizeof(int) * (size_t)std::max(nbR[0] * cap0, nbR[1] * cap1));
+    L.part = take(sizeof(float2) * kBsMaxSplit * (size_t)std::max(n, m));
     L.total = o;
     return L;
 }
@@ -1182,6 +1194,8 @@ fs_status fs_bs_attach(fs_problem* p, void* workspace, size_t workspace_bytes, v
     p->bs_rfit = (float4*)(w + L.rfit);
     p->bs_kfit = (float4*)(w + L.kfit);
     p->bs_list = (int*)(w + L.list);
+    p->bs_part = (float2*)(w + L.part);
+    p->bs_best = (int*)(w + L.best);
     p->bs_last_side = -1;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;

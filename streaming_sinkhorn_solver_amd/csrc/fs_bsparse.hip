@@ -21,9 +21,15 @@
 //   beta(I, J) = (c_I + H(I, J)) c_bias + G_J   (base 2),
 //
 // so that for every row i of I the mass of J relative to the row's target,
-// sum_{j in J} b_j exp((f_i + g_j - C_ij)/eps), is at most 2^beta.  J is kept
-// for I when beta >= log2(delta / N_J) (less a rounding margin), so the
-// skipped mass of a row stays below delta * a_i.
+// sum_{j in J} b_j exp((f_i + g_j - C_ij)/eps), is at most 2^beta.  A second
+// bound of the same kind comes from the dot-product split of the exponent,
+// f_i + g_j - C_ij = phi_i + psi_j + 2 x_i.y_j (phi = f - |x|^2, psi =
+// g - |y|^2): the fits taken of phi and psi, and H2 = max over the boxes of
+// u2.x + v2.y + 2 x.y, bilinear per coordinate, at a corner.  The first is
+// tight where f is nearly linear over a block, the second where phi is (a map
+// that concentrates mass); beta is the smaller.  J is kept for I when
+// beta >= log2(delta / N_J) (less a rounding margin), so the skipped mass of
+// a row stays below delta * a_i.
 //
 // Layout: row blocks are the 256 rows of one workgroup of the streaming
 // kernel, key blocks the 32 keys of one matrix-core block.  Per-block boxes
@@ -343,9 +349,10 @@ __global__ __launch_bounds__(256) void block_box_kernel(const float* __restrict_
     }
 }
 
-// Per-block fit of a potential.  Row side (KEY = false): (u, c) with c the
-// maximum of pot_i - u.x_i.  Key side (KEY = true): (v, G) with G the base-2
-// log-sum of lw2_j + (pot_j - v.y_j) c_bias.
+// Per-block fits of a potential p and of p - |x|^2 (the two forms of the
+// bound), written as fit[2*blk] and fit[2*blk+1].  Row side (KEY = false):
+// (u, c) with c the maximum of value_i - u.x_i.  Key side (KEY = true):
+// (v, G) with G the base-2 log-sum of lw2_j + (value_j - v.y_j) c_bias.
 template <int GS, bool KEY>
 __global__ __launch_bounds__(256) void block_fit_kernel(const float* __restrict__ ops,
                                                         const float* __restrict__ centre, int d,
@@ -363,31 +370,39 @@ __global__ __launch_bounds__(256) void block_fit_kernel(const float* __restrict_
         load_point(ops, centre, d, i, x);
         p = pot[i];
     }
-    float s1[5] = {valid ? x[0] : 0.f, valid ? x[1] : 0.f, valid ? x[2] : 0.f, p,
-                   valid ? 1.f : 0.f};
+    const float q = p - (x[0] * x[0] + x[1] * x[1] + x[2] * x[2]);  // p - |x|^2
+    float s1[6] = {valid ? x[0] : 0.f, valid ? x[1] : 0.f, valid ? x[2] : 0.f,
+                   valid ? p : 0.f,    valid ? q : 0.f,    valid ? 1.f : 0.f};
     group_sum<GS>(s1, red);
-    const float inv = s1[4] > 0.f ? 1.f / s1[4] : 0.f;
+    const float inv = s1[5] > 0.f ? 1.f / s1[5] : 0.f;
     const float cx = x[0] - s1[0] * inv, cy = x[1] - s1[1] * inv, cz = x[2] - s1[2] * inv;
-    const float cp = p - s1[3] * inv;
-    float S[9] = {cx * cx, cy * cy, cz * cz, cx * cy, cx * cz, cy * cz, cx * cp, cy * cp, cz * cp};
+    const float cp = p - s1[3] * inv, cq = q - s1[4] * inv;
+    float S[12] = {cx * cx, cy * cy, cz * cz, cx * cy, cx * cz, cy * cz,
+                   cx * cp, cy * cp, cz * cp, cx * cq, cy * cq, cz * cq};
     if (!valid)
 #pragma unroll
-        for (int q = 0; q < 9; ++q) S[q] = 0.f;
+        for (int k = 0; k < 12; ++k) S[k] = 0.f;
     group_sum<GS>(S, red);
-    float u[3];
-    solve_slope(S, u);
-    const float r = p - (u[0] * x[0] + u[1] * x[1] + u[2] * x[2]);
-    float out;
-    if constexpr (!KEY) {
-        out = group_max<GS>(valid ? r : -INFINITY, red);
-    } else {
-        const float z = valid ? fmaf(r, c_bias, lw2[i]) : -INFINITY;
-        const float M = group_max<GS>(z, red);
-        float e[1] = {M > -INFINITY ? ex2(z - M) : 0.f};
-        group_sum<GS>(e, red);
-        out = M > -INFINITY ? M + lg2(e[0]) : -INFINITY;
+#pragma unroll
+    for (int form = 0; form < 2; ++form) {
+        const float Sf[9] = {S[0], S[1], S[2], S[3], S[4], S[5], S[6 + 3 * form],
+                             S[7 + 3 * form], S[8 + 3 * form]};
+        float u[3];
+        solve_slope(Sf, u);
+        const float r = (form ? q : p) - (u[0] * x[0] + u[1] * x[1] + u[2] * x[2]);
+        float out;
+        if constexpr (!KEY) {
+            out = group_max<GS>(valid ? r : -INFINITY, red);
+        } else {
+            const float z = valid ? fmaf(r, c_bias, lw2[i]) : -INFINITY;
+            const float M = group_max<GS>(z, red);
+            float e[1] = {M > -INFINITY ? ex2(z - M) : 0.f};
+            group_sum<GS>(e, red);
+            out = M > -INFINITY ? M + lg2(e[0]) : -INFINITY;
+        }
+        if ((threadIdx.x % GS) == 0 && blk < nb)
+            fit[2 * blk + form] = make_float4(u[0], u[1], u[2], out);
     }
-    if ((threadIdx.x % GS) == 0 && blk < nb) fit[blk] = make_float4(u[0], u[1], u[2], out);
 }
 
 // ---------------------------------------------------------------- screening
@@ -407,11 +422,17 @@ __device__ __forceinline__ float hmax1(float u, float v, float a1, float b1, flo
                  fmaxf(hq(u, v, x3, a2), hq(u, v, x4, b2)));
 }
 
+// max of u x + v y + 2 x y over x in [a1, b1], y in [a2, b2] (a corner)
+__device__ __forceinline__ float bmax1(float u, float v, float a1, float b1, float a2, float b2) {
+    auto h = [&](float x, float y) { return fmaf(u, x, fmaf(v, y, 2.f * x * y)); };
+    return fmaxf(fmaxf(h(a1, a2), h(a1, b2)), fmaxf(h(b1, a2), h(b1, b2)));
+}
+
 struct ScreenArgs {
     const float4* rbox;  // [nbR][2]
-    const float4* rfit;  // [nbR]: (u, c)
+    const float4* rfit;  // [nbR][2]: (u, c) of f and of f - |x|^2
     const float4* kbox;  // [nbK][2]
-    const float4* kfit;  // [nbK]: (v, G)
+    const float4* kfit;  // [nbK][2]: (v, G) of g and of g - |y|^2
     int nbR, nbK;
     float c_bias;
     float thr2;          // log2(delta / nbK), -inf for delta = 0
@@ -419,6 +440,7 @@ struct ScreenArgs {
     float mag;           // magnitude of the coordinates (1 + max |coordinate|^2 sum)
     int* list;           // [nbR][cap]
     int* count;          // [nbR]
+    int* best;           // [nbR]: the key block of largest bound
     int cap;
     int sentinel;
 };
@@ -430,9 +452,10 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
     const int I = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const float4 rlo = a.rbox[2 * I], rhi = a.rbox[2 * I + 1];
-    const float4 rf = a.rfit[I];
-    const float base2 = rf.w * a.c_bias;
-    const float thr = a.thr2 - a.margin_rel * a.c_bias * (a.mag + fabsf(rf.w));
+    const float4 rf = a.rfit[2 * I], rq = a.rfit[2 * I + 1];
+    const float base2 = rf.w * a.c_bias, baseq = rq.w * a.c_bias;
+    const float thr =
+        a.thr2 - a.margin_rel * a.c_bias * (a.mag + fmaxf(fabsf(rf.w), fabsf(rq.w)));
     int* __restrict__ out = a.list + (int64_t)I * a.cap;
     const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     int count = 0;
@@ -442,12 +465,16 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
         const int J = J0 + tid;
         bool keep = false;
         if (J < a.nbK) {
-            const float4 kf = a.kfit[J];
+            const float4 kf = a.kfit[2 * J], kq = a.kfit[2 * J + 1];
             const float4 klo = a.kbox[2 * J], khi = a.kbox[2 * J + 1];
             const float H = hmax1(rf.x, kf.x, rlo.x, rhi.x, klo.x, khi.x) +
                             hmax1(rf.y, kf.y, rlo.y, rhi.y, klo.y, khi.y) +
                             hmax1(rf.z, kf.z, rlo.z, rhi.z, klo.z, khi.z);
-            const float beta = fmaf(H, a.c_bias, base2) + kf.w;
+            const float H2 = bmax1(rq.x, kq.x, rlo.x, rhi.x, klo.x, khi.x) +
+                             bmax1(rq.y, kq.y, rlo.y, rhi.y, klo.y, khi.y) +
+                             bmax1(rq.z, kq.z, rlo.z, rhi.z, klo.z, khi.z);
+            const float beta =
+                fminf(fmaf(H, a.c_bias, base2) + kf.w, fmaf(H2, a.c_bias, baseq) + kq.w);
             keep = beta >= thr;
             if (beta > best) {
                 best = beta;
@@ -466,8 +493,9 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
         count += tot;
         __syncthreads();
     }
-    if (count == 0) {
-        // keep the block of largest bound (first on ties)
+    {
+        // the block of largest bound (first on ties): where the streaming
+        // kernel takes its rows' starting reference; kept if nothing else is
         float b = best;
         int j = bestJ;
 #pragma unroll
@@ -492,9 +520,10 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
                     bb = bred[q];
                     jj = jred[q];
                 }
-            out[0] = jj;
+            a.best[I] = jj;
+            if (count == 0) out[0] = jj;
         }
-        count = 1;
+        if (count == 0) count = 1;
     }
     const int padded = (count + 15) / 16 * 16;
     for (int k = count + tid; k < padded; k += 256) out[k] = a.sentinel;
@@ -603,7 +632,7 @@ hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_
 
 hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const float4* kbox,
                          const float4* kfit, int nbK, float c_bias, float thr2, float mag,
-                         int* list, int* count, int cap, int sentinel, hipStream_t s) {
+                         int* list, int* count, int* best, int cap, int sentinel, hipStream_t s) {
     ScreenArgs a;
     a.rbox = rbox;
     a.rfit = rfit;
@@ -617,6 +646,7 @@ hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const 
     a.mag = mag;
     a.list = list;
     a.count = count;
+    a.best = best;
     a.cap = cap;
     a.sentinel = sentinel;
     screen_kernel<<<nbR, 256, 0, s>>>(a);

@@ -83,9 +83,12 @@ struct LseArgs {
     // block-sparse form (PATH_SMALL, d <= 3; see fs_bsparse.hip): per row
     // block of 256 rows, the kept 32-key blocks [row blocks][bs_cap] padded to
     // whole tiles of 16 with bs_sentinel (the block of -inf records right
-    // after the padded keys), and their count.  NULL: the dense pass.
+    // after the padded keys), and their count.  NULL: the dense pass.  With
+    // n_split = S > 1, workgroup s of a row block takes the list's tiles
+    // s, s + S, s + 2S, .. and writes a partial (M, s) like a key-range split.
     const int* bs_list;
     const int* bs_count;
+    const int* bs_best;  // per row block: the block whose scores set the starting reference
     int bs_cap;
     int bs_sentinel;
 };
@@ -205,8 +208,9 @@ size_t small_f16_rec_bytes(int d);  // per key (0 if d > 4)
 // Largest L1 norm over the (converted, fp32) points of a cloud into *out.
 hipError_t launch_row_l1max(const float* ops, int64_t n, int d, float* out, hipStream_t s);
 hipError_t launch_lse_small(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin);
-// the block-sparse form (a.bs_list set, a.n_split == 1, d <= 3; the key
-// records must hold the sentinel block: a.krec_keys = padded keys + 32)
+// the block-sparse form (a.bs_list set, d <= 3; the key records must hold the
+// sentinel block: a.krec_keys = padded keys + 32; a.part must hold
+// a.n_split * n_rows partials when a.n_split > 1)
 hipError_t launch_lse_small_sparse(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin);
 
 // ---- block-sparse low-dimensional path (fs_bsparse.hip) ----
@@ -225,15 +229,18 @@ hipError_t launch_unpermute(const float* src, const int32_t* perm, int64_t n, in
 // stored as centred fp32 rows of 4 (plus its centre).
 hipError_t launch_block_boxes(const float* ops, const float* centre, int d, int64_t n, int gs,
                               float4* box, hipStream_t s);
-// Per-block linear fit of a potential: rows (gs 256, key false) -> (u, c),
-// keys (gs 32, key true) -> (v, G) with G in base 2 (uses lw2 and c_bias).
+// Per-block linear fits of a potential p and of p - |x|^2 into fit[2*blk]
+// and fit[2*blk+1]: rows (gs 256, key false) -> (u, c), keys (gs 32, key
+// true) -> (v, G) with G in base 2 (uses lw2 and c_bias).
 hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_t n, int gs,
                             bool key, const float* pot, const float* lw2, float c_bias,
                             float4* fit, hipStream_t s);
-// Kept key blocks of every row block (threshold thr2 = log2(delta / nbK)).
+// Kept key blocks of every row block (threshold thr2 = log2(delta / nbK)),
+// their count, and the key block of largest bound.
 hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const float4* kbox,
                          const float4* kfit, int nbK, float c_bias, float thr2, float mag,
-                         int* list, int* count, int cap, int sentinel, hipStream_t s);
+                         int* list, int* count, int* best, int cap, int sentinel,
+                         hipStream_t s);
 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
 // Matrix paths: the streaming transport kernel serves operand rows of up to

@@ -171,7 +171,8 @@ __device__ __forceinline__ void sload_words(const int* p, int (&o)[N]) {
 // range but the 32-key blocks listed for its row block by the screening
 // (LseArgs::bs_list, padded to whole tiles with a block of -inf records);
 // a tile gathers 16 listed blocks, each wave-wide copy instruction fetching
-// whole blocks at per-lane offsets.  No key-range split.
+// whole blocks at per-lane offsets.  With n_split = S the list's tiles are
+// dealt round-robin to S workgroups (partials merged as for key ranges).
 template <int KP, bool SPARSE = false>
 __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs a) {
     constexpr int W = kSmallWaves;
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     constexpr int F16_TILE = HAS_F16 ? TK * kF16RecBytes : 0;
     constexpr int BUF_BYTES = F16_TILE > F32_TILE ? F16_TILE : F32_TILE;
     __shared__ __attribute__((aligned(16))) uint4 tbuf[kNbuf][BUF_BYTES / 16];
+    __shared__ __attribute__((aligned(16))) uint4 ibuf[SPARSE ? 64 : 1];  // sparse: starting block
     __shared__ float red[16];
 
     const int tid = threadIdx.x;
@@ -194,9 +196,17 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     constexpr int SUB_BLOCKS = TK / 32;  // 32-key blocks per tile
     const int j0 = SPARSE ? 0 : split * a.keys_per_split;
     const int j1 = min(a.n_keys, j0 + a.keys_per_split);
-    const int* __restrict__ lst = SPARSE ? a.bs_list + (int64_t)row_block * a.bs_cap : nullptr;
-    const int ntiles = SPARSE ? (a.bs_count[row_block] + SUB_BLOCKS - 1) / SUB_BLOCKS
-                              : (j1 - j0 + TK - 1) / TK;
+    // sparse: this workgroup's tiles are list tiles split, split + S, ..
+    const int* __restrict__ lst =
+        SPARSE ? a.bs_list + (int64_t)row_block * a.bs_cap + split * SUB_BLOCKS : nullptr;
+    const int list_step = SPARSE ? a.n_split * SUB_BLOCKS : 0;
+    int ntiles;
+    if constexpr (SPARSE) {
+        const int all = (a.bs_count[row_block] + SUB_BLOCKS - 1) / SUB_BLOCKS;
+        ntiles = all > split ? (all - split + a.n_split - 1) / a.n_split : 0;
+    } else {
+        ntiles = (j1 - j0 + TK - 1) / TK;
+    }
     const int d = a.dp;
     const int stride = d <= 4 ? 4 : 8;
     const float* __restrict__ xr = (const float*)a.rows + (int64_t)row * stride;
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
                         constexpr int LPB = 64 / BPI;
                         static_assert(1024 % BLK == 0, "whole blocks per instruction");
                         int ent[BPI];
-                        sload_words<BPI>(lst + k * SUB_BLOCKS + L * BPI, ent);
+                        sload_words<BPI>(lst + k * list_step + L * BPI, ent);
                         int J = ent[0];
 #pragma unroll
                         for (int q = 1; q < BPI; ++q)
@@ -309,6 +319,17 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
                 }
             }
         };
+        if constexpr (SPARSE) {
+            // the block of largest bound, for the starting reference
+            if (ntiles > 0 && wave == 0) {
+                constexpr int LPB = 64 / (1024 / (32 * REC_BYTES));
+                int ent[1];
+                sload_words<1>(a.bs_best + row_block, ent);
+                const uint32_t Jc = min((uint32_t)ent[0], (uint32_t)a.bs_sentinel);
+                dma_to_lds16(recs, Jc * (uint32_t)(32 * REC_BYTES) + (uint32_t)(lane % LPB) * 16u,
+                             &ibuf[0]);
+            }
+        }
         if (ntiles > 0) {
 #pragma unroll
             for (int k = 0; k < kNbuf - 1; ++k) issue_tile(min(k, ntiles - 1), k);
@@ -361,10 +382,11 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
 
         // R starts at the maximum of the first 32-key block (finite wherever
         // the lane sees a key at all; a lane that never does keeps s = 0, the
-        // empty state).
+        // empty state); in the sparse form, of the block of largest bound,
+        // whose scores are near the row maxima, so that R rarely moves.
         if (ntiles > 0) {
             f32x16 acc;
-            scores((const char*)&tbuf[0][0], acc);
+            scores(SPARSE ? (const char*)&ibuf[0] : (const char*)&tbuf[0][0], acc);
             const float t = block_max(acc);
             R = t > -INFINITY ? t : 0.f;
         }
@@ -438,7 +460,7 @@ hipError_t small_launch(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
         a.key_lw2, a.c_bias, a.krec, f16 ? (_Float16*)a.krec16 : nullptr, (Guard*)a.krec_guard);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-    const dim3 grid((a.n_rows + kSmallWaves * 32 - 1) / (kSmallWaves * 32), SPARSE ? 1 : a.n_split);
+    const dim3 grid((a.n_rows + kSmallWaves * 32 - 1) / (kSmallWaves * 32), a.n_split);
     lse_small_kernel<KP, SPARSE><<<grid, kSmallWaves * 64, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -473,7 +495,8 @@ size_t small_f32_rec_bytes(int d) { return (size_t)f32_rec_bytes(small_kp(d)); }
 size_t small_f16_rec_bytes(int d) { return small_kp(d) <= 2 ? (size_t)kF16RecBytes : 0; }
 
 hipError_t launch_lse_small_sparse(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
-    if (a.n_split != 1 || !a.bs_list || !a.bs_count) return hipErrorInvalidValue;
+    if (a.n_split < 1 || !a.bs_list || !a.bs_count || (a.n_split > 1 && !a.part))
+        return hipErrorInvalidValue;
     switch (small_kp(a.dp)) {
         case 1: return small_launch<1, true>(a, s, ev_begin);
         case 2: return small_launch<2, true>(a, s, ev_begin);

@@ -9,9 +9,10 @@ B1  bit interleaving against a recursive Z-order enumeration of the grid
 B2  quantisation: the box corners map to cells 0 and 2^B - 1, cells are
     monotone in each coordinate, a flat axis maps to 0, ties keep index order;
 B3  the box gap is a lower bound of every pair cost of two blocks (brute
-    force) and exact for one-point blocks; the pair bound H (the maximum of
-    u.x + v.y - |x - y|^2 over two boxes) is above its value at every pair of
-    points and every point of a fine grid of the boxes, and attained on it;
+    force) and exact for one-point blocks; the pair bounds H (the maximum of
+    u.x + v.y - |x - y|^2 over two boxes) and H2 (of u.x + v.y + 2 x.y) are
+    above their values at every pair of points and every point of a fine
+    grid of the boxes, and attained on it;
 B4  delta = 0 keeps every block: the update equals the dense oracle update;
 B5  every skipped block's true mass (brute force over its pairs) is below
     delta / N_J of the row's target, so the skipped mass of a row is below
@@ -129,8 +130,19 @@ def test_b3_pair_bound_is_the_box_maximum():
         H = bs.pair_bound(u, v, P.min(0), P.max(0), Q.min(0), Q.max(0))
         vals = P @ u[:, None] + (Q @ v)[None, :] - ((P[:, None] - Q[None]) ** 2).sum(-1)
         assert H >= vals.max() - 1e-12
-    # one-point boxes: the bound is the value itself
+    for _ in range(300):
+        u, v = rng.normal(0, 2, 2)
+        a1, a2 = rng.uniform(-1, 1, 2)
+        b1, b2 = a1 + rng.uniform(0, 1.5), a2 + rng.uniform(0, 1.5)
+        h = bs.bilinear_bound([u], [v], [a1], [b1], [a2], [b2])
+        x = np.linspace(a1, b1, 201)[:, None]
+        y = np.linspace(a2, b2, 201)[None, :]
+        assert h == pytest.approx((u * x + v * y + 2 * x * y).max(), abs=1e-12)
+    # one-point boxes: the bounds are the values themselves
     p, q = rng.standard_normal(3), rng.standard_normal(3)
+    u, v = rng.normal(0, 1, 3), rng.normal(0, 1, 3)
+    assert bs.bilinear_bound(u, v, p, p, q, q) == pytest.approx(u @ p + v @ q + 2 * p @ q,
+                                                               abs=1e-12)
     u, v = rng.normal(0, 1, 3), rng.normal(0, 1, 3)
     assert bs.pair_bound(u, v, p, p, q, q) == pytest.approx(u @ p + v @ q - ((p - q) ** 2).sum(),
                                                            abs=1e-12)
