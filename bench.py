@@ -10,7 +10,15 @@ transport product (here the barycentric projection P.Y / a).
 
 ``--workload c1|c2|c4|c5`` runs one of the other recipes the same way (its own
 sizes, precision, schedule and transport), for measurements beside the
-headline line.
+headline line.  ``--workload fs2`` measures the block-sparse form
+(fs_bs_*) on two uniform samples of 250k points in the unit cube at
+eps = (mean spacing)^2: the clouds are Morton-ordered and the solve annealed
+to the final eps once (untimed, reported in `setup_ms`); a step restores that
+warm start and runs 10 block-sparse iterations (fits, screening, the
+retained-block LSE passes), `value` being those iterations per second.  Its
+`block_sparse` field reports the kept share of block pairs per side, the
+dense path's rate on the same potentials and the certificate bound; the c5
+line carries the same field for its own clouds and eps.
 
 Prints one JSON line with
   value      Sinkhorn iterations per second over whole steps
@@ -58,7 +66,9 @@ CSRC = os.path.join(HERE, "streaming_sinkhorn_solver_amd", "csrc")
 EXP_PEAK = 256 * 32 * 2.4e9 / 1e12  # T exponentials/s
 
 # recipe -> the fs_probe_peak kind of its bounding unit
-PROBES = {"c1": "exp", "c2": "mfma-fp32", "c3": "mfma-bf16", "c4": "mfma-fp16", "c5": "exp"}
+PROBES = {"c1": "exp", "c2": "mfma-fp32", "c3": "mfma-bf16", "c4": "mfma-fp16", "c5": "exp",
+          "fs2": "exp"}
+BS_DELTA = 1e-3  # skipped mass per row / column below this share of its target
 
 # recipe -> (score precision, roofline peak, unit, dtype label, description)
 RECIPES = {
@@ -77,7 +87,98 @@ RECIPES = {
     "c5": ("auto", EXP_PEAK, "Texp/s", "f32",
            "n=m=250000, d=3, X uniform in the unit cube, Y an 8-component mixture (std 0.05), "
            "uniform weights, eps=0.01, 10 iterations (seed 5)"),
+    "fs2": ("auto", EXP_PEAK, "Texp/s", "f32",
+            "n=m=250000, d=3, two independent uniform samples of the unit cube, uniform "
+            "weights, eps=n^(-2/3) (entropic blur = mean spacing), block-sparse form with "
+            "delta=1e-3: Morton order, annealed warm start 0.1 -> eps over 12 stages x 10 "
+            "(untimed), then 10 timed block-sparse iterations per step (seed 6)"),
 }
+
+
+def block_sparse_run(w, eps, steps, warmup, dev, binding, torch):
+    """Block-sparse form on the workload's clouds at `eps`: Morton order,
+    problem, annealed warm start (0.1 -> eps, 12 x 10, block-sparse), then
+    `steps` timed steps of 10 block-sparse iterations each from that warm
+    start; the dense path's 10 iterations from the same start beside it."""
+    import numpy as np
+
+    X = torch.from_numpy(w.X).to(dev)
+    Y = torch.from_numpy(w.Y).to(dev)
+    a = torch.from_numpy(w.a).to(dev)
+    b = torch.from_numpy(w.b).to(dev)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    Xs, a_s, px = binding.fs_morton_sort(X, a)
+    Ys, b_s, py = binding.fs_morton_sort(Y, b)
+    e[1].record()
+    f0 = torch.zeros(w.n, device=dev)
+    g0 = torch.zeros(w.m, device=dev)
+    p = binding.fs_potentials_init(Xs, Ys, a_s, b_s, f=f0, g=g0)
+    binding.fs_bs_attach(p)
+    e[2].record()
+    binding.fs_bs_sinkhorn_solve(p, f0, g0, eps_end=eps, eps_start=0.1, n_stages=12,
+                                 iters_per_stage=10, delta=BS_DELTA)
+    e[3].record()
+    torch.cuda.synchronize()
+    setup = {"morton_sort_ms": round(e[0].elapsed_time(e[1]), 3),
+             "init_attach_ms": round(e[1].elapsed_time(e[2]), 3),
+             "anneal_ms": round(e[2].elapsed_time(e[3]), 3)}
+    f, g = f0.clone(), g0.clone()
+    lse = {"ms": 0.0, "n": 0}
+
+    def bs_step(timed):
+        f.copy_(f0)
+        g.copy_(g0)
+        info = binding.fs_bs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=10,
+                                            delta=BS_DELTA, warm_start=True, time_kernels=timed)
+        if timed:
+            lse["ms"] += info["lse_ms"]
+            lse["n"] += info["lse_launches"]
+
+    for _ in range(warmup):
+        bs_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bs_step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kept = {}
+    pairs_per_iter = 0.0
+    for side, name in ((0, "f"), (1, "g")):
+        cnt = binding.fs_bs_read_screen(p, side)
+        sh = binding.fs_bs_shape(p, side)
+        kept[name] = round(float(cnt.sum()) / (sh["row_blocks"] * sh["key_blocks"]), 5)
+        pairs_per_iter += float(cnt.sum()) * 32 * 256  # kept block pairs x pairs per block
+    res = torch.zeros(2, device=dev)
+    binding.fs_marginal_residual(p, eps, f, g, res)
+    # the dense path, same potentials, same iterations
+    fd, gd = f0.clone(), g0.clone()
+    binding.fs_sinkhorn_solve(p, fd, gd, eps_end=eps, iters_per_stage=10, warm_start=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fd.copy_(f0)
+    gd.copy_(g0)
+    binding.fs_sinkhorn_solve(p, fd, gd, eps_end=eps, iters_per_stage=10, warm_start=True)
+    torch.cuda.synchronize()
+    dense_it_s = 10 / (time.perf_counter() - t1)
+    it_s = 10 * steps / dt
+    lse_mean_ms = lse["ms"] / max(lse["n"], 1)
+    diff = float((f - fd).abs().max()) / eps
+    r = res.cpu().numpy()
+    return {
+        "iters_per_s": round(it_s, 3), "ms_per_iter": round(dt / (10 * steps) * 1e3, 4),
+        "dense_iters_per_s": round(dense_it_s, 3), "speedup_vs_dense": round(it_s / dense_it_s, 3),
+        "eps": eps, "delta": BS_DELTA, "kept_block_pairs": kept,
+        "kept_pairs_per_iter": pairs_per_iter,
+        "lse_mean_launch_ms": round(lse_mean_ms, 4), "lse_launches": lse["n"],
+        "dense_marginal_residual_after": [float(r[0]), float(r[1])],
+        "max_abs_f_minus_dense_over_eps": round(diff, 4),
+        "setup": setup,
+        "what": "10 block-sparse iterations from the annealed warm start (per-block fits, "
+                "screening, retained-block LSE passes) vs 10 dense iterations from the same "
+                "start; kept shares are of the last screening of each side",
+    }
 
 
 def file_sha(*names) -> str:
@@ -90,7 +191,7 @@ def file_sha(*names) -> str:
 
 def kernel_source_sha(workload: str = "c3") -> str:
     """Hash of the source of the recipe's streaming LSE kernel."""
-    return file_sha("fs_lse_small.hip" if workload in ("c1", "c5") else "fs_lse.hip")
+    return file_sha("fs_lse_small.hip" if workload in ("c1", "c5", "fs2") else "fs_lse.hip")
 
 
 def traffic_file(workload: str) -> str:
@@ -114,6 +215,27 @@ def counter_mode(w, prec: str, half_steps: int = 6) -> None:
     X, Y, a, b = (torch.from_numpy(v).to(dev) for v in (w.X, w.Y, w.a, w.b))
     f = torch.empty(w.n, device=dev)
     g = torch.empty(w.m, device=dev)
+    if w.name == "fs2":
+        # Morton order, a dense annealed warm start (no block-sparse launch
+        # before the counted ones), then the block-sparse half-steps
+        Xs, a_s, _ = binding.fs_morton_sort(X, a)
+        Ys, b_s, _ = binding.fs_morton_sort(Y, b)
+        p = binding.fs_potentials_init(Xs, Ys, a_s, b_s, f=f, g=g)
+        binding.fs_bs_attach(p)
+        binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, eps_start=w.eps_start,
+                                  n_stages=w.n_stages, iters_per_stage=w.iters)
+        f2, g2 = torch.empty_like(f), torch.empty_like(g)
+        for k in range(half_steps):
+            if k % 2 == 0:
+                binding.fs_bs_lse_update_f(p, w.eps, BS_DELTA, g, f, f2)
+                f, f2 = f2, f
+            else:
+                binding.fs_bs_lse_update_g(p, w.eps, BS_DELTA, f, g, g2)
+                g, g2 = g2, g
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_mode": "done", "half_steps": half_steps,
+                          "copy_bytes": float(1 << 30)}), flush=True)
+        return
     p = binding.fs_potentials_init(X, Y, a, b, prec=prec, f=f, g=g)
     for k in range(half_steps):
         if k % 2 == 0:
@@ -214,6 +336,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hvp", action="store_true",
                     help="skip the Hessian-vector product measurement (d <= 64 recipes)")
+    ap.add_argument("--no-block-sparse", action="store_true",
+                    help="skip the block-sparse measurement of the c5 line")
     ap.add_argument("--counters", action="store_true",
                     help="run the hardware-counter workload instead of the benchmark")
     args = ap.parse_args()
@@ -235,6 +359,9 @@ def main():
     w = workloads.make(wl)
     if args.counters:
         counter_mode(w, prec)
+        return
+    if wl == "fs2":
+        main_block_sparse(args, w, peak, unit, dtype, desc, binding, torch)
         return
     iters = args.iters or w.iters
     total_iters = iters * w.n_stages
@@ -390,9 +517,74 @@ def main():
         out["backward"] = backward
     if hvp:
         out["hvp"] = hvp
+    if wl == "c5" and not args.no_block_sparse:
+        out["block_sparse"] = block_sparse_run(w, w.eps, 3, 1, dev, binding, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
+
+
+def main_block_sparse(args, w, peak, unit, dtype, desc, binding, torch):
+    dev = torch.device("cuda:0")
+    sampler = PowerSampler()
+    sampler.start()
+    bs = block_sparse_run(w, w.eps, args.steps, args.warmup, dev, binding, torch)
+    sampler.halt.set()
+    sampler.join(timeout=30)
+    sink = torch.zeros(1, device=dev)
+    peak_measured = binding.fs_probe_peak("exp", sink) / 1e12
+    # one exponential per kept pair; launches alternate the two sides
+    achieved = bs["kept_pairs_per_iter"] / 2 / (bs["lse_mean_launch_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "alu", "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic_per_launch("fs2"),
+                "peak_measured": round(peak_measured, 2),
+                "frac_measured": round(achieved / peak_measured, 4), "peak_probe": "exp",
+                "kernel": "lse_small_kernel<2, sparse> (one half-step; work = exponentials of "
+                          "the kept 32 x 256 block pairs)",
+                "mean_launch_ms": bs["lse_mean_launch_ms"], "launches": bs["lse_launches"]}
+    it_s = bs["iters_per_s"]
+    out = {
+        "metric": METRIC, "value": it_s, "unit": "iters/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(10e3 / it_s, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": desc, "recipe": "fs2", "n": w.n, "m": w.m, "d": w.d,
+                   "eps": w.eps, "delta": BS_DELTA, "iters_per_step": 10,
+                   "score_path": "fp32-small-mfma (block-sparse)"},
+        "pair_evals_per_s": bs["kept_pairs_per_iter"] * it_s,
+        "dense_equivalent_pair_evals_per_s": 2.0 * w.n * w.m * it_s,
+        "clocks": sampler.summary(),
+        "roofline": roofline,
+        "block_sparse": bs,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block_sparse(w, bs)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_block_sparse(w, bs, row_blocks=(0, 1)) -> dict:
+    """The block-sparse oracle (oracle/blocksparse.py, numpy) on two row
+    blocks of the f-update at the warm start's final eps, from zero
+    potentials (its screening of those blocks plus their retained-block
+    LSE), scaled to iterations per second of the whole problem."""
+    import numpy as np
+
+    from oracle import blocksparse as obs
+
+    X = w.X[obs.morton_order(w.X)]
+    Y = w.Y[obs.morton_order(w.Y)]
+    t = time.perf_counter()
+    obs.update_sparse(X, Y, w.b, np.zeros(w.m), np.zeros(w.n), w.eps, BS_DELTA,
+                      row_blocks=list(row_blocks))
+    dt = time.perf_counter() - t
+    rows = 256 * len(row_blocks)
+    per_half = dt * w.n / rows
+    return {"value": round(1.0 / (2 * per_half), 6), "unit": "iters/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle/blocksparse.py update_sparse on {len(row_blocks)} row blocks "
+                      f"({rows} rows; screening against all key blocks, then the retained "
+                      f"blocks' LSE) of the f-update from zero potentials at eps={w.eps:.3g}, "
+                      f"{dt:.1f} s, scaled to both half-steps of all rows"}
 
 
 if __name__ == "__main__":

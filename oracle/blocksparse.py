@@ -180,20 +180,23 @@ def bilinear_bound(u, v, lo1, hi1, lo2, hi2) -> float:
 
 
 def screen(R, K, w_keys, pot_rows, pot_keys, eps: float, delta: float, BR: int = 256,
-           BK: int = 32, return_bounds: bool = False):
+           BK: int = 32, return_bounds: bool = False, row_blocks=None):
     """Kept key blocks (ascending indices) of every row block, for the update
     of the rows' potential from the keys' potential (see the header).
     With return_bounds, also the log bound matrix beta[I, J] and the log
-    threshold."""
+    threshold.  row_blocks: screen only these row blocks (lists and rows of
+    beta in that order)."""
     R, K = np.asarray(R, np.float64), np.asarray(K, np.float64)
     w_keys = np.asarray(w_keys, np.float64)
     pot_rows = np.asarray(pot_rows, np.float64)
     pot_keys = np.asarray(pot_keys, np.float64)
     rlo, rhi = block_boxes(R, BR)
     klo, khi = block_boxes(K, BK)
-    nbR, nbK = rlo.shape[0], klo.shape[0]
+    nbK = klo.shape[0]
+    blocks = list(range(rlo.shape[0])) if row_blocks is None else [int(I) for I in row_blocks]
+    nbR = len(blocks)
     U, c, U2, c2 = [], [], [], []
-    for I in range(nbR):
+    for I in blocks:
         P, f = R[I * BR:(I + 1) * BR], pot_rows[I * BR:(I + 1) * BR]
         phi = f - (P * P).sum(axis=1)
         U.append(slope(P, f))
@@ -211,14 +214,14 @@ def screen(R, K, w_keys, pot_rows, pot_keys, eps: float, delta: float, BR: int =
     thr = np.log(delta / nbK) if delta > 0 else -np.inf
     beta = np.empty((nbR, nbK))
     lists = []
-    for I in range(nbR):
+    for k, I in enumerate(blocks):
         for J in range(nbK):
-            H = pair_bound(U[I], V[J], rlo[I], rhi[I], klo[J], khi[J])
-            H2 = bilinear_bound(U2[I], V2[J], rlo[I], rhi[I], klo[J], khi[J])
-            beta[I, J] = min(c[I] / eps + G[J] + H / eps, c2[I] / eps + G2[J] + H2 / eps)
-        keep = np.nonzero(beta[I] >= thr)[0]
+            H = pair_bound(U[k], V[J], rlo[I], rhi[I], klo[J], khi[J])
+            H2 = bilinear_bound(U2[k], V2[J], rlo[I], rhi[I], klo[J], khi[J])
+            beta[k, J] = min(c[k] / eps + G[J] + H / eps, c2[k] / eps + G2[J] + H2 / eps)
+        keep = np.nonzero(beta[k] >= thr)[0]
         if keep.size == 0:
-            keep = np.array([int(np.argmax(beta[I]))])
+            keep = np.array([int(np.argmax(beta[k]))])
         lists.append(keep)
     if return_bounds:
         return lists, beta, thr
@@ -226,14 +229,16 @@ def screen(R, K, w_keys, pot_rows, pot_keys, eps: float, delta: float, BR: int =
 
 
 def update_sparse(R, K, w_keys, pot_keys, pot_rows, eps: float, delta: float, BR: int = 256,
-                  BK: int = 32):
-    """Retained-block update of the rows' potential; returns (new, lists)."""
+                  BK: int = 32, row_blocks=None):
+    """Retained-block update of the rows' potential; returns (new, lists).
+    row_blocks: update only these row blocks (the other entries are NaN)."""
     R, K = np.asarray(R, np.float64), np.asarray(K, np.float64)
     w_keys = np.asarray(w_keys, np.float64)
     pot_keys = np.asarray(pot_keys, np.float64)
-    lists = screen(R, K, w_keys, pot_rows, pot_keys, eps, delta, BR, BK)
-    out = np.empty(R.shape[0])
-    for I, keep in enumerate(lists):
+    lists = screen(R, K, w_keys, pot_rows, pot_keys, eps, delta, BR, BK, row_blocks=row_blocks)
+    blocks = range(len(lists)) if row_blocks is None else [int(I) for I in row_blocks]
+    out = np.full(R.shape[0], np.nan)
+    for I, keep in zip(blocks, lists):
         rows = np.arange(I * BR, min((I + 1) * BR, R.shape[0]))
         keys = np.concatenate([np.arange(J * BK, min((J + 1) * BK, K.shape[0])) for J in keep])
         C = ((R[rows, None, :] - K[None, keys, :]) ** 2).sum(-1)

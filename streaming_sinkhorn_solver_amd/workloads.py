@@ -25,6 +25,9 @@ they do not describe; the five recipes below stand in for them:
 * ``c5`` 250k x 250k points in 3-D, X uniform in the unit cube, Y an
   8-component Gaussian mixture (means uniform in the cube, std 0.05),
   uniform weights, eps 0.01, 10 iterations.
+* ``fs2`` (the block-sparse form) 250k x 250k points, two independent
+  uniform samples of the unit cube, eps = n^(-2/3) (entropic blur equal to
+  the mean interparticle distance), annealed from 0.1 over 12 stages.
 
 Every recipe accepts smaller ``n``/``m`` (and, where it makes sense, ``d``)
 so the same distributions can be drawn at sizes the oracle finishes in
@@ -148,7 +151,19 @@ def _c5(seed, n=250_000, m=250_000, d=3):
                     eps=0.01, iters=10, seed=seed)
 
 
-_BUILDERS = {"c1": _c1, "c2": _c2, "c3": _c3, "c4": _c4, "c5": _c5}
+def _fs2(seed, n=250_000, m=250_000, d=3):
+    # Two independent uniform samples of the unit cube at eps = (mean spacing)^2
+    # = n^(-2/3): the regime of the block-sparse form (entropic blur equal to
+    # the interparticle distance, as in the "FlashSinkhorn 2" explainer's
+    # large experiment), annealed from 0.1 over 12 stages of 10 iterations.
+    rng = np.random.default_rng(seed)
+    X = rng.random((n, d))
+    Y = rng.random((m, d))
+    return Workload("fs2", _f32(X), _f32(Y), _uniform_weights(n), _uniform_weights(m),
+                    eps=float(n) ** (-2.0 / d), iters=10, n_stages=12, eps_start=0.1, seed=seed)
+
+
+_BUILDERS = {"c1": _c1, "c2": _c2, "c3": _c3, "c4": _c4, "c5": _c5, "fs2": _fs2}
 
 #: full-size shapes of the five recipes, (n, m, d)
 CONFIGS = {
@@ -159,16 +174,19 @@ CONFIGS = {
     "c5": (250_000, 250_000, 3),
 }
 
-_DEFAULT_SEED = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+#: the block-sparse form's workload (not one of the five recipes above)
+FS2_CONFIG = (250_000, 250_000, 3)
+
+_DEFAULT_SEED = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "fs2": 6}
 
 
 def make(name: str, n: Optional[int] = None, m: Optional[int] = None,
          d: Optional[int] = None, seed: Optional[int] = None, **kw) -> Workload:
-    """Draw recipe ``name`` (``c1`` .. ``c5``), optionally at a smaller size."""
+    """Draw recipe ``name`` (``c1`` .. ``c5``, ``fs2``), optionally at a smaller size."""
     name = name.lower()
     if name not in _BUILDERS:
         raise KeyError(f"unknown workload {name!r}; choose from {sorted(_BUILDERS)}")
-    n0, m0, d0 = CONFIGS[name]
+    n0, m0, d0 = FS2_CONFIG if name == "fs2" else CONFIGS[name]
     s = _DEFAULT_SEED[name] if seed is None else int(seed)
     return _BUILDERS[name](s, n=n or n0, m=m or m0, d=d or d0, **kw)
 

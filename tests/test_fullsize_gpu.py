@@ -158,3 +158,75 @@ def test_full_size_hvp_symmetry(fs):
     rhs = float(np.sum(V.astype(np.float64) * hu))
     print(f"c3 HVP symmetry: {lhs:.6e} vs {rhs:.6e}; CG {iu} {iv}")
     assert abs(lhs - rhs) <= 5e-3 * max(abs(lhs), abs(rhs))
+
+
+# (recipe, eps override, delta): the c5 clouds at their own eps and in the
+# blur-equals-spacing regime, and the uniform pair of the block-sparse form
+BLOCK_SPARSE = [("c5", None, 1e-3), ("c5", 250_000 ** (-2 / 3), 1e-3), ("fs2", None, 1e-3)]
+
+
+@pytest.mark.parametrize("name,eps,delta", BLOCK_SPARSE)
+def test_full_size_block_sparse(fs, name, eps, delta):
+    """The block-sparse form at 250k x 250k (d = 3) in the configuration
+    bench.py times (GPU Morton order, annealed block-sparse solve to the
+    final eps), then one more f- and g-update compared on 512 sampled rows
+    and columns with the dense oracle update through the certificate
+    (-tol <= new - dense <= eps log(1 + delta exp((new - cur)/eps)) + tol,
+    tol = 1e-3 eps), and two row blocks' skipped key blocks checked by
+    brute force against the mass bound."""
+    import torch
+
+    from oracle import blocksparse as obs
+
+    B = fs
+    w = workloads.make(name)
+    eps = w.eps if eps is None else eps
+    Xs, a_s, px = B.fs_morton_sort(dev(w.X), dev(w.a))
+    Ys, b_s, py = B.fs_morton_sort(dev(w.Y), dev(w.b))
+    torch.cuda.synchronize()
+    assert np.array_equal(px.cpu().numpy(), obs.morton_order(w.X))
+    X, Y, a, b = host(Xs), host(Ys), host(a_s), host(b_s)
+    f = torch.zeros(w.n, device="cuda")
+    g = torch.zeros(w.m, device="cuda")
+    p = B.fs_potentials_init(Xs, Ys, a_s, b_s, f=f, g=g)
+    B.fs_bs_attach(p)
+    B.fs_bs_sinkhorn_solve(p, f, g, eps_end=eps, eps_start=0.1, n_stages=12,
+                           iters_per_stage=10, delta=delta)
+    f_new = torch.empty_like(f)
+    B.fs_bs_lse_update_f(p, eps, delta, g, f, f_new)
+    torch.cuda.synchronize()
+    fc, gc, fn = host(f), host(g), host(f_new)
+    cnt_f, lists_f = B.fs_bs_read_screen(p, 0, lists=True)
+    g_new = torch.empty_like(g)
+    B.fs_bs_lse_update_g(p, eps, delta, f_new, g, g_new)
+    torch.cuda.synchronize()
+    gn = host(g_new)
+    rng = np.random.default_rng(88)
+    rows = np.sort(rng.choice(w.n, SAMPLES, replace=False))
+    cols = np.sort(rng.choice(w.m, SAMPLES, replace=False))
+    ref_f = oracle.f_update_rows(X, Y, b, gc, eps, rows)
+    ref_g = oracle.g_update_cols(X, Y, a, fn, eps, cols)
+    for new, ref, cur, idx in ((fn, ref_f, fc, rows), (gn, ref_g, gc, cols)):
+        diff = new[idx] - ref
+        cert = obs.certificate(new[idx], cur[idx], eps, delta)
+        print(f"{name} eps {eps:.3g}: diff [{diff.min() / eps:.2e}, {diff.max() / eps:.2e}] eps, "
+              f"certificate max {cert.max() / eps:.2e} eps")
+        assert diff.min() >= -1e-3 * eps
+        assert np.all(diff <= cert + 1e-3 * eps)
+    # brute-force mass of the skipped blocks of two row blocks (f side)
+    nbK = (w.m + 31) // 32
+    for I in (0, len(cnt_f) // 2):
+        kept = lists_f[I, :cnt_f[I]]
+        skip = np.setdiff1d(np.arange(nbK), kept)
+        r = np.arange(I * 256, min(I * 256 + 256, w.n))
+        keys = np.concatenate([np.arange(J * 32, min(J * 32 + 32, w.m)) for J in skip])
+        blk = np.repeat(np.arange(len(skip)), [min(J * 32 + 32, w.m) - J * 32 for J in skip])
+        mass = np.zeros((len(r), len(skip)))
+        for c0 in range(0, len(keys), 65536):
+            kk = keys[c0:c0 + 65536]
+            C = ((X[r, None, :] - Y[None, kk, :]) ** 2).sum(-1)
+            z = b[kk][None, :] * np.exp((fc[r, None] + gc[None, kk] - C) / eps)
+            np.add.at(mass.T, blk[c0:c0 + 65536], z.T)
+        print(f"  row block {I}: kept {len(kept)} of {nbK} key blocks, largest skipped mass "
+              f"{mass.max():.2e} (bound {delta / nbK:.2e})")
+        assert mass.max() < delta / nbK * 1.001
