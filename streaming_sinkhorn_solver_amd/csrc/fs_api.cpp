@@ -60,6 +60,7 @@ struct fs_problem {
     float4* bs_kfit = nullptr;                // per pass: [2] fits (v, G) of the key blocks
     int* bs_cnt[2] = {nullptr, nullptr};      // kept blocks per row block, last pass of a side
     int* bs_best = nullptr;                   // per row block: the block of largest bound
+    float4* bs_org = nullptr;                 // per row block: [2] origin and format flag
     int* bs_list = nullptr;                   // kept blocks of the last pass
     float2* bs_part = nullptr;                // [kBsMaxSplit][max(n, m)] partials
     int bs_last_side = -1;
@@ -1056,7 +1057,7 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
     const int sentinel = (int)(K.n_pad / 32);
     if ((e = launch_screen(p->bs_rbox[side], p->bs_rfit, nbR, p->bs_kbox[side], p->bs_kfit, nbK,
                            c_bias, thr2, p->bs_mag, p->bs_list, p->bs_cnt[side], p->bs_best,
-                           p->bs_cap[side], sentinel, s)) != hipSuccess)
+                           cR, cK, p->d, p->bs_org, p->bs_cap[side], sentinel, s)) != hipSuccess)
         return hip_fail(e, "screening launch");
     p->bs_last_side = side;
     LseArgs a = base_args(p, f_side, eps);
@@ -1072,6 +1073,7 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
     a.bs_list = p->bs_list;
     a.bs_count = p->bs_cnt[side];
     a.bs_best = p->bs_best;
+    a.bs_org = p->bs_org;
     a.bs_cap = p->bs_cap[side];
     a.bs_sentinel = sentinel;
     if ((e = launch_lse(p->path, a, s, eb, ee)) != hipSuccess)
@@ -1080,7 +1082,7 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
 }
 
 struct BsLayout {
-    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], best, list, part, total;
+    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], best, org, list, part, total;
 };
 
 BsLayout bs_layout(const fs_problem* p) {
@@ -1101,6 +1103,7 @@ BsLayout bs_layout(const fs_problem* p) {
     }
     L.rfit = take(sizeof(float4) * 2 * std::max(nbR[0], nbR[1]));
     L.best = take(sizeof(int) * std::max(nbR[0], nbR[1]));
+    L.org = take(sizeof(float4) * 2 * std::max(nbR[0], nbR[1]));
     L.kfit = take(sizeof(float4) * 2 * std::max(nbK[0], nbK[1]));
     const int64_t cap0 = (nbK[0] + 15) / 16 * 16, cap1 = (nbK[1] + 15) / 16 * 16;
     L.list = take(sizeof(int) * (size_t)std::max(nbR[0] * cap0, nbR[1] * cap1));
@@ -1196,6 +1199,7 @@ fs_status fs_bs_attach(fs_problem* p, void* workspace, size_t workspace_bytes, v
     p->bs_list = (int*)(w + L.list);
     p->bs_part = (float2*)(w + L.part);
     p->bs_best = (int*)(w + L.best);
+    p->bs_org = (float4*)(w + L.org);
     p->bs_last_side = -1;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;

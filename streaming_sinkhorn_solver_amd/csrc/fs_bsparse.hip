@@ -441,6 +441,13 @@ struct ScreenArgs {
     int* list;           // [nbR][cap]
     int* count;          // [nbR]
     int* best;           // [nbR]: the key block of largest bound
+    // origin of each row block for the streaming kernel's shifted fp16
+    // operands: org[2I] = (O - row cloud centre, format flag), org[2I+1] =
+    // (O - key cloud centre, 0), O the centre of the row block's box
+    const float* cR;
+    const float* cK;
+    int d;
+    float4* org;
     int cap;
     int sentinel;
 };
@@ -461,6 +468,15 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
     int count = 0;
     float best = -INFINITY;
     int bestJ = 0;
+    // box centre O and the largest |y - O| over the kept key blocks' boxes
+    const float O[3] = {0.5f * (rlo.x + rhi.x), 0.5f * (rlo.y + rhi.y), 0.5f * (rlo.z + rhi.z)};
+    auto reach = [&](int J) {
+        const float4 klo = a.kbox[2 * J], khi = a.kbox[2 * J + 1];
+        return fmaxf(fmaxf(fmaxf(fabsf(klo.x - O[0]), fabsf(khi.x - O[0])),
+                           fmaxf(fabsf(klo.y - O[1]), fabsf(khi.y - O[1]))),
+                     fmaxf(fabsf(klo.z - O[2]), fabsf(khi.z - O[2])));
+    };
+    float wmax = 0.f;
     for (int J0 = 0; J0 < a.nbK; J0 += 256) {
         const int J = J0 + tid;
         bool keep = false;
@@ -489,7 +505,10 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
             if (q < w) pre += wcnt[q];
             tot += wcnt[q];
         }
-        if (keep) out[count + pre + (int)__popcll(m & lt)] = J;
+        if (keep) {
+            out[count + pre + (int)__popcll(m & lt)] = J;
+            wmax = fmaxf(wmax, reach(J));
+        }
         count += tot;
         __syncthreads();
     }
@@ -521,9 +540,39 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
                     jj = jred[q];
                 }
             a.best[I] = jj;
-            if (count == 0) out[0] = jj;
+            if (count == 0) {
+                out[0] = jj;
+                wmax = reach(jj);
+            }
         }
         if (count == 0) count = 1;
+    }
+    // origin and fp16 format flag of the row block (the same bounds as the
+    // dense kernel's fp16 format, on the shifted magnitudes: rows within the
+    // box's half extents of O, kept keys within wmax)
+    {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, o, 64));
+        __syncthreads();
+        if (lane == 0) bred[w] = wmax;
+        __syncthreads();
+        if (tid == 0) {
+            const float wm = fmaxf(fmaxf(bred[0], bred[1]), fmaxf(bred[2], bred[3]));
+            const float cs = 2.f * a.c_bias;
+            float half = 0.f, l1o = 0.f, ox[3] = {0.f, 0.f, 0.f}, oy[3] = {0.f, 0.f, 0.f};
+            const float hx[3] = {0.5f * (rhi.x - rlo.x), 0.5f * (rhi.y - rlo.y),
+                                 0.5f * (rhi.z - rlo.z)};
+            for (int c = 0; c < a.d; ++c) {
+                ox[c] = O[c] - a.cR[c];
+                oy[c] = O[c] - a.cK[c];
+                half += hx[c];
+                l1o += fabsf(ox[c]);
+            }
+            const bool ok = cs * half * wm <= 500.f && cs * l1o * wm <= 16384.f &&
+                            cs * half <= 16384.f && wm <= 16384.f;
+            a.org[2 * I] = make_float4(ox[0], ox[1], ox[2], ok ? 1.f : 0.f);
+            a.org[2 * I + 1] = make_float4(oy[0], oy[1], oy[2], 0.f);
+        }
     }
     const int padded = (count + 15) / 16 * 16;
     for (int k = count + tid; k < padded; k += 256) out[k] = a.sentinel;
@@ -632,7 +681,8 @@ hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_
 
 hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const float4* kbox,
                          const float4* kfit, int nbK, float c_bias, float thr2, float mag,
-                         int* list, int* count, int* best, int cap, int sentinel, hipStream_t s) {
+                         int* list, int* count, int* best, const float* cR, const float* cK,
+                         int d, float4* org, int cap, int sentinel, hipStream_t s) {
     ScreenArgs a;
     a.rbox = rbox;
     a.rfit = rfit;
@@ -647,6 +697,10 @@ hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const 
     a.list = list;
     a.count = count;
     a.best = best;
+    a.cR = cR;
+    a.cK = cK;
+    a.d = d;
+    a.org = org;
     a.cap = cap;
     a.sentinel = sentinel;
     screen_kernel<<<nbR, 256, 0, s>>>(a);

@@ -89,6 +89,7 @@ struct LseArgs {
     const int* bs_list;
     const int* bs_count;
     const int* bs_best;  // per row block: the block whose scores set the starting reference
+    const float4* bs_org;  // per row block: origin and fp16-format flag (see fs_bsparse.hip)
     int bs_cap;
     int bs_sentinel;
 };
@@ -237,10 +238,12 @@ hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_
                             float4* fit, hipStream_t s);
 // Kept key blocks of every row block (threshold thr2 = log2(delta / nbK)),
 // their count, and the key block of largest bound.
+// Also the row block's origin for shifted fp16 operands and its format flag
+// (org[2I], org[2I+1]; cR, cK: the row and key clouds' centres).
 hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const float4* kbox,
                          const float4* kfit, int nbK, float c_bias, float thr2, float mag,
-                         int* list, int* count, int* best, int cap, int sentinel,
-                         hipStream_t s);
+                         int* list, int* count, int* best, const float* cR, const float* cK,
+                         int d, float4* org, int cap, int sentinel, hipStream_t s);
 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
 // Matrix paths: the streaming transport kernel serves operand rows of up to

@@ -180,8 +180,17 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     constexpr int TK = small_tile_keys(KP);
     constexpr int F32_TILE = TK * f32_rec_bytes(KP);
     constexpr int F16_TILE = HAS_F16 ? TK * kF16RecBytes : 0;
+    // (the sparse form's shifted fp16 operands are made in LDS: a tile of fp32
+    // records fills the lower half of its slot, and the converted records of
+    // its first and second 256 keys go to the upper halves of that slot and of
+    // the slot two ahead, which no copy in flight touches)
     constexpr int BUF_BYTES = F16_TILE > F32_TILE ? F16_TILE : F32_TILE;
-    __shared__ __attribute__((aligned(16))) uint4 tbuf[kNbuf][BUF_BYTES / 16];
+    constexpr bool SHIFT = SPARSE && HAS_F16;
+    constexpr int NB = kNbuf;
+    static_assert(!SHIFT || (TK == W * 64 && F32_TILE * 2 <= BUF_BYTES && F16_TILE == BUF_BYTES &&
+                             NB == 4),
+                  "shifted conversion: one key per thread, fp32 tile in half a slot");
+    __shared__ __attribute__((aligned(16))) uint4 tbuf[NB][BUF_BYTES / 16];
     __shared__ __attribute__((aligned(16))) uint4 ibuf[SPARSE ? 64 : 1];  // sparse: starting block
     __shared__ float red[16];
 
@@ -224,6 +233,36 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         const float ymax = __uint_as_float(g->ymax_bits);
         const float rl1 = a.c_score * *a.row_l1;
         use16 = rl1 * ymax <= kF16Bound && rl1 <= kF16Range && g->bad == 0;
+    }
+
+    // Sparse form, shifted fp16 operands: with O the row block's origin
+    // (o_x = O - own centre, o_y = O - key cloud's centre), the score is
+    //   c x~.y~ + beta = c (x~ - o_x).(y~ - o_y) + [beta + c o_x.(y~ - o_y)] + c x~.o_y,
+    // the first term a product of small vectors (rows and kept keys lie near
+    // O), the bracket the key's new bias, the last a constant of the row,
+    // added to its result.  Taken when the pass-wide fp16 format does not
+    // hold but the screening found the shifted magnitudes within its bound for
+    // this row block (and the packing flagged no key).
+    bool shifted = false;
+    float rowc = 0.f;
+    float cox[3] = {0.f, 0.f, 0.f}, oy[3] = {0.f, 0.f, 0.f};
+    if constexpr (SHIFT) {
+        const float4 o0 = a.bs_org[2 * row_block], o1 = a.bs_org[2 * row_block + 1];
+        shifted = !use16 && o0.w != 0.f && ((const Guard*)a.krec_guard)->bad == 0;
+        if (shifted) {
+            const float ox[3] = {o0.x, o0.y, o0.z};
+            oy[0] = o1.x;
+            oy[1] = o1.y;
+            oy[2] = o1.z;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if (k < d) {
+                    rowc = fmaf(r[k], oy[k], rowc);
+                    r[k] = a.c_score * (xr[k] - ox[k]);
+                    cox[k] = a.c_score * ox[k];
+                }
+            }
+        }
     }
 
     float R = 0.f;      // reference: the running maximum, moved lazily
@@ -274,19 +313,68 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         }
     };
 
-    // The tile loop for one operand format.
-    auto run = [&](auto f16_c) __attribute__((always_inline)) {
-        constexpr bool F16 = decltype(f16_c)::value;
-        constexpr int REC_BYTES = F16 ? kF16RecBytes : f32_rec_bytes(KP);
-        constexpr int TILE_BYTES = TK * REC_BYTES;
+    // Shifted fp16 records of nkeys fp32 records at src (one key per thread):
+    // y~ - o_y split into fp16 parts, the bias beta + c o_x.(y~ - o_y) into
+    // three; a -inf bias (padding) stays -inf with zero parts.  Keys 0..255 go
+    // to dst0, 256..511 to dst1.
+    auto convert = [&](const char* src, int nkeys, char* dst0,
+                       char* dst1) __attribute__((always_inline)) {
+        const int t = threadIdx.x;
+        if (t < nkeys) {
+            const float* rf = (const float*)(src + (size_t)t * f32_rec_bytes(KP));
+            _Float16 hv[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) hv[k] = (_Float16)0.f;
+            float beta = rf[(d & 1) * KP + (d >> 1)];
+            if (beta == -INFINITY) {
+                hv[3 * d] = (_Float16)(-INFINITY);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    if (c < d) {
+                        const float w = rf[(c & 1) * KP + (c >> 1)] - oy[c];
+                        beta = fmaf(cox[c], w, beta);
+                        const _Float16 wh = (_Float16)w;
+                        const _Float16 wl = (_Float16)(w - (float)wh);
+                        hv[3 * c] = wh;
+                        hv[3 * c + 1] = wl;
+                        hv[3 * c + 2] = wh;
+                    }
+                }
+                const _Float16 bh = (_Float16)beta;
+                const float r1 = beta - (float)bh;
+                const _Float16 bm = (_Float16)r1;
+                hv[3 * d] = bh;
+                hv[3 * d + 1] = bm;
+                hv[3 * d + 2] = (_Float16)(r1 - (float)bm);
+            }
+            uint4 w0, w1;
+            __builtin_memcpy(&w0, &hv[0], 16);
+            __builtin_memcpy(&w1, &hv[8], 16);
+            uint4* o = (uint4*)((t < 256 ? dst0 + (size_t)t * kF16RecBytes
+                                         : dst1 + (size_t)(t - 256) * kF16RecBytes));
+            o[0] = w0;
+            o[1] = w1;
+        }
+    };
+
+    // The tile loop for one operand format: MODE 0 fp32 records, 1 fp16-split
+    // records, 2 (sparse) fp32 records turned into shifted fp16 ones in LDS.
+    auto run = [&](auto mode_c) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode_c)::value;
+        constexpr bool F16 = MODE != 0;
+        constexpr bool CONV = MODE == 2;
+        constexpr int REC_BYTES = F16 ? kF16RecBytes : f32_rec_bytes(KP);  // as multiplied
+        constexpr int DREC_BYTES = MODE == 1 ? kF16RecBytes : f32_rec_bytes(KP);  // as loaded
+        constexpr int TILE_BYTES = TK * DREC_BYTES;
         constexpr int TILE_INSTR = TILE_BYTES / 1024;  // wave-wide 1 KiB loads per tile
         constexpr int INSTR_PER_WAVE = (TILE_INSTR + W - 1) / W;
         constexpr int MIN_INSTR = TILE_INSTR / W;
         constexpr int SUB = TK / 32;                   // 32-key blocks per tile
         static_assert(TILE_BYTES % 1024 == 0 && TILE_BYTES <= BUF_BYTES, "tile geometry");
         const char* __restrict__ recs =
-            F16 ? (const char*)a.krec16 + (int64_t)j0 * REC_BYTES
-                : (const char*)a.krec + (int64_t)j0 * REC_BYTES;
+            MODE == 1 ? (const char*)a.krec16 + (int64_t)j0 * DREC_BYTES
+                      : (const char*)a.krec + (int64_t)j0 * DREC_BYTES;
 
         // tile k -> slot (contiguous copy; records past j1 in the last tile
         // are padding records of score -inf: splits are whole tiles)
@@ -299,7 +387,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
                     if constexpr (SPARSE) {
                         // instruction L covers blocks L*BPI .. L*BPI+BPI-1 of the tile;
                         // lane `lane` fetches 16 bytes of block L*BPI + lane/LPB
-                        constexpr int BLK = 32 * REC_BYTES;
+                        constexpr int BLK = 32 * DREC_BYTES;
                         constexpr int BPI = 1024 / BLK;
                         constexpr int LPB = 64 / BPI;
                         static_assert(1024 % BLK == 0, "whole blocks per instruction");
@@ -322,17 +410,17 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         if constexpr (SPARSE) {
             // the block of largest bound, for the starting reference
             if (ntiles > 0 && wave == 0) {
-                constexpr int LPB = 64 / (1024 / (32 * REC_BYTES));
+                constexpr int LPB = 64 / (1024 / (32 * DREC_BYTES));
                 int ent[1];
                 sload_words<1>(a.bs_best + row_block, ent);
                 const uint32_t Jc = min((uint32_t)ent[0], (uint32_t)a.bs_sentinel);
-                dma_to_lds16(recs, Jc * (uint32_t)(32 * REC_BYTES) + (uint32_t)(lane % LPB) * 16u,
+                dma_to_lds16(recs, Jc * (uint32_t)(32 * DREC_BYTES) + (uint32_t)(lane % LPB) * 16u,
                              &ibuf[0]);
             }
         }
         if (ntiles > 0) {
 #pragma unroll
-            for (int k = 0; k < kNbuf - 1; ++k) issue_tile(min(k, ntiles - 1), k);
+            for (int k = 0; k < NB - 1; ++k) issue_tile(min(k, ntiles - 1), k);
         }
 
         // B operand of this lane: row `row`, the lane half's contraction slots
@@ -386,47 +474,82 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         // whose scores are near the row maxima, so that R rarely moves.
         if (ntiles > 0) {
             f32x16 acc;
-            scores(SPARSE ? (const char*)&ibuf[0] : (const char*)&tbuf[0][0], acc);
+            if constexpr (CONV) {
+                char* up0 = (char*)&tbuf[0][0] + BUF_BYTES / 2;
+                convert((const char*)&ibuf[0], 32, up0, up0);
+                __syncthreads();
+                scores(up0, acc);
+                __syncthreads();  // rewritten by the first tile's conversion
+            } else {
+                scores(SPARSE ? (const char*)&ibuf[0] : (const char*)&tbuf[0][0], acc);
+            }
             const float t = block_max(acc);
             R = t > -INFINITY ? t : 0.f;
         }
 
         for (int t = 0; t < ntiles; ++t) {
-            const int slot = t % kNbuf;
-            issue_tile(min(t + kNbuf - 1, ntiles - 1), (t + kNbuf - 1) % kNbuf);
+            const int slot = t % NB;
+            issue_tile(min(t + NB - 1, ntiles - 1), (t + NB - 1) % NB);
             const char* tb = (const char*)&tbuf[slot][0];
+            // 32-key block u of the tile as multiplied
+            const char* tb2 = tb;
+            if constexpr (CONV) {
+                char* up0 = (char*)&tbuf[slot][0] + BUF_BYTES / 2;
+                char* up1 = (char*)&tbuf[(slot + 2) % NB][0] + BUF_BYTES / 2;
+                convert(tb, TK, up0, up1);
+                stage_barrier();
+                tb = up0;
+                tb2 = up1 - (SUB / 2) * 32 * REC_BYTES;
+            }
+            auto blk = [&](int u) __attribute__((always_inline)) {
+                return (CONV && u >= SUB / 2 ? tb2 : tb) + u * 32 * REC_BYTES;
+            };
 #pragma unroll
             for (int q = 0; q < 16; ++q) cm[q] = -R;
             delta = 0.f;
             f32x16 acc0, acc1;
-            scores(tb, acc0);
+            scores(blk(0), acc0);
 #pragma unroll
             for (int u = 0; u < SUB; u += 2) {
-                scores(tb + (u + 1) * 32 * REC_BYTES, acc1);
+                scores(blk(u + 1), acc1);
                 epilogue(acc0);
-                if (u + 2 < SUB) scores(tb + (u + 2) * 32 * REC_BYTES, acc0);
+                if (u + 2 < SUB) scores(blk(u + 2), acc0);
                 epilogue(acc1);
             }
-            // tiles issued after tile t+1: t+2 .. t+kNbuf-1
+            // tiles issued after tile t+1: t+2 .. t+NB-1
             if constexpr (MIN_INSTR == 0)
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             else
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kNbuf - 2) * MIN_INSTR) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * MIN_INSTR) : "memory");
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
-    if constexpr (HAS_F16) {
+    if constexpr (SPARSE) {
+        // the pass-wide fp16 records when they hold (no conversion), else the
+        // shifted ones when this row block allows them, else fp32
+        if constexpr (SHIFT) {
+            if (use16) {
+                run(std::integral_constant<int, 1>{});
+            } else if (shifted) {
+                run(std::integral_constant<int, 2>{});
+            } else {
+                run(std::integral_constant<int, 0>{});
+            }
+        } else {
+            run(std::integral_constant<int, 0>{});
+        }
+    } else if constexpr (HAS_F16) {
         if (use16)
-            run(std::true_type{});
+            run(std::integral_constant<int, 1>{});
         else
-            run(std::false_type{});
+            run(std::integral_constant<int, 0>{});
     } else {
-        run(std::false_type{});
+        run(std::integral_constant<int, 0>{});
     }
 
     // the two lane halves hold the same row over disjoint keys
-    float M = s > 0.f ? R : -INFINITY;
+    float M = s > 0.f ? R + rowc : -INFINITY;
     {
         const float M2 = __shfl_xor(M, 32, 64);
         const float S2 = __shfl_xor(s, 32, 64);
