@@ -61,6 +61,9 @@ struct fs_problem {
     int* bs_cnt[2] = {nullptr, nullptr};      // kept blocks per row block, last pass of a side
     int* bs_best = nullptr;                   // per row block: the block of largest bound
     float4* bs_org = nullptr;                 // per row block: [2] origin and format flag
+    int* bs_nsplit = nullptr;                 // work plan: splits per row block
+    int* bs_map = nullptr;                    //   (row block, split) per workgroup
+    int* bs_total = nullptr;                  //   planned workgroups
     int* bs_list = nullptr;                   // kept blocks of the last pass
     float2* bs_part = nullptr;                // [kBsMaxSplit][max(n, m)] partials
     int bs_last_side = -1;
@@ -1031,11 +1034,15 @@ namespace {
 // Block-sparse low-dimensional form ("FlashSinkhorn 2" explainer, sections on
 // cutting space and on guaranteeing the skip; see fs_bsparse.hip).
 
-// Workgroups per row block of the block-sparse pass: the lists' tiles are
-// dealt to S workgroups so that about 2048 are launched (uneven list lengths
-// then even out over several rounds of the 256 compute units).
-constexpr int kBsMaxSplit = 8;
-int bs_splits(int nbR) { return std::max(1, std::min(kBsMaxSplit, (2048 + nbR - 1) / nbR)); }
+// Work plan of the block-sparse pass: the kept tiles are dealt so that about
+// kBsTarget workgroups share them evenly (a row block's list to at most
+// kBsMaxSplit of them); the kernel is launched with row blocks + kBsTarget
+// workgroups, the plan's upper bound.
+#ifndef FS_BS_SPLIT_TARGET
+#define FS_BS_SPLIT_TARGET 4096
+#endif
+constexpr int kBsTarget = FS_BS_SPLIT_TARGET;
+constexpr int kBsMaxSplit = 16;
 
 fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, const float* cur,
                           const float* other, float* out, float* resid, hipStream_t s,
@@ -1060,14 +1067,21 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
                            cR, cK, p->d, p->bs_org, p->bs_cap[side], sentinel, s)) != hipSuccess)
         return hip_fail(e, "screening launch");
     p->bs_last_side = side;
+    if ((e = launch_split_plan(p->bs_cnt[side], nbR, kBsTarget, kBsMaxSplit, p->bs_nsplit,
+                               p->bs_map, p->bs_total, s)) != hipSuccess)
+        return hip_fail(e, "split plan launch");
     LseArgs a = base_args(p, f_side, eps);
     a.key_pot = other;
     a.out = out;
     a.mode = 0;
     a.cur = resid ? cur : nullptr;
     a.resid_out = resid;
-    a.n_split = bs_splits(nbR);
+    a.n_split = kBsMaxSplit;  // the partial form; the splits are planned per row block
     a.part = p->bs_part;
+    a.bs_nsplit = p->bs_nsplit;
+    a.bs_map = p->bs_map;
+    a.bs_total = p->bs_total;
+    a.bs_grid = nbR + kBsTarget;
     a.keys_per_split = (int)K.n_pad;
     a.krec_keys = (int)K.n_pad + 32;
     a.bs_list = p->bs_list;
@@ -1082,7 +1096,7 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
 }
 
 struct BsLayout {
-    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], best, org, list, part, total;
+    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], best, org, nsplit, map, ptotal, list, part, total;
 };
 
 BsLayout bs_layout(const fs_problem* p) {
@@ -1104,6 +1118,9 @@ BsLayout bs_layout(const fs_problem* p) {
     L.rfit = take(sizeof(float4) * 2 * std::max(nbR[0], nbR[1]));
     L.best = take(sizeof(int) * std::max(nbR[0], nbR[1]));
     L.org = take(sizeof(float4) * 2 * std::max(nbR[0], nbR[1]));
+    L.nsplit = take(sizeof(int) * std::max(nbR[0], nbR[1]));
+    L.map = take(sizeof(int) * 2 * (std::max(nbR[0], nbR[1]) + kBsTarget));
+    L.ptotal = take(sizeof(int) * 4);
     L.kfit = take(sizeof(float4) * 2 * std::max(nbK[0], nbK[1]));
     const int64_t cap0 = (nbK[0] + 15) / 16 * 16, cap1 = (nbK[1] + 15) / 16 * 16;
     L.list = take(sizeof(int) * (size_t)std::max(nbR[0] * cap0, nbR[1] * cap1));
@@ -1200,6 +1217,9 @@ fs_status fs_bs_attach(fs_problem* p, void* workspace, size_t workspace_bytes, v
     p->bs_part = (float2*)(w + L.part);
     p->bs_best = (int*)(w + L.best);
     p->bs_org = (float4*)(w + L.org);
+    p->bs_nsplit = (int*)(w + L.nsplit);
+    p->bs_map = (int*)(w + L.map);
+    p->bs_total = (int*)(w + L.ptotal);
     p->bs_last_side = -1;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;

@@ -579,9 +579,72 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
     if (tid == 0) a.count[I] = count;
 }
 
+// Work plan of the retained-block pass: row block I's list of tiles_I =
+// ceil(count_I / 16) tiles is dealt to S_I = min(smax, ceil(tiles_I / T))
+// workgroups, T = ceil(total tiles / target), so that long and short lists
+// take about the same time; map[2k], map[2k+1] = (row block, split) of
+// workgroup k, total[0] = sum of S_I (<= nbR + target).  One workgroup.
+__global__ __launch_bounds__(1024) void split_plan_kernel(const int* __restrict__ count, int nbR,
+                                                          int target, int smax,
+                                                          int* __restrict__ nsplit,
+                                                          int* __restrict__ map,
+                                                          int* __restrict__ total) {
+    __shared__ int red[16];
+    __shared__ int carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // total tiles (fixed-order sum)
+    int t = 0;
+    for (int I = tid; I < nbR; I += 1024) t += (count[I] + 15) / 16;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+    if (lane == 0) red[wid] = t;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    int all = 0;
+    for (int w = 0; w < 16; ++w) all += red[w];
+    const int T = max(1, (all + target - 1) / target);
+    __syncthreads();
+    for (int base = 0; base < nbR; base += 1024) {
+        const int I = base + tid;
+        const int tiles = I < nbR ? (count[I] + 15) / 16 : 0;
+        const int S = I < nbR ? min(smax, max(1, (tiles + T - 1) / T)) : 0;
+        int inc = S;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += v;
+        }
+        if (lane == 63) red[wid] = inc;
+        __syncthreads();
+        int pre = 0, tot = 0;
+        for (int w = 0; w < 16; ++w) {
+            if (w < wid) pre += red[w];
+            tot += red[w];
+        }
+        const int off = carry_s + pre + inc - S;
+        if (I < nbR) {
+            nsplit[I] = S;
+            for (int q = 0; q < S; ++q) {
+                map[2 * (off + q)] = I;
+                map[2 * (off + q) + 1] = q;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) carry_s += tot;
+        __syncthreads();
+    }
+    if (tid == 0) total[0] = carry_s;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_split_plan(const int* count, int nbR, int target, int smax, int* nsplit,
+                             int* map, int* total, hipStream_t s) {
+    split_plan_kernel<<<1, 1024, 0, s>>>(count, nbR, target, smax, nsplit, map, total);
+    return hipGetLastError();
+}
 
 int morton_bits(int d) { return 30 / d; }
 

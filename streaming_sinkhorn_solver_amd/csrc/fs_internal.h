@@ -83,13 +83,22 @@ struct LseArgs {
     // block-sparse form (PATH_SMALL, d <= 3; see fs_bsparse.hip): per row
     // block of 256 rows, the kept 32-key blocks [row blocks][bs_cap] padded to
     // whole tiles of 16 with bs_sentinel (the block of -inf records right
-    // after the padded keys), and their count.  NULL: the dense pass.  With
-    // n_split = S > 1, workgroup s of a row block takes the list's tiles
-    // s, s + S, s + 2S, .. and writes a partial (M, s) like a key-range split.
+    // after the padded keys), and their count.  NULL: the dense pass.  A row
+    // block with S splits (bs_nsplit) has its list's tiles s, s + S, s + 2S, ..
+    // taken by the workgroup of split s, which writes a partial (M, s) like a
+    // key-range split (n_split > 1 then only marks the partial form).
     const int* bs_list;
     const int* bs_count;
     const int* bs_best;  // per row block: the block whose scores set the starting reference
     const float4* bs_org;  // per row block: origin and fp16-format flag (see fs_bsparse.hip)
+    // work plan (launch_split_plan): per row block its split count, per
+    // workgroup its (row block, split), the number of planned workgroups,
+    // and the grid launched (an upper bound; the rest exit at once).  Partials
+    // go to part[split][n_rows] and the merge takes bs_nsplit[row / 256].
+    const int* bs_nsplit;
+    const int* bs_map;
+    const int* bs_total;
+    int bs_grid;
     int bs_cap;
     int bs_sentinel;
 };
@@ -236,6 +245,9 @@ hipError_t launch_block_boxes(const float* ops, const float* centre, int d, int6
 hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_t n, int gs,
                             bool key, const float* pot, const float* lw2, float c_bias,
                             float4* fit, hipStream_t s);
+// Work plan of the retained-block pass from the kept counts (see LseArgs).
+hipError_t launch_split_plan(const int* count, int nbR, int target, int smax, int* nsplit,
+                             int* map, int* total, hipStream_t s);
 // Kept key blocks of every row block (threshold thr2 = log2(delta / nbK)),
 // their count, and the key block of largest bound.
 // Also the row block's origin for shifted fp16 operands and its format flag

@@ -962,7 +962,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(LseArgs a) {
     float r = 0.f;
     if (i < a.n_rows) {
         float M = -INFINITY, S = 0.f;
-        for (int s = 0; s < a.n_split; ++s) {
+        const int ns = a.bs_nsplit ? a.bs_nsplit[i / 256] : a.n_split;  // block-sparse: per row block
+        for (int s = 0; s < ns; ++s) {
             const float2 p = a.part[(int64_t)s * a.n_rows + i];
             lse_merge(M, S, p.x, p.y);
         }

@@ -52,6 +52,11 @@ namespace {
 constexpr int kSmallWaves = 8;        // waves per workgroup, 32 rows each
 constexpr float kSlack = 8.f;         // R moves to a block maximum more than 2^8 above it
 constexpr float kBigSum = 0x1p64f;    // common path: a block's terms sum to at most this
+// The block-sparse form lets a block's terms reach 2^96 before R moves (a row
+// sums at most 2^27 kept keys, so s stays below 2^123): its rows start from
+// the best block's maximum, which at small eps may sit tens of bits under
+// the row maximum, and should not move for that.
+constexpr float kBigSumSparse = 0x1p96f;
 constexpr float kF16Bound = 512.f;    // fp16 format: sum_c |c x_c| * max|y| <= this
 constexpr float kF16Range = 16384.f;  // fp16 format: |c x|, |y| <= this, |beta| <= twice it
 constexpr int kNbuf = 4;
@@ -133,13 +138,19 @@ __global__ __launch_bounds__(256) void pack_key_records_kernel(
         }
     }
     if (rec16) {
-        // one atomic per wave for each guard word
+        // at most one atomic per wave for each guard word, and none where the
+        // word already holds as much (the maximum is the same every pass, so
+        // after the first waves of a pass almost none is issued: contended
+        // atomics on one word would otherwise serialise the whole grid)
         float wm = ymax;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
         const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
         if ((threadIdx.x & 63) == 0) {
-            if (wm > 0.f) atomicMax(&guard->ymax_bits, __float_as_uint(wm));
+            const unsigned seen = __hip_atomic_load(&guard->ymax_bits, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            if (wm > 0.f && __float_as_uint(wm) > seen)
+                atomicMax(&guard->ymax_bits, __float_as_uint(wm));
             if (wbad) atomicOr(&guard->bad, 1u);
         }
     }
@@ -199,8 +210,19 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 31;
     const int h = lane >> 5;
-    int row_block, split;
-    xcd_work(row_block, split);
+    int row_block, split, nsp = a.n_split;
+    if constexpr (SPARSE) {
+        // planned (row block, split) of this workgroup, XCD-aware over the
+        // 1-D grid; workgroups past the plan have nothing to do
+        int idx, unused;
+        xcd_work(idx, unused);
+        if (idx >= *a.bs_total) return;
+        row_block = a.bs_map[2 * idx];
+        split = a.bs_map[2 * idx + 1];
+        nsp = a.bs_nsplit[row_block];
+    } else {
+        xcd_work(row_block, split);
+    }
     const int row = row_block * (W * 32) + wave * 32 + ln;  // rows are padded: always readable
     constexpr int SUB_BLOCKS = TK / 32;  // 32-key blocks per tile
     const int j0 = SPARSE ? 0 : split * a.keys_per_split;
@@ -208,11 +230,11 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     // sparse: this workgroup's tiles are list tiles split, split + S, ..
     const int* __restrict__ lst =
         SPARSE ? a.bs_list + (int64_t)row_block * a.bs_cap + split * SUB_BLOCKS : nullptr;
-    const int list_step = SPARSE ? a.n_split * SUB_BLOCKS : 0;
+    const int list_step = SPARSE ? nsp * SUB_BLOCKS : 0;
     int ntiles;
     if constexpr (SPARSE) {
         const int all = (a.bs_count[row_block] + SUB_BLOCKS - 1) / SUB_BLOCKS;
-        ntiles = all > split ? (all - split + a.n_split - 1) / a.n_split : 0;
+        ntiles = all > split ? (all - split + nsp - 1) / nsp : 0;
     } else {
         ntiles = (j1 - j0 + TK - 1) / TK;
     }
@@ -293,7 +315,8 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         for (int w = 1; w < 16; w <<= 1)
 #pragma unroll
             for (int q = 0; q < 16; q += 2 * w) e[q] += e[q + w];
-        if (__builtin_amdgcn_ballot_w64(!(e[0] <= kBigSum) || delta != 0.f)) {
+        if (__builtin_amdgcn_ballot_w64(!(e[0] <= (SPARSE ? kBigSumSparse : kBigSum)) ||
+                                        delta != 0.f)) {
             const float t = block_max(acc) - delta;  // block maximum relative to R
             const float dl = t > kSlack ? t : 0.f;
             const float sh = delta + dl;
@@ -583,7 +606,9 @@ hipError_t small_launch(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
         a.key_lw2, a.c_bias, a.krec, f16 ? (_Float16*)a.krec16 : nullptr, (Guard*)a.krec_guard);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-    const dim3 grid((a.n_rows + kSmallWaves * 32 - 1) / (kSmallWaves * 32), a.n_split);
+    const dim3 grid = SPARSE ? dim3(a.bs_grid, 1)
+                             : dim3((a.n_rows + kSmallWaves * 32 - 1) / (kSmallWaves * 32),
+                                    a.n_split);
     lse_small_kernel<KP, SPARSE><<<grid, kSmallWaves * 64, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -618,7 +643,8 @@ size_t small_f32_rec_bytes(int d) { return (size_t)f32_rec_bytes(small_kp(d)); }
 size_t small_f16_rec_bytes(int d) { return small_kp(d) <= 2 ? (size_t)kF16RecBytes : 0; }
 
 hipError_t launch_lse_small_sparse(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
-    if (a.n_split < 1 || !a.bs_list || !a.bs_count || (a.n_split > 1 && !a.part))
+    if (a.n_split < 2 || !a.bs_list || !a.bs_count || !a.part || !a.bs_nsplit || !a.bs_map ||
+        !a.bs_total || a.bs_grid < 1)
         return hipErrorInvalidValue;
     switch (small_kp(a.dp)) {
         case 1: return small_launch<1, true>(a, s, ev_begin);
