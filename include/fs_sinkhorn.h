@@ -351,6 +351,67 @@ fs_status fs_bs_lse_update_g(fs_problem* p, float eps, float delta, const float*
 fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* opts, float delta, float* f,
                                float* g, fs_solve_info* info, void* stream);
 
+/* ---- Coarse (centroid) stage ---------------------------------------------
+ * "FlashSinkhorn 2" explainer, solving at a coarse resolution first and
+ * trusting the lifted solution (no formula on the page; the reading used):
+ * cells are runs of `cell` consecutive points of a Morton-ordered cloud (the
+ * last may be shorter); the coarse problem is the transport between the two
+ * centroid clouds; its potentials are lifted by giving every point its
+ * cell's value; a lift is accepted when the relative L1 marginal errors over
+ * sampled rows and columns,
+ *     sum_{i in S} |r_i - a_i| / sum_{i in S} a_i,  r_i = sum_j P_ij,
+ * (exact, against every point of the other cloud) are at most a tolerance,
+ * else the coarse iteration continues.  The lift's error is set by the cell
+ * size against sqrt(eps), so the fine block-sparse stage finishes the solve. */
+
+/* Centroids C (nc x d, weighted means, fp64 sums in a fixed order) and
+ * weights W (nc, sums) of the runs of `cell` points of P (n x d, d <= 8) with
+ * weights w; nc = ceil(n / cell).  Device arrays; outputs may not overlap
+ * inputs. */
+fs_status fs_centroids(const float* P, const float* w, int64_t n, int32_t d, int32_t cell,
+                       float* C, float* W, void* stream);
+
+/* f[i] = F[i / cell] for i < n (device arrays). */
+fs_status fs_lift(const float* F, int64_t n, int32_t cell, float* f, void* stream);
+
+/* The sampled marginal check of (f, g) on the clouds X (n x d), Y (m x d)
+ * with weights a, b (fp32 device arrays, squared-Euclidean cost computed in
+ * fp32 from the points): out2[0] = relative L1 error of the rows listed in
+ * `rows` (device int32), out2[1] that of the columns in `cols` (device
+ * float[2]); an index outside its cloud is clamped into it.  workspace:
+ * fs_sampled_workspace_bytes(nrows, ncols) bytes, 256-byte aligned.  Cost:
+ * (nrows m + ncols n) d. */
+size_t fs_sampled_workspace_bytes(int32_t nrows, int32_t ncols);
+fs_status fs_sampled_marginal_error(const float* X, const float* Y, const float* a,
+                                    const float* b, int64_t n, int64_t m, int32_t d, float eps,
+                                    const float* f, const float* g, const int32_t* rows,
+                                    int32_t nrows, const int32_t* cols, int32_t ncols,
+                                    float* out2, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+typedef struct {
+    int32_t rounds;    /* checks made */
+    int32_t accepted;  /* 1 if the last check passed */
+    float err_rows;    /* the last check's relative errors */
+    float err_cols;
+} fs_coarse_info;
+
+/* The coarse stage: fs_sinkhorn_solve on `coarse` (a problem built by
+ * fs_potentials_init on the fs_centroids of both clouds with this `cell`)
+ * with `opts` into F, G; then repeatedly lift them into f (n) and g (m),
+ * check them on the sampled rows and columns at opts->eps_end, and, unless
+ * both errors are at most check_tol or max_rounds checks were made, run
+ * more_iters further coarse iterations from (F, G).  Synchronises once per
+ * check.  workspace: fs_sampled_workspace_bytes(nrows, ncols) + 256 bytes.
+ * f and g are then a warm start for the fine (block-sparse) solve. */
+fs_status fs_bs_coarse_start(fs_problem* coarse, const fs_solve_opts* opts, int32_t more_iters,
+                             const float* X, const float* Y, const float* a, const float* b,
+                             int64_t n, int64_t m, int32_t d, int32_t cell, float check_tol,
+                             int32_t max_rounds, const int32_t* rows, int32_t nrows,
+                             const int32_t* cols, int32_t ncols, float* F, float* G, float* f,
+                             float* g, void* workspace, size_t workspace_bytes,
+                             fs_coarse_info* info, void* stream);
+
 /* Introspection (host): side 0 = the f-update (rows X, keys Y), side 1 = the
  * g-update.  fs_bs_shape: block counts and the row stride of the lists.
  * fs_bs_read_screen (synchronises): the kept-block count of every row block

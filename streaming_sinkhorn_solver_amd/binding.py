@@ -25,7 +25,8 @@ __all__ = [
     "COST_SQEUCLIDEAN", "COST_COSINE",
     "fs_morton_workspace_bytes", "fs_morton_sort", "fs_unpermute", "fs_bs_workspace_bytes",
     "fs_bs_attach", "fs_bs_lse_update_f", "fs_bs_lse_update_g", "fs_bs_sinkhorn_solve",
-    "fs_bs_shape", "fs_bs_read_screen",
+    "fs_bs_shape", "fs_bs_read_screen", "fs_centroids", "fs_lift",
+    "fs_sampled_marginal_error", "fs_bs_coarse_start",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -61,6 +62,11 @@ class SolveInfo(ctypes.Structure):
 
 class HvpInfo(ctypes.Structure):
     _fields_ = [("cg_iters", ctypes.c_int32), ("cg_residual", ctypes.c_float)]
+
+
+class CoarseInfo(ctypes.Structure):
+    _fields_ = [("rounds", ctypes.c_int32), ("accepted", ctypes.c_int32),
+                ("err_rows", ctypes.c_float), ("err_cols", ctypes.c_float)]
 
 
 class FsError(RuntimeError):
@@ -152,6 +158,19 @@ def load():
     lib.fs_bs_shape.argtypes = [_vp, i32] + [ctypes.POINTER(i32)] * 3
     lib.fs_bs_read_screen.restype = ctypes.c_int
     lib.fs_bs_read_screen.argtypes = [_vp, i32, _vp, _vp, _vp]
+    lib.fs_centroids.restype = ctypes.c_int
+    lib.fs_centroids.argtypes = [_fp, _fp, i64, i32, i32, _fp, _fp, _vp]
+    lib.fs_lift.restype = ctypes.c_int
+    lib.fs_lift.argtypes = [_fp, i64, i32, _fp, _vp]
+    lib.fs_sampled_workspace_bytes.restype = sz
+    lib.fs_sampled_workspace_bytes.argtypes = [i32, i32]
+    lib.fs_sampled_marginal_error.restype = ctypes.c_int
+    lib.fs_sampled_marginal_error.argtypes = [_fp, _fp, _fp, _fp, i64, i64, i32, f32, _fp, _fp,
+                                              _fp, i32, _fp, i32, _fp, _vp, sz, _vp]
+    lib.fs_bs_coarse_start.restype = ctypes.c_int
+    lib.fs_bs_coarse_start.argtypes = [_vp, ctypes.POINTER(SolveOpts), i32, _fp, _fp, _fp, _fp,
+                                       i64, i64, i32, i32, f32, i32, _fp, i32, _fp, i32, _fp,
+                                       _fp, _fp, _fp, _vp, sz, ctypes.POINTER(CoarseInfo), _vp]
     _LIB = lib
     return lib
 
@@ -499,6 +518,69 @@ def fs_bs_read_screen(p: Problem, side: int, lists: bool = False, stream=None):
                                     L.ctypes.data if lists else None, _stream(stream)),
            "fs_bs_read_screen")
     return (counts, L) if lists else counts
+
+
+def fs_centroids(P, w, cell: int, C=None, W=None, stream=None):
+    """Centroids and weights of runs of `cell` points; returns (C, W)."""
+    n, d = P.shape
+    nc = (n + cell - 1) // cell if cell >= 1 else 1  # (the library rejects cell < 1)
+    C = torch.empty((nc, d), device=P.device) if C is None else C
+    W = torch.empty(nc, device=P.device) if W is None else W
+    _check(load().fs_centroids(_dev(P, "P", n * d), _dev(w, "w", n), n, d, int(cell),
+                               _dev(C, "C", nc * d), _dev(W, "W", nc), _stream(stream)),
+           "fs_centroids")
+    return C, W
+
+
+def fs_lift(F, n: int, cell: int, f=None, stream=None):
+    f = torch.empty(n, device=F.device) if f is None else f
+    _check(load().fs_lift(_dev(F, "F", (n + cell - 1) // cell), n, int(cell), _dev(f, "f", n),
+                          _stream(stream)), "fs_lift")
+    return f
+
+
+def fs_sampled_marginal_error(X, Y, a, b, f, g, eps: float, rows, cols, out2=None,
+                              workspace=None, stream=None):
+    """(err_rows, err_cols) as a 2-element device tensor."""
+    lib = load()
+    n, d = X.shape
+    m = Y.shape[0]
+    nr, nc = rows.numel(), cols.numel()
+    out2 = torch.empty(2, device=X.device) if out2 is None else out2
+    need = lib.fs_sampled_workspace_bytes(nr, nc)
+    workspace = torch.empty(need, dtype=torch.uint8, device=X.device) if workspace is None \
+        else workspace
+    _check(lib.fs_sampled_marginal_error(
+        _dev(X, "X", n * d), _dev(Y, "Y", m * d), _dev(a, "a", n), _dev(b, "b", m), n, m, d,
+        float(eps), _dev(f, "f", n), _dev(g, "g", m), _idev(rows, "rows", nr), nr,
+        _idev(cols, "cols", nc), nc, _dev(out2, "out2", 2), workspace.data_ptr(),
+        workspace.numel(), _stream(stream)), "fs_sampled_marginal_error")
+    return out2
+
+
+def fs_bs_coarse_start(coarse: Problem, X, Y, a, b, cell: int, f, g, F, G, rows, cols, *,
+                       eps_end: float, iters_per_stage: int, n_stages: int = 1,
+                       eps_start: Optional[float] = None, more_iters: int = 10,
+                       check_tol: float = 1e-2, max_rounds: int = 5, stream=None) -> dict:
+    """The coarse stage (see include/fs_sinkhorn.h); fills F, G (coarse) and
+    f, g (lifted); returns rounds, accepted and the last errors."""
+    lib = load()
+    n, d = X.shape
+    m = Y.shape[0]
+    nr, nc = rows.numel(), cols.numel()
+    need = lib.fs_sampled_workspace_bytes(nr, nc) + 256
+    ws = torch.empty(need, dtype=torch.uint8, device=X.device)
+    opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
+                     float(eps_end), int(iters_per_stage), 0.0, 1, 0, 0)
+    info = CoarseInfo()
+    _check(lib.fs_bs_coarse_start(
+        coarse.handle, ctypes.byref(opts), int(more_iters), _dev(X, "X", n * d),
+        _dev(Y, "Y", m * d), _dev(a, "a", n), _dev(b, "b", m), n, m, d, int(cell),
+        float(check_tol), int(max_rounds), _idev(rows, "rows", nr), nr, _idev(cols, "cols", nc),
+        nc, _dev(F, "F", coarse.n), _dev(G, "G", coarse.m), _dev(f, "f", n), _dev(g, "g", m),
+        ws.data_ptr(), need, ctypes.byref(info), _stream(stream)), "fs_bs_coarse_start")
+    return {"rounds": info.rounds, "accepted": bool(info.accepted), "err_rows": info.err_rows,
+            "err_cols": info.err_cols}
 
 
 def solve(X, Y, a, b, *, eps: float, iters: int, prec="auto", n_stages: int = 1,

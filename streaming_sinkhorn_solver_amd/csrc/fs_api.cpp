@@ -1380,6 +1380,114 @@ fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delt
     return FS_OK;
 }
 
+fs_status fs_centroids(const float* P, const float* w, int64_t n, int32_t d, int32_t cell,
+                       float* C, float* W, void* stream) {
+    if (!P || !w || !C || !W) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (n < 1 || n > 0x7fffffffLL || d < 1 || d > 8 || cell < 1)
+        return fail(FS_ERR_INVALID_ARG, "need 1 <= n <= 2^31-1, 1 <= d <= 8, cell >= 1");
+    const int64_t nc = (n + cell - 1) / cell;
+    if (overlaps(C, 4 * (size_t)nc * d, P, 4 * (size_t)n * d) ||
+        overlaps(W, 4 * (size_t)nc, w, 4 * (size_t)n))
+        return fail(FS_ERR_INVALID_ARG, "outputs may not overlap inputs");
+    hipError_t e = launch_centroids(P, w, n, d, cell, C, W, (hipStream_t)stream);
+    return e == hipSuccess ? FS_OK : hip_fail(e, "fs_centroids");
+}
+
+fs_status fs_lift(const float* F, int64_t n, int32_t cell, float* f, void* stream) {
+    if (!F || !f) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (n < 1 || n > 0x7fffffffLL || cell < 1)
+        return fail(FS_ERR_INVALID_ARG, "need 1 <= n <= 2^31-1 and cell >= 1");
+    if (overlaps(F, 4 * (size_t)((n + cell - 1) / cell), f, 4 * (size_t)n))
+        return fail(FS_ERR_INVALID_ARG, "f overlaps F");
+    hipError_t e = launch_lift(F, n, cell, f, (hipStream_t)stream);
+    return e == hipSuccess ? FS_OK : hip_fail(e, "fs_lift");
+}
+
+size_t fs_sampled_workspace_bytes(int32_t nrows, int32_t ncols) {
+    if (nrows < 0 || ncols < 0) return 0;
+    return up(sizeof(float2) * ((size_t)nrows + ncols + 1), kAlign);
+}
+
+fs_status fs_sampled_marginal_error(const float* X, const float* Y, const float* a,
+                                    const float* b, int64_t n, int64_t m, int32_t d, float eps,
+                                    const float* f, const float* g, const int32_t* rows,
+                                    int32_t nrows, const int32_t* cols, int32_t ncols,
+                                    float* out2, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    if (!X || !Y || !a || !b || !f || !g || !out2 || (nrows > 0 && !rows) || (ncols > 0 && !cols))
+        return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (n < 1 || m < 1 || n > 0x7fffffffLL || m > 0x7fffffffLL || d < 1 || d > 8)
+        return fail(FS_ERR_INVALID_ARG, "need 1 <= n, m <= 2^31-1 and 1 <= d <= 8");
+    if (nrows < 0 || ncols < 0 || nrows > 1 << 20 || ncols > 1 << 20)
+        return fail(FS_ERR_INVALID_ARG, "sample counts must be in [0, 2^20]");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!workspace || (uintptr_t)workspace % kAlign ||
+        workspace_bytes < fs_sampled_workspace_bytes(nrows, ncols))
+        return fail(FS_ERR_WORKSPACE, "workspace must be 256-byte aligned and hold %zu bytes",
+                    fs_sampled_workspace_bytes(nrows, ncols));
+    const float c_bias = (float)(1.4426950408889634 / (double)eps);
+    hipError_t e = launch_sampled_marginal(X, Y, a, b, n, m, d, c_bias, f, g, rows, nrows, cols,
+                                           ncols, (float2*)workspace, out2, (hipStream_t)stream);
+    return e == hipSuccess ? FS_OK : hip_fail(e, "fs_sampled_marginal_error");
+}
+
+fs_status fs_bs_coarse_start(fs_problem* coarse, const fs_solve_opts* opts, int32_t more_iters,
+                             const float* X, const float* Y, const float* a, const float* b,
+                             int64_t n, int64_t m, int32_t d, int32_t cell, float check_tol,
+                             int32_t max_rounds, const int32_t* rows, int32_t nrows,
+                             const int32_t* cols, int32_t ncols, float* F, float* G, float* f,
+                             float* g, void* workspace, size_t workspace_bytes,
+                             fs_coarse_info* info, void* stream) {
+    if (!coarse || !opts || !F || !G || !f || !g) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    if (cell < 1 || max_rounds < 1 || more_iters < 0 || !(check_tol >= 0.f))
+        return fail(FS_ERR_INVALID_ARG, "need cell >= 1, max_rounds >= 1, more_iters >= 0, "
+                                        "check_tol >= 0");
+    if (coarse->n != (n + cell - 1) / cell || coarse->m != (m + cell - 1) / cell ||
+        coarse->d != d)
+        return fail(FS_ERR_INVALID_ARG, "the coarse problem must hold the centroids of cells "
+                                        "of %d points of both clouds", cell);
+    if (workspace_bytes < fs_sampled_workspace_bytes(nrows, ncols) + kAlign)
+        return fail(FS_ERR_WORKSPACE, "workspace must hold %zu bytes",
+                    fs_sampled_workspace_bytes(nrows, ncols) + kAlign);
+    hipStream_t s = (hipStream_t)stream;
+    fs_status st = fs_sinkhorn_solve(coarse, opts, F, G, nullptr, stream);
+    if (st != FS_OK && st != FS_ERR_NOT_CONVERGED) return st;
+    float* out2 = (float*)((char*)workspace + fs_sampled_workspace_bytes(nrows, ncols));
+    fs_solve_opts more{};
+    more.n_stages = 1;
+    more.eps_end = opts->eps_end;
+    more.eps_start = opts->eps_end;
+    more.iters_per_stage = more_iters;
+    more.warm_start = 1;
+    float err[2] = {0.f, 0.f};
+    int k = 0;
+    bool ok = false;
+    for (;;) {
+        hipError_t e;
+        if ((e = launch_lift(F, n, cell, f, s)) != hipSuccess ||
+            (e = launch_lift(G, m, cell, g, s)) != hipSuccess)
+            return hip_fail(e, "lift");
+        if ((st = fs_sampled_marginal_error(X, Y, a, b, n, m, d, opts->eps_end, f, g, rows, nrows,
+                                            cols, ncols, out2, workspace, workspace_bytes,
+                                            stream)) != FS_OK)
+            return st;
+        if ((e = hipMemcpyAsync(err, out2, sizeof(err), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+            (e = hipStreamSynchronize(s)) != hipSuccess)
+            return hip_fail(e, "check readback");
+        ++k;
+        ok = err[0] <= check_tol && err[1] <= check_tol;
+        if (ok || k >= max_rounds) break;
+        if ((st = fs_sinkhorn_solve(coarse, &more, F, G, nullptr, stream)) != FS_OK) return st;
+    }
+    if (info) {
+        info->rounds = k;
+        info->accepted = ok ? 1 : 0;
+        info->err_rows = err[0];
+        info->err_cols = err[1];
+    }
+    return FS_OK;
+}
+
 fs_status fs_bs_shape(const fs_problem* p, int32_t side, int32_t* n_row_blocks,
                       int32_t* n_key_blocks, int32_t* list_stride) {
     if (!p || !p->bs_on) return fail(FS_ERR_INVALID_ARG, "NULL handle or fs_bs_attach not called");

@@ -636,9 +636,140 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int* __restrict_
     if (tid == 0) total[0] = carry_s;
 }
 
+// ---------------------------------------------------------------- coarse stage
+// "FlashSinkhorn 2" explainer, solving at a coarse resolution first: cells
+// are runs of `cell` consecutive (Morton-ordered) points; a cell's centroid
+// is the weighted mean of its points (fp64 sums, fixed order), its weight
+// their sum.
+__global__ __launch_bounds__(256) void centroid_kernel(const float* __restrict__ P,
+                                                       const float* __restrict__ w, int64_t n,
+                                                       int d, int cell, int64_t nc,
+                                                       float* __restrict__ C,
+                                                       float* __restrict__ W) {
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k >= nc) return;
+    const int64_t i0 = k * cell, i1 = min(n, i0 + cell);
+    double sw = 0.0, sx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t i = i0; i < i1; ++i) {
+        const double wi = w[i];
+        sw += wi;
+        for (int c = 0; c < d; ++c) sx[c] += wi * (double)P[i * d + c];
+    }
+    W[k] = (float)sw;
+    for (int c = 0; c < d; ++c) C[k * d + c] = (float)(sx[c] / sw);
+}
+
+// The lift: every point takes its cell's potential.
+__global__ __launch_bounds__(256) void lift_kernel(const float* __restrict__ F, int64_t n,
+                                                   int cell, float* __restrict__ f) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) f[i] = F[i / cell];
+}
+
+// The sampled marginal check (trusting the lifted solution): for sampled
+// point q of one side (one workgroup each), its exact marginal under (f, g)
+// against every point of the other side, as the pair (|r_q - w_q|, w_q):
+//   r_q / w_q = 2^(pot_q c_bias + LSE2_j (log2 w'_j + (pot'_j - C_qj) c_bias)).
+__global__ __launch_bounds__(256) void sampled_marginal_kernel(
+    const float* __restrict__ P, const float* __restrict__ w, const float* __restrict__ pot,
+    int64_t np_, const int32_t* __restrict__ idx, const float* __restrict__ Q,
+    const float* __restrict__ wq, const float* __restrict__ potq, int64_t mq, int d,
+    float c_bias, float2* __restrict__ out) {
+    __shared__ float smax[256], ssum[256];
+    // (an index outside [0, np_) is clamped into it)
+    const int64_t i = min((int64_t)max(idx[blockIdx.x], 0), np_ - 1);
+    float x[8];
+    for (int c = 0; c < 8; ++c) x[c] = c < d ? P[i * d + c] : 0.f;
+    float M = -INFINITY, S = 0.f;
+    for (int64_t j = threadIdx.x; j < mq; j += 256) {
+        float cost = 0.f;
+        for (int c = 0; c < d; ++c) {
+            const float t = x[c] - Q[j * d + c];
+            cost = fmaf(t, t, cost);
+        }
+        const float z = __log2f(wq[j]) + (potq[j] - cost) * c_bias;
+        lse_merge(M, S, z, 1.f);
+    }
+    smax[threadIdx.x] = M;
+    ssum[threadIdx.x] = S;
+    __syncthreads();
+    for (int o = 128; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o) {
+            float m1 = smax[threadIdx.x], s1 = ssum[threadIdx.x];
+            lse_merge(m1, s1, smax[threadIdx.x + o], ssum[threadIdx.x + o]);
+            smax[threadIdx.x] = m1;
+            ssum[threadIdx.x] = s1;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const float z = pot[i] * c_bias + smax[0] + lg2(ssum[0]);
+        out[blockIdx.x] = make_float2(w[i] * fabsf(ex2(z) - 1.f), w[i]);
+    }
+}
+
+// (sum |r - w|) / (sum w) over the samples of each side, fixed order.
+__global__ __launch_bounds__(256) void sampled_reduce_kernel(const float2* __restrict__ part,
+                                                             int nrows, int ncols,
+                                                             float* __restrict__ out2) {
+    __shared__ double se[256], sw[256];
+    for (int side = 0; side < 2; ++side) {
+        const int base = side ? nrows : 0, cnt = side ? ncols : nrows;
+        double e = 0.0, ww = 0.0;
+        for (int k = threadIdx.x; k < cnt; k += 256) {
+            e += part[base + k].x;
+            ww += part[base + k].y;
+        }
+        se[threadIdx.x] = e;
+        sw[threadIdx.x] = ww;
+        __syncthreads();
+        for (int o = 128; o >= 1; o >>= 1) {
+            if ((int)threadIdx.x < o) {
+                se[threadIdx.x] += se[threadIdx.x + o];
+                sw[threadIdx.x] += sw[threadIdx.x + o];
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) out2[side] = sw[0] > 0.0 ? (float)(se[0] / sw[0]) : 0.f;
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_centroids(const float* P, const float* w, int64_t n, int d, int cell,
+                            float* C, float* W, hipStream_t s) {
+    const int64_t nc = (n + cell - 1) / cell;
+    centroid_kernel<<<(unsigned)((nc + 255) / 256), 256, 0, s>>>(P, w, n, d, cell, nc, C, W);
+    return hipGetLastError();
+}
+
+hipError_t launch_lift(const float* F, int64_t n, int cell, float* f, hipStream_t s) {
+    lift_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(F, n, cell, f);
+    return hipGetLastError();
+}
+
+hipError_t launch_sampled_marginal(const float* X, const float* Y, const float* a,
+                                   const float* b, int64_t n, int64_t m, int d, float c_bias,
+                                   const float* f, const float* g, const int32_t* rows,
+                                   int nrows, const int32_t* cols, int ncols, float2* part,
+                                   float* out2, hipStream_t s) {
+    hipError_t e;
+    if (nrows > 0) {
+        sampled_marginal_kernel<<<nrows, 256, 0, s>>>(X, a, f, n, rows, Y, b, g, m, d, c_bias,
+                                                      part);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (ncols > 0) {
+        sampled_marginal_kernel<<<ncols, 256, 0, s>>>(Y, b, g, m, cols, X, a, f, n, d, c_bias,
+                                                      part + nrows);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    sampled_reduce_kernel<<<1, 256, 0, s>>>(part, nrows, ncols, out2);
+    return hipGetLastError();
+}
 
 hipError_t launch_split_plan(const int* count, int nbR, int target, int smax, int* nsplit,
                              int* map, int* total, hipStream_t s) {

@@ -245,6 +245,18 @@ hipError_t launch_block_boxes(const float* ops, const float* centre, int d, int6
 hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_t n, int gs,
                             bool key, const float* pot, const float* lw2, float c_bias,
                             float4* fit, hipStream_t s);
+// Coarse stage: centroids (weighted means) and weights of runs of `cell`
+// points (d <= 8); the lift f[i] = F[i / cell]; the sampled marginal check
+// (out2 = relative L1 marginal error over the sampled rows, then columns;
+// part: nrows + ncols float2 of scratch).
+hipError_t launch_centroids(const float* P, const float* w, int64_t n, int d, int cell,
+                            float* C, float* W, hipStream_t s);
+hipError_t launch_lift(const float* F, int64_t n, int cell, float* f, hipStream_t s);
+hipError_t launch_sampled_marginal(const float* X, const float* Y, const float* a,
+                                   const float* b, int64_t n, int64_t m, int d, float c_bias,
+                                   const float* f, const float* g, const int32_t* rows,
+                                   int nrows, const int32_t* cols, int ncols, float2* part,
+                                   float* out2, hipStream_t s);
 // Work plan of the retained-block pass from the kept counts (see LseArgs).
 hipError_t launch_split_plan(const int* count, int nbR, int target, int smax, int* nsplit,
                              int* map, int* total, hipStream_t s);
