@@ -191,17 +191,16 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     constexpr int TK = small_tile_keys(KP);
     constexpr int F32_TILE = TK * f32_rec_bytes(KP);
     constexpr int F16_TILE = HAS_F16 ? TK * kF16RecBytes : 0;
-    // (the sparse form's shifted fp16 operands are made in LDS: a tile of fp32
-    // records fills the lower half of its slot, and the converted records of
-    // its first and second 256 keys go to the upper halves of that slot and of
-    // the slot two ahead, which no copy in flight touches)
+    // The tile ring is kNbuf slots of the larger tile.  The sparse form, whose
+    // tiles are gathered from scattered blocks and wait longer for their
+    // copies, cuts the same bytes into more slots when its tiles are fp32
+    // records (8 slots; 6 slots and a conversion area for the shifted fp16
+    // operands, see run()).
     constexpr int BUF_BYTES = F16_TILE > F32_TILE ? F16_TILE : F32_TILE;
     constexpr bool SHIFT = SPARSE && HAS_F16;
-    constexpr int NB = kNbuf;
-    static_assert(!SHIFT || (TK == W * 64 && F32_TILE * 2 <= BUF_BYTES && F16_TILE == BUF_BYTES &&
-                             NB == 4),
-                  "shifted conversion: one key per thread, fp32 tile in half a slot");
-    __shared__ __attribute__((aligned(16))) uint4 tbuf[NB][BUF_BYTES / 16];
+    constexpr int RING_BYTES = kNbuf * BUF_BYTES;
+    static_assert(!SHIFT || TK == W * 64, "shifted conversion: one key per thread");
+    __shared__ __attribute__((aligned(16))) uint4 tbuf[RING_BYTES / 16];
     __shared__ __attribute__((aligned(16))) uint4 ibuf[SPARSE ? 64 : 1];  // sparse: starting block
     __shared__ float red[16];
 
@@ -212,11 +211,16 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     const int h = lane >> 5;
     int row_block, split, nsp = a.n_split;
     if constexpr (SPARSE) {
-        // planned (row block, split) of this workgroup, XCD-aware over the
-        // 1-D grid; workgroups past the plan have nothing to do
-        int idx, unused;
-        xcd_work(idx, unused);
-        if (idx >= *a.bs_total) return;
+        // planned (row block, split) of this workgroup: the plan's entries
+        // are dealt to the 8 XCDs (workgroups go to XCD id % 8) in
+        // contiguous, equal shares, so that neighbouring row blocks share an
+        // L2 and every XCD has work; the grid is an upper bound of the plan
+        // and the workgroups past an XCD's share have nothing to do
+        const int total = *a.bs_total;
+        const int id = blockIdx.x, x = id & 7, kk = id >> 3;
+        const int q = total >> 3, r = total & 7;
+        if (kk >= q + (x < r ? 1 : 0)) return;
+        const int idx = x * q + min(x, r) + kk;
         row_block = a.bs_map[2 * idx];
         split = a.bs_map[2 * idx + 1];
         nsp = a.bs_nsplit[row_block];
@@ -339,7 +343,8 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     // Shifted fp16 records of nkeys fp32 records at src (one key per thread):
     // y~ - o_y split into fp16 parts, the bias beta + c o_x.(y~ - o_y) into
     // three; a -inf bias (padding) stays -inf with zero parts.  Keys 0..255 go
-    // to dst0, 256..511 to dst1.
+    // to dst0, 256..511 to dst1 (each 256 records after the other when the
+    // two are contiguous).
     auto convert = [&](const char* src, int nkeys, char* dst0,
                        char* dst1) __attribute__((always_inline)) {
         const int t = threadIdx.x;
@@ -390,6 +395,13 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         constexpr int REC_BYTES = F16 ? kF16RecBytes : f32_rec_bytes(KP);  // as multiplied
         constexpr int DREC_BYTES = MODE == 1 ? kF16RecBytes : f32_rec_bytes(KP);  // as loaded
         constexpr int TILE_BYTES = TK * DREC_BYTES;
+        // ring of this format: NB slots of SLOT bytes (+ the conversion area)
+        constexpr int NB = !SPARSE ? kNbuf : (MODE == 1 ? kNbuf : (MODE == 0 ? 8 : 6));
+        constexpr int SLOT = !SPARSE ? BUF_BYTES : TILE_BYTES;
+        constexpr int CONV_BYTES = TK * kF16RecBytes;
+        static_assert(NB * SLOT + (CONV ? CONV_BYTES : 0) <= RING_BYTES, "ring fits");
+        char* const ring = (char*)&tbuf[0];
+        char* const conv = ring + NB * SLOT;  // MODE 2: converted records of one tile
         constexpr int TILE_INSTR = TILE_BYTES / 1024;  // wave-wide 1 KiB loads per tile
         constexpr int INSTR_PER_WAVE = (TILE_INSTR + W - 1) / W;
         constexpr int MIN_INSTR = TILE_INSTR / W;
@@ -422,10 +434,10 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
                             if (lane / LPB == q) J = ent[q];
                         const uint32_t Jc = min((uint32_t)J, (uint32_t)a.bs_sentinel);
                         dma_to_lds16(recs, Jc * (uint32_t)BLK + (uint32_t)(lane % LPB) * 16u,
-                                     &tbuf[slot][L * 64]);
+                                     ring + slot * SLOT + L * 1024);
                     } else {
                         dma_to_lds16(recs + (int64_t)k * TILE_BYTES + L * 1024, lane16,
-                                     &tbuf[slot][L * 64]);
+                                     ring + slot * SLOT + L * 1024);
                     }
                 }
             }
@@ -498,13 +510,12 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         if (ntiles > 0) {
             f32x16 acc;
             if constexpr (CONV) {
-                char* up0 = (char*)&tbuf[0][0] + BUF_BYTES / 2;
-                convert((const char*)&ibuf[0], 32, up0, up0);
+                convert((const char*)&ibuf[0], 32, conv, conv);
                 __syncthreads();
-                scores(up0, acc);
+                scores(conv, acc);
                 __syncthreads();  // rewritten by the first tile's conversion
             } else {
-                scores(SPARSE ? (const char*)&ibuf[0] : (const char*)&tbuf[0][0], acc);
+                scores(SPARSE ? (const char*)&ibuf[0] : ring, acc);
             }
             const float t = block_max(acc);
             R = t > -INFINITY ? t : 0.f;
@@ -513,20 +524,14 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         for (int t = 0; t < ntiles; ++t) {
             const int slot = t % NB;
             issue_tile(min(t + NB - 1, ntiles - 1), (t + NB - 1) % NB);
-            const char* tb = (const char*)&tbuf[slot][0];
-            // 32-key block u of the tile as multiplied
-            const char* tb2 = tb;
+            const char* tb = ring + slot * SLOT;
             if constexpr (CONV) {
-                char* up0 = (char*)&tbuf[slot][0] + BUF_BYTES / 2;
-                char* up1 = (char*)&tbuf[(slot + 2) % NB][0] + BUF_BYTES / 2;
-                convert(tb, TK, up0, up1);
+                convert(tb, TK, conv, conv + (TK / 2) * kF16RecBytes);
                 stage_barrier();
-                tb = up0;
-                tb2 = up1 - (SUB / 2) * 32 * REC_BYTES;
+                tb = conv;
             }
-            auto blk = [&](int u) __attribute__((always_inline)) {
-                return (CONV && u >= SUB / 2 ? tb2 : tb) + u * 32 * REC_BYTES;
-            };
+            // 32-key block u of the tile as multiplied
+            auto blk = [&](int u) __attribute__((always_inline)) { return tb + u * 32 * REC_BYTES; };
 #pragma unroll
             for (int q = 0; q < 16; ++q) cm[q] = -R;
             delta = 0.f;
