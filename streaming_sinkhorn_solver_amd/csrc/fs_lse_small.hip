@@ -294,6 +294,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     float R = 0.f;      // reference: the running maximum, moved lazily
     float s = 0.f;      // sum of 2^(z2 - R) over the keys seen
     float delta = 0.f;  // R minus the reference baked into cm (moves within a tile)
+    float baked = 0.f;  // sparse form: the reference baked into cm now (refreshed on a move)
     f32x16 cm;          // MFMA C operand: minus the reference, refreshed per tile
 #pragma unroll
     for (int q = 0; q < 16; ++q) cm[q] = 0.f;
@@ -310,7 +311,15 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     // sum costs one compare; the maximum is only formed on the other path,
     // which moves R, where needed, to the block maximum.  Only per-lane
     // scalars change, so the common path carries no register-tuple copies.
-    auto epilogue = [&](const f32x16& acc) __attribute__((always_inline)) {
+    // REBAKE: bk is the reference baked into cm when acc's matrix instruction
+    // was issued, and a move re-bakes cm, so that only the block already in
+    // flight takes the slow path; taken by the sparse form's formats that
+    // serve small eps, whose rows move often (their start is shared by 256
+    // rows).  Otherwise one baked reference per tile, R minus it in delta (a
+    // loop-invariant cm keeps the common path free of register-tuple copies).
+    auto epilogue = [&](const f32x16& acc, float bk, auto rebake_c) __attribute__((always_inline)) {
+        constexpr bool REBAKE = decltype(rebake_c)::value;
+        const float dlt = REBAKE ? R - bk : delta;
         float e[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) e[q] = ex2(acc[q]);
@@ -320,10 +329,10 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
 #pragma unroll
             for (int q = 0; q < 16; q += 2 * w) e[q] += e[q + w];
         if (__builtin_amdgcn_ballot_w64(!(e[0] <= (SPARSE ? kBigSumSparse : kBigSum)) ||
-                                        delta != 0.f)) {
-            const float t = block_max(acc) - delta;  // block maximum relative to R
+                                        dlt != 0.f)) {
+            const float t = block_max(acc) - dlt;  // block maximum relative to R
             const float dl = t > kSlack ? t : 0.f;
-            const float sh = delta + dl;
+            const float sh = dlt + dl;
 #pragma unroll
             for (int q = 0; q < 16; ++q) e[q] = ex2(acc[q] - sh);
             // same summation tree as the common path: a lane that does not
@@ -334,7 +343,13 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
                 for (int q = 0; q < 16; q += 2 * w) e[q] += e[q + w];
             s = s * ex2(-dl) + e[0];
             R += dl;
-            delta = sh;
+            if constexpr (REBAKE) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) cm[q] = -R;
+                baked = R;
+            } else {
+                delta = sh;
+            }
         } else {
             s += e[0];
         }
@@ -535,14 +550,20 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
 #pragma unroll
             for (int q = 0; q < 16; ++q) cm[q] = -R;
             delta = 0.f;
+            baked = R;
             f32x16 acc0, acc1;
             scores(blk(0), acc0);
+            float b0 = baked, b1;
 #pragma unroll
             for (int u = 0; u < SUB; u += 2) {
                 scores(blk(u + 1), acc1);
-                epilogue(acc0);
-                if (u + 2 < SUB) scores(blk(u + 2), acc0);
-                epilogue(acc1);
+                b1 = baked;
+                epilogue(acc0, b0, std::integral_constant<bool, SPARSE && MODE != 1>{});
+                if (u + 2 < SUB) {
+                    scores(blk(u + 2), acc0);
+                    b0 = baked;
+                }
+                epilogue(acc1, b1, std::integral_constant<bool, SPARSE && MODE != 1>{});
             }
             // tiles issued after tile t+1: t+2 .. t+NB-1
             if constexpr (MIN_INSTR == 0)
