@@ -14,7 +14,11 @@ by translation invariance and by the single-target closed form
 (``tests/test_oracle_gradient.py``).  ``oracle/hvp.py`` (numpy, dense) holds
 the Hessian-vector product, pinned by finite differences of the gradient at
 re-converged potentials, symmetry and a closed form
-(``tests/test_oracle_hvp.py``).
+(``tests/test_oracle_hvp.py``).  ``oracle/blocksparse.py`` (numpy) holds the
+block-sparse form (Morton order, block bounds, screening, retained-block
+update; ``tests/test_oracle_blocksparse.py``) and ``oracle/coarse.py`` its
+coarse stage (centroids, lift, sampled marginal check;
+``tests/test_oracle_coarse.py``).
 """
 from __future__ import annotations
 
