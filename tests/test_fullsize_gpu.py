@@ -230,3 +230,64 @@ def test_full_size_block_sparse(fs, name, eps, delta):
         print(f"  row block {I}: kept {len(kept)} of {nbK} key blocks, largest skipped mass "
               f"{mass.max():.2e} (bound {delta / nbK:.2e})")
         assert mass.max() < delta / nbK * 1.001
+
+
+def test_full_size_coarse_stage_and_pipeline(fs):
+    """The two-stage solve of the block-sparse form at 250k x 250k (the
+    bench's fs2 pipeline): centroids against the oracle's (1e-6 relative),
+    the sampled check against the oracle's on the lifted potentials (1e-4
+    relative), then the block-sparse solve from the lift to a 1% residual,
+    whose result is checked against the dense oracle update on 512 sampled
+    rows through the certificate (the last g-update makes the columns exact,
+    so the rows carry the residual)."""
+    import torch
+
+    from oracle import blocksparse as obs
+    from oracle import coarse as oc
+
+    B = fs
+    w = workloads.make("fs2")
+    eps, cell = w.eps, 8
+    Xs, a_s, _ = B.fs_morton_sort(dev(w.X), dev(w.a))
+    Ys, b_s, _ = B.fs_morton_sort(dev(w.Y), dev(w.b))
+    X, Y, a, b = host(Xs), host(Ys), host(a_s), host(b_s)
+    CX, WX = B.fs_centroids(Xs, a_s, cell)
+    CY, WY = B.fs_centroids(Ys, b_s, cell)
+    torch.cuda.synchronize()
+    cx_ref, wx_ref = oc.centroids(X, a, cell)
+    np.testing.assert_allclose(host(WX), wx_ref, rtol=1e-6)
+    np.testing.assert_allclose(host(CX), cx_ref, rtol=1e-6, atol=1e-7)
+    rng = np.random.default_rng(12)
+    rows = rng.choice(w.n, 64, replace=False).astype(np.int32)
+    cols = rng.choice(w.m, 64, replace=False).astype(np.int32)
+    F = torch.empty(CX.shape[0], device="cuda")
+    G = torch.empty(CY.shape[0], device="cuda")
+    pc = B.fs_potentials_init(CX, CY, WX, WY, f=F, g=G)
+    f = torch.empty(w.n, device="cuda")
+    g = torch.empty(w.m, device="cuda")
+    info = B.fs_bs_coarse_start(pc, Xs, Ys, a_s, b_s, cell, f, g, F, G,
+                                torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda(),
+                                eps_end=eps, eps_start=0.1, n_stages=12, iters_per_stage=10,
+                                more_iters=20, check_tol=0.5, max_rounds=2)
+    torch.cuda.synchronize()
+    ref = oc.sampled_marginal_error(X, Y, a, b, host(f), host(g), eps, rows, cols)
+    print(f"coarse stage: {info}; oracle check {ref}")
+    np.testing.assert_allclose([info["err_rows"], info["err_cols"]], ref, rtol=1e-4)
+    p = B.fs_potentials_init(Xs, Ys, a_s, b_s)
+    B.fs_bs_attach(p)
+    sol = B.fs_bs_sinkhorn_solve(p, f, g, eps_end=eps, iters_per_stage=3000, delta=1e-3,
+                                 tol=1e-2, check_every=10, warm_start=True)
+    assert sol["residual"] <= 1e-2
+    f_cur = host(f).copy()
+    f_new = torch.empty_like(f)
+    B.fs_bs_lse_update_f(p, eps, 1e-3, g, f, f_new)
+    torch.cuda.synchronize()
+    sample = np.sort(rng.choice(w.n, SAMPLES, replace=False))
+    ref_f = oracle.f_update_rows(X, Y, b, host(g), eps, sample)
+    fn = host(f_new)[sample]
+    diff = fn - ref_f
+    cert = obs.certificate(fn, f_cur[sample], eps, 1e-3)
+    print(f"pipeline: {sol['iters_done']} iterations, residual {sol['residual']:.2e}; "
+          f"f diff [{diff.min() / eps:.2e}, {diff.max() / eps:.2e}] eps")
+    assert diff.min() >= -1e-3 * eps
+    assert np.all(diff <= cert + 1e-3 * eps)
