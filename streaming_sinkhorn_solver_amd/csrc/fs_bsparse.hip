@@ -37,8 +37,6 @@
 // for every half-step, since they depend on the potentials.  The list of a
 // row block holds the kept key-block indices in increasing order, padded to a
 // whole tile of 16 blocks with a sentinel block of -inf records.
-#include <float.h>
-
 #include <algorithm>
 
 #include "fs_device.hpp"
