@@ -114,7 +114,7 @@ def block_sparse_run(w, eps, steps, warmup, dev, binding, torch):
     e[1].record()
     f0 = torch.zeros(w.n, device=dev)
     g0 = torch.zeros(w.m, device=dev)
-    p = binding.fs_potentials_init(Xs, Ys, a_s, b_s, f=f0, g=g0)
+    p = binding.fs_potentials_init(Xs, Ys, a_s, b_s, f=f0, g=g0, dv_max=w.d)
     binding.fs_bs_attach(p)
     e[2].record()
     # the warm start on the dense path, so that every block-sparse launch of
@@ -166,6 +166,20 @@ def block_sparse_run(w, eps, steps, warmup, dev, binding, torch):
     torch.cuda.synchronize()
     dense_it_s = 10 / (time.perf_counter() - t1)
     it_s = 10 * steps / dt
+    # the barycentric projection P.Y / a at the final potentials, block-sparse
+    # and dense (one untimed call each first)
+    U = torch.empty((w.n, w.d), device=dev)
+    tr = {}
+    for name, call in (("block_sparse", lambda: binding.fs_bs_apply_transport(
+            p, eps, BS_DELTA, f, g, Ys, U, divide_by_a=True)),
+            ("dense", lambda: binding.fs_apply_transport(p, eps, f, g, Ys, U, divide_by_a=True))):
+        call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        tr[name] = round(e0.elapsed_time(e1), 3)
     lse_mean_ms = lse["ms"] / max(lse["n"], 1)
     diff = float((f - fd).abs().max()) / eps
     r = res.cpu().numpy()
@@ -178,6 +192,7 @@ def block_sparse_run(w, eps, steps, warmup, dev, binding, torch):
         "dense_marginal_residual_after": [float(r[0]), float(r[1])],
         "max_abs_f_minus_dense_over_eps": round(diff, 4),
         "setup": setup,
+        "barycentric_projection_ms": tr,
         "what": "10 block-sparse iterations from the annealed warm start (per-block fits, "
                 "screening, retained-block LSE passes) vs 10 dense iterations from the same "
                 "start; kept shares are of the last screening of each side",

@@ -351,6 +351,18 @@ fs_status fs_bs_lse_update_g(fs_problem* p, float eps, float delta, const float*
 fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* opts, float delta, float* f,
                                float* g, fs_solve_info* info, void* stream);
 
+/* The transport U = P.V (divide_by_a: P.V / a, the barycentric projection
+ * when V holds the key points) of the block-sparse form: the f-side
+ * screening of (f, g) with this delta, then the sum over the kept blocks'
+ * keys only.  Since the skipped mass of every row is below delta * a_i,
+ * |U_i - U_dense_i| < delta a_i max_j |V_j| per component (delta max |V|
+ * after the division).  V (m x dv, the problem's key order, i.e. Morton-
+ * ordered like Y), U (n x dv): device fp32, 1 <= dv <= 16, U overlapping no
+ * input.  Leaves the f-side lists as the last screening. */
+fs_status fs_bs_apply_transport(fs_problem* p, float eps, float delta, const float* f,
+                               const float* g, const float* V, int32_t dv, float* U,
+                               int32_t divide_by_a, void* stream);
+
 /* ---- Coarse (centroid) stage ---------------------------------------------
  * "FlashSinkhorn 2" explainer, solving at a coarse resolution first and
  * trusting the lifted solution (no formula on the page; the reading used):

@@ -26,7 +26,7 @@ __all__ = [
     "fs_morton_workspace_bytes", "fs_morton_sort", "fs_unpermute", "fs_bs_workspace_bytes",
     "fs_bs_attach", "fs_bs_lse_update_f", "fs_bs_lse_update_g", "fs_bs_sinkhorn_solve",
     "fs_bs_shape", "fs_bs_read_screen", "fs_centroids", "fs_lift",
-    "fs_sampled_marginal_error", "fs_bs_coarse_start",
+    "fs_sampled_marginal_error", "fs_bs_coarse_start", "fs_bs_apply_transport",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -158,6 +158,8 @@ def load():
     lib.fs_bs_shape.argtypes = [_vp, i32] + [ctypes.POINTER(i32)] * 3
     lib.fs_bs_read_screen.restype = ctypes.c_int
     lib.fs_bs_read_screen.argtypes = [_vp, i32, _vp, _vp, _vp]
+    lib.fs_bs_apply_transport.restype = ctypes.c_int
+    lib.fs_bs_apply_transport.argtypes = [_vp, f32, f32, _fp, _fp, _fp, i32, _fp, i32, _vp]
     lib.fs_centroids.restype = ctypes.c_int
     lib.fs_centroids.argtypes = [_fp, _fp, i64, i32, i32, _fp, _fp, _vp]
     lib.fs_lift.restype = ctypes.c_int
@@ -518,6 +520,16 @@ def fs_bs_read_screen(p: Problem, side: int, lists: bool = False, stream=None):
                                     L.ctypes.data if lists else None, _stream(stream)),
            "fs_bs_read_screen")
     return (counts, L) if lists else counts
+
+
+def fs_bs_apply_transport(p: Problem, eps: float, delta: float, f, g, V, U,
+                          divide_by_a: bool = False, stream=None):
+    dv = V.shape[1]
+    return _check(load().fs_bs_apply_transport(p.handle, float(eps), float(delta),
+                                               _dev(f, "f", p.n), _dev(g, "g", p.m),
+                                               _dev(V, "V", p.m * dv), dv,
+                                               _dev(U, "U", p.n * dv), int(bool(divide_by_a)),
+                                               _stream(stream)), "fs_bs_apply_transport")
 
 
 def fs_centroids(P, w, cell: int, C=None, W=None, stream=None):

@@ -1380,6 +1380,45 @@ fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delt
     return FS_OK;
 }
 
+fs_status fs_bs_apply_transport(fs_problem* p, float eps, float delta, const float* f,
+                               const float* g, const float* V, int32_t dv, float* U,
+                               int32_t divide_by_a, void* stream) {
+    fs_status st = bs_check(p);
+    if (st != FS_OK) return st;
+    if (!p->bs_on) return fail(FS_ERR_INVALID_ARG, "call fs_bs_attach first");
+    if (!f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL f, g, V or U");
+    if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!(delta >= 0.f && delta < 1.f)) return fail(FS_ERR_INVALID_ARG, "delta must be in [0, 1)");
+    if (dv < 1 || dv > 16) return fail(FS_ERR_INVALID_ARG, "dv must be in [1, 16] (got %d)", dv);
+    if (overlaps(U, 4 * (size_t)p->n * dv, V, 4 * (size_t)p->m * dv) ||
+        overlaps(U, 4 * (size_t)p->n * dv, f, 4 * (size_t)p->n) ||
+        overlaps(U, 4 * (size_t)p->n * dv, g, 4 * (size_t)p->m))
+        return fail(FS_ERR_INVALID_ARG, "U overlaps an input");
+    hipStream_t s = (hipStream_t)stream;
+    const float c_bias = (float)(1.4426950408889634 / (double)eps);
+    const float c_score = (float)(2.8853900817779268 / (double)eps);
+    const int nbR = p->bs_nbR[0], nbK = p->bs_nbK[0];
+    hipError_t e;
+    if ((e = launch_block_fit((const float*)p->X.ops, p->centre, p->d, p->n, 256, false, f, nullptr,
+                              c_bias, p->bs_rfit, s)) != hipSuccess ||
+        (e = launch_block_fit((const float*)p->Y.ops, p->centre + p->d, p->d, p->m, 32, true, g,
+                              p->Y.lw2, c_bias, p->bs_kfit, s)) != hipSuccess)
+        return hip_fail(e, "block fit launch");
+    const float thr2 = delta > 0.f ? (float)std::log2((double)delta / (double)nbK) : -INFINITY;
+    if ((e = launch_screen(p->bs_rbox[0], p->bs_rfit, nbR, p->bs_kbox[0], p->bs_kfit, nbK, c_bias,
+                           thr2, p->bs_mag, p->bs_list, p->bs_cnt[0], p->bs_best, p->centre,
+                           p->centre + p->d, p->d, p->bs_org, p->bs_cap[0],
+                           (int)(p->Y.n_pad / 32), s)) != hipSuccess)
+        return hip_fail(e, "screening launch");
+    p->bs_last_side = 0;
+    if ((e = launch_bs_transport((const float*)p->X.ops, p->X.nrm, p->X.lw2, f, p->X.w, (int)p->n,
+                                 (const float*)p->Y.ops, p->Y.nrm, p->Y.lw2, g, (int)p->m, V, dv,
+                                 c_bias, c_score, divide_by_a ? 1 : 0, p->bs_list, p->bs_cnt[0],
+                                 p->bs_cap[0], nbR, U, s)) != hipSuccess)
+        return hip_fail(e, "block-sparse transport launch");
+    return FS_OK;
+}
+
 fs_status fs_centroids(const float* P, const float* w, int64_t n, int32_t d, int32_t cell,
                        float* C, float* W, void* stream) {
     if (!P || !w || !C || !W) return fail(FS_ERR_INVALID_ARG, "NULL argument");

@@ -733,9 +733,106 @@ __global__ __launch_bounds__(256) void sampled_reduce_kernel(const float2* __res
     }
 }
 
+// ---------------------------------------------------------------- transport
+// The transport U = P.V over the kept blocks of the f-side screening (the
+// skipped mass of every row is below delta * a_i, so each component of U
+// moves by less than delta a_i max |V|): one workgroup per 256-row block,
+// one row per thread, stages of 8 listed key blocks (256 keys) through LDS;
+//   log2 P_ij = lw2_i + (f_i - A_i) c_bias + c_score x~_i.y~_j + lw2_j + (g_j - B_j) c_bias.
+struct BsTransportArgs {
+    const float* rows;  // x~ [n_pad][4]
+    const float* row_nrm;
+    const float* row_lw2;
+    const float* row_pot;
+    const float* row_w;
+    const float* keys;  // y~ [m_pad][4]
+    const float* key_nrm;
+    const float* key_lw2;
+    const float* key_pot;
+    const float* V;  // [m][dv]
+    int dv, n_rows, n_keys;
+    float c_bias, c_score;
+    int divide;
+    const int* list;
+    const int* count;
+    int cap;
+    float* U;  // [n][dv]
+};
+
+template <int DV>
+__global__ __launch_bounds__(256) void bs_transport_kernel(BsTransportArgs a) {
+    __shared__ float4 ky[256];
+    __shared__ float kv[256][DV];
+    const int I = blockIdx.x, tid = threadIdx.x;
+    const int64_t i = (int64_t)I * 256 + tid;
+    const bool live = i < a.n_rows;
+    float x[3] = {0.f, 0.f, 0.f};
+    float rt = -INFINITY;
+    if (live) {
+        const float4 r = *(const float4*)(a.rows + i * 4);
+        x[0] = r.x * a.c_score;
+        x[1] = r.y * a.c_score;
+        x[2] = r.z * a.c_score;
+        rt = fmaf(a.row_pot[i] - a.row_nrm[i], a.c_bias, a.row_lw2[i]);
+    }
+    float acc[DV];
+#pragma unroll
+    for (int c = 0; c < DV; ++c) acc[c] = 0.f;
+    const int cnt = a.count[I];
+    const int* __restrict__ lst = a.list + (int64_t)I * a.cap;
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+        // 8 listed blocks (entries past the count are the -inf sentinel)
+        __syncthreads();
+        {
+            const int J = lst[k0 + (tid >> 5)];
+            const int64_t j = (int64_t)J * 32 + (tid & 31);
+            if (j < a.n_keys) {
+                const float4 y = *(const float4*)(a.keys + j * 4);
+                ky[tid] = make_float4(y.x, y.y, y.z,
+                                      fmaf(a.key_pot[j] - a.key_nrm[j], a.c_bias, a.key_lw2[j]));
+            } else {
+                ky[tid] = make_float4(0.f, 0.f, 0.f, -INFINITY);
+            }
+            for (int c = 0; c < DV; ++c)
+                kv[tid][c] = (j < a.n_keys && c < a.dv) ? a.V[j * a.dv + c] : 0.f;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < 256; ++kk) {
+            const float4 y = ky[kk];
+            const float z = fmaf(x[0], y.x, fmaf(x[1], y.y, fmaf(x[2], y.z, y.w + rt)));
+            const float p = ex2(z);
+#pragma unroll
+            for (int c = 0; c < DV; ++c) acc[c] = fmaf(p, kv[kk][c], acc[c]);
+        }
+    }
+    if (live) {
+        const float inv = a.divide ? 1.f / a.row_w[i] : 1.f;
+        for (int c = 0; c < a.dv; ++c) a.U[i * a.dv + c] = acc[c] * inv;
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_bs_transport(const float* rows, const float* row_nrm, const float* row_lw2,
+                               const float* row_pot, const float* row_w, int n_rows,
+                               const float* keys, const float* key_nrm, const float* key_lw2,
+                               const float* key_pot, int n_keys, const float* V, int dv,
+                               float c_bias, float c_score, int divide, const int* list,
+                               const int* count, int cap, int nbR, float* U, hipStream_t s) {
+    BsTransportArgs a{rows, row_nrm, row_lw2, row_pot, row_w, keys, key_nrm, key_lw2, key_pot,
+                      V, dv, n_rows, n_keys, c_bias, c_score, divide, list, count, cap, U};
+    if (dv <= 4)
+        bs_transport_kernel<4><<<nbR, 256, 0, s>>>(a);
+    else if (dv <= 8)
+        bs_transport_kernel<8><<<nbR, 256, 0, s>>>(a);
+    else if (dv <= 16)
+        bs_transport_kernel<16><<<nbR, 256, 0, s>>>(a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_centroids(const float* P, const float* w, int64_t n, int d, int cell,
                             float* C, float* W, hipStream_t s) {

@@ -253,3 +253,37 @@ def test_bs_argument_errors():
         B.fs_bs_lse_update_f(p3, 0.1, 1e-3, f, f, f, row_resid=torch.empty(1, device="cuda"))
     with pytest.raises(B.FsError):
         B.fs_morton_sort(dev(np.zeros((10, 9), np.float32)))
+
+
+@pytest.mark.parametrize("delta", [1e-3, 0.0])
+def test_bs_transport(delta):
+    """U = P.V over the kept blocks against the dense oracle transport:
+    |U - U_dense| <= delta a_i max|V| (the skipped mass) + 2e-3 (P.|V|)_i
+    (fp32), and the barycentric projection P.Y / a the same way."""
+    import torch
+
+    B = _bind()
+    X, Y, a, b = _sorted_problem(61, 3000, 2500, 3)
+    eps = 2e-3
+    f, g = _dense_converged(X, Y, a, b, eps, iters=150)
+    p = _gpu_problem(X, Y, a, b)
+    rng = np.random.default_rng(62)
+    V = rng.normal(size=(2500, 5)).astype(np.float32)
+    U = torch.empty((3000, 5), device="cuda")
+    B.fs_bs_apply_transport(p, eps, delta, dev(f), dev(g), dev(V), U)
+    torch.cuda.synchronize()
+    ref = oracle.transport(X, Y, a, b, f, g, V, eps)
+    ref_abs = oracle.transport(X, Y, a, b, f, g, np.abs(V), eps)
+    env = delta * a[:, None] * np.abs(V).max() + 2e-3 * ref_abs
+    assert np.all(np.abs(host(U) - ref) <= env)
+    # barycentric projection
+    Ub = torch.empty((3000, 3), device="cuda")
+    B.fs_bs_apply_transport(p, eps, delta, dev(f), dev(g), dev(Y), Ub, divide_by_a=True)
+    torch.cuda.synchronize()
+    refb = oracle.transport(X, Y, a, b, f, g, Y, eps, divide_by_a=True)
+    refb_abs = oracle.transport(X, Y, a, b, f, g, np.abs(Y), eps, divide_by_a=True)
+    envb = delta * np.abs(Y).max() + 2e-3 * refb_abs
+    assert np.all(np.abs(host(Ub) - refb) <= envb)
+    if delta > 0:
+        counts = B.fs_bs_read_screen(p, 0)
+        assert counts.sum() < len(counts) * ((2500 + 31) // 32)  # blocks were skipped

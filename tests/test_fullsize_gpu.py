@@ -213,6 +213,16 @@ def test_full_size_block_sparse(fs, name, eps, delta):
               f"certificate max {cert.max() / eps:.2e} eps")
         assert diff.min() >= -1e-3 * eps
         assert np.all(diff <= cert + 1e-3 * eps)
+    # the barycentric projection over the kept blocks on the sampled rows:
+    # |U - U_dense| <= delta max|Y| + 2e-3 (P.|Y| / a) (the skipped mass, fp32)
+    Ub = torch.empty((w.n, 3), device="cuda")
+    B.fs_bs_apply_transport(p, eps, delta, f_new, g_new, Ys, Ub, divide_by_a=True)
+    torch.cuda.synchronize()
+    ref_u = oracle.transport(X, Y, a, b, fn, gn, Y, eps, divide_by_a=True, rows=rows)
+    ref_ua = oracle.transport(X, Y, a, b, fn, gn, np.abs(Y), eps, divide_by_a=True, rows=rows)
+    du = np.abs(host(Ub)[rows] - ref_u)
+    print(f"  barycentric projection: max error {du.max():.2e} (skip bound {delta * np.abs(Y).max():.2e})")
+    assert np.all(du <= delta * np.abs(Y).max() + 2e-3 * ref_ua)
     # brute-force mass of the skipped blocks of two row blocks (f side)
     nbK = (w.m + 31) // 32
     for I in (0, len(cnt_f) // 2):
