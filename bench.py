@@ -166,13 +166,19 @@ def block_sparse_run(w, eps, steps, warmup, dev, binding, torch):
     torch.cuda.synchronize()
     dense_it_s = 10 / (time.perf_counter() - t1)
     it_s = 10 * steps / dt
-    # the barycentric projection P.Y / a at the final potentials, block-sparse
-    # and dense (one untimed call each first)
+    # the barycentric projection P.Y / a and the gradient (both clouds) at the
+    # final potentials, block-sparse and dense (one untimed call each first)
     U = torch.empty((w.n, w.d), device=dev)
+    GX = torch.empty((w.n, w.d), device=dev)
+    GY = torch.empty((w.m, w.d), device=dev)
     tr = {}
-    for name, call in (("block_sparse", lambda: binding.fs_bs_apply_transport(
+    for name, call in (("projection_block_sparse", lambda: binding.fs_bs_apply_transport(
             p, eps, BS_DELTA, f, g, Ys, U, divide_by_a=True)),
-            ("dense", lambda: binding.fs_apply_transport(p, eps, f, g, Ys, U, divide_by_a=True))):
+            ("projection_dense", lambda: binding.fs_apply_transport(
+                p, eps, f, g, Ys, U, divide_by_a=True)),
+            ("gradient_block_sparse", lambda: binding.fs_bs_gradient(
+                p, eps, BS_DELTA, f, g, GX, GY)),
+            ("gradient_dense", lambda: binding.fs_gradient(p, eps, f, g, Xs, Ys, GX, GY))):
         call()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -192,7 +198,7 @@ def block_sparse_run(w, eps, steps, warmup, dev, binding, torch):
         "dense_marginal_residual_after": [float(r[0]), float(r[1])],
         "max_abs_f_minus_dense_over_eps": round(diff, 4),
         "setup": setup,
-        "barycentric_projection_ms": tr,
+        "apply_ms": tr,
         "what": "10 block-sparse iterations from the annealed warm start (per-block fits, "
                 "screening, retained-block LSE passes) vs 10 dense iterations from the same "
                 "start; kept shares are of the last screening of each side",

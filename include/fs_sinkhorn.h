@@ -363,6 +363,25 @@ fs_status fs_bs_apply_transport(fs_problem* p, float eps, float delta, const flo
                                const float* g, const float* V, int32_t dv, float* U,
                                int32_t divide_by_a, void* stream);
 
+/* The column side: U_j = sum_i P_ij W_i (divide_by_b: / b_j) over the blocks
+ * the g-side screening of (f, g) keeps; the same bound with b_j and max|W_i|.
+ * W (n x dv, X's order), U (m x dv).  Leaves the g-side lists. */
+fs_status fs_bs_apply_transport_t(fs_problem* p, float eps, float delta, const float* f,
+                                 const float* g, const float* W, int32_t dv, float* U,
+                                 int32_t divide_by_b, void* stream);
+
+/* The gradient of the dual objective at fixed (f, g) in block-sparse form
+ * (squared Euclidean cost): grad_x_i = 2 sum_j P_ij (x_i - y_j) over the
+ * blocks the f-side screening keeps, grad_y_j = 2 sum_i P_ij (y_j - x_i)
+ * over the g-side ones (NULL skips a side).  Sections of the explainer on
+ * the streaming gradient and on block sparsity.  Skipped mass below delta
+ * a_i bounds the error of grad_x_i by 2 delta a_i max_j |x_i - y_j| per
+ * component (the mirror for grad_y).  grad_x (n x d), grad_y (m x d): device
+ * fp32 in the problem's (Morton) order, overlapping neither f, g nor each
+ * other.  Leaves the lists of the last side computed. */
+fs_status fs_bs_gradient(fs_problem* p, float eps, float delta, const float* f, const float* g,
+                         float* grad_x, float* grad_y, void* stream);
+
 /* ---- Coarse (centroid) stage ---------------------------------------------
  * "FlashSinkhorn 2" explainer, solving at a coarse resolution first and
  * trusting the lifted solution (no formula on the page; the reading used):

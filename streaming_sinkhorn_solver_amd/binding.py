@@ -27,6 +27,7 @@ __all__ = [
     "fs_bs_attach", "fs_bs_lse_update_f", "fs_bs_lse_update_g", "fs_bs_sinkhorn_solve",
     "fs_bs_shape", "fs_bs_read_screen", "fs_centroids", "fs_lift",
     "fs_sampled_marginal_error", "fs_bs_coarse_start", "fs_bs_apply_transport",
+    "fs_bs_apply_transport_t", "fs_bs_gradient",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -160,6 +161,10 @@ def load():
     lib.fs_bs_read_screen.argtypes = [_vp, i32, _vp, _vp, _vp]
     lib.fs_bs_apply_transport.restype = ctypes.c_int
     lib.fs_bs_apply_transport.argtypes = [_vp, f32, f32, _fp, _fp, _fp, i32, _fp, i32, _vp]
+    lib.fs_bs_apply_transport_t.restype = ctypes.c_int
+    lib.fs_bs_apply_transport_t.argtypes = [_vp, f32, f32, _fp, _fp, _fp, i32, _fp, i32, _vp]
+    lib.fs_bs_gradient.restype = ctypes.c_int
+    lib.fs_bs_gradient.argtypes = [_vp, f32, f32, _fp, _fp, _fp, _fp, _vp]
     lib.fs_centroids.restype = ctypes.c_int
     lib.fs_centroids.argtypes = [_fp, _fp, i64, i32, i32, _fp, _fp, _vp]
     lib.fs_lift.restype = ctypes.c_int
@@ -530,6 +535,25 @@ def fs_bs_apply_transport(p: Problem, eps: float, delta: float, f, g, V, U,
                                                _dev(V, "V", p.m * dv), dv,
                                                _dev(U, "U", p.n * dv), int(bool(divide_by_a)),
                                                _stream(stream)), "fs_bs_apply_transport")
+
+
+def fs_bs_apply_transport_t(p: Problem, eps: float, delta: float, f, g, W, U,
+                            divide_by_b: bool = False, stream=None):
+    dv = W.shape[1]
+    return _check(load().fs_bs_apply_transport_t(p.handle, float(eps), float(delta),
+                                                 _dev(f, "f", p.n), _dev(g, "g", p.m),
+                                                 _dev(W, "W", p.n * dv), dv,
+                                                 _dev(U, "U", p.m * dv), int(bool(divide_by_b)),
+                                                 _stream(stream)), "fs_bs_apply_transport_t")
+
+
+def fs_bs_gradient(p: Problem, eps: float, delta: float, f, g, grad_x=None, grad_y=None,
+                   stream=None):
+    gx = _dev(grad_x, "grad_x", p.n * p.d) if grad_x is not None else None
+    gy = _dev(grad_y, "grad_y", p.m * p.d) if grad_y is not None else None
+    return _check(load().fs_bs_gradient(p.handle, float(eps), float(delta), _dev(f, "f", p.n),
+                                        _dev(g, "g", p.m), gx, gy, _stream(stream)),
+                  "fs_bs_gradient")
 
 
 def fs_centroids(P, w, cell: int, C=None, W=None, stream=None):

@@ -1044,9 +1044,11 @@ namespace {
 constexpr int kBsTarget = FS_BS_SPLIT_TARGET;
 constexpr int kBsMaxSplit = 16;
 
-fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, const float* cur,
-                          const float* other, float* out, float* resid, hipStream_t s,
-                          hipEvent_t eb, hipEvent_t ee) {
+// The per-block fits of the row side's potential `cur` and the key side's
+// `other`, then the screening of side 0 (rows X, keys Y) or 1 (rows Y, keys
+// X) into the problem's list buffer.
+fs_status bs_screen_side(fs_problem* p, bool f_side, float eps, float delta, const float* cur,
+                         const float* other, hipStream_t s) {
     const int side = f_side ? 0 : 1;
     const Cloud& R = f_side ? p->X : p->Y;
     const Cloud& K = f_side ? p->Y : p->X;
@@ -1067,6 +1069,19 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
                            cR, cK, p->d, p->bs_org, p->bs_cap[side], sentinel, s)) != hipSuccess)
         return hip_fail(e, "screening launch");
     p->bs_last_side = side;
+    return FS_OK;
+}
+
+fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, const float* cur,
+                          const float* other, float* out, float* resid, hipStream_t s,
+                          hipEvent_t eb, hipEvent_t ee) {
+    const int side = f_side ? 0 : 1;
+    const Cloud& K = f_side ? p->Y : p->X;
+    const int nbR = p->bs_nbR[side];
+    const int sentinel = (int)(K.n_pad / 32);
+    fs_status st = bs_screen_side(p, f_side, eps, delta, cur, other, s);
+    if (st != FS_OK) return st;
+    hipError_t e;
     if ((e = launch_split_plan(p->bs_cnt[side], nbR, kBsTarget, kBsMaxSplit, p->bs_nsplit,
                                p->bs_map, p->bs_total, s)) != hipSuccess)
         return hip_fail(e, "split plan launch");
@@ -1380,42 +1395,99 @@ fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delt
     return FS_OK;
 }
 
-fs_status fs_bs_apply_transport(fs_problem* p, float eps, float delta, const float* f,
-                               const float* g, const float* V, int32_t dv, float* U,
-                               int32_t divide_by_a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Block-sparse transport or gradient of one side: screening of that side at
+// (f, g), then one launch over its kept blocks.  Side 0: rows X (potential
+// f), keys Y (g), V [m][dv] -> U [n][dv]; side 1 the roles swapped.  V == NULL
+// asks for the gradient 2 sum_j P_ij (x_i - y_j) (dv = d).
+fs_status bs_transport_side(fs_problem* p, bool f_side, float eps, float delta, const float* f,
+                            const float* g, const float* V, int32_t dv, float* U, int divide,
+                            hipStream_t s) {
+    const int side = f_side ? 0 : 1;
+    const Cloud& R = f_side ? p->X : p->Y;
+    const Cloud& K = f_side ? p->Y : p->X;
+    const float* rpot = f_side ? f : g;
+    const float* kpot = f_side ? g : f;
+    fs_status st = bs_screen_side(p, f_side, eps, delta, rpot, kpot, s);
+    if (st != FS_OK) return st;
+    const float c_bias = (float)(1.4426950408889634 / (double)eps);
+    const float c_score = (float)(2.8853900817779268 / (double)eps);
+    hipError_t e = launch_bs_transport(
+        (const float*)R.ops, R.nrm, R.lw2, rpot, R.w, (int)R.n, (const float*)K.ops, K.nrm, K.lw2,
+        kpot, (int)K.n, V, dv, c_bias, c_score, divide, p->bs_list, p->bs_cnt[side],
+        p->bs_cap[side], p->bs_nbR[side], p->centre + (f_side ? 0 : p->d),
+        p->centre + (f_side ? p->d : 0), U, s);
+    if (e != hipSuccess) return hip_fail(e, "block-sparse transport launch");
+    return FS_OK;
+}
+
+fs_status bs_transport_check(fs_problem* p, float eps, float delta, const float* f,
+                             const float* g) {
     fs_status st = bs_check(p);
     if (st != FS_OK) return st;
     if (!p->bs_on) return fail(FS_ERR_INVALID_ARG, "call fs_bs_attach first");
-    if (!f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL f, g, V or U");
+    if (!f || !g) return fail(FS_ERR_INVALID_ARG, "NULL f or g");
     if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (!(delta >= 0.f && delta < 1.f)) return fail(FS_ERR_INVALID_ARG, "delta must be in [0, 1)");
+    return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fs_status fs_bs_apply_transport(fs_problem* p, float eps, float delta, const float* f,
+                               const float* g, const float* V, int32_t dv, float* U,
+                               int32_t divide_by_a, void* stream) {
+    fs_status st = bs_transport_check(p, eps, delta, f, g);
+    if (st != FS_OK) return st;
+    if (!V || !U) return fail(FS_ERR_INVALID_ARG, "NULL V or U");
     if (dv < 1 || dv > 16) return fail(FS_ERR_INVALID_ARG, "dv must be in [1, 16] (got %d)", dv);
     if (overlaps(U, 4 * (size_t)p->n * dv, V, 4 * (size_t)p->m * dv) ||
         overlaps(U, 4 * (size_t)p->n * dv, f, 4 * (size_t)p->n) ||
         overlaps(U, 4 * (size_t)p->n * dv, g, 4 * (size_t)p->m))
         return fail(FS_ERR_INVALID_ARG, "U overlaps an input");
+    return bs_transport_side(p, true, eps, delta, f, g, V, dv, U, divide_by_a ? 1 : 0,
+                             (hipStream_t)stream);
+}
+
+fs_status fs_bs_apply_transport_t(fs_problem* p, float eps, float delta, const float* f,
+                                 const float* g, const float* W, int32_t dv, float* U,
+                                 int32_t divide_by_b, void* stream) {
+    fs_status st = bs_transport_check(p, eps, delta, f, g);
+    if (st != FS_OK) return st;
+    if (!W || !U) return fail(FS_ERR_INVALID_ARG, "NULL W or U");
+    if (dv < 1 || dv > 16) return fail(FS_ERR_INVALID_ARG, "dv must be in [1, 16] (got %d)", dv);
+    if (overlaps(U, 4 * (size_t)p->m * dv, W, 4 * (size_t)p->n * dv) ||
+        overlaps(U, 4 * (size_t)p->m * dv, f, 4 * (size_t)p->n) ||
+        overlaps(U, 4 * (size_t)p->m * dv, g, 4 * (size_t)p->m))
+        return fail(FS_ERR_INVALID_ARG, "U overlaps an input");
+    return bs_transport_side(p, false, eps, delta, f, g, W, dv, U, divide_by_b ? 1 : 0,
+                             (hipStream_t)stream);
+}
+
+fs_status fs_bs_gradient(fs_problem* p, float eps, float delta, const float* f, const float* g,
+                         float* grad_x, float* grad_y, void* stream) {
+    fs_status st = bs_transport_check(p, eps, delta, f, g);
+    if (st != FS_OK) return st;
+    const size_t bx = 4 * (size_t)p->n * p->d, by = 4 * (size_t)p->m * p->d;
+    if (grad_x && (overlaps(grad_x, bx, f, 4 * (size_t)p->n) ||
+                   overlaps(grad_x, bx, g, 4 * (size_t)p->m)))
+        return fail(FS_ERR_INVALID_ARG, "grad_x overlaps f or g");
+    if (grad_y && (overlaps(grad_y, by, f, 4 * (size_t)p->n) ||
+                   overlaps(grad_y, by, g, 4 * (size_t)p->m) ||
+                   (grad_x && overlaps(grad_y, by, grad_x, bx))))
+        return fail(FS_ERR_INVALID_ARG, "grad_y overlaps f, g or grad_x");
     hipStream_t s = (hipStream_t)stream;
-    const float c_bias = (float)(1.4426950408889634 / (double)eps);
-    const float c_score = (float)(2.8853900817779268 / (double)eps);
-    const int nbR = p->bs_nbR[0], nbK = p->bs_nbK[0];
-    hipError_t e;
-    if ((e = launch_block_fit((const float*)p->X.ops, p->centre, p->d, p->n, 256, false, f, nullptr,
-                              c_bias, p->bs_rfit, s)) != hipSuccess ||
-        (e = launch_block_fit((const float*)p->Y.ops, p->centre + p->d, p->d, p->m, 32, true, g,
-                              p->Y.lw2, c_bias, p->bs_kfit, s)) != hipSuccess)
-        return hip_fail(e, "block fit launch");
-    const float thr2 = delta > 0.f ? (float)std::log2((double)delta / (double)nbK) : -INFINITY;
-    if ((e = launch_screen(p->bs_rbox[0], p->bs_rfit, nbR, p->bs_kbox[0], p->bs_kfit, nbK, c_bias,
-                           thr2, p->bs_mag, p->bs_list, p->bs_cnt[0], p->bs_best, p->centre,
-                           p->centre + p->d, p->d, p->bs_org, p->bs_cap[0],
-                           (int)(p->Y.n_pad / 32), s)) != hipSuccess)
-        return hip_fail(e, "screening launch");
-    p->bs_last_side = 0;
-    if ((e = launch_bs_transport((const float*)p->X.ops, p->X.nrm, p->X.lw2, f, p->X.w, (int)p->n,
-                                 (const float*)p->Y.ops, p->Y.nrm, p->Y.lw2, g, (int)p->m, V, dv,
-                                 c_bias, c_score, divide_by_a ? 1 : 0, p->bs_list, p->bs_cnt[0],
-                                 p->bs_cap[0], nbR, U, s)) != hipSuccess)
-        return hip_fail(e, "block-sparse transport launch");
+    if (grad_x && (st = bs_transport_side(p, true, eps, delta, f, g, nullptr, p->d, grad_x, 0,
+                                          s)) != FS_OK)
+        return st;
+    if (grad_y && (st = bs_transport_side(p, false, eps, delta, f, g, nullptr, p->d, grad_y, 0,
+                                          s)) != FS_OK)
+        return st;
     return FS_OK;
 }
 

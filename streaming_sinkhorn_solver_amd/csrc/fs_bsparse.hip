@@ -749,32 +749,41 @@ struct BsTransportArgs {
     const float* key_nrm;
     const float* key_lw2;
     const float* key_pot;
-    const float* V;  // [m][dv]
+    const float* V;  // [m][dv] (unused by the gradient form)
     int dv, n_rows, n_keys;
     float c_bias, c_score;
     int divide;
     const int* list;
     const int* count;
     int cap;
+    const float* cR;  // centres of the row and key clouds (gradient form)
+    const float* cK;
     float* U;  // [n][dv]
 };
 
-template <int DV>
+// Row block I (one workgroup, a row per thread) against its kept key blocks,
+// eight at a time (256 keys staged in LDS).  Transport form: U_i = sum_j
+// P_ij V_j (/ a_i).  Gradient form (GRAD, dv = d <= 3): with the centred
+// coordinates x' = x - cR, y' = y - cK it accumulates S_i = sum_j P_ij y'_j and
+// r_i = sum_j P_ij, and writes 2 (r_i (x'_i + cR - cK) - S_i), which is
+// 2 sum_j P_ij (x_i - y_j).
+template <int DV, bool GRAD>
 __global__ __launch_bounds__(256) void bs_transport_kernel(BsTransportArgs a) {
     __shared__ float4 ky[256];
-    __shared__ float kv[256][DV];
+    __shared__ float kv[GRAD ? 1 : 256][DV];
     const int I = blockIdx.x, tid = threadIdx.x;
     const int64_t i = (int64_t)I * 256 + tid;
     const bool live = i < a.n_rows;
-    float x[3] = {0.f, 0.f, 0.f};
+    float xr[3] = {0.f, 0.f, 0.f};
     float rt = -INFINITY;
     if (live) {
         const float4 r = *(const float4*)(a.rows + i * 4);
-        x[0] = r.x * a.c_score;
-        x[1] = r.y * a.c_score;
-        x[2] = r.z * a.c_score;
+        xr[0] = r.x;
+        xr[1] = r.y;
+        xr[2] = r.z;
         rt = fmaf(a.row_pot[i] - a.row_nrm[i], a.c_bias, a.row_lw2[i]);
     }
+    const float x0 = xr[0] * a.c_score, x1 = xr[1] * a.c_score, x2 = xr[2] * a.c_score;
     float acc[DV];
 #pragma unroll
     for (int c = 0; c < DV; ++c) acc[c] = 0.f;
@@ -793,19 +802,31 @@ __global__ __launch_bounds__(256) void bs_transport_kernel(BsTransportArgs a) {
             } else {
                 ky[tid] = make_float4(0.f, 0.f, 0.f, -INFINITY);
             }
-            for (int c = 0; c < DV; ++c)
-                kv[tid][c] = (j < a.n_keys && c < a.dv) ? a.V[j * a.dv + c] : 0.f;
+            if constexpr (!GRAD)
+                for (int c = 0; c < DV; ++c)
+                    kv[tid][c] = (j < a.n_keys && c < a.dv) ? a.V[j * a.dv + c] : 0.f;
         }
         __syncthreads();
         for (int kk = 0; kk < 256; ++kk) {
             const float4 y = ky[kk];
-            const float z = fmaf(x[0], y.x, fmaf(x[1], y.y, fmaf(x[2], y.z, y.w + rt)));
+            const float z = fmaf(x0, y.x, fmaf(x1, y.y, fmaf(x2, y.z, y.w + rt)));
             const float p = ex2(z);
+            if constexpr (GRAD) {
+                acc[0] = fmaf(p, y.x, acc[0]);
+                acc[1] = fmaf(p, y.y, acc[1]);
+                acc[2] = fmaf(p, y.z, acc[2]);
+                acc[3] += p;
+            } else {
 #pragma unroll
-            for (int c = 0; c < DV; ++c) acc[c] = fmaf(p, kv[kk][c], acc[c]);
+                for (int c = 0; c < DV; ++c) acc[c] = fmaf(p, kv[kk][c], acc[c]);
+            }
         }
     }
-    if (live) {
+    if (!live) return;
+    if constexpr (GRAD) {
+        for (int c = 0; c < a.dv; ++c)
+            a.U[i * a.dv + c] = 2.f * (acc[3] * (xr[c] + (a.cR[c] - a.cK[c])) - acc[c]);
+    } else {
         const float inv = a.divide ? 1.f / a.row_w[i] : 1.f;
         for (int c = 0; c < a.dv; ++c) a.U[i * a.dv + c] = acc[c] * inv;
     }
@@ -820,17 +841,22 @@ hipError_t launch_bs_transport(const float* rows, const float* row_nrm, const fl
                                const float* keys, const float* key_nrm, const float* key_lw2,
                                const float* key_pot, int n_keys, const float* V, int dv,
                                float c_bias, float c_score, int divide, const int* list,
-                               const int* count, int cap, int nbR, float* U, hipStream_t s) {
+                               const int* count, int cap, int nbR, const float* cR,
+                               const float* cK, float* U, hipStream_t s) {
     BsTransportArgs a{rows, row_nrm, row_lw2, row_pot, row_w, keys, key_nrm, key_lw2, key_pot,
-                      V, dv, n_rows, n_keys, c_bias, c_score, divide, list, count, cap, U};
-    if (dv <= 4)
-        bs_transport_kernel<4><<<nbR, 256, 0, s>>>(a);
-    else if (dv <= 8)
-        bs_transport_kernel<8><<<nbR, 256, 0, s>>>(a);
-    else if (dv <= 16)
-        bs_transport_kernel<16><<<nbR, 256, 0, s>>>(a);
-    else
+                      V, dv, n_rows, n_keys, c_bias, c_score, divide, list, count, cap, cR, cK, U};
+    if (!V) {  // the gradient form
+        if (dv > 3 || !cR || !cK) return hipErrorInvalidValue;
+        bs_transport_kernel<4, true><<<nbR, 256, 0, s>>>(a);
+    } else if (dv <= 4) {
+        bs_transport_kernel<4, false><<<nbR, 256, 0, s>>>(a);
+    } else if (dv <= 8) {
+        bs_transport_kernel<8, false><<<nbR, 256, 0, s>>>(a);
+    } else if (dv <= 16) {
+        bs_transport_kernel<16, false><<<nbR, 256, 0, s>>>(a);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

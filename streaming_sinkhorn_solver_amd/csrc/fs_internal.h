@@ -257,14 +257,17 @@ hipError_t launch_sampled_marginal(const float* X, const float* Y, const float* 
                                    const float* f, const float* g, const int32_t* rows,
                                    int nrows, const int32_t* cols, int ncols, float2* part,
                                    float* out2, hipStream_t s);
-// Transport U = P.V (dv <= 16) over the kept blocks of an f-side screening
-// (list/count/cap of nbR row blocks of 256; rows and keys as fp32 rows of 4).
+// Transport U = P.V (dv <= 16) over the kept blocks of a screening (list/
+// count/cap of nbR row blocks of 256; rows and keys as fp32 rows of 4).  With
+// V == NULL it is the gradient form: U_i = 2 sum_j P_ij (x_i - y_j), dv = d <= 3,
+// cR/cK the centres the rows and keys were taken about.
 hipError_t launch_bs_transport(const float* rows, const float* row_nrm, const float* row_lw2,
                                const float* row_pot, const float* row_w, int n_rows,
                                const float* keys, const float* key_nrm, const float* key_lw2,
                                const float* key_pot, int n_keys, const float* V, int dv,
                                float c_bias, float c_score, int divide, const int* list,
-                               const int* count, int cap, int nbR, float* U, hipStream_t s);
+                               const int* count, int cap, int nbR, const float* cR,
+                               const float* cK, float* U, hipStream_t s);
 // Work plan of the retained-block pass from the kept counts (see LseArgs).
 hipError_t launch_split_plan(const int* count, int nbR, int target, int smax, int* nsplit,
                              int* map, int* total, hipStream_t s);

@@ -287,3 +287,81 @@ def test_bs_transport(delta):
     if delta > 0:
         counts = B.fs_bs_read_screen(p, 0)
         assert counts.sum() < len(counts) * ((2500 + 31) // 32)  # blocks were skipped
+
+
+@pytest.mark.parametrize("delta", [1e-3, 0.0])
+def test_bs_transport_t(delta):
+    """The column side U_j = sum_i P_ij W_i over the g-side kept blocks against
+    the dense oracle: |U - U_dense| <= delta b_j max|W| + 2e-3 (P^T.|W|)_j, and
+    the column barycentric projection P^T.X / b the same way."""
+    import torch
+
+    B = _bind()
+    X, Y, a, b = _sorted_problem(63, 2600, 3100, 3, xkind="mixture", ykind="uniform")
+    eps = 2e-3
+    f, g = _dense_converged(X, Y, a, b, eps, iters=150)
+    p = _gpu_problem(X, Y, a, b)
+    rng = np.random.default_rng(64)
+    W = rng.normal(size=(2600, 4)).astype(np.float32)
+    U = torch.empty((3100, 4), device="cuda")
+    B.fs_bs_apply_transport_t(p, eps, delta, dev(f), dev(g), dev(W), U)
+    torch.cuda.synchronize()
+    ref = oracle.transport_t(X, Y, a, b, f, g, W, eps)
+    ref_abs = oracle.transport_t(X, Y, a, b, f, g, np.abs(W), eps)
+    env = delta * b[:, None] * np.abs(W).max() + 2e-3 * ref_abs
+    assert np.all(np.abs(host(U) - ref) <= env)
+    Ub = torch.empty((3100, 3), device="cuda")
+    B.fs_bs_apply_transport_t(p, eps, delta, dev(f), dev(g), dev(X), Ub, divide_by_b=True)
+    torch.cuda.synchronize()
+    refb = oracle.transport_t(X, Y, a, b, f, g, X, eps, divide_by_b=True)
+    refb_abs = oracle.transport_t(X, Y, a, b, f, g, np.abs(X), eps, divide_by_b=True)
+    assert np.all(np.abs(host(Ub) - refb) <= delta * np.abs(X).max() + 2e-3 * refb_abs)
+    if delta > 0:
+        counts = B.fs_bs_read_screen(p, 1)
+        assert counts.sum() < len(counts) * ((2600 + 31) // 32)
+    with pytest.raises(B.FsError):  # more than 16 columns
+        B.fs_bs_apply_transport_t(p, eps, delta, dev(f), dev(g),
+                                  dev(np.zeros((2600, 17), np.float32)),
+                                  torch.empty((3100, 17), device="cuda"))
+
+
+@pytest.mark.parametrize("delta,d", [(1e-3, 3), (0.0, 3), (1e-3, 2), (1e-3, 1)])
+def test_bs_gradient(delta, d):
+    """grad_x_i = 2 sum_j P_ij (x_i - y_j) and grad_y over the kept blocks
+    against the dense oracle gradient, per component within the skipped-mass
+    bound 2 delta a_i max_j |x_ic - y_jc| plus 2e-3 of 2 sum_j P_ij |x_ic - y_jc|
+    (the relative error of the fp32 plan entries) plus 1e-5 a_i for the fp32
+    sums (the mirror for grad_y; bounds by brute force in float64)."""
+    import torch
+
+    B = _bind()
+    n, m = 2800, 2300
+    X, Y, a, b = _sorted_problem(65 + d, n, m, d)
+    eps = 2e-3
+    f, g = _dense_converged(X, Y, a, b, eps, iters=150)
+    p = _gpu_problem(X, Y, a, b)
+    gx = torch.empty((n, d), device="cuda")
+    gy = torch.empty((m, d), device="cuda")
+    B.fs_bs_gradient(p, eps, delta, dev(f), dev(g), gx, gy)
+    torch.cuda.synchronize()
+    rx, ry = oracle.gradient(X, Y, a, b, f, g, eps)
+    X64, Y64 = X.astype(np.float64), Y.astype(np.float64)
+    D = X64[:, None, :] - Y64[None, :, :]                       # n x m x d
+    P = a[:, None] * b[None, :] * np.exp((f[:, None] + g[None, :] - (D ** 2).sum(-1)) / eps)
+    absD = np.abs(D)
+    env_x = (2 * delta * a[:, None] * absD.max(axis=1)
+             + 2e-3 * 2 * np.einsum("ij,ijc->ic", P, absD) + 1e-5 * a[:, None])
+    env_y = (2 * delta * b[:, None] * absD.max(axis=0)
+             + 2e-3 * 2 * np.einsum("ij,ijc->jc", P, absD) + 1e-5 * b[:, None])
+    ex, ey = np.abs(host(gx) - rx), np.abs(host(gy) - ry)
+    print(f"d={d} delta={delta}: grad_x error {ex.max():.2e}, grad_y error {ey.max():.2e}")
+    assert np.all(ex <= env_x)
+    assert np.all(ey <= env_y)
+    # one side alone gives the same values
+    gx2 = torch.empty((n, d), device="cuda")
+    B.fs_bs_gradient(p, eps, delta, dev(f), dev(g), grad_x=gx2)
+    torch.cuda.synchronize()
+    assert torch.equal(gx, gx2)
+    with pytest.raises(B.FsError):  # an output on top of an input
+        fdev = dev(np.zeros(n * d, np.float32))
+        B.fs_bs_gradient(p, eps, delta, fdev[:n], dev(g), grad_x=fdev.view(n, d))

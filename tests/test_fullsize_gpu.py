@@ -223,6 +223,28 @@ def test_full_size_block_sparse(fs, name, eps, delta):
     du = np.abs(host(Ub)[rows] - ref_u)
     print(f"  barycentric projection: max error {du.max():.2e} (skip bound {delta * np.abs(Y).max():.2e})")
     assert np.all(du <= delta * np.abs(Y).max() + 2e-3 * ref_ua)
+    # the gradient over the kept blocks on the sampled rows, by brute force in
+    # float64: 2 sum_j P_ij (x_i - y_j), within 2 delta a_i max_j |x_ic - y_jc|
+    # + 2e-3 (2 sum_j P_ij |x_ic - y_jc|) + 1e-5 a_i
+    gx = torch.empty((w.n, 3), device="cuda")
+    B.fs_bs_gradient(p, eps, delta, f_new, g_new, grad_x=gx)
+    torch.cuda.synchronize()
+    gxs = host(gx)[rows]
+    Y64 = Y.astype(np.float64)
+    worst = 0.0
+    for r0 in range(0, len(rows), 16):
+        rr = rows[r0:r0 + 16]
+        D = X[rr].astype(np.float64)[:, None, :] - Y64[None, :, :]
+        P = a[rr, None].astype(np.float64) * b[None, :] * np.exp(
+            (fn[rr, None].astype(np.float64) + gn[None, :] - (D ** 2).sum(-1)) / eps)
+        ref = 2 * np.einsum("ij,ijc->ic", P, D)
+        absD = np.abs(D)
+        env = (2 * delta * a[rr, None] * absD.max(axis=1)
+               + 2e-3 * 2 * np.einsum("ij,ijc->ic", P, absD) + 1e-5 * a[rr, None])
+        err = np.abs(gxs[r0:r0 + 16] - ref)
+        worst = max(worst, float((err / env).max()))
+        assert np.all(err <= env)
+    print(f"  gradient: largest error / envelope {worst:.2e}")
     # brute-force mass of the skipped blocks of two row blocks (f side)
     nbK = (w.m + 31) // 32
     for I in (0, len(cnt_f) // 2):
