@@ -360,6 +360,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hvp", action="store_true",
                     help="skip the Hessian-vector product measurement (d <= 64 recipes)")
+    ap.add_argument("--pipeline-n", type=int, default=0,
+                    help="fs2: also run the two-stage pipeline on two uniform clouds of this "
+                         "many points at eps = n^(-2/3) (one dense iteration timed beside it)")
     ap.add_argument("--no-block-sparse", action="store_true",
                     help="skip the block-sparse measurement of the c5 line")
     ap.add_argument("--counters", action="store_true",
@@ -548,13 +551,16 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def fs2_pipeline(w, dev, binding, torch, cell=8, tol=1e-2, max_iters=3000):
+def fs2_pipeline(w, dev, binding, torch, cell=8, tol=1e-2, max_iters=3000, dense_full=True,
+                 coarse_delta=0.0):
     """The whole two-stage solve on the workload (outside the timed steps):
     Morton order, the coarse stage (centroids of `cell` points, a dense solve
     on them annealed 0.1 -> eps, lift, sampled check on 1024 rows and columns,
     at most 2 rounds), then block-sparse iterations at eps from the lift until
     the L1 marginal residual of the retained blocks' plan is at most `tol`
-    (checked every 10 iterations)."""
+    (checked every 10 iterations).  coarse_delta > 0 runs the coarse solve in
+    block-sparse form.  Beside it the dense path from the same lift: to the
+    same target (dense_full), else one timed dense iteration."""
     import numpy as np
 
     X = torch.from_numpy(w.X).to(dev)
@@ -573,12 +579,14 @@ def fs2_pipeline(w, dev, binding, torch, cell=8, tol=1e-2, max_iters=3000):
     F = torch.empty(CX.shape[0], device=dev)
     G = torch.empty(CY.shape[0], device=dev)
     pc = binding.fs_potentials_init(CX, CY, WX, WY, f=F, g=G)
+    if coarse_delta > 0:
+        binding.fs_bs_attach(pc)
     f = torch.empty(w.n, device=dev)
     g = torch.empty(w.m, device=dev)
     cinfo = binding.fs_bs_coarse_start(pc, Xs, Ys, a_s, b_s, cell, f, g, F, G, rows, cols,
                                        eps_end=w.eps, eps_start=0.1, n_stages=12,
                                        iters_per_stage=10, more_iters=20, check_tol=0.5,
-                                       max_rounds=2)
+                                       max_rounds=2, coarse_delta=coarse_delta)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     f_lift, g_lift = f.clone(), g.clone()
@@ -595,23 +603,29 @@ def fs2_pipeline(w, dev, binding, torch, cell=8, tol=1e-2, max_iters=3000):
     # the dense path from the same lift to the same target
     t3 = time.perf_counter()
     dinfo = binding.fs_sinkhorn_solve(p, f_lift, g_lift, eps_end=w.eps,
-                                      iters_per_stage=max_iters, tol=tol, check_every=10,
+                                      iters_per_stage=max_iters if dense_full else 1,
+                                      tol=tol if dense_full else 0.0, check_every=10,
                                       warm_start=True, raise_not_converged=False)
     torch.cuda.synchronize()
     t4 = time.perf_counter()
-    return {"cell": cell, "coarse_points": [int(CX.shape[0]), int(CY.shape[0])],
-            "dense_fine_iters": dinfo["iters_done"], "dense_fine_ms": round((t4 - t3) * 1e3, 3),
+    dense = ({"dense_fine_iters": dinfo["iters_done"], "dense_fine_ms": round((t4 - t3) * 1e3, 3)}
+             if dense_full else {"dense_ms_per_iter": round((t4 - t3) * 1e3, 3)})
+    return {"n": w.n, "m": w.m, "eps": w.eps, "cell": cell, "coarse_delta": coarse_delta,
+            "coarse_points": [int(CX.shape[0]), int(CY.shape[0])], **dense,
             "coarse_ms": round((t1 - t0) * 1e3, 3), "coarse": cinfo,
             "fine_iters": info["iters_done"], "fine_ms": round((t2 - t1) * 1e3, 3),
             "fine_residual_retained": info["residual"],
             "dense_residual_after": [float(r[0]), float(r[1])],
             "total_ms": round((t2 - t0) * 1e3, 3), "target_residual": tol,
-            "what": "Morton order + coarse stage (dense solve on centroids, lift, sampled "
-                    "check) + block-sparse iterations from the lift to an L1 marginal "
+            "what": "Morton order + coarse stage (solve on centroids, block-sparse when "
+                    "coarse_delta > 0, lift, sampled check) + block-sparse iterations from "
+                    "the lift to an L1 marginal "
                     "residual <= target (wall clock, including the set-up)"}
 
 
 def main_block_sparse(args, w, peak, unit, dtype, desc, binding, torch):
+    from streaming_sinkhorn_solver_amd import workloads
+
     dev = torch.device("cuda:0")
     sampler = PowerSampler()
     sampler.start()
@@ -643,7 +657,11 @@ def main_block_sparse(args, w, peak, unit, dtype, desc, binding, torch):
         "clocks": sampler.summary(),
         "roofline": roofline,
         "block_sparse": bs,
-        "pipeline": fs2_pipeline(w, dev, binding, torch),
+        "pipeline": fs2_pipeline(w, dev, binding, torch, coarse_delta=BS_DELTA),
+        # cells of 16 points: the fastest of 4, 8, 16 and 32 on two 2M-point clouds
+        **({"pipeline_large": fs2_pipeline(
+            workloads.make("fs2", n=args.pipeline_n, m=args.pipeline_n), dev, binding, torch,
+            cell=16, dense_full=False, coarse_delta=BS_DELTA)} if args.pipeline_n else {}),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_block_sparse(w, bs)

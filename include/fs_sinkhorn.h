@@ -434,8 +434,14 @@ typedef struct {
  * both errors are at most check_tol or max_rounds checks were made, run
  * more_iters further coarse iterations from (F, G).  Synchronises once per
  * check.  workspace: fs_sampled_workspace_bytes(nrows, ncols) + 256 bytes.
- * f and g are then a warm start for the fine (block-sparse) solve. */
+ * f and g are then a warm start for the fine (block-sparse) solve.
+ * coarse_delta in [0, 1): 0 solves the coarse problem on the dense path; a
+ * positive value runs the coarse solves in block-sparse form
+ * (fs_bs_sinkhorn_solve with that delta; the coarse problem must have been
+ * attached with fs_bs_attach), which pays once the centroid clouds are large
+ * (the centroids of Morton-ordered cells keep that order's locality). */
 fs_status fs_bs_coarse_start(fs_problem* coarse, const fs_solve_opts* opts, int32_t more_iters,
+                             float coarse_delta,
                              const float* X, const float* Y, const float* a, const float* b,
                              int64_t n, int64_t m, int32_t d, int32_t cell, float check_tol,
                              int32_t max_rounds, const int32_t* rows, int32_t nrows,

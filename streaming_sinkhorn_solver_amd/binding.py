@@ -175,7 +175,8 @@ def load():
     lib.fs_sampled_marginal_error.argtypes = [_fp, _fp, _fp, _fp, i64, i64, i32, f32, _fp, _fp,
                                               _fp, i32, _fp, i32, _fp, _vp, sz, _vp]
     lib.fs_bs_coarse_start.restype = ctypes.c_int
-    lib.fs_bs_coarse_start.argtypes = [_vp, ctypes.POINTER(SolveOpts), i32, _fp, _fp, _fp, _fp,
+    lib.fs_bs_coarse_start.argtypes = [_vp, ctypes.POINTER(SolveOpts), i32, f32, _fp, _fp, _fp,
+                                       _fp,
                                        i64, i64, i32, i32, f32, i32, _fp, i32, _fp, i32, _fp,
                                        _fp, _fp, _fp, _vp, sz, ctypes.POINTER(CoarseInfo), _vp]
     _LIB = lib
@@ -597,9 +598,11 @@ def fs_sampled_marginal_error(X, Y, a, b, f, g, eps: float, rows, cols, out2=Non
 def fs_bs_coarse_start(coarse: Problem, X, Y, a, b, cell: int, f, g, F, G, rows, cols, *,
                        eps_end: float, iters_per_stage: int, n_stages: int = 1,
                        eps_start: Optional[float] = None, more_iters: int = 10,
-                       check_tol: float = 1e-2, max_rounds: int = 5, stream=None) -> dict:
+                       check_tol: float = 1e-2, max_rounds: int = 5, coarse_delta: float = 0.0,
+                       stream=None) -> dict:
     """The coarse stage (see include/fs_sinkhorn.h); fills F, G (coarse) and
-    f, g (lifted); returns rounds, accepted and the last errors."""
+    f, g (lifted); returns rounds, accepted and the last errors.  coarse_delta
+    > 0 solves the coarse problem in block-sparse form (attach it first)."""
     lib = load()
     n, d = X.shape
     m = Y.shape[0]
@@ -610,7 +613,8 @@ def fs_bs_coarse_start(coarse: Problem, X, Y, a, b, cell: int, f, g, F, G, rows,
                      float(eps_end), int(iters_per_stage), 0.0, 1, 0, 0)
     info = CoarseInfo()
     _check(lib.fs_bs_coarse_start(
-        coarse.handle, ctypes.byref(opts), int(more_iters), _dev(X, "X", n * d),
+        coarse.handle, ctypes.byref(opts), int(more_iters), float(coarse_delta),
+        _dev(X, "X", n * d),
         _dev(Y, "Y", m * d), _dev(a, "a", n), _dev(b, "b", m), n, m, d, int(cell),
         float(check_tol), int(max_rounds), _idev(rows, "rows", nr), nr, _idev(cols, "cols", nc),
         nc, _dev(F, "F", coarse.n), _dev(G, "G", coarse.m), _dev(f, "f", n), _dev(g, "g", m),

@@ -1543,7 +1543,7 @@ fs_status fs_sampled_marginal_error(const float* X, const float* Y, const float*
 }
 
 fs_status fs_bs_coarse_start(fs_problem* coarse, const fs_solve_opts* opts, int32_t more_iters,
-                             const float* X, const float* Y, const float* a, const float* b,
+                             float coarse_delta, const float* X, const float* Y, const float* a, const float* b,
                              int64_t n, int64_t m, int32_t d, int32_t cell, float check_tol,
                              int32_t max_rounds, const int32_t* rows, int32_t nrows,
                              const int32_t* cols, int32_t ncols, float* F, float* G, float* f,
@@ -1557,11 +1557,21 @@ fs_status fs_bs_coarse_start(fs_problem* coarse, const fs_solve_opts* opts, int3
         coarse->d != d)
         return fail(FS_ERR_INVALID_ARG, "the coarse problem must hold the centroids of cells "
                                         "of %d points of both clouds", cell);
+    if (!(coarse_delta >= 0.f && coarse_delta < 1.f))
+        return fail(FS_ERR_INVALID_ARG, "coarse_delta must be in [0, 1)");
+    if (coarse_delta > 0.f && !coarse->bs_on)
+        return fail(FS_ERR_INVALID_ARG, "coarse_delta > 0 needs fs_bs_attach on the coarse problem");
     if (workspace_bytes < fs_sampled_workspace_bytes(nrows, ncols) + kAlign)
         return fail(FS_ERR_WORKSPACE, "workspace must hold %zu bytes",
                     fs_sampled_workspace_bytes(nrows, ncols) + kAlign);
     hipStream_t s = (hipStream_t)stream;
-    fs_status st = fs_sinkhorn_solve(coarse, opts, F, G, nullptr, stream);
+    // the coarse solves: dense, or block-sparse with coarse_delta
+    auto coarse_solve = [&](const fs_solve_opts* o) {
+        return coarse_delta > 0.f ? fs_bs_sinkhorn_solve(coarse, o, coarse_delta, F, G, nullptr,
+                                                         stream)
+                                  : fs_sinkhorn_solve(coarse, o, F, G, nullptr, stream);
+    };
+    fs_status st = coarse_solve(opts);
     if (st != FS_OK && st != FS_ERR_NOT_CONVERGED) return st;
     float* out2 = (float*)((char*)workspace + fs_sampled_workspace_bytes(nrows, ncols));
     fs_solve_opts more{};
@@ -1588,7 +1598,7 @@ fs_status fs_bs_coarse_start(fs_problem* coarse, const fs_solve_opts* opts, int3
         ++k;
         ok = err[0] <= check_tol && err[1] <= check_tol;
         if (ok || k >= max_rounds) break;
-        if ((st = fs_sinkhorn_solve(coarse, &more, F, G, nullptr, stream)) != FS_OK) return st;
+        if ((st = coarse_solve(&more)) != FS_OK) return st;
     }
     if (info) {
         info->rounds = k;

@@ -106,6 +106,57 @@ def test_coarse_start(cell, tol, rounds):
     np.testing.assert_allclose([info["err_rows"], info["err_cols"]], ref["errors"], rtol=2e-3)
 
 
+def test_coarse_start_block_sparse():
+    """The coarse stage with its coarse solves in block-sparse form: the coarse
+    potentials equal those of fs_bs_sinkhorn_solve run with the same schedule
+    and delta on the same coarse problem (bit for bit: same launches, and that
+    solve has its own parity tests against the oracle's sparse iteration), the
+    lift copies them exactly, and the check's errors match the oracle's
+    sampled check on the lifted potentials (1e-4 relative)."""
+    import torch
+
+    B = _bind()
+    n, m, cell = 24000, 20000, 4
+    X, Y, a, b = _pair(14, n, m)
+    rng = np.random.default_rng(15)
+    rows = rng.choice(n, 128, replace=False).astype(np.int32)
+    cols = rng.choice(m, 128, replace=False).astype(np.int32)
+    eps, delta = 2e-3, 1e-3
+    Xd, Yd, ad, bd = dev(X), dev(Y), dev(a), dev(b)
+    CX, WX = B.fs_centroids(Xd, ad, cell)
+    CY, WY = B.fs_centroids(Yd, bd, cell)
+    F = torch.empty(CX.shape[0], device="cuda")
+    G = torch.empty(CY.shape[0], device="cuda")
+    pc = B.fs_potentials_init(CX, CY, WX, WY, f=F, g=G)
+    with pytest.raises(B.FsError):  # not attached
+        B.fs_bs_coarse_start(pc, Xd, Yd, ad, bd, cell, torch.empty(n, device="cuda"),
+                             torch.empty(m, device="cuda"), F, G, torch.from_numpy(rows).cuda(),
+                             torch.from_numpy(cols).cuda(), eps_end=eps, iters_per_stage=5,
+                             coarse_delta=delta)
+    B.fs_bs_attach(pc)
+    f = torch.empty(n, device="cuda")
+    g = torch.empty(m, device="cuda")
+    sched = dict(eps_end=eps, iters_per_stage=10, n_stages=6, eps_start=0.1)
+    info = B.fs_bs_coarse_start(pc, Xd, Yd, ad, bd, cell, f, g, F, G,
+                                torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda(),
+                                more_iters=0, check_tol=1e-9, max_rounds=1, coarse_delta=delta,
+                                **sched)
+    F2 = torch.zeros_like(F)
+    G2 = torch.zeros_like(G)
+    B.fs_bs_sinkhorn_solve(pc, F2, G2, delta=delta, **sched)
+    torch.cuda.synchronize()
+    assert torch.equal(F, F2) and torch.equal(G, G2)
+    counts = B.fs_bs_read_screen(pc, 1)
+    sh = B.fs_bs_shape(pc, 1)
+    assert counts.sum() < sh["row_blocks"] * sh["key_blocks"]  # the coarse solve skipped blocks
+    fh, gh = host(f), host(g)
+    assert np.array_equal(fh, host(F)[np.arange(n) // cell])
+    assert np.array_equal(gh, host(G)[np.arange(m) // cell])
+    ref = oc.sampled_marginal_error(X, Y, a, b, fh, gh, eps, rows, cols)
+    np.testing.assert_allclose([info["err_rows"], info["err_cols"]], ref, rtol=1e-4)
+    assert info["rounds"] == 1 and not info["accepted"]
+
+
 def test_coarse_argument_errors():
     import torch
 
