@@ -179,13 +179,35 @@ def bilinear_bound(u, v, lo1, hi1, lo2, hi2) -> float:
     return float(tot)
 
 
+def _key_group_fits(K, w_keys, pot_keys, eps, size):
+    """Per group of `size` consecutive keys: slopes and log-sum-exp terms of
+    both forms (g and g - |y|^2), as for a key block."""
+    V, G, V2, G2 = [], [], [], []
+    for J in range((K.shape[0] + size - 1) // size):
+        Q, g, w = K[J * size:(J + 1) * size], pot_keys[J * size:(J + 1) * size], \
+            w_keys[J * size:(J + 1) * size]
+        psi = g - (Q * Q).sum(axis=1)
+        V.append(slope(Q, g))
+        G.append(_lse(np.log(w) + (g - Q @ V[-1]) / eps))
+        V2.append(slope(Q, psi))
+        G2.append(_lse(np.log(w) + (psi - Q @ V2[-1]) / eps))
+    return V, G, V2, G2
+
+
 def screen(R, K, w_keys, pot_rows, pot_keys, eps: float, delta: float, BR: int = 256,
-           BK: int = 32, return_bounds: bool = False, row_blocks=None):
+           BK: int = 32, return_bounds: bool = False, row_blocks=None, chunk: int = 0):
     """Kept key blocks (ascending indices) of every row block, for the update
     of the rows' potential from the keys' potential (see the header).
     With return_bounds, also the log bound matrix beta[I, J] and the log
-    threshold.  row_blocks: screen only these row blocks (lists and rows of
-    beta in that order)."""
+    threshold (and, with chunks, the chunk bound matrix).  row_blocks: screen
+    only these row blocks (lists and rows of beta in that order).
+
+    chunk > 0: two-level screening.  Chunks of `chunk` consecutive key blocks
+    get a bound of their own (the same two forms over the chunk's box and
+    keys); a chunk whose bound is below the threshold is skipped whole, since
+    each of its blocks holds at most the chunk's mass.  Only the blocks of the
+    other chunks, and always those of the chunk of largest bound, are
+    screened one by one; the fallback block is the best of those."""
     R, K = np.asarray(R, np.float64), np.asarray(K, np.float64)
     w_keys = np.asarray(w_keys, np.float64)
     pot_rows = np.asarray(pot_rows, np.float64)
@@ -203,39 +225,49 @@ def screen(R, K, w_keys, pot_rows, pot_keys, eps: float, delta: float, BR: int =
         c.append((f - P @ U[-1]).max())
         U2.append(slope(P, phi))
         c2.append((phi - P @ U2[-1]).max())
-    V, G, V2, G2 = [], [], [], []
-    for J in range(nbK):
-        Q, g, w = K[J * BK:(J + 1) * BK], pot_keys[J * BK:(J + 1) * BK], w_keys[J * BK:(J + 1) * BK]
-        psi = g - (Q * Q).sum(axis=1)
-        V.append(slope(Q, g))
-        G.append(_lse(np.log(w) + (g - Q @ V[-1]) / eps))
-        V2.append(slope(Q, psi))
-        G2.append(_lse(np.log(w) + (psi - Q @ V2[-1]) / eps))
+    V, G, V2, G2 = _key_group_fits(K, w_keys, pot_keys, eps, BK)
     thr = np.log(delta / nbK) if delta > 0 else -np.inf
     beta = np.empty((nbR, nbK))
+
+    def bound(k, I, u, gg, u2, gg2, lo, hi):
+        H = pair_bound(U[k], u, rlo[I], rhi[I], lo, hi)
+        H2 = bilinear_bound(U2[k], u2, rlo[I], rhi[I], lo, hi)
+        return min(c[k] / eps + gg + H / eps, c2[k] / eps + gg2 + H2 / eps)
+
+    if chunk > 0:
+        nbC = (nbK + chunk - 1) // chunk
+        clo, chi = block_boxes(K, BK * chunk)
+        CV, CG, CV2, CG2 = _key_group_fits(K, w_keys, pot_keys, eps, BK * chunk)
+        cbeta = np.array([[bound(k, I, CV[C], CG[C], CV2[C], CG2[C], clo[C], chi[C])
+                           for C in range(nbC)] for k, I in enumerate(blocks)])
     lists = []
     for k, I in enumerate(blocks):
+        if chunk > 0:
+            live = cbeta[k] >= thr
+            live[int(np.argmax(cbeta[k]))] = True
         for J in range(nbK):
-            H = pair_bound(U[k], V[J], rlo[I], rhi[I], klo[J], khi[J])
-            H2 = bilinear_bound(U2[k], V2[J], rlo[I], rhi[I], klo[J], khi[J])
-            beta[k, J] = min(c[k] / eps + G[J] + H / eps, c2[k] / eps + G2[J] + H2 / eps)
+            if chunk > 0 and not live[J // chunk]:
+                beta[k, J] = -np.inf  # not screened
+                continue
+            beta[k, J] = bound(k, I, V[J], G[J], V2[J], G2[J], klo[J], khi[J])
         keep = np.nonzero(beta[k] >= thr)[0]
         if keep.size == 0:
             keep = np.array([int(np.argmax(beta[k]))])
         lists.append(keep)
     if return_bounds:
-        return lists, beta, thr
+        return (lists, beta, thr, cbeta) if chunk > 0 else (lists, beta, thr)
     return lists
 
 
 def update_sparse(R, K, w_keys, pot_keys, pot_rows, eps: float, delta: float, BR: int = 256,
-                  BK: int = 32, row_blocks=None):
+                  BK: int = 32, row_blocks=None, chunk: int = 0):
     """Retained-block update of the rows' potential; returns (new, lists).
     row_blocks: update only these row blocks (the other entries are NaN)."""
     R, K = np.asarray(R, np.float64), np.asarray(K, np.float64)
     w_keys = np.asarray(w_keys, np.float64)
     pot_keys = np.asarray(pot_keys, np.float64)
-    lists = screen(R, K, w_keys, pot_rows, pot_keys, eps, delta, BR, BK, row_blocks=row_blocks)
+    lists = screen(R, K, w_keys, pot_rows, pot_keys, eps, delta, BR, BK, row_blocks=row_blocks,
+                   chunk=chunk)
     blocks = range(len(lists)) if row_blocks is None else [int(I) for I in row_blocks]
     out = np.full(R.shape[0], np.nan)
     for I, keep in zip(blocks, lists):

@@ -17,6 +17,8 @@ B4  delta = 0 keeps every block: the update equals the dense oracle update;
 B5  every skipped block's true mass (brute force over its pairs) is below
     delta / N_J of the row's target, so the skipped mass of a row is below
     delta * a_i;
+    The two-level form (chunks of blocks skipped whole on a bound of their
+    own) passes the same brute-force check;
 B6  the certificate: 0 <= f_sparse - f_dense <= eps log(1 + delta
     exp((f_sparse - f_cur)/eps)) against the dense update, on problems where
     blocks are skipped;
@@ -178,9 +180,9 @@ def _converged(X, Y, a, b, eps):
     return r["f"], r["g"]
 
 
-def _block_mass_ok(R, K, w, pot_rows, pot_keys, eps, delta, BR, BK):
+def _block_mass_ok(R, K, w, pot_rows, pot_keys, eps, delta, BR, BK, chunk=0):
     """B5 check; returns the fraction of skipped (I, J) pairs."""
-    lists = bs.screen(R, K, w, pot_rows, pot_keys, eps, delta, BR, BK)
+    lists = bs.screen(R, K, w, pot_rows, pot_keys, eps, delta, BR, BK, chunk=chunk)
     nbK = (len(K) + BK - 1) // BK
     skipped = 0
     for I, keep in enumerate(lists):
@@ -206,6 +208,32 @@ def test_b5_skipped_block_mass(delta):
     assert frac > 0.1  # the check is not vacuous
     frac = _block_mass_ok(Y, X, a, g, f, eps, delta, 32, 32)
     assert frac > 0.1
+
+
+@pytest.mark.parametrize("delta", [1e-3, 0.0])
+def test_b5_two_level_screening(delta):
+    """The two-level form (chunks of 4 blocks of 32 keys): every skipped
+    block's true mass is still below delta / N_J (brute force), whole chunks
+    are skipped, every block of a live chunk that the one-level screening
+    keeps is kept, and delta = 0 keeps every block."""
+    X, Y, a, b = _clouds(9, 800, 2400)
+    eps = 1e-3
+    f, g = _converged(X, Y, a, b, eps)
+    frac = _block_mass_ok(X, Y, b, f, g, eps, delta, 32, 32, chunk=4)
+    lists, beta, thr, cbeta = bs.screen(X, Y, b, f, g, eps, delta, 32, 32, return_bounds=True,
+                                        chunk=4)
+    flat = bs.screen(X, Y, b, f, g, eps, delta, 32, 32)
+    nbK = (2400 + 31) // 32
+    if delta == 0:
+        assert frac == 0 and all(len(l) == nbK for l in lists)
+        return
+    assert frac > 0.3
+    dead = cbeta < thr
+    assert dead.mean() > 0.05  # chunks skipped whole, not only blocks
+    for k, (keep, ref) in enumerate(zip(lists, flat)):
+        assert set(keep.tolist()) <= set(ref.tolist()) | {int(np.argmax(beta[k]))}
+        live_ref = [J for J in ref.tolist() if not dead[k, J // 4]]
+        assert set(live_ref) <= set(keep.tolist())
 
 
 @pytest.mark.parametrize("warm", [True, False])
