@@ -330,7 +330,13 @@ size_t fs_bs_workspace_bytes(const fs_problem* p);
  * fs_bs_workspace_bytes(p) bytes, 256-byte aligned, owned by the caller,
  * which must outlive the handle's block-sparse calls.  Computes the blocks'
  * boxes and synchronises once (their magnitude).  Up to 2^27 - 544 points
- * per cloud. */
+ * per cloud.  Screening is two-level for a key cloud of at least
+ * FS_BS_MIN_CHUNKS (environment, read here; default 64, from 2 to 16384)
+ * chunks of 8192 keys: a chunk whose own mass bound (the same two fitted
+ * forms over its box) is below the threshold is skipped whole, which keeps
+ * the per-block guarantee since a block holds at most its chunk's mass; the
+ * blocks of the other chunks, and of the chunk of largest bound, are
+ * screened one by one. */
 fs_status fs_bs_attach(fs_problem* p, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One block-sparse half-step: screening with (f_cur, g), then

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
@@ -58,6 +59,9 @@ struct fs_problem {
     float4* bs_kbox[2] = {nullptr, nullptr};  // [nbK][2] of 32-key blocks
     float4* bs_rfit = nullptr;                // per pass: [2] fits (u, c) of the row blocks
     float4* bs_kfit = nullptr;                // per pass: [2] fits (v, G) of the key blocks
+    float4* bs_cbox = nullptr;                // per pass: [2] boxes of the key chunks
+    float4* bs_cfit = nullptr;                // per pass: [2] fits (v, G) of the key chunks
+    int bs_min_chunks = 64;                   // two-level screening from this many chunks
     int* bs_cnt[2] = {nullptr, nullptr};      // kept blocks per row block, last pass of a side
     int* bs_best = nullptr;                   // per row block: the block of largest bound
     float4* bs_org = nullptr;                 // per row block: [2] origin and format flag
@@ -1044,6 +1048,21 @@ namespace {
 constexpr int kBsTarget = FS_BS_SPLIT_TARGET;
 constexpr int kBsMaxSplit = 16;
 
+// Chunks of kChunkKeys keys in a key cloud of n points (0 above the LDS flag
+// limit of the screening).
+int bs_chunks_of(int64_t n) {
+    const int64_t c = (n + kChunkKeys - 1) / kChunkKeys;
+    return c <= kMaxChunks ? (int)c : 0;
+}
+
+// The chunks the screening uses for a key cloud of n points: the two-level
+// form from min_chunks chunks on (below that, its one-workgroup-per-chunk fit
+// costs more latency than the first level saves), else 0.
+int bs_chunks(int64_t n, int min_chunks) {
+    const int c = bs_chunks_of(n);
+    return c >= std::max(min_chunks, 2) ? c : 0;
+}
+
 // The per-block fits of the row side's potential `cur` and the key side's
 // `other`, then the screening of side 0 (rows X, keys Y) or 1 (rows Y, keys
 // X) into the problem's list buffer.
@@ -1064,9 +1083,15 @@ fs_status bs_screen_side(fs_problem* p, bool f_side, float eps, float delta, con
         return hip_fail(e, "block fit launch");
     const float thr2 = delta > 0.f ? (float)std::log2((double)delta / (double)nbK) : -INFINITY;
     const int sentinel = (int)(K.n_pad / 32);
+    // the two-level form once there are at least 4 chunks of 256 key blocks
+    const int nbC = bs_chunks(K.n, p->bs_min_chunks);
+    if (nbC > 0 && (e = launch_chunk_fit((const float*)K.ops, cK, p->d, K.n, other, K.lw2,
+                                         c_bias, p->bs_cbox, p->bs_cfit, s)) != hipSuccess)
+        return hip_fail(e, "chunk fit launch");
     if ((e = launch_screen(p->bs_rbox[side], p->bs_rfit, nbR, p->bs_kbox[side], p->bs_kfit, nbK,
                            c_bias, thr2, p->bs_mag, p->bs_list, p->bs_cnt[side], p->bs_best,
-                           cR, cK, p->d, p->bs_org, p->bs_cap[side], sentinel, s)) != hipSuccess)
+                           cR, cK, p->d, p->bs_org, p->bs_cap[side], sentinel, p->bs_cbox,
+                           p->bs_cfit, nbC, s)) != hipSuccess)
         return hip_fail(e, "screening launch");
     p->bs_last_side = side;
     return FS_OK;
@@ -1111,7 +1136,8 @@ fs_status fs_bs_half_step(fs_problem* p, bool f_side, float eps, float delta, co
 }
 
 struct BsLayout {
-    size_t rbox[2], kbox[2], rfit, kfit, cnt[2], best, org, nsplit, map, ptotal, list, part, total;
+    size_t rbox[2], kbox[2], rfit, kfit, cbox, cfit, cnt[2], best, org, nsplit, map, ptotal, list,
+        part, total;
 };
 
 BsLayout bs_layout(const fs_problem* p) {
@@ -1137,6 +1163,9 @@ BsLayout bs_layout(const fs_problem* p) {
     L.map = take(sizeof(int) * 2 * (std::max(nbR[0], nbR[1]) + kBsTarget));
     L.ptotal = take(sizeof(int) * 4);
     L.kfit = take(sizeof(float4) * 2 * std::max(nbK[0], nbK[1]));
+    const int64_t nbC = std::max<int64_t>(1, std::max(bs_chunks_of(m), bs_chunks_of(n)));
+    L.cbox = take(sizeof(float4) * 2 * nbC);
+    L.cfit = take(sizeof(float4) * 2 * nbC);
     const int64_t cap0 = (nbK[0] + 15) / 16 * 16, cap1 = (nbK[1] + 15) / 16 * 16;
     L.list = take(sizeof(int) * (size_t)std::max(nbR[0] * cap0, nbR[1] * cap1));
     L.part = take(sizeof(float2) * kBsMaxSplit * (size_t)std::max(n, m));
@@ -1228,6 +1257,13 @@ fs_status fs_bs_attach(fs_problem* p, void* workspace, size_t workspace_bytes, v
     }
     p->bs_rfit = (float4*)(w + L.rfit);
     p->bs_kfit = (float4*)(w + L.kfit);
+    p->bs_cbox = (float4*)(w + L.cbox);
+    p->bs_cfit = (float4*)(w + L.cfit);
+    {
+        const char* env = std::getenv("FS_BS_MIN_CHUNKS");
+        const long v = env ? std::strtol(env, nullptr, 10) : 64;
+        p->bs_min_chunks = v >= 2 && v <= kMaxChunks ? (int)v : 64;
+    }
     p->bs_list = (int*)(w + L.list);
     p->bs_part = (float2*)(w + L.part);
     p->bs_best = (int*)(w + L.best);

@@ -403,6 +403,105 @@ __global__ __launch_bounds__(256) void block_fit_kernel(const float* __restrict_
     }
 }
 
+// Box and key-side fits (both forms, as block_fit_kernel with KEY = true) of
+// chunks of kChunkKeys consecutive keys, one workgroup per chunk, each thread
+// taking every 256th key of it: cbox[2C], cbox[2C+1] = lo, hi; cfit[2C + form].
+__global__ __launch_bounds__(256) void chunk_fit_kernel(const float* __restrict__ ops,
+                                                        const float* __restrict__ centre, int d,
+                                                        int64_t n, const float* __restrict__ pot,
+                                                        const float* __restrict__ lw2,
+                                                        float c_bias, float4* __restrict__ cbox,
+                                                        float4* __restrict__ cfit) {
+    __shared__ float red[64];
+    constexpr int PER = kChunkKeys / 256;
+    const int C = blockIdx.x;
+    const int64_t i0 = (int64_t)C * kChunkKeys + threadIdx.x;
+    float s1[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+    auto point = [&](int k, float (&x)[3], float& p, float& q) {
+        const int64_t i = i0 + (int64_t)k * 256;
+        if (i >= n) return false;
+        load_point(ops, centre, d, i, x);
+        p = pot[i];
+        q = p - (x[0] * x[0] + x[1] * x[1] + x[2] * x[2]);
+        return true;
+    };
+    for (int k = 0; k < PER; ++k) {
+        float x[3], p, q;
+        if (!point(k, x, p, q)) break;
+        s1[0] += x[0];
+        s1[1] += x[1];
+        s1[2] += x[2];
+        s1[3] += p;
+        s1[4] += q;
+        s1[5] += 1.f;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            lo[c] = fminf(lo[c], x[c]);
+            hi[c] = fmaxf(hi[c], x[c]);
+        }
+    }
+    group_sum<256>(s1, red);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        hi[c] = group_max<256>(hi[c], red);
+        lo[c] = -group_max<256>(-lo[c], red);
+    }
+    const float inv = s1[5] > 0.f ? 1.f / s1[5] : 0.f;
+    float S[12] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < PER; ++k) {
+        float x[3], p, q;
+        if (!point(k, x, p, q)) break;
+        const float cx = x[0] - s1[0] * inv, cy = x[1] - s1[1] * inv, cz = x[2] - s1[2] * inv;
+        const float cp = p - s1[3] * inv, cq = q - s1[4] * inv;
+        S[0] += cx * cx;
+        S[1] += cy * cy;
+        S[2] += cz * cz;
+        S[3] += cx * cy;
+        S[4] += cx * cz;
+        S[5] += cy * cz;
+        S[6] += cx * cp;
+        S[7] += cy * cp;
+        S[8] += cz * cp;
+        S[9] += cx * cq;
+        S[10] += cy * cq;
+        S[11] += cz * cq;
+    }
+    group_sum<256>(S, red);
+    if (threadIdx.x == 0) {
+        cbox[2 * C] = make_float4(lo[0], lo[1], lo[2], 0.f);
+        cbox[2 * C + 1] = make_float4(hi[0], hi[1], hi[2], 0.f);
+    }
+#pragma unroll
+    for (int form = 0; form < 2; ++form) {
+        const float Sf[9] = {S[0], S[1], S[2], S[3], S[4], S[5], S[6 + 3 * form],
+                             S[7 + 3 * form], S[8 + 3 * form]};
+        float u[3];
+        solve_slope(Sf, u);
+        // base-2 log-sum of lw2_j + (value_j - u.y_j) c_bias over the chunk
+        float M = -INFINITY;
+        for (int k = 0; k < PER; ++k) {
+            float x[3], p, q;
+            if (!point(k, x, p, q)) break;
+            const float r = (form ? q : p) - (u[0] * x[0] + u[1] * x[1] + u[2] * x[2]);
+            M = fmaxf(M, fmaf(r, c_bias, lw2[i0 + (int64_t)k * 256]));
+        }
+        M = group_max<256>(M, red);
+        float e[1] = {0.f};
+        if (M > -INFINITY)
+            for (int k = 0; k < PER; ++k) {
+                float x[3], p, q;
+                if (!point(k, x, p, q)) break;
+                const float r = (form ? q : p) - (u[0] * x[0] + u[1] * x[1] + u[2] * x[2]);
+                e[0] += ex2(fmaf(r, c_bias, lw2[i0 + (int64_t)k * 256]) - M);
+            }
+        group_sum<256>(e, red);
+        if (threadIdx.x == 0)
+            cfit[2 * C + form] =
+                make_float4(u[0], u[1], u[2], M > -INFINITY ? M + lg2(e[0]) : -INFINITY);
+    }
+}
+
 // ---------------------------------------------------------------- screening
 
 __device__ __forceinline__ float hq(float u, float v, float x, float y) {
@@ -448,12 +547,17 @@ struct ScreenArgs {
     float4* org;
     int cap;
     int sentinel;
+    // two-level form (nbC > 0): boxes and fits of chunks of 256 key blocks
+    const float4* cbox;  // [nbC][2]
+    const float4* cfit;  // [nbC][2]
+    int nbC;
 };
 
 __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
     __shared__ int wcnt[4];
     __shared__ float bred[4];
     __shared__ int jred[4];
+    __shared__ unsigned char clive[kMaxChunks];
     const int I = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const float4 rlo = a.rbox[2 * I], rhi = a.rbox[2 * I + 1];
@@ -474,21 +578,65 @@ __global__ __launch_bounds__(256) void screen_kernel(ScreenArgs a) {
                            fmaxf(fabsf(klo.y - O[1]), fabsf(khi.y - O[1]))),
                      fmaxf(fabsf(klo.z - O[2]), fabsf(khi.z - O[2])));
     };
+    // log2 bound of the mass a key group (box klo..khi, fits kf, kq) can hold
+    // in any row of this row block
+    auto bound = [&](float4 kf, float4 kq, float4 klo, float4 khi) {
+        const float H = hmax1(rf.x, kf.x, rlo.x, rhi.x, klo.x, khi.x) +
+                        hmax1(rf.y, kf.y, rlo.y, rhi.y, klo.y, khi.y) +
+                        hmax1(rf.z, kf.z, rlo.z, rhi.z, klo.z, khi.z);
+        const float H2 = bmax1(rq.x, kq.x, rlo.x, rhi.x, klo.x, khi.x) +
+                         bmax1(rq.y, kq.y, rlo.y, rhi.y, klo.y, khi.y) +
+                         bmax1(rq.z, kq.z, rlo.z, rhi.z, klo.z, khi.z);
+        return fminf(fmaf(H, a.c_bias, base2) + kf.w, fmaf(H2, a.c_bias, baseq) + kq.w);
+    };
+    if (a.nbC > 0) {
+        // first level: a chunk below the threshold holds less than that mass in
+        // every one of its blocks; the chunk of largest bound is always opened
+        float cb = -INFINITY;
+        int cj = 0;
+        for (int C = tid; C < a.nbC; C += 256) {
+            const float beta =
+                bound(a.cfit[2 * C], a.cfit[2 * C + 1], a.cbox[2 * C], a.cbox[2 * C + 1]);
+            clive[C] = beta >= thr ? 1 : 0;
+            if (beta > cb) {
+                cb = beta;
+                cj = C;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float b2 = __shfl_xor(cb, o, 64);
+            const int j2 = __shfl_xor(cj, o, 64);
+            if (b2 > cb || (b2 == cb && j2 < cj)) {
+                cb = b2;
+                cj = j2;
+            }
+        }
+        if (lane == 0) {
+            bred[w] = cb;
+            jred[w] = cj;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float bb = bred[0];
+            int jj = jred[0];
+            for (int q = 1; q < 4; ++q)
+                if (bred[q] > bb || (bred[q] == bb && jred[q] < jj)) {
+                    bb = bred[q];
+                    jj = jred[q];
+                }
+            clive[jj] = 1;
+        }
+        __syncthreads();
+    }
     float wmax = 0.f;
     for (int J0 = 0; J0 < a.nbK; J0 += 256) {
+        if (a.nbC > 0 && !clive[J0 >> 8]) continue;  // uniform: J0 is the same in every thread
         const int J = J0 + tid;
         bool keep = false;
         if (J < a.nbK) {
-            const float4 kf = a.kfit[2 * J], kq = a.kfit[2 * J + 1];
-            const float4 klo = a.kbox[2 * J], khi = a.kbox[2 * J + 1];
-            const float H = hmax1(rf.x, kf.x, rlo.x, rhi.x, klo.x, khi.x) +
-                            hmax1(rf.y, kf.y, rlo.y, rhi.y, klo.y, khi.y) +
-                            hmax1(rf.z, kf.z, rlo.z, rhi.z, klo.z, khi.z);
-            const float H2 = bmax1(rq.x, kq.x, rlo.x, rhi.x, klo.x, khi.x) +
-                             bmax1(rq.y, kq.y, rlo.y, rhi.y, klo.y, khi.y) +
-                             bmax1(rq.z, kq.z, rlo.z, rhi.z, klo.z, khi.z);
             const float beta =
-                fminf(fmaf(H, a.c_bias, base2) + kf.w, fmaf(H2, a.c_bias, baseq) + kq.w);
+                bound(a.kfit[2 * J], a.kfit[2 * J + 1], a.kbox[2 * J], a.kbox[2 * J + 1]);
             keep = beta >= thr;
             if (beta > best) {
                 best = beta;
@@ -994,10 +1142,23 @@ hipError_t launch_block_fit(const float* ops, const float* centre, int d, int64_
     return hipGetLastError();
 }
 
+hipError_t launch_chunk_fit(const float* ops, const float* centre, int d, int64_t n,
+                            const float* pot, const float* lw2, float c_bias, float4* cbox,
+                            float4* cfit, hipStream_t s) {
+    const int64_t nbC = (n + kChunkKeys - 1) / kChunkKeys;
+    if (nbC < 1 || nbC > kMaxChunks) return hipErrorInvalidValue;
+    chunk_fit_kernel<<<(unsigned)nbC, 256, 0, s>>>(ops, centre, d, n, pot, lw2, c_bias, cbox,
+                                                   cfit);
+    return hipGetLastError();
+}
+
 hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const float4* kbox,
                          const float4* kfit, int nbK, float c_bias, float thr2, float mag,
                          int* list, int* count, int* best, const float* cR, const float* cK,
-                         int d, float4* org, int cap, int sentinel, hipStream_t s) {
+                         int d, float4* org, int cap, int sentinel, const float4* cbox,
+                         const float4* cfit, int nbC, hipStream_t s) {
+    if (nbC < 0 || nbC > kMaxChunks || (nbC > 0 && nbC != (nbK + 255) / 256))
+        return hipErrorInvalidValue;
     ScreenArgs a;
     a.rbox = rbox;
     a.rfit = rfit;
@@ -1018,6 +1179,9 @@ hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const 
     a.org = org;
     a.cap = cap;
     a.sentinel = sentinel;
+    a.cbox = cbox;
+    a.cfit = cfit;
+    a.nbC = nbC;
     screen_kernel<<<nbR, 256, 0, s>>>(a);
     return hipGetLastError();
 }

@@ -275,10 +275,22 @@ hipError_t launch_split_plan(const int* count, int nbR, int target, int smax, in
 // their count, and the key block of largest bound.
 // Also the row block's origin for shifted fp16 operands and its format flag
 // (org[2I], org[2I+1]; cR, cK: the row and key clouds' centres).
+// Two-level screening: chunks of kChunkKeys keys (256 key blocks of 32), at
+// most kMaxChunks of them (the screening keeps one flag per chunk in LDS).
+constexpr int kChunkKeys = 8192;
+constexpr int kMaxChunks = 16384;
+// Boxes and key-side fits of the chunks of a cloud (n keys, ceil(n /
+// kChunkKeys) <= kMaxChunks chunks).
+hipError_t launch_chunk_fit(const float* ops, const float* centre, int d, int64_t n,
+                            const float* pot, const float* lw2, float c_bias, float4* cbox,
+                            float4* cfit, hipStream_t s);
+// nbC > 0 (= ceil(nbK / 256)): skip the chunks whose own bound is below the
+// threshold before screening the blocks of the others.
 hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const float4* kbox,
                          const float4* kfit, int nbK, float c_bias, float thr2, float mag,
                          int* list, int* count, int* best, const float* cR, const float* cK,
-                         int d, float4* org, int cap, int sentinel, hipStream_t s);
+                         int d, float4* org, int cap, int sentinel, const float4* cbox,
+                         const float4* cfit, int nbC, hipStream_t s);
 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
 // Matrix paths: the streaming transport kernel serves operand rows of up to

@@ -82,14 +82,18 @@ def _gpu_problem(X, Y, a, b):
     return p
 
 
-def _check_lists(p, side, R, K, w_keys, pot_rows, pot_keys, eps, delta):
+def _check_lists(p, side, R, K, w_keys, pot_rows, pot_keys, eps, delta, chunk=0):
     """Every skipped block's true mass is below delta/N_J of its rows' targets;
-    every block the oracle keeps with a margin is kept."""
+    every block the oracle keeps with a margin is kept (with chunks: a block
+    whose own and whose chunk's bounds clear the threshold by that margin)."""
     B = _bind()
     counts, L = B.fs_bs_read_screen(p, side, lists=True)
     nbR, nbK = len(counts), (len(K) + 31) // 32
-    ref_lists, beta, thr = obs.screen(R, K, w_keys, pot_rows, pot_keys, eps, delta, 256, 32,
-                                      return_bounds=True)
+    bounds = obs.screen(R, K, w_keys, pot_rows, pot_keys, eps, delta, 256, 32,
+                        return_bounds=True, chunk=chunk)
+    ref_lists, beta, thr = bounds[:3]
+    if chunk:
+        beta = np.where(np.repeat(bounds[3] >= thr + 1e-3, chunk, axis=1)[:, :nbK], beta, -np.inf)
     R64, K64 = R.astype(np.float64), K.astype(np.float64)
     skipped = 0
     for I in range(nbR):
@@ -156,6 +160,45 @@ def test_bs_update_certificate(n, m, d, eps, delta, min_skip):
     assert np.all(gs - ref <= cert + TOL * eps)
     print(f"skipped block pairs: f {frac_f:.3f}  g {frac_g:.3f}")
     assert frac_f >= min_skip and frac_g >= min_skip
+
+
+@pytest.mark.parametrize("delta", [1e-3, 0.0])
+def test_bs_two_level_screening(delta, monkeypatch):
+    """With FS_BS_MIN_CHUNKS=4 a key cloud of 5 chunks of 8192 keys takes the
+    two-level screening: the kept lists against the oracle's two-level screening
+    (brute-force mass of every skipped block, every block kept by the oracle
+    with a margin kept), on both sides, and the update within the
+    certificate of the dense oracle update."""
+    import torch
+
+    B = _bind()
+    n, m, eps = 1024, 33000, 2e-3
+    X, Y, a, b = _sorted_problem(71, n, m, 3, xkind="mixture", ykind="uniform")
+    # a consistent pair (f the exact update from g = 0: every row's mass sums
+    # to its target), at which far blocks hold little mass
+    g = np.zeros(m)
+    f = oracle.f_update(X, Y, b, g, eps)
+    monkeypatch.setenv("FS_BS_MIN_CHUNKS", "4")  # read by fs_bs_attach
+    p = _gpu_problem(X, Y, a, b)
+    f_new = torch.empty(n, device="cuda")
+    B.fs_bs_lse_update_f(p, eps, delta, dev(g), dev(f), f_new)
+    torch.cuda.synchronize()
+    frac = _check_lists(p, 0, X, Y, b, f, g, eps, delta, chunk=256)
+    if delta > 0:
+        assert frac > 0.3
+        counts, L = B.fs_bs_read_screen(p, 0, lists=True)
+        nbC = (m + 8191) // 8192
+        open_chunks = [set((L[I, :counts[I]] // 256).tolist()) for I in range(len(counts))]
+        assert min(len(c) for c in open_chunks) < nbC  # whole chunks were skipped
+    ref = oracle.f_update(X, Y, b, g, eps)
+    fn = host(f_new)
+    cert = obs.certificate(fn, f, eps, delta)
+    assert np.all(fn - ref >= -TOL * eps) and np.all(fn - ref <= cert + TOL * eps)
+    # the g side: keys X (1024 points, one-level form)
+    g_new = torch.empty(m, device="cuda")
+    B.fs_bs_lse_update_g(p, eps, delta, dev(f), dev(g), g_new)
+    torch.cuda.synchronize()
+    _check_lists(p, 1, Y, X, a, g, f, eps, delta)
 
 
 def test_bs_delta_zero_is_the_dense_update():
