@@ -286,7 +286,8 @@ def test_b7_planted_slips_are_caught(monkeypatch):
     _block_mass_ok(X, Y, b, f, g, eps, delta, 32, 32)  # the rule itself holds for any f
     orig_screen = bs.screen
 
-    def screen_mean(R, K, w, pr, pk, eps_, delta_, BR=256, BK=32, return_bounds=False):
+    def screen_mean(R, K, w, pr, pk, eps_, delta_, BR=256, BK=32, return_bounds=False, chunk=0):
+        assert chunk == 0
         lists, beta, thr = orig_screen(R, K, w, pr, pk, eps_, delta_, BR, BK, True)
         out = []
         for I in range(beta.shape[0]):
