@@ -36,9 +36,8 @@ def common_flags() -> list:
             "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str, obj: str, defines=()) -> None:
-    cmd = [hipcc()] + common_flags() + [f"-D{d}" for d in defines] + \
-        ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str) -> None:
+    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
@@ -49,14 +48,13 @@ def _compile(src: str, obj: str, defines=()) -> None:
         print(f"[build] {src}:\n{rest}", file=sys.stderr)
 
 
-def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
-    """Compile all sources (always) and link the library; returns its path.
-    ``defines`` are extra -D macros (launch-shape variants for tuning)."""
+def build(verbose: bool = True, out: str = LIB) -> str:
+    """Compile all sources (always) and link the library; returns its path."""
     tmp = tempfile.mkdtemp(prefix="fs_build_")
     try:
         objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
         with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-            list(ex.map(lambda so: _compile(so[0], so[1], defines), zip(SOURCES, objs)))
+            list(ex.map(lambda so: _compile(so[0], so[1]), zip(SOURCES, objs)))
         out_tmp = out + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp] + objs
         subprocess.run(cmd, check=True, capture_output=True, text=True)

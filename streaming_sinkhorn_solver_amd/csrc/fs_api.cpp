@@ -616,16 +616,18 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
     bool have_next_f = false;  // pot_tmp already holds the next f-update (same eps)
     fs_status st;
     auto check = [&](float eps_c, bool& reusable_next) -> fs_status {
-        // Row term of the residual of (f, g) via a dry-run f-update into
-        // pot_tmp; the column term is identically zero after a g-update (the
-        // stored g is exactly the g-update of f, and the pass is deterministic).
-        fs_status s2 = half_step(p, true, eps_c, g, p->pot_tmp, f, p->scal, 0, s);
+        // Both terms of the L1 residual of (f, g) from dry-run updates: the
+        // column term (a g-update of f into pot_tmp, against g) first, then
+        // the row term (an f-update of g into pot_tmp, against f), whose
+        // output is the next iteration's f-update and is kept for it.
+        fs_status s2 = half_step(p, false, eps_c, f, p->pot_tmp, g, p->scal + 1, 0, s);
+        if (s2 == FS_OK) s2 = half_step(p, true, eps_c, g, p->pot_tmp, f, p->scal, 0, s);
         if (s2 != FS_OK) return s2;
-        float h = 0.f;
-        hipError_t e2 = hipMemcpyAsync(&h, p->scal, sizeof(float), hipMemcpyDeviceToHost, s);
+        float h[2] = {0.f, 0.f};
+        hipError_t e2 = hipMemcpyAsync(h, p->scal, sizeof(h), hipMemcpyDeviceToHost, s);
         if (e2 == hipSuccess) e2 = hipStreamSynchronize(s);
         if (e2 != hipSuccess) return hip_fail(e2, "residual readback");
-        resid = h;
+        resid = h[0] + h[1];
         reusable_next = true;
         return FS_OK;
     };
@@ -1042,10 +1044,7 @@ namespace {
 // kBsTarget workgroups share them evenly (a row block's list to at most
 // kBsMaxSplit of them); the kernel is launched with row blocks + kBsTarget
 // workgroups, the plan's upper bound.
-#ifndef FS_BS_SPLIT_TARGET
-#define FS_BS_SPLIT_TARGET 4096
-#endif
-constexpr int kBsTarget = FS_BS_SPLIT_TARGET;
+constexpr int kBsTarget = 4096;
 constexpr int kBsMaxSplit = 16;
 
 // Chunks of kChunkKeys keys in a key cloud of n points (0 above the LDS flag
@@ -1366,16 +1365,20 @@ fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delt
     float resid = -1.f, eps = o->eps_end;
     bool converged = false;
     auto check = [&](float eps_c) -> fs_status {
-        // row term of the residual of (f, g) from a dry-run update into pot_tmp;
-        // the column term is zero right after a g-update
-        fs_status s2 = fs_bs_half_step(p, true, eps_c, delta, f, g, p->pot_tmp, p->scal, s,
+        // both terms of the residual of (f, g) (of the plan on the kept
+        // blocks) from dry-run updates into pot_tmp: the column term, then
+        // the row term
+        fs_status s2 = fs_bs_half_step(p, false, eps_c, delta, g, f, p->pot_tmp, p->scal + 1, s,
                                        nullptr, nullptr);
+        if (s2 == FS_OK)
+            s2 = fs_bs_half_step(p, true, eps_c, delta, f, g, p->pot_tmp, p->scal, s, nullptr,
+                                 nullptr);
         if (s2 != FS_OK) return s2;
-        float h = 0.f;
-        hipError_t e2 = hipMemcpyAsync(&h, p->scal, sizeof(float), hipMemcpyDeviceToHost, s);
+        float h[2] = {0.f, 0.f};
+        hipError_t e2 = hipMemcpyAsync(h, p->scal, sizeof(h), hipMemcpyDeviceToHost, s);
         if (e2 == hipSuccess) e2 = hipStreamSynchronize(s);
         if (e2 != hipSuccess) return hip_fail(e2, "residual readback");
-        resid = h;
+        resid = h[0] + h[1];
         return FS_OK;
     };
     for (int si = 0; si < o->n_stages && !converged; ++si) {

@@ -133,58 +133,16 @@ __global__ __launch_bounds__(256) void lse_valu_kernel(LseArgs a) {
 }
 
 // ------------------------------------------------------ matrix-core path
-#ifndef FS_MFMA_WAVES
-#define FS_MFMA_WAVES 8
-#endif
-#ifndef FS_MFMA_QB_MAX
-#define FS_MFMA_QB_MAX 2
-#endif
-constexpr int kMfmaWaves = FS_MFMA_WAVES;  // waves per workgroup of the matrix-core kernel
-constexpr int kQbMax = FS_MFMA_QB_MAX;     // cap on 32-row blocks per wave
-#ifdef FS_NO_PINGPONG
-constexpr bool kPingPong = false;
-#else
-constexpr bool kPingPong = true;  // opposite MFMA/epilogue order in the two wave halves
-#endif
-#ifndef FS_APIPE
-#define FS_APIPE 8
-#endif
-constexpr int kAPipe = FS_APIPE;  // operand fragments in flight, one wave per SIMD
-#ifndef FS_APIPE8
-#define FS_APIPE8 4
-#endif
-constexpr int kAPipe8 = FS_APIPE8;  // operand fragments in flight, two waves per SIMD
-#ifdef FS_NO_PIN_SCHED
-constexpr bool kPinSched = false;
-#else
-constexpr bool kPinSched = true;
-#endif
-#ifndef FS_VALU_PER_SLOT
-#define FS_VALU_PER_SLOT 6
-#endif
-constexpr int kValuPerSlot = FS_VALU_PER_SLOT;  // epilogue instructions per operand fragment
-#ifndef FS_VALU_MASK
-#define FS_VALU_MASK 0x002
-#endif
-#ifdef FS_NO_LAG_DMA
-constexpr bool kLagDma = false;
-#else
-constexpr bool kLagDma = true;  // two waves per SIMD: the lagging waves issue all tile loads
-#endif
-#ifdef FS_EXACT_MAX
-constexpr bool kLazyRef = false;
-#else
-constexpr bool kLazyRef = true;  // two waves per SIMD: lazy LSE reference (below)
-#endif
+constexpr int kMfmaWaves = 8;    // waves per workgroup of the matrix-core kernel
+constexpr int kQbMax = 2;        // cap on 32-row blocks per wave
+constexpr int kAPipe = 8;        // operand fragments in flight, one wave per SIMD
+constexpr int kAPipe8 = 4;       // operand fragments in flight, two waves per SIMD
+constexpr int kValuPerSlot = 6;  // epilogue instructions per operand fragment (one wave per SIMD)
 // Lazy reference: a tile's terms 2^(z2 - R) are summed against the running
 // reference R as they come; only when some lane's tile sum is not at most
 // this bound (a score more than ~64 above R, or R still -inf) does the wave
 // move R to the exact running maximum and rescale.
 constexpr float kLazyBound = 0x1p64f;
-#ifndef FS_WIDE_DMA
-#define FS_WIDE_DMA 1
-#endif
-constexpr int kWideDma = FS_WIDE_DMA;  // tile-load placement of the 1024-wide kernel
 
 
 template <int OP, class TA, class TB>
@@ -252,7 +210,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     // With two waves per SIMD the tile loads are issued by the four lagging
     // waves only (whose epilogue phase has issue slots to spare), so the
     // leading waves go from the barrier straight into their matrix work.
-    constexpr bool LAG_DMA = WAVES == 8 && kLagDma && kPingPong;
+    constexpr bool LAG_DMA = WAVES == 8;
     constexpr int DMA_WAVES = LAG_DMA ? WAVES / 2 : WAVES;
     constexpr int INSTR_PER_WAVE = (TILE_INSTR + DMA_WAVES - 1) / DMA_WAVES;
     constexpr int MIN_INSTR = TILE_INSTR / DMA_WAVES;  // loads per tile of every loading wave
@@ -452,13 +410,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         constexpr int G1 = decltype(g1_c)::value;
         constexpr bool FIRST = decltype(first_c)::value;
         constexpr int VPS = decltype(vps_c)::value;
-        if constexpr (kPinSched) {
+        {
             if constexpr (FIRST) __builtin_amdgcn_sched_group_barrier(0x100, AP + 4 * QB, 0);
 #pragma unroll
             for (int g = G0; g < G1; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, MF_PER_FRAG, 0);
                 if (g + AP < NG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (VPS > 0) __builtin_amdgcn_sched_group_barrier(FS_VALU_MASK, VPS, 0);
+                if (VPS > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPS, 0);
             }
         }
     };
@@ -596,7 +554,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     __syncthreads();
 
     // waves whose epilogue runs one tile behind their scores
-    const bool lagging = WAVES != 8 || (kPingPong && wave >= 4);
+    const bool lagging = WAVES != 8 || wave >= 4;
     // One stage (tile s in buffer slot I = s % NBUF; the load of tile
     // s+NBUF-1 goes to slot I-1, which every wave finished reading before the
     // previous barrier).  Past the end the load is clamped to the last tile:
@@ -614,21 +572,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
             if (!lagging) {
                 mfma_tile(i_c, bb, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (kLazyRef)
-                    epilogue_lazy(acc);
-                else
-                    epilogue(acc);
+                epilogue_lazy(acc);
             } else {
                 if constexpr (LAG_DMA) {
                     issue_tile(min(s + NBUF - 1, ntiles - 1), buf((I + NBUF - 1) % NBUF));
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                if (s > 0) {
-                    if constexpr (kLazyRef)
-                        epilogue_lazy(prev);
-                    else
-                        epilogue(prev);
-                }
+                if (s > 0) epilogue_lazy(prev);
                 __builtin_amdgcn_sched_barrier(0);
                 mfma_tile(i_c, bb, acc);
             }
@@ -748,16 +698,13 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
     const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
     const char* __restrict__ keys = (const char*)a.keys;
 
-    // Tile loads: 64 slices of 1 KiB (half a key row each).  kWideDma 0: the
-    // second waves issue 16 slices each at the start of a stage; 1: the first
-    // waves issue 16 each, one after every other matrix instruction; 2: both,
-    // 8 each (second waves at the start, first waves every fourth matrix
-    // instruction).
-    constexpr int SHARE = kWideDma == 2 ? 8 : 16;
-    const bool loader = kWideDma == 2 || (kWideDma == 1) == first;
+    // Tile loads: 64 slices of 1 KiB (half a key row each); the first waves
+    // issue 16 each, one after every other matrix instruction.
+    constexpr int SHARE = 16;
+    const bool loader = first;
     const uint32_t lane16 = (uint32_t)lane * 16u;
     auto issue_slice = [&](int k, int slot, int l) __attribute__((always_inline)) {
-        const int L = kWideDma == 2 ? l * 8 + rg + 4 * dh : l * 4 + rg;
+        const int L = l * 4 + rg;
         const char* tbase = keys + (int64_t)(j0 + k * kKeyTile) * ROW_BYTES;
         const int m = L >> 1;
         uint32_t sw = (uint32_t)(m & 15) * 16u;
@@ -836,7 +783,7 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
             if constexpr (DE > 0)
                 if (g % DE == DE - 1) issue_slice(kd, 1 - decltype(slot_c)::value, g / DE);
         }
-        if constexpr (kPinSched) {
+        {
             __builtin_amdgcn_sched_group_barrier(0x100, AP, 0);
 #pragma unroll
             for (int g = 0; g < HG; ++g) {
@@ -893,8 +840,7 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
     using S1 = std::integral_constant<int, 1>;
     f32x16 accA, accB;
     auto stage = [&](int s, auto slot_c, f32x16& acc, f32x16& prev) __attribute__((always_inline)) {
-        constexpr int SL = decltype(slot_c)::value;
-        using DF = std::integral_constant<int, kWideDma == 0 ? 0 : (kWideDma == 1 ? 2 : 4)>;
+        using DF = std::integral_constant<int, 2>;  // a slice after every other matrix instruction
         using D0 = std::integral_constant<int, 0>;
         const int kn = min(s + 1, ntiles - 1);
         if (first) {
@@ -904,7 +850,6 @@ __global__ __launch_bounds__(512, 1) void lse_wide_kernel(LseArgs a) {
             put(acc, s & 1);
             if (s > 0) epilogue(prev, (s - 1) & 1);
         } else {
-            if constexpr (kWideDma != 1) issue_tile(kn, 1 - SL);
             __builtin_amdgcn_sched_barrier(0);
             if (s > 0) epilogue(prev, (s - 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -1058,11 +1003,6 @@ int mfma_qb(int path, int ng) {
 
 int ng_of(int path, int dp) { return path == PATH_MFMA_F32 ? dp / 8 : dp / 16; }
 
-#ifdef FS_NO_WIDE_LSE
-constexpr bool kWideLse = false;
-#else
-constexpr bool kWideLse = true;
-#endif
 
 template <int OP>
 hipError_t wide_launch(const LseArgs& a, hipStream_t s) {
@@ -1074,7 +1014,7 @@ hipError_t wide_launch(const LseArgs& a, hipStream_t s) {
 }  // namespace
 
 bool lse_wide(int path, int dp) {
-    return kWideLse && (path == PATH_MFMA_BF16 || path == PATH_MFMA_F16) && dp == 1024;
+    return (path == PATH_MFMA_BF16 || path == PATH_MFMA_F16) && dp == 1024;
 }
 
 // The vector path uses 4 rows per lane when there are enough rows to fill the

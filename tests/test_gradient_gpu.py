@@ -7,12 +7,7 @@ Bars:
   P^T.W          relative Frobenius error <= 1e-3 (the transport bar: f16
                  weights in (0, 1] and an f16 copy of W scaled by a power of
                  two, ~2^-11 per product, averaged);
-  gradient       <= 1e-3 relative to the Frobenius norm of the transported
-                 term, 2 ||sum_j P_ij (y_j - mu)||: the gradient is that term
-                 subtracted from an fp32-exact one, so the transport's
-                 relative error carries over at that scale (at convergence
-                 the two terms nearly cancel, and the gradient itself can be
-                 far smaller than either);
+  gradient       relative Frobenius error <= 1e-3 of the gradient itself;
   dual value     relative 1e-12 (fp64 sums of exact fp32 x fp32 products).
 For the bf16/fp16 paths the reference is the plan of the problem the path
 solves (rounded centred points, fp32 per-point cost terms; see
@@ -94,18 +89,14 @@ def test_gradient(fs, prec, d, n, m):
         moved = _plan_products(X, Y, a, b, fh, gh, eps, prec, Q_ - c, side)
         mass = _plan_products(X, Y, a, b, fh, gh, eps, prec, np.ones((Q_.shape[0], 1)), side)
         want = 2.0 * (mass * (P_ - c) - moved)
-        err = np.linalg.norm(got - want) / (2.0 * np.linalg.norm(moved))
         rel = np.linalg.norm(got - want) / np.linalg.norm(want)
-        print(f"{prec} d={d} {side}: error {err:.2e} of the transported term "
-              f"({rel:.2e} of the gradient)")
-        assert err <= 1e-3
+        print(f"{prec} d={d} {side}: relative error {rel:.2e} of the gradient")
+        assert rel <= 1e-3
     if prec in ("auto", "fp32-valu"):
         # on the fp32 paths the definition itself, summed pair by pair
         gXo, gYo = oracle.gradient(X, Y, a, b, fh, gh, eps)
-        assert np.linalg.norm(host(gX) - gXo) <= 1e-3 * 2 * np.linalg.norm(
-            _plan_products(X, Y, a, b, fh, gh, eps, prec, Y64 - mu, "row"))
-        assert np.linalg.norm(host(gY) - gYo) <= 1e-3 * 2 * np.linalg.norm(
-            _plan_products(X, Y, a, b, fh, gh, eps, prec, X64 - nu, "col"))
+        assert np.linalg.norm(host(gX) - gXo) <= 1e-3 * np.linalg.norm(gXo)
+        assert np.linalg.norm(host(gY) - gYo) <= 1e-3 * np.linalg.norm(gYo)
 
 
 def test_gradient_needs_dv_max(fs):
@@ -129,6 +120,16 @@ def test_dual_value(fs, prec, d):
     v = float(binding.fs_dual_value(p, f, g).cpu()[0])
     want = float(np.asarray(a, np.float64) @ host(f) + np.asarray(b, np.float64) @ host(g))
     assert abs(v - want) <= 1e-12 * max(1.0, abs(want))
+    # against the oracle: its dual objective after the same iterations (the
+    # exponential term vanishes after a g-update, up to the fp32 weight sums),
+    # within the potentials' bar times the total mass sum(a) + sum(b)
+    from helpers import oracle_solve
+
+    ref = oracle_solve(X, Y, a, b, eps=eps, iters=5)
+    d_ref = oracle.dual_objective(X, Y, a, b, ref["f"], ref["g"], eps)
+    bar = (1e-3 if prec == "auto" else 2e-2) * eps * 2.0
+    print(f"{prec} d={d}: dual {v:.8f} vs oracle {d_ref:.8f} ({abs(v - d_ref) / eps:.2e} eps)")
+    assert abs(v - d_ref) <= bar
 
 
 def _back(P, Pn, G):

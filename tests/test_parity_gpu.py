@@ -125,14 +125,24 @@ def test_lowp_mfma_path(fs, prec, d, n, m):
     assert max_err(host(f), rr["f"]) <= TOL_LOWP_ROUNDED * eps
     assert max_err(host(g), rr["g"]) <= TOL_LOWP_ROUNDED * eps
     if prec == "bf16" and d < 64:
-        # bf16 keeps 8 significant bits: at d = 16 on this distribution the
-        # rounding of the centred points alone moves f by about 3e-2 eps
-        # (the oracle on the path's own problem, above, is the kernel's
-        # parity check there).
+        # the original points' bar at this d: test_bf16_low_d_against_oracle
         return
     ref = oracle_solve(X, Y, a, b, eps=eps, iters=10)
     assert max_err(host(f), ref["f"]) <= TOL_LOWP * eps
     assert max_err(host(g), ref["g"]) <= TOL_LOWP * eps
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "bf16 keeps 8 significant bits: at d = 16 on the two-mixture recipe the rounding of "
+    "the centred points alone moves f by about 3e-2 eps, over the 2e-2 eps bar; the "
+    "header documents bf16 as meeting the bar from d >= 64 on this recipe (fp16 and fp32 "
+    "meet it at every d, test_lowp_mfma_path and test_fp32_mfma_path)"))
+def test_bf16_low_d_against_oracle(fs):
+    w = workloads.make("c3", n=900, m=1300, d=16)
+    _, f, g, _, _ = gpu_solve(w.X, w.Y, w.a, w.b, eps=w.eps, iters=10, prec="bf16")
+    ref = oracle_solve(w.X, w.Y, w.a, w.b, eps=w.eps, iters=10)
+    assert max_err(host(f), ref["f"]) <= TOL_LOWP * w.eps
+    assert max_err(host(g), ref["g"]) <= TOL_LOWP * w.eps
 
 
 @pytest.mark.parametrize("prec,d", [("fp16", 1024), ("bf16", 512), ("auto", 64)])
