@@ -478,6 +478,32 @@ fs_status fs_bs_shape(const fs_problem* p, int32_t side, int32_t* n_row_blocks,
 fs_status fs_bs_read_screen(fs_problem* p, int32_t side, int32_t* counts, int32_t* lists,
                             void* stream);
 
+/* ---- Allocation-free set-up + solve ------------------------------------
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): fs_potentials_init
+ * followed by fs_sinkhorn_solve, squared-Euclidean cost, no transport buffers,
+ * with the workspace in a static device array of the library instead of
+ * caller memory.  The caller passes only the inputs (X, Y, a, b) and the
+ * outputs (f, g), as for those two calls; nothing is allocated on the device
+ * or the host.
+ *
+ * The array holds FS_STATIC_SCRATCH_BYTES; a problem whose
+ * fs_workspace_bytes(n, m, d, 0, prec) exceeds it returns FS_ERR_WORKSPACE
+ * before anything is enqueued (fs_static_scratch_bytes() reports the limit).
+ * Every GPU the library is loaded on holds one such array for the lifetime
+ * of the process; all calls on one GPU share it and each leaves its contents
+ * behind, so calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller.  opts->time_kernels must be 0 (it
+ * would create HIP events).  Errors and results as for the two calls it
+ * replaces: the set-up's one synchronisation (its validity flag) and, with
+ * tol > 0, the residual checks'. */
+#define FS_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t fs_static_scratch_bytes(void);
+fs_status fs_sinkhorn_solve_static(const float* X, const float* Y, const float* a,
+                                   const float* b, int64_t n, int64_t m, int32_t d,
+                                   fs_score_prec prec, const fs_solve_opts* opts, float* f,
+                                   float* g, fs_solve_info* info, void* stream);
+
 /* Frees the host handle only (the workspace is the caller's). */
 void fs_destroy(fs_problem* p);
 

@@ -27,7 +27,8 @@ __all__ = [
     "fs_bs_attach", "fs_bs_lse_update_f", "fs_bs_lse_update_g", "fs_bs_sinkhorn_solve",
     "fs_bs_shape", "fs_bs_read_screen", "fs_centroids", "fs_lift",
     "fs_sampled_marginal_error", "fs_bs_coarse_start", "fs_bs_apply_transport",
-    "fs_bs_apply_transport_t", "fs_bs_gradient",
+    "fs_bs_apply_transport_t", "fs_bs_gradient", "fs_static_scratch_bytes",
+    "fs_sinkhorn_solve_static",
 ]
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
@@ -179,6 +180,12 @@ def load():
                                        _fp,
                                        i64, i64, i32, i32, f32, i32, _fp, i32, _fp, i32, _fp,
                                        _fp, _fp, _fp, _vp, sz, ctypes.POINTER(CoarseInfo), _vp]
+    lib.fs_static_scratch_bytes.restype = sz
+    lib.fs_static_scratch_bytes.argtypes = []
+    lib.fs_sinkhorn_solve_static.restype = ctypes.c_int
+    lib.fs_sinkhorn_solve_static.argtypes = [_fp, _fp, _fp, _fp, i64, i64, i32, ctypes.c_int,
+                                             ctypes.POINTER(SolveOpts), _fp, _fp,
+                                             ctypes.POINTER(SolveInfo), _vp]
     _LIB = lib
     return lib
 
@@ -621,6 +628,32 @@ def fs_bs_coarse_start(coarse: Problem, X, Y, a, b, cell: int, f, g, F, G, rows,
         ws.data_ptr(), need, ctypes.byref(info), _stream(stream)), "fs_bs_coarse_start")
     return {"rounds": info.rounds, "accepted": bool(info.accepted), "err_rows": info.err_rows,
             "err_cols": info.err_cols}
+
+
+def fs_static_scratch_bytes() -> int:
+    return int(load().fs_static_scratch_bytes())
+
+
+def fs_sinkhorn_solve_static(X, Y, a, b, f, g, *, eps_end: float, iters_per_stage: int,
+                             prec="auto", n_stages: int = 1, eps_start: Optional[float] = None,
+                             tol: float = 0.0, check_every: int = 10, warm_start: bool = False,
+                             stream=None, raise_not_converged: bool = True) -> dict:
+    """fs_sinkhorn_solve_static: set-up and solve with the library's static
+    device scratch as the workspace (no allocation)."""
+    n, d = X.shape
+    m = Y.shape[0]
+    opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
+                     float(eps_end), int(iters_per_stage), float(tol), int(check_every),
+                     int(bool(warm_start)), 0)
+    info = SolveInfo()
+    st = load().fs_sinkhorn_solve_static(_dev(X, "X", n * d), _dev(Y, "Y", m * d),
+                                         _dev(a, "a", n), _dev(b, "b", m), n, m, d, _prec(prec),
+                                         ctypes.byref(opts), _dev(f, "f", n), _dev(g, "g", m),
+                                         ctypes.byref(info), _stream(stream))
+    allow = () if raise_not_converged else (FS_ERR_NOT_CONVERGED,)
+    _check(st, "fs_sinkhorn_solve_static", allow)
+    return {"status": st, "iters_done": info.iters_done, "final_eps": info.final_eps,
+            "residual": info.residual}
 
 
 def solve(X, Y, a, b, *, eps: float, iters: int, prec="auto", n_stages: int = 1,

@@ -415,32 +415,16 @@ fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, 
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-size_t fs_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec) {
-    Shape sh;
-    Layout L;
-    if (plan(n, m, d, dv_max, prec, sh, L) != FS_OK) return 0;
-    return L.total;
-}
-
-fs_status fs_potentials_init(const float* X, const float* Y, const float* a, const float* b,
-                             int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec,
-                             void* workspace, size_t workspace_bytes, float* f, float* g,
-                             void* stream, fs_problem** out) {
-    return fs_potentials_init_cost(X, Y, a, b, n, m, d, dv_max, prec, FS_COST_SQEUCLIDEAN,
-                                   workspace, workspace_bytes, f, g, stream, out);
-}
-
-fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a,
-                                  const float* b, int64_t n, int64_t m, int32_t d,
-                                  int32_t dv_max, fs_score_prec prec, fs_cost cost,
-                                  void* workspace, size_t workspace_bytes, float* f, float* g,
-                                  void* stream, fs_problem** out) {
-    if (!out) return fail(FS_ERR_INVALID_ARG, "out handle pointer is NULL");
+// fs_potentials_init_cost into a problem struct the caller provides (host
+// memory it owns); on failure *p is left unusable and nothing needs freeing.
+fs_status init_problem(fs_problem* p, const float* X, const float* Y, const float* a,
+                       const float* b, int64_t n, int64_t m, int32_t d, int32_t dv_max,
+                       fs_score_prec prec, fs_cost cost, void* workspace,
+                       size_t workspace_bytes, float* f, float* g, void* stream) {
     if (cost != FS_COST_SQEUCLIDEAN && cost != FS_COST_COSINE)
         return fail(FS_ERR_INVALID_ARG, "unknown fs_cost %d", (int)cost);
-    *out = nullptr;
     if (!X || !Y || !a || !b) return fail(FS_ERR_INVALID_ARG, "X, Y, a and b must be non-NULL");
     Shape sh;
     Layout L;
@@ -455,8 +439,7 @@ fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a
     int dev = 0;
     if ((st = check_device(&dev)) != FS_OK) return st;
 
-    fs_problem* p = new (std::nothrow) fs_problem();
-    if (!p) return fail(FS_ERR_DEVICE, "host allocation failed");
+    *p = fs_problem();
     char* w = (char*)workspace;
     p->device = dev;
     p->cost = (int)cost;
@@ -531,7 +514,6 @@ fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a
             goto hip_error;
         if ((e = hipStreamSynchronize(s)) != hipSuccess) goto hip_error;
         if (flag) {
-            delete p;
             if (flag & 1) return fail(FS_ERR_NONFINITE, "X or Y holds a NaN or Inf");
             if (flag & 2) return fail(FS_ERR_NONFINITE, "a weight is <= 0, subnormal, NaN or Inf");
             if (flag & 8)
@@ -542,12 +524,50 @@ fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a
                         "(and eps by the square of the scale) or use FS_PREC_BF16");
         }
     }
-    *out = p;
     return FS_OK;
 hip_error:
-    delete p;
     return hip_fail(e, "fs_potentials_init");
 }
+
+}  // namespace
+
+extern "C" {
+
+size_t fs_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec) {
+    Shape sh;
+    Layout L;
+    if (plan(n, m, d, dv_max, prec, sh, L) != FS_OK) return 0;
+    return L.total;
+}
+
+fs_status fs_potentials_init(const float* X, const float* Y, const float* a, const float* b,
+                             int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_prec prec,
+                             void* workspace, size_t workspace_bytes, float* f, float* g,
+                             void* stream, fs_problem** out) {
+    return fs_potentials_init_cost(X, Y, a, b, n, m, d, dv_max, prec, FS_COST_SQEUCLIDEAN,
+                                   workspace, workspace_bytes, f, g, stream, out);
+}
+
+
+fs_status fs_potentials_init_cost(const float* X, const float* Y, const float* a,
+                                  const float* b, int64_t n, int64_t m, int32_t d,
+                                  int32_t dv_max, fs_score_prec prec, fs_cost cost,
+                                  void* workspace, size_t workspace_bytes, float* f, float* g,
+                                  void* stream, fs_problem** out) {
+    if (!out) return fail(FS_ERR_INVALID_ARG, "out handle pointer is NULL");
+    *out = nullptr;
+    fs_problem* p = new (std::nothrow) fs_problem();
+    if (!p) return fail(FS_ERR_DEVICE, "host allocation failed");
+    const fs_status st = init_problem(p, X, Y, a, b, n, m, d, dv_max, prec, cost, workspace,
+                                      workspace_bytes, f, g, stream);
+    if (st != FS_OK) {
+        delete p;
+        return st;
+    }
+    *out = p;
+    return FS_OK;
+}
+
 
 fs_status fs_lse_update_f(fs_problem* p, float eps, const float* g, float* f_out,
                           const float* f_cur, float* row_resid, void* stream) {
@@ -1677,3 +1697,27 @@ fs_status fs_bs_read_screen(fs_problem* p, int32_t side, int32_t* counts, int32_
 }
 
 }  // extern "C"
+
+namespace fs {
+
+fs_status report(fs_status s, const char* msg) { return fail(s, "%s", msg); }
+
+// Set-up and solve in one call, with the problem struct on this stack frame
+// and every device buffer in `workspace`: nothing is allocated, on the host
+// or the device.  The allocation-free entry point passes its static scratch
+// array here.
+fs_status solve_in_workspace(const float* X, const float* Y, const float* a, const float* b,
+                             int64_t n, int64_t m, int32_t d, fs_score_prec prec,
+                             const fs_solve_opts* opts, void* workspace, size_t workspace_bytes,
+                             float* f, float* g, fs_solve_info* info, void* stream) {
+    if (!opts) return fail(FS_ERR_INVALID_ARG, "NULL opts");
+    if (opts->time_kernels)
+        return fail(FS_ERR_INVALID_ARG, "time_kernels creates HIP events; not available here");
+    fs_problem p;
+    fs_status st = init_problem(&p, X, Y, a, b, n, m, d, 0, prec, FS_COST_SQEUCLIDEAN,
+                                workspace, workspace_bytes, f, g, stream);
+    if (st != FS_OK) return st;
+    return fs_sinkhorn_solve(&p, opts, f, g, info, stream);
+}
+
+}  // namespace fs

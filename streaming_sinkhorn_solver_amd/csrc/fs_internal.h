@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fs_sinkhorn.h"
+
 namespace fs {
 
 // Score path of a problem.
@@ -301,5 +303,16 @@ bool transport_streams(int path, int dp);
 hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratch,
                             void* Vt_buf, int64_t m_pad, float* key_bias_buf, float* part_buf,
                             hipStream_t s);
+
+// Sets the thread's fs_last_error() message and returns s.
+fs_status report(fs_status s, const char* msg);
+
+// Set-up and alternating solve in one call with every device buffer in
+// `workspace` and the problem struct on the stack (fs_api.cpp): the body of
+// the allocation-free entry point, which passes its static scratch array.
+fs_status solve_in_workspace(const float* X, const float* Y, const float* a, const float* b,
+                             int64_t n, int64_t m, int32_t d, fs_score_prec prec,
+                             const fs_solve_opts* opts, void* workspace, size_t workspace_bytes,
+                             float* f, float* g, fs_solve_info* info, void* stream);
 
 }  // namespace fs
