@@ -46,7 +46,7 @@ struct fs_problem {
     float* pot_tmp;   // max(n, m) floats
     void* vt;         // f16 [dv_max][m_pad] (matrix paths with dv_max > 0)
     float* kbias;     // [m_pad] key biases of the streaming transport kernel
-    float* lbias;     // [max(n_pad, m_pad)] key seeds of the 1024-wide LSE kernel
+    float* lbias;     // [max(n_pad, m_pad) + 256] key seeds of the matrix-core LSE kernels
     float* upart;     // [kTransportMaxSplit][n][dv_max] its partial products
     float* krec;      // small-d matrix path: key records of one pass (fp32)
     void* krec16;     //   fp16-split records (d <= 4)
@@ -244,7 +244,9 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.kguard = take(small ? 32 : 0);  // packing guard [2], cloud L1 maxima [2]
     L.rsx = take(sizeof(float) * n);  // cosine cost: 1/|x_i|
     L.rsy = take(sizeof(float) * m);
-    L.lbias = take(lse_wide(sh.path, sh.lse_dp) ? sizeof(float) * kmax : 0);
+    // key seeds of the matrix-core LSE kernels, plus one 256-key slice of
+    // padding for the copy of a split's seeds to LDS
+    L.lbias = take(!small_d_path(sh.path) ? sizeof(float) * (kmax + 256) : 0);
     L.total = o;
     return L;
 }
@@ -472,7 +474,7 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
         p->kbias = streams ? (float*)(w + L.kbias) : nullptr;
         p->upart = streams ? (float*)(w + L.upart) : nullptr;
     }
-    p->lbias = lse_wide(sh.path, sh.lse_dp) ? (float*)(w + L.lbias) : nullptr;
+    p->lbias = !small_d_path(sh.path) ? (float*)(w + L.lbias) : nullptr;
     p->krec = sh.path == PATH_SMALL ? (float*)(w + L.krec) : nullptr;
     p->krec16 = sh.path == PATH_SMALL ? (void*)(w + L.krec16) : nullptr;
     p->kguard = sh.path == PATH_SMALL ? (void*)(w + L.kguard) : nullptr;

@@ -170,9 +170,10 @@ __device__ __forceinline__ f32x16 mfma_step(const TA& av, const TB& bv, f32x16 a
 constexpr int kLdsBytes = 163840;
 constexpr int nbuf_for(int ng) { return ng >= 64 ? 2 : 4; }
 constexpr int tile_bytes_for(int ng) { return kKeyTile * 2 * ng * 16; }
+// (a whole number of 256-key slices, the granule of the biases' copy to LDS)
 constexpr int kps_max_for(int ng) {
-    return ((kLdsBytes - nbuf_for(ng) * tile_bytes_for(ng) - 2048) / 4 / kKeyTile * kKeyTile) < 16384
-               ? (kLdsBytes - nbuf_for(ng) * tile_bytes_for(ng) - 2048) / 4 / kKeyTile * kKeyTile
+    return ((kLdsBytes - nbuf_for(ng) * tile_bytes_for(ng) - 2048) / 4 / 256 * 256) < 16384
+               ? (kLdsBytes - nbuf_for(ng) * tile_bytes_for(ng) - 2048) / 4 / 256 * 256
                : 16384;
 }
 
@@ -202,7 +203,6 @@ constexpr int kps_max_for(int ng) {
 // m*CPR + (c ^ (m & SWZ))) so that one operand fetch hits distinct banks.
 template <int OP, int NG, int QB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
-    constexpr int NT = WAVES * 64;
     constexpr int CPR = 2 * NG;                      // 16-byte chunks per row
     constexpr int ROW_BYTES = CPR * 16;
     constexpr int TILE_CHUNKS = kKeyTile * CPR;      // chunks per key tile (>= 64)
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 
     constexpr int TILE_BYTES = TILE_CHUNKS * 16;
     __shared__ __attribute__((aligned(16))) uint4 kbuf[NBUF * TILE_CHUNKS];
-    __shared__ __attribute__((aligned(16))) float bkeys[KPS_MAX];
+    __shared__ __attribute__((aligned(16))) float bkeys[KPS_MAX];  // KPS_MAX: whole 1 KiB slices
     __shared__ float red[16];
 
     const int tid = threadIdx.x;
@@ -275,38 +275,42 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
         return kbuf + i * TILE_CHUNKS;
     };
 
-    // prologue: tiles 0..NBUF-2 in flight (every split holds at least one
-    // key; the guard keeps an empty range from reading before it), the key
-    // biases of the whole range, the resident row block
-    if (ntiles > 0 && (!LAG_DMA || dwave >= 0)) {
-#pragma unroll
-        for (int k = 0; k < NBUF - 1; ++k) issue_tile(min(k, ntiles - 1), buf(k));
-    }
-    // Key bias in dot-product units: the base-2 score of a pair is
-    // c_score * (x~.y~ + bk) with bk = (g - |y~|^2)/2 + log2(b)/(2 c_bias)
-    // (c_score = 2 c_bias exactly), so bk can seed the accumulator.
-    const float half_inv_cb = 0.5f / a.c_bias;
-    for (int k = tid; k < ntiles * kKeyTile; k += NT) {
-        const int j = j0 + k;
-        bkeys[k] = j < j1 ? fmaf(a.key_lw2[j], half_inv_cb, 0.5f * (a.key_pot[j] - a.key_nrm[j]))
-                          : -INFINITY;
-    }
+    // Prologue: the resident row block, tiles 0..NBUF-2 (every split holds
+    // at least one key; the guard keeps an empty range from reading before
+    // it) and the key biases of the whole range, all in flight at once and
+    // waited for together.  The biases come from a_kbias, written once per
+    // pass by key_seed_kernel in dot-product units: the base-2 score of a pair
+    // is c_score * (x~.y~ + bk) with bk = (g - |y~|^2)/2 + log2(b)/(2 c_bias)
+    // (c_score = 2 c_bias exactly), so bk can seed the accumulator.  They are
+    // copied in 1 KiB slices (256 keys) straight into LDS; the seed array is
+    // padded so that the last slice stays inside it.
     // lane (ln, h) holds chunk 2g+h of row row0+qb*32+ln.  With one wave
     // per SIMD and a block of more than 128 registers it is placed in the
     // accumulation registers (AGPRs), which the matrix instructions read
     // directly, leaving the vector registers to the accumulators, operand
     // ring and epilogue.
     constexpr bool Q_AGPR = WAVES == 4 && QB * NG * 4 > 128;
+    auto issue_prologue_dma = [&]() __attribute__((always_inline)) {
+        if (ntiles > 0 && (!LAG_DMA || dwave >= 0)) {
+#pragma unroll
+            for (int k = 0; k < NBUF - 1; ++k) issue_tile(min(k, ntiles - 1), buf(k));
+        }
+        const int slices = (ntiles * kKeyTile + 255) / 256;
+        const char* kb = (const char*)(a.kbias + j0);
+        for (int c = wave; c < slices; c += WAVES) dma_to_lds16(kb + c * 1024, lane16, bkeys + c * 256);
+    };
     u32x4 q[QB][NG];
     {
         const char* __restrict__ rows = (const char*)a.rows;
-        // Either way the block is consumed here, so that the compiler's own
-        // waits for these loads are placed in the prologue: left to their
-        // first use inside the tile loop they would be re-executed every
-        // tile, and there they would also wait for the tile loads in flight.
-        // Loads go out in batches of QLB before the first of them is
-        // consumed (staged in vector registers on the way to the AGPRs).
+        // Either way the block is consumed in the prologue, so that the
+        // compiler's own waits for these loads are placed there: left to
+        // their first use inside the tile loop they would be re-executed
+        // every tile, and there they would also wait for the tile loads in
+        // flight.  Vector-register blocks: all loads, then the copies, then
+        // one wait for everything.  AGPR blocks: the copies first, then the
+        // loads in batches of QLB staged in vector registers on the way.
         constexpr int QLB = Q_AGPR ? 8 : NG;
+        if constexpr (Q_AGPR) issue_prologue_dma();
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const char* rp = rows + (int64_t)(row0 + qb * 32 + ln) * ROW_BYTES + h * 16;
@@ -319,14 +323,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
 #pragma unroll
                 for (int u = 0; u < QLB; ++u) {
                     if (g0 + u >= NG) continue;
-                    if constexpr (Q_AGPR) {
+                    if constexpr (Q_AGPR)
                         asm volatile("" : "=a"(q[qb][g0 + u]) : "0"(v[u]));
-                    } else {
+                    else
                         q[qb][g0 + u] = v[u];
-                        asm volatile("" ::"v"(q[qb][g0 + u]));
-                    }
                 }
             }
+        }
+        if constexpr (!Q_AGPR) {
+            issue_prologue_dma();
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) asm volatile("" ::"v"(q[qb][g]));
         }
     }
 
@@ -1047,8 +1057,9 @@ hipError_t launch_lse(int path, const LseArgs& a, hipStream_t s, hipEvent_t ev_b
                       hipEvent_t ev_end) {
     hipError_t e;
     const bool wide = lse_wide(path, a.dp);
-    if (wide) {
-        // the key seeds go first, outside the kernel's timed bracket
+    if (!small_d_path(path)) {
+        // the key seeds of the matrix-core kernels go first, outside the
+        // kernel's timed bracket
         if (!a.kbias || a.kbias_keys < (a.n_keys + kKeyTile - 1) / kKeyTile * kKeyTile)
             return hipErrorInvalidValue;
         key_seed_kernel<<<(a.kbias_keys + 255) / 256, 256, 0, s>>>(a);

@@ -4,8 +4,12 @@
     python -m streaming_sinkhorn_solver_amd.profiling traffic FETCH_DB WRITE_DB OUT.json \
         --copy-bytes B --kernel lse_mfma_kernel --source fs_lse.hip \
         --command-fetch "..." --command-write "..."
+    python -m streaming_sinkhorn_solver_amd.profiling counters OUT.md --db P1 --db P2 \
+        --kernel lse_mfma_kernel --command "..." --command "..."
 
 `stats` tabulates kernel-trace durations (calls, mean, min, max, share).
+`counters` tabulates the mean per dispatch of every counter of one kernel over
+several counter passes, with the clock and matrix-pipe share derived from them.
 `traffic` turns the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of one
 kernel into HBM bytes per launch, each scaled by the factor that makes the
 same counter read exactly the known size of a plain copy in the same run
@@ -100,6 +104,72 @@ def write_traffic(fetch_db: str, write_db: str, out_json: str, copy_bytes: float
     return rec
 
 
+def kernel_durations(db: str, name_substr: str):
+    """Durations (ns) of the dispatches of matching kernels, by dispatch id
+    (empty if the database holds no kernel trace)."""
+    con = sqlite3.connect(db)
+    try:
+        rows = con.execute("select name, dispatch_id, duration from kernels").fetchall()
+    except sqlite3.Error:
+        return {}
+    return {did: dur for name, did, dur in rows if name_substr in name}
+
+
+def write_counters_md(dbs, out_md: str, kernel: str, commands, n_cu: int = 256,
+                      n_xcd: int = 8) -> dict:
+    """Mean per dispatch of every counter of the matching kernel over the
+    given databases (one per counter pass), with the graphics clock
+    (GRBM_GUI_ACTIVE of one XCD over the traced duration) and the matrix-pipe
+    busy share (SQ_VALU_MFMA_BUSY_CYCLES over the active cycles x CUs x 4
+    SIMDs)."""
+    vals, durs = {}, []
+    for db in dbs:
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, dispatch_id, counter_name, value "
+                           "from counters_collection").fetchall()
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        for kn, did, cn, v in rows:
+            if kernel in kn:
+                per[cn][did] += v
+        d = kernel_durations(db, kernel)
+        for cn, by in per.items():
+            vals[cn] = sum(by.values()) / len(by)
+            if "GRBM_GUI_ACTIVE" == cn and d:
+                clk = [by[k] / d[k] for k in by if k in d and d[k] > 0]
+                vals.setdefault("_clock_ghz", [])
+                vals["_clock_ghz"] += clk
+        durs += list(d.values())
+    derived = {}
+    # GRBM_GUI_ACTIVE is returned per XCD (8 on MI355X) and summed here
+    if vals.get("_clock_ghz"):
+        derived["graphics clock over the kernel (GHz)"] = (
+            sum(vals["_clock_ghz"]) / len(vals["_clock_ghz"]) / n_xcd)
+    vals.pop("_clock_ghz", None)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
+        active = vals["GRBM_GUI_ACTIVE"] / n_xcd
+        derived["matrix pipe busy share (per SIMD)"] = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (
+            active * n_cu * 4)
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals:
+            derived["matrix and vector issue overlapping (share of cycles, per SIMD)"] = (
+                vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / (active * n_cu * 4))
+    if durs:
+        derived["mean traced duration (us)"] = sum(durs) / len(durs) / 1e3
+    lines = [f"# Hardware counters: {os.path.basename(out_md)}", "",
+             f"Kernel: `{kernel}` (mean per dispatch; counters summed over their instances).",
+             "", "Commands (run from the repository root on one MI355X):", ""]
+    for c in commands:
+        lines += ["```", c, "```", ""]
+    lines += ["| counter | mean per dispatch |", "|---|---:|"]
+    for k in sorted(vals):
+        lines.append(f"| `{k}` | {vals[k]:.6g} |")
+    lines += ["", "| derived | value |", "|---|---:|"]
+    for k, v in derived.items():
+        lines.append(f"| {k} | {v:.4g} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return {"counters": vals, "derived": derived}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -117,7 +187,15 @@ def main(argv=None):
     s2.add_argument("--source", default="fs_lse.hip", help="kernel source file under csrc/")
     s2.add_argument("--command-fetch", required=True)
     s2.add_argument("--command-write", required=True)
+    s3 = sub.add_parser("counters")
+    s3.add_argument("out")
+    s3.add_argument("--db", action="append", required=True)
+    s3.add_argument("--kernel", default="lse_mfma_kernel")
+    s3.add_argument("--command", action="append", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        print(json.dumps(write_counters_md(a.db, a.out, a.kernel, a.command), indent=1))
+        return 0
     if a.cmd == "stats":
         write_stats_md(a.db, a.out, a.command)
         print(a.out)

@@ -37,7 +37,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 # recipe -> (score precision, expected path, potential bar in eps)
 RECIPES = {
     "c2": ("fp32", "fp32-mfma", 1e-3),
-    "c3": ("bf16", "bf16-mfma", 2e-2),
+    "c3": ("fp16", "fp16-mfma", 2e-2),
     "c4": ("fp16", "fp16-mfma", 2e-2),
     "c5": ("auto", "fp32-small-mfma", 1e-3),
 }
@@ -109,3 +109,52 @@ def test_full_schedule_against_oracle(fs, name):
         assert rel <= 1e-3
     if "residual" in ref:
         assert abs(r_gpu - r_ref) <= 2e-2 * r_ref + 4e-6
+
+
+def test_c3_bf16_potentials(fs):
+    """The 50k x 50k x 512 recipe in bf16 over its 100 iterations: potentials
+    within the 2e-2 eps bar of the oracle (measured 3.2e-3 eps)."""
+    ref, _ = _golden("c3")
+    f, g, _ = _run_c3_bf16()
+    w = workloads.make("c3")
+    ef = float(np.max(np.abs(f - ref["f"]))) / w.eps
+    eg = float(np.max(np.abs(g - ref["g"]))) / w.eps
+    print(f"c3 bf16: max|f - f_ref| = {ef:.3e} eps, max|g - g_ref| = {eg:.3e} eps")
+    assert ef <= 2e-2 and eg <= 2e-2
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "bf16 operands keep 8 significant bits: after the 100 iterations of the 50k x 50k x "
+    "512 recipe the potentials sit about 3e-3 eps from the float64 iteration, which moves "
+    "the barycentric projection P.Y/a by about 1.2e-3 relative (Frobenius over the 512 "
+    "stored rows), just over the 1e-3 bar; the recipe runs in fp16 (same matrix-core "
+    "rate; 1.6e-4 measured)"))
+def test_c3_bf16_transport(fs):
+    ref, _ = _golden("c3")
+    _, _, U = _run_c3_bf16()
+    rows = ref["rows"]
+    rel = float(np.linalg.norm(U[rows] - ref["U_rows"]) / np.linalg.norm(ref["U_rows"]))
+    print(f"c3 bf16 transport rel {rel:.3e}")
+    assert rel <= 1e-3
+
+
+_C3_BF16 = {}
+
+
+def _run_c3_bf16():
+    import torch
+
+    from streaming_sinkhorn_solver_amd import binding
+
+    if "out" not in _C3_BF16:
+        w = workloads.make("c3")
+        X, Y, a, b, V = dev(w.X), dev(w.Y), dev(w.a), dev(w.b), dev(w.V)
+        f = torch.empty(w.n, device="cuda")
+        g = torch.empty(w.m, device="cuda")
+        p = binding.fs_potentials_init(X, Y, a, b, dv_max=w.d, prec="bf16", f=f, g=g)
+        binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, iters_per_stage=w.iters)
+        U = torch.empty((w.n, w.d), device="cuda")
+        binding.fs_apply_transport(p, w.eps, f, g, V, U, divide_by_a=True)
+        torch.cuda.synchronize()
+        _C3_BF16["out"] = (host(f), host(g), host(U))
+    return _C3_BF16["out"]

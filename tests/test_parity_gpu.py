@@ -100,7 +100,7 @@ def test_small_d_tiny_sides(fs, prec, path, n, m):
 
 
 @pytest.mark.parametrize("d,n,m", [(9, 700, 1100), (16, 1500, 900), (64, 2100, 1700),
-                                   (100, 600, 1300), (256, 640, 500)])
+                                   (100, 600, 1300), (256, 640, 500), (400, 900, 1300)])
 def test_fp32_mfma_path(fs, d, n, m):
     X, Y, a, b = _problem(200 + d, n, m, d, scale=1.0 / np.sqrt(d))
     eps = 0.05
