@@ -67,7 +67,7 @@ CSRC = os.path.join(HERE, "streaming_sinkhorn_solver_amd", "csrc")
 EXP_PEAK = 256 * 32 * 2.4e9 / 1e12  # T exponentials/s
 
 # recipe -> the fs_probe_peak kind of its bounding unit
-PROBES = {"c1": "exp", "c2": "mfma-fp32", "c3": "mfma-fp16", "c4": "mfma-fp16", "c5": "exp",
+PROBES = {"c1": "exp", "c2": "mfma-fp32", "c3": "mfma-bf16", "c4": "mfma-fp16", "c5": "exp",
           "fs2": "exp"}
 BS_DELTA = 1e-3  # skipped mass per row / column below this share of its target
 
@@ -79,10 +79,11 @@ RECIPES = {
     "c2": ("fp32", 157.3, "TFLOP/s", "f32",
            "n=m=10000, d=64, X~N(0,I/d), Y~N(mu,0.5 I/d), uniform weights, eps=0.05, "
            "200 iterations (seed 2)"),
-    "c3": ("fp16", 2500.0, "TFLOP/s", "f16",
+    "c3": ("bf16-refine", 2500.0, "TFLOP/s", "bf16 (iterations 1-99); f16 (iteration 100, P.Y/a)",
            "n=m=50000, d=512, two 10-component Gaussian mixtures, Dirichlet(1) weights, "
            "eps=0.1, 100 alternating iterations + barycentric projection P.Y/a (seed 3); "
-           "fp16 matrix-core scores (the bf16 rate on gfx950; bf16 operands miss the 1e-3 "
+           "bf16 matrix-core scores with the last iteration and the projection on fp16 "
+           "copies of the points (FS_PREC_BF16_REFINE: bf16 throughout misses the 1e-3 "
            "transport bar on this recipe)"),
     "c4": ("fp16", 2500.0, "TFLOP/s", "f16",
            "n=50000, m=30000, d=1024, X on the unit sphere, Y~N(0,I/d) with a 0.25 shift on 16 "
@@ -395,7 +396,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="c3", choices=sorted(RECIPES))
-    ap.add_argument("--prec", default=None, choices=["auto", "fp32", "bf16", "fp16", "fp32-valu"],
+    ap.add_argument("--prec", default=None,
+                    choices=["auto", "fp32", "bf16", "fp16", "fp32-valu", "bf16-refine"],
                     help="override the recipe's score precision (the line then names it)")
     ap.add_argument("--iters", type=int, default=None, help="override iterations per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -426,7 +428,9 @@ def main():
     prec, peak, unit, dtype, desc = RECIPES[wl]
     if args.prec and args.prec != prec:
         prec = args.prec
-        dtype = {"bf16": "bf16", "fp16": "f16"}.get(prec, "f32")
+        dtype = {"bf16": "bf16", "fp16": "f16",
+                 "bf16-refine": "bf16 (all but the last iteration); f16 (last iteration, "
+                                "transport)"}.get(prec, "f32")
         desc += f" [score precision overridden: {prec}]"
     w = workloads.make(wl)
     if args.counters:
@@ -557,10 +561,12 @@ def main():
     kernel = {"c1": "lse_small_kernel<2> (fp16 split scores)",
               "c5": "lse_small_kernel<2> (fp16 split scores)",
               "c2": "lse_mfma_kernel<fp32, d_pad 64>",
-              "c3": f"lse_mfma_kernel<{prec}, d_pad 512>",
+              "c3": "lse_mfma_kernel<%s, d_pad 512>" % ("bf16" if prec == "bf16-refine"
+                                                         else prec),
               "c4": "lse_wide_kernel<fp16> (1024-wide rows, contraction split over wave pairs)"}[wl]
     sink = torch.zeros(1, device=dev)
-    probe = {"bf16": "mfma-bf16", "fp16": "mfma-fp16"}.get(prec, PROBES[wl]) \
+    probe = {"bf16": "mfma-bf16", "bf16-refine": "mfma-bf16",
+             "fp16": "mfma-fp16"}.get(prec, PROBES[wl]) \
         if unit == "TFLOP/s" and prec != "fp32" else PROBES[wl]
     peak_measured = binding.fs_probe_peak(probe, sink) / 1e12
     roofline = {"bound": "mfma" if unit == "TFLOP/s" else "alu",

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "FS_OK", "FS_ERR_INVALID_ARG", "FS_ERR_WORKSPACE", "FS_ERR_DEVICE", "FS_ERR_NONFINITE",
     "FS_ERR_NOT_CONVERGED", "PREC_AUTO", "PREC_FP32", "PREC_BF16", "PREC_FP16", "PREC_FP32_VALU",
+    "PREC_BF16_REFINE",
     "FsError",
     "Problem", "load", "lib_path", "fs_workspace_bytes", "fs_potentials_init",
     "fs_lse_update_f", "fs_lse_update_g", "fs_marginal_residual", "fs_sinkhorn_solve",
@@ -33,13 +34,14 @@ __all__ = [
 
 FS_OK, FS_ERR_INVALID_ARG, FS_ERR_WORKSPACE, FS_ERR_DEVICE, FS_ERR_NONFINITE, \
     FS_ERR_NOT_CONVERGED = range(6)
-PREC_AUTO, PREC_FP32, PREC_BF16, PREC_FP16, PREC_FP32_VALU = range(5)
+PREC_AUTO, PREC_FP32, PREC_BF16, PREC_FP16, PREC_FP32_VALU, PREC_BF16_REFINE = range(6)
 _PREC_NAMES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16, "fp16": PREC_FP16,
-               "fp32-valu": PREC_FP32_VALU}
+               "fp32-valu": PREC_FP32_VALU, "bf16-refine": PREC_BF16_REFINE}
 COST_SQEUCLIDEAN, COST_COSINE = 0, 1
 _COST_NAMES = {"sqeuclidean": COST_SQEUCLIDEAN, "cosine": COST_COSINE}
 PROBE_KINDS = {"mfma-bf16": 1, "mfma-fp16": 2, "mfma-fp32": 3, "exp": 4}
-PATH_NAMES = {0: "fp32-valu", 1: "fp32-mfma", 2: "bf16-mfma", 3: "fp16-mfma", 4: "fp32-small-mfma"}
+PATH_NAMES = {0: "fp32-valu", 1: "fp32-mfma", 2: "bf16-mfma", 3: "fp16-mfma", 4: "fp32-small-mfma",
+              5: "bf16-mfma-fp16-refine"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

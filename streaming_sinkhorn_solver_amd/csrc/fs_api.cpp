@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "fs_internal.h"
@@ -28,6 +29,13 @@ struct fs_problem {
     int device;
     int cost;  // fs_cost
     int path;
+    // FS_PREC_BF16_REFINE: the fp16 copies of the operands and their path;
+    // RefineScope exchanges them with X.ops, Y.ops and path while a pass
+    // that is to run in fp16 is enqueued
+    bool refine = false;
+    void* xops16 = nullptr;
+    void* yops16 = nullptr;
+    int path16 = -1;
     int64_t n, m;
     int d;       // true dimension
     int dp;      // operand row stride in elements
@@ -109,6 +117,7 @@ struct Shape {
     int lse_dp = 0;  // launcher dp
     size_t es = 4;   // element size
     int f_split = 1, f_kps = 0, g_split = 1, g_kps = 0;
+    bool refine = false;  // FS_PREC_BF16_REFINE: an fp16 copy of the operands too
 };
 
 // Returns FS_OK and fills sh, or an error.
@@ -148,9 +157,16 @@ fs_status choose_path(int64_t n, int64_t m, int32_t d, int32_t dv_max, fs_score_
                             d);
             }
             break;
+        case FS_PREC_BF16_REFINE:
+            if (d <= 8)
+                return fail(FS_ERR_INVALID_ARG,
+                            "FS_PREC_BF16_REFINE needs d > 8 (got %d): the d <= 8 paths score "
+                            "in fp32", d);
+            sh.refine = true;
+            [[fallthrough]];
         case FS_PREC_BF16:
         case FS_PREC_FP16:
-            sh.path = prec == FS_PREC_BF16 ? PATH_MFMA_BF16 : PATH_MFMA_F16;
+            sh.path = prec == FS_PREC_FP16 ? PATH_MFMA_F16 : PATH_MFMA_BF16;
             sh.dp = 16 * next_pow2((d + 15) / 16);
             sh.lse_dp = sh.dp;
             sh.es = 2;
@@ -197,7 +213,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 }
 
 struct Layout {
-    size_t centre, bmin, bmax, flag, xops, yops, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
+    size_t centre, bmin, bmax, flag, xops, yops, xops16, yops16, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
         vt, kbias, upart, krec, krec16, kguard, rsx, rsy, lbias, total;
 };
 
@@ -216,6 +232,8 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.flag = take(sizeof(int) * 4);
     L.xops = take(sh.es * (size_t)np * sh.dp);
     L.yops = take(sh.es * (size_t)mp * sh.dp);
+    L.xops16 = take(sh.refine ? sh.es * (size_t)np * sh.dp : 0);
+    L.yops16 = take(sh.refine ? sh.es * (size_t)mp * sh.dp : 0);
     L.xn = take(sizeof(float) * n);
     L.xl = take(sizeof(float) * n);
     L.xw = take(sizeof(float) * n);
@@ -284,6 +302,26 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const char* y = (const char*)b;
     return x < y + nb && y < x + na;
 }
+
+// While alive (and `on`), passes enqueued on p use the fp16 copies of a
+// FS_PREC_BF16_REFINE problem: its operands and path are exchanged with the
+// fp16 ones and put back at the end of the scope.  (Handles are not
+// thread-safe, and every pass reads these fields when it is enqueued.)
+struct RefineScope {
+    fs_problem* p;
+    bool active;
+    RefineScope(fs_problem* p_, bool on = true) : p(p_), active(on && p_ && p_->refine) {
+        if (active) swap();
+    }
+    ~RefineScope() {
+        if (active) swap();
+    }
+    void swap() {
+        std::swap(p->X.ops, p->xops16);
+        std::swap(p->Y.ops, p->yops16);
+        std::swap(p->path, p->path16);
+    }
+};
 
 LseArgs base_args(const fs_problem* p, bool f_side, float eps) {
     LseArgs a{};
@@ -446,6 +484,12 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
     p->device = dev;
     p->cost = (int)cost;
     p->path = sh.path;
+    p->refine = sh.refine;
+    if (sh.refine) {
+        p->xops16 = w + L.xops16;
+        p->yops16 = w + L.yops16;
+        p->path16 = PATH_MFMA_F16;
+    }
     p->n = n;
     p->m = m;
     p->d = d;
@@ -502,6 +546,13 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
         goto hip_error;
     if ((e = launch_convert(Y, p->Y.rscale, m, p->Y.n_pad, d, p->dp, p->path, p->centre + d,
                             p->centre, p->Y.ops, p->Y.nrm, p->flag, s)) != hipSuccess)
+        goto hip_error;
+    // the fp16 copies (the cost terms are written again, with the same values)
+    if (p->refine &&
+        ((e = launch_convert(X, p->X.rscale, n, p->X.n_pad, d, p->dp, p->path16, p->centre,
+                             p->centre + d, p->xops16, p->X.nrm, p->flag, s)) != hipSuccess ||
+         (e = launch_convert(Y, p->Y.rscale, m, p->Y.n_pad, d, p->dp, p->path16, p->centre + d,
+                             p->centre, p->yops16, p->Y.nrm, p->flag, s)) != hipSuccess))
         goto hip_error;
     if (p->path == PATH_SMALL &&
         ((e = launch_row_l1max((const float*)p->X.ops, n, d, p->X.l1max, s)) != hipSuccess ||
@@ -601,6 +652,7 @@ fs_status fs_marginal_residual(fs_problem* p, float eps, const float* f, const f
                                float* out2, void* stream) {
     if (!p || !f || !g || !out2) return fail(FS_ERR_INVALID_ARG, "NULL argument");
     if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    RefineScope fp16_passes(p);
     hipStream_t s = (hipStream_t)stream;
     fs_status st = half_step(p, true, eps, g, p->pot_tmp, f, out2, 0, s);
     if (st != FS_OK) return st;
@@ -662,6 +714,10 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
                                    (double)st_i / (double)(o->n_stages - 1)));
         if (have_next_f) have_next_f = false;  // new stage: eps changed
         for (int it = 0; it < o->iters_per_stage; ++it) {
+            // the last iteration of a fixed-count schedule runs on the fp16
+            // copies of a FS_PREC_BF16_REFINE problem
+            RefineScope last(p, !use_tol && st_i == o->n_stages - 1 &&
+                                    it == o->iters_per_stage - 1);
             if (have_next_f) {
                 if ((e = hipMemcpyAsync(f, p->pot_tmp, sizeof(float) * p->n,
                                         hipMemcpyDeviceToDevice, s)) != hipSuccess)
@@ -688,6 +744,15 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
         bool dummy = false;
         if ((st = check(eps, dummy)) != FS_OK) return st;
         converged = resid <= o->tol;
+    }
+    if (use_tol && p->refine) {
+        // FS_PREC_BF16_REFINE with a residual stop: the checks measure the
+        // bf16 iteration itself; one iteration on the fp16 copies follows
+        // the stop
+        RefineScope fp16_passes(p);
+        if ((st = half_step(p, true, eps, g, f, nullptr, nullptr, 0, s, tp)) != FS_OK) return st;
+        if ((st = half_step(p, false, eps, f, g, nullptr, nullptr, 0, s, tp)) != FS_OK) return st;
+        ++done;
     }
     float lse_ms = 0.f;
     int lse_n = 0;
@@ -717,6 +782,7 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
 fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const float* g,
                              const float* V, int32_t dv, float* U, int32_t divide_by_a,
                              void* stream) {
+    RefineScope fp16_passes(p);
     return transport_side(p, true, eps, f, g, V, dv, U, divide_by_a, nullptr, nullptr,
                           (hipStream_t)stream);
 }
@@ -724,6 +790,7 @@ fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const flo
 fs_status fs_apply_transport_t(fs_problem* p, float eps, const float* f, const float* g,
                                const float* W, int32_t dv, float* U, int32_t divide_by_b,
                                void* stream) {
+    RefineScope fp16_passes(p);
     return transport_side(p, false, eps, f, g, W, dv, U, divide_by_b, nullptr, nullptr,
                           (hipStream_t)stream);
 }
@@ -731,6 +798,7 @@ fs_status fs_apply_transport_t(fs_problem* p, float eps, const float* f, const f
 fs_status fs_gradient(fs_problem* p, float eps, const float* f, const float* g, const float* X,
                       const float* Y, float* grad_x, float* grad_y, void* stream) {
     if (!p || !f || !g || !X || !Y) return fail(FS_ERR_INVALID_ARG, "NULL argument");
+    RefineScope fp16_passes(p);
     if (p->dv_max < p->d)
         return fail(FS_ERR_INVALID_ARG,
                     "the gradient needs dv_max >= d at init (dv_max=%d, d=%d)", p->dv_max, p->d);
@@ -852,6 +920,7 @@ fs_status fs_hvp(fs_problem* p, float eps, const float* f, const float* g, const
                  const float* Y, int32_t wrt, const float* V, float* HV, float cg_tol,
                  int32_t cg_max_iter, void* workspace, size_t workspace_bytes, fs_hvp_info* info,
                  void* stream) {
+    RefineScope fp16_passes(p);
     if (!p || !f || !g || !X || !Y || !V || !HV || !workspace)
         return fail(FS_ERR_INVALID_ARG, "NULL argument");
     if (wrt != 0 && wrt != 1) return fail(FS_ERR_INVALID_ARG, "wrt must be 0 (X) or 1 (Y)");
@@ -1047,7 +1116,7 @@ fs_status fs_probe_peak(fs_probe_kind kind, float* sink, int32_t reps, void* str
 fs_status fs_problem_info(const fs_problem* p, int32_t* path, int32_t* d_pad, int32_t* f_splits,
                           int32_t* g_splits) {
     if (!p) return fail(FS_ERR_INVALID_ARG, "NULL handle");
-    if (path) *path = p->path;
+    if (path) *path = p->refine ? 5 : p->path;
     if (d_pad) *d_pad = p->dp;
     if (f_splits) *f_splits = p->f_split;
     if (g_splits) *g_splits = p->g_split;

@@ -37,7 +37,8 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 # recipe -> (score precision, expected path, potential bar in eps)
 RECIPES = {
     "c2": ("fp32", "fp32-mfma", 1e-3),
-    "c3": ("fp16", "fp16-mfma", 2e-2),
+    "c3": ("bf16-refine", "bf16-mfma-fp16-refine", 2e-2),
+    "c3-fp16": ("fp16", "fp16-mfma", 2e-2),
     "c4": ("fp16", "fp16-mfma", 2e-2),
     "c5": ("auto", "fp32-small-mfma", 1e-3),
 }
@@ -60,8 +61,9 @@ def test_full_schedule_against_oracle(fs, name):
 
     from streaming_sinkhorn_solver_amd import binding
 
-    ref, meta = _golden(name)
     prec, path, bar = RECIPES[name]
+    name = name.split("-")[0]
+    ref, meta = _golden(name)
     w = workloads.make(name)
     assert (meta["n"], meta["m"], meta["d"], meta["iterations"]) == \
         (w.n, w.m, w.d, w.iters * w.n_stages)
@@ -127,8 +129,8 @@ def test_c3_bf16_potentials(fs):
     "bf16 operands keep 8 significant bits: after the 100 iterations of the 50k x 50k x "
     "512 recipe the potentials sit about 3e-3 eps from the float64 iteration, which moves "
     "the barycentric projection P.Y/a by about 1.2e-3 relative (Frobenius over the 512 "
-    "stored rows), just over the 1e-3 bar; the recipe runs in fp16 (same matrix-core "
-    "rate; 1.6e-4 measured)"))
+    "stored rows), just over the 1e-3 bar; the recipe runs with its last iteration and "
+    "the projection on fp16 copies (FS_PREC_BF16_REFINE: 1.6e-4 measured)"))
 def test_c3_bf16_transport(fs):
     ref, _ = _golden("c3")
     _, _, U = _run_c3_bf16()
