@@ -55,7 +55,8 @@ class SolveOpts(ctypes.Structure):
     _fields_ = [("n_stages", ctypes.c_int32), ("eps_start", ctypes.c_float),
                 ("eps_end", ctypes.c_float), ("iters_per_stage", ctypes.c_int32),
                 ("tol", ctypes.c_float), ("check_every", ctypes.c_int32),
-                ("warm_start", ctypes.c_int32), ("time_kernels", ctypes.c_int32)]
+                ("warm_start", ctypes.c_int32), ("time_kernels", ctypes.c_int32),
+                ("single_launch", ctypes.c_int32)]
 
 
 class SolveInfo(ctypes.Structure):
@@ -313,10 +314,11 @@ def fs_marginal_residual(p: Problem, eps: float, f, g, out2, stream=None):
 def fs_sinkhorn_solve(p: Problem, f, g, *, eps_end: float, iters_per_stage: int,
                       n_stages: int = 1, eps_start: Optional[float] = None, tol: float = 0.0,
                       check_every: int = 10, warm_start: bool = False, stream=None,
-                      raise_not_converged: bool = True, time_kernels: bool = False) -> dict:
+                      raise_not_converged: bool = True, time_kernels: bool = False,
+                      single_launch: int = 0) -> dict:
     opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
                      float(eps_end), int(iters_per_stage), float(tol), int(check_every),
-                     int(bool(warm_start)), int(bool(time_kernels)))
+                     int(bool(warm_start)), int(bool(time_kernels)), int(single_launch))
     info = SolveInfo()
     st = load().fs_sinkhorn_solve(p.handle, ctypes.byref(opts), _dev(f, "f", p.n),
                                   _dev(g, "g", p.m), ctypes.byref(info), _stream(stream))
@@ -646,7 +648,7 @@ def fs_sinkhorn_solve_static(X, Y, a, b, f, g, *, eps_end: float, iters_per_stag
     m = Y.shape[0]
     opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
                      float(eps_end), int(iters_per_stage), float(tol), int(check_every),
-                     int(bool(warm_start)), 0)
+                     int(bool(warm_start)), 0, 0)
     info = SolveInfo()
     st = load().fs_sinkhorn_solve_static(_dev(X, "X", n * d), _dev(Y, "Y", m * d),
                                          _dev(a, "a", n), _dev(b, "b", m), n, m, d, _prec(prec),

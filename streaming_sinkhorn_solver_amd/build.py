@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfs_sinkhorn.so")
 SOURCES = ["fs_api.cpp", "fs_prep.hip", "fs_lse.hip", "fs_lse_small.hip", "fs_transport.hip",
-           "fs_grad.hip", "fs_probe.hip", "fs_hvp.hip", "fs_bsparse.hip", "fs_static.hip"]
+           "fs_grad.hip", "fs_probe.hip", "fs_hvp.hip", "fs_bsparse.hip", "fs_static.hip",
+           "fs_persistent.hip"]
 ARCH = "gfx950"
 
 

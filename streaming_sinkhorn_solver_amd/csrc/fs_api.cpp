@@ -683,6 +683,61 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
         if ((e = launch_fill(f, p->n, 0.f, s)) != hipSuccess) return hip_fail(e, "fill f");
     }
     const bool use_tol = o->tol > 0.f;
+    // the whole schedule as one launch (small d <= 8 problems, fixed count)
+    const bool sl_allowed = !use_tol && small_d_path(p->path) && !p->refine &&
+                            o->n_stages <= kPersistentMaxStages && o->iters_per_stage > 0 &&
+                            p->n <= persistent_max_points(p->d) &&
+                            p->m <= persistent_max_points(p->d);
+    if (sl_allowed && (o->single_launch == 1 ||
+                       (o->single_launch == 0 && p->n * p->m <= ((int64_t)1 << 19)))) {
+        PersistentArgs pa{};
+        pa.X = (const float*)p->X.ops;
+        pa.Y = (const float*)p->Y.ops;
+        pa.xn = p->X.nrm;
+        pa.yn = p->Y.nrm;
+        pa.xl = p->X.lw2;
+        pa.yl = p->Y.lw2;
+        pa.f = f;
+        pa.g = g;
+        pa.n = (int)p->n;
+        pa.m = (int)p->m;
+        pa.d = p->d;
+        pa.stride = p->dp;
+        pa.W = persistent_workgroups(p->n, p->m);
+        pa.rec_cap = (int)std::max(p->n, p->m);
+        pa.n_stages = o->n_stages;
+        pa.iters = o->iters_per_stage;
+        for (int st_i = 0; st_i < o->n_stages; ++st_i)
+            pa.eps[st_i] = o->n_stages == 1
+                               ? o->eps_end
+                               : (float)((double)o->eps_start *
+                                         std::pow((double)o->eps_end / (double)o->eps_start,
+                                                  (double)st_i / (double)(o->n_stages - 1)));
+        pa.counter = (unsigned*)(p->scal + 4);
+        pa.err = (int*)(p->scal + 5);
+        hipEvent_t eb = nullptr, ee = nullptr;
+        if (tp) tp->next(eb, ee);
+        if ((e = launch_fill(p->scal + 4, 2, 0.f, s)) != hipSuccess) return hip_fail(e, "fill");
+        if (eb && (e = hipEventRecord(eb, s)) != hipSuccess) return hip_fail(e, "event");
+        if ((e = launch_solve_persistent(pa, s)) != hipSuccess)
+            return hip_fail(e, "single-launch solve");
+        if (ee && (e = hipEventRecord(ee, s)) != hipSuccess) return hip_fail(e, "event");
+        float ms = 0.f;
+        if (tp) {
+            if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "timing sync");
+            if ((e = hipEventElapsedTime(&ms, eb, ee)) != hipSuccess)
+                return hip_fail(e, "hipEventElapsedTime");
+        }
+        if (info) {
+            info->iters_done = o->n_stages * o->iters_per_stage;
+            info->final_eps = pa.eps[o->n_stages - 1];
+            info->residual = -1.f;
+            // one launch: reported as its half-steps, each the launch's mean share
+            info->lse_launches = tp ? 2 * info->iters_done : 0;
+            info->lse_ms = ms;
+        }
+        return FS_OK;
+    }
     int done = 0;
     float resid = -1.f;
     float eps = o->eps_end;

@@ -304,6 +304,30 @@ hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratc
                             void* Vt_buf, int64_t m_pad, float* key_bias_buf, float* part_buf,
                             hipStream_t s);
 
+// The whole alternating schedule of a small d <= 8 problem in one launch
+// (fs_persistent.hip): W <= 16 workgroups with a grid barrier between
+// half-steps.  X, Y: the problem's fp32 operand rows (stride floats apart);
+// xn, yn: cost terms A, B; xl, yl: log2 weights; f, g: the potentials (g read
+// first); counter, err: two zeroed words.  rec_cap >= max(n, m).
+constexpr int kPersistentMaxStages = 32;
+struct PersistentArgs {
+    const float* X;
+    const float* Y;
+    const float* xn;
+    const float* yn;
+    const float* xl;
+    const float* yl;
+    float* f;
+    float* g;
+    int n, m, d, stride, W, rec_cap, n_stages, iters;
+    float eps[kPersistentMaxStages];
+    unsigned* counter;
+    int* err;
+};
+hipError_t launch_solve_persistent(const PersistentArgs& a, hipStream_t s);
+int persistent_max_points(int d);   // n, m limit of the persistent solve
+int persistent_workgroups(int64_t n, int64_t m);
+
 // Sets the thread's fs_last_error() message and returns s.
 fs_status report(fs_status s, const char* msg);
 
