@@ -119,15 +119,15 @@ typedef struct fs_problem fs_problem;
  * new f), carrying f and g across stages.  With tol > 0 the L1 marginal
  * residual  sum_i |sum_j P_ij - a_i| + sum_j |sum_i P_ij - b_j|  of the current
  * (f, g) is evaluated after every check_every-th iteration and the solve stops
- * at the first one <= tol, returning that (f, g).  Small d <= 8 problems run
- * the whole fixed-count schedule in one launch (single_launch below): a few
- * workgroups with a grid barrier between half-steps, fp32 vector scores; a
- * barrier that cannot complete (workgroups not resident together) ends the
- * launch with f and g set to NaN.  Both terms are evaluated
+ * at the first one <= tol, returning that (f, g).  Both terms are evaluated
  * (each by a dry-run update: two extra half-steps per check; the row term's
  * f-update is then reused as the next iteration's).  warm_start != 0 starts from
  * the f, g passed in (g is what the first f-update reads); otherwise g starts
- * at 0. */
+ * at 0.  Small d <= 8 problems can run the whole fixed-count schedule in one
+ * launch (single_launch below): up to 64 workgroups, each holding both clouds
+ * in LDS, with a grid barrier between half-steps and fp32 vector scores; a
+ * barrier that cannot complete (workgroups not resident together) ends the
+ * launch with f and g set to NaN. */
 typedef struct {
     int32_t n_stages;        /* >= 1 */
     float eps_start;         /* > 0, used when n_stages > 1 */
@@ -139,8 +139,8 @@ typedef struct {
     int32_t time_kernels;    /* != 0: time every streaming LSE kernel launch with HIP
                                 events on `stream` (synchronises once at the end) */
     int32_t single_launch;   /* the whole schedule as one kernel launch (d <= 8, tol <= 0,
-                                at most 32 stages, n and m within the single-launch limit:
-                                3584 points for d <= 3, 1792 for d <= 7, 1194 for d = 8):
+                                at most 32 stages, n + m within the single-launch limit:
+                                2389 points for d <= 3, 1433 for d <= 7, 1024 for d = 8):
                                 0 = when the problem is also small (n m <= 2^19 pairs),
                                 1 = whenever allowed, -1 = never */
 } fs_solve_opts;
@@ -153,6 +153,7 @@ typedef struct {
     int32_t lse_launches;    /* time_kernels: number of streaming LSE kernels timed */
     float lse_ms;            /* time_kernels: their summed duration in milliseconds
                                 (the split-merge pass, when any, is not included) */
+    int32_t single_launch;   /* 1 if the schedule ran as one launch, else 0 */
 } fs_solve_info;
 
 /* Bytes of workspace needed for a problem of this shape.  dv_max bounds the

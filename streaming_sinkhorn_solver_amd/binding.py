@@ -62,7 +62,7 @@ class SolveOpts(ctypes.Structure):
 class SolveInfo(ctypes.Structure):
     _fields_ = [("iters_done", ctypes.c_int32), ("final_eps", ctypes.c_float),
                 ("residual", ctypes.c_float), ("lse_launches", ctypes.c_int32),
-                ("lse_ms", ctypes.c_float)]
+                ("lse_ms", ctypes.c_float), ("single_launch", ctypes.c_int32)]
 
 
 class HvpInfo(ctypes.Structure):
@@ -326,7 +326,7 @@ def fs_sinkhorn_solve(p: Problem, f, g, *, eps_end: float, iters_per_stage: int,
     _check(st, "fs_sinkhorn_solve", allow)
     return {"status": st, "iters_done": info.iters_done, "final_eps": info.final_eps,
             "residual": info.residual, "lse_launches": info.lse_launches,
-            "lse_ms": info.lse_ms}
+            "lse_ms": info.lse_ms, "single_launch": bool(info.single_launch)}
 
 
 def fs_apply_transport(p: Problem, eps: float, f, g, V, U, divide_by_a: bool = False,
@@ -515,7 +515,7 @@ def fs_bs_sinkhorn_solve(p: Problem, f, g, *, eps_end: float, iters_per_stage: i
     _check(st, "fs_bs_sinkhorn_solve", allow)
     return {"status": st, "iters_done": info.iters_done, "final_eps": info.final_eps,
             "residual": info.residual, "lse_launches": info.lse_launches,
-            "lse_ms": info.lse_ms}
+            "lse_ms": info.lse_ms, "single_launch": bool(info.single_launch)}
 
 
 def fs_bs_shape(p: Problem, side: int) -> dict:

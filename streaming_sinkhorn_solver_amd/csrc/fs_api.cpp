@@ -55,6 +55,7 @@ struct fs_problem {
     void* vt;         // f16 [dv_max][m_pad] (matrix paths with dv_max > 0)
     float* kbias;     // [m_pad] key biases of the streaming transport kernel
     float* lbias;     // [max(n_pad, m_pad) + 256] key seeds of the matrix-core LSE kernels
+    unsigned long long* ptag;  // [n + m + 1] single-launch solve (small d): tagged f, g, error
     float* upart;     // [kTransportMaxSplit][n][dv_max] its partial products
     float* krec;      // small-d matrix path: key records of one pass (fp32)
     void* krec16;     //   fp16-split records (d <= 4)
@@ -214,7 +215,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 
 struct Layout {
     size_t centre, bmin, bmax, flag, xops, yops, xops16, yops16, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
-        vt, kbias, upart, krec, krec16, kguard, rsx, rsy, lbias, total;
+        vt, kbias, upart, krec, krec16, kguard, rsx, rsy, lbias, ptag, total;
 };
 
 Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
@@ -265,6 +266,10 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     // key seeds of the matrix-core LSE kernels, plus one 256-key slice of
     // padding for the copy of a split's seeds to LDS
     L.lbias = take(!small_d_path(sh.path) ? sizeof(float) * (kmax + 256) : 0);
+    // single-launch solve: the tagged potentials of both sides and an error word
+    L.ptag = take(small_d_path(sh.path) && persistent_fits(n, m, d)
+                      ? sizeof(unsigned long long) * (size_t)(n + m + 1)
+                      : 0);
     L.total = o;
     return L;
 }
@@ -519,6 +524,9 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
         p->upart = streams ? (float*)(w + L.upart) : nullptr;
     }
     p->lbias = !small_d_path(sh.path) ? (float*)(w + L.lbias) : nullptr;
+    p->ptag = small_d_path(sh.path) && persistent_fits(n, m, d)
+                  ? (unsigned long long*)(w + L.ptag)
+                  : nullptr;
     p->krec = sh.path == PATH_SMALL ? (float*)(w + L.krec) : nullptr;
     p->krec16 = sh.path == PATH_SMALL ? (void*)(w + L.krec16) : nullptr;
     p->kguard = sh.path == PATH_SMALL ? (void*)(w + L.kguard) : nullptr;
@@ -678,19 +686,22 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
         if ((e = timer.reserve(half_steps)) != hipSuccess) return hip_fail(e, "hipEventCreate");
     }
     KernelTimer* tp = o->time_kernels ? &timer : nullptr;
-    if (!o->warm_start) {
-        if ((e = launch_fill(g, p->m, 0.f, s)) != hipSuccess) return hip_fail(e, "fill g");
-        if ((e = launch_fill(f, p->n, 0.f, s)) != hipSuccess) return hip_fail(e, "fill f");
-    }
     const bool use_tol = o->tol > 0.f;
     // the whole schedule as one launch (small d <= 8 problems, fixed count)
     const bool sl_allowed = !use_tol && small_d_path(p->path) && !p->refine &&
                             o->n_stages <= kPersistentMaxStages && o->iters_per_stage > 0 &&
-                            p->n <= persistent_max_points(p->d) &&
-                            p->m <= persistent_max_points(p->d);
-    if (sl_allowed && (o->single_launch == 1 ||
-                       (o->single_launch == 0 && p->n * p->m <= ((int64_t)1 << 19)))) {
+                            2 * (int64_t)o->n_stages * o->iters_per_stage < (int64_t)0xffffffff &&
+                            p->ptag != nullptr;
+    const bool single = sl_allowed && (o->single_launch == 1 ||
+                                       (o->single_launch == 0 && p->n * p->m <= ((int64_t)1 << 19)));
+    // the single launch starts from g = 0 by itself and writes f and g
+    if (!o->warm_start && !single) {
+        if ((e = launch_fill(g, p->m, 0.f, s)) != hipSuccess) return hip_fail(e, "fill g");
+        if ((e = launch_fill(f, p->n, 0.f, s)) != hipSuccess) return hip_fail(e, "fill f");
+    }
+    if (single) {
         PersistentArgs pa{};
+        pa.g_zero = o->warm_start ? 0 : 1;
         pa.X = (const float*)p->X.ops;
         pa.Y = (const float*)p->Y.ops;
         pa.xn = p->X.nrm;
@@ -704,7 +715,6 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
         pa.d = p->d;
         pa.stride = p->dp;
         pa.W = persistent_workgroups(p->n, p->m);
-        pa.rec_cap = (int)std::max(p->n, p->m);
         pa.n_stages = o->n_stages;
         pa.iters = o->iters_per_stage;
         for (int st_i = 0; st_i < o->n_stages; ++st_i)
@@ -713,11 +723,13 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
                                : (float)((double)o->eps_start *
                                          std::pow((double)o->eps_end / (double)o->eps_start,
                                                   (double)st_i / (double)(o->n_stages - 1)));
-        pa.counter = (unsigned*)(p->scal + 4);
-        pa.err = (int*)(p->scal + 5);
+        pa.tf = p->ptag;
+        pa.tg = p->ptag + p->n;
+        pa.err = (int*)(p->ptag + p->n + p->m);
         hipEvent_t eb = nullptr, ee = nullptr;
         if (tp) tp->next(eb, ee);
-        if ((e = launch_fill(p->scal + 4, 2, 0.f, s)) != hipSuccess) return hip_fail(e, "fill");
+        if ((e = launch_fill((float*)p->ptag, 2 * (p->n + p->m + 1), 0.f, s)) != hipSuccess)
+            return hip_fail(e, "fill");
         if (eb && (e = hipEventRecord(eb, s)) != hipSuccess) return hip_fail(e, "event");
         if ((e = launch_solve_persistent(pa, s)) != hipSuccess)
             return hip_fail(e, "single-launch solve");
@@ -735,6 +747,7 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
             // one launch: reported as its half-steps, each the launch's mean share
             info->lse_launches = tp ? 2 * info->iters_done : 0;
             info->lse_ms = ms;
+            info->single_launch = 1;
         }
         return FS_OK;
     }
@@ -827,6 +840,7 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
         info->residual = use_tol ? resid : -1.f;
         info->lse_launches = lse_n;
         info->lse_ms = lse_ms;
+        info->single_launch = 0;
     }
     if (use_tol && !converged)
         return fail(FS_ERR_NOT_CONVERGED, "residual %g above tol %g after %d iterations",
@@ -1502,10 +1516,6 @@ fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delt
         const size_t half_steps = 2 * (size_t)o->n_stages * (size_t)o->iters_per_stage + 8;
         if ((e = timer.reserve(half_steps)) != hipSuccess) return hip_fail(e, "hipEventCreate");
     }
-    if (!o->warm_start) {
-        if ((e = launch_fill(g, p->m, 0.f, s)) != hipSuccess) return hip_fail(e, "fill g");
-        if ((e = launch_fill(f, p->n, 0.f, s)) != hipSuccess) return hip_fail(e, "fill f");
-    }
     const bool use_tol = o->tol > 0.f;
     int done = 0;
     float resid = -1.f, eps = o->eps_end;
@@ -1573,6 +1583,7 @@ fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delt
         info->residual = use_tol ? resid : -1.f;
         info->lse_launches = lse_n;
         info->lse_ms = lse_ms;
+        info->single_launch = 0;
     }
     if (use_tol && !converged)
         return fail(FS_ERR_NOT_CONVERGED, "residual %g above tol %g after %d iterations",

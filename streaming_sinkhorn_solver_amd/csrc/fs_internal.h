@@ -305,10 +305,12 @@ hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratc
                             hipStream_t s);
 
 // The whole alternating schedule of a small d <= 8 problem in one launch
-// (fs_persistent.hip): W <= 16 workgroups with a grid barrier between
-// half-steps.  X, Y: the problem's fp32 operand rows (stride floats apart);
-// xn, yn: cost terms A, B; xl, yl: log2 weights; f, g: the potentials (g read
-// first); counter, err: two zeroed words.  rec_cap >= max(n, m).
+// (fs_persistent.hip): W <= 64 workgroups, each holding both clouds in LDS,
+// exchanging the potentials of each half-step as tagged words.  X, Y: the
+// problem's fp32 operand rows (stride floats apart); xn, yn: cost terms A, B;
+// xl, yl: log2 weights; f, g: the potentials (g read first, unless g_zero:
+// then the first f-update takes g = 0 and g is only written); tf [n], tg [m]:
+// zeroed tagged copies of f and g; err: a zeroed word.
 constexpr int kPersistentMaxStages = 32;
 struct PersistentArgs {
     const float* X;
@@ -319,13 +321,16 @@ struct PersistentArgs {
     const float* yl;
     float* f;
     float* g;
-    int n, m, d, stride, W, rec_cap, n_stages, iters;
+    int n, m, d, stride, W, n_stages, iters, g_zero;
     float eps[kPersistentMaxStages];
-    unsigned* counter;
+    unsigned long long* tf;
+    unsigned long long* tg;
     int* err;
 };
 hipError_t launch_solve_persistent(const PersistentArgs& a, hipStream_t s);
-int persistent_max_points(int d);   // n, m limit of the persistent solve
+// whether an n x m problem in d dimensions fits the persistent solve (both
+// clouds within one workgroup's 64 KiB of LDS)
+bool persistent_fits(int64_t n, int64_t m, int d);
 int persistent_workgroups(int64_t n, int64_t m);
 
 // Sets the thread's fs_last_error() message and returns s.
