@@ -680,12 +680,6 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
     if (overlaps(f, 4 * p->n, g, 4 * p->m)) return fail(FS_ERR_INVALID_ARG, "f overlaps g");
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    KernelTimer timer;
-    if (o->time_kernels) {
-        const size_t half_steps = 2 * (size_t)o->n_stages * (size_t)o->iters_per_stage + 8;
-        if ((e = timer.reserve(half_steps)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-    }
-    KernelTimer* tp = o->time_kernels ? &timer : nullptr;
     const bool use_tol = o->tol > 0.f;
     // the whole schedule as one launch (small d <= 8 problems, fixed count)
     const bool sl_allowed = !use_tol && small_d_path(p->path) && !p->refine &&
@@ -694,6 +688,14 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
                             p->ptag != nullptr;
     const bool single = sl_allowed && (o->single_launch == 1 ||
                                        (o->single_launch == 0 && p->n * p->m <= ((int64_t)1 << 19)));
+    KernelTimer timer;
+    if (o->time_kernels) {
+        // one begin/end pair per streaming launch (one for the single launch)
+        const size_t pairs =
+            single ? 1 : 2 * (size_t)o->n_stages * (size_t)o->iters_per_stage + 8;
+        if ((e = timer.reserve(pairs)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    KernelTimer* tp = o->time_kernels ? &timer : nullptr;
     // the single launch starts from g = 0 by itself and writes f and g
     if (!o->warm_start && !single) {
         if ((e = launch_fill(g, p->m, 0.f, s)) != hipSuccess) return hip_fail(e, "fill g");
