@@ -102,6 +102,9 @@ fs_status hip_fail(hipError_t e, const char* where) {
 }
 
 constexpr int kBboxParts = 64;
+// preparation in two launches (launch_prep_small) up to this many points in
+// both clouds: one workgroup per cloud forms its centre
+constexpr int64_t kSmallPrepPoints = 32768;
 constexpr size_t kAlign = 256;
 
 size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -541,6 +544,36 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (cost == FS_COST_SQEUCLIDEAN && small_d_path(p->path) && n + m <= kSmallPrepPoints) {
+        // small problems: the same preparation in two launches
+        SmallPrepArgs sp{};
+        sp.X = X;
+        sp.Y = Y;
+        sp.a = a;
+        sp.b = b;
+        sp.n = n;
+        sp.m = m;
+        sp.n_pad = p->X.n_pad;
+        sp.m_pad = p->Y.n_pad;
+        sp.d = d;
+        sp.dp = p->dp;
+        sp.centre = p->centre;
+        sp.xops = (float*)p->X.ops;
+        sp.yops = (float*)p->Y.ops;
+        sp.xn = p->X.nrm;
+        sp.yn = p->Y.nrm;
+        sp.xlw = p->X.lw2;
+        sp.ylw = p->Y.lw2;
+        sp.xw = p->X.w;
+        sp.yw = p->Y.w;
+        sp.f = f;
+        sp.g = g;
+        sp.xl1 = p->path == PATH_SMALL ? p->X.l1max : nullptr;
+        sp.yl1 = p->path == PATH_SMALL ? p->Y.l1max : nullptr;
+        sp.flag = p->flag;
+        if ((e = launch_prep_small(sp, s)) != hipSuccess) goto hip_error;
+        goto check_flag;
+    }
     if ((e = launch_zero_flag(p->flag, s)) != hipSuccess) goto hip_error;
     if (cost == FS_COST_COSINE &&
         ((e = launch_inv_norm(X, n, d, p->X.rscale, p->flag, s)) != hipSuccess ||
@@ -568,6 +601,7 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
         goto hip_error;
     if ((e = launch_weights(a, n, p->X.lw2, p->X.w, f, p->flag, s)) != hipSuccess) goto hip_error;
     if ((e = launch_weights(b, m, p->Y.lw2, p->Y.w, g, p->flag, s)) != hipSuccess) goto hip_error;
+check_flag:
     {
         int flag = 0;
         if ((e = hipMemcpyAsync(&flag, p->flag, sizeof(int), hipMemcpyDeviceToHost, s)) !=
@@ -686,8 +720,9 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
                             o->n_stages <= kPersistentMaxStages && o->iters_per_stage > 0 &&
                             2 * (int64_t)o->n_stages * o->iters_per_stage < (int64_t)0xffffffff &&
                             p->ptag != nullptr;
-    const bool single = sl_allowed && (o->single_launch == 1 ||
-                                       (o->single_launch == 0 && p->n * p->m <= ((int64_t)1 << 19)));
+    const bool single =
+        sl_allowed && (o->single_launch == 1 ||
+                       (o->single_launch == 0 && p->n * p->m <= ((int64_t)1 << 19)));
     KernelTimer timer;
     if (o->time_kernels) {
         // one begin/end pair per streaming launch (one for the single launch)

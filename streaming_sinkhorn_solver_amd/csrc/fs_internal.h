@@ -148,6 +148,21 @@ hipError_t launch_bbox(const float* X, const float* xscale, int64_t n, const flo
 hipError_t launch_convert(const float* P, const float* rscale, int64_t n, int64_t n_pad, int d,
                           int dp, int path, const float* own_centre, const float* other_centre,
                           void* ops, float* nrm, int* flag, hipStream_t s);
+// The preparation of a small squared-Euclidean problem with fp32 operands
+// (d <= 8) in two launches: both centres, then every row's operand, cost
+// term, L1 norm (into xl1 / yl1 when non-null) and weight terms, with the
+// same arithmetic as the separate kernels.  Clears the flag and the L1 words.
+struct SmallPrepArgs {
+    const float *X, *Y, *a, *b;
+    int64_t n, m, n_pad, m_pad;
+    int d, dp;
+    float* centre;  // [2][d]
+    float *xops, *yops, *xn, *yn, *xlw, *ylw, *xw, *yw;
+    float *f, *g;      // zeroed when non-null
+    float *xl1, *yl1;  // nullable
+    int* flag;
+};
+hipError_t launch_prep_small(const SmallPrepArgs& a, hipStream_t s);
 hipError_t launch_weights(const float* w, int64_t n, float* lw2, float* wcopy, float* pot,
                           int* flag, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);

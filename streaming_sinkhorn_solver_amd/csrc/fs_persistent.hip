@@ -75,7 +75,7 @@ __device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
 
 // One cloud in LDS: records rec[j*F + c] (coordinates, then the bias slot)
 // and aux[2j] = cost term, aux[2j+1] = log2 weight.
-struct Cloud {
+struct LdsCloud {
     float* rec;
     float* aux;
 };
@@ -88,8 +88,8 @@ struct Cloud {
 // Returns false when the wait for the keys' potentials timed out here or in
 // another workgroup (the same value in every thread of the workgroup).
 template <int D>
-__device__ bool persistent_half_step(const PersistentArgs& a, Cloud R, Cloud K, int nr, int nk,
-                                     const float* kpot, const unsigned long long* ktag,
+__device__ bool persistent_half_step(const PersistentArgs& a, LdsCloud R, LdsCloud K, int nr,
+                                     int nk, const float* kpot, const unsigned long long* ktag,
                                      float* out, unsigned long long* otag, unsigned h, float eps,
                                      int wg, float2* __restrict__ lds_part, int* lds_bad) {
     constexpr int F = record_floats(D);
@@ -271,8 +271,8 @@ __global__ __launch_bounds__(kPThreads) void solve_persistent_kernel(PersistentA
     constexpr int F = record_floats(D);
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const int nm = a.n + a.m;
-    const Cloud cx{lds, lds + nm * F};
-    const Cloud cy{lds + a.n * F, lds + nm * F + 2 * a.n};
+    const LdsCloud cx{lds, lds + nm * F};
+    const LdsCloud cy{lds + a.n * F, lds + nm * F + 2 * a.n};
     float2* lds_part = (float2*)(lds + nm * (F + 2));
     // both clouds into LDS, once
     for (int t = threadIdx.x; t < nm * F; t += kPThreads) {

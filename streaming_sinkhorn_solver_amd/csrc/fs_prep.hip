@@ -87,22 +87,19 @@ __device__ __forceinline__ __bf16 to_elem<__bf16>(float v) { return (__bf16)v; }
 template <>
 __device__ __forceinline__ _Float16 to_elem<_Float16>(float v) { return (_Float16)v; }  // RNE
 
-// One wave per row: ops[i][k] = T(P[i][k] - own[k]) (0 in the padding) and
+// Row i by one wave: ops[i][k] = T(P[i][k] - own[k]) (0 in the padding) and
 // the row's cost term |P[i] - oth|^2 - |own - oth|^2 / 2 in fp32, summed in a
-// fixed order (own: this cloud's centre, oth: the other cloud's).
+// fixed order (own: this cloud's centre, oth: the other cloud's).  Returns
+// the lane's last converted value (for dp <= 64 lane k holds element k).
 template <typename T>
-__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ P,
-                                                      const float* __restrict__ rscale, int64_t n,
-                                                      int64_t n_pad, int d, int dp,
-                                                      const float* __restrict__ own,
-                                                      const float* __restrict__ oth,
-                                                      T* __restrict__ ops,
-                                                      float* __restrict__ nrm,
-                                                      int* __restrict__ flag) {
+__device__ __forceinline__ float convert_row(const float* __restrict__ P,
+                                            const float* __restrict__ rscale, int64_t i,
+                                            int64_t n, int d, int dp,
+                                            const float* __restrict__ own,
+                                            const float* __restrict__ oth, T* __restrict__ ops,
+                                            float* __restrict__ nrm, int* __restrict__ flag) {
     const int lane = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= n_pad) return;
-    float acc = 0.f, off = 0.f;
+    float acc = 0.f, off = 0.f, last = 0.f;
     int bad = 0;
     for (int k = lane; k < dp; k += 64) {
         T t = to_elem<T>(0.f);
@@ -116,11 +113,28 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
             off = fmaf(c, c, off);
         }
         ops[i * dp + k] = t;
+        last = (float)t;
     }
     acc = wave_sum(acc);
     off = wave_sum(off);
     if (i < n && lane == 0) nrm[i] = fmaf(off, -0.5f, acc);
     if (bad) atomicOr(flag, bad);
+    return last;
+}
+
+// One wave per row (4 rows per workgroup).
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ P,
+                                                      const float* __restrict__ rscale, int64_t n,
+                                                      int64_t n_pad, int d, int dp,
+                                                      const float* __restrict__ own,
+                                                      const float* __restrict__ oth,
+                                                      T* __restrict__ ops,
+                                                      float* __restrict__ nrm,
+                                                      int* __restrict__ flag) {
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= n_pad) return;
+    convert_row<T>(P, rscale, i, n, d, dp, own, oth, ops, nrm, flag);
 }
 
 // One wave per row: inv[i] = 1 / |P[i]| (cosine cost: the points are
@@ -145,13 +159,9 @@ __global__ __launch_bounds__(256) void inv_norm_kernel(const float* __restrict__
     }
 }
 
-__global__ __launch_bounds__(256) void weights_kernel(const float* __restrict__ w, int64_t n,
-                                                      float* __restrict__ lw2,
-                                                      float* __restrict__ wcopy,
-                                                      float* __restrict__ pot,
-                                                      int* __restrict__ flag) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
+__device__ __forceinline__ void weight_point(const float* __restrict__ w, int64_t i,
+                                             float* __restrict__ lw2, float* __restrict__ wcopy,
+                                             float* __restrict__ pot, int* __restrict__ flag) {
     const float v = w[i];
     // Weights must be normal positive floats (log2 of a subnormal would lose
     // accuracy on the transcendental unit).
@@ -159,6 +169,98 @@ __global__ __launch_bounds__(256) void weights_kernel(const float* __restrict__ 
     lw2[i] = lg2(v);
     wcopy[i] = v;
     if (pot) pot[i] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void weights_kernel(const float* __restrict__ w, int64_t n,
+                                                      float* __restrict__ lw2,
+                                                      float* __restrict__ wcopy,
+                                                      float* __restrict__ pot,
+                                                      int* __restrict__ flag) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    weight_point(w, i, lw2, wcopy, pot, flag);
+}
+
+// ---- small problems: the whole preparation in two launches
+// (the same arithmetic as the kernels above, so the results are the same
+// bits; only the launches are merged)
+
+// Workgroup c (0: X, 1: Y) forms its cloud's centre from the exact
+// per-coordinate min and max over all its rows (d <= 8); workgroup 0 also
+// clears the flag word and the two L1 maxima.
+__global__ __launch_bounds__(256) void prep_small_centre_kernel(SmallPrepArgs a) {
+    __shared__ float red[2][8][256];
+    const int c = blockIdx.x;
+    const float* __restrict__ P = c ? a.Y : a.X;
+    const int64_t n = c ? a.m : a.n;
+    const int d = a.d;
+    if (c == 0 && threadIdx.x == 0) {
+        a.flag[0] = 0;
+        if (a.xl1) *a.xl1 = 0.f;
+        if (a.yl1) *a.yl1 = 0.f;
+    }
+    float mn[8], mx[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        mn[k] = INFINITY;
+        mx[k] = -INFINITY;
+    }
+    for (int64_t r = threadIdx.x; r < n; r += 256)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k < d) {
+                const float v = P[r * d + k];
+                mn[k] = fminf(mn[k], v);
+                mx[k] = fmaxf(mx[k], v);
+            }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        red[0][k][threadIdx.x] = mn[k];
+        red[1][k][threadIdx.x] = mx[k];
+    }
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (threadIdx.x < w)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                red[0][k][threadIdx.x] = fminf(red[0][k][threadIdx.x], red[0][k][threadIdx.x + w]);
+                red[1][k][threadIdx.x] = fmaxf(red[1][k][threadIdx.x], red[1][k][threadIdx.x + w]);
+            }
+        __syncthreads();
+    }
+    if (threadIdx.x < d) {
+        // midpoint of the bounding box; 0 if the coordinate is all-NaN or
+        // unbounded (the row pass reports the NaN / Inf)
+        float ctr = (red[0][threadIdx.x][0] + red[1][threadIdx.x][0]) * 0.5f;
+        if (!(fabsf(ctr) <= 3.402823466e38f)) ctr = 0.f;
+        a.centre[c * d + threadIdx.x] = ctr;
+    }
+}
+
+// One wave per padded row of either cloud (rows of X first): the fp32
+// operand row and cost term (convert_row), the row's L1 norm into the
+// cloud's maximum when asked (as row_l1max_kernel), and the point's weight
+// terms (weight_point).
+__global__ __launch_bounds__(256) void prep_small_rows_kernel(SmallPrepArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.n_pad + a.m_pad) return;
+    const bool xs = t < a.n_pad;
+    const int64_t i = xs ? t : t - a.n_pad;
+    const int64_t n = xs ? a.n : a.m;
+    const float* own = a.centre + (xs ? 0 : a.d);
+    const float* oth = a.centre + (xs ? a.d : 0);
+    float* ops = xs ? a.xops : a.yops;
+    const float tv = convert_row<float>(xs ? a.X : a.Y, nullptr, i, n, a.d, a.dp, own, oth, ops,
+                                        xs ? a.xn : a.yn, a.flag);
+    float* l1 = xs ? a.xl1 : a.yl1;
+    // the row's L1 norm summed in coordinate order, from the lanes' values
+    float v = 0.f;
+    for (int k = 0; k < a.d; ++k) v += fabsf(__shfl(tv, k, 64));
+    if ((threadIdx.x & 63) == 0 && i < n) {
+        if (l1 && v > 0.f) atomicMax((unsigned*)l1, __float_as_uint(v));
+        weight_point(xs ? a.a : a.b, i, xs ? a.xlw : a.ylw, xs ? a.xw : a.yw, xs ? a.f : a.g,
+                     a.flag);
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, int64_t n, float v) {
@@ -220,6 +322,13 @@ hipError_t launch_convert(const float* P, const float* rscale, int64_t n, int64_
 hipError_t launch_weights(const float* w, int64_t n, float* lw2, float* wcopy, float* pot,
                           int* flag, hipStream_t s) {
     weights_kernel<<<(n + 255) / 256, 256, 0, s>>>(w, n, lw2, wcopy, pot, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_small(const SmallPrepArgs& a, hipStream_t s) {
+    if (a.d < 1 || a.d > 8 || a.n < 1 || a.m < 1) return hipErrorInvalidValue;
+    prep_small_centre_kernel<<<2, 256, 0, s>>>(a);
+    prep_small_rows_kernel<<<(unsigned)((a.n_pad + a.m_pad + 3) / 4), 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
