@@ -196,10 +196,11 @@ constexpr int kps_max_for(int ng) {
 // epilogue of tile s-1 then the scores of tile s -- so that each SIMD's matrix
 // pipe is fed by one wave while the other runs vector/transcendental work,
 // and every wave has a single accumulator set live during its matrix phase.
-// Four waves (one per SIMD, larger row blocks): the epilogue of tile s-1 is
-// threaded between the matrix instructions of tile s in four fenced chunks.
-// The key biases of the workgroup's whole key range are computed into LDS
-// once, up front.  Tiles are stored XOR-swizzled (chunk c of key m at
+// With tiles of at most 8 KiB the eight waves take two tiles per stage
+// (TWO_TILES below).  Four waves (one per SIMD, larger row blocks): the
+// epilogue of tile s-1 is threaded between the matrix instructions of tile s
+// in four fenced chunks.  The key biases of the workgroup's whole key range
+// are copied into LDS once, up front.  Tiles are stored XOR-swizzled (chunk c of key m at
 // m*CPR + (c ^ (m & SWZ))) so that one operand fetch hits distinct banks.
 template <int OP, int NG, int QB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
@@ -222,6 +223,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     constexpr int AP = APW < NG ? APW : NG;          // operand fragments in flight
     constexpr int MF_PER_FRAG = QB * (OP == OP_F32 ? 4 : 1);
     static_assert(NBUF == 2 || NBUF == 4, "pipeline depth");
+    // Tiles of at most 8 KiB (two-byte rows to 128 values, fp32 to 64) take
+    // two per barrier: their stages are short, so the barrier costs more
+    // than the shallower load pipeline (measured: bf16 at 64 / 128 values
+    // 7.5% / 3.5% faster, fp32 at 64 2.4%; bf16 at 256 and 512 values 6.5% /
+    // 5.6% slower with two per barrier).
+    constexpr bool TWO_TILES = WAVES == 8 && NBUF == 4 && NG <= 8;
 
     constexpr int TILE_BYTES = TILE_CHUNKS * 16;
     __shared__ __attribute__((aligned(16))) uint4 kbuf[NBUF * TILE_CHUNKS];
@@ -292,8 +299,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     constexpr bool Q_AGPR = WAVES == 4 && QB * NG * 4 > 128;
     auto issue_prologue_dma = [&]() __attribute__((always_inline)) {
         if (ntiles > 0 && (!LAG_DMA || dwave >= 0)) {
+            constexpr int PRE = TWO_TILES ? 2 : NBUF - 1;
 #pragma unroll
-            for (int k = 0; k < NBUF - 1; ++k) issue_tile(min(k, ntiles - 1), buf(k));
+            for (int k = 0; k < PRE; ++k) issue_tile(min(k, ntiles - 1), buf(k));
         }
         const int slices = (ntiles * kKeyTile + 255) / 256;
         const char* kb = (const char*)(a.kbias + j0);
@@ -606,20 +614,69 @@ __global__ __launch_bounds__(WAVES * 64, 1) void lse_mfma_kernel(LseArgs a) {
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     f32x16 accA[QB], accB[QB];
-    for (int t = 0; t < ntiles; t += NBUF) {
-        stage(t, I0{}, accA, accB);
-        if (t + 1 < ntiles) stage(t + 1, I1{}, accB, accA);
-        if constexpr (NBUF > 2) {
-            if (t + 2 < ntiles) stage(t + 2, I2{}, accA, accB);
-            if (t + 3 < ntiles) stage(t + 3, I3{}, accB, accA);
+    if constexpr (TWO_TILES) {
+        // Two tiles per stage: leading waves scores(s), epilogue(s),
+        // scores(s+1), epilogue(s+1); lagging waves epilogue(s-1), scores(s),
+        // epilogue(s), scores(s+1) -- the same per-wave tile order and state
+        // updates as one tile per stage, with half the barriers; the tiles of
+        // the next stage load during this one.
+        auto dstage = [&](int s, auto i_c, auto j_c) __attribute__((always_inline)) {
+            constexpr int I = decltype(i_c)::value;
+            const bool two = s + 1 < ntiles;
+            const float* bb = bkeys + s * kKeyTile;
+            if (!lagging) {
+                mfma_tile(i_c, bb, accA);
+                __builtin_amdgcn_sched_barrier(0);
+                epilogue_lazy(accA);
+                if (two) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_tile(j_c, bb + kKeyTile, accB);
+                    __builtin_amdgcn_sched_barrier(0);
+                    epilogue_lazy(accB);
+                }
+            } else {
+                issue_tile(min(s + 2, ntiles - 1), buf((I + 2) % 4));
+                issue_tile(min(s + 3, ntiles - 1), buf((I + 3) % 4));
+                __builtin_amdgcn_sched_barrier(0);
+                if (s > 0) epilogue_lazy(accB);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_tile(i_c, bb, accA);
+                if (two) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    epilogue_lazy(accA);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_tile(j_c, bb + kKeyTile, accB);
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            stage_barrier();
+        };
+        for (int t = 0; t < ntiles; t += 4) {
+            dstage(t, I0{}, I1{});
+            if (t + 2 < ntiles) dstage(t + 2, I2{}, I3{});
         }
-    }
-    // the lagging waves' epilogue of the last tile
-    if (lagging && ntiles > 0) {
-        if ((ntiles - 1) % 2 == 0)
-            epilogue(accA);
-        else
-            epilogue(accB);
+        if (lagging && ntiles > 0) {
+            if (ntiles % 2 == 0)
+                epilogue(accB);
+            else
+                epilogue(accA);
+        }
+    } else {
+        for (int t = 0; t < ntiles; t += NBUF) {
+            stage(t, I0{}, accA, accB);
+            if (t + 1 < ntiles) stage(t + 1, I1{}, accB, accA);
+            if constexpr (NBUF > 2) {
+                if (t + 2 < ntiles) stage(t + 2, I2{}, accA, accB);
+                if (t + 3 < ntiles) stage(t + 3, I3{}, accB, accA);
+            }
+        }
+        // the lagging waves' epilogue of the last tile
+        if (lagging && ntiles > 0) {
+            if ((ntiles - 1) % 2 == 0)
+                epilogue(accA);
+            else
+                epilogue(accB);
+        }
     }
     // No tile load may still be writing this workgroup's LDS when it exits.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
