@@ -84,21 +84,26 @@ typedef enum {
     FS_PREC_BF16_REFINE = 5
 } fs_score_prec;
 /* BF16_REFINE (d > 8): the problem keeps both a bf16 and an fp16 copy of the
- *   centred points.  fs_lse_update_f/g and every iteration of
- *   fs_sinkhorn_solve but the last use the bf16 copy; the last iteration of
- *   a fixed-count solve and every pass evaluated at given potentials
- *   (fs_marginal_residual, the transports, fs_gradient, fs_hvp) use the fp16
- *   copy.  With tol > 0 the residual checks measure the bf16 iteration and
- *   one fp16 iteration follows the stop (counted in iters_done; residual is
- *   the last check's).  The potentials of one fp16
- *   iteration from bf16-converged ones sit within the fp16 error of the exact
+ *   centred points.  fs_lse_update_f/g and the iterations of
+ *   fs_sinkhorn_solve use the bf16 copy, except the last refine_iters
+ *   iterations of a fixed-count schedule (fs_solve_opts; default 1, counted
+ *   over all stages), which use the fp16 copy, as does every pass evaluated at
+ *   given potentials (fs_marginal_residual, the transports, fs_gradient,
+ *   fs_hvp).  With tol > 0 the residual checks measure the bf16 iterations
+ *   and refine_iters fp16 iterations follow the stop (counted in iters_done;
+ *   residual is the last check's).  Iterations on the fp16 copy from
+ *   bf16-converged potentials bring them within the fp16 error of the exact
  *   iteration: on two 10-component Gaussian mixtures at 50k x 50k x 512, eps
- *   0.1, 100 iterations, 3.9e-4 eps (bf16 throughout: 3.2e-3 eps) and the
- *   barycentric projection 1.6e-4 relative (bf16 throughout: 1.2e-3), at the
- *   bf16 iterations' speed (fp16 operands, at the same instruction rate, run
- *   about 7% slower on real data).  Twice the operand workspace; an fp16
- *   range overflow of a centred coordinate is reported as for FS_PREC_FP16.
- *   fs_problem_info reports path 5. */
+ *   0.1, 100 iterations, one fp16 iteration gives 3.9e-4 eps (bf16 throughout:
+ *   3.2e-3 eps) and the barycentric projection 1.6e-4 relative (bf16
+ *   throughout: 1.2e-3); at 50k x 30k x 1024 annealed 1 -> 0.01 over 10 x 20
+ *   iterations, an fp16 last stage (refine_iters = 20) gives 8.4e-3 eps and
+ *   P.V 8.6e-4 relative, as fp16 throughout (one fp16 iteration: 3.5e-2 eps;
+ *   bf16 throughout: 6.4e-2 eps, 1.2e-2).  The bf16 iterations run about 7%
+ *   faster than fp16 ones on real data (same instruction rate, less power).
+ *   Twice the operand workspace; an fp16 range overflow of a centred
+ *   coordinate is reported as for FS_PREC_FP16.  fs_problem_info reports
+ *   path 5. */
 
 /* Ground cost.  SQEUCLIDEAN: C_ij = |x_i - y_j|^2.  COSINE: C_ij =
  * 2 - 2 cos(x_i, y_j) = |x_i/|x_i| - y_j/|y_j||^2, the squared-Euclidean
@@ -143,6 +148,8 @@ typedef struct {
                                 2389 points for d <= 3, 1433 for d <= 7, 1024 for d = 8):
                                 0 = when the problem is also small (n m <= 2^19 pairs),
                                 1 = whenever allowed, -1 = never */
+    int32_t refine_iters;    /* FS_PREC_BF16_REFINE: the last refine_iters iterations
+                                (0 = 1) run on the fp16 copy; >= 0, ignored otherwise */
 } fs_solve_opts;
 
 /* Filled on the host by fs_sinkhorn_solve (synchronises at the end when tol > 0). */

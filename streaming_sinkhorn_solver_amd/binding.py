@@ -56,7 +56,7 @@ class SolveOpts(ctypes.Structure):
                 ("eps_end", ctypes.c_float), ("iters_per_stage", ctypes.c_int32),
                 ("tol", ctypes.c_float), ("check_every", ctypes.c_int32),
                 ("warm_start", ctypes.c_int32), ("time_kernels", ctypes.c_int32),
-                ("single_launch", ctypes.c_int32)]
+                ("single_launch", ctypes.c_int32), ("refine_iters", ctypes.c_int32)]
 
 
 class SolveInfo(ctypes.Structure):
@@ -315,10 +315,11 @@ def fs_sinkhorn_solve(p: Problem, f, g, *, eps_end: float, iters_per_stage: int,
                       n_stages: int = 1, eps_start: Optional[float] = None, tol: float = 0.0,
                       check_every: int = 10, warm_start: bool = False, stream=None,
                       raise_not_converged: bool = True, time_kernels: bool = False,
-                      single_launch: int = 0) -> dict:
+                      single_launch: int = 0, refine_iters: int = 0) -> dict:
     opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
                      float(eps_end), int(iters_per_stage), float(tol), int(check_every),
-                     int(bool(warm_start)), int(bool(time_kernels)), int(single_launch))
+                     int(bool(warm_start)), int(bool(time_kernels)), int(single_launch),
+                     int(refine_iters))
     info = SolveInfo()
     st = load().fs_sinkhorn_solve(p.handle, ctypes.byref(opts), _dev(f, "f", p.n),
                                   _dev(g, "g", p.m), ctypes.byref(info), _stream(stream))
@@ -641,14 +642,15 @@ def fs_static_scratch_bytes() -> int:
 def fs_sinkhorn_solve_static(X, Y, a, b, f, g, *, eps_end: float, iters_per_stage: int,
                              prec="auto", n_stages: int = 1, eps_start: Optional[float] = None,
                              tol: float = 0.0, check_every: int = 10, warm_start: bool = False,
-                             stream=None, raise_not_converged: bool = True) -> dict:
+                             stream=None, raise_not_converged: bool = True,
+                             refine_iters: int = 0) -> dict:
     """fs_sinkhorn_solve_static: set-up and solve with the library's static
     device scratch as the workspace (no allocation)."""
     n, d = X.shape
     m = Y.shape[0]
     opts = SolveOpts(int(n_stages), float(eps_start if eps_start is not None else eps_end),
                      float(eps_end), int(iters_per_stage), float(tol), int(check_every),
-                     int(bool(warm_start)), 0, 0)
+                     int(bool(warm_start)), 0, 0, int(refine_iters))
     info = SolveInfo()
     st = load().fs_sinkhorn_solve_static(_dev(X, "X", n * d), _dev(Y, "Y", m * d),
                                          _dev(a, "a", n), _dev(b, "b", m), n, m, d, _prec(prec),

@@ -706,6 +706,7 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
     if (!p || !o || !f || !g) return fail(FS_ERR_INVALID_ARG, "NULL handle, opts, f or g");
     if (o->n_stages < 1) return fail(FS_ERR_INVALID_ARG, "n_stages must be >= 1");
     if (o->iters_per_stage < 0) return fail(FS_ERR_INVALID_ARG, "iters_per_stage must be >= 0");
+    if (o->refine_iters < 0) return fail(FS_ERR_INVALID_ARG, "refine_iters must be >= 0");
     if (!eps_ok(o->eps_end) || (o->n_stages > 1 && !eps_ok(o->eps_start)))
         return fail(FS_ERR_INVALID_ARG, "eps_start/eps_end must be finite and > 0");
     if (!std::isfinite(o->tol)) return fail(FS_ERR_INVALID_ARG, "tol must be finite");
@@ -792,6 +793,8 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
     float resid = -1.f;
     float eps = o->eps_end;
     bool converged = false;
+    const int64_t total_iters = (int64_t)o->n_stages * o->iters_per_stage;
+    const int refine_iters = o->refine_iters > 0 ? o->refine_iters : 1;
     bool have_next_f = false;  // pot_tmp already holds the next f-update (same eps)
     fs_status st;
     auto check = [&](float eps_c, bool& reusable_next) -> fs_status {
@@ -819,10 +822,10 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
                                    (double)st_i / (double)(o->n_stages - 1)));
         if (have_next_f) have_next_f = false;  // new stage: eps changed
         for (int it = 0; it < o->iters_per_stage; ++it) {
-            // the last iteration of a fixed-count schedule runs on the fp16
-            // copies of a FS_PREC_BF16_REFINE problem
-            RefineScope last(p, !use_tol && st_i == o->n_stages - 1 &&
-                                    it == o->iters_per_stage - 1);
+            // the last refine_iters iterations of a fixed-count schedule run
+            // on the fp16 copies of a FS_PREC_BF16_REFINE problem
+            RefineScope last(p, !use_tol && (int64_t)st_i * o->iters_per_stage + it >=
+                                                total_iters - refine_iters);
             if (have_next_f) {
                 if ((e = hipMemcpyAsync(f, p->pot_tmp, sizeof(float) * p->n,
                                         hipMemcpyDeviceToDevice, s)) != hipSuccess)
@@ -852,12 +855,16 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float* f, flo
     }
     if (use_tol && p->refine) {
         // FS_PREC_BF16_REFINE with a residual stop: the checks measure the
-        // bf16 iteration itself; one iteration on the fp16 copies follows
-        // the stop
+        // bf16 iterations themselves; refine_iters iterations on the fp16
+        // copies follow the stop
         RefineScope fp16_passes(p);
-        if ((st = half_step(p, true, eps, g, f, nullptr, nullptr, 0, s, tp)) != FS_OK) return st;
-        if ((st = half_step(p, false, eps, f, g, nullptr, nullptr, 0, s, tp)) != FS_OK) return st;
-        ++done;
+        for (int r = 0; r < refine_iters; ++r) {
+            if ((st = half_step(p, true, eps, g, f, nullptr, nullptr, 0, s, tp)) != FS_OK)
+                return st;
+            if ((st = half_step(p, false, eps, f, g, nullptr, nullptr, 0, s, tp)) != FS_OK)
+                return st;
+            ++done;
+        }
     }
     float lse_ms = 0.f;
     int lse_n = 0;
@@ -1539,6 +1546,7 @@ fs_status fs_bs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* o, float delt
     if (!o || !f || !g) return fail(FS_ERR_INVALID_ARG, "NULL opts, f or g");
     if (o->n_stages < 1) return fail(FS_ERR_INVALID_ARG, "n_stages must be >= 1");
     if (o->iters_per_stage < 0) return fail(FS_ERR_INVALID_ARG, "iters_per_stage must be >= 0");
+    if (o->refine_iters < 0) return fail(FS_ERR_INVALID_ARG, "refine_iters must be >= 0");
     if (!eps_ok(o->eps_end) || (o->n_stages > 1 && !eps_ok(o->eps_start)))
         return fail(FS_ERR_INVALID_ARG, "eps_start/eps_end must be finite and > 0");
     if (!std::isfinite(o->tol)) return fail(FS_ERR_INVALID_ARG, "tol must be finite");

@@ -34,13 +34,16 @@ pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
-# recipe -> (score precision, expected path, potential bar in eps)
+# recipe -> (score precision, expected path, potential bar in eps, fp16
+# iterations of a refined solve: the 1024-D recipe runs its whole last stage
+# on the fp16 copies, as bench.py does)
 RECIPES = {
-    "c2": ("fp32", "fp32-mfma", 1e-3),
-    "c3": ("bf16-refine", "bf16-mfma-fp16-refine", 2e-2),
-    "c3-fp16": ("fp16", "fp16-mfma", 2e-2),
-    "c4": ("fp16", "fp16-mfma", 2e-2),
-    "c5": ("auto", "fp32-small-mfma", 1e-3),
+    "c2": ("fp32", "fp32-mfma", 1e-3, 0),
+    "c3": ("bf16-refine", "bf16-mfma-fp16-refine", 2e-2, 0),
+    "c3-fp16": ("fp16", "fp16-mfma", 2e-2, 0),
+    "c4": ("bf16-refine", "bf16-mfma-fp16-refine", 2e-2, 20),
+    "c4-fp16": ("fp16", "fp16-mfma", 2e-2, 0),
+    "c5": ("auto", "fp32-small-mfma", 1e-3, 0),
 }
 
 
@@ -61,7 +64,7 @@ def test_full_schedule_against_oracle(fs, name):
 
     from streaming_sinkhorn_solver_amd import binding
 
-    prec, path, bar = RECIPES[name]
+    prec, path, bar, refine = RECIPES[name]
     name = name.split("-")[0]
     ref, meta = _golden(name)
     w = workloads.make(name)
@@ -79,7 +82,8 @@ def test_full_schedule_against_oracle(fs, name):
     p = binding.fs_potentials_init(X, Y, a, b, dv_max=dv, prec=prec, f=f, g=g, workspace=ws)
     assert p.info["path"] == path
     info = binding.fs_sinkhorn_solve(p, f, g, eps_end=w.eps, eps_start=w.eps_start,
-                                     n_stages=w.n_stages, iters_per_stage=w.iters)
+                                     n_stages=w.n_stages, iters_per_stage=w.iters,
+                                     refine_iters=refine)
     assert info["iters_done"] == w.iters * w.n_stages
     U = None
     if dv:

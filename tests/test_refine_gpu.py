@@ -1,11 +1,13 @@
-"""FS_PREC_BF16_REFINE: bf16 iterations with the last iteration and the
-passes at given potentials on fp16 copies of the same centred points.
+"""FS_PREC_BF16_REFINE: bf16 iterations with the last refine_iters
+iterations and the passes at given potentials on fp16 copies of the same
+centred points.
 
-* Composition, bit for bit: a refined solve of K iterations equals K - 1
-  iterations of a bf16 problem followed by one iteration of an fp16 problem
-  on the same inputs (annealed schedules too: the last iteration of the last
-  stage); its transport, gradient and residual equal the fp16 problem's at
-  the same potentials.
+* Composition, bit for bit: a refined solve of K iterations equals K - r
+  iterations of a bf16 problem followed by r iterations of an fp16 problem on
+  the same inputs (r = refine_iters, default 1; annealed schedules too, with r
+  a whole last stage or more); its transport, gradient and residual equal the
+  fp16 problem's at the same potentials; with a residual stop, r fp16
+  iterations follow the stop.
 * Parity with the float64 oracle on the 512-D two-mixture recipe at a small
   size: potentials within 2e-2 eps and the barycentric projection within
   1e-3 relative of the oracle's, both after the same iterations.
@@ -32,10 +34,34 @@ def _pair(w, dv):
     return pr, pb, ph, (X, Y, a, b)
 
 
-@pytest.mark.parametrize("name,n,m,d,iters,stages", [("c3", 1100, 900, 512, 12, 1),
-                                                     ("c4", 700, 600, 1024, 3, 4),
-                                                     ("c2", 1500, 1300, 64, 20, 1)])
-def test_refined_solve_composes(fs, name, n, m, d, iters, stages):
+def _split_schedule(binding, pb, ph, f, g, w, stages, iters, refine):
+    """The schedule with its first stages*iters - refine iterations on the bf16
+    problem and the rest on the fp16 problem, stage by stage."""
+    import math
+
+    e0 = w.eps_start if stages > 1 else w.eps
+    a0, a1 = float(np.float32(e0)), float(np.float32(w.eps))
+    t0 = stages * iters - refine
+    started = False
+    for s in range(stages):
+        e = a1 if stages == 1 else float(np.float32(a0 * math.pow(a1 / a0, s / (stages - 1))))
+        lo, hi = s * iters, (s + 1) * iters
+        for p, k in ((pb, max(0, min(hi, t0) - lo)), (ph, max(0, hi - max(lo, t0)))):
+            if k:
+                binding.fs_sinkhorn_solve(p, f, g, eps_end=e, iters_per_stage=k,
+                                          warm_start=started)
+                started = True
+
+
+@pytest.mark.parametrize("name,n,m,d,iters,stages,refine", [("c3", 1100, 900, 512, 12, 1, 0),
+                                                            ("c3", 1100, 900, 512, 12, 1, 3),
+                                                            ("c4", 700, 600, 1024, 3, 4, 0),
+                                                            ("c4", 700, 600, 1024, 3, 4, 3),
+                                                            ("c4", 700, 600, 1024, 3, 4, 5),
+                                                            ("c2", 1500, 1300, 64, 20, 1, 0)])
+def test_refined_solve_composes(fs, name, n, m, d, iters, stages, refine):
+    """refine = 0 (one fp16 iteration), a whole last stage (c4: 3), or more
+    than a stage (c4: 5, across the stage boundary)."""
     import torch
 
     from streaming_sinkhorn_solver_amd import binding
@@ -45,25 +71,13 @@ def test_refined_solve_composes(fs, name, n, m, d, iters, stages):
     pr, pb, ph, (X, Y, _, _) = _pair(w, max(d, 70))
     assert pr.info["path"] == "bf16-mfma-fp16-refine"
     f1, g1 = torch.empty(n, device="cuda"), torch.empty(m, device="cuda")
-    binding.fs_sinkhorn_solve(pr, f1, g1, eps_end=w.eps, eps_start=e0, n_stages=stages,
-                              iters_per_stage=iters)
-    # the same schedule: all but the last iteration in bf16, the last in fp16
-    import math
-
+    info = binding.fs_sinkhorn_solve(pr, f1, g1, eps_end=w.eps, eps_start=e0, n_stages=stages,
+                                     iters_per_stage=iters, refine_iters=refine)
+    assert info["iters_done"] == stages * iters
+    # the same schedule: all but the last max(refine, 1) iterations in bf16,
+    # those in fp16
     f2, g2 = torch.empty(n, device="cuda"), torch.empty(m, device="cuda")
-    if stages == 1:
-        binding.fs_sinkhorn_solve(pb, f2, g2, eps_end=w.eps, iters_per_stage=iters - 1)
-        e_last = w.eps
-    else:
-        a0, a1 = float(np.float32(e0)), float(np.float32(w.eps))
-        for s in range(stages):
-            e = float(np.float32(a0 * math.pow(a1 / a0, s / (stages - 1))))
-            k = iters if s < stages - 1 else iters - 1
-            if k:
-                binding.fs_sinkhorn_solve(pb, f2, g2, eps_end=e, iters_per_stage=k,
-                                          warm_start=s > 0)
-        e_last = e
-    binding.fs_sinkhorn_solve(ph, f2, g2, eps_end=e_last, iters_per_stage=1, warm_start=True)
+    _split_schedule(binding, pb, ph, f2, g2, w, stages, iters, max(refine, 1))
     torch.cuda.synchronize()
     assert np.array_equal(host(f1), host(f2)) and np.array_equal(host(g1), host(g2))
     # passes at given potentials run on the fp16 copies
@@ -135,6 +149,17 @@ def test_refined_residual_stop(fs):
     assert info["iters_done"] == info_b["iters_done"] + 1 and info["iters_done"] % 5 == 1
     assert info["residual"] == info_b["residual"] and info["residual"] <= 1e-3
     assert np.array_equal(host(f1), host(f2)) and np.array_equal(host(g1), host(g2))
+    # refine_iters fp16 iterations after the stop
+    f3, g3 = torch.empty(w.n, device="cuda"), torch.empty(w.m, device="cuda")
+    info3 = binding.fs_sinkhorn_solve(pr, f3, g3, eps_end=w.eps, iters_per_stage=400, tol=1e-3,
+                                      check_every=5, refine_iters=3)
+    binding.fs_sinkhorn_solve(ph, f2, g2, eps_end=w.eps, iters_per_stage=2, warm_start=True)
+    torch.cuda.synchronize()
+    assert info3["iters_done"] == info_b["iters_done"] + 3
+    assert np.array_equal(host(f3), host(f2)) and np.array_equal(host(g3), host(g2))
+    with pytest.raises(binding.FsError) as e:
+        binding.fs_sinkhorn_solve(pr, f3, g3, eps_end=w.eps, iters_per_stage=4, refine_iters=-1)
+    assert e.value.status == binding.FS_ERR_INVALID_ARG
 
 
 def test_refined_rejects_small_d_and_doubles_operands(fs):
