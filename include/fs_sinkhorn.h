@@ -130,9 +130,11 @@ typedef struct fs_problem fs_problem;
  * the f, g passed in (g is what the first f-update reads); otherwise g starts
  * at 0.  Small d <= 8 problems can run the whole fixed-count schedule in one
  * launch (single_launch below): up to 64 workgroups, each holding both clouds
- * in LDS, with a grid barrier between half-steps and fp32 vector scores; a
- * barrier that cannot complete (workgroups not resident together) ends the
- * launch with f and g set to NaN. */
+ * in LDS, fp32 vector scores, the potentials of each half-step passed between
+ * workgroups as words in the workspace tagged with the half-step's number; a
+ * wait that cannot complete (workgroups not resident together) ends the
+ * launch with f and g set to NaN.  Two solves of the same problem must not
+ * overlap (they share those words). */
 typedef struct {
     int32_t n_stages;        /* >= 1 */
     float eps_start;         /* > 0, used when n_stages > 1 */
