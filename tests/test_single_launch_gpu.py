@@ -141,3 +141,14 @@ def test_single_launch_not_taken_when_not_allowed(fs):
     assert not info["single_launch"]  # 10^6 pairs > 2^19: not by default
     _, _, info = _solve(w, 0.2, 2, 1)
     assert info["single_launch"]
+
+
+def test_single_launch_long_schedule(fs):
+    # thousands of half-steps in one launch (every word tag distinct), against
+    # the separate launches of the same schedule
+    w = workloads.random_cloud(9, 400, 350, 2, weights="exp", scale=0.7)
+    f, g, info = _solve(w, 0.05, 1500, 1, n_stages=3, eps_start=0.5)
+    assert info["single_launch"] and info["iters_done"] == 4500
+    f2, g2, _ = _solve(w, 0.05, 1500, -1, n_stages=3, eps_start=0.5)
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+    assert max_err(f, f2) <= TOL * 0.05 and max_err(g, g2) <= TOL * 0.05
