@@ -233,7 +233,14 @@ fs_status fs_sinkhorn_solve(fs_problem* p, const fs_solve_opts* opts, float* f, 
 
 /* Transport application: U = P.V with V (m x dv) and U (n x dv), P from (f, g)
  * at this eps, or the barycentric projection U_i = (P.V)_i / a_i when
- * divide_by_a != 0.  1 <= dv <= dv_max of the problem; U must not overlap V. */
+ * divide_by_a != 0.  1 <= dv <= dv_max of the problem; U must not overlap V.
+ * On the matrix paths with rows of up to 512 two-byte (256 fp32) values the
+ * plan's weights are referred to each row's value of its own update, read
+ * from f (no separate LSE pass); rows whose f is far from that value (the
+ * weights out of float16 range or too small for its rounding) are found
+ * after the pass and recomputed against their score maxima, so any finite
+ * (f, g) gives the same accuracy.  The other paths run an exact LSE pass
+ * first. */
 fs_status fs_apply_transport(fs_problem* p, float eps, const float* f, const float* g,
                              const float* V, int32_t dv, float* U, int32_t divide_by_a,
                              void* stream);
@@ -256,8 +263,10 @@ fs_status fs_apply_transport_t(fs_problem* p, float eps, const float* f, const f
  * ("FlashSinkhorn" explainer, "Method" part 3 and "Results").  X (n x d) and
  * Y (m x d) are the fp32 points passed to fs_potentials_init; grad_x (n x d)
  * and grad_y (m x d) are written, either may be NULL, neither may overlap X
- * or Y.  Each output costs one exact LSE pass and one transport application
- * of width d (so the problem needs dv_max >= d, else FS_ERR_INVALID_ARG).
+ * or Y.  Each output costs one transport application of width d (so the
+ * problem needs dv_max >= d, else FS_ERR_INVALID_ARG), which also gives the
+ * row sums of P, plus an exact LSE pass before it where fs_apply_transport
+ * runs one.
  * The matrix paths carry the transport's relative error (about 1e-3 of the
  * terms); the transported values are the other cloud's points minus its
  * centre, which keeps that error relative to the cloud's spread. */

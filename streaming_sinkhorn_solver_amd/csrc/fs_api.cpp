@@ -57,6 +57,7 @@ struct fs_problem {
     float* lbias;     // [max(n_pad, m_pad) + 256] key seeds of the matrix-core LSE kernels
     unsigned long long* ptag;  // [n + m + 1] single-launch solve (small d): tagged f, g, error
     float* upart;     // [kTransportMaxSplit][n][dv_max] its partial products
+    float* uref;      // its row references, weight sums, maxima [3][kTransportMaxSplit][n], flags [n]
     float* krec;      // small-d matrix path: key records of one pass (fp32)
     void* krec16;     //   fp16-split records (d <= 4)
     void* kguard;     //   guard words of the packing
@@ -218,7 +219,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 
 struct Layout {
     size_t centre, bmin, bmax, flag, xops, yops, xops16, yops16, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
-        vt, kbias, upart, krec, krec16, kguard, rsx, rsy, lbias, ptag, total;
+        vt, kbias, upart, uref, krec, krec16, kguard, rsx, rsy, lbias, ptag, total;
 };
 
 Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
@@ -258,6 +259,8 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     L.kbias = take(streams ? sizeof(float) * kp : 0);
     L.upart = take(streams ? sizeof(float) * kTransportMaxSplit * (size_t)std::max(n, m) * dv_max
                            : 0);
+    L.uref = take(streams ? sizeof(float) * (3 * kTransportMaxSplit + 1) * (size_t)std::max(n, m)
+                          : 0);
     const bool small = sh.path == PATH_SMALL;
     const size_t kmax = (size_t)std::max(np, mp);
     // (+32 records: the -inf sentinel block of the block-sparse form)
@@ -411,11 +414,15 @@ bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.f; }
 // One transport application.  f_side: U_i = sum_j P_ij (V_j - voff) over the
 // keys Y (U: n x dv, V: m x dv); otherwise U_j = sum_i P_ij (V_i - voff) over
 // the keys X (U: m x dv, V: n x dv).  divide_by_w divides by a_i (b_j).
-// Leaves the rows' exact LSE2 in pot_tmp.
+// lse2: the rows' exact LSE2 under these potentials, when the caller holds
+// it.  Otherwise the streaming kernel takes its references from the row
+// potential (no LSE pass) and the other kernels get an LSE pass first; with
+// need_lse the rows' LSE2 is left in pot_tmp either way.
 fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, const float* g,
                          const float* V, int32_t dv, float* U, int32_t divide_by_w,
                          const float* voff, const float* vrs, hipStream_t s,
-                         const float* lse2 = nullptr, const void* rows2 = nullptr) {
+                         const float* lse2 = nullptr, const void* rows2 = nullptr,
+                         bool need_lse = false) {
     if (!p || !f || !g || !V || !U) return fail(FS_ERR_INVALID_ARG, "NULL argument");
     if (!eps_ok(eps)) return fail(FS_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (dv < 1 || dv > p->dv_max)
@@ -426,13 +433,17 @@ fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, 
         return fail(FS_ERR_INVALID_ARG, "U overlaps V");
     const float* row_pot = f_side ? f : g;
     const float* key_pot = f_side ? g : f;
+    const bool online = !lse2 && p->uref &&
+                        transport_online(p->path, p->lse_dp, dv, K.n_pad, rows2 != nullptr);
     // exact row LSE (base 2) of this side's update scores, unless the caller
-    // holds it for these potentials
-    if (!lse2) {
+    // holds it for these potentials or the kernel needs none
+    if (!lse2 && !online) {
         fs_status st = half_step(p, f_side, eps, key_pot, p->pot_tmp, nullptr, nullptr, 1, s);
         if (st != FS_OK) return st;
     }
     TransportArgs t{};
+    t.ref_mode = online ? REF_ONLINE : REF_GIVEN;
+    t.lse_out = online && need_lse ? p->pot_tmp : nullptr;
     t.rows = R.ops;
     t.row_lse2 = lse2 ? lse2 : p->pot_tmp;
     t.row_pot = row_pot;
@@ -456,7 +467,8 @@ fs_status transport_side(fs_problem* p, bool f_side, float eps, const float* f, 
     t.divide_by_a = divide_by_w ? 1 : 0;
     t.U = U;
     t.rows2 = rows2;
-    hipError_t e = launch_transport(p->path, t, p->scal + 2, p->vt, K.n_pad, p->kbias, p->upart, s);
+    hipError_t e = launch_transport(p->path, t, p->scal + 2, p->vt, K.n_pad, p->kbias, p->upart,
+                                    p->uref, s);
     if (e != hipSuccess) return hip_fail(e, "transport launch");
     return FS_OK;
 }
@@ -525,6 +537,7 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
         const bool streams = p->vt && transport_streams(sh.path, sh.lse_dp);
         p->kbias = streams ? (float*)(w + L.kbias) : nullptr;
         p->upart = streams ? (float*)(w + L.upart) : nullptr;
+        p->uref = streams ? (float*)(w + L.uref) : nullptr;
     }
     p->lbias = !small_d_path(sh.path) ? (float*)(w + L.lbias) : nullptr;
     p->ptag = small_d_path(sh.path) && persistent_fits(n, m, d)
@@ -927,14 +940,16 @@ fs_status fs_gradient(fs_problem* p, float eps, const float* f, const float* g, 
     const float* mu = p->centre + p->d;   // centre of Y
     if (grad_x) {
         // grad_x <- sum_j P_ij (y_j - mu), then 2 (r_i (x_i - mu) - that)
-        fs_status st = transport_side(p, true, eps, f, g, Y, p->d, grad_x, 0, mu, p->Y.rscale, s);
+        fs_status st = transport_side(p, true, eps, f, g, Y, p->d, grad_x, 0, mu, p->Y.rscale, s,
+                                      nullptr, nullptr, true);
         if (st != FS_OK) return st;
         hipError_t e = launch_grad_finish(X, p->X.rscale, mu, p->pot_tmp, f, p->X.nrm, p->X.w,
                                           c_bias, p->n, p->d, grad_x, s);
         if (e != hipSuccess) return hip_fail(e, "gradient launch");
     }
     if (grad_y) {
-        fs_status st = transport_side(p, false, eps, f, g, X, p->d, grad_y, 0, nu, p->X.rscale, s);
+        fs_status st = transport_side(p, false, eps, f, g, X, p->d, grad_y, 0, nu, p->X.rscale, s,
+                                      nullptr, nullptr, true);
         if (st != FS_OK) return st;
         hipError_t e = launch_grad_finish(Y, p->Y.rscale, nu, p->pot_tmp, g, p->Y.nrm, p->Y.w,
                                           c_bias, p->m, p->d, grad_y, s);

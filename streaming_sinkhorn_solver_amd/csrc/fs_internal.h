@@ -106,9 +106,16 @@ struct LseArgs {
 };
 
 // Arguments of the transport application U = P.V (or P.V / a).
+// Where the streaming transport kernel takes each row's reference R (its
+// weights are 2^(z2 - R)): the exact LSE2 it is given, minus a slack; the
+// row potential's value of it (R = (|x~|^2 - f) c_bias - slack, the LSE2 of
+// the f-update that produced f), moved up lazily when a tile's scores exceed
+// it; or, in the repair pass, the row's score maximum found by the first pass.
+enum TransportRef : int { REF_GIVEN = 0, REF_ONLINE = 1, REF_REPAIR = 2 };
+
 struct TransportArgs {
     const void* rows;        // X~ [n_pad][dp]
-    const float* row_lse2;   // exact LSE2 of each row under the current g
+    const float* row_lse2;   // exact LSE2 of each row under the current g (REF_GIVEN)
     const float* row_pot;    // f
     const float* row_nrm;    // rows' cost term (A(x) for X, B(y) for Y)
     const float* row_w;      // a
@@ -134,6 +141,15 @@ struct TransportArgs {
     // second-moment form (Hessian-vector product): direction rows in the
     // score type [n_pad][dp], or NULL for a plain transport
     const void* rows2;
+    // streaming kernel's references (NULL: the other kernels, which take
+    // row_lse2 as it is): per key range and row, the final reference R, the
+    // sum of the weights relative to it and the score maximum (base 2)
+    int ref_mode;            // TransportRef
+    float* row_ref;          // [n_split][n]
+    float* row_sum;          // [n_split][n]
+    float* row_max;          // [n_split][n]
+    int* row_flag;           // [n] rows the repair pass recomputes
+    float* lse_out;          // nullable [n]: each row's LSE2, R + log2(sum)
 };
 
 // ---- launchers (each returns the first HIP error, enqueues on `s`) ----
@@ -315,9 +331,17 @@ hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const 
 // kTransportMaxSplit parts, whose partial products need n * dv floats each.
 constexpr int kTransportMaxSplit = 4;
 bool transport_streams(int path, int dp);
+// True when launch_transport with these shapes runs the streaming kernel with
+// references of its own (REF_ONLINE: no LSE pass needed before it).
+bool transport_online(int path, int dp, int dv, int64_t m_pad, bool moment);
+// ref_buf: 3 * kTransportMaxSplit * n_rows floats + n_rows ints (streaming
+// kernel only).  With a.ref_mode == REF_ONLINE the launch runs the first
+// pass, marks the rows whose weights came out too small for their float16
+// rounding (all far below the reference: a row potential far from its
+// update's), recomputes their row blocks from the score maxima, then merges.
 hipError_t launch_transport(int path, const TransportArgs& a, float* vmax_scratch,
                             void* Vt_buf, int64_t m_pad, float* key_bias_buf, float* part_buf,
-                            hipStream_t s);
+                            float* ref_buf, hipStream_t s);
 
 // The whole alternating schedule of a small d <= 8 problem in one launch
 // (fs_persistent.hip): W <= 64 workgroups, each holding both clouds in LDS,

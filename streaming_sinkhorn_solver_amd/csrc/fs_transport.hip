@@ -8,11 +8,16 @@
 // With the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps) and the base-2
 // scores z2_ij = c_score x~_i.y~_j + beta_j, beta_j = (g_j - |y~_j|^2) c_bias
 // + log2 b_j (the f-update's scores under the current g):
-//     P_ij = a_i 2^(z2_ij - L_i) 2^(L_i + (f_i - |x~_i|^2) c_bias),
-// where L_i = log2 sum_j 2^(z2_ij) is the exact row LSE, computed first by one
-// streaming LSE pass.  The weights p_ij = 2^(z2_ij - L_i) lie in (0, 1] and
-// sum to 1 over j, so they are well scaled for a float16 product; the row
-// factor is applied once at the end.
+//     P_ij = a_i 2^(z2_ij - R_i) 2^(R_i + (f_i - |x~_i|^2) c_bias)
+// for any row reference R_i.  The weights p_ij = 2^(z2_ij - R_i) go through
+// a float16 product, so R_i must keep them in range: near the row LSE
+// L_i = log2 sum_j 2^(z2_ij) they lie in (0, 1] and sum to 1.  The vector and
+// 1024-wide kernels take R_i = L_i from an exact LSE pass run first.  The
+// streaming kernel takes R_i = L_i - 10, with L_i read from the row
+// potential when no LSE is given -- f_i is the f-update's output, -L_i/c_bias
+// + |x~_i|^2, up to the change of g since -- and checks afterwards that the
+// weights stayed in range (rows that did not are recomputed); the row factor
+// is applied once at the end.
 //
 // Matrix-core kernel: per 32-key tile the score MFMAs of the LSE kernel give,
 // in each lane, 16 weights of ONE row; they are packed to f16 and used
@@ -437,6 +442,16 @@ __global__ __launch_bounds__(256, 1) void transport_mfma_kernel(TransportArgs a,
 
 // ------------------------------------------- streaming kernel (d <= 512)
 // Key biases in dot-product units, the seeds of the score accumulators:
+// The streaming kernel's row reference R sits kRefSlack below the row's LSE2
+// (when it is known), so the weights of a row sum to about 2^10 and its
+// largest weights are normal float16 values whatever the number of keys,
+// while none exceeds 2^10.  A reference taken from the row potential is
+// checked after the pass: rows whose score maximum exceeds it by more than
+// kMaxOver (weights near the float16 limit) or whose weights are too small
+// for their rounding are recomputed against their score maximum.
+constexpr float kRefSlack = 10.f;
+constexpr float kMaxOver = 15.f;
+
 // kb[j] = (g_j - B_j)/2 + log2(b_j)/(2 c_bias) (c_score = 2 c_bias), -inf for
 // the padding keys m <= j < m_pad.  Written with the same expression as the
 // LSE kernel's seeds, so both passes form bit-identical scores.
@@ -450,7 +465,11 @@ __global__ __launch_bounds__(256) void key_bias_kernel(TransportArgs a, int64_t 
 }
 
 // U = P.V for one (row block, column block, key range): 4 waves x 32 rows,
-// 32*NBV output columns, keys [j0, j1).  Everything the pass needs per row
+// 32*NBV output columns, keys [j0, j1), weights against the row reference R
+// (REF_GIVEN: row_lse2 - kRefSlack; REF_ONLINE: from the row potential;
+// REF_REPAIR: the score maximum the first pass recorded, only in row blocks
+// holding a marked row).  With row_ref the pass records per row its R, the
+// sum of its weights and its score maximum.  Everything the pass needs per row
 // stays in registers: the resident row block (B operand of the scores), the
 // 16 score accumulators of two tiles and the NBV output blocks (32 x 32 each;
 // with NBV = 16 they take the 256 accumulation registers).
@@ -462,7 +481,7 @@ __global__ __launch_bounds__(256) void key_bias_kernel(TransportArgs a, int64_t 
 //       clamped to the last tile: in-bounds copies into slots no one reads);
 //   (2) the score instructions of tile t+1 (accumulators seeded with the key
 //       biases, as in the LSE kernel);
-//   (3) the weights of tile t, p = 2^(c_score acc - L) in (0, 1], packed to
+//   (3) the weights of tile t, p = 2^(c_score acc - R) (summed into S), packed to
 //       f16 in accumulator order: register r of lane (row, h) holds key
 //       8(r/4) + 4h + (r%4), so registers 0..7 and 8..15 are the A operands
 //       of the two 16-key products of the tile;
@@ -565,6 +584,13 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         }
     };
 
+    // the repair pass recomputes only row blocks holding a marked row
+    if (a.ref_mode == REF_REPAIR) {
+        const int r = row_block * (WAVES * 32) + tid;
+        const int fl = tid < WAVES * 32 && r < a.n_rows ? a.row_flag[r] : 0;
+        if (!__syncthreads_or(fl)) return;
+    }
+
     // prologue: K tiles 0, 1 (clamped), V^T tile 0, the resident rows
 #pragma unroll
     for (int k = 0; k < NB; ++k) issue_k(min(k, ntiles - 1), k);
@@ -580,9 +606,24 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         }
     }
     const int myrow = row0 + ln;
-    // rows past n: L = +inf makes every weight 0
-    float L = myrow < a.n_rows ? a.row_lse2[myrow] : INFINITY;
-    asm volatile("" : "+v"(L));  // its load's wait stays in the prologue
+    // the row's reference (rows past n: +inf makes every weight 0); the
+    // repair pass starts from the row's score maximum over all key ranges
+    float R = INFINITY;
+    if (myrow < a.n_rows) {
+        if (a.ref_mode == REF_GIVEN) {
+            R = a.row_lse2[myrow] - kRefSlack;
+        } else if (a.ref_mode == REF_ONLINE) {
+            R = (a.row_nrm[myrow] - a.row_pot[myrow]) * a.c_bias - kRefSlack;
+        } else {
+            R = -INFINITY;
+            for (int sp = 0; sp < a.n_split; ++sp)
+                R = fmaxf(R, a.row_max[(int64_t)sp * a.n_rows + myrow]);
+            if (!(R > -INFINITY)) R = 0.f;
+        }
+    }
+    asm volatile("" : "+v"(R));  // its load's wait stays in the prologue
+    // the lane's weight sum (relative to 2^R) and accumulator maximum
+    float S = 0.f, Mraw = -INFINITY;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -634,7 +675,8 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         constexpr int R1 = decltype(r1_c)::value;
 #pragma unroll
         for (int r = R0; r < R1; ++r) {
-            const float w = ex2(fmaf(acc[r], a.c_score, -L));
+            const float w = ex2(fmaf(acc[r], a.c_score, -R));
+            S += w;
             if (r < 8)
                 p0[r] = (_Float16)w;
             else
@@ -729,6 +771,8 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         __builtin_amdgcn_sched_barrier(0);
         f32x16 cur = acc;
         asm volatile("" : "+v"(cur));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Mraw = fmaxf(Mraw, cur[r]);
         f16x8 p0, p1;
         uint4 av[AP];
         score_begin(ns, acc, av);
@@ -760,15 +804,33 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         ns = ns + 1 == NB ? 0 : ns + 1;
     }
 
-    // Row factor 2^(L_i + (f_i - A_i) c_bias) [* a_i] * 2^-s, or 1 when the
-    // key range is one of several (the merge applies it to the sum).
+    // Row factor 2^(R_i + (f_i - A_i) c_bias) [* a_i] * 2^-s, or 1 when the
+    // key range is one of several (the merge applies it to the sum, from the
+    // references recorded here).
+    // both lane halves of a row: the sum in a fixed order, the maximum
+    float M;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(S), __float_as_uint(S),
+                                                         false, false);
+        S = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const auto mw = __builtin_amdgcn_permlane32_swap(__float_as_uint(Mraw),
+                                                         __float_as_uint(Mraw), false, false);
+        M = fmaxf(__uint_as_float(mw[0]), __uint_as_float(mw[1])) * a.c_score;
+    }
     if (h == 0) {
         float sc = 0.f;
         if (myrow < a.n_rows) {
+            if (a.row_ref) {
+                const int64_t o = (int64_t)split * a.n_rows + myrow;
+                a.row_ref[o] = R;
+                a.row_sum[o] = S;
+                a.row_max[o] = M;
+            }
             if (a.n_split == 1) {
-                sc = ex2(L + (a.row_pot[myrow] - a.row_nrm[myrow]) * a.c_bias);
+                sc = ex2(R + (a.row_pot[myrow] - a.row_nrm[myrow]) * a.c_bias);
                 if (!a.divide_by_a) sc *= a.row_w[myrow];
                 sc *= a.v_unscale_dev[0];
+                if (a.lse_out) a.lse_out[myrow] = R + lg2(S);
             } else {
                 sc = 1.f;
             }
@@ -1140,19 +1202,68 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
     }
 }
 
-// U = (sum over key ranges of the partial products, in range order) times
-// the row factor.
+// U = (sum over key ranges of the partial products, in range order, each
+// brought to the largest of the ranges' references Rb) times the row factor
+// 2^(Rb + (f_i - A_i) c_bias) [* a_i] * 2^-s.  Kernels that record no
+// references (row_ref NULL) weighted every range against row_lse2.  With
+// lse_out, column 0 also writes the row's LSE2, Rb + log2(sum of the ranges'
+// weight sums brought to Rb).
 __global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)a.n_rows * a.dv;
     if (idx >= total) return;
     const int row = (int)(idx / a.dv);
-    float acc = 0.f;
-    for (int s = 0; s < a.n_split; ++s) acc += a.U_part[(int64_t)s * a.part_stride + idx];
-    float sc = ex2(a.row_lse2[row] + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
+    float acc = 0.f, Rb;
+    if (a.row_ref) {
+        Rb = -INFINITY;
+        for (int s = 0; s < a.n_split; ++s) Rb = fmaxf(Rb, a.row_ref[(int64_t)s * a.n_rows + row]);
+        for (int s = 0; s < a.n_split; ++s)
+            acc += a.U_part[(int64_t)s * a.part_stride + idx] *
+                   ex2(a.row_ref[(int64_t)s * a.n_rows + row] - Rb);
+        if (a.lse_out && idx == (int64_t)row * a.dv) {
+            float T = 0.f;
+            for (int s = 0; s < a.n_split; ++s)
+                T += a.row_sum[(int64_t)s * a.n_rows + row] *
+                     ex2(a.row_ref[(int64_t)s * a.n_rows + row] - Rb);
+            a.lse_out[row] = Rb + lg2(T);
+        }
+    } else {
+        Rb = a.row_lse2[row];
+        for (int s = 0; s < a.n_split; ++s) acc += a.U_part[(int64_t)s * a.part_stride + idx];
+    }
+    float sc = ex2(Rb + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
     if (!a.divide_by_a) sc *= a.row_w[row];
     sc *= a.v_unscale_dev[0];
     a.U[idx] = acc * sc;
+}
+
+// Marks the rows whose first-pass weights may be wrong: a weight above
+// 2^kMaxOver (near the float16 limit) in some key range, or weights too small
+// for their rounding -- float16 errs by at most 2^-12 of a weight, or 2^-25
+// absolutely where the weight is subnormal, so the absolute bound, m_s
+// 2^(R_s - 25) summed over the key ranges, is compared with the relative
+// one, 2^-13 of the row's weight sum.  Only a row potential far from its
+// update's value (the reference taken from it far from the row's LSE2) trips
+// either.
+__global__ __launch_bounds__(256) void transport_flag_kernel(TransportArgs a) {
+    const int row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= a.n_rows) return;
+    float Rb = -INFINITY;
+    bool over = false;
+    for (int s = 0; s < a.n_split; ++s) {
+        const int64_t o = (int64_t)s * a.n_rows + row;
+        Rb = fmaxf(Rb, a.row_ref[o]);
+        over = over || a.row_max[o] > a.row_ref[o] + kMaxOver;
+    }
+    float T = 0.f, E = 0.f;
+    for (int s = 0; s < a.n_split; ++s) {
+        const int64_t o = (int64_t)s * a.n_rows + row;
+        const float fac = ex2(a.row_ref[o] - Rb);
+        const int ms = min(a.keys_per_split, a.n_keys - s * a.keys_per_split);
+        T += a.row_sum[o] * fac;
+        E += (float)ms * fac;
+    }
+    a.row_flag[row] = (!over && E <= 4096.f * T) ? 0 : 1;
 }
 
 template <int D, int DVC>
@@ -1212,8 +1323,15 @@ hipError_t transport_stream_launch(const TransportArgs& a, int64_t m_pad, hipStr
     return hipGetLastError();
 }
 
+// output blocks per wave of the streaming kernel: 4 up to 128 columns, else
+// 8, or 16 (all 512 columns of a wide V in one block, so the scores are
+// formed once) where the row block leaves room for them
+constexpr int stream_nbv(int ng, int dv) { return dv <= 128 ? 4 : (dv <= 256 || ng < 16) ? 8 : 16; }
+
 template <int OP, int NG>
 hipError_t transport_stream_nbv(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
+    if constexpr (NG >= 16)
+        if (stream_nbv(NG, a.dv) == 16) return transport_stream_launch<OP, NG, 16>(a, m_pad, s);
     return a.dv <= 128 ? transport_stream_launch<OP, NG, 4>(a, m_pad, s)
                        : transport_stream_launch<OP, NG, 8>(a, m_pad, s);
 }
@@ -1279,14 +1397,14 @@ hipError_t transport_stream_dispatch(int ng, const TransportArgs& a, int64_t m_p
 // (row blocks x column blocks x splits) fill the compute units in whole
 // rounds best, charging each workgroup a fixed start-up of 8 tiles and each
 // extra range the traffic of its partial product (written once, read once).
-void transport_split(const TransportArgs& a, bool wide, int max_split, int& S, int& kps) {
+void transport_split(const TransportArgs& a, bool wide, int ng, int max_split, int& S, int& kps) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
     const int rpb = wide ? 64 : 128;
-    const int cpb = wide ? 64 * wide_nbv(a.dv) : 32 * (a.dv <= 128 ? 4 : 8);
+    const int cpb = wide ? 64 * wide_nbv(a.dv) : 32 * stream_nbv(ng, a.dv);
     const int64_t wg = (int64_t)((a.n_rows + rpb - 1) / rpb) * ((a.dv + cpb - 1) / cpb);
     const int64_t m_tiles = (a.n_keys + kKeyTile - 1) / kKeyTile;
     // one tile-stage of a workgroup ~ 1 us; partial traffic at ~4 bytes/ps
@@ -1324,9 +1442,18 @@ bool transport_streams(int path, int dp) {
     return ng <= 32 || ((path == PATH_MFMA_BF16 || path == PATH_MFMA_F16) && ng == 64);
 }
 
+bool transport_online(int path, int dp, int dv, int64_t m_pad, bool moment) {
+    (void)dv;
+    (void)m_pad;
+    return !moment && transport_streams(path, dp) && dp < 1024;
+}
+
 hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, void* Vt_buf,
-                            int64_t m_pad, float* key_bias_buf, float* part_buf, hipStream_t s) {
+                            int64_t m_pad, float* key_bias_buf, float* part_buf, float* ref_buf,
+                            hipStream_t s) {
     TransportArgs a = a0;
+    if (a.ref_mode != REF_GIVEN && !transport_online(path, a.dp, a.dv, m_pad, a.rows2 != nullptr))
+        return hipErrorInvalidValue;
     if (small_d_path(path)) {
         switch (a.dp) {
             case 1: return transport_valu_launch<1>(a, s);
@@ -1373,19 +1500,45 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
         a.key_bias = key_bias_buf;
         a.U_part = part_buf;
         a.part_stride = (int64_t)a.n_rows * a.dv;
-        transport_split(a, wide, kTransportMaxSplit, a.n_split, a.keys_per_split);
+        transport_split(a, wide, ng, kTransportMaxSplit, a.n_split, a.keys_per_split);
+        // the streaming kernel records its references; the others weight
+        // against row_lse2 as given
+        const bool own_ref = !wide && ref_buf != nullptr;
+        if (own_ref) {
+            const int64_t nr = (int64_t)kTransportMaxSplit * a.n_rows;
+            a.row_ref = ref_buf;
+            a.row_sum = ref_buf + nr;
+            a.row_max = ref_buf + 2 * nr;
+            a.row_flag = (int*)(ref_buf + 3 * nr);
+        } else {
+            if (a.ref_mode != REF_GIVEN) return hipErrorInvalidValue;
+            a.row_ref = a.row_sum = a.row_max = nullptr;
+            a.row_flag = nullptr;
+            a.lse_out = nullptr;
+        }
         if (moment)
             e = path == PATH_MFMA_BF16 ? transport_moment_dispatch<OP_BF16>(ng, a, m_pad, s)
                                        : transport_moment_dispatch<OP_F16>(ng, a, m_pad, s);
         else if (wide)
             e = path == PATH_MFMA_BF16 ? transport_wide_dispatch<OP_BF16>(a, m_pad, s)
                                        : transport_wide_dispatch<OP_F16>(a, m_pad, s);
-        else if (path == PATH_MFMA_F32)
-            e = transport_stream_dispatch<OP_F32>(ng, a, m_pad, s);
-        else if (path == PATH_MFMA_BF16)
-            e = transport_stream_dispatch<OP_BF16>(ng, a, m_pad, s);
-        else
-            e = transport_stream_dispatch<OP_F16>(ng, a, m_pad, s);
+        else {
+            auto pass = [&](const TransportArgs& t) {
+                if (path == PATH_MFMA_F32) return transport_stream_dispatch<OP_F32>(ng, t, m_pad, s);
+                if (path == PATH_MFMA_BF16) return transport_stream_dispatch<OP_BF16>(ng, t, m_pad, s);
+                return transport_stream_dispatch<OP_F16>(ng, t, m_pad, s);
+            };
+            e = pass(a);
+            if (e == hipSuccess && a.ref_mode == REF_ONLINE) {
+                // mark the rows whose weights came out too small, then
+                // recompute their row blocks from the score maxima
+                transport_flag_kernel<<<(unsigned)((a.n_rows + 255) / 256), 256, 0, s>>>(a);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                TransportArgs r = a;
+                r.ref_mode = REF_REPAIR;
+                e = pass(r);
+            }
+        }
         if (e != hipSuccess || a.n_split == 1) return e;
         const int64_t total = (int64_t)a.n_rows * a.dv;
         transport_merge_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);

@@ -326,6 +326,49 @@ def test_transport(fs, prec, d, dv):
         assert rel <= 1e-3, rel
 
 
+# The streaming kernel takes its row references from the row potential: with
+# potentials far from consistent (some rows' f raised by 1, weights near
+# 2^24 against that reference; others lowered by 3, weights near 2^-33) the
+# marked rows' blocks are recomputed against their score maxima.  Rows left
+# alone keep their first-pass result, so both kinds of block occur; one and
+# several key ranges, one and two 512-column blocks.
+@pytest.mark.parametrize("prec,d,dv,m", [("auto", 64, 300, 850), ("bf16", 512, 300, 850),
+                                         ("fp16", 256, 513, 850), ("bf16", 512, 512, 20000)])
+def test_transport_inconsistent_potentials(fs, prec, d, dv, m):
+    import torch
+    from streaming_sinkhorn_solver_amd import binding
+
+    n = 700
+    X, Y, a, b = _problem(1900 + d, n, m, d, scale=1.0 / np.sqrt(d))
+    V = np.random.default_rng(1901 + dv).standard_normal((m, dv)).astype(np.float32)
+    eps = 0.1
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=8, prec=prec, dv_max=dv)
+    fh = host(f).astype(np.float32)
+    shift = np.zeros(n, np.float32)
+    shift[0:n:3] = 1.0
+    shift[1:n:7] = -3.0
+    shift[300:428] = 0.0  # one 128-row block without a marked row
+    fs_ = (fh + shift).astype(np.float32)
+    U = torch.empty((n, dv), dtype=torch.float32, device="cuda")
+    T = torch.empty((n, dv), dtype=torch.float32, device="cuda")
+    binding.fs_apply_transport(p, eps, dev(fs_), g, dev(V), U)
+    binding.fs_apply_transport(p, eps, dev(fs_), g, dev(V), T, divide_by_a=True)
+    torch.cuda.synchronize()
+    if prec in ("bf16", "fp16"):
+        rp = RoundedProblem(X, Y, prec)
+        U_ref = rp.transport(a, b, fs_, host(g), V, eps)
+        T_ref = rp.transport(a, b, fs_, host(g), V, eps, divide_by_a=True)
+    else:
+        U_ref = oracle.transport(X, Y, a, b, fs_, host(g), V, eps)
+        T_ref = oracle.transport(X, Y, a, b, fs_, host(g), V, eps, divide_by_a=True)
+    for got, ref in ((host(U), U_ref), (host(T), T_ref)):
+        assert np.all(np.isfinite(got))
+        # row by row: the shifted rows' scales differ by e^40
+        num = np.linalg.norm(got - ref, axis=1)
+        den = np.linalg.norm(ref, axis=1)
+        assert np.max(num / den) <= 1e-3, np.max(num / den)
+
+
 # The d <= 8 transport: every column-block width (dv = 1, 2, 4, 5, 16 and
 # 33, i.e. 1 to 32 columns per thread and two blocks), one and several rows
 # per thread (the larger row count fills enough workgroups for the latter),
