@@ -211,6 +211,34 @@ __device__ __forceinline__ f32x16 score_step(const uint4& av, const uint4& bv, f
     }
 }
 
+// The same two-byte score step with the accumulators in vector registers.
+// The streaming kernel's 512-column output block takes all 256 accumulation
+// registers, so its score accumulators must live in vector registers; the
+// compiler places every matrix instruction's accumulators in the
+// accumulation registers of a kernel that uses them and would shuttle one
+// output block in and out of them on every tile.  Written as inline
+// assembly, the instruction has no compiler-inserted hazard waits, so the
+// caller keeps the rules of its result: back-to-back accumulation into the
+// same registers needs none; a vector instruction reading the result waits
+// for the instruction to finish (score_result_wait); a vector write of the
+// accumulators right before the first step is covered by score_seed_wait.
+template <int OP>
+__device__ __forceinline__ void score_step_vgpr(const uint4& av, const u32x4& bv, f32x16& acc) {
+    const u32x4 a = __builtin_bit_cast(u32x4, av);
+    if constexpr (OP == OP_BF16)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(bv));
+    else
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(bv));
+}
+// 24 wait states: more than an 8-pass matrix instruction's result needs
+// before a vector instruction may read it.
+__device__ __forceinline__ void score_result_wait(f32x16& acc) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+__device__ __forceinline__ void score_seed_wait(f32x16& acc) {
+    asm volatile("s_nop 3" : "+v"(acc));
+}
+
 // 16x16x32 score step of the 1024-wide kernel (two-byte types only)
 template <int OP>
 __device__ __forceinline__ f32x4 mfma16_step(const uint4& av, const u32x4& bv, f32x4 acc) {
@@ -506,6 +534,8 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
     constexpr int AP = NG < 4 ? NG : 4;  // key fragments in flight
     constexpr int DVC = 32 * NBV;
     constexpr int VT_CHUNKS = DVC * 4;
+    // score accumulators in vector registers (see score_step_vgpr)
+    constexpr bool VGPR_SCORES = NBV == 16 && OP != OP_F32;
     constexpr int VT_INSTR = VT_CHUNKS / 64;
     constexpr int VT_PER_WAVE = (VT_INSTR + WAVES - 1) / WAVES;
 
@@ -584,6 +614,45 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         }
     };
 
+    // One stage's loads as NPIECE single instructions (K slices, the biases,
+    // V^T slices), so the loop can spread them over its score instructions:
+    // a wave's load instructions issued back to back hold up the matrix
+    // instructions behind them.
+    constexpr int NPIECE = KT_PER_WAVE + 1 + VT_PER_WAVE;
+    auto issue_piece = [&](int i, int kt, int kslot, int vt, int vslot)
+                           __attribute__((always_inline)) {
+        if (i < KT_PER_WAVE) {
+            const char* tbase = keys + (int64_t)(j0 + kt * kKeyTile) * ROW_BYTES;
+            uint4* dst = kbuf + kslot * KT_CHUNKS;
+            const int L = i * WAVES + wave;
+            if (KT_INSTR % WAVES == 0 || L < KT_INSTR) {
+                if constexpr (CPR >= 64) {
+                    constexpr int IPR = CPR / 64;
+                    const int m = L / IPR;
+                    uint32_t sw = (uint32_t)(m & SWZ) * 16u;
+                    asm volatile("" : "+s"(sw));
+                    dma_to_lds16(tbase + m * ROW_BYTES + (L % IPR) * 1024, lane16 ^ sw,
+                                 dst + L * 64);
+                } else {
+                    const int P = L * 64 + lane;
+                    const int m = P / CPR, cp = P % CPR;
+                    dma_to_lds16(tbase, (uint32_t)(m * ROW_BYTES + (cp ^ (m & SWZ)) * 16),
+                                 dst + L * 64);
+                }
+            }
+        } else if (i == KT_PER_WAVE) {
+            if (lane < 8)
+                dma_to_lds16(kbias + (int64_t)(j0 + kt * kKeyTile) * 4, lane16,
+                             bbuf + kslot * kKeyTile);
+        } else {
+            const int l = i - KT_PER_WAVE - 1;
+            const int L = l * WAVES + wave;
+            if (VT_INSTR % WAVES == 0 || L < VT_INSTR)
+                dma_to_lds16(Vt + (int64_t)(j0 + vt * kKeyTile) * 2, voffs[l],
+                             vbuf + vslot * VT_CHUNKS + L * 64);
+        }
+    };
+
     // the repair pass recomputes only row blocks holding a marked row
     if (a.ref_mode == REF_REPAIR) {
         const int r = row_block * (WAVES * 32) + tid;
@@ -649,24 +718,29 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         }
 #pragma unroll
         for (int g = 0; g < AP; ++g) av[g] = kfrag(kb, g);
+        if constexpr (VGPR_SCORES) score_seed_wait(acc);
     };
-    // fragments [G0, G1) of the tile in K slot `slot`
-    auto score_steps = [&](int slot, f32x16& acc, uint4 (&av)[AP], auto g0_c, auto g1_c)
-                           __attribute__((always_inline)) {
+    // fragments [G0, G1) of the tile in K slot `slot`; dma(g) after fragment g
+    auto score_steps = [&](int slot, f32x16& acc, uint4 (&av)[AP], auto g0_c, auto g1_c,
+                           auto&& dma) __attribute__((always_inline)) {
         constexpr int G0 = decltype(g0_c)::value;
         constexpr int G1 = decltype(g1_c)::value;
         const char* kb = (const char*)(kbuf + slot * KT_CHUNKS);
 #pragma unroll
         for (int g = G0; g < G1; ++g) {
-            acc = score_step<OP>(av[g % AP], __builtin_bit_cast(uint4, q[g]), acc);
+            if constexpr (VGPR_SCORES)
+                score_step_vgpr<OP>(av[g % AP], q[g], acc);
+            else
+                acc = score_step<OP>(av[g % AP], __builtin_bit_cast(uint4, q[g]), acc);
             if (g + AP < NG) av[g % AP] = kfrag(kb, g + AP);
+            dma(g);
         }
     };
     auto scores = [&](int slot, f32x16& acc) __attribute__((always_inline)) {
         uint4 av[AP];
         score_begin(slot, acc, av);
         score_steps(slot, acc, av, std::integral_constant<int, 0>{},
-                    std::integral_constant<int, NG>{});
+                    std::integral_constant<int, NG>{}, [](int) {});
     };
     // (3) weights of scores [R0, R1) of a tile
     auto weights = [&](const f32x16& acc, f16x8& p0, f16x8& p1, auto r0_c, auto r1_c)
@@ -766,9 +840,21 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
                               (VT_INSTR % WAVES == 0 ? VT_INSTR / WAVES : -1000);
     int cs = 0, ns = 1, ls = NB - 1;  // slots of tiles t, t+1 and t+NB-1
     for (int t = 0; t < ntiles; ++t) {
-        issue_k(min(t + NB, ntiles - 1), cs);
-        issue_v(min(t + NB - 1, ntiles - 1), ls);
+        const int kt = min(t + NB, ntiles - 1), vt = min(t + NB - 1, ntiles - 1);
+        const int kslot = cs, vslot = ls;
+        // with NPIECE <= NG, piece i goes after score fragment i*NG/NPIECE
+        auto dma = [&](int g) __attribute__((always_inline)) {
+            if constexpr (VGPR_SCORES && NPIECE <= NG) {
+                const int i = (g * NPIECE + NG - 1) / NG;
+                if (i < NPIECE && (i * NG) / NPIECE == g) issue_piece(i, kt, kslot, vt, vslot);
+            }
+        };
+        if constexpr (!(VGPR_SCORES && NPIECE <= NG)) {
+            issue_k(kt, cs);
+            issue_v(vt, ls);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (VGPR_SCORES) score_result_wait(acc);
         f32x16 cur = acc;
         asm volatile("" : "+v"(cur));
 #pragma unroll
@@ -776,19 +862,19 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
         f16x8 p0, p1;
         uint4 av[AP];
         score_begin(ns, acc, av);
-        score_steps(ns, acc, av, F0{}, F1{});
+        score_steps(ns, acc, av, F0{}, F1{}, dma);
         weights(cur, p0, p1, W0{}, W1{});
         pin_scores(F0{}, F1{}, std::true_type{});
         __builtin_amdgcn_sched_barrier(0);
-        score_steps(ns, acc, av, F1{}, F2{});
+        score_steps(ns, acc, av, F1{}, F2{}, dma);
         weights(cur, p0, p1, W1{}, W2{});
         pin_scores(F1{}, F2{}, std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
-        score_steps(ns, acc, av, F2{}, F3{});
+        score_steps(ns, acc, av, F2{}, F3{}, dma);
         weights(cur, p0, p1, W2{}, W3{});
         pin_scores(F2{}, F3{}, std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
-        score_steps(ns, acc, av, F3{}, F4{});
+        score_steps(ns, acc, av, F3{}, F4{}, dma);
         weights(cur, p0, p1, W3{}, W4{});
         pin_scores(F3{}, F4{}, std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
