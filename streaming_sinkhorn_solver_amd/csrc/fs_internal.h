@@ -113,6 +113,8 @@ struct LseArgs {
 // it; or, in the repair pass, the row's score maximum found by the first pass.
 enum TransportRef : int { REF_GIVEN = 0, REF_ONLINE = 1, REF_REPAIR = 2 };
 
+constexpr int kTransportMaxSplit = 4;
+
 struct TransportArgs {
     const void* rows;        // X~ [n_pad][dp]
     const float* row_lse2;   // exact LSE2 of each row under the current g (REF_GIVEN)
@@ -137,7 +139,11 @@ struct TransportArgs {
     float* U_part;           // [n_split][n][dv] partial products of the key ranges
     int64_t part_stride;     // n * dv
     int n_split;             // key ranges (1: U written directly)
-    int keys_per_split;      // multiple of 32
+    int keys_per_split;      // multiple of 32 (1024-wide kernel: equal ranges)
+    // streaming kernel: range s is key tiles [split_tile[s], split_tile[s+1])
+    // (longest first); its work units are (row block, column block) pairs
+    int split_tile[kTransportMaxSplit + 1];
+    int n_units;
     // second-moment form (Hessian-vector product): direction rows in the
     // score type [n_pad][dp], or NULL for a plain transport
     const void* rows2;
@@ -328,8 +334,8 @@ hipError_t launch_screen(const float4* rbox, const float4* rfit, int nbR, const 
 // Transport: V -> f16 transposed scaled copy, then the streaming product.
 // Matrix paths: the streaming transport kernel serves operand rows of up to
 // 512 two-byte (or 256 fp32) values and may split the key range into up to
-// kTransportMaxSplit parts, whose partial products need n * dv floats each.
-constexpr int kTransportMaxSplit = 4;
+// kTransportMaxSplit parts (kTransportMaxSplit is defined above
+// TransportArgs), whose partial products need n * dv floats each.
 bool transport_streams(int path, int dp);
 // True when launch_transport with these shapes runs the streaming kernel with
 // references of its own (REF_ONLINE: no LSE pass needed before it).

@@ -31,6 +31,8 @@
 // transport_mfma_kernel (the remaining matrix case, fp32 at d_pad = 512) and
 // transport_valu_kernel (d <= 8, fp32 vector arithmetic).
 #include <algorithm>
+#include <functional>
+#include <vector>
 
 #include "fs_device.hpp"
 #include "fs_internal.h"
@@ -550,14 +552,29 @@ __global__ __launch_bounds__(256, 1) void transport_stream_kernel(TransportArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 31, h = lane >> 5;
-    int row_block, yb;
-    xcd_work(row_block, yb);
     const int n_cb = (a.dv + DVC - 1) / DVC;
-    const int cb = yb % n_cb, split = yb / n_cb;
+    // Work (1-D grid): workgroup b runs on XCD b % 8 as that XCD's item
+    // k = b / 8.  Each XCD owns a contiguous run of Ux work units ((row
+    // block, column block) pairs) and runs all their first key ranges, then
+    // all their second ones, ...: the ranges come longest first, so the
+    // XCD's compute units take the short ones as they free up, and the
+    // workgroups an XCD runs together stream the same key range through its
+    // L2.  Items past the XCD's share exit at once.
+    int row_block, cb, split;
+    {
+        const int b = blockIdx.x, x = b & 7, k = b >> 3;
+        const int q = a.n_units >> 3, rem = a.n_units & 7;
+        const int ux = q + (x < rem ? 1 : 0), start = x * q + min(x, rem);
+        if (k >= ux * a.n_split) return;
+        split = k / ux;
+        const int u = start + (k - split * ux);
+        row_block = u / n_cb;
+        cb = u - row_block * n_cb;
+    }
     const int row0 = row_block * (WAVES * 32) + wave * 32;
     const int c0 = cb * DVC;
-    const int j0 = split * a.keys_per_split;
-    const int j1 = min(a.n_keys, j0 + a.keys_per_split);
+    const int j0 = a.split_tile[split] * kKeyTile;
+    const int j1 = min(a.n_keys, a.split_tile[split + 1] * kKeyTile);
     const int ntiles = (j1 - j0 + kKeyTile - 1) / kKeyTile;
     const char* __restrict__ keys = (const char*)a.keys;
     const char* __restrict__ Vt = (const char*)a.Vt;
@@ -1345,7 +1362,7 @@ __global__ __launch_bounds__(256) void transport_flag_kernel(TransportArgs a) {
     for (int s = 0; s < a.n_split; ++s) {
         const int64_t o = (int64_t)s * a.n_rows + row;
         const float fac = ex2(a.row_ref[o] - Rb);
-        const int ms = min(a.keys_per_split, a.n_keys - s * a.keys_per_split);
+        const int ms = min(a.n_keys, a.split_tile[s + 1] * kKeyTile) - a.split_tile[s] * kKeyTile;
         T += a.row_sum[o] * fac;
         E += (float)ms * fac;
     }
@@ -1403,9 +1420,9 @@ hipError_t transport_mfma_dispatch(int ng, const TransportArgs& a, int64_t m_pad
 
 template <int OP, int NG, int NBV>
 hipError_t transport_stream_launch(const TransportArgs& a, int64_t m_pad, hipStream_t s) {
-    const int n_cb = (a.dv + 32 * NBV - 1) / (32 * NBV);
-    const dim3 grid((a.n_rows + 127) / 128, n_cb * a.n_split);
-    transport_stream_kernel<OP, NG, NBV><<<grid, 256, 0, s>>>(a, m_pad);
+    // n_units = row blocks x column blocks (set by the planner for this NBV)
+    const int64_t blocks = 8 * (int64_t)((a.n_units + 7) / 8) * a.n_split;
+    transport_stream_kernel<OP, NG, NBV><<<(unsigned)blocks, 256, 0, s>>>(a, m_pad);
     return hipGetLastError();
 }
 
@@ -1511,6 +1528,91 @@ void transport_split(const TransportArgs& a, bool wide, int ng, int max_split, i
     }
 }
 
+// Makespan, in tiles, of one XCD of c compute units that runs ux work units
+// in each of the s key ranges (sizes[] tiles each, longest first), every
+// workgroup taking the next item as a unit frees up, plus a start-up of
+// `overhead` tiles per workgroup.
+double xcd_makespan(int ux, int c, const int* sizes, int s, int overhead) {
+    std::vector<double> heap((size_t)c, 0.0);
+    for (int r = 0; r < s; ++r)
+        for (int i = 0; i < ux; ++i) {
+            std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+            heap.back() += sizes[r] + overhead;
+            std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+        }
+    return *std::max_element(heap.begin(), heap.end());
+}
+
+// Key ranges of the streaming kernel: up to kTransportMaxSplit ranges of
+// unequal length (longest first) chosen by simulating the fullest XCD's
+// schedule (xcd_makespan), charging each extra range its partial product's
+// traffic (written once, read once at ~4 TB/s) in tile times of this kernel
+// (one 32-key tile of a 128-row block at about half the matrix peak and
+// 2 GHz).  Candidates: 1 to 4 equal ranges, and two and three unequal ones
+// on a coarse grid refined around its best point.
+void stream_ranges(TransportArgs& a, int ng, int nbv, bool f32) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    const int c = std::max(1, cus / 8);
+    const int n_cb = (a.dv + 32 * nbv - 1) / (32 * nbv);
+    a.n_units = ((a.n_rows + 127) / 128) * n_cb;
+    const int ux = (a.n_units + 7) / 8;
+    const int m = (a.n_keys + kKeyTile - 1) / kKeyTile;
+    const double dpe = f32 ? 8.0 * ng : 16.0 * ng;
+    const double tile_flops = 128.0 * kKeyTile * 2.0 * (dpe + 32.0 * nbv);
+    const double flops_per_us = (f32 ? 256.0 : 4096.0) * 0.5 * 2.0e3;
+    const double tile_us = tile_flops / flops_per_us;
+    const double range_tiles = (double)a.n_rows * a.dv * 4.0 / 4.0e6 / tile_us;
+    double best = 1e300;
+    int bs = 1, bsz[kTransportMaxSplit] = {m, 0, 0, 0};
+    auto consider = [&](const int* sz, int s) {
+        for (int r = 0; r < s; ++r)
+            if (sz[r] < 1 || (r > 0 && sz[r] > sz[r - 1])) return;
+        const double t = xcd_makespan(ux, c, sz, s, 8) + (s > 1 ? (s + 1) * range_tiles : 0.0);
+        if (t < best - 1e-9) {
+            best = t;
+            bs = s;
+            for (int r = 0; r < s; ++r) bsz[r] = sz[r];
+        }
+    };
+    for (int s = 1; s <= kTransportMaxSplit && s <= m; ++s) {
+        int sz[kTransportMaxSplit];
+        const int per = (m + s - 1) / s;
+        for (int r = 0; r < s; ++r) sz[r] = std::min(per, m - r * per);
+        consider(sz, s);
+    }
+    if (m >= 2) {
+        const int st = std::max(1, m / 64);
+        for (int x = (m + 1) / 2; x < m; x += st) {
+            const int sz[2] = {x, m - x};
+            consider(sz, 2);
+        }
+    }
+    if (m >= 3) {
+        auto grid3 = [&](int a0, int a1, int b0, int b1, int st) {
+            for (int x = std::max(1, a0); x <= std::min(m - 2, a1); x += st)
+                for (int y = std::max(1, b0); y <= std::min(x, b1); y += st) {
+                    const int sz[3] = {x, y, m - x - y};
+                    consider(sz, 3);
+                }
+        };
+        const int st = std::max(1, m / 24);
+        grid3((m + 2) / 3, m - 2, 1, m, st);
+        if (bs == 3) {
+            const int x = bsz[0], y = bsz[1], f = std::max(1, st / 4);
+            grid3(x - st, x + st, y - st, y + st, f);
+        }
+    }
+    a.n_split = bs;
+    a.split_tile[0] = 0;
+    for (int r = 0; r < bs; ++r) a.split_tile[r + 1] = a.split_tile[r] + bsz[r];
+    for (int r = bs + 1; r <= kTransportMaxSplit; ++r) a.split_tile[r] = m;
+    a.keys_per_split = bsz[0] * kKeyTile;
+}
+
 }  // namespace
 
 namespace {
@@ -1586,7 +1688,11 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
         a.key_bias = key_bias_buf;
         a.U_part = part_buf;
         a.part_stride = (int64_t)a.n_rows * a.dv;
-        transport_split(a, wide, ng, kTransportMaxSplit, a.n_split, a.keys_per_split);
+        if (wide) {
+            transport_split(a, wide, ng, kTransportMaxSplit, a.n_split, a.keys_per_split);
+        } else {
+            stream_ranges(a, ng, stream_nbv(ng, a.dv), path == PATH_MFMA_F32);
+        }
         // the streaming kernel records its references; the others weight
         // against row_lse2 as given
         const bool own_ref = !wide && ref_buf != nullptr;
