@@ -60,8 +60,24 @@ __global__ __launch_bounds__(256) void vmax_kernel(const float* __restrict__ V, 
     __shared__ float red[256];
     float mx = 0.f;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < count; k += stride)
-        mx = fmaxf(mx, fabsf(v_value(V, k / dv, dv, (int)(k % dv), rs, off)));
+    if (!rs && !off) {
+        // plain values: no row/column index needed; 16-byte loads when aligned
+        int64_t k0 = 0;
+        if (((uintptr_t)V & 15) == 0) {
+            const int64_t n4 = count / 4;
+            const float4* V4 = (const float4*)V;
+            for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n4; k += stride) {
+                const float4 v = V4[k];
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            k0 = n4 * 4;
+        }
+        for (int64_t k = k0 + (int64_t)blockIdx.x * 256 + threadIdx.x; k < count; k += stride)
+            mx = fmaxf(mx, fabsf(V[k]));
+    } else {
+        for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < count; k += stride)
+            mx = fmaxf(mx, fabsf(v_value(V, k / dv, dv, (int)(k % dv), rs, off)));
+    }
     red[threadIdx.x] = mx;
     __syncthreads();
     for (int o = 128; o >= 1; o >>= 1) {
@@ -1311,33 +1327,51 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
 // references (row_ref NULL) weighted every range against row_lse2.  With
 // lse_out, column 0 also writes the row's LSE2, Rb + log2(sum of the ranges'
 // weight sums brought to Rb).
+// Grid: x = row, y = blocks of 1024 columns; each thread 4 columns (16-byte
+// accesses when every row starts 16-byte aligned).  The row's range factors
+// and scale are computed once per thread, uniform over the block.
 __global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)a.n_rows * a.dv;
-    if (idx >= total) return;
-    const int row = (int)(idx / a.dv);
-    float acc = 0.f, Rb;
+    const int row = blockIdx.x;
+    float fac[kTransportMaxSplit];
+    float Rb;
     if (a.row_ref) {
         Rb = -INFINITY;
         for (int s = 0; s < a.n_split; ++s) Rb = fmaxf(Rb, a.row_ref[(int64_t)s * a.n_rows + row]);
-        for (int s = 0; s < a.n_split; ++s)
-            acc += a.U_part[(int64_t)s * a.part_stride + idx] *
-                   ex2(a.row_ref[(int64_t)s * a.n_rows + row] - Rb);
-        if (a.lse_out && idx == (int64_t)row * a.dv) {
+        for (int s = 0; s < a.n_split; ++s) fac[s] = ex2(a.row_ref[(int64_t)s * a.n_rows + row] - Rb);
+        if (a.lse_out && blockIdx.y == 0 && threadIdx.x == 0) {
             float T = 0.f;
-            for (int s = 0; s < a.n_split; ++s)
-                T += a.row_sum[(int64_t)s * a.n_rows + row] *
-                     ex2(a.row_ref[(int64_t)s * a.n_rows + row] - Rb);
+            for (int s = 0; s < a.n_split; ++s) T += a.row_sum[(int64_t)s * a.n_rows + row] * fac[s];
             a.lse_out[row] = Rb + lg2(T);
         }
     } else {
         Rb = a.row_lse2[row];
-        for (int s = 0; s < a.n_split; ++s) acc += a.U_part[(int64_t)s * a.part_stride + idx];
+        for (int s = 0; s < a.n_split; ++s) fac[s] = 1.f;
     }
     float sc = ex2(Rb + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
     if (!a.divide_by_a) sc *= a.row_w[row];
     sc *= a.v_unscale_dev[0];
-    a.U[idx] = acc * sc;
+    const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+    if (c >= a.dv) return;
+    const int64_t base = (int64_t)row * a.dv + c;
+    const bool vec = (a.dv & 3) == 0 && (((uintptr_t)a.U | (uintptr_t)a.U_part) & 15) == 0;
+    if (vec) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < a.n_split; ++s) {
+            const float4 v = *(const float4*)(a.U_part + (int64_t)s * a.part_stride + base);
+            acc.x += v.x * fac[s];
+            acc.y += v.y * fac[s];
+            acc.z += v.z * fac[s];
+            acc.w += v.w * fac[s];
+        }
+        *(float4*)(a.U + base) = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+    } else {
+        for (int k = 0; k < 4 && c + k < a.dv; ++k) {
+            float acc = 0.f;
+            for (int s = 0; s < a.n_split; ++s)
+                acc += a.U_part[(int64_t)s * a.part_stride + base + k] * fac[s];
+            a.U[base + k] = acc * sc;
+        }
+    }
 }
 
 // Marks the rows whose first-pass weights may be wrong: a weight above
@@ -1732,8 +1766,8 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
             }
         }
         if (e != hipSuccess || a.n_split == 1) return e;
-        const int64_t total = (int64_t)a.n_rows * a.dv;
-        transport_merge_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
+        const dim3 mgrid((unsigned)a.n_rows, (unsigned)((a.dv + 1023) / 1024));
+        transport_merge_kernel<<<mgrid, 256, 0, s>>>(a);
         return hipGetLastError();
     }
     if (path == PATH_MFMA_F32) return transport_mfma_dispatch<OP_F32>(ng, a, m_pad, s);
