@@ -42,6 +42,9 @@ Prints one JSON line with
              runs of a few seconds includes the idle time before them
   phases_ms  mean time per step of problem preparation, the solve and the
              transport (HIP events on the solver's stream)
+  transport_roofline  (matrix-core recipes with a transport) the transport
+             phase against the same dense peak, counting 2 n m (d + dv)
+             flops: the scores and the product with V
   backward   (recipes with a transport of width >= d) one fs_gradient call
              for both clouds at the final potentials, timed after the steps
   cpu_baseline  the float64 oracle's f-update timed on this host's cores on a
@@ -271,8 +274,9 @@ def traffic_file(workload: str) -> str:
 
 def counter_mode(w, prec: str, half_steps: int = 6) -> None:
     """Workload for hardware-counter runs: a 1 GiB elementwise read+write of
-    known size (the counters' calibration), then problem preparation and
-    `half_steps` alternating LSE passes of the recipe at its final eps."""
+    known size (the counters' calibration), then problem preparation,
+    `half_steps` alternating LSE passes of the recipe at its final eps and,
+    for recipes with a transport, one more f-update and two transports."""
     import torch
 
     from streaming_sinkhorn_solver_amd import binding
@@ -307,15 +311,26 @@ def counter_mode(w, prec: str, half_steps: int = 6) -> None:
         print(json.dumps({"counter_mode": "done", "half_steps": half_steps,
                           "copy_bytes": float(1 << 30)}), flush=True)
         return
-    p = binding.fs_potentials_init(X, Y, a, b, prec=prec, f=f, g=g)
+    dv = w.V.shape[1] if w.V is not None else 0
+    p = binding.fs_potentials_init(X, Y, a, b, prec=prec, f=f, g=g, dv_max=dv)
     for k in range(half_steps):
         if k % 2 == 0:
             binding.fs_lse_update_f(p, w.eps, g, f)
         else:
             binding.fs_lse_update_g(p, w.eps, f, g)
+    transports = 0
+    if dv:
+        # then the recipe's transport, twice, after one more f-update (so f
+        # is its own update's output under g)
+        binding.fs_lse_update_f(p, w.eps, g, f)
+        V = torch.from_numpy(w.V).to(dev)
+        U = torch.empty((w.n, dv), device=dev)
+        for _ in range(2):
+            binding.fs_apply_transport(p, w.eps, f, g, V, U, divide_by_a=w.divide_by_a)
+        transports = 2
     torch.cuda.synchronize()
     print(json.dumps({"counter_mode": "done", "half_steps": half_steps,
-                      "copy_bytes": float(1 << 30)}), flush=True)
+                      "transports": transports, "copy_bytes": float(1 << 30)}), flush=True)
 
 
 def traffic_per_launch(workload: str):
@@ -630,6 +645,16 @@ def main():
         "clocks": clocks,
         "roofline": roofline,
     }
+    if dv and unit == "TFLOP/s" and phases["transport"] > 0:
+        # the transport phase (every launch of one application) against the
+        # matrix peak: 2 n m (d + dv) algorithmic flops
+        t_flops = 2.0 * w.n * w.m * (w.d + dv)
+        t_ach = t_flops / (phases["transport"] * 1e-3) / 1e12
+        out["transport_roofline"] = {
+            "bound": "mfma", "flops": t_flops, "achieved": round(t_ach, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(t_ach / peak, 4),
+            "what": "phases_ms.transport (all launches of one application, event-timed) "
+                    "against 2 n m (d + dv) flops"}
     if backward:
         out["backward"] = backward
     if hvp:

@@ -116,22 +116,25 @@ def kernel_durations(db: str, name_substr: str):
 
 
 def write_counters_md(dbs, out_md: str, kernel: str, commands, n_cu: int = 256,
-                      n_xcd: int = 8) -> dict:
+                      n_xcd: int = 8, min_us: float = 0.0) -> dict:
     """Mean per dispatch of every counter of the matching kernel over the
     given databases (one per counter pass), with the graphics clock
     (GRBM_GUI_ACTIVE of one XCD over the traced duration) and the matrix-pipe
     busy share (SQ_VALU_MFMA_BUSY_CYCLES over the active cycles x CUs x 4
-    SIMDs)."""
+    SIMDs).  With min_us, dispatches shorter than that are left out (they
+    need the kernel trace of the same run)."""
     vals, durs = {}, []
     for db in dbs:
         con = sqlite3.connect(db)
         rows = con.execute("select kernel_name, dispatch_id, counter_name, value "
                            "from counters_collection").fetchall()
+        d = kernel_durations(db, kernel)
+        if min_us > 0:
+            d = {k: v for k, v in d.items() if v >= min_us * 1e3}
         per = collections.defaultdict(lambda: collections.defaultdict(float))
         for kn, did, cn, v in rows:
-            if kernel in kn:
+            if kernel in kn and (min_us <= 0 or did in d):
                 per[cn][did] += v
-        d = kernel_durations(db, kernel)
         for cn, by in per.items():
             vals[cn] = sum(by.values()) / len(by)
             if "GRBM_GUI_ACTIVE" == cn and d:
@@ -192,9 +195,12 @@ def main(argv=None):
     s3.add_argument("--db", action="append", required=True)
     s3.add_argument("--kernel", default="lse_mfma_kernel")
     s3.add_argument("--command", action="append", required=True)
+    s3.add_argument("--min-us", type=float, default=0.0,
+                    help="leave out dispatches shorter than this (needs the kernel trace)")
     a = ap.parse_args(argv)
     if a.cmd == "counters":
-        print(json.dumps(write_counters_md(a.db, a.out, a.kernel, a.command), indent=1))
+        print(json.dumps(write_counters_md(a.db, a.out, a.kernel, a.command,
+                                           min_us=a.min_us), indent=1))
         return 0
     if a.cmd == "stats":
         write_stats_md(a.db, a.out, a.command)
