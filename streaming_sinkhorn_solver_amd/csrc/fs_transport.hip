@@ -1039,6 +1039,7 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
     // 0-1 the scores' row blocks, 2-3 (MOMENT) the direction scores'
     __shared__ __attribute__((aligned(16))) float4 xbuf[2][2][2][NP][64];
     __shared__ float rowscale[64];
+    __shared__ float rowref[64];  // each row's final reference (score layout -> P.V layout)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1098,6 +1099,12 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
         if (wave == 0 && lane < 4)
             dma_to_lds16(kbias + (int64_t)(j0 + k * KT) * 4, lane16, &bbuf[slot][0]);
     };
+    // the repair pass recomputes only row blocks holding a marked row
+    if (a.ref_mode == REF_REPAIR) {
+        const int r = row_block * 64 + tid;
+        const int fl = tid < 64 && r < a.n_rows ? a.row_flag[r] : 0;
+        if (!__syncthreads_or(fl)) return;
+    }
     if (ntiles > 0) {
 #pragma unroll
         for (int l = 0; l < KPW; ++l) issue_k_slice(0, 0, l);
@@ -1130,12 +1137,28 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
                 if constexpr (MOMENT) asm volatile("" ::"v"(vq[rb][ks]));
             }
     }
-    // rows past n: L = +inf makes every weight 0
-    float Lr[2];
+    // each row's reference, as in the streaming kernel (the second-moment
+    // form keeps the exact LSE: its weights carry the direction scores too);
+    // rows past n: +inf makes every weight 0
+    constexpr float slack = MOMENT ? 0.f : kRefSlack;
+    float Lr[2], S[2] = {0.f, 0.f}, Mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int row = row0 + 16 * rb + l16;
-        Lr[rb] = row < a.n_rows ? a.row_lse2[row] : INFINITY;
+        float R = INFINITY;
+        if (row < a.n_rows) {
+            if (a.ref_mode == REF_GIVEN) {
+                R = a.row_lse2[row] - slack;
+            } else if (a.ref_mode == REF_ONLINE) {
+                R = (a.row_nrm[row] - a.row_pot[row]) * a.c_bias - slack;
+            } else {
+                R = -INFINITY;
+                for (int sp = 0; sp < a.n_split; ++sp)
+                    R = fmaxf(R, a.row_max[(int64_t)sp * a.n_rows + row]);
+                if (!(R > -INFINITY)) R = 0.f;
+            }
+        }
+        Lr[rb] = R;
         asm volatile("" : "+v"(Lr[rb]));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1238,7 +1261,13 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) wt[rb][e] = ex2(fmaf(z[rb][e], a.c_score, -Lr[rb]));
+                for (int e = 0; e < 4; ++e) {
+                    wt[rb][e] = ex2(fmaf(z[rb][e], a.c_score, -Lr[rb]));
+                    if constexpr (!MOMENT) {
+                        S[rb] += wt[rb][e];
+                        Mx[rb] = fmaxf(Mx[rb], z[rb][e]);
+                    }
+                }
             if constexpr (MOMENT) {
                 // weights p_ij s_ij
 #pragma unroll
@@ -1289,14 +1318,41 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
         stage_barrier();
     }
 
-    // Row factor 2^(L_i + (f_i - A_i) c_bias) [* a_i] * 2^-s, or 1 when the
-    // key range is one of several (the merge applies it to the sum).
+    // Each row's weight sum and maximum over the four key groups of its
+    // lanes (the same in both waves of the pair, which form the same
+    // weights); the records and the reference for the P.V layout from wave
+    // dh = 0, key group 0.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        S[rb] += __shfl_xor(S[rb], 16, 64);
+        S[rb] += __shfl_xor(S[rb], 32, 64);
+        Mx[rb] = fmaxf(Mx[rb], __shfl_xor(Mx[rb], 16, 64));
+        Mx[rb] = fmaxf(Mx[rb], __shfl_xor(Mx[rb], 32, 64));
+    }
+    if (dh == 0 && kg == 0) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int rr = 16 * rb + l16, row = row0 + rr;
+            rowref[rg * 32 + rr] = Lr[rb];
+            if (row < a.n_rows && a.row_ref) {
+                const int64_t o = (int64_t)split * a.n_rows + row;
+                a.row_ref[o] = Lr[rb];
+                a.row_sum[o] = S[rb];
+                a.row_max[o] = Mx[rb] * a.c_score;
+            }
+            if (row < a.n_rows && a.n_split == 1 && a.lse_out) a.lse_out[row] = Lr[rb] + lg2(S[rb]);
+        }
+    }
+    __syncthreads();
+    // Row factor 2^(R_i + (f_i - A_i) c_bias) [* a_i] * 2^-s, or 1 when the
+    // key range is one of several (the merge applies it to the sum, from the
+    // references recorded above).
     if (dh == 0 && hh == 0) {
         const int row = row0 + l32;
         float sc = 0.f;
         if (row < a.n_rows) {
             if (a.n_split == 1) {
-                sc = ex2(a.row_lse2[row] + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
+                sc = ex2(rowref[rg * 32 + l32] + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
                 if (!a.divide_by_a) sc *= a.row_w[row];
                 sc *= a.v_unscale_dev[0];
             } else {
@@ -1665,9 +1721,8 @@ bool transport_streams(int path, int dp) {
 }
 
 bool transport_online(int path, int dp, int dv, int64_t m_pad, bool moment) {
-    (void)dv;
-    (void)m_pad;
-    return !moment && transport_streams(path, dp) && dp < 1024;
+    return !moment && transport_streams(path, dp) &&
+           (dp < 1024 || transport_wide(path, dp, dv, m_pad));
 }
 
 hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, void* Vt_buf,
@@ -1724,12 +1779,15 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
         a.part_stride = (int64_t)a.n_rows * a.dv;
         if (wide) {
             transport_split(a, wide, ng, kTransportMaxSplit, a.n_split, a.keys_per_split);
+            // equal ranges (for the check kernel's key counts)
+            for (int r = 0; r <= kTransportMaxSplit; ++r)
+                a.split_tile[r] = std::min(r, a.n_split) * (a.keys_per_split / kKeyTile);
         } else {
             stream_ranges(a, ng, stream_nbv(ng, a.dv), path == PATH_MFMA_F32);
         }
         // the streaming kernel records its references; the others weight
         // against row_lse2 as given
-        const bool own_ref = !wide && ref_buf != nullptr;
+        const bool own_ref = !moment && ref_buf != nullptr;
         if (own_ref) {
             const int64_t nr = (int64_t)kTransportMaxSplit * a.n_rows;
             a.row_ref = ref_buf;
@@ -1742,14 +1800,15 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
             a.row_flag = nullptr;
             a.lse_out = nullptr;
         }
-        if (moment)
-            e = path == PATH_MFMA_BF16 ? transport_moment_dispatch<OP_BF16>(ng, a, m_pad, s)
-                                       : transport_moment_dispatch<OP_F16>(ng, a, m_pad, s);
-        else if (wide)
-            e = path == PATH_MFMA_BF16 ? transport_wide_dispatch<OP_BF16>(a, m_pad, s)
-                                       : transport_wide_dispatch<OP_F16>(a, m_pad, s);
-        else {
+        {
             auto pass = [&](const TransportArgs& t) {
+                if (moment)
+                    return path == PATH_MFMA_BF16
+                               ? transport_moment_dispatch<OP_BF16>(ng, t, m_pad, s)
+                               : transport_moment_dispatch<OP_F16>(ng, t, m_pad, s);
+                if (wide)
+                    return path == PATH_MFMA_BF16 ? transport_wide_dispatch<OP_BF16>(t, m_pad, s)
+                                                  : transport_wide_dispatch<OP_F16>(t, m_pad, s);
                 if (path == PATH_MFMA_F32) return transport_stream_dispatch<OP_F32>(ng, t, m_pad, s);
                 if (path == PATH_MFMA_BF16) return transport_stream_dispatch<OP_BF16>(ng, t, m_pad, s);
                 return transport_stream_dispatch<OP_F16>(ng, t, m_pad, s);

@@ -326,14 +326,16 @@ def test_transport(fs, prec, d, dv):
         assert rel <= 1e-3, rel
 
 
-# The streaming kernel takes its row references from the row potential: with
-# potentials far from consistent (some rows' f raised by 1, weights near
+# The streaming kernels take their row references from the row potential:
+# with potentials far from consistent (some rows' f raised by 1, weights near
 # 2^24 against that reference; others lowered by 3, weights near 2^-33) the
 # marked rows' blocks are recomputed against their score maxima.  Rows left
 # alone keep their first-pass result, so both kinds of block occur; one and
-# several key ranges, one and two 512-column blocks.
+# several key ranges, one and two 512-column blocks, and the 1024-wide
+# kernel (64-row blocks).
 @pytest.mark.parametrize("prec,d,dv,m", [("auto", 64, 300, 850), ("bf16", 512, 300, 850),
-                                         ("fp16", 256, 513, 850), ("bf16", 512, 512, 20000)])
+                                         ("fp16", 256, 513, 850), ("bf16", 512, 512, 20000),
+                                         ("fp16", 1024, 300, 850), ("bf16", 1024, 1024, 3000)])
 def test_transport_inconsistent_potentials(fs, prec, d, dv, m):
     import torch
     from streaming_sinkhorn_solver_amd import binding
@@ -347,7 +349,7 @@ def test_transport_inconsistent_potentials(fs, prec, d, dv, m):
     shift = np.zeros(n, np.float32)
     shift[0:n:3] = 1.0
     shift[1:n:7] = -3.0
-    shift[300:428] = 0.0  # one 128-row block without a marked row
+    shift[256:384] = 0.0  # a 128-row block (two 64-row blocks) without a marked row
     fs_ = (fh + shift).astype(np.float32)
     U = torch.empty((n, dv), dtype=torch.float32, device="cuda")
     T = torch.empty((n, dv), dtype=torch.float32, device="cuda")
