@@ -545,12 +545,10 @@ def main():
         binding.fs_gradient(p, w.eps, f, g, X, Y, gX, gY)
         e1.record()
         torch.cuda.synchronize()
-        one_pass = w.d < 1024  # the streaming kernel needs no LSE pass before it
         backward = {"gradient_ms": round(e0.elapsed_time(e1), 3),
                     "what": "fs_gradient for both clouds at the final potentials (two transport "
-                            "applications of width d" + (
-                                ", each also leaving its rows' LSE2)" if one_pass else
-                                ", each after an exact LSE pass)")}
+                            "applications of width d, each also leaving its rows' LSE2 for "
+                            "the finishing pass)"}
         del gX, gY
 
     hvp = None
