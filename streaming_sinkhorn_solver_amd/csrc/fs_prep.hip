@@ -33,28 +33,41 @@ __global__ void zero_flag_kernel(int* flag) {
     if (threadIdx.x == 0) flag[0] = 0;
 }
 
-// Per-coordinate min/max of one row chunk.  grid = (ceil(d/256), parts).
-// rscale (nullable): the points are P[r] * rscale[r] (unit rows for the
-// cosine cost).
+// Per-coordinate min/max of one row chunk.  grid = (ceil(d/64), parts):
+// 64 coordinates per workgroup, its four waves taking every fourth row of
+// the chunk (each wave reads 64 consecutive floats of a row), then the four
+// partial results combined through LDS.  rscale (nullable): the points are
+// P[r] * rscale[r] (unit rows for the cosine cost).
 __global__ __launch_bounds__(256) void bbox_partial_kernel(const float* __restrict__ P,
                                                            const float* __restrict__ rscale,
                                                            int64_t n, int d, int parts,
                                                            float* __restrict__ pmin,
                                                            float* __restrict__ pmax) {
-    const int k = blockIdx.x * 256 + threadIdx.x;
-    if (k >= d) return;
+    __shared__ float smn[4][64], smx[4][64];
+    const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+    const int k = blockIdx.x * 64 + c;
     const int part = blockIdx.y;
     const int64_t chunk = (n + parts - 1) / parts;
     const int64_t r0 = part * chunk;
     const int64_t r1 = r0 + chunk < n ? r0 + chunk : n;
     float mn = INFINITY, mx = -INFINITY;
-    for (int64_t r = r0; r < r1; ++r) {
-        const float v = rscale ? P[r * d + k] * rscale[r] : P[r * d + k];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+    if (k < d) {
+#pragma unroll 8
+        for (int64_t r = r0 + rg; r < r1; r += 4) {
+            const float v = rscale ? P[r * d + k] * rscale[r] : P[r * d + k];
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+        }
     }
-    pmin[(int64_t)part * d + k] = mn;
-    pmax[(int64_t)part * d + k] = mx;
+    smn[rg][c] = mn;
+    smx[rg][c] = mx;
+    __syncthreads();
+    if (rg == 0 && k < d) {
+        mn = fminf(fminf(smn[0][c], smn[1][c]), fminf(smn[2][c], smn[3][c]));
+        mx = fmaxf(fmaxf(smx[0][c], smx[1][c]), fmaxf(smx[2][c], smx[3][c]));
+        pmin[(int64_t)part * d + k] = mn;
+        pmax[(int64_t)part * d + k] = mx;
+    }
 }
 
 // Centre of one cloud from its parts' boxes.  grid = (ceil(d/256), 2): y-block
@@ -284,7 +297,7 @@ hipError_t launch_inv_norm(const float* P, int64_t n, int d, float* inv, int* fl
 hipError_t launch_bbox(const float* X, const float* xscale, int64_t n, const float* Y,
                        const float* yscale, int64_t m, int d, float* part_min, float* part_max,
                        int parts, float* centres, hipStream_t s) {
-    const dim3 grid((d + 255) / 256, parts);
+    const dim3 grid((d + 63) / 64, parts);
     bbox_partial_kernel<<<grid, 256, 0, s>>>(X, xscale, n, d, parts, part_min, part_max);
     bbox_partial_kernel<<<grid, 256, 0, s>>>(Y, yscale, m, d, parts,
                                              part_min + (int64_t)parts * d,
