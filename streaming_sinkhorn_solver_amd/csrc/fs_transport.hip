@@ -84,7 +84,13 @@ __global__ __launch_bounds__(256) void vmax_kernel(const float* __restrict__ V, 
         if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
         __syncthreads();
     }
-    if (threadIdx.x == 0) atomicMax(maxbits, __float_as_uint(red[0]));
+    // one atomic per workgroup, and none where the word already holds as
+    // much (after the first workgroups almost none: contended atomics on one
+    // word would serialise the grid)
+    if (threadIdx.x == 0) {
+        const unsigned seen = __hip_atomic_load(maxbits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__float_as_uint(red[0]) > seen) atomicMax(maxbits, __float_as_uint(red[0]));
+    }
 }
 
 // scratch[0] = 2^s, scratch[1] = 2^-s, with s chosen so max|V| 2^s < 2^14.
@@ -1383,18 +1389,20 @@ __global__ __launch_bounds__(256, 1) void transport_wide_kernel(TransportArgs a,
 // references (row_ref NULL) weighted every range against row_lse2.  With
 // lse_out, column 0 also writes the row's LSE2, Rb + log2(sum of the ranges'
 // weight sums brought to Rb).
-// Grid: x = row, y = blocks of 1024 columns; each thread 4 columns (16-byte
-// accesses when every row starts 16-byte aligned).  The row's range factors
-// and scale are computed once per thread, uniform over the block.
-__global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a) {
-    const int row = blockIdx.x;
+// Grid: x = groups of 256/tpr rows, y = blocks of 4*tpr columns; tpr threads
+// per row, each 4 columns (16-byte accesses when every row starts 16-byte
+// aligned).  The row's range factors and scale are computed once per thread.
+__global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a, int tpr) {
+    const int row = blockIdx.x * (256 / tpr) + threadIdx.x / tpr;
+    if (row >= a.n_rows) return;
+    const int t = threadIdx.x % tpr;
     float fac[kTransportMaxSplit];
     float Rb;
     if (a.row_ref) {
         Rb = -INFINITY;
         for (int s = 0; s < a.n_split; ++s) Rb = fmaxf(Rb, a.row_ref[(int64_t)s * a.n_rows + row]);
         for (int s = 0; s < a.n_split; ++s) fac[s] = ex2(a.row_ref[(int64_t)s * a.n_rows + row] - Rb);
-        if (a.lse_out && blockIdx.y == 0 && threadIdx.x == 0) {
+        if (a.lse_out && blockIdx.y == 0 && t == 0) {
             float T = 0.f;
             for (int s = 0; s < a.n_split; ++s) T += a.row_sum[(int64_t)s * a.n_rows + row] * fac[s];
             a.lse_out[row] = Rb + lg2(T);
@@ -1406,7 +1414,7 @@ __global__ __launch_bounds__(256) void transport_merge_kernel(TransportArgs a) {
     float sc = ex2(Rb + (a.row_pot[row] - a.row_nrm[row]) * a.c_bias);
     if (!a.divide_by_a) sc *= a.row_w[row];
     sc *= a.v_unscale_dev[0];
-    const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+    const int c = (blockIdx.y * tpr + t) * 4;
     if (c >= a.dv) return;
     const int64_t base = (int64_t)row * a.dv + c;
     const bool vec = (a.dv & 3) == 0 && (((uintptr_t)a.U | (uintptr_t)a.U_part) & 15) == 0;
@@ -1825,8 +1833,10 @@ hipError_t launch_transport(int path, const TransportArgs& a0, float* scratch, v
             }
         }
         if (e != hipSuccess || a.n_split == 1) return e;
-        const dim3 mgrid((unsigned)a.n_rows, (unsigned)((a.dv + 1023) / 1024));
-        transport_merge_kernel<<<mgrid, 256, 0, s>>>(a);
+        const int tpr = a.dv <= 256 ? 64 : (a.dv <= 512 ? 128 : 256);
+        const dim3 mgrid((unsigned)((a.n_rows + 256 / tpr - 1) / (256 / tpr)),
+                         (unsigned)((a.dv + 4 * tpr - 1) / (4 * tpr)));
+        transport_merge_kernel<<<mgrid, 256, 0, s>>>(a, tpr);
         return hipGetLastError();
     }
     if (path == PATH_MFMA_F32) return transport_mfma_dispatch<OP_F32>(ng, a, m_pad, s);
