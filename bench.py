@@ -114,9 +114,10 @@ def small_path_dtype(X, Y, a, b, f, g, eps: float) -> str:
     """The score arithmetic the d <= 8 matrix path takes, per half-step: fp16
     hi/lo splits of the products (fp32 accumulation) when its guard holds --
     c_score * max_i sum_c |x'_ic| * max_jc |y'_jc| <= 2^9 on centred points,
-    with every magnitude and key bias in the fp16 range -- else fp32
-    products.  Evaluated on the host from the inputs and the final
-    potentials, for the label of the line."""
+    with every magnitude and key bias in the fp16 range -- else bf16
+    three-part splits (d <= 4) or fp32 products (d > 4).  Evaluated on the
+    host from the inputs and the final potentials, for the label of the
+    line."""
     import numpy as np
 
     log2e = 1.4426950408889634
@@ -139,11 +140,12 @@ def small_path_dtype(X, Y, a, b, f, g, eps: float) -> str:
 
     f_side = split_ok(Xc, Yc, B, g, b)
     g_side = split_ok(Yc, Xc, A, f, a)
+    other = "bf16x3-split/f32-acc" if Xf.shape[1] <= 4 else "f32"
     if f_side and g_side:
         return "f16x3-split/f32-acc"
     if not f_side and not g_side:
-        return "f32"
-    return "f16x3-split/f32-acc (one side), f32 (other)"
+        return other
+    return "f16x3-split/f32-acc (one side), %s (other)" % other
 
 
 def block_sparse_run(w, eps, steps, warmup, dev, binding, torch):
@@ -761,11 +763,12 @@ def main_block_sparse(args, w, peak, unit, dtype, desc, binding, torch):
         "metric": METRIC, "value": it_s, "unit": "iters/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(10e3 / it_s, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16x3-split/f32-acc (f32 products in a pass whose guard fails)",
+        "dtype": "bf16x3-split/f32-acc (f16x3-split/f32-acc in a pass or row block whose "
+                 "fp16 guard holds)",
         "data": "synthetic",
         "config": {"workload": desc, "recipe": "fs2", "n": w.n, "m": w.m, "d": w.d,
                    "eps": w.eps, "delta": BS_DELTA, "iters_per_step": 10,
-                   "score_path": "fp32-small-mfma (block-sparse)"},
+                   "score_path": "small-mfma (block-sparse)"},
         "pair_evals_per_s": bs["kept_pairs_per_iter"] * it_s,
         "dense_equivalent_pair_evals_per_s": 2.0 * w.n * w.m * it_s,
         "clocks": sampler.summary(),

@@ -60,6 +60,7 @@ struct fs_problem {
     float* uref;      // its row references, weight sums, maxima [3][kTransportMaxSplit][n], flags [n]
     float* krec;      // small-d matrix path: key records of one pass (fp32)
     void* krec16;     //   fp16-split records (d <= 4)
+    void* krec3;      //   bf16 three-part records (d <= 4)
     void* kguard;     //   guard words of the packing
     // block-sparse form (fs_bs_attach): side 0 = rows X / keys Y (f-update),
     // side 1 = rows Y / keys X (g-update)
@@ -219,7 +220,7 @@ void choose_split(int path, int lse_dp, int64_t n_rows, int64_t n_keys, int& S_o
 
 struct Layout {
     size_t centre, bmin, bmax, flag, xops, yops, xops16, yops16, xn, xl, xw, yn, yl, yw, part, rpart, scal, ptmp,
-        vt, kbias, upart, uref, krec, krec16, kguard, rsx, rsy, lbias, ptag, total;
+        vt, kbias, upart, uref, krec, krec16, krec3, kguard, rsx, rsy, lbias, ptag, total;
 };
 
 Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
@@ -266,6 +267,7 @@ Layout make_layout(int64_t n, int64_t m, int d, int dv_max, const Shape& sh) {
     // (+32 records: the -inf sentinel block of the block-sparse form)
     L.krec = take(small ? small_f32_rec_bytes(d) * (kmax + 32) : 0);
     L.krec16 = take(small ? small_f16_rec_bytes(d) * (kmax + 32) : 0);
+    L.krec3 = take(small ? small_b3_rec_bytes(d) * (kmax + 32) : 0);
     L.kguard = take(small ? 32 : 0);  // packing guard [2], cloud L1 maxima [2]
     L.rsx = take(sizeof(float) * n);  // cosine cost: 1/|x_i|
     L.rsy = take(sizeof(float) * m);
@@ -357,6 +359,7 @@ LseArgs base_args(const fs_problem* p, bool f_side, float eps) {
     a.resid_part = p->resid_part;
     a.krec = p->krec;
     a.krec16 = p->krec16;
+    a.krec3 = p->krec3;
     a.krec_guard = p->kguard;
     a.krec_keys = (int)K.n_pad;
     a.row_l1 = R.l1max;
@@ -545,6 +548,7 @@ fs_status init_problem(fs_problem* p, const float* X, const float* Y, const floa
                   : nullptr;
     p->krec = sh.path == PATH_SMALL ? (float*)(w + L.krec) : nullptr;
     p->krec16 = sh.path == PATH_SMALL ? (void*)(w + L.krec16) : nullptr;
+    p->krec3 = sh.path == PATH_SMALL && small_b3_rec_bytes(d) ? (void*)(w + L.krec3) : nullptr;
     p->kguard = sh.path == PATH_SMALL ? (void*)(w + L.kguard) : nullptr;
     if (sh.path == PATH_SMALL) {
         p->X.l1max = (float*)(w + L.kguard) + 2;

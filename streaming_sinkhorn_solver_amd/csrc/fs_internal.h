@@ -72,9 +72,11 @@ struct LseArgs {
     float* resid_part;  // one partial per finalizing block
     float* resid_out;   // 1 float
     // PATH_SMALL (workspace): key records of this pass, fp32 [krec_keys][2*kp]
-    // and, for d <= 4, fp16-split [krec_keys][16]; two guard words.
+    // and, for d <= 4, fp16-split [krec_keys][16] and bf16 three-part
+    // [krec_keys][32]; two guard words.
     float* krec;
     void* krec16;
+    void* krec3;
     void* krec_guard;
     int krec_keys;      // records packed (the key cloud's padded count)
     const float* row_l1;  // largest L1 norm of a row point (device scalar)
@@ -254,6 +256,7 @@ int small_tile(int d);
 int small_rows_per_block();
 size_t small_f32_rec_bytes(int d);  // per key
 size_t small_f16_rec_bytes(int d);  // per key (0 if d > 4)
+size_t small_b3_rec_bytes(int d);   // per key (0 if d > 4)
 // Largest L1 norm over the (converted, fp32) points of a cloud into *out.
 hipError_t launch_row_l1max(const float* ops, int64_t n, int d, float* out, hipStream_t s);
 hipError_t launch_lse_small(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin);

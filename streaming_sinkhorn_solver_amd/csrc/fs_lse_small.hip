@@ -30,7 +30,15 @@
 //    only if c_score * max_i sum_c |x_ic| * max_jc |y_jc| <= 2^9 (f then moves
 //    by less than about 2e-4 eps from this error) and every bias fits fp16
 //    with margin; otherwise
-//  * fp32: A and B in fp32, ceil((d+1)/2) v_mfma_f32_32x32x2f32 per block.
+//  * bf16 three parts, d <= 4 (where the fp16 bound fails): every value split
+//    into three bf16 parts (v = v1 + v2 + v3 exactly: 24 significant bits,
+//    fp32's exponent range), the 32 contraction slots holding the six
+//    products x1y1, x1y2, x2y1, x1y3, x2y2, x3y1 per coordinate (the three
+//    dropped ones are below 2^-24 of x y) and b1, b2, b3: two
+//    v_mfma_f32_32x32x16_bf16 per block, with the error of the fp32 products
+//    and, unlike them, issued alongside the exponentials of other waves;
+//  * fp32 (d > 4): A and B in fp32, ceil((d+1)/2) v_mfma_f32_32x32x2f32 per
+//    block.
 //
 // R_i is only moved when a block's terms 2^(z2 - R) grow large (their sum
 // above 2^64, checked with one compare) or on the row's first block; the move
@@ -66,6 +74,7 @@ constexpr int kNbuf = 4;
 constexpr int small_tile_keys(int kp) { return kp <= 2 ? 512 : 256; }
 constexpr int f32_rec_bytes(int kp) { return 8 * kp; }
 constexpr int kF16RecBytes = 32;
+constexpr int kB3RecBytes = 64;  // bf16 three-part record: 32 slots
 
 // Guard words written by the packing: the bits of max |y_c| over all keys,
 // and nonzero if a bias or coordinate does not fit the fp16 format.
@@ -80,11 +89,23 @@ struct Guard {
 // fp16 record (d <= 4): slots 3c, 3c+1, 3c+2 hold yh_c, yl_c, yh_c; slots
 // 3d..3d+2 the parts bh, bm, bl of beta; the rest 0.  Padding keys (j >=
 // n_keys) get beta = -inf (bh = -inf, the other parts 0).
+// bf16 three-part record (d <= 4): slots 6c..6c+5 hold y1, y2, y1, y3, y2,
+// y1 of coordinate c (paired with the row's x1, x1, x2, x1, x2, x3), slots
+// 6d..6d+2 the parts of beta (paired with 1); the rest 0; padding keys get
+// b1 = -inf.
+__device__ __forceinline__ void split3_bf16(float v, __bf16& v1, __bf16& v2, __bf16& v3) {
+    v1 = (__bf16)v;
+    const float r1 = v - (float)v1;
+    v2 = (__bf16)r1;
+    v3 = (__bf16)(r1 - (float)v2);
+}
+
 template <int KP>
 __global__ __launch_bounds__(256) void pack_key_records_kernel(
     const float* __restrict__ keys, int stride, int d, int n_keys, int n_pad,
     const float* __restrict__ pot, const float* __restrict__ nrm, const float* __restrict__ lw2,
-    float c_bias, float* __restrict__ rec32, _Float16* __restrict__ rec16, Guard* guard) {
+    float c_bias, float* __restrict__ rec32, _Float16* __restrict__ rec16,
+    __bf16* __restrict__ rec3, Guard* guard) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const bool in = j < n_pad;
     const bool real = j < n_keys;
@@ -135,6 +156,34 @@ __global__ __launch_bounds__(256) void pack_key_records_kernel(
             uint4* o16 = (uint4*)(rec16 + (int64_t)j * 16);
             o16[0] = w0;
             o16[1] = w1;
+        }
+        if (rec3) {
+            __bf16 bv[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) bv[k] = (__bf16)0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (c < d) {
+                    __bf16 v1, v2, v3;
+                    split3_bf16(y[c], v1, v2, v3);
+                    bv[6 * c] = v1;
+                    bv[6 * c + 1] = v2;
+                    bv[6 * c + 2] = v1;
+                    bv[6 * c + 3] = v3;
+                    bv[6 * c + 4] = v2;
+                    bv[6 * c + 5] = v1;
+                }
+            }
+            if (real) {
+                split3_bf16(beta, bv[6 * d], bv[6 * d + 1], bv[6 * d + 2]);
+            } else {
+                bv[6 * d] = (__bf16)(-INFINITY);
+            }
+            uint4 w[4];
+            __builtin_memcpy(&w[0], &bv[0], 64);
+            uint4* o3 = (uint4*)(rec3 + (int64_t)j * 32);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o3[q] = w[q];
         }
     }
     if (rec16) {
@@ -201,7 +250,8 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     constexpr int RING_BYTES = kNbuf * BUF_BYTES;
     static_assert(!SHIFT || TK == W * 64, "shifted conversion: one key per thread");
     __shared__ __attribute__((aligned(16))) uint4 tbuf[RING_BYTES / 16];
-    __shared__ __attribute__((aligned(16))) uint4 ibuf[SPARSE ? 64 : 1];  // sparse: starting block
+    // sparse: the starting block (2 KiB: a bf16 three-part block)
+    __shared__ __attribute__((aligned(16))) uint4 ibuf[SPARSE ? 128 : 1];
     __shared__ float red[16];
 
     const int tid = threadIdx.x;
@@ -402,16 +452,24 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     };
 
     // The tile loop for one operand format: MODE 0 fp32 records, 1 fp16-split
-    // records, 2 (sparse) fp32 records turned into shifted fp16 ones in LDS.
+    // records, 2 (sparse) fp32 records turned into shifted fp16 ones in LDS,
+    // 3 bf16 three-part records.  A ring tile holds SK keys: TK, or half a
+    // tile of TK keys for the 64-byte bf16 records (splits and the sparse
+    // form's list tiles stay whole tiles of TK keys).
     auto run = [&](auto mode_c) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_c)::value;
-        constexpr bool F16 = MODE != 0;
+        constexpr bool F16 = MODE == 1 || MODE == 2;
+        constexpr bool B3 = MODE == 3;
         constexpr bool CONV = MODE == 2;
-        constexpr int REC_BYTES = F16 ? kF16RecBytes : f32_rec_bytes(KP);  // as multiplied
-        constexpr int DREC_BYTES = MODE == 1 ? kF16RecBytes : f32_rec_bytes(KP);  // as loaded
-        constexpr int TILE_BYTES = TK * DREC_BYTES;
+        constexpr int REC_BYTES =  // as multiplied
+            B3 ? kB3RecBytes : (F16 ? kF16RecBytes : f32_rec_bytes(KP));
+        constexpr int DREC_BYTES =  // as loaded
+            B3 ? kB3RecBytes : (MODE == 1 ? kF16RecBytes : f32_rec_bytes(KP));
+        constexpr int SK = B3 ? TK / 2 : TK;
+        constexpr int HALVES = TK / SK;
+        constexpr int TILE_BYTES = SK * DREC_BYTES;
         // ring of this format: NB slots of SLOT bytes (+ the conversion area)
-        constexpr int NB = !SPARSE ? kNbuf : (MODE == 1 ? kNbuf : (MODE == 0 ? 8 : 6));
+        constexpr int NB = !SPARSE ? kNbuf : (MODE == 1 || B3 ? kNbuf : (MODE == 0 ? 8 : 6));
         constexpr int SLOT = !SPARSE ? BUF_BYTES : TILE_BYTES;
         constexpr int CONV_BYTES = TK * kF16RecBytes;
         static_assert(NB * SLOT + (CONV ? CONV_BYTES : 0) <= RING_BYTES, "ring fits");
@@ -420,11 +478,13 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         constexpr int TILE_INSTR = TILE_BYTES / 1024;  // wave-wide 1 KiB loads per tile
         constexpr int INSTR_PER_WAVE = (TILE_INSTR + W - 1) / W;
         constexpr int MIN_INSTR = TILE_INSTR / W;
-        constexpr int SUB = TK / 32;                   // 32-key blocks per tile
+        constexpr int SUB = SK / 32;                   // 32-key blocks per ring tile
         static_assert(TILE_BYTES % 1024 == 0 && TILE_BYTES <= BUF_BYTES, "tile geometry");
         const char* __restrict__ recs =
-            MODE == 1 ? (const char*)a.krec16 + (int64_t)j0 * DREC_BYTES
-                      : (const char*)a.krec + (int64_t)j0 * DREC_BYTES;
+            B3          ? (const char*)a.krec3 + (int64_t)j0 * DREC_BYTES
+            : MODE == 1 ? (const char*)a.krec16 + (int64_t)j0 * DREC_BYTES
+                        : (const char*)a.krec + (int64_t)j0 * DREC_BYTES;
+        const int ntl = ntiles * HALVES;  // ring tiles
 
         // tile k -> slot (contiguous copy; records past j1 in the last tile
         // are padding records of score -inf: splits are whole tiles)
@@ -434,7 +494,18 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             for (int l = 0; l < INSTR_PER_WAVE; ++l) {
                 const int L = l * W + wave;
                 if (TILE_INSTR % W == 0 || L < TILE_INSTR) {
-                    if constexpr (SPARSE) {
+                    if constexpr (SPARSE && B3) {
+                        // 2 KiB blocks: instruction L covers half L % 2 of block
+                        // L / 2 of the ring tile, which is half k % 2 of list tile k / 2
+                        int ent[1];
+                        sload_words<1>(lst + (k / HALVES) * list_step + (k % HALVES) * SUB + L / 2,
+                                       ent);
+                        const uint32_t Jc = min((uint32_t)ent[0], (uint32_t)a.bs_sentinel);
+                        dma_to_lds16(recs,
+                                     Jc * (uint32_t)(32 * DREC_BYTES) + (uint32_t)(L & 1) * 1024u +
+                                         lane16,
+                                     ring + slot * SLOT + L * 1024);
+                    } else if constexpr (SPARSE) {
                         // instruction L covers blocks L*BPI .. L*BPI+BPI-1 of the tile;
                         // lane `lane` fetches 16 bytes of block L*BPI + lane/LPB
                         constexpr int BLK = 32 * DREC_BYTES;
@@ -460,23 +531,55 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         if constexpr (SPARSE) {
             // the block of largest bound, for the starting reference
             if (ntiles > 0 && wave == 0) {
-                constexpr int LPB = 64 / (1024 / (32 * DREC_BYTES));
                 int ent[1];
                 sload_words<1>(a.bs_best + row_block, ent);
                 const uint32_t Jc = min((uint32_t)ent[0], (uint32_t)a.bs_sentinel);
-                dma_to_lds16(recs, Jc * (uint32_t)(32 * DREC_BYTES) + (uint32_t)(lane % LPB) * 16u,
-                             &ibuf[0]);
+                if constexpr (B3) {
+                    dma_to_lds16(recs, Jc * (uint32_t)(32 * DREC_BYTES) + lane16, &ibuf[0]);
+                    dma_to_lds16(recs, Jc * (uint32_t)(32 * DREC_BYTES) + 1024u + lane16, &ibuf[64]);
+                } else {
+                    constexpr int LPB = 64 / (1024 / (32 * DREC_BYTES));
+                    dma_to_lds16(recs,
+                                 Jc * (uint32_t)(32 * DREC_BYTES) + (uint32_t)(lane % LPB) * 16u,
+                                 &ibuf[0]);
+                }
             }
         }
-        if (ntiles > 0) {
+        if (ntl > 0) {
 #pragma unroll
-            for (int k = 0; k < NB - 1; ++k) issue_tile(min(k, ntiles - 1), k);
+            for (int k = 0; k < NB - 1; ++k) issue_tile(min(k, ntl - 1), k);
         }
 
         // B operand of this lane: row `row`, the lane half's contraction slots
         f16x8 b16;
         float b32[KP];
-        if constexpr (F16) {
+        bf16x8 b3a, b3b;  // bf16 three-part: slots 8h.. of each 16-slot product
+        if constexpr (B3) {
+            __bf16 sl[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) sl[k] = (__bf16)0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (c < d) {
+                    __bf16 x1, x2, x3;
+                    split3_bf16(r[c], x1, x2, x3);
+                    sl[6 * c] = x1;
+                    sl[6 * c + 1] = x1;
+                    sl[6 * c + 2] = x2;
+                    sl[6 * c + 3] = x1;
+                    sl[6 * c + 4] = x2;
+                    sl[6 * c + 5] = x3;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                if (k >= 6 * d && k < 6 * d + 3) sl[k] = (__bf16)1.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                b3a[k] = h ? sl[8 + k] : sl[k];
+                b3b[k] = h ? sl[24 + k] : sl[16 + k];
+            }
+        } else if constexpr (F16) {
             _Float16 sl[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) sl[k] = (_Float16)0.f;
@@ -503,7 +606,13 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             }
         }
         auto scores = [&](const char* rb, f32x16& acc) __attribute__((always_inline)) {
-            if constexpr (F16) {
+            if constexpr (B3) {
+                const char* kr = rb + (size_t)ln * REC_BYTES + h * 16;
+                const bf16x8 a0 = *(const bf16x8*)kr;
+                const bf16x8 a1 = *(const bf16x8*)(kr + 32);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b3a, cm, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b3b, acc, 0, 0, 0);
+            } else if constexpr (F16) {
                 const f16x8 av = *(const f16x8*)(rb + (size_t)ln * REC_BYTES + h * 16);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b16, cm, 0, 0, 0);
             } else {
@@ -536,9 +645,9 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             R = t > -INFINITY ? t : 0.f;
         }
 
-        for (int t = 0; t < ntiles; ++t) {
+        for (int t = 0; t < ntl; ++t) {
             const int slot = t % NB;
-            issue_tile(min(t + NB - 1, ntiles - 1), (t + NB - 1) % NB);
+            issue_tile(min(t + NB - 1, ntl - 1), (t + NB - 1) % NB);
             const char* tb = ring + slot * SLOT;
             if constexpr (CONV) {
                 convert(tb, TK, conv, conv + (TK / 2) * kF16RecBytes);
@@ -576,14 +685,14 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     };
     if constexpr (SPARSE) {
         // the pass-wide fp16 records when they hold (no conversion), else the
-        // shifted ones when this row block allows them, else fp32
+        // shifted ones when this row block allows them, else bf16 three-part
         if constexpr (SHIFT) {
             if (use16) {
                 run(std::integral_constant<int, 1>{});
             } else if (shifted) {
                 run(std::integral_constant<int, 2>{});
             } else {
-                run(std::integral_constant<int, 0>{});
+                run(std::integral_constant<int, 3>{});
             }
         } else {
             run(std::integral_constant<int, 0>{});
@@ -592,7 +701,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         if (use16)
             run(std::integral_constant<int, 1>{});
         else
-            run(std::integral_constant<int, 0>{});
+            run(std::integral_constant<int, 3>{});
     } else {
         run(std::integral_constant<int, 0>{});
     }
@@ -629,7 +738,8 @@ hipError_t small_launch(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
     if (f16 && (e = launch_fill((float*)a.krec_guard, 2, 0.f, s)) != hipSuccess) return e;
     pack_key_records_kernel<KP><<<(n_pad_keys + 255) / 256, 256, 0, s>>>(
         (const float*)a.keys, a.dp <= 4 ? 4 : 8, a.dp, a.n_keys, n_pad_keys, a.key_pot, a.key_nrm,
-        a.key_lw2, a.c_bias, a.krec, f16 ? (_Float16*)a.krec16 : nullptr, (Guard*)a.krec_guard);
+        a.key_lw2, a.c_bias, a.krec, f16 ? (_Float16*)a.krec16 : nullptr,
+        f16 ? (__bf16*)a.krec3 : nullptr, (Guard*)a.krec_guard);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
     const dim3 grid = SPARSE ? dim3(a.bs_grid, 1)
@@ -667,6 +777,7 @@ int small_tile(int d) { return small_tile_keys(small_kp(d)); }
 int small_rows_per_block() { return kSmallWaves * 32; }
 size_t small_f32_rec_bytes(int d) { return (size_t)f32_rec_bytes(small_kp(d)); }
 size_t small_f16_rec_bytes(int d) { return small_kp(d) <= 2 ? (size_t)kF16RecBytes : 0; }
+size_t small_b3_rec_bytes(int d) { return small_kp(d) <= 2 ? (size_t)kB3RecBytes : 0; }
 
 hipError_t launch_lse_small_sparse(const LseArgs& a, hipStream_t s, hipEvent_t ev_begin) {
     if (a.n_split < 2 || !a.bs_list || !a.bs_count || !a.part || !a.bs_nsplit || !a.bs_map ||
