@@ -65,6 +65,11 @@ constexpr float kBigSum = 0x1p64f;    // common path: a block's terms sum to at 
 // the best block's maximum, which at small eps may sit tens of bits under
 // the row maximum, and should not move for that.
 constexpr float kBigSumSparse = 0x1p96f;
+// ... and its references sit 2^64 above the block maxima they start from or
+// move to, so that a row may lie 160 bits above its start before it moves.
+// Terms more than 126 - 64 = 62 bits under the row maximum may flush to zero:
+// with at most 2^27 of them that is under 2^-35 of the sum.
+constexpr float kSparseLift = 64.f;
 constexpr float kF16Bound = 512.f;    // fp16 format: sum_c |c x_c| * max|y| <= this
 constexpr float kF16Range = 16384.f;  // fp16 format: |c x|, |y| <= this, |beta| <= twice it
 constexpr int kNbuf = 4;
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         if (__builtin_amdgcn_ballot_w64(!(e[0] <= (SPARSE ? kBigSumSparse : kBigSum)) ||
                                         dlt != 0.f)) {
             const float t = block_max(acc) - dlt;  // block maximum relative to R
-            const float dl = t > kSlack ? t : 0.f;
+            const float dl = t > kSlack ? t + (SPARSE ? kSparseLift : 0.f) : 0.f;
             const float sh = dlt + dl;
 #pragma unroll
             for (int q = 0; q < 16; ++q) e[q] = ex2(acc[q] - sh);
@@ -391,7 +396,10 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             for (int w = 1; w < 16; w <<= 1)
 #pragma unroll
                 for (int q = 0; q < 16; q += 2 * w) e[q] += e[q + w];
-            s = s * ex2(-dl) + e[0];
+            // the old sum, scaled in two halves: 2^-dl alone may flush to
+            // zero (dl > 126) where the scaled sum is still a normal float
+            const float hf = ex2(-0.5f * dl);
+            s = s * hf * hf + e[0];
             R += dl;
             if constexpr (REBAKE) {
 #pragma unroll
@@ -629,8 +637,9 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
 
         // R starts at the maximum of the first 32-key block (finite wherever
         // the lane sees a key at all; a lane that never does keeps s = 0, the
-        // empty state); in the sparse form, of the block of largest bound,
-        // whose scores are near the row maxima, so that R rarely moves.
+        // empty state); in the sparse form, kSparseLift above that of the
+        // block of largest bound, whose scores are near the row maxima, so
+        // that R rarely moves.
         if (ntiles > 0) {
             f32x16 acc;
             if constexpr (CONV) {
@@ -642,7 +651,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
                 scores(SPARSE ? (const char*)&ibuf[0] : ring, acc);
             }
             const float t = block_max(acc);
-            R = t > -INFINITY ? t : 0.f;
+            R = t > -INFINITY ? t + (SPARSE ? kSparseLift : 0.f) : 0.f;
         }
 
         for (int t = 0; t < ntl; ++t) {
@@ -706,6 +715,15 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         run(std::integral_constant<int, 0>{});
     }
 
+    // The sum's binary exponent moves into the reference (s in [1/2, 1)), so
+    // that the merges below, which scale a sum by 2^(M - M_max), see M near
+    // the row's log-sum: a reference far under it with a large sum (the
+    // sparse form's rows that do not move) would otherwise underflow there.
+    if (s > 0.f) {
+        int ex;
+        s = frexpf(s, &ex);
+        R += (float)ex;
+    }
     // the two lane halves hold the same row over disjoint keys
     float M = s > 0.f ? R + rowc : -INFINITY;
     {
