@@ -396,10 +396,16 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             for (int w = 1; w < 16; w <<= 1)
 #pragma unroll
                 for (int q = 0; q < 16; q += 2 * w) e[q] += e[q + w];
-            // the old sum, scaled in two halves: 2^-dl alone may flush to
-            // zero (dl > 126) where the scaled sum is still a normal float
-            const float hf = ex2(-0.5f * dl);
-            s = s * hf * hf + e[0];
+            if constexpr (SPARSE) {
+                // the old sum, scaled in two halves: 2^-dl alone may flush to
+                // zero (dl > 126) where the scaled sum is still a normal
+                // float (a lifted reference moves that far; the dense form's
+                // moves stay under 2^64 + 2^8 and its sums under 2^91)
+                const float hf = ex2(-0.5f * dl);
+                s = s * hf * hf + e[0];
+            } else {
+                s = s * ex2(-dl) + e[0];
+            }
             R += dl;
             if constexpr (REBAKE) {
 #pragma unroll
@@ -632,8 +638,15 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             }
         };
 
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // The first NB - 1 tiles are in flight.  The sparse form waits here
+        // only for its starting block (issued before them), the dense form
+        // for tile 0, which holds its starting block; the barriers below do
+        // not fence, so the copies behind keep streaming meanwhile.
+        if constexpr (MIN_INSTR == 0)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - (SPARSE ? 1 : 2)) * MIN_INSTR) : "memory");
+        stage_barrier();
 
         // R starts at the maximum of the first 32-key block (finite wherever
         // the lane sees a key at all; a lane that never does keeps s = 0, the
@@ -644,14 +657,22 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             f32x16 acc;
             if constexpr (CONV) {
                 convert((const char*)&ibuf[0], 32, conv, conv);
-                __syncthreads();
+                stage_barrier();
                 scores(conv, acc);
-                __syncthreads();  // rewritten by the first tile's conversion
+                stage_barrier();  // rewritten by the first tile's conversion
             } else {
                 scores(SPARSE ? (const char*)&ibuf[0] : ring, acc);
             }
             const float t = block_max(acc);
             R = t > -INFINITY ? t + (SPARSE ? kSparseLift : 0.f) : 0.f;
+        }
+        if constexpr (SPARSE) {
+            // tile 0 (tiles 1 .. NB-2 may still be in flight)
+            if constexpr (MIN_INSTR == 0)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * MIN_INSTR) : "memory");
+            stage_barrier();
         }
 
         for (int t = 0; t < ntl; ++t) {
@@ -719,7 +740,9 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
     // that the merges below, which scale a sum by 2^(M - M_max), see M near
     // the row's log-sum: a reference far under it with a large sum (the
     // sparse form's rows that do not move) would otherwise underflow there.
-    if (s > 0.f) {
+    // (The dense form's sums stay under 2^91: what such a merge could lose
+    // there is under 2^-35 of the row's sum.)
+    if (SPARSE && s > 0.f) {
         int ex;
         s = frexpf(s, &ex);
         R += (float)ex;
