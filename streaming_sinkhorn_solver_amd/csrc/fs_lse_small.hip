@@ -239,20 +239,25 @@ __device__ __forceinline__ void sload_words(const int* p, int (&o)[N]) {
 // whole blocks at per-lane offsets.  With n_split = S the list's tiles are
 // dealt round-robin to S workgroups (partials merged as for key ranges).
 template <int KP, bool SPARSE = false>
-__global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs a) {
+__global__ __launch_bounds__(kSmallWaves * 64, SPARSE ? 6 : 2) void lse_small_kernel(LseArgs a) {
     constexpr int W = kSmallWaves;
     constexpr bool HAS_F16 = KP <= 2;  // the fp16 format covers d <= 4
     constexpr int TK = small_tile_keys(KP);
     constexpr int F32_TILE = TK * f32_rec_bytes(KP);
     constexpr int F16_TILE = HAS_F16 ? TK * kF16RecBytes : 0;
-    // The tile ring is kNbuf slots of the larger tile.  The sparse form, whose
+    // The tile ring is kNbuf slots of the larger tile (three in the sparse
+    // form, below), cut per record format in run(): the sparse form, whose
     // tiles are gathered from scattered blocks and wait longer for their
     // copies, cuts the same bytes into more slots when its tiles are fp32
-    // records (8 slots; 6 slots and a conversion area for the shifted fp16
-    // operands, see run()).
+    // records (6 slots; 4 slots and a conversion area for the shifted fp16
+    // operands).
     constexpr int BUF_BYTES = F16_TILE > F32_TILE ? F16_TILE : F32_TILE;
     constexpr bool SHIFT = SPARSE && HAS_F16;
-    constexpr int RING_BYTES = kNbuf * BUF_BYTES;
+    // The sparse form runs three workgroups per CU (six waves per SIMD, 80
+    // registers each): more waves to cover its gathered copies and the
+    // start-up of its short workgroups than a deeper ring would (fs2 launch
+    // 0.369 -> 0.329 ms), so its ring is three slots of the larger tile.
+    constexpr int RING_BYTES = (SPARSE ? 3 : kNbuf) * BUF_BYTES;
     static_assert(!SHIFT || TK == W * 64, "shifted conversion: one key per thread");
     __shared__ __attribute__((aligned(16))) uint4 tbuf[RING_BYTES / 16];
     // sparse: the starting block (2 KiB: a bf16 three-part block)
@@ -483,7 +488,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
         constexpr int HALVES = TK / SK;
         constexpr int TILE_BYTES = SK * DREC_BYTES;
         // ring of this format: NB slots of SLOT bytes (+ the conversion area)
-        constexpr int NB = !SPARSE ? kNbuf : (MODE == 1 || B3 ? kNbuf : (MODE == 0 ? 8 : 6));
+        constexpr int NB = !SPARSE ? kNbuf : (MODE == 1 || B3 ? 3 : (MODE == 0 ? 6 : 4));
         constexpr int SLOT = !SPARSE ? BUF_BYTES : TILE_BYTES;
         constexpr int CONV_BYTES = TK * kF16RecBytes;
         static_assert(NB * SLOT + (CONV ? CONV_BYTES : 0) <= RING_BYTES, "ring fits");
@@ -690,6 +695,16 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
             for (int q = 0; q < 16; ++q) cm[q] = -R;
             delta = 0.f;
             baked = R;
+            if constexpr (SPARSE) {
+                // one accumulator set (the other waves of the SIMD hide the
+                // matrix latency; two sets spill at 80 registers)
+#pragma unroll
+                for (int u = 0; u < SUB; ++u) {
+                    f32x16 acc;
+                    scores(blk(u), acc);
+                    epilogue(acc, baked, std::integral_constant<bool, MODE != 1>{});
+                }
+            } else {
             f32x16 acc0, acc1;
             scores(blk(0), acc0);
             float b0 = baked, b1;
@@ -703,6 +718,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 2) void lse_small_kernel(LseArgs 
                     b0 = baked;
                 }
                 epilogue(acc1, b1, std::integral_constant<bool, SPARSE && MODE != 1>{});
+            }
             }
             // tiles issued after tile t+1: t+2 .. t+NB-1
             if constexpr (MIN_INSTR == 0)
