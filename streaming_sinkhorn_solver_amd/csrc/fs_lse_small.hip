@@ -72,7 +72,7 @@ constexpr float kBigSumSparse = 0x1p96f;
 constexpr float kSparseLift = 64.f;
 constexpr float kF16Bound = 512.f;    // fp16 format: sum_c |c x_c| * max|y| <= this
 constexpr float kF16Range = 16384.f;  // fp16 format: |c x|, |y| <= this, |beta| <= twice it
-constexpr int kNbuf = 4;
+constexpr int kNbuf = 3;
 
 // Keys per streamed tile (splits are whole tiles): fp32 records are 2*KP
 // floats (8 KiB tiles for KP <= 2); fp16 records are 32 bytes.
@@ -239,25 +239,26 @@ __device__ __forceinline__ void sload_words(const int* p, int (&o)[N]) {
 // whole blocks at per-lane offsets.  With n_split = S the list's tiles are
 // dealt round-robin to S workgroups (partials merged as for key ranges).
 template <int KP, bool SPARSE = false>
-__global__ __launch_bounds__(kSmallWaves * 64, SPARSE ? 6 : 2) void lse_small_kernel(LseArgs a) {
+__global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs a) {
     constexpr int W = kSmallWaves;
     constexpr bool HAS_F16 = KP <= 2;  // the fp16 format covers d <= 4
     constexpr int TK = small_tile_keys(KP);
     constexpr int F32_TILE = TK * f32_rec_bytes(KP);
     constexpr int F16_TILE = HAS_F16 ? TK * kF16RecBytes : 0;
-    // The tile ring is kNbuf slots of the larger tile (three in the sparse
-    // form, below), cut per record format in run(): the sparse form, whose
+    // The tile ring is kNbuf slots of the larger tile, cut per record
+    // format in run(): the sparse form, whose
     // tiles are gathered from scattered blocks and wait longer for their
     // copies, cuts the same bytes into more slots when its tiles are fp32
     // records (6 slots; 4 slots and a conversion area for the shifted fp16
     // operands).
     constexpr int BUF_BYTES = F16_TILE > F32_TILE ? F16_TILE : F32_TILE;
     constexpr bool SHIFT = SPARSE && HAS_F16;
-    // The sparse form runs three workgroups per CU (six waves per SIMD, 80
-    // registers each): more waves to cover its gathered copies and the
-    // start-up of its short workgroups than a deeper ring would (fs2 launch
-    // 0.369 -> 0.329 ms), so its ring is three slots of the larger tile.
-    constexpr int RING_BYTES = (SPARSE ? 3 : kNbuf) * BUF_BYTES;
+    // Three workgroups per CU (six waves per SIMD, 80 registers each): more
+    // waves to cover the copies (gathered, in the sparse form) and the
+    // start-up of short workgroups than a deeper ring would (fs2 launch 0.369
+    // -> 0.329 ms, C5 half-step 5.48 -> 5.33 ms), so the ring is three slots
+    // of the larger tile.
+    constexpr int RING_BYTES = kNbuf * BUF_BYTES;
     static_assert(!SHIFT || TK == W * 64, "shifted conversion: one key per thread");
     __shared__ __attribute__((aligned(16))) uint4 tbuf[RING_BYTES / 16];
     // sparse: the starting block (2 KiB: a bf16 three-part block)
@@ -372,8 +373,8 @@ __global__ __launch_bounds__(kSmallWaves * 64, SPARSE ? 6 : 2) void lse_small_ke
     // which moves R, where needed, to the block maximum.  Only per-lane
     // scalars change, so the common path carries no register-tuple copies.
     // REBAKE: bk is the reference baked into cm when acc's matrix instruction
-    // was issued, and a move re-bakes cm, so that only the block already in
-    // flight takes the slow path; taken by the sparse form's formats that
+    // was issued, and a move re-bakes cm, so that the blocks after it take
+    // the common path again; taken by the sparse form's formats that
     // serve small eps, whose rows move often (their start is shared by 256
     // rows).  Otherwise one baked reference per tile, R minus it in delta (a
     // loop-invariant cm keeps the common path free of register-tuple copies).
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, SPARSE ? 6 : 2) void lse_small_ke
         constexpr int HALVES = TK / SK;
         constexpr int TILE_BYTES = SK * DREC_BYTES;
         // ring of this format: NB slots of SLOT bytes (+ the conversion area)
-        constexpr int NB = !SPARSE ? kNbuf : (MODE == 1 || B3 ? 3 : (MODE == 0 ? 6 : 4));
+        constexpr int NB = !SPARSE || MODE == 1 || B3 ? kNbuf : (MODE == 0 ? 6 : 4);
         constexpr int SLOT = !SPARSE ? BUF_BYTES : TILE_BYTES;
         constexpr int CONV_BYTES = TK * kF16RecBytes;
         static_assert(NB * SLOT + (CONV ? CONV_BYTES : 0) <= RING_BYTES, "ring fits");
@@ -695,30 +696,14 @@ __global__ __launch_bounds__(kSmallWaves * 64, SPARSE ? 6 : 2) void lse_small_ke
             for (int q = 0; q < 16; ++q) cm[q] = -R;
             delta = 0.f;
             baked = R;
-            if constexpr (SPARSE) {
-                // one accumulator set (the other waves of the SIMD hide the
-                // matrix latency; two sets spill at 80 registers)
+            // one accumulator set per wave: the other waves of the SIMD hide
+            // the matrix latency (six per SIMD, 80 registers each; a second
+            // set spilled at that budget)
 #pragma unroll
-                for (int u = 0; u < SUB; ++u) {
-                    f32x16 acc;
-                    scores(blk(u), acc);
-                    epilogue(acc, baked, std::integral_constant<bool, MODE != 1>{});
-                }
-            } else {
-            f32x16 acc0, acc1;
-            scores(blk(0), acc0);
-            float b0 = baked, b1;
-#pragma unroll
-            for (int u = 0; u < SUB; u += 2) {
-                scores(blk(u + 1), acc1);
-                b1 = baked;
-                epilogue(acc0, b0, std::integral_constant<bool, SPARSE && MODE != 1>{});
-                if (u + 2 < SUB) {
-                    scores(blk(u + 2), acc0);
-                    b0 = baked;
-                }
-                epilogue(acc1, b1, std::integral_constant<bool, SPARSE && MODE != 1>{});
-            }
+            for (int u = 0; u < SUB; ++u) {
+                f32x16 acc;
+                scores(blk(u), acc);
+                epilogue(acc, baked, std::integral_constant<bool, SPARSE && MODE != 1>{});
             }
             // tiles issued after tile t+1: t+2 .. t+NB-1
             if constexpr (MIN_INSTR == 0)
