@@ -232,6 +232,14 @@ __device__ __forceinline__ void sload_words(const int* p, int (&o)[N]) {
     }
 }
 
+// Word at a wave-uniform address, read through the constant address space:
+// a scalar load whose wait the compiler places before the first use, so it
+// can be issued a tile early (the vector-memory counter still counts only
+// tile copies: the kernel checks in its ISA that no vector load is emitted).
+__device__ __forceinline__ int cload(const int* p) {
+    return *(const __attribute__((address_space(4))) int*)p;
+}
+
 // SPARSE: the block-sparse form.  The workgroup's keys are not a contiguous
 // range but the 32-key blocks listed for its row block by the screening
 // (LseArgs::bs_list, padded to whole tiles with a block of -inf records);
@@ -506,38 +514,49 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
                         : (const char*)a.krec + (int64_t)j0 * DREC_BYTES;
         const int ntl = ntiles * HALVES;  // ring tiles
 
+        // sparse: the list words of ring tile k that this wave's copies need
+        // (one per instruction of 2 KiB bf16 three-part blocks, BPI per
+        // instruction otherwise), read a tile ahead of their copies
+        constexpr int BLK = 32 * DREC_BYTES;
+        constexpr int BPI = !SPARSE || B3 ? 1 : 1024 / BLK;
+        static_assert(!SPARSE || B3 || 1024 % BLK == 0, "whole blocks per instruction");
+        auto tile_words = [&](int k, int (&w)[INSTR_PER_WAVE][BPI]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int l = 0; l < INSTR_PER_WAVE; ++l) {
+                const int L = l * W + wave;
+#pragma unroll
+                for (int q = 0; q < BPI; ++q) {
+                    // B3: instruction L covers half L % 2 of block L / 2 of the
+                    // ring tile, which is half k % 2 of list tile k / 2
+                    const int off = B3 ? (k / HALVES) * list_step + (k % HALVES) * SUB + L / 2
+                                       : k * list_step + L * BPI + q;
+                    w[l][q] = (TILE_INSTR % W == 0 || L < TILE_INSTR) ? cload(lst + off) : 0;
+                }
+            }
+        };
         // tile k -> slot (contiguous copy; records past j1 in the last tile
-        // are padding records of score -inf: splits are whole tiles)
+        // are padding records of score -inf: splits are whole tiles); the
+        // sparse form's copies take the list words of their tile
         const uint32_t lane16 = (uint32_t)lane * 16u;
-        auto issue_tile = [&](int k, int slot) __attribute__((always_inline)) {
+        auto issue_tile = [&](int k, int slot, const int (&w)[INSTR_PER_WAVE][BPI])
+                              __attribute__((always_inline)) {
 #pragma unroll
             for (int l = 0; l < INSTR_PER_WAVE; ++l) {
                 const int L = l * W + wave;
                 if (TILE_INSTR % W == 0 || L < TILE_INSTR) {
                     if constexpr (SPARSE && B3) {
-                        // 2 KiB blocks: instruction L covers half L % 2 of block
-                        // L / 2 of the ring tile, which is half k % 2 of list tile k / 2
-                        int ent[1];
-                        sload_words<1>(lst + (k / HALVES) * list_step + (k % HALVES) * SUB + L / 2,
-                                       ent);
-                        const uint32_t Jc = min((uint32_t)ent[0], (uint32_t)a.bs_sentinel);
+                        const uint32_t Jc = min((uint32_t)w[l][0], (uint32_t)a.bs_sentinel);
                         dma_to_lds16(recs,
-                                     Jc * (uint32_t)(32 * DREC_BYTES) + (uint32_t)(L & 1) * 1024u +
-                                         lane16,
+                                     Jc * (uint32_t)BLK + (uint32_t)(L & 1) * 1024u + lane16,
                                      ring + slot * SLOT + L * 1024);
                     } else if constexpr (SPARSE) {
                         // instruction L covers blocks L*BPI .. L*BPI+BPI-1 of the tile;
                         // lane `lane` fetches 16 bytes of block L*BPI + lane/LPB
-                        constexpr int BLK = 32 * DREC_BYTES;
-                        constexpr int BPI = 1024 / BLK;
                         constexpr int LPB = 64 / BPI;
-                        static_assert(1024 % BLK == 0, "whole blocks per instruction");
-                        int ent[BPI];
-                        sload_words<BPI>(lst + k * list_step + L * BPI, ent);
-                        int J = ent[0];
+                        int J = w[l][0];
 #pragma unroll
                         for (int q = 1; q < BPI; ++q)
-                            if (lane / LPB == q) J = ent[q];
+                            if (lane / LPB == q) J = w[l][q];
                         const uint32_t Jc = min((uint32_t)J, (uint32_t)a.bs_sentinel);
                         dma_to_lds16(recs, Jc * (uint32_t)BLK + (uint32_t)(lane % LPB) * 16u,
                                      ring + slot * SLOT + L * 1024);
@@ -548,6 +567,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
                 }
             }
         };
+        int wnext[INSTR_PER_WAVE][BPI];  // sparse: words of the next tile to copy
         if constexpr (SPARSE) {
             // the block of largest bound, for the starting reference
             if (ntiles > 0 && wave == 0) {
@@ -567,7 +587,11 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
         }
         if (ntl > 0) {
 #pragma unroll
-            for (int k = 0; k < NB - 1; ++k) issue_tile(min(k, ntl - 1), k);
+            for (int k = 0; k < NB - 1; ++k) {
+                if constexpr (SPARSE) tile_words(min(k, ntl - 1), wnext);
+                issue_tile(min(k, ntl - 1), k, wnext);
+            }
+            if constexpr (SPARSE) tile_words(min(NB - 1, ntl - 1), wnext);
         }
 
         // B operand of this lane: row `row`, the lane half's contraction slots
@@ -683,7 +707,8 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
 
         for (int t = 0; t < ntl; ++t) {
             const int slot = t % NB;
-            issue_tile(min(t + NB - 1, ntl - 1), (t + NB - 1) % NB);
+            issue_tile(min(t + NB - 1, ntl - 1), (t + NB - 1) % NB, wnext);
+            if constexpr (SPARSE) tile_words(min(t + NB, ntl - 1), wnext);
             const char* tb = ring + slot * SLOT;
             if constexpr (CONV) {
                 convert(tb, TK, conv, conv + (TK / 2) * kF16RecBytes);
