@@ -72,6 +72,29 @@ def test_small_d_wide_score_range(fs, prec, path):
     assert max_err(host(g), ref["g"]) <= TOL_FP32 * w.eps
 
 
+@pytest.mark.parametrize("d", [1, 2, 3, 4])
+def test_small_d_three_part_format(fs, d):
+    # A small eps on unit-variance clouds: the fp16 split's bound (c_score
+    # times the largest row sum of |x| times the largest |y|, under 2^9 on
+    # centred points) fails for any centring, so d <= 4 takes the bf16
+    # three-part records (six products per coordinate, two bf16 matrix
+    # instructions per block) and must still meet the fp32 bar.  (The
+    # products they drop are 2^-24 of c_score |x| |y|, as is the rounding of
+    # the fp32 accumulation itself, so the bar holds while that product stays
+    # within a few thousand base-2 units; it is about 2 * 10^3 here.)
+    X, Y, a, b = _problem(900 + d, 1300, 1100, d, scale=1.0 / np.sqrt(d))
+    eps = 0.015
+    c_score = 2.0 / (eps * np.log(2.0))
+    for o in (X.mean(0), Y.mean(0), 0.5 * (np.r_[X, Y].min(0) + np.r_[X, Y].max(0))):
+        bound = c_score * np.abs(X - o).sum(1).max() * np.abs(Y - o).max()
+        assert bound > 2 * 512, bound
+    p, f, g, _, _ = gpu_solve(X, Y, a, b, eps=eps, iters=6)
+    assert p.info["path"] == "fp32-small-mfma"
+    ref = oracle_solve(X, Y, a, b, eps=eps, iters=6)
+    assert max_err(host(f), ref["f"]) <= TOL_FP32 * eps
+    assert max_err(host(g), ref["g"]) <= TOL_FP32 * eps
+
+
 @pytest.mark.parametrize("prec,path", SMALL_D_PATHS)
 def test_small_d_splits(fs, prec, path):
     # Few rows, many keys: the key range is split across workgroups.
