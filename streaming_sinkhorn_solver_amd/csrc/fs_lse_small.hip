@@ -240,6 +240,19 @@ __device__ __forceinline__ int cload(const int* p) {
     return *(const __attribute__((address_space(4))) int*)p;
 }
 
+// Chunk-major LDS layout of a 32-key block of R-byte records (R / 16
+// chunks of 16 bytes per key): chunk h of key k sits at byte (32 h + k) 16,
+// so the matrix instruction's operand reads (lane k, chunk h) cover 16
+// consecutive bytes per lane across the wave, free of bank conflicts (the
+// record-major layout put the lanes R bytes apart: 4-way conflicts for
+// 64-byte records, 2-way for 32-byte ones).  A copy lane that fills LDS
+// position p of the block (in 16-byte units) reads chunk p / 32 of key
+// p % 32; the byte offset of that source within the block:
+template <int R>
+__device__ __forceinline__ uint32_t cmaj_src(uint32_t p) {
+    return (p & 31u) * (uint32_t)R + (p >> 5) * 16u;
+}
+
 // SPARSE: the block-sparse form.  The workgroup's keys are not a contiguous
 // range but the 32-key blocks listed for its row block by the screening
 // (LseArgs::bs_list, padded to whole tiles with a block of -inf records);
@@ -472,10 +485,12 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
             uint4 w0, w1;
             __builtin_memcpy(&w0, &hv[0], 16);
             __builtin_memcpy(&w1, &hv[8], 16);
-            uint4* o = (uint4*)((t < 256 ? dst0 + (size_t)t * kF16RecBytes
-                                         : dst1 + (size_t)(t - 256) * kF16RecBytes));
+            // chunk-major 32-key blocks (see cmaj_src)
+            const int tt = t < 256 ? t : t - 256;
+            uint4* o = (uint4*)((t < 256 ? dst0 : dst1) + (tt >> 5) * 32 * kF16RecBytes +
+                                (tt & 31) * 16);
             o[0] = w0;
-            o[1] = w1;
+            o[32] = w1;
         }
     };
 
@@ -547,7 +562,8 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
                     if constexpr (SPARSE && B3) {
                         const uint32_t Jc = min((uint32_t)w[l][0], (uint32_t)a.bs_sentinel);
                         dma_to_lds16(recs,
-                                     Jc * (uint32_t)BLK + (uint32_t)(L & 1) * 1024u + lane16,
+                                     Jc * (uint32_t)BLK +
+                                         cmaj_src<DREC_BYTES>((uint32_t)(L & 1) * 64u + lane),
                                      ring + slot * SLOT + L * 1024);
                     } else if constexpr (SPARSE) {
                         // instruction L covers blocks L*BPI .. L*BPI+BPI-1 of the tile;
@@ -558,11 +574,22 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
                         for (int q = 1; q < BPI; ++q)
                             if (lane / LPB == q) J = w[l][q];
                         const uint32_t Jc = min((uint32_t)J, (uint32_t)a.bs_sentinel);
-                        dma_to_lds16(recs, Jc * (uint32_t)BLK + (uint32_t)(lane % LPB) * 16u,
-                                     ring + slot * SLOT + L * 1024);
+                        const uint32_t voff = MODE == 1 ? cmaj_src<DREC_BYTES>(lane)
+                                                        : (uint32_t)(lane % LPB) * 16u;
+                        dma_to_lds16(recs, Jc * (uint32_t)BLK + voff, ring + slot * SLOT + L * 1024);
                     } else {
-                        dma_to_lds16(recs + (int64_t)k * TILE_BYTES + L * 1024, lane16,
-                                     ring + slot * SLOT + L * 1024);
+                        if constexpr (F16 || B3) {
+                            // instruction L fills 1 KiB at byte L * 1024 of the
+                            // tile: part of the block (L * 1024) / BLK
+                            const int64_t blk_base = (int64_t)(L * 1024 / BLK) * BLK;
+                            const uint32_t p0 = (uint32_t)(L * 1024 % BLK) / 16u;
+                            dma_to_lds16(recs + (int64_t)k * TILE_BYTES + blk_base,
+                                         cmaj_src<DREC_BYTES>(p0 + lane),
+                                         ring + slot * SLOT + L * 1024);
+                        } else {
+                            dma_to_lds16(recs + (int64_t)k * TILE_BYTES + L * 1024, lane16,
+                                         ring + slot * SLOT + L * 1024);
+                        }
                     }
                 }
             }
@@ -575,8 +602,11 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
                 sload_words<1>(a.bs_best + row_block, ent);
                 const uint32_t Jc = min((uint32_t)ent[0], (uint32_t)a.bs_sentinel);
                 if constexpr (B3) {
-                    dma_to_lds16(recs, Jc * (uint32_t)(32 * DREC_BYTES) + lane16, &ibuf[0]);
-                    dma_to_lds16(recs, Jc * (uint32_t)(32 * DREC_BYTES) + 1024u + lane16, &ibuf[64]);
+                    dma_to_lds16(recs, Jc * (uint32_t)BLK + cmaj_src<DREC_BYTES>(lane), &ibuf[0]);
+                    dma_to_lds16(recs, Jc * (uint32_t)BLK + cmaj_src<DREC_BYTES>(64u + lane),
+                                 &ibuf[64]);
+                } else if constexpr (MODE == 1) {
+                    dma_to_lds16(recs, Jc * (uint32_t)BLK + cmaj_src<DREC_BYTES>(lane), &ibuf[0]);
                 } else {
                     constexpr int LPB = 64 / (1024 / (32 * DREC_BYTES));
                     dma_to_lds16(recs,
@@ -651,13 +681,13 @@ __global__ __launch_bounds__(kSmallWaves * 64, 6) void lse_small_kernel(LseArgs 
         }
         auto scores = [&](const char* rb, f32x16& acc) __attribute__((always_inline)) {
             if constexpr (B3) {
-                const char* kr = rb + (size_t)ln * REC_BYTES + h * 16;
+                const char* kr = rb + h * 512 + ln * 16;  // chunk-major block
                 const bf16x8 a0 = *(const bf16x8*)kr;
-                const bf16x8 a1 = *(const bf16x8*)(kr + 32);
+                const bf16x8 a1 = *(const bf16x8*)(kr + 1024);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b3a, cm, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b3b, acc, 0, 0, 0);
             } else if constexpr (F16) {
-                const f16x8 av = *(const f16x8*)(rb + (size_t)ln * REC_BYTES + h * 16);
+                const f16x8 av = *(const f16x8*)(rb + h * 512 + ln * 16);  // chunk-major block
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b16, cm, 0, 0, 0);
             } else {
                 const float* rf = (const float*)rb + (size_t)ln * 2 * KP + h * KP;
