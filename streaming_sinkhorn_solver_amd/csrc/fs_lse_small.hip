@@ -21,7 +21,7 @@
 // that plays the role of the running maximum.  The vector side is left with
 // one exponential and one addition per pair.
 //
-// Two operand formats:
+// Three operand formats:
 //  * fp16, d <= 4: every value v is split into fp16 parts (v = vh + vl, the
 //    bias into three parts); the 16 contraction slots hold the products
 //    rh*yh, rh*yl, rl*yh per coordinate and bh, bm, bl, so one
@@ -42,14 +42,17 @@
 //
 // R_i is only moved when a block's terms 2^(z2 - R) grow large (their sum
 // above 2^64, checked with one compare) or on the row's first block; the move
-// goes to the block maximum if that exceeds R by more than 2^8.  (R, s) is
+// goes to the block maximum if that exceeds R by more than 2^8.  (The
+// block-sparse form lets the sum reach 2^96 and keeps R 2^64 above the block
+// maxima it starts from or moves to; see kSparseLift.)  (R, s) is
 // the same base-2 (max, sum) pair as in the exact online LSE, with R a valid
 // shift instead of the exact maximum: R + log2 s is unchanged, and the merge
 // and finalize stages are shared with the other paths.
 //
 // The key records (A rows, with the bias of the current potential) are packed
 // once per half-step by pack_key_records_kernel, streamed through LDS in tiles
-// of TK keys, and read by every wave of the workgroup.
+// of TK keys (the 16-bit formats stored chunk-major, see cmaj_src), and read
+// by every wave of the workgroup; three workgroups of 8 waves share a CU.
 #include "fs_device.hpp"
 #include "fs_internal.h"
 
