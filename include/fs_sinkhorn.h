@@ -53,10 +53,14 @@ typedef enum {
 } fs_status;
 
 /* Element type of the score contraction 2 x.y (everything after it is fp32).
- * AUTO, FP32: fp32 scores on the matrix cores.  For d <= 8 the whole biased
- *   score is one small fp32 matrix product per 32x32 block of pairs, so that
- *   the vector unit is left almost entirely to the one exponential per pair;
- *   for 8 < d <= 512 the points are zero-padded fp32 matrix operands.
+ * AUTO, FP32: fp32-accurate scores on the matrix cores.  For d <= 8 the
+ *   whole biased score is one small matrix product per 32x32 block of pairs,
+ *   so that the vector unit is left almost entirely to the one exponential
+ *   per pair: for d <= 4 on fp16 hi/lo splits of the operands where their
+ *   error bound holds, else on bf16 three-part splits (six products per
+ *   coordinate, fp32 accumulation, the error of fp32 products), for
+ *   5 <= d <= 8 on fp32 operands; for 8 < d <= 512 the points are
+ *   zero-padded fp32 matrix operands.
  * FP32_VALU (d <= 8 only): fp32 scores by vector FMA, one lane per row (the
  *   plain vector formulation; slower on gfx950, where exponentials and vector
  *   instructions share issue slots).
