@@ -438,7 +438,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this solver has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1",
+              "(its key ranges would shard across GPUs, but that is not built); "
+              "run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
